@@ -1,0 +1,244 @@
+"""Seeded synthetic inputs for the NVFP4 routed-MoE layer.
+
+This module only *makes* inputs: random weights and their NVFP4 encoding,
+activations, router logits, the shared-expert gate vector, and the byte
+layout of an expert slot.  It holds none of the layer's arithmetic (no
+decode of codes or scales, no routing, no expert FFN): both the HIP library
+and the CPU oracle read the bytes written here and decode them with their
+own code.
+
+Workloads follow the offloaded-MoE serving pages (FreeToken PR #385 "What
+this adds" and issue #62 "What it touches"): gate_up is [2I, H] with the
+gate rows first and the up rows after them, down is [H, I]; each row carries
+packed 4-bit codes, one FP8 scale per 16 consecutive elements of the row,
+and one fp32 global.  Sizes are the decode/prefill shapes of that model
+family (H = 2560, I = 640) with 256 experts and top-8.
+
+Encoding recipe (our reading; the pages do not state one): per row,
+g = amax/(6*448) (1 when the row is all zero); per 16-block,
+s = E4M3(amax_blk/(6*g)) rounded to nearest even and saturated at 448;
+each element becomes the E2M1 code nearest to w/(s*g), ties to the even
+mantissa, saturated at 6; a block whose scale rounds to 0 gets all-zero
+codes.  Element 2j of a row sits in the low nibble of byte j.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# Slot byte layout: [gu_codes | gu_scales | gu_globals | dn_codes | dn_scales | dn_globals]
+# ----------------------------------------------------------------------------
+
+
+def slot_regions(H: int, I: int):
+    """Byte (offset, size) of the six regions of one expert slot, in order."""
+    sizes = [
+        2 * I * H // 2,   # gate_up codes   u8 [2I, H/2]
+        2 * I * H // 16,  # gate_up scales  u8 [2I, H/16]
+        2 * I * 4,        # gate_up globals f32 [2I]
+        H * I // 2,       # down codes      u8 [H, I/2]
+        H * I // 16,      # down scales     u8 [H, I/16]
+        H * 4,            # down globals    f32 [H]
+    ]
+    out, off = [], 0
+    for s in sizes:
+        out.append((off, s))
+        off += s
+    return out
+
+
+def slot_nbytes(H: int, I: int) -> int:
+    off, size = slot_regions(H, I)[-1]
+    return off + size
+
+
+# ----------------------------------------------------------------------------
+# Encoders (float -> code bytes).  Generation only.
+# ----------------------------------------------------------------------------
+
+
+def encode_e4m3_nonneg(v: np.ndarray):
+    """Round non-negative values to OCP E4M3FN, nearest-even, saturating at 448.
+
+    Returns (byte codes u8, the rounded values as float32)."""
+    v = np.minimum(np.asarray(v, dtype=np.float64), 448.0)
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -6)))      # >= -6
+    q = np.exp2(e - 3.0)                                  # spacing of the binade
+    m = np.rint(v / q)                                    # half-to-even
+    val = m * q
+    mant, ex = np.frexp(val)                              # val = mant * 2^ex, mant in [0.5, 1)
+    normal = val >= 2.0 ** -6
+    E = np.where(normal, ex + 6, 0)
+    M = np.where(normal, np.rint((mant * 2.0 - 1.0) * 8.0), np.rint(val / 2.0 ** -9))
+    byte = (E.astype(np.int64) << 3) | M.astype(np.int64)
+    byte = np.where(val == 0.0, 0, byte)
+    return byte.astype(np.uint8), val.astype(np.float32)
+
+
+def encode_e2m1(r: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code (ties to even mantissa, saturating at 6) of float32 r."""
+    a = np.abs(r)
+    mag = ((a > 0.25).astype(np.uint8) + (a >= 0.75) + (a > 1.25) + (a >= 1.75)
+           + (a > 2.5) + (a >= 3.5) + (a > 5.0))
+    sign = (np.signbit(r)).astype(np.uint8) << 3
+    return (mag.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def quantize_nvfp4(W: np.ndarray):
+    """Quantize float32 W [rows, K] (K % 16 == 0) to (codes [rows,K/2], scales [rows,K/16], globals [rows])."""
+    W = np.asarray(W, dtype=np.float32)
+    rows, K = W.shape
+    assert K % 16 == 0
+    absW = np.abs(W)
+    amax = absW.max(axis=1)
+    g = np.where(amax > 0, amax / np.float32(6.0 * 448.0), np.float32(1.0)).astype(np.float32)
+    blk = absW.reshape(rows, K // 16, 16).max(axis=2)
+    target = (blk / (np.float32(6.0) * g[:, None])).astype(np.float32)
+    s_byte, s_val = encode_e4m3_nonneg(target)
+    denom = (s_val * g[:, None]).astype(np.float32)
+    safe = np.where(denom > 0, denom, np.float32(1.0))
+    r = (W.reshape(rows, K // 16, 16) / safe[..., None]).astype(np.float32)
+    codes = encode_e2m1(r)
+    codes = np.where((s_val > 0)[..., None], codes, np.uint8(0)).reshape(rows, K)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, s_byte.reshape(rows, K // 16), g
+
+
+def pack_slot(gu, dn, H: int, I: int) -> np.ndarray:
+    """Concatenate the quantized gate_up and down parts into one slot (u8 vector)."""
+    out = np.empty(slot_nbytes(H, I), dtype=np.uint8)
+    parts = [gu[0], gu[1], gu[2], dn[0], dn[1], dn[2]]
+    for (off, size), p in zip(slot_regions(H, I), parts):
+        b = np.ascontiguousarray(p).view(np.uint8).reshape(-1)
+        assert b.size == size, (b.size, size)
+        out[off:off + size] = b
+    return out
+
+
+def random_expert_slot(rng: np.random.Generator, H: int, I: int, std: float = 0.02) -> np.ndarray:
+    """One expert: W_gu ~ N(0, std) [2I, H] and W_dn ~ N(0, std) [H, I], quantized and packed."""
+    Wgu = rng.standard_normal((2 * I, H), dtype=np.float32) * np.float32(std)
+    Wdn = rng.standard_normal((H, I), dtype=np.float32) * np.float32(std)
+    return pack_slot(quantize_nvfp4(Wgu), quantize_nvfp4(Wdn), H, I)
+
+
+# ----------------------------------------------------------------------------
+# Activations and router logits
+# ----------------------------------------------------------------------------
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def zipf_gumbel_logits(rng: np.random.Generator, T: int, E: int, s: float, ranks: np.ndarray) -> np.ndarray:
+    """Logits whose top-k is sampling without replacement with p_e proportional to rank_e^-s.
+
+    ln p_e + Gumbel(0,1) noise per (token, expert); ranks is a permutation of 1..E."""
+    logp = -s * np.log(ranks.astype(np.float64))
+    logp -= np.log(np.exp(logp).sum())
+    u = rng.random((T, E))
+    gumbel = -np.log(-np.log(np.clip(u, 1e-300, 1.0 - 1e-16)))
+    return (logp[None, :] + gumbel).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Layer workloads
+# ----------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    H: int
+    I: int
+    E: int
+    k: int
+    T: int
+    bank: np.ndarray            # u8 [n_slots, slot_bytes]; slot E holds the shared expert
+    slot_of_expert: np.ndarray  # i32 [E]
+    shared_slot: int            # index into bank, or -1 for no shared expert
+    wg: np.ndarray              # u16 bf16 bits [H], shared-expert gate projection
+    x: np.ndarray               # u16 bf16 bits [T, H]
+    logits: np.ndarray          # f32 [T, E]
+
+    @property
+    def slot_bytes(self) -> int:
+        return self.bank.shape[1]
+
+
+CONFIGS = {
+    # name: (H, I, E, k, T, seed, logit kind)
+    "tiny": (256, 64, 8, 2, 4, 0, "normal"),
+    "decode_bs1": (2560, 640, 256, 8, 1, 1, "uniform"),
+    "decode_bs16": (2560, 640, 256, 8, 16, 16, "uniform"),
+    "prefill_2048": (2560, 640, 256, 8, 2048, 2048, "zipf"),
+}
+
+
+def make_bank(rng: np.random.Generator, H: int, I: int, n_slots: int, n_distinct: int | None = None) -> np.ndarray:
+    """n_slots quantized expert slots.  With n_distinct < n_slots, slot j repeats base expert j % n_distinct
+    (every slot keeps its own address; values stay those of properly quantized experts)."""
+    nd = n_slots if n_distinct is None else max(1, min(n_distinct, n_slots))
+    sb = slot_nbytes(H, I)
+    bank = np.empty((n_slots, sb), dtype=np.uint8)
+    for j in range(nd):
+        bank[j] = random_expert_slot(rng, H, I)
+    for j in range(nd, n_slots):
+        bank[j] = bank[j % nd]
+    return bank
+
+
+def make_logits(rng: np.random.Generator, T: int, E: int, kind: str) -> np.ndarray:
+    if kind == "normal":
+        return rng.standard_normal((T, E), dtype=np.float32)
+    if kind == "uniform":
+        return rng.random((T, E), dtype=np.float32)
+    if kind == "zipf":
+        ranks = rng.permutation(E) + 1
+        return zipf_gumbel_logits(rng, T, E, 1.2, ranks)
+    raise ValueError(kind)
+
+
+def make_layer(name: str, T: int | None = None, n_distinct: int | None = None, seed: int | None = None,
+               shared: bool = True) -> LayerInputs:
+    """Build one configuration's inputs from its seed: streams (weights, x, logits, w_g)."""
+    H, I, E, k, T0, seed0, kind = CONFIGS[name]
+    T = T0 if T is None else T
+    seed = seed0 if seed is None else seed
+    r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
+    n_slots = E + 1
+    bank = make_bank(r_w, H, I, n_slots, n_distinct)
+    x = f32_to_bf16_bits(r_x.standard_normal((T, H), dtype=np.float32))
+    logits = make_logits(r_l, T, E, kind)
+    wg = f32_to_bf16_bits(r_g.standard_normal(H, dtype=np.float32) * np.float32(0.02))
+    return LayerInputs(H, I, E, k, T, bank, np.arange(E, dtype=np.int32), E if shared else -1, wg, x, logits)
+
+
+def fresh_tokens(seed: int, T: int, H: int, E: int, kind: str):
+    """New activations and logits for another step of the same layer (bench rotation)."""
+    r_x, r_l = np.random.default_rng(seed).spawn(2)
+    return f32_to_bf16_bits(r_x.standard_normal((T, H), dtype=np.float32)), make_logits(r_l, T, E, kind)
+
+
+def expected_distinct(T: int, E: int, k: int) -> float:
+    """E[#distinct experts] for T tokens each picking k of E uniformly without replacement."""
+    return E * (1.0 - (1.0 - k / E) ** T)
+
+
+def prefill_flops(T: int, H: int, I: int, k: int, shared: bool = True) -> float:
+    """Algorithmic FLOPs of one prefill chunk: 2*3*I*H per (token, expert) pair."""
+    return 2.0 * 3.0 * I * H * (T * k + (T if shared else 0))
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+

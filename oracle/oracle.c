@@ -1,0 +1,377 @@
+/*
+ * CPU oracle for the NVFP4 routed-MoE layer of an offloaded-MoE server.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously-correct
+ * definition that the HIP library is checked against.  Only the test suite,
+ * the package smoke check and the CPU-baseline leg of the benchmark may load
+ * it.  It shares no code, header, table or constant generator with the HIP
+ * library, and the library never calls it.
+ *
+ * Sources (FreeToken pages): PR #385 "What this adds" (NVFP4 expert banks
+ * with packed codes, 16-wide scale blocks and per-row globals; sliced along
+ * the intermediate axis; combine routed + sigmoid(gate) * shared before one
+ * reduction) and issue #62 "What it touches" (gate_up is [2I, H] with gate
+ * rows [0, I) and up rows [I, 2I); down is [H, I]; a rank's slice is two
+ * disjoint gate/up row ranges plus a down column slice), and the R9700
+ * interim report on #62 (norm_topk_prob: the k selected weights are
+ * renormalised; the router is replicated).  Number formats: E2M1 and E4M3FN
+ * are the OCP 8-bit / microscaling element formats.
+ *
+ * Readings where the pages are silent (each one is listed in the design doc):
+ *  - code nibble order: element 2j is the low nibble of byte j;
+ *  - scale blocks run along the contraction axis (H for gate_up, I for down);
+ *  - dequant: W = f32( f32(e2m1 * e4m3) * global ), the inner product exact;
+ *  - routing weights: softmax over the k selected logits (the same as a full
+ *    softmax followed by renormalisation over the top k), ties in selection
+ *    broken by the lower expert index;
+ *  - activation: SwiGLU, silu(gate) * up, no clamp;
+ *  - shared gate: s_t = sigmoid(x_t . w_g), applied after the shared expert.
+ *
+ * Arithmetic: fp32 dequant, double accumulation, one rounding to f32 at the
+ * output.  Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- formats */
+
+/* E2M1: sign bit, 2 exponent bits (bias 1), 1 mantissa bit; no inf/NaN.
+ * Exponent field 0 is subnormal: value 0.5 * m. */
+double oracle_e2m1(int code) {
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* E4M3FN (OCP): sign, 4 exponent bits (bias 7), 3 mantissa bits; no inf;
+ * S.1111.111 is NaN; exponent field 0 is subnormal: (m/8) * 2^-6. */
+double oracle_e4m3(int byte) {
+    int s = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+static double bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* One dequantised row: out[c] = f32( f32(e2m1(code) * e4m3(scale)) * g ). */
+static void dequant_row(const uint8_t* codes, const uint8_t* scales, float g, int K, float* out) {
+    for (int c = 0; c < K; ++c) {
+        int code = (codes[c / 2] >> (4 * (c & 1))) & 0xF;
+        float q = (float)(oracle_e2m1(code) * oracle_e4m3(scales[c / 16]));
+        out[c] = q * g;
+    }
+}
+
+/* Dequantise a [rows, K] NVFP4 matrix into fp32. */
+void oracle_dequant(const uint8_t* codes, const uint8_t* scales, const float* globals, int rows, int K,
+                    float* out) {
+    for (int r = 0; r < rows; ++r)
+        dequant_row(codes + (size_t)r * (K / 2), scales + (size_t)r * (K / 16), globals[r], K,
+                    out + (size_t)r * K);
+}
+
+/* ---------------------------------------------------------------- routing */
+
+/* Top-k by (logit descending, expert index ascending); weights are the
+ * softmax over the k chosen logits, in double, stored rounded to f32.
+ * Returns 0, or -1 if a logit is NaN (a precondition violation). */
+int oracle_route(const float* logits, int T, int E, int k, int32_t* ids, float* w) {
+    char* taken = (char*)malloc((size_t)E);
+    double* ex = (double*)malloc(sizeof(double) * (size_t)k);
+    int rc = 0;
+    for (int t = 0; t < T && rc == 0; ++t) {
+        const float* l = logits + (size_t)t * E;
+        memset(taken, 0, (size_t)E);
+        for (int e = 0; e < E; ++e)
+            if (isnan(l[e])) rc = -1;
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e; /* strict: the lower index wins ties */
+            }
+            taken[best] = 1;
+            ids[(size_t)t * k + j] = best;
+        }
+        double m = l[ids[(size_t)t * k]];
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) {
+            ex[j] = exp((double)l[ids[(size_t)t * k + j]] - m);
+            sum += ex[j];
+        }
+        for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = (float)(ex[j] / sum);
+    }
+    free(taken);
+    free(ex);
+    return rc;
+}
+
+/* Counting sort of the T*k assignments by expert.  offsets[E+1] is the
+ * exclusive scan of the per-expert counts; sorted_assign lists flat indices
+ * t*k+j ordered by (expert, t, j); assign_pos is its inverse. */
+void oracle_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* sorted_assign,
+                    int32_t* assign_pos) {
+    int n = T * k;
+    int32_t* fill = (int32_t*)calloc((size_t)E + 1, sizeof(int32_t));
+    for (int e = 0; e <= E; ++e) offsets[e] = 0;
+    for (int a = 0; a < n; ++a) offsets[ids[a] + 1] += 1;
+    for (int e = 0; e < E; ++e) offsets[e + 1] += offsets[e];
+    for (int a = 0; a < n; ++a) {
+        int e = ids[a];
+        int p = offsets[e] + fill[e]++;
+        sorted_assign[p] = a;
+        assign_pos[a] = p;
+    }
+    free(fill);
+}
+
+/* ---------------------------------------------------------------- layer */
+
+typedef struct {
+    const uint8_t *gu_codes, *gu_scales, *dn_codes, *dn_scales;
+    const float *gu_glob, *dn_glob;
+} slot_view;
+
+/* Region order in a slot: gate_up codes, gate_up scales, gate_up globals,
+ * down codes, down scales, down globals (row-major, no padding). */
+static slot_view view_slot(const uint8_t* slot, int H, int I) {
+    slot_view v;
+    size_t off = 0;
+    v.gu_codes = slot + off; off += (size_t)2 * I * H / 2;
+    v.gu_scales = slot + off; off += (size_t)2 * I * H / 16;
+    v.gu_glob = (const float*)(slot + off); off += (size_t)2 * I * 4;
+    v.dn_codes = slot + off; off += (size_t)H * I / 2;
+    v.dn_scales = slot + off; off += (size_t)H * I / 16;
+    v.dn_glob = (const float*)(slot + off);
+    return v;
+}
+
+size_t oracle_slot_bytes(int H, int I) {
+    return (size_t)2 * I * H / 2 + (size_t)2 * I * H / 16 + (size_t)2 * I * 4 + (size_t)H * I / 2 +
+           (size_t)H * I / 16 + (size_t)H * 4;
+}
+
+/* silu(z) * up with silu(z) = z / (1 + exp(-z)). */
+static double swiglu(double gate, double up) { return gate / (1.0 + exp(-gate)) * up; }
+
+/* Expert FFN for one token: a = W_gu x; h = silu(a[:I]) * a[I:]; o = W_dn h. */
+static void expert_ffn(const uint8_t* slot, int H, int I, const double* x, double* a, double* h, float* row,
+                       double* o) {
+    slot_view v = view_slot(slot, H, I);
+    for (int r = 0; r < 2 * I; ++r) {
+        dequant_row(v.gu_codes + (size_t)r * (H / 2), v.gu_scales + (size_t)r * (H / 16), v.gu_glob[r], H, row);
+        double acc = 0.0;
+        for (int c = 0; c < H; ++c) acc += (double)row[c] * x[c];
+        a[r] = acc;
+    }
+    for (int i = 0; i < I; ++i) h[i] = swiglu(a[i], a[I + i]);
+    for (int r = 0; r < H; ++r) {
+        dequant_row(v.dn_codes + (size_t)r * (I / 2), v.dn_scales + (size_t)r * (I / 16), v.dn_glob[r], I, row);
+        double acc = 0.0;
+        for (int c = 0; c < I; ++c) acc += (double)row[c] * h[c];
+        o[r] = acc;
+    }
+}
+
+/* Shared-expert gate: s_t = 1 / (1 + exp(-(x_t . w_g))), dot in double. */
+void oracle_shared_gate(const uint16_t* x, int T, int H, const uint16_t* wg, double* s) {
+    for (int t = 0; t < T; ++t) {
+        double g = 0.0;
+        for (int c = 0; c < H; ++c) g += bf16_to_double(x[(size_t)t * H + c]) * bf16_to_double(wg[c]);
+        s[t] = 1.0 / (1.0 + exp(-g));
+    }
+}
+
+/* y_t = sum_j w_tj * FFN_{ids[t,j]}(x_t) + s_t * FFN_shared(x_t), in double,
+ * rounded once to f32.  Experts are found through slot_of_expert in the
+ * bank (slot index, or -1 to leave that expert out); shared_slot < 0 means
+ * no shared term.  Computes the n_tokens rows listed in tokens (all T when
+ * tokens is NULL), y laid out in list order.  Returns 0 or -1 on bad input. */
+int oracle_forward(int H, int I, int E, int k, const uint8_t* bank, size_t slot_bytes, const int32_t* slot_of_expert,
+                   long shared_slot, const uint16_t* wg, const uint16_t* x, int T, const int32_t* ids, const float* w,
+                   const int32_t* tokens, int n_tokens, float* y, int nthreads) {
+    if (slot_bytes != oracle_slot_bytes(H, I) || H % 16 || I % 16) return -1;
+    if (tokens == NULL) n_tokens = T;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel reduction(| : bad)
+#endif
+    {
+        double* xd = (double*)malloc(sizeof(double) * (size_t)H);
+        double* a = (double*)malloc(sizeof(double) * (size_t)2 * I);
+        double* h = (double*)malloc(sizeof(double) * (size_t)I);
+        double* o = (double*)malloc(sizeof(double) * (size_t)H);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+        float* row = (float*)malloc(sizeof(float) * (size_t)(H > I ? H : I));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int n = 0; n < n_tokens; ++n) {
+            int t = tokens ? tokens[n] : n;
+            if (t < 0 || t >= T) { bad = 1; continue; }
+            for (int c = 0; c < H; ++c) xd[c] = bf16_to_double(x[(size_t)t * H + c]);
+            for (int c = 0; c < H; ++c) acc[c] = 0.0;
+            for (int j = 0; j < k; ++j) {
+                int e = ids[(size_t)t * k + j];
+                if (e < 0 || e >= E) { bad = 1; continue; }
+                int s = slot_of_expert[e];
+                if (s < 0) continue;
+                expert_ffn(bank + (size_t)s * slot_bytes, H, I, xd, a, h, row, o);
+                double wj = (double)w[(size_t)t * k + j];
+                for (int c = 0; c < H; ++c) acc[c] += wj * o[c];
+            }
+            if (shared_slot >= 0) {
+                double g = 0.0;
+                for (int c = 0; c < H; ++c) g += xd[c] * bf16_to_double(wg[c]);
+                double st = 1.0 / (1.0 + exp(-g));
+                expert_ffn(bank + (size_t)shared_slot * slot_bytes, H, I, xd, a, h, row, o);
+                for (int c = 0; c < H; ++c) acc[c] += st * o[c];
+            }
+            for (int c = 0; c < H; ++c) y[(size_t)n * H + c] = (float)acc[c];
+        }
+        free(xd); free(a); free(h); free(o); free(acc); free(row);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------- slicing */
+
+/* Slice r of n along the intermediate axis, I_l = I / n: gate rows
+ * [r*I_l, (r+1)*I_l) followed by up rows [I + r*I_l, I + (r+1)*I_l) with
+ * their scales and globals; down columns [r*I_l, (r+1)*I_l) of every one of
+ * the H rows (code bytes and scale columns cut to match, all H globals
+ * kept).  dst is a slot of shape (H, I_l).  Returns 0, or -1 if the slice
+ * does not fall on whole scale blocks. */
+int oracle_slice_slot(const uint8_t* src, int H, int I, int r, int n, uint8_t* dst) {
+    if (n <= 0 || r < 0 || r >= n || I % n) return -1;
+    int Il = I / n;
+    if (Il % 16) return -1;
+    slot_view s = view_slot(src, H, I);
+    uint8_t* p = dst;
+    /* gate_up codes, then scales, then globals: the gate range then the up range */
+    const int rows0[2] = {r * Il, I + r * Il};
+    for (int part = 0; part < 2; ++part)
+        for (int i = 0; i < Il; ++i) {
+            memcpy(p, s.gu_codes + (size_t)(rows0[part] + i) * (H / 2), (size_t)H / 2);
+            p += H / 2;
+        }
+    for (int part = 0; part < 2; ++part)
+        for (int i = 0; i < Il; ++i) {
+            memcpy(p, s.gu_scales + (size_t)(rows0[part] + i) * (H / 16), (size_t)H / 16);
+            p += H / 16;
+        }
+    for (int part = 0; part < 2; ++part)
+        for (int i = 0; i < Il; ++i) {
+            memcpy(p, &s.gu_glob[rows0[part] + i], 4);
+            p += 4;
+        }
+    for (int row = 0; row < H; ++row) {
+        memcpy(p, s.dn_codes + (size_t)row * (I / 2) + (size_t)r * (Il / 2), (size_t)Il / 2);
+        p += Il / 2;
+    }
+    for (int row = 0; row < H; ++row) {
+        memcpy(p, s.dn_scales + (size_t)row * (I / 16) + (size_t)r * (Il / 16), (size_t)Il / 16);
+        p += Il / 16;
+    }
+    memcpy(p, s.dn_glob, (size_t)H * 4);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- LRU model */
+
+/* One global pool of C cache slots shared by every (layer, expert), cold
+ * at the start.  For each step and each layer in order: take the distinct
+ * routed experts in ascending order; first mark the ones already cached as
+ * most recently used (ascending order), then give each missing one, in
+ * ascending order, the lowest free slot or else the slot of the least
+ * recently used entry, which is evicted.
+ *
+ * ids: [steps][L][T*k] routed expert ids.  Outputs per (step, layer):
+ * hits and misses counts; slot_map [steps][L][E] (cache slot of each routed
+ * expert after the fill, -1 for experts not routed); miss_slots
+ * [steps][L][T*k] lists, in ascending expert order, the slot each miss was
+ * put in (unused entries -1).  Returns 0, or -1 if C is smaller than the
+ * number of distinct experts one layer-step needs. */
+int oracle_lru_run(int L, int E, int C, int steps, int T, int k, const int32_t* ids, int32_t* hits, int32_t* misses,
+                   int32_t* slot_map, int32_t* miss_slots) {
+    int n = T * k;
+    int32_t* where = (int32_t*)malloc(sizeof(int32_t) * (size_t)L * E); /* (l,e) -> slot or -1 */
+    int32_t* owner = (int32_t*)malloc(sizeof(int32_t) * (size_t)C);     /* slot -> l*E+e or -1 */
+    int32_t* prev = (int32_t*)malloc(sizeof(int32_t) * (size_t)C);      /* recency list over slots */
+    int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)C);
+    char* routed = (char*)malloc((size_t)E);
+    int head = -1, tail = -1; /* head = least recently used, tail = most recently used */
+    int rc = 0;
+    for (size_t i = 0; i < (size_t)L * E; ++i) where[i] = -1;
+    for (int c = 0; c < C; ++c) owner[c] = -1, prev[c] = next[c] = -1;
+#define UNLINK(c)                                   \
+    do {                                            \
+        if (prev[c] >= 0) next[prev[c]] = next[c];  \
+        else head = next[c];                        \
+        if (next[c] >= 0) prev[next[c]] = prev[c];  \
+        else tail = prev[c];                        \
+        prev[c] = next[c] = -1;                     \
+    } while (0)
+#define PUSH_MRU(c)                                 \
+    do {                                            \
+        prev[c] = tail; next[c] = -1;               \
+        if (tail >= 0) next[tail] = c; else head = c; \
+        tail = c;                                   \
+    } while (0)
+    int n_free_next = 0; /* slots [n_free_next, C) have never been used */
+    for (int st = 0; st < steps && rc == 0; ++st) {
+        for (int l = 0; l < L; ++l) {
+            size_t sl = (size_t)st * L + l;
+            const int32_t* id = ids + sl * n;
+            memset(routed, 0, (size_t)E);
+            int distinct = 0;
+            for (int a = 0; a < n; ++a)
+                if (!routed[id[a]]) routed[id[a]] = 1, distinct++;
+            if (distinct > C) { rc = -1; break; }
+            int h = 0, m = 0;
+            for (int e = 0; e < E; ++e) {
+                if (!routed[e]) continue;
+                int c = where[(size_t)l * E + e];
+                if (c >= 0) { UNLINK(c); PUSH_MRU(c); h++; }
+            }
+            int32_t* ms = miss_slots ? miss_slots + sl * n : NULL;
+            if (ms) for (int a = 0; a < n; ++a) ms[a] = -1;
+            for (int e = 0; e < E; ++e) {
+                if (!routed[e] || where[(size_t)l * E + e] >= 0) continue;
+                int c;
+                if (n_free_next < C) c = n_free_next++;
+                else {
+                    c = head;
+                    UNLINK(c);
+                    where[owner[c]] = -1;
+                }
+                owner[c] = l * E + e;
+                where[(size_t)l * E + e] = c;
+                PUSH_MRU(c);
+                if (ms) ms[m] = c;
+                m++;
+            }
+            hits[sl] = h;
+            misses[sl] = m;
+            if (slot_map)
+                for (int e = 0; e < E; ++e) slot_map[sl * E + e] = routed[e] ? where[(size_t)l * E + e] : -1;
+        }
+    }
+#undef UNLINK
+#undef PUSH_MRU
+    free(where); free(owner); free(prev); free(next); free(routed);
+    return rc;
+}

@@ -1,0 +1,338 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test checks an oracle function against something other than its own
+formula: format tables from the OCP specifications (golden files), a
+library decoder (torch's float8_e4m3fn), library sorting/softmax/matmul,
+closed forms, hand-worked traces and algebraic invariants.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from expert_offload_serving_amd import synth
+
+
+def _read_table(path):
+    rows = []
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- formats
+
+def test_e2m1_matches_ocp_table(golden_dir):
+    rows = _read_table(os.path.join(golden_dir, "e2m1_values.txt"))
+    assert len(rows) == 16
+    for code, val in rows:
+        got = oracle.e2m1(int(code))
+        want = float(val)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (code, got, want)
+
+
+def test_e4m3_spot_values(golden_dir):
+    for byte, val in _read_table(os.path.join(golden_dir, "e4m3_spot.txt")):
+        got = oracle.e4m3(int(byte, 16))
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), (byte, got)
+
+
+def test_e4m3_all_bytes_match_torch_decoder():
+    lib_vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for b in range(256):
+        got = oracle.e4m3(b)
+        if math.isnan(lib_vals[b]):
+            assert math.isnan(got), b
+        else:
+            assert got == lib_vals[b] and math.copysign(1, got) == math.copysign(1, lib_vals[b]), b
+
+
+def test_e2m1_times_e4m3_is_exact_in_f32_and_bf16():
+    """Every code x scale product has <= 6 significant bits: exact in f32 and bf16."""
+    for c in range(16):
+        for b in range(256):
+            s = oracle.e4m3(b)
+            if math.isnan(s):
+                continue
+            p = oracle.e2m1(c) * s
+            p32 = float(np.float32(p))
+            assert p32 == p
+            pb = float(torch.tensor(p, dtype=torch.float64).to(torch.bfloat16).to(torch.float64))
+            assert pb == p
+
+
+# ---------------------------------------------------------------- dequant
+
+def _independent_dequant(codes, scales, g):
+    """Dequant via a literal E2M1 table and torch's E4M3 decoder, numpy float32 ops."""
+    table = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0],
+                     dtype=np.float32)
+    rows, half = codes.shape
+    nib = np.empty((rows, half * 2), dtype=np.uint8)
+    nib[:, 0::2] = codes & 0xF
+    nib[:, 1::2] = codes >> 4
+    sv = torch.from_numpy(scales.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    q = table[nib] * np.repeat(sv, 16, axis=1)          # exact
+    return (q * g[:, None]).astype(np.float32)           # one rounding
+
+
+def test_dequant_matches_independent_decode_bitexact():
+    rng = np.random.default_rng(5)
+    rows, K = 37, 96
+    codes = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (rows, K // 16), dtype=np.uint8)
+    scales[(scales & 0x7F) == 0x7F] = 0x38                # avoid NaN scales (not produced by the encoder)
+    g = (rng.standard_normal(rows) * 1e-3).astype(np.float32)
+    got = oracle.dequant(codes, scales, g)
+    want = _independent_dequant(codes, scales, g)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_dequant_nibble_order_and_scale_blocks():
+    """Byte 0x21 holds element 0 = code 1 (0.5) in its low nibble and element 1 = code 2 (1.0) in its high nibble;
+    scale byte j covers elements [16j, 16j+16) of the row."""
+    K = 32
+    codes = np.zeros((1, K // 2), dtype=np.uint8)
+    codes[0, 0] = 0x21
+    codes[0, 8] = 0xF7                                    # elements 16, 17: code 7 (6.0), code 15 (-6.0)
+    scales = np.array([[0x38, 0x40]], dtype=np.uint8)     # 1.0 for block 0, 2.0 for block 1
+    out = oracle.dequant(codes, scales, np.array([0.5], dtype=np.float32))
+    assert out[0, 0] == 0.25 and out[0, 1] == 0.5
+    assert out[0, 16] == 6.0 and out[0, 17] == -6.0
+    assert np.all(out[0, 2:16] == 0) and np.all(out[0, 18:] == 0)
+
+
+# ---------------------------------------------------------------- routing
+
+def test_route_matches_bruteforce_sort_and_softmax():
+    rng = np.random.default_rng(11)
+    for T, E, k in [(5, 8, 2), (3, 64, 8), (4, 16, 16), (2, 9, 1)]:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        ids, w = oracle.route(logits, k)
+        for t in range(T):
+            want = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
+            assert list(ids[t]) == want
+            sw = scipy.special.softmax(logits[t, want].astype(np.float64)).astype(np.float32)
+            np.testing.assert_allclose(w[t], sw, rtol=2e-7, atol=0)
+            assert abs(float(np.sum(w[t].astype(np.float64))) - 1.0) <= k * 2.0 ** -23
+
+
+def test_route_ties_go_to_lower_index_and_k1_weight_is_one():
+    logits = np.array([[-1.0, 3.0, 3.0, -0.0, 0.0, 3.0]], dtype=np.float32)
+    ids, w = oracle.route(logits, 4)
+    assert list(ids[0]) == [1, 2, 5, 3]                   # -0 == +0: index 3 before 4
+    np.testing.assert_allclose(w[0, :3], w[0, 0])
+    ids1, w1 = oracle.route(logits, 1)
+    assert ids1[0, 0] == 1 and w1[0, 0] == 1.0
+
+
+def test_route_rejects_nan():
+    with pytest.raises(ValueError):
+        oracle.route(np.array([[0.0, np.nan]], dtype=np.float32), 1)
+
+
+def test_permute_matches_stable_argsort():
+    rng = np.random.default_rng(3)
+    for T, E, k in [(1, 256, 8), (16, 256, 8), (300, 32, 4), (7, 5, 5)]:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        off, srt, pos = oracle.permute(ids, E)
+        flat = ids.reshape(-1)
+        want = np.argsort(flat, kind="stable")
+        assert np.array_equal(srt, want)
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+        assert np.array_equal(pos[srt], np.arange(T * k))
+
+
+# ---------------------------------------------------------------- layer
+
+def _dense_dequant_slot(slot, H, I):
+    reg = synth.slot_regions(H, I)
+    def part(i, shape, dt=np.uint8):
+        off, size = reg[i]
+        return slot[off:off + size].view(dt).reshape(shape)
+    Wgu = _independent_dequant(part(0, (2 * I, H // 2)), part(1, (2 * I, H // 16)), part(2, (2 * I,), np.float32))
+    Wdn = _independent_dequant(part(3, (H, I // 2)), part(4, (H, I // 16)), part(5, (H,), np.float32))
+    return Wgu.astype(np.float64), Wdn.astype(np.float64)
+
+
+def _bruteforce_layer(L, ids, w, shared=True):
+    """Dense float64 reference: torch matmul, torch.nn.functional.silu, torch.sigmoid."""
+    X = torch.from_numpy(synth.bf16_bits_to_f32(L.x).astype(np.float64))
+    Y = torch.zeros((L.T, L.H), dtype=torch.float64)
+    dense = {}
+    def ffn(slot_idx, xrows):
+        if slot_idx not in dense:
+            dense[slot_idx] = [torch.from_numpy(m) for m in _dense_dequant_slot(L.bank[slot_idx], L.H, L.I)]
+        Wgu, Wdn = dense[slot_idx]
+        A = xrows @ Wgu.T
+        Hh = torch.nn.functional.silu(A[:, :L.I]) * A[:, L.I:]
+        return Hh @ Wdn.T
+    for t in range(L.T):
+        for j in range(L.k):
+            s = int(L.slot_of_expert[ids[t, j]])
+            if s >= 0:
+                Y[t] += float(w[t, j]) * ffn(s, X[t:t + 1])[0]
+        if shared and L.shared_slot >= 0:
+            gate = torch.sigmoid(X[t] @ torch.from_numpy(synth.bf16_bits_to_f32(L.wg).astype(np.float64)))
+            Y[t] += gate * ffn(L.shared_slot, X[t:t + 1])[0]
+    return Y.numpy()
+
+
+def _run_oracle(L, ids, w, **kw):
+    return oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w, **kw)
+
+
+def test_forward_tiny_matches_dense_bruteforce():
+    L = synth.make_layer("tiny")
+    ids, w = oracle.route(L.logits, L.k)
+    y = _run_oracle(L, ids, w)
+    ref = _bruteforce_layer(L, ids, w)
+    assert np.max(np.abs(y - ref)) <= 1e-6 * np.max(np.abs(ref))
+    assert np.abs(ref).max() > 0
+
+
+def test_forward_token_subset_and_skipped_experts():
+    L = synth.make_layer("tiny", T=6)
+    ids, w = oracle.route(L.logits, L.k)
+    full = _run_oracle(L, ids, w)
+    sub = _run_oracle(L, ids, w, tokens=[4, 1])
+    assert np.array_equal(sub, full[[4, 1]])
+    # leaving every routed expert out leaves exactly the gated shared expert
+    L2 = synth.make_layer("tiny", T=6)
+    L2.slot_of_expert = np.full(L2.E, -1, dtype=np.int32)
+    only_shared = _run_oracle(L2, ids, w)
+    ref = _bruteforce_layer(L2, ids, w)
+    assert np.max(np.abs(only_shared - ref)) <= 1e-6 * np.max(np.abs(ref))
+
+
+def test_forward_special_cases():
+    L = synth.make_layer("tiny")
+    ids, w = oracle.route(L.logits, L.k)
+    # all-zero bank -> y = 0
+    Z = synth.make_layer("tiny")
+    Z.bank = np.zeros_like(Z.bank)
+    assert np.all(_run_oracle(Z, ids, w) == 0)
+    # w_g = 0 -> sigmoid(0) = 1/2: y = routed + shared/2
+    G = synth.make_layer("tiny")
+    G.wg = np.zeros_like(G.wg)
+    y = _run_oracle(G, ids, w)
+    G2 = synth.make_layer("tiny"); G2.wg = np.zeros_like(G2.wg); G2.shared_slot = -1
+    routed = _run_oracle(G2, ids, w)
+    G3 = synth.make_layer("tiny"); G3.wg = np.zeros_like(G3.wg); G3.slot_of_expert[:] = -1
+    shared = _run_oracle(G3, ids, w)
+    np.testing.assert_allclose(y, routed + shared, rtol=1e-6, atol=1e-7)
+    s = oracle.shared_gate(G.x, G.wg)
+    assert np.all(s == 0.5)
+
+
+def test_forward_closed_form_all_ones_expert():
+    """One expert whose every weight is 1 (codes 2 = 1.0, scale 0x38 = 1.0, globals 1): with x = 0.5 everywhere,
+    a_r = H/2 for every row, h_i = silu(H/2) * H/2, o_r = I * h; k=1 gives w=1 and y = o."""
+    H, I, E = 32, 16, 1
+    sb = synth.slot_nbytes(H, I)
+    slot = np.zeros(sb, dtype=np.uint8)
+    reg = synth.slot_regions(H, I)
+    for i in (0, 3):
+        off, size = reg[i]; slot[off:off + size] = 0x22
+    for i in (1, 4):
+        off, size = reg[i]; slot[off:off + size] = 0x38
+    for i in (2, 5):
+        off, size = reg[i]; slot[off:off + size] = np.ones(size // 4, dtype=np.float32).view(np.uint8)
+    bank = slot[None, :]
+    x = synth.f32_to_bf16_bits(np.full((1, H), 0.5, dtype=np.float32))
+    a = H / 2.0
+    want = I * (a / (1.0 + math.exp(-a))) * a
+    y = oracle.forward(H, I, E, 1, bank, np.array([0], np.int32), -1, np.zeros(H, np.uint16), x,
+                       np.array([[0]], np.int32), np.array([[1.0]], np.float32))
+    assert np.all(y == np.float32(want))
+
+
+# ---------------------------------------------------------------- slicing and geometry
+
+def test_slot_geometry_matches_pages():
+    assert oracle.slot_bytes(2560, 640) == 2_780_160
+    assert oracle.slot_bytes(256, 64) == 29_184
+    half = oracle.slot_bytes(2560, 320)
+    assert half == 1_395_200
+    # PR #385 / issue #62 R9700 comment: 655 half-slots of "~1.33 MiB" are about 0.848 GiB
+    assert round(half / 2 ** 20, 2) == 1.33
+    assert abs(655 * half / 2 ** 30 - 0.848) < 0.005
+
+
+def test_slice_dequant_equals_dequant_slice():
+    H, I = 64, 64
+    slot = synth.random_expert_slot(np.random.default_rng(2), H, I)
+    Wgu, Wdn = _dense_dequant_slot(slot, H, I)
+    for n in (2, 4):
+        Il = I // n
+        for r in range(n):
+            sl = oracle.slice_slot(slot, H, I, r, n)
+            Sgu, Sdn = _dense_dequant_slot(sl, H, Il)
+            rows = np.r_[r * Il:(r + 1) * Il, I + r * Il:I + (r + 1) * Il]
+            assert np.array_equal(Sgu, Wgu[rows])
+            assert np.array_equal(Sdn, Wdn[:, r * Il:(r + 1) * Il])
+
+
+def test_slice_partials_sum_to_full():
+    L = synth.make_layer("tiny", T=5)
+    ids, w = oracle.route(L.logits, L.k)
+    full = _run_oracle(L, ids, w).astype(np.float64)
+    tot = np.zeros_like(full)
+    for r in range(2):
+        S = synth.make_layer("tiny", T=5)
+        S.bank = np.stack([oracle.slice_slot(b, L.H, L.I, r, 2) for b in L.bank])
+        S.I = L.I // 2
+        tot += _run_oracle(S, ids, w)
+    assert np.max(np.abs(tot - full)) <= 1e-6 * np.max(np.abs(full))
+
+
+def test_slice_rejects_partial_blocks():
+    with pytest.raises(ValueError):
+        oracle.slice_slot(np.zeros(synth.slot_nbytes(64, 32), np.uint8), 64, 32, 0, 4)
+
+
+# ---------------------------------------------------------------- LRU model
+
+def test_lru_hand_trace(golden_dir):
+    rows = []
+    for line in open(os.path.join(golden_dir, "lru_trace.txt")):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            a, b, c = line.split("|")
+            rows.append(([int(v) for v in a.split()], [int(v) for v in b.split()], [int(v) for v in c.split()]))
+    steps, L = 3, 2
+    ids = np.zeros((steps, L, 2), dtype=np.int32)
+    for (st, l, i0, i1), _, _ in rows:
+        ids[st, l] = (i0, i1)
+    hits, misses, smap, mslots = oracle.lru_run(ids, E=4, C=3)
+    for (st, l, _, _), (h, m), ms in rows:
+        assert hits[st, l] == h and misses[st, l] == m
+        assert list(mslots[st, l][:m]) == ms
+    assert list(smap[2, 1]) == [0, -1, 1, -1]
+
+
+def test_lru_invariants():
+    rng = np.random.default_rng(9)
+    steps, L, E, n = 20, 3, 16, 6
+    ids = rng.integers(0, E, (steps, L, n), dtype=np.int32)
+    hits, misses, smap, mslots = oracle.lru_run(ids, E=E, C=12)
+    for st in range(steps):
+        for l in range(L):
+            d = len(set(ids[st, l].tolist()))
+            assert hits[st, l] + misses[st, l] == d
+            routed = sorted(set(ids[st, l].tolist()))
+            slots = smap[st, l][routed]
+            assert np.all(slots >= 0) and len(set(slots.tolist())) == d
+    # a pool holding everything misses only on first touch
+    h2, m2, _, _ = oracle.lru_run(ids, E=E, C=L * E)
+    first = sum(len(set(ids[:, l].reshape(-1).tolist())) for l in range(L))
+    assert int(m2.sum()) == first
