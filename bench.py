@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 routed-MoE layer (route + forward) on one MI355X.
+
+A step is one pass of the layer over one batch of synthetic tokens: top-k
+routing and permutation, then the NVFP4 expert forward with the shared
+expert and the combine.  Inputs (activations, logits, weights) are resident
+in HBM before timing; every step uses fresh routing and, to keep the 256 MB
+Infinity Cache from serving repeated experts, one of several copies of the
+expert bank in turn.  The steps are captured in a HIP graph and replayed.
+
+Default workload (the decode shape the metric is quoted on): H=2560,
+I=640, 256 experts top-8 with uniform-random logits, one shared expert,
+batch 1.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME|all]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "MoE-layer tokens/s + expert-weight HBM GB/s (% peak), H2560 I640 NVFP4"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- inputs
+
+def build_inputs(name: str, steps: int, replicas: int, distinct: int):
+    """Host inputs: the expert bank (E routed + 1 shared slot), per-step activations and logits."""
+    from expert_offload_serving_amd import synth
+    H, I, E, k, T, seed, kind = synth.CONFIGS[name]
+    r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
+    t0 = time.time()
+    bank = synth.make_bank(r_w, H, I, E + 1, distinct)
+    log(f"{name}: quantized {min(distinct, E + 1)} distinct experts into {E + 1} slots in {time.time() - t0:.1f}s")
+    wg = synth.f32_to_bf16_bits(r_g.standard_normal(H, dtype=np.float32) * np.float32(0.02))
+    xs = synth.f32_to_bf16_bits(r_x.standard_normal((steps, T, H), dtype=np.float32))
+    logits = np.stack([synth.make_logits(r_l, T, E, kind) for _ in range(steps)])
+    return dict(H=H, I=I, E=E, k=k, T=T, bank=bank, wg=wg, xs=xs, logits=logits, replicas=replicas)
+
+
+# ---------------------------------------------------------------- GPU run
+
+def run_gpu(inp, steps: int, warmup: int):
+    import torch
+    from expert_offload_serving_amd import _lib
+    from expert_offload_serving_amd import layer as dl
+
+    H, I, E, k, T, R = inp["H"], inp["I"], inp["E"], inp["k"], inp["T"], inp["replicas"]
+    dev = torch.device("cuda:0")
+    nslot = E + 1
+    base = dl.to_device_u8(inp["bank"], dev)
+    bank = torch.empty((R * nslot, base.shape[1]), dtype=torch.uint8, device=dev)
+    for r in range(R):
+        bank[r * nslot:(r + 1) * nslot].copy_(base)
+    del base
+    wg = dl.to_device_bf16(inp["wg"], dev)
+    maps = torch.arange(E, dtype=torch.int32, device=dev)[None, :] + nslot * torch.arange(
+        R, dtype=torch.int32, device=dev)[:, None]
+    layers = [dl.DeviceLayer(H, I, E, k, bank, maps[r].contiguous(), r * nslot + E, wg) for r in range(R)]
+    structs = [l.struct() for l in layers]
+    total = steps + warmup
+    xs = dl.to_device_bf16(inp["xs"][:total].reshape(total * T, H), dev).view(total, T, H)
+    logits = torch.from_numpy(np.ascontiguousarray(inp["logits"][:total])).to(dev)
+    routes = [dl.Routing.empty(T, E, k, dev) for _ in range(total)]
+    ws = dl.workspace(T, layers[0])
+    y = torch.empty((total, T, H), dtype=torch.float32, device=dev)
+    rws = _lib.moe_route_workspace_bytes(T, E, k)
+    rws_t = torch.empty(max(1, rws), dtype=torch.uint8, device=dev)
+
+    def step(s: int, do_route: bool = True, do_forward: bool = True):
+        r = routes[s]
+        if do_route:
+            _lib.check(_lib.moe_route_topk(logits[s], T, E, k, r.ids, r.w, r.offsets, r.sorted_assign,
+                                           r.assign_pos, rws_t, rws, None))
+        if do_forward:
+            _lib.check(_lib.moe_nvfp4_forward(structs[s % R], xs[s], T, r.ids, r.w, r.offsets, r.sorted_assign,
+                                              r.assign_pos, y[s], 0, ws, ws.numel(), None))
+
+    # eager warm-up, then an eager reference of the last timed step
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    step(total - 1)
+    torch.cuda.synchronize()
+    y_eager = y[total - 1].clone()
+
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    g_step, g_fwd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g_step, stream=s):
+            for i in range(warmup, total):
+                step(i)
+        with torch.cuda.graph(g_fwd, stream=s):
+            for i in range(warmup, total):
+                step(i, do_route=False)
+    torch.cuda.synchronize()
+    # graphs replayed once untimed (first replay uploads the graph)
+    g_step.replay()
+    g_fwd.replay()
+    torch.cuda.synchronize()
+
+    # timed region: whole steps (route + forward)
+    cur = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g_step.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    replay_ok = torch.equal(y[total - 1], y_eager)
+
+    # forward kernels only, HIP events on the stream they run on
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(cur)
+    g_fwd.replay()
+    ev1.record(cur)
+    torch.cuda.synchronize()
+    fwd_ms = ev0.elapsed_time(ev1) / steps
+    # route kernel only
+    g_route = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g_route, stream=s):
+            for i in range(warmup, total):
+                step(i, do_forward=False)
+    g_route.replay()
+    torch.cuda.synchronize()
+    ev0.record(cur)
+    g_route.replay()
+    ev1.record(cur)
+    torch.cuda.synchronize()
+    route_ms = ev0.elapsed_time(ev1) / steps
+
+    distinct = []
+    for i in range(warmup, total):
+        off = routes[i].offsets.cpu().numpy()
+        distinct.append(int(np.count_nonzero(np.diff(off))))
+    counts = np.diff(routes[total - 1].offsets.cpu().numpy())
+    return dict(wall=wall, fwd_ms=fwd_ms, route_ms=route_ms, distinct=distinct, replay_ok=replay_ok,
+                y_last=y[total - 1].cpu().numpy(), ids_last=routes[total - 1].ids.cpu().numpy(),
+                counts_max=int(counts.max()), counts_min=int(counts.min()))
+
+
+# ---------------------------------------------------------------- CPU baseline (the oracle)
+
+def cpu_baseline(inp, n_tokens: int, unit: str):
+    import oracle
+    from expert_offload_serving_amd import synth
+    H, I, E, k, T = inp["H"], inp["I"], inp["E"], inp["k"], inp["T"]
+    x = inp["xs"].reshape(-1, H)[:n_tokens]
+    logits = inp["logits"].reshape(-1, E)[:n_tokens]
+    ids, w = oracle.route(logits, k)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    threads = min(threads, n_tokens)
+    t0 = time.perf_counter()
+    oracle.forward(H, I, E, k, inp["bank"], np.arange(E, dtype=np.int32), E, inp["wg"], x, ids, w,
+                   nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 3), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{n_tokens} tokens of the same workload (routing, all expert FFNs, shared expert, combine) "
+                      f"through oracle_forward, fp64 accumulation, {dt:.1f} s"}
+
+
+def parity_sample(inp, res, tokens):
+    """Relative L2 error of the last timed step's output against the oracle (a few tokens)."""
+    import oracle
+    H, I, E, k, T = inp["H"], inp["I"], inp["E"], inp["k"], inp["T"]
+    s = len(inp["xs"]) - 1 if False else None
+    last = res["last_index"]
+    x = inp["xs"][last]
+    lg = inp["logits"][last]
+    ids, w = oracle.route(lg, k)
+    if not np.array_equal(ids, res["ids_last"]):
+        return {"ids_bitexact": False}
+    toks = np.arange(min(tokens, T), dtype=np.int32)
+    ref = oracle.forward(H, I, E, k, inp["bank"], np.arange(E, dtype=np.int32), E, inp["wg"], x, ids, w,
+                         tokens=toks)
+    got = res["y_last"][toks].astype(np.float64)
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    return {"ids_bitexact": True, "rel_l2": rel, "tokens_checked": int(toks.size)}
+
+
+# ---------------------------------------------------------------- main
+
+def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: int, want_cpu: bool, cpu_tokens: int):
+    from expert_offload_serving_amd import synth
+    inp = build_inputs(name, steps + warmup, replicas, distinct)
+    H, I, E, k, T = inp["H"], inp["I"], inp["E"], inp["k"], inp["T"]
+    log(f"{name}: running {warmup} warmup + {steps} timed steps, {replicas} bank copies")
+    res = run_gpu(inp, steps, warmup)
+    res["last_index"] = steps + warmup - 1
+    sb = synth.slot_nbytes(H, I)
+    ms_step = res["wall"] * 1e3 / steps
+    tokens_s = T * steps / res["wall"]
+    mean_d = float(np.mean(res["distinct"]))
+    bytes_fwd = (mean_d + 1) * sb                       # touched expert slots incl. the shared expert
+    fwd_s = res["fwd_ms"] * 1e-3
+    gbs = bytes_fwd / fwd_s / 1e9
+    prefill = T > 16
+    flops = synth.prefill_flops(T, H, I, k)
+    if prefill:
+        tf = flops / fwd_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "moe_nvfp4_forward prefill (gateup_mfma + down_mfma + combine)",
+                "per_launch": f"{flops / 1e9:.2f} GFLOP per forward (2*3*I*H*(T*k+T))"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "moe_nvfp4_forward decode (decode_gateup_kernel + decode_down_kernel)",
+                "per_launch": f"{bytes_fwd / 1e6:.2f} MB expert weights per forward ((D+1) x {sb} B, "
+                              f"mean D = {mean_d:.2f})"}
+    out = {
+        "metric": METRIC, "value": round(tokens_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if prefill else "f32", "data": "synthetic",
+        "config": {"workload": name, "H": H, "I": I, "E": E, "k": k, "T": T, "shared_expert": True,
+                   "bank_copies": replicas, "distinct_quantized_experts": min(distinct, E + 1),
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"route_us": round(res["route_ms"] * 1e3, 2), "forward_us": round(res["fwd_ms"] * 1e3, 2),
+                  "step_us": round(ms_step * 1e3, 2), "expert_weight_GBps_forward": round(gbs, 1),
+                  "expert_weight_GBps_step": round(bytes_fwd / (ms_step * 1e-3) / 1e9, 1),
+                  "graph_replay_matches_eager": bool(res["replay_ok"])},
+    }
+    if prefill:
+        out["layer"]["forward_TFLOPs"] = round(flops / fwd_s / 1e12, 2)
+        out["layer"]["expert_count_range"] = [res["counts_min"], res["counts_max"]]
+    try:
+        out["parity"] = parity_sample(inp, res, 4)
+    except Exception as e:  # the parity sample is a report, not the measurement
+        out["parity"] = {"error": str(e)}
+    if want_cpu:
+        log(f"{name}: timing the oracle on {cpu_tokens} tokens")
+        out["cpu_baseline"] = cpu_baseline(inp, cpu_tokens, "tokens/s")
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode_bs1",
+                    choices=["decode_bs1", "decode_bs16", "prefill_2048", "all"])
+    ap.add_argument("--replicas", type=int, default=8, help="copies of the expert bank rotated over steps")
+    ap.add_argument("--distinct", type=int, default=32, help="distinct quantized experts tiled over the slots")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=48)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the layer runs on a single MI355X here (--gpus {args.gpus}, "
+              f"WORLD_SIZE {world} requested); see the design notes for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from expert_offload_serving_amd import _lib
+    _lib.lib()
+    names = ["decode_bs1", "decode_bs16", "prefill_2048"] if args.config == "all" else [args.config]
+    for name in names:
+        steps, warmup = args.steps, args.warmup
+        if name == "prefill_2048":
+            steps, warmup = max(1, min(steps, 20)), max(1, min(warmup, 3))
+        reps = args.replicas if name != "prefill_2048" else min(args.replicas, 4)
+        out = bench_config(name, steps, warmup, reps, args.distinct, not args.no_cpu_baseline, args.cpu_tokens)
+        print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

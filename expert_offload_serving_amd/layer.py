@@ -1,0 +1,119 @@
+"""Device-side convenience wrappers over the C ABI (allocation of outputs and
+workspaces with torch, struct packing, error checks).  No computation happens
+here: every step runs in libmoe_nvfp4.so's kernels.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import check
+
+
+def to_device_u8(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(device)
+
+
+def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """bf16 bit patterns (uint16) -> a torch.bfloat16 device tensor with the same bits."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+@dataclasses.dataclass
+class DeviceLayer:
+    """One layer's expert storage in HBM: a bank of equally sized slots, the
+    expert -> slot map, the shared expert's slot (index into the bank, -1 for
+    none) and the shared gate vector (bf16 [H])."""
+    H: int
+    I: int
+    E: int
+    k: int
+    bank: torch.Tensor            # u8 [num_slots, slot_bytes]
+    slot_of_expert: torch.Tensor  # i32 [E]
+    shared_slot: int
+    wg: torch.Tensor              # bf16 [H]
+
+    def __post_init__(self):
+        sb = _lib.moe_nvfp4_slot_bytes(self.H, self.I)
+        if sb == 0 or self.bank.dim() != 2 or self.bank.shape[1] != sb:
+            raise ValueError(f"bank must be [slots, {sb}] bytes for H={self.H}, I={self.I}")
+
+    @property
+    def slot_bytes(self) -> int:
+        return self.bank.shape[1]
+
+    def struct(self, slot_of_expert: torch.Tensor | None = None, shared: bool = True) -> _lib.LayerStruct:
+        s = _lib.LayerStruct()
+        s.H, s.I, s.E, s.k = self.H, self.I, self.E, self.k
+        s.bank_base = self.bank.data_ptr()
+        s.slot_bytes = self.slot_bytes
+        s.num_slots = self.bank.shape[0]
+        s.slot_of_expert = (self.slot_of_expert if slot_of_expert is None else slot_of_expert).data_ptr()
+        if shared and self.shared_slot >= 0:
+            s.shared_slot = self.bank[self.shared_slot].data_ptr()
+            s.shared_gate_w = self.wg.data_ptr()
+        else:
+            s.shared_slot = None
+            s.shared_gate_w = None
+        return s
+
+
+@dataclasses.dataclass
+class Routing:
+    ids: torch.Tensor            # i32 [T, k]
+    w: torch.Tensor              # f32 [T, k]
+    offsets: torch.Tensor        # i32 [E+1]
+    sorted_assign: torch.Tensor  # i32 [T*k]
+    assign_pos: torch.Tensor     # i32 [T*k]
+
+    @staticmethod
+    def empty(T: int, E: int, k: int, device="cuda") -> "Routing":
+        i32 = dict(dtype=torch.int32, device=device)
+        return Routing(torch.empty((T, k), **i32), torch.empty((T, k), dtype=torch.float32, device=device),
+                       torch.empty(E + 1, **i32), torch.empty(T * k, **i32), torch.empty(T * k, **i32))
+
+
+def route(logits: torch.Tensor, k: int, out: Routing | None = None, stream=None) -> Routing:
+    T, E = logits.shape
+    r = Routing.empty(T, E, k, logits.device) if out is None else out
+    nb = _lib.moe_route_workspace_bytes(T, E, k)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=logits.device) if nb else None
+    check(_lib.moe_route_topk(logits, T, E, k, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, ws, nb, stream))
+    return r
+
+
+def workspace(T: int, layer: DeviceLayer) -> torch.Tensor:
+    nb = _lib.moe_nvfp4_forward_workspace_bytes(T, layer.H, layer.I, layer.E, layer.k)
+    return torch.empty(nb, dtype=torch.uint8, device=layer.bank.device)
+
+
+def forward(layer: DeviceLayer, x: torch.Tensor, r: Routing, y: torch.Tensor | None = None, accumulate: bool = False,
+            ws: torch.Tensor | None = None, slot_of_expert: torch.Tensor | None = None, shared: bool = True,
+            stream=None) -> torch.Tensor:
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, layer.H), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(T, layer)
+    st = layer.struct(slot_of_expert, shared)
+    check(_lib.moe_nvfp4_forward(st, x, T, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y, int(accumulate),
+                                 ws, ws.numel(), stream))
+    return y
+
+
+def dequant(codes: torch.Tensor, scales: torch.Tensor, globals_: torch.Tensor, stream=None) -> torch.Tensor:
+    rows, half = codes.shape
+    out = torch.empty((rows, 2 * half), dtype=torch.float32, device=codes.device)
+    check(_lib.moe_nvfp4_dequant(codes, scales, globals_, rows, 2 * half, out, stream))
+    return out
+
+
+def slice_bank(bank: torch.Tensor, H: int, I: int, r: int, n: int, stream=None) -> torch.Tensor:
+    sb = _lib.moe_nvfp4_slot_bytes(H, I // n)
+    out = torch.empty((bank.shape[0], sb), dtype=torch.uint8, device=bank.device)
+    check(_lib.moe_nvfp4_slice_bank(bank, bank.shape[0], H, I, r, n, out, stream))
+    return out

@@ -1,0 +1,178 @@
+/*
+ * moe_nvfp4.h - C ABI of the MI355X (gfx950) NVFP4 routed-MoE layer library.
+ *
+ * What the library computes comes from the FreeToken pages on offloaded MoE
+ * serving: PR #385 ("What this adds": NVFP4 expert banks of packed 4-bit
+ * codes, 16-wide FP8 scale blocks and per-row fp32 globals, sliced along the
+ * intermediate axis; one combine routed + sigmoid(gate) * shared) and issue
+ * #62 ("What it touches": gate_up is [2I, H] with gate rows [0, I) and up
+ * rows [I, 2I), down is [H, I]; "The fix that fits": an I-slice turns the
+ * down projection into partial sums; "Why TP=2 loses today": experts live in
+ * a GPU slot cache filled from host banks over PCIe on misses).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless marked "host".  The caller owns all
+ *    memory; the library allocates and frees nothing on the GPU.
+ *  - Calls validate their arguments synchronously, before anything is
+ *    enqueued; a failed call enqueues nothing and returns a nonzero status.
+ *    moe_last_error() then returns a message for the calling thread.
+ *  - Work is enqueued on the given stream and the call returns; device faults
+ *    surface at the caller's next synchronisation.  moe_route_topk and
+ *    moe_nvfp4_forward make no host synchronisation and no allocation.
+ *  - Shapes: H % 32 == 0, I % 32 == 0 (the fp4 scale-block guard of issue #62
+ *    "What it touches"), 1 <= k <= E <= 1024, T >= 0 (T == 0 is a no-op).
+ *  - bf16 values are passed as their uint16 bit patterns.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,
+    MOE_ERR_UNSUPPORTED_SHAPE = 2,
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_NOT_PINNED = 4,
+    MOE_ERR_HIP = 5,
+};
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------ slots
+ * One expert slot holds, in this order and without padding:
+ *   gate_up codes   u8  [2I, H/2]   element 2j of a row in the low nibble of byte j
+ *   gate_up scales  u8  [2I, H/16]  E4M3FN (OCP), one per 16 consecutive elements of a row
+ *   gate_up globals f32 [2I]        one per row
+ *   down codes      u8  [H, I/2]
+ *   down scales     u8  [H, I/16]
+ *   down globals    f32 [H]
+ * The weight is W[r,c] = e2m1(code) * e4m3(scale[r, c/16]) * global[r]
+ * (PR #385 "What this adds": packed codes, 16-wide scale blocks, per-row
+ * globals).  Returns the slot size in bytes, or 0 if H or I is not a
+ * positive multiple of 32. */
+size_t moe_nvfp4_slot_bytes(int H, int I);
+
+/* ------------------------------------------------------------------ routing
+ * Top-k expert selection with renormalised weights (issue #62, R9700 interim
+ * report: norm_topk_prob renormalises the selected weights; the router is
+ * replicated) and the permutation of the T*k assignments by expert.
+ *   logits          f32 [T, E] router logits (NaN is a precondition violation)
+ *   topk_ids        i32 [T, k] out: experts by (logit descending, index ascending)
+ *   topk_w          f32 [T, k] out: softmax over the k selected logits
+ *   expert_offsets  i32 [E+1]  out: exclusive scan of per-expert counts
+ *   sorted_assign   i32 [T*k]  out: flat indices t*k+j ordered by (expert, t, j)
+ *   assign_pos      i32 [T*k]  out: inverse of sorted_assign
+ *   ws, ws_bytes    device scratch of at least moe_route_workspace_bytes(T, E, k)
+ * The result is deterministic (no atomics decide any order). */
+size_t moe_route_workspace_bytes(int T, int E, int k);
+int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                   int32_t* expert_offsets, int32_t* sorted_assign, int32_t* assign_pos, void* ws, size_t ws_bytes,
+                   hipStream_t stream);
+
+/* ------------------------------------------------------------------ layer
+ * A layer's expert storage: E routed experts addressed through a slot map
+ * into a bank of equally sized slots, plus an optional shared expert.
+ *   bank_base       device base of the slot array (256-byte aligned)
+ *   slot_bytes      must equal moe_nvfp4_slot_bytes(H, I)
+ *   slot_of_expert  device i32 [E]: slot index of each expert, or -1 to leave it
+ *                   out of this call (its assignments then contribute nothing)
+ *   num_slots       number of slots at bank_base (slot indices must be below it)
+ *   shared_slot     device pointer to the shared expert's slot (same layout,
+ *                   same H and I), or NULL for no shared expert
+ *   shared_gate_w   device bf16 [H]: the shared expert's scalar gate
+ *                   s_t = sigmoid(x_t . w); ignored when shared_slot is NULL
+ * The struct is read during the call only (host pointer, not retained). */
+typedef struct {
+    int H, I, E, k;
+    const void* bank_base;
+    size_t slot_bytes;
+    int num_slots;
+    const int32_t* slot_of_expert;
+    const void* shared_slot;
+    const uint16_t* shared_gate_w;
+} moe_nvfp4_layer_t;
+
+/* Workspace the forward needs for T tokens; 0 on bad shapes. */
+size_t moe_nvfp4_forward_workspace_bytes(int T, int H, int I, int E, int k);
+
+/* The routed-MoE layer (PR #385 "What this adds": routed + sigmoid(gate) *
+ * shared; issue #62 "What it touches": gate/up rows, down columns):
+ *   y_t (=|+=) sum_j w_tj * FFN_{e_tj}(x_t) + s_t * FFN_shared(x_t)
+ *   FFN(x) = W_dn (silu(W_gate x) * (W_up x)),  s_t = sigmoid(x_t . w_g)
+ *   x        bf16 [T, H] activations
+ *   routing  the outputs of moe_route_topk for the same T, E, k
+ *   y        f32 [T, H]; accumulate = 0 writes y, 1 adds into y
+ * T <= 16 runs the decode path (NVFP4 GEMV with wavefront reductions, fp32
+ * hidden state); larger T runs the prefill path (grouped bf16 MFMA GEMM over
+ * the permuted tokens with the weights dequantised in LDS, bf16 hidden
+ * state).  Expert slots referenced by slot_of_expert must lie inside the
+ * bank; the kernels do not range-check them.  Output order of summation is
+ * fixed, so repeated calls give bit-identical results. */
+int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
+                      const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
+                      const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* ------------------------------------------------------------------ expert cache
+ * Copy n expert slots from pinned host banks into GPU cache slots
+ * (issue #62 "Why TP=2 loses today" and PR #385 "What this adds": the GPU
+ * holds a fraction of the experts and streams misses over PCIe each step).
+ *   cache_base   device base of num_slots slots of slot_bytes each
+ *   dst_slots    host i32 [n]: destination slot of each copy (0 <= slot < num_slots)
+ *   src          host array of n host pointers, each to slot_bytes of page-locked
+ *                (hipHostMalloc / pinned) memory; non-pinned sources are refused
+ *   copy_stream  stream the copies are enqueued on (one hipMemcpyAsync each)
+ *   done         event recorded on copy_stream after the last copy, or NULL
+ * Returns after enqueueing; the caller orders compute after `done`. */
+int expert_cache_fill(void* cache_base, size_t slot_bytes, int num_slots, const int32_t* dst_slots,
+                      const void* const* src, int n, hipStream_t copy_stream, hipEvent_t done);
+
+/* Host-side slot manager for the expert cache: one pool of num_slots GPU
+ * slots shared by every (layer, expert), least-recently-used replacement.
+ * For one layer-step, moe_cache_plan takes the routed ids (host, any order,
+ * repeats allowed), marks cached experts as most recent (ascending expert
+ * order), assigns each missing expert, in ascending order, the lowest
+ * never-used slot or else the least recently used entry's slot, and reports:
+ *   slot_of_expert  host i32 [E]: slot of every routed expert, -1 otherwise
+ *   miss_experts    host i32 [n]: missing experts in ascending order (first *n_miss)
+ *   miss_slots      host i32 [n]: the slot each miss must be filled into
+ * Returns MOE_ERR_INVALID_ARGUMENT if one layer-step needs more distinct
+ * experts than the pool holds.  Not thread-safe per handle. */
+typedef struct moe_expert_cache moe_expert_cache_t;
+moe_expert_cache_t* moe_cache_create(int num_layers, int num_experts, int num_slots);
+void moe_cache_destroy(moe_expert_cache_t* cache);
+int moe_cache_plan(moe_expert_cache_t* cache, int layer, const int32_t* ids, int n, int32_t* slot_of_expert,
+                   int32_t* miss_experts, int32_t* miss_slots, int* n_miss, int* n_hit);
+
+/* ------------------------------------------------------------------ bank slicing
+ * Intermediate-axis slice r of n of every slot in a bank (issue #62 "What it
+ * touches": gate_up gives two disjoint row ranges, down a column slice; PR
+ * #385: codes, scale blocks and per-row globals sliced to match):
+ * dst slot j (shape H, I/n) gets gate rows [r*Il, (r+1)*Il) and up rows
+ * [I + r*Il, I + (r+1)*Il) of src slot j, with their scales and globals, and
+ * down columns [r*Il, (r+1)*Il) of all H rows, with all H globals.
+ * Requires Il = I/n to be a multiple of 32. */
+int moe_nvfp4_slice_bank(const void* src_bank, int num_slots, int H, int I, int r, int n, void* dst_bank,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------ test hook
+ * Dequantise an NVFP4 matrix [rows, K] to fp32 with the same decode the
+ * forward kernels use: out[r,c] = f32(f32(e2m1 * e4m3) * globals[r]).
+ * K % 32 == 0. */
+int moe_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* globals, int rows, int K,
+                      float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_NVFP4_H */

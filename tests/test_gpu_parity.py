@@ -1,0 +1,361 @@
+"""GPU parity of the HIP library against the CPU oracle (marker: gpu).
+
+Integer work (top-k ids, the permutation, dequantised bits, sliced bytes)
+must match bit for bit; layer outputs must be within relative L2 2e-3 and
+max |err| <= 1e-2 * max |ref|.  Inputs are the seeded synthetic workloads of
+expert_offload_serving_amd.synth.
+"""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_offload_serving_amd import _lib
+from expert_offload_serving_amd import layer as dl
+from expert_offload_serving_amd import synth
+from tests.gpu_common import assert_close, device_layer, device_logits, device_x, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    _lib.lib()  # loud failure if the library is missing on a GPU machine
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------- dequant
+
+def test_dequant_bitexact_all_code_scale_pairs():
+    """Every (code, scale byte) pair under several globals, against oracle_dequant bit for bit."""
+    _announce("dequant 16 codes x 256 scales x 5 globals")
+    K = 256
+    codes_row = np.array([((2 * j) % 16) | (((2 * j + 1) % 16) << 4) for j in range(K // 2)], dtype=np.uint8)
+    gl = [1.0, 0.5, 3.7e-5, -2.25, 1.0e30]
+    rows = 256 * len(gl)
+    codes = np.tile(codes_row, (rows, 1))
+    scales = np.repeat(np.tile(np.arange(256, dtype=np.uint8), len(gl))[:, None], K // 16, axis=1)
+    globals_ = np.repeat(np.array(gl, dtype=np.float32), 256)
+    want = oracle.dequant(codes, scales, globals_)
+    got = dl.dequant(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                     torch.from_numpy(globals_).cuda()).cpu().numpy()
+    nan_w, nan_g = np.isnan(want), np.isnan(got)
+    assert np.array_equal(nan_w, nan_g)
+    assert np.array_equal(want[~nan_w].view(np.uint32), got[~nan_g].view(np.uint32))
+
+
+def test_dequant_bitexact_real_bank():
+    _announce("dequant real expert slot (H=2560, I=640)")
+    H, I = 2560, 640
+    slot = synth.random_expert_slot(np.random.default_rng(7), H, I)
+    reg = synth.slot_regions(H, I)
+    def part(i, shape, dt=np.uint8):
+        off, size = reg[i]
+        return np.ascontiguousarray(slot[off:off + size].view(dt).reshape(shape))
+    for (ci, si, gi, rows, K) in [(0, 1, 2, 2 * I, H), (3, 4, 5, H, I)]:
+        c, s, g = part(ci, (rows, K // 2)), part(si, (rows, K // 16)), part(gi, (rows,), np.float32)
+        want = oracle.dequant(c, s, g)
+        got = dl.dequant(torch.from_numpy(c).cuda(), torch.from_numpy(s).cuda(), torch.from_numpy(g).cuda())
+        assert np.array_equal(want.view(np.uint32), got.cpu().numpy().view(np.uint32))
+
+
+# ---------------------------------------------------------------- routing
+
+def _route_both(logits: np.ndarray, k: int):
+    T, E = logits.shape
+    r = dl.route(torch.from_numpy(np.ascontiguousarray(logits)).cuda(), k)
+    torch.cuda.synchronize()
+    ids, w = oracle.route(logits, k)
+    off, srt, pos = oracle.permute(ids, E)
+    return r, (ids, w, off, srt, pos)
+
+
+def _check_route(logits, k, what):
+    _announce(f"route {what} T={logits.shape[0]} E={logits.shape[1]} k={k}")
+    r, (ids, w, off, srt, pos) = _route_both(logits, k)
+    assert np.array_equal(r.ids.cpu().numpy(), ids), what
+    assert np.array_equal(r.offsets.cpu().numpy(), off), what
+    assert np.array_equal(r.sorted_assign.cpu().numpy(), srt), what
+    assert np.array_equal(r.assign_pos.cpu().numpy(), pos), what
+    gw = r.w.cpu().numpy()
+    ulps = np.abs(gw.view(np.int32).astype(np.int64) - w.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1, f"{what}: weights differ by {ulps.max()} ulp"
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_bs1", "decode_bs16", "prefill_2048"])
+def test_route_bitexact_configs(name):
+    H, I, E, k, T, seed, kind = synth.CONFIGS[name]
+    rng = np.random.default_rng(seed)
+    logits = synth.make_logits(rng, T, E, kind)
+    _check_route(logits, k, name)
+
+
+def test_route_ties_zero_counts_and_extremes():
+    rng = np.random.default_rng(1)
+    # heavy ties: logits from a tiny set of values
+    logits = rng.integers(0, 3, (37, 64)).astype(np.float32)
+    logits[:, 5] = -0.0
+    logits[:, 6] = 0.0
+    _check_route(logits, 8, "ties")
+    # zero-count experts: 16 experts forced to lose (prefill case with skew)
+    lg = synth.make_logits(np.random.default_rng(2), 300, 256, "zipf")
+    lg[:, :16] = -1e30
+    _check_route(lg, 8, "zero-count experts")
+    _check_route(rng.standard_normal((5, 32)).astype(np.float32), 1, "k=1")
+    _check_route(rng.standard_normal((3, 16)).astype(np.float32), 16, "k=E")
+    _check_route(rng.standard_normal((20, 1024)).astype(np.float32), 8, "E=1024 two-kernel path")
+    _check_route(rng.standard_normal((16, 1024)).astype(np.float32), 300, "k=300 fused path")
+
+
+# ---------------------------------------------------------------- forward
+
+def _gpu_forward(L, T=None, slot_map=None, shared=True, y=None, accumulate=False):
+    dev = device_layer(L)
+    x = device_x(L)
+    r = dl.route(device_logits(L), L.k)
+    sm = None if slot_map is None else torch.from_numpy(np.ascontiguousarray(slot_map, dtype=np.int32)).cuda()
+    out = dl.forward(dev, x, r, y=y, accumulate=accumulate, slot_of_expert=sm, shared=shared)
+    torch.cuda.synchronize()
+    return out, r
+
+
+def _oracle_forward(L, tokens=None, slot_map=None, shared=True):
+    ids, w = oracle.route(L.logits, L.k)
+    sm = L.slot_of_expert if slot_map is None else slot_map
+    return oracle.forward(L.H, L.I, L.E, L.k, L.bank, sm, L.shared_slot if shared else -1, L.wg, L.x, ids, w,
+                          tokens=tokens)
+
+
+def test_forward_tiny():
+    _announce("forward tiny H=256 I=64 E=8 k=2 T=4")
+    L = synth.make_layer("tiny")
+    y, _ = _gpu_forward(L)
+    rel = assert_close(y.cpu().numpy(), _oracle_forward(L), "tiny")
+    print(f"tiny rel L2 {rel:.2e}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 16])
+def test_forward_decode_shapes(T):
+    _announce(f"forward decode H=2560 I=640 E=256 k=8 T={T}")
+    L = synth.make_layer("decode_bs16", T=T, n_distinct=12, seed=100 + T)
+    y, _ = _gpu_forward(L)
+    ref = _oracle_forward(L)
+    rel = assert_close(y.cpu().numpy(), ref, f"decode T={T}")
+    print(f"decode T={T} rel L2 {rel:.2e}")
+
+
+def test_forward_decode_bs1_config():
+    _announce("forward decode_bs1 config (seed 1)")
+    L = synth.make_layer("decode_bs1", n_distinct=16)
+    y, _ = _gpu_forward(L)
+    assert_close(y.cpu().numpy(), _oracle_forward(L), "decode_bs1")
+
+
+def test_forward_small_shapes_and_ragged():
+    """Odd sizes exercising partial row blocks and tiles: H=96 (3 chunks per row), I=32, E=5."""
+    for (H, I, E, k, T) in [(96, 32, 5, 2, 3), (96, 32, 5, 2, 17), (320, 96, 7, 3, 40), (256, 64, 8, 8, 16)]:
+        _announce(f"forward H={H} I={I} E={E} k={k} T={T}")
+        rng = np.random.default_rng(H + I + T)
+        bank = np.stack([synth.random_expert_slot(rng, H, I) for _ in range(E + 1)])
+        L = synth.LayerInputs(H, I, E, k, T, bank, np.arange(E, dtype=np.int32), E,
+                              synth.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32) * 0.02),
+                              synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)),
+                              rng.standard_normal((T, E)).astype(np.float32))
+        y, _ = _gpu_forward(L)
+        assert_close(y.cpu().numpy(), _oracle_forward(L), f"H={H} I={I} T={T}")
+
+
+def test_forward_no_shared_and_skipped_experts():
+    _announce("forward without shared expert; slot map with skipped experts")
+    L = synth.make_layer("tiny", T=6)
+    y, _ = _gpu_forward(L, shared=False)
+    assert_close(y.cpu().numpy(), _oracle_forward(L, shared=False), "no shared")
+    sm = L.slot_of_expert.copy()
+    sm[[1, 4, 6]] = -1
+    y2, _ = _gpu_forward(L, slot_map=sm)
+    assert_close(y2.cpu().numpy(), _oracle_forward(L, slot_map=sm), "skipped experts")
+    # every expert skipped and no shared expert: y = 0, or y unchanged with accumulate
+    none = np.full(L.E, -1, dtype=np.int32)
+    y3, _ = _gpu_forward(L, slot_map=none, shared=False)
+    assert np.all(y3.cpu().numpy() == 0)
+    base = torch.full((L.T, L.H), 1.5, dtype=torch.float32, device="cuda")
+    y4, _ = _gpu_forward(L, slot_map=none, shared=False, y=base, accumulate=True)
+    assert np.all(y4.cpu().numpy() == 1.5)
+
+
+def test_forward_accumulate_split_equals_whole():
+    """Offload pattern: hits-only call, then misses-only call with accumulate, equals the single call."""
+    for name, T in [("decode_bs16", 16), ("prefill_2048", 64)]:
+        _announce(f"split hits/misses {name} T={T}")
+        L = synth.make_layer(name, T=T, n_distinct=8)
+        whole, _ = _gpu_forward(L)
+        rng = np.random.default_rng(3)
+        miss = rng.random(L.E) < 0.4
+        hits_map = np.where(miss, -1, L.slot_of_expert).astype(np.int32)
+        miss_map = np.where(miss, L.slot_of_expert, -1).astype(np.int32)
+        y, _ = _gpu_forward(L, slot_map=hits_map)
+        y2, _ = _gpu_forward(L, slot_map=miss_map, shared=False, y=y, accumulate=True)
+        w = whole.cpu().numpy()
+        assert_close(y2.cpu().numpy(), w, f"split {name}")
+        assert_close(y2.cpu().numpy(), _oracle_forward(L), f"split vs oracle {name}")
+
+
+def test_forward_run_to_run_bitidentical():
+    for name, T in [("decode_bs16", 16), ("decode_bs1", 1), ("prefill_2048", 200)]:
+        _announce(f"bit-identical reruns {name} T={T}")
+        L = synth.make_layer(name, T=T, n_distinct=8)
+        dev = device_layer(L)
+        x = device_x(L)
+        r = dl.route(device_logits(L), L.k)
+        ws = dl.workspace(T, dev)
+        outs = [dl.forward(dev, x, r, ws=ws).cpu().numpy() for _ in range(3)]
+        assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
+
+
+# ---------------------------------------------------------------- prefill
+
+def test_forward_prefill_small_vs_oracle():
+    _announce("prefill T=300 H=2560 I=640 E=256 k=8, all tokens")
+    L = synth.make_layer("prefill_2048", T=300, n_distinct=8)
+    y, _ = _gpu_forward(L)
+    rel = assert_close(y.cpu().numpy(), _oracle_forward(L), "prefill T=300")
+    print(f"prefill T=300 rel L2 {rel:.2e}")
+
+
+def test_forward_prefill_2048_sampled():
+    """The 2048-token config in the launch configuration the benchmark times; 48 sampled tokens vs the oracle."""
+    _announce("prefill 2048 sampled tokens")
+    L = synth.make_layer("prefill_2048", n_distinct=16)
+    y, r = _gpu_forward(L)
+    counts = np.diff(r.offsets.cpu().numpy())
+    print(f"per-expert counts: min {counts.min()} median {int(np.median(counts))} max {counts.max()}")
+    toks = np.random.default_rng(0).choice(L.T, 48, replace=False).astype(np.int32)
+    ref = _oracle_forward(L, tokens=toks)
+    assert_close(y.cpu().numpy()[toks], ref, "prefill 2048 sampled")
+
+
+def test_forward_prefill_zero_count_experts():
+    _announce("prefill with 16 zero-count experts")
+    L = synth.make_layer("prefill_2048", T=160, n_distinct=8)
+    L.logits[:, :16] = -1e30
+    y, r = _gpu_forward(L)
+    assert np.all(np.diff(r.offsets.cpu().numpy())[:16] == 0)
+    assert_close(y.cpu().numpy(), _oracle_forward(L), "prefill zero-count")
+
+
+# ---------------------------------------------------------------- I-slice
+
+@pytest.mark.parametrize("T", [16, 64])
+def test_slice_partials_sum_to_full(T):
+    """Intermediate-axis slices I_local = 320 run one after the other on one GPU; their sum equals the full-I result."""
+    _announce(f"I-slice check T={T}")
+    L = synth.make_layer("decode_bs16", T=T, n_distinct=6)
+    dev = device_layer(L)
+    x = device_x(L)
+    r = dl.route(device_logits(L), L.k)
+    full = dl.forward(dev, x, r)
+    acc = torch.zeros_like(full)
+    for rr in range(2):
+        sb = dl.slice_bank(dev.bank, L.H, L.I, rr, 2)
+        want_bytes = np.stack([oracle.slice_slot(s, L.H, L.I, rr, 2) for s in L.bank])
+        assert np.array_equal(sb.cpu().numpy(), want_bytes), "sliced bytes differ from the oracle's slicer"
+        part = dl.DeviceLayer(L.H, L.I // 2, L.E, L.k, sb, dev.slot_of_expert, L.shared_slot, dev.wg)
+        dl.forward(part, x, r, y=acc, accumulate=rr > 0)
+    torch.cuda.synchronize()
+    assert_close(acc.cpu().numpy(), full.cpu().numpy(), "slice sum vs full (GPU)")
+    assert_close(acc.cpu().numpy(), _oracle_forward(L), "slice sum vs oracle")
+
+
+# ---------------------------------------------------------------- expert cache
+
+def test_cache_fill_bytes_and_pinned_check():
+    _announce("expert_cache_fill")
+    H, I = 256, 64
+    sb = synth.slot_nbytes(H, I)
+    rng = np.random.default_rng(4)
+    host = torch.from_numpy(rng.integers(0, 256, (6, sb), dtype=np.uint8)).pin_memory()
+    cache = torch.zeros((4, sb), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+    srcs = [host[i].data_ptr() for i in (5, 0, 3)]
+    _lib.check(_lib.expert_cache_fill(cache, sb, 4, [2, 0, 3], srcs, side, done))
+    torch.cuda.current_stream().wait_event(done)
+    torch.cuda.synchronize()
+    got = cache.cpu().numpy()
+    assert np.array_equal(got[2], host[5].numpy()) and np.array_equal(got[0], host[0].numpy())
+    assert np.array_equal(got[3], host[3].numpy()) and np.all(got[1] == 0)
+    unpinned = np.zeros(sb, dtype=np.uint8)
+    rc = _lib.expert_cache_fill(cache, sb, 4, [1], [unpinned.ctypes.data], side, None)
+    assert rc == _lib.MOE_ERR_NOT_PINNED
+    rc = _lib.expert_cache_fill(cache, sb, 4, [4], srcs[:1], side, None)
+    assert rc == _lib.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_offload_layer_steps_match_resident():
+    """A few offloaded layer-steps (cache smaller than the experts, host LRU, fills on a side stream,
+    hits then misses) give the resident result; hit/miss counts match the oracle's LRU model."""
+    _announce("offload steps vs resident")
+    H, I, E, k, T, L_layers, steps, C = 256, 64, 16, 2, 3, 3, 5, 10
+    rng = np.random.default_rng(48)
+    sb = synth.slot_nbytes(H, I)
+    base = np.stack([synth.random_expert_slot(rng, H, I) for _ in range(E + 1)])
+    host = torch.empty((L_layers, E, sb), dtype=torch.uint8).pin_memory()
+    for l in range(L_layers):
+        for e in range(E):
+            host[l, e] = torch.from_numpy(base[(e + 5 * l) % E])
+    wg = synth.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32) * 0.02)
+    cache = torch.zeros((C, sb), dtype=torch.uint8, device="cuda")
+    shared = dl.to_device_u8(base[E][None, :])
+    mgr = _lib.ExpertCache(L_layers, E, C)
+    side = torch.cuda.Stream()
+    all_ids = []
+    for st in range(steps):
+        for l in range(L_layers):
+            x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+            logits = rng.standard_normal((T, E)).astype(np.float32)
+            r = dl.route(torch.from_numpy(logits).cuda(), k)
+            ids = r.ids.cpu().numpy()
+            all_ids.append(ids.reshape(-1).copy())
+            som, miss_e, miss_s, n_hit = mgr.plan(l, ids.reshape(-1))
+            som = np.array(som, dtype=np.int32)
+            hits_map = som.copy()
+            hits_map[miss_e] = -1
+            miss_map = np.full(E, -1, dtype=np.int32)
+            miss_map[miss_e] = som[miss_e]
+            done = torch.cuda.Event()
+            _lib.check(_lib.expert_cache_fill(cache, sb, C, miss_s, [host[l, e].data_ptr() for e in miss_e], side,
+                                              done))
+            dev = dl.DeviceLayer(H, I, E, k, cache, torch.from_numpy(som).cuda(), -1, dl.to_device_bf16(wg))
+            xd = dl.to_device_bf16(x)
+            # hits first (the copies may still be in flight), then wait and add the misses
+            sh_layer = dl.DeviceLayer(H, I, E, k, cache, torch.from_numpy(hits_map).cuda(), -1, dev.wg)
+            st_h = sh_layer.struct()
+            st_h.shared_slot = shared.data_ptr()
+            st_h.shared_gate_w = dev.wg.data_ptr()
+            y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+            ws = dl.workspace(T, dev)
+            _lib.check(_lib.moe_nvfp4_forward(st_h, xd, T, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y,
+                                              0, ws, ws.numel()))
+            torch.cuda.current_stream().wait_event(done)
+            hm = torch.from_numpy(miss_map).cuda()
+            dl.forward(dev, xd, r, y=y, accumulate=True, ws=ws, slot_of_expert=hm, shared=False)
+            torch.cuda.synchronize()
+            # resident reference from the host bank of this layer
+            bank = np.concatenate([host[l].numpy(), base[E][None, :]])
+            ids_o, w_o = oracle.route(logits, k)
+            ref = oracle.forward(H, I, E, k, bank, np.arange(E, dtype=np.int32), E, wg, x, ids_o, w_o)
+            assert_close(y.cpu().numpy(), ref, f"offload step {st} layer {l}")
+    hits, misses, _, _ = oracle.lru_run(np.array(all_ids, dtype=np.int32).reshape(steps, L_layers, -1), E, C)
+    mgr2 = _lib.ExpertCache(L_layers, E, C)
+    ids_arr = np.array(all_ids).reshape(steps, L_layers, -1)
+    for st in range(steps):
+        for l in range(L_layers):
+            _, me, _, nh = mgr2.plan(l, ids_arr[st, l])
+            assert nh == hits[st, l] and len(me) == misses[st, l]
