@@ -30,8 +30,31 @@ struct SlotGeom {
 };
 SlotGeom slot_geom(int H, int I);
 
-// Forward workspace (forward.cpp)
-size_t forward_ws_bytes(int T, int H, int I, int E, int k);
+// Forward workspace: byte offsets of its regions (each 256-byte aligned).
+//   h      hidden state, (T*k + T) rows of I values (f32 on the decode path, f16 on prefill)
+//   o      per-assignment expert outputs, (T*k + T) rows of H f32
+//   s      shared-gate sigmoid per token, T f32
+//   x16    prefill: scaled fp16 activations [T, H]; xinv: their inverse scales [T]
+//   tiles  prefill work lists: 4 counts, then 3 classes x tile_cap (group, m0) pairs
+struct WsLayout {
+    size_t h, o, s, x16, xinv, tiles, total;
+    int tile_cap;
+};
+inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
+    const size_t rows = (size_t)T * k + T;
+    WsLayout L;
+    L.h = 0;
+    L.o = L.h + align256(rows * I * 4);
+    L.s = L.o + align256(rows * H * 4);
+    L.x16 = L.s + align256((size_t)T * 4);
+    L.xinv = L.x16 + align256((size_t)T * H * 2);
+    L.tiles = L.xinv + align256((size_t)T * 4);
+    L.tile_cap = (int)((rows + 31) / 32 + E + 1);
+    L.total = L.tiles + align256((4 + 3 * 2 * (size_t)L.tile_cap) * 4);
+    return L;
+}
+inline size_t forward_ws_bytes(int T, int H, int I, int E, int k) { return ws_layout(T, H, I, E, k).total; }
 
 // Decode path, T <= 16 (decode.hip)
 constexpr int kDecodeMaxT = 16;

@@ -3,29 +3,44 @@
 // With thousands of tokens each expert sees a dense block of rows, so the
 // expert FFN becomes a grouped GEMM over the permuted tokens (the
 // permutation groups the T*k assignments by expert; the shared expert is one
-// more group holding every token).  NVFP4 is not an MFMA input format with
-// E4M3 16-blocks, but e2m1 * e4m3 has at most 6 significant bits, so each
-// weight tile is dequantised exactly to bf16 in LDS and fed to
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the per-row global
-// multiplies the accumulator in the epilogue.
+// more group holding every token).  The contraction runs on
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation:
+//  - weights: e2m1 * e4m3 has at most 6 significant bits and lies in
+//    [2^-10, 2688], so every dequantised weight is exact in fp16.  Each wave
+//    dequantises its own B fragments from the packed codes in registers
+//    (v_cvt_scalef32_pk_f16_fp4 with unit scale, then v_pk_mul_f16 by the
+//    block scale), so weights never pass through LDS; the per-row global
+//    multiplies the accumulator in the epilogue.
+//  - activations: each token row is multiplied by a power of two that puts
+//    its largest magnitude in [2^14, 2^15), which makes the bf16 -> fp16
+//    conversion exact in the fp16 normal range (values more than 28 binades
+//    below the row maximum round to fp16 subnormals); the epilogue undoes
+//    the scale exactly.
+//  - hidden state: silu(gate) * up is stored in fp16 (11-bit significand,
+//    saturated at the fp16 maximum) as the A operand of the down GEMM.
+// K is consumed in steps of 128: quarter q of the wave holds k in
+// [32q, 32q + 32) of the step, so each lane loads 16 contiguous code bytes and
+// MFMA j uses elements [8j, 8j + 8) of that slice; the activation tile in LDS
+// is read with the same permutation.
 //
-//   plan:     list the (group, 128-row m-tile) work items of active groups
-//   gate_up:  C[m, n] = sum_h x[tok(m), h] W_gu[n, h] for 64 gate rows and the
-//             matching 64 up rows per tile; epilogue h = silu(gate) * up -> bf16
-//   down:     O[m, n] = sum_i h[m, i] W_dn[n, i] -> fp32 per assignment row
-//   combine:  y_t = sum_j w_tj O[pos(t,j)] + sigmoid(x_t . w_g) O[shared row t]
-// The hidden state is rounded to bf16 (the MFMA input type); everything else
-// accumulates in fp32, and the combine order is fixed.
+//   prep:     per-token scale, fp16 activations, shared gate sigmoid(x_t . w_g)
+//   plan:     (group, m0) tiles of 128 rows plus one 32/64/128-row remainder
+//   gate_up:  C = x W_gu^T over 64 gate and the 64 matching up rows per tile,
+//             epilogue h = silu(gate) * up -> fp16
+//   down:     O = h W_dn^T over 128 output rows per tile -> fp32
+//   combine:  y_t = sum_j w_tj O[pos(t,j)] + s_t O[shared row t] (fixed order)
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128;        // tokens per tile
-constexpr int BN = 128;        // weight rows per tile (gate_up: 64 gate + 64 up)
-constexpr int BK = 64;         // contraction step
-constexpr int LDSP = BK + 8;   // LDS row pitch in bf16 elements (144 B: spreads rows over banks)
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int BK = 128;           // contraction step
+constexpr int APITCH = BK + 8;    // LDS row pitch of the activation tile, in fp16 elements
+constexpr int kClasses = 3;       // row-tile classes: 128, 64, 32 rows
 
 struct PrefillArgs {
     const uint8_t* bank;
@@ -40,9 +55,13 @@ struct PrefillArgs {
     const int32_t* offsets;
     const int32_t* sorted_assign;
     const int32_t* assign_pos;
-    uint16_t* hbuf;   // bf16 [(T*k + T), I]
+    _Float16* hbuf;   // fp16 [(T*k + T), I]
     float* obuf;      // f32  [(T*k + T), H]
-    int* tiles;       // [1 + 2 * max_tiles]: count, then (group, m0) pairs
+    _Float16* x16;    // fp16 [T, H] scaled activations
+    float* xinv;      // f32  [T] inverse activation scale
+    float* sbuf;      // f32  [T] shared gate
+    int* tiles;       // [4 + kClasses * 2 * cap]: per-class counts, then (group, m0) pairs per class
+    int cap;
     float* y;
     int accumulate;
     size_t gu_codes, gu_scales, gu_glob, dn_codes, dn_scales, dn_glob;
@@ -64,343 +83,404 @@ __device__ __forceinline__ const uint8_t* group_slot(const PrefillArgs& a, int g
     return g == a.E ? a.shared : a.bank + (size_t)a.slot_of_expert[g] * a.slot_bytes;
 }
 
+// ------------------------------------------------------------------ prep
+__global__ void __launch_bounds__(256) prep_kernel(PrefillArgs a) {
+    __shared__ float red[2][4];
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int H = a.H, nvec = H / 8;
+    const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * H);
+    const u32x4_t* wr = reinterpret_cast<const u32x4_t*>(a.wg);
+    constexpr int kMaxV = 4;  // H <= 8192
+    u32x4_t xv[kMaxV];
+    float amax = 0.0f, dot = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMaxV; ++q) {
+        const int v = tid + 256 * q;
+        xv[q] = v < nvec ? xr[v] : u32x4_t{0, 0, 0, 0};
+        const uint32_t ws[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+        u32x4_t wv = (a.shared != nullptr && v < nvec) ? wr[v] : u32x4_t{0, 0, 0, 0};
+        const uint32_t gs[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            amax = fmaxf(amax, fabsf(bf16_bits_f32(ws[m] & 0xFFFF)));
+            amax = fmaxf(amax, fabsf(bf16_bits_f32(ws[m] >> 16)));
+            dot = dot2_bf16(as_bf16x2(ws[m]), as_bf16x2(gs[m]), dot);
+        }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+        dot += __shfl_xor(dot, off, kWave);
+    }
+    if (lane == 0) red[0][wave] = amax, red[1][wave] = dot;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    // scale = 2^(14 - floor(log2 amax)) puts the row maximum in [2^14, 2^15)
+    int e = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
+    const int shift = amax > 0.0f ? 15 - e : 0;
+    const float sc = ldexpf(1.0f, shift);
+    if (tid == 0) {
+        a.xinv[t] = ldexpf(1.0f, -shift);
+        if (a.shared != nullptr) a.sbuf[t] = sigmoidf_(red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+    }
+    f16x2_t* dst = reinterpret_cast<f16x2_t*>(a.x16 + (size_t)t * H);
+#pragma unroll
+    for (int q = 0; q < kMaxV; ++q) {
+        const int v = tid + 256 * q;
+        if (v >= nvec) continue;
+        const uint32_t ws[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f16x2_t h2;
+            h2.x = (_Float16)(bf16_bits_f32(ws[m] & 0xFFFF) * sc);
+            h2.y = (_Float16)(bf16_bits_f32(ws[m] >> 16) * sc);
+            dst[v * 4 + m] = h2;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ plan
+__device__ __forceinline__ int tile_class(int rows) { return rows > 64 ? 0 : (rows > 32 ? 1 : 2); }
+
 __global__ void __launch_bounds__(256) plan_kernel(PrefillArgs a) {
-    __shared__ int wsum[4];
+    __shared__ int wsum[kClasses][4];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int G = a.E + 1;
     const int per = (G + 255) / 256;
     const int g0 = tid * per, g1 = min(G, g0 + per);
-    int cnt = 0;
-    for (int g = g0; g < g1; ++g)
-        if (group_active(a, g)) cnt += ceil_div(group_end(a, g) - group_begin(a, g), BM);
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        int o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
-    }
-    if (lane == kWave - 1) wsum[wave] = incl;
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int i = 0; i < 4; ++i) {
-        if (i < wave) before += wsum[i];
-        total += wsum[i];
-    }
-    int pos = before + incl - cnt;
+    int cnt[kClasses] = {0, 0, 0};
     for (int g = g0; g < g1; ++g) {
         if (!group_active(a, g)) continue;
         const int n = group_end(a, g) - group_begin(a, g);
-        for (int m0 = 0; m0 < n; m0 += BM) {
-            a.tiles[1 + 2 * pos] = g;
-            a.tiles[2 + 2 * pos] = m0;
-            ++pos;
-        }
+        cnt[0] += n / 128;
+        if (n % 128) cnt[tile_class(n % 128)] += 1;
     }
-    if (tid == 0) a.tiles[0] = total;
-}
-
-// Dequantise 32 consecutive elements (16 code bytes, 2 scale bytes) to bf16 in LDS.
-__device__ __forceinline__ void dequant32_to_lds(u32x4_t cw, uint32_t s16, __bf16* dst) {
-    const float s0 = e4m3_f32<0>(s16), s1 = e4m3_f32<1>(s16);
-    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
-    uint32_t packed[16];
+    int pos[kClasses];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float s = q < 2 ? s0 : s1;
-        f32x2_t v0 = e2m1x2_f32<0>(words[q]), v1 = e2m1x2_f32<1>(words[q]);
-        f32x2_t v2 = e2m1x2_f32<2>(words[q]), v3 = e2m1x2_f32<3>(words[q]);
-        // products are exact in bf16; the conversion only drops zero bits
-        bf16x2_t b0 = {(__bf16)(v0.x * s), (__bf16)(v0.y * s)};
-        bf16x2_t b1 = {(__bf16)(v1.x * s), (__bf16)(v1.y * s)};
-        bf16x2_t b2 = {(__bf16)(v2.x * s), (__bf16)(v2.y * s)};
-        bf16x2_t b3 = {(__bf16)(v3.x * s), (__bf16)(v3.y * s)};
-        packed[4 * q + 0] = __builtin_bit_cast(uint32_t, b0);
-        packed[4 * q + 1] = __builtin_bit_cast(uint32_t, b1);
-        packed[4 * q + 2] = __builtin_bit_cast(uint32_t, b2);
-        packed[4 * q + 3] = __builtin_bit_cast(uint32_t, b3);
-    }
-    u32x4_t* d = reinterpret_cast<u32x4_t*>(dst);
+    for (int c = 0; c < kClasses; ++c) {
+        int incl = cnt[c];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d[q] = u32x4_t{packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]};
-}
-
-__device__ __forceinline__ bf16x8_t lds_frag(const __bf16* p) {
-    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
-}
-
-// Row i (0..31 within a 32x32 block) of accumulator register r for lane l.
-__device__ __forceinline__ int acc_row(int r, int lane) { return (r / 4) * 8 + (lane / 32) * 4 + (r % 4); }
-
-// ------------------------------------------------------------------ gate_up + SwiGLU
-__global__ void __launch_bounds__(256) gateup_mfma_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 sA[BM * LDSP];
-    __shared__ __attribute__((aligned(16))) __bf16 sB[BN * LDSP];
-    __shared__ int tok[BM];
-
-    const int n_tiles_n = ceil_div(a.I, BN / 2);
-    const int tile = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
-    if (tile >= a.tiles[0]) return;
-    const int g = a.tiles[1 + 2 * tile], m0 = a.tiles[2 + 2 * tile];
-    const int gb = group_begin(a, g), cnt = min(BM, group_end(a, g) - gb - m0);
-    const uint8_t* slot = group_slot(a, g);
-    const int H = a.H, I = a.I;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = nt * (BN / 2);  // first h column (gate row) of the tile
-
-    for (int m = tid; m < BM; m += 256) {
-        int t = -1;
-        if (m < cnt) {
-            const int p = gb + m0 + m;
-            t = g < a.E ? a.sorted_assign[p] / a.k : p - a.T * a.k;
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int o = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += o;
         }
-        tok[m] = t;
+        if (lane == kWave - 1) wsum[c][wave] = incl;
+        pos[c] = incl - cnt[c];
     }
     __syncthreads();
-
-    // loader roles: row = tid / 2, 32-element half = tid % 2
-    const int lrow = tid >> 1, lhalf = tid & 1;
-    const int my_tok = tok[lrow];
-    // B row: tile rows [0, 64) are gate rows n0.., [64, 128) are up rows I + n0..
-    const int hcol = n0 + (lrow & 63);
-    const bool brow_ok = hcol < I;
-    const int wrow = (lrow < 64 ? 0 : I) + (brow_ok ? hcol : 0);
-    const uint8_t* bcodes = slot + a.gu_codes + (size_t)wrow * (H / 2);
-    const uint8_t* bscales = slot + a.gu_scales + (size_t)wrow * (H / 16);
-    const uint16_t* xrow = a.x + (size_t)(my_tok < 0 ? 0 : my_tok) * H;
-
-    f32x16_t acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    for (int k0 = 0; k0 < H; k0 += BK) {
-        const int kc = k0 + 32 * lhalf;
-        const bool kok = kc < H;
-        // A: 32 activations of row lrow
-        u32x4_t av[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) av[q] = u32x4_t{0, 0, 0, 0};
-        if (my_tok >= 0 && kok) {
-            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xrow + kc);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) av[q] = src[q];
+    for (int c = 0; c < kClasses; ++c) {
+        int before = 0, total = 0;
+        for (int i = 0; i < 4; ++i) {
+            if (i < wave) before += wsum[c][i];
+            total += wsum[c][i];
         }
-        // B: 32 weights of row lrow
-        u32x4_t cw = u32x4_t{0, 0, 0, 0};
-        uint32_t s16 = 0;
-        if (brow_ok && kok) {
-            cw = *reinterpret_cast<const u32x4_t*>(bcodes + kc / 2);
-            s16 = *reinterpret_cast<const uint16_t*>(bscales + kc / 16);
-        }
-        __syncthreads();
-        u32x4_t* da = reinterpret_cast<u32x4_t*>(sA + lrow * LDSP + 32 * lhalf);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) da[q] = av[q];
-        dequant32_to_lds(cw, s16, sB + lrow * LDSP + 32 * lhalf);
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            const int ko = kk + 8 * (lane / 32);
-            bf16x8_t fa[2], fb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = lds_frag(sA + (64 * wm + 32 * i + lane % 32) * LDSP + ko);
-            // j = 0: gate rows, j = 1: up rows, both for h columns [32 wn, 32 wn + 32)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) fb[j] = lds_frag(sB + (64 * j + 32 * wn + lane % 32) * LDSP + ko);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
+        pos[c] += before;
+        if (tid == 0) a.tiles[c] = total;
     }
-
-    // epilogue: lane holds column (lane % 32) of each 32x32 block
-    const int col = n0 + 32 * wn + lane % 32;
-    if (col < I) {
-        const float* gl = reinterpret_cast<const float*>(slot + a.gu_glob);
-        const float gg = gl[col], gu = gl[I + col];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = 64 * wm + 32 * i + acc_row(r, lane);
-                if (m < cnt) {
-                    const float gate = acc[i][0][r] * gg, up = acc[i][1][r] * gu;
-                    const __bf16 hv = (__bf16)(gate * sigmoidf_(gate) * up);
-                    a.hbuf[(size_t)(gb + m0 + m) * I + col] = __builtin_bit_cast(uint16_t, hv);
-                }
-            }
+    for (int g = g0; g < g1; ++g) {
+        if (!group_active(a, g)) continue;
+        const int n = group_end(a, g) - group_begin(a, g);
+        for (int m0 = 0; m0 < n; m0 += 128) {
+            const int c = (n - m0 >= 128) ? 0 : tile_class(n - m0);
+            int* e = a.tiles + 4 + 2 * (c * a.cap + pos[c]);
+            e[0] = g;
+            e[1] = m0;
+            ++pos[c];
+        }
     }
 }
 
-// ------------------------------------------------------------------ down
-__global__ void __launch_bounds__(256) down_mfma_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 sA[BM * LDSP];
-    __shared__ __attribute__((aligned(16))) __bf16 sB[BN * LDSP];
+// ------------------------------------------------------------------ grouped GEMM (gate_up and down)
 
-    const int n_tiles_n = ceil_div(a.H, BN);
+__device__ __forceinline__ f16x8_t lds_frag(const _Float16* p) {
+    return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+}
+
+// 32 consecutive weights of one row (16 code bytes, 2 scale bytes) -> 16 words
+// of fp16 pairs, exact: e2m1 decoded with unit scale, times the E4M3 block scale.
+__device__ __forceinline__ void dequant32_f16(u32x4_t cw, uint32_t s16, uint32_t* out) {
+    const _Float16 s0 = (_Float16)e4m3_f32<0>(s16), s1 = (_Float16)e4m3_f32<1>(s16);
+    const f16x2_t S0 = {s0, s0}, S1 = {s1, s1};
+    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f16x2_t S = q < 2 ? S0 : S1;
+        const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[q], 1.0f, 0) * S;
+        const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[q], 1.0f, 1) * S;
+        const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[q], 1.0f, 2) * S;
+        const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[q], 1.0f, 3) * S;
+        out[4 * q + 0] = __builtin_bit_cast(uint32_t, v0);
+        out[4 * q + 1] = __builtin_bit_cast(uint32_t, v1);
+        out[4 * q + 2] = __builtin_bit_cast(uint32_t, v2);
+        out[4 * q + 3] = __builtin_bit_cast(uint32_t, v3);
+    }
+}
+
+// One workgroup = one (tile, 64 h-columns) for gate_up or (tile, 128 output
+// rows) for down.  4 waves as WMW (rows) x WNW (columns); each wave owns
+// MB = BM/WMW/16 row blocks and NBW column blocks of 16.
+template <int BM, bool GATEUP>
+__global__ void __launch_bounds__(256) gemm_kernel(PrefillArgs a, int cls, int n_tiles_n) {
+    constexpr int WMW = BM == 32 ? 1 : 2;
+    constexpr int WNW = 4 / WMW;
+    constexpr int MB = BM / WMW / 16;
+    constexpr int NCOLS = GATEUP ? 64 : 128;       // h columns (gate_up) or output rows (down) per tile
+    constexpr int CW = NCOLS / WNW;                 // columns per wave
+    constexpr int NBW = GATEUP ? 2 * (CW / 16) : CW / 16;  // column blocks per wave (gate and up for gate_up)
+    __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * APITCH];
+    __shared__ int tok[BM];
+
     const int tile = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
-    if (tile >= a.tiles[0]) return;
-    const int g = a.tiles[1 + 2 * tile], m0 = a.tiles[2 + 2 * tile];
+    if (tile >= a.tiles[cls]) return;
+    const int* te = a.tiles + 4 + 2 * (cls * a.cap + tile);
+    const int g = te[0], m0 = te[1];
     const int gb = group_begin(a, g), cnt = min(BM, group_end(a, g) - gb - m0);
     const uint8_t* slot = group_slot(a, g);
-    const int H = a.H, I = a.I;
+    const int H = a.H, I = a.I, T = a.T, k = a.k;
+    const int K = GATEUP ? H : I;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = nt * BN;
+    const int wm = wave / WNW, wn = wave % WNW;
+    const int l16 = lane % 16, q4 = lane / 16;
 
-    const int lrow = tid >> 1, lhalf = tid & 1;
-    const bool arow_ok = lrow < cnt;
-    const uint16_t* hrow = a.hbuf + (size_t)(gb + m0 + (arow_ok ? lrow : 0)) * I;
-    const int orow = n0 + lrow;
-    const bool brow_ok = orow < H;
-    const uint8_t* bcodes = slot + a.dn_codes + (size_t)(brow_ok ? orow : 0) * (I / 2);
-    const uint8_t* bscales = slot + a.dn_scales + (size_t)(brow_ok ? orow : 0) * (I / 16);
-
-    f32x16_t acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    for (int k0 = 0; k0 < I; k0 += BK) {
-        const int kc = k0 + 32 * lhalf;
-        const bool kok = kc < I;
-        u32x4_t av[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) av[q] = u32x4_t{0, 0, 0, 0};
-        if (arow_ok && kok) {
-            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(hrow + kc);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) av[q] = src[q];
-        }
-        u32x4_t cw = u32x4_t{0, 0, 0, 0};
-        uint32_t s16 = 0;
-        if (brow_ok && kok) {
-            cw = *reinterpret_cast<const u32x4_t*>(bcodes + kc / 2);
-            s16 = *reinterpret_cast<const uint16_t*>(bscales + kc / 16);
+    if (GATEUP) {
+        for (int m = tid; m < BM; m += 256) {
+            int t = -1;
+            if (m < cnt) {
+                const int p = gb + m0 + m;
+                t = g < a.E ? a.sorted_assign[p] / k : p - T * k;
+            }
+            tok[m] = t;
         }
         __syncthreads();
-        u32x4_t* da = reinterpret_cast<u32x4_t*>(sA + lrow * LDSP + 32 * lhalf);
+    }
+
+    // B rows of this wave: column block b of the wave -> weight row
+    const uint8_t* bcodes[NBW];
+    const uint8_t* bscales[NBW];
+    bool bok[NBW];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) da[q] = av[q];
-        dequant32_to_lds(cw, s16, sB + lrow * LDSP + 32 * lhalf);
-        __syncthreads();
+    for (int b = 0; b < NBW; ++b) {
+        int wrow;
+        if (GATEUP) {
+            const int half = b / (NBW / 2), cb = b % (NBW / 2);   // half 0 = gate, 1 = up
+            const int hc = nt * 64 + wn * CW + cb * 16 + l16;
+            bok[b] = hc < I;
+            wrow = half * I + (hc < I ? hc : 0);
+        } else {
+            const int oc = nt * 128 + wn * CW + b * 16 + l16;
+            bok[b] = oc < H;
+            wrow = oc < H ? oc : 0;
+        }
+        bcodes[b] = slot + (GATEUP ? a.gu_codes : a.dn_codes) + (size_t)wrow * (K / 2);
+        bscales[b] = slot + (GATEUP ? a.gu_scales : a.dn_scales) + (size_t)wrow * (K / 16);
+    }
+
+    // A tile loader: 16 threads per row, 16 bytes (8 fp16) each
+    constexpr int ROWS_PER_PASS = 256 / 16;
+    constexpr int APASSES = (BM + ROWS_PER_PASS - 1) / ROWS_PER_PASS;
+    const int arow0 = tid / 16, apiece = tid % 16;
+    u32x4_t areg[APASSES];
+    auto load_a = [&](int k0) {
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            const int ko = kk + 8 * (lane / 32);
-            bf16x8_t fa[2], fb[2];
+        for (int ps = 0; ps < APASSES; ++ps) {
+            const int m = arow0 + ps * ROWS_PER_PASS;
+            const int kk = k0 + apiece * 8;
+            u32x4_t v = u32x4_t{0, 0, 0, 0};
+            if (m < BM && m < cnt && kk < K) {
+                const _Float16* src;
+                if (GATEUP) src = a.x16 + (size_t)tok[m] * H + kk;
+                else src = a.hbuf + (size_t)(gb + m0 + m) * I + kk;
+                v = *reinterpret_cast<const u32x4_t*>(src);
+            }
+            areg[ps] = v;
+        }
+    };
+    auto store_a = [&](int buf) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = lds_frag(sA + (64 * wm + 32 * i + lane % 32) * LDSP + ko);
+        for (int ps = 0; ps < APASSES; ++ps) {
+            const int m = arow0 + ps * ROWS_PER_PASS;
+            if (m < BM) *reinterpret_cast<u32x4_t*>(&sA[buf][m * APITCH + apiece * 8]) = areg[ps];
+        }
+    };
+    u32x4_t bcw[NBW];
+    uint32_t bsc[NBW];
+    auto load_b = [&](int k0) {
+        const int kc = k0 + 32 * q4;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) fb[j] = lds_frag(sB + (64 * wn + 32 * j + lane % 32) * LDSP + ko);
+        for (int b = 0; b < NBW; ++b) {
+            if (bok[b] && kc < K) {
+                bcw[b] = *reinterpret_cast<const u32x4_t*>(bcodes[b] + kc / 2);
+                bsc[b] = *reinterpret_cast<const uint16_t*>(bscales[b] + kc / 16);
+            } else {
+                bcw[b] = u32x4_t{0, 0, 0, 0};
+                bsc[b] = 0;
+            }
+        }
+    };
+
+    f32x4_t acc[MB][NBW];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int b = 0; b < NBW; ++b) acc[i][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int nsteps = (K + BK - 1) / BK;
+    load_a(0);
+    load_b(0);
+    store_a(0);
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
+        // dequantise this step's B fragments, then prefetch the next step
+        uint32_t bw[NBW][16];
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) dequant32_f16(bcw[b], bsc[b], bw[b]);
+        if (s + 1 < nsteps) {
+            load_a((s + 1) * BK);
+            load_b((s + 1) * BK);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f16x8_t fa[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                fa[i] = lds_frag(&sA[buf][(wm * MB * 16 + i * 16 + l16) * APITCH + 32 * q4 + 8 * j]);
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                const u32x4_t bv = u32x4_t{bw[b][4 * j], bw[b][4 * j + 1], bw[b][4 * j + 2], bw[b][4 * j + 3]};
+                const f16x8_t fb = __builtin_bit_cast(f16x8_t, bv);
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[i][b], 0, 0, 0);
+            }
+        }
+        if (s + 1 < nsteps) {
+            store_a(buf ^ 1);
+            __syncthreads();
         }
     }
 
-    const float* gl = reinterpret_cast<const float*>(slot + a.dn_glob);
+    // epilogue: lane holds rows 4*q4 + r (r < 4) of column l16 of each 16x16 block
+    if (GATEUP) {
+        const float* gl = reinterpret_cast<const float*>(slot + a.gu_glob);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int col = n0 + 64 * wn + 32 * j + lane % 32;
-        if (col >= H) continue;
-        const float gd = gl[col];
+        for (int cb = 0; cb < NBW / 2; ++cb) {
+            const int hc = nt * 64 + wn * CW + cb * 16 + l16;
+            if (hc >= I) continue;
+            const float gg = gl[hc], gu = gl[I + hc];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = 64 * wm + 32 * i + acc_row(r, lane);
-                if (m < cnt) a.obuf[(size_t)(gb + m0 + m) * H + col] = acc[i][j][r] * gd;
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const int m = wm * MB * 16 + i * 16 + 4 * q4 + r;
+                    if (m >= cnt) continue;
+                    const float inv = a.xinv[tok[m]];
+                    const float gate = acc[i][cb][r] * inv * gg;
+                    const float up = acc[i][NBW / 2 + cb][r] * inv * gu;
+                    float h = gate * sigmoidf_(gate) * up;
+                    h = fminf(fmaxf(h, -65504.0f), 65504.0f);
+                    a.hbuf[(size_t)(gb + m0 + m) * I + hc] = (_Float16)h;
+                }
+        }
+    } else {
+        const float* gl = reinterpret_cast<const float*>(slot + a.dn_glob);
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+            const int oc = nt * 128 + wn * CW + b * 16 + l16;
+            if (oc >= H) continue;
+            const float gd = gl[oc];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = wm * MB * 16 + i * 16 + 4 * q4 + r;
+                    if (m < cnt) a.obuf[(size_t)(gb + m0 + m) * H + oc] = acc[i][b][r] * gd;
+                }
+        }
     }
 }
 
 // ------------------------------------------------------------------ combine
-__global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a) {
-    __shared__ float red[4];
-    __shared__ float s_sh;
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+__global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a, int nchunk) {
+    __shared__ int pos_s[1024];
+    __shared__ float w_s[1024];
+    const int t = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+    const int tid = threadIdx.x;
     const int H = a.H, T = a.T, k = a.k;
-    if (a.shared != nullptr) {
-        float acc = 0.0f;
-        for (int c = tid; c < H; c += 256)
-            acc += bf16_bits_f32(a.x[(size_t)t * H + c]) * bf16_bits_f32(a.wg[c]);
-        acc = wave_sum(acc);
-        if (lane == 0) red[wave] = acc;
-        __syncthreads();
-        if (tid == 0) s_sh = sigmoidf_(red[0] + red[1] + red[2] + red[3]);
-        __syncthreads();
+    for (int j = tid; j < k; j += 256) {
+        const int aidx = t * k + j;
+        const bool ok = a.slot_of_expert[a.ids[aidx]] >= 0;
+        pos_s[j] = ok ? a.assign_pos[aidx] : -1;
+        w_s[j] = a.w[aidx];
     }
-    for (int n = tid; n < H; n += 256) {
-        float acc = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const int aidx = t * k + j;
-            if (a.slot_of_expert[a.ids[aidx]] >= 0) acc += a.w[aidx] * a.obuf[(size_t)a.assign_pos[aidx] * H + n];
-        }
-        if (a.shared != nullptr) acc += s_sh * a.obuf[(size_t)(T * k + t) * H + n];
-        float* yp = a.y + (size_t)t * H + n;
-        *yp = a.accumulate ? *yp + acc : acc;
+    const float st = a.shared != nullptr ? a.sbuf[t] : 0.0f;
+    __syncthreads();
+    const int n = chunk * 256 + tid;
+    if (n >= H) return;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        const int p = pos_s[j];
+        if (p >= 0) acc += w_s[j] * a.obuf[(size_t)p * H + n];
     }
+    if (a.shared != nullptr) acc += st * a.obuf[(size_t)(T * k + t) * H + n];
+    float* yp = a.y + (size_t)t * H + n;
+    *yp = a.accumulate ? *yp + acc : acc;
+}
+
+template <int BM, bool GATEUP>
+hipError_t launch_gemm(const PrefillArgs& a, int cls, int max_tiles, int ntn, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_kernel<BM, GATEUP>), dim3(max_tiles * ntn), dim3(256), 0, s, a, cls, ntn);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-bool prefill_shape_supported(int H, int I) { return H % 32 == 0 && I % 32 == 0; }
+bool prefill_shape_supported(int H, int I) { return H % 32 == 0 && I % 32 == 0 && H <= 8192; }
 
 hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                           const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
                           int accumulate, void* ws, hipStream_t s) {
     const int H = L.H, I = L.I, E = L.E, k = L.k;
-    const int nrows_all = T * k + T;
     uint8_t* p = static_cast<uint8_t*>(ws);
+    const WsLayout wl = ws_layout(T, H, I, E, k);
     PrefillArgs a;
     a.bank = L.bank; a.slot_bytes = L.slot_bytes; a.slot_of_expert = L.slot_of_expert;
     a.shared = L.shared; a.wg = L.wg; a.x = x;
     a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
     a.w = w; a.ids = ids; a.offsets = offsets; a.sorted_assign = sorted_assign; a.assign_pos = assign_pos;
-    a.hbuf = reinterpret_cast<uint16_t*>(p);
-    p += (size_t)nrows_all * I * 4;  // sized for the f32 decode layout; bf16 uses half
-    a.obuf = reinterpret_cast<float*>(p);
-    p += (size_t)nrows_all * H * 4;
-    p += 256 * ((T * 4 + 255) / 256);
-    p += 256 * (((H + 63) / 64 * 4 + 255) / 256);
-    a.tiles = reinterpret_cast<int*>(p);
+    a.hbuf = reinterpret_cast<_Float16*>(p + wl.h);
+    a.obuf = reinterpret_cast<float*>(p + wl.o);
+    a.x16 = reinterpret_cast<_Float16*>(p + wl.x16);
+    a.xinv = reinterpret_cast<float*>(p + wl.xinv);
+    a.sbuf = reinterpret_cast<float*>(p + wl.s);
+    a.tiles = reinterpret_cast<int*>(p + wl.tiles);
+    a.cap = wl.tile_cap;
     a.y = y; a.accumulate = accumulate;
     SlotGeom gm = slot_geom(H, I);
     a.gu_codes = gm.gu_codes; a.gu_scales = gm.gu_scales; a.gu_glob = gm.gu_glob;
     a.dn_codes = gm.dn_codes; a.dn_scales = gm.dn_scales; a.dn_glob = gm.dn_glob;
 
-    const int max_tiles = ceil_div(nrows_all, BM) + E + 1;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, a);
+    const int rows = T * k + T;
+    const int G = E + 1;
+    const int max128 = min(a.cap, rows / 128 + G);
+    const int maxsmall = min(a.cap, G);
+    hipLaunchKernelGGL(prep_kernel, dim3(T), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gateup_mfma_kernel, dim3(max_tiles * ceil_div(I, BN / 2)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(down_mfma_kernel, dim3(max_tiles * ceil_div(H, BN)), dim3(256), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, s, a);
+    const int ntn_gu = ceil_div(I, 64), ntn_dn = ceil_div(H, 128);
+    if ((e = launch_gemm<128, true>(a, 0, max128, ntn_gu, s)) != hipSuccess) return e;
+    if ((e = launch_gemm<64, true>(a, 1, maxsmall, ntn_gu, s)) != hipSuccess) return e;
+    if ((e = launch_gemm<32, true>(a, 2, maxsmall, ntn_gu, s)) != hipSuccess) return e;
+    if ((e = launch_gemm<128, false>(a, 0, max128, ntn_dn, s)) != hipSuccess) return e;
+    if ((e = launch_gemm<64, false>(a, 1, maxsmall, ntn_dn, s)) != hipSuccess) return e;
+    if ((e = launch_gemm<32, false>(a, 2, maxsmall, ntn_dn, s)) != hipSuccess) return e;
+    const int nchunk = ceil_div(H, 256);
+    hipLaunchKernelGGL(combine_kernel, dim3(T * nchunk), dim3(256), 0, s, a, nchunk);
     return hipGetLastError();
-}
-
-size_t forward_ws_bytes(int T, int H, int I, int E, int k) {
-    const size_t nrows_all = (size_t)T * k + T;
-    size_t b = nrows_all * I * 4 + nrows_all * H * 4;
-    b += 256 * (((size_t)T * 4 + 255) / 256);
-    b += 256 * ((((size_t)H + 63) / 64 * 4 + 255) / 256);
-    const size_t max_tiles = (nrows_all + BM - 1) / BM + E + 1;
-    b += 256 * (((1 + 2 * max_tiles) * 4 + 255) / 256);
-    return b;
 }
 
 }  // namespace moe

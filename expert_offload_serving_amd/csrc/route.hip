@@ -30,25 +30,27 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
     return ia < ib;
 }
 
-// One wave selects the top-k of row `l` (E logits) and writes ids and weights.
+// One wave selects the top-k of row `l` (E <= 64 * VPL logits) and writes ids and weights.
+template <int VPL>
 __device__ void topk_one_token(const float* __restrict__ l, int E, int k, int32_t* __restrict__ ids,
                                float* __restrict__ w, int lane) {
-    float v[kVPL];
+    static_assert(VPL <= kVPL, "too many logits per lane");
+    float v[VPL];
     uint32_t taken = 0;
 #pragma unroll
-    for (int i = 0; i < kVPL; ++i) {
+    for (int i = 0; i < VPL; ++i) {
         int idx = lane + kWave * i;
         v[i] = idx < E ? l[idx] : 0.0f;
     }
-    float held_v[kVPL];  // logit of selection j is kept by lane j % 64 in slot j / 64
+    float held_v[VPL];  // logit of selection j is kept by lane j % 64 in slot j / 64
 #pragma unroll
-    for (int i = 0; i < kVPL; ++i) held_v[i] = 0.0f;
+    for (int i = 0; i < VPL; ++i) held_v[i] = 0.0f;
     float m = 0.0f;
     for (int j = 0; j < k; ++j) {
         float bv = 0.0f;
         int bi = -1;
 #pragma unroll
-        for (int i = 0; i < kVPL; ++i) {
+        for (int i = 0; i < VPL; ++i) {
             int idx = lane + kWave * i;
             bool ok = idx < E && !((taken >> i) & 1u);
             if (ok && ranks_before(v[i], idx, bv, bi)) bv = v[i], bi = idx;
@@ -68,30 +70,31 @@ __device__ void topk_one_token(const float* __restrict__ l, int E, int k, int32_
         }
     }
     // Softmax over the selected logits in double, summed in selection order.
-    double ex[kVPL];
+    double ex[VPL];
 #pragma unroll
-    for (int i = 0; i < kVPL; ++i) ex[i] = exp((double)held_v[i] - (double)m);
+    for (int i = 0; i < VPL; ++i) ex[i] = (lane + kWave * i < k) ? exp((double)held_v[i] - (double)m) : 0.0;
     double sum = 0.0;
     for (int j = 0; j < k; ++j) {
         double e = 0.0;
 #pragma unroll
-        for (int i = 0; i < kVPL; ++i)
+        for (int i = 0; i < VPL; ++i)
             if (i == j / kWave) e = ex[i];
         sum += __shfl(e, j % kWave, kWave);
     }
 #pragma unroll
-    for (int i = 0; i < kVPL; ++i) {
+    for (int i = 0; i < VPL; ++i) {
         int j = lane + kWave * i;
         if (j < k) w[j] = (float)(ex[i] / sum);
     }
 }
 
+template <int VPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                     int32_t* __restrict__ ids, float* __restrict__ w) {
     int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
     int lane = threadIdx.x % kWave;
-    topk_one_token(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, lane);
+    topk_one_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, lane);
 }
 
 // Stable counting sort of n = T*k assignments by expert, one workgroup of
@@ -169,27 +172,57 @@ __global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict
     permute_block(ids, n, E, offsets, sorted_assign, assign_pos, cnt, run, wsum);
 }
 
-// T <= 16 and T*k <= kFusedMaxAssign: top-k by waves 0..T-1, then the
-// permutation, in one workgroup (one launch per decode layer).
-constexpr int kFusedMaxAssign = 4096;
+// Decode batches (T <= 16, T*k <= kDirectMaxAssign): one workgroup with one
+// wave per token selects the top-k, then ranks every assignment directly:
+//   offsets[e] = #{assignments with expert < e}
+//   pos(a)     = #{a' : (e', a') < (e, a)}   (expert, then flat index)
+// which is the same stable grouping as the counting sort, in one launch.
+constexpr int kDirectMaxAssign = 256;
 
-__global__ void __launch_bounds__(1024) route_fused_kernel(const float* __restrict__ logits, int T, int E, int k,
+template <int VPL>
+__global__ void __launch_bounds__(1024) route_small_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                             int32_t* __restrict__ ids, float* __restrict__ w,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ sorted_assign,
                                                             int32_t* __restrict__ assign_pos) {
-    __shared__ int cnt[kMaxE];
-    __shared__ int run[kMaxE];
-    __shared__ int wsum[16];
-    __shared__ int32_t ids_lds[kFusedMaxAssign];
+    __shared__ int32_t ids_lds[kDirectMaxAssign];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    if (wave < T) {
-        topk_one_token(logits + (size_t)wave * E, E, k, ids_lds + wave * k, w + (size_t)wave * k, lane);
-    }
+    if (wave < T) topk_one_token<VPL>(logits + (size_t)wave * E, E, k, ids_lds + wave * k, w + (size_t)wave * k, lane);
     __syncthreads();
     const int n = T * k;
-    for (int a = threadIdx.x; a < n; a += 1024) ids[a] = ids_lds[a];
-    permute_block(ids_lds, n, E, offsets, sorted_assign, assign_pos, cnt, run, wsum);
+    for (int a = threadIdx.x; a < n; a += blockDim.x) {
+        const int e = ids_lds[a];
+        int pos = 0;
+        for (int b = 0; b < n; ++b) {
+            const int eb = ids_lds[b];
+            pos += (eb < e || (eb == e && b < a)) ? 1 : 0;
+        }
+        ids[a] = e;
+        sorted_assign[pos] = a;
+        assign_pos[a] = pos;
+    }
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+        int c = 0;
+        for (int b = 0; b < n; ++b) c += ids_lds[b] < e ? 1 : 0;
+        offsets[e] = c;
+    }
+}
+
+template <int VPL>
+hipError_t launch_route_vpl(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,
+                            int32_t* sorted_assign, int32_t* assign_pos, hipStream_t s) {
+    if (T <= 16 && T * k <= kDirectMaxAssign) {
+        const int threads = kWave * max(4, T);
+        hipLaunchKernelGGL(route_small_kernel<VPL>, dim3(1), dim3(threads), 0, s, logits, T, E, k, ids, w, offsets,
+                           sorted_assign, assign_pos);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(topk_kernel<VPL>, dim3(ceil_div(T, 4)), dim3(256), 0, s, logits, T, E, k, ids, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, ids, T * k, E, offsets, sorted_assign,
+                       assign_pos);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -198,17 +231,12 @@ size_t route_ws_bytes(int, int, int) { return 0; }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_assign, int32_t* assign_pos, void*, hipStream_t s) {
-    if (T <= 16 && T * k <= kFusedMaxAssign) {
-        hipLaunchKernelGGL(route_fused_kernel, dim3(1), dim3(1024), 0, s, logits, T, E, k, ids, w, offsets,
-                           sorted_assign, assign_pos);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(topk_kernel, dim3(ceil_div(T, 4)), dim3(256), 0, s, logits, T, E, k, ids, w);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, ids, T * k, E, offsets, sorted_assign,
-                       assign_pos);
-    return hipGetLastError();
+    const int vpl = ceil_div(E, kWave);
+    if (vpl <= 1) return launch_route_vpl<1>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, s);
+    if (vpl <= 2) return launch_route_vpl<2>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, s);
+    if (vpl <= 4) return launch_route_vpl<4>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, s);
+    if (vpl <= 8) return launch_route_vpl<8>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, s);
+    return launch_route_vpl<16>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, s);
 }
 
 }  // namespace moe
