@@ -77,6 +77,11 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<kWave>(v); }
 
+// Opaque to the optimiser: keeps code words from being decoded once and held
+// decoded across a loop (which would multiply their register footprint).
+__device__ __forceinline__ void keep_packed(u32x4_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void keep_packed(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 }  // namespace moe

@@ -9,7 +9,7 @@
 // descending, expert index ascending).  The permutation groups the T*k
 // assignments by expert with a stable counting sort (per-expert counts,
 // exclusive scan, then stable ranks from wave ballots), so the grouping is
-// bit-reproducible: no atomic operation decides an order.
+// bit-reproducible: no atomic operation decides an order (atomics only count).
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -28,6 +28,36 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
     if (va > vb) return true;
     if (va < vb) return false;
     return ia < ib;
+}
+
+// DPP row operations of the GCN/CDNA ISA (gfx9 encodings).
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr3 = 0x113, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// One step of a wave arg-max: combine each lane's (v, i) with the pair DPP
+// control CTRL brings in; lanes the masks disable or whose source is out of
+// range keep their own pair.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK,
+                                                                BANK_MASK, false));
+    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, BANK_MASK, false);
+    if (ranks_before(ov, oi, v, i)) v = ov, i = oi;
+}
+
+// Wave-wide best (v, i) by ranks_before, returned to every lane.  The DPP
+// sequence leaves the result in lane 63 (shifts within each 16-lane row,
+// then the row broadcasts); max-like merges tolerate the overlaps.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+    argmax_step<kDppRowShr1, 0xF, 0xF>(v, i);
+    argmax_step<kDppRowShr2, 0xF, 0xF>(v, i);
+    argmax_step<kDppRowShr3, 0xF, 0xF>(v, i);
+    argmax_step<kDppRowShr4, 0xF, 0xE>(v, i);
+    argmax_step<kDppRowShr8, 0xF, 0xC>(v, i);
+    argmax_step<kDppRowBcast15, 0xA, 0xF>(v, i);
+    argmax_step<kDppRowBcast31, 0xC, 0xF>(v, i);
+    v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    i = __builtin_amdgcn_readlane(i, 63);
 }
 
 // One wave selects the top-k of row `l` (E <= 64 * VPL logits) and writes ids and weights.
@@ -55,13 +85,7 @@ __device__ void topk_one_token(const float* __restrict__ l, int E, int k, int32_
             bool ok = idx < E && !((taken >> i) & 1u);
             if (ok && ranks_before(v[i], idx, bv, bi)) bv = v[i], bi = idx;
         }
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) {
-            float ov = __shfl_xor(bv, off, kWave);
-            int oi = __shfl_xor(bi, off, kWave);
-            if (ranks_before(ov, oi, bv, bi)) bv = ov, bi = oi;
-        }
-        // bi is the same on every lane (a strict total order without NaN).
+        wave_argmax(bv, bi);
         if (bi >= 0 && (bi % kWave) == lane) taken |= 1u << (bi / kWave);
         if (j == 0) m = bv;
         if ((j % kWave) == lane) {
@@ -97,79 +121,87 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     topk_one_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, lane);
 }
 
-// Stable counting sort of n = T*k assignments by expert, one workgroup of
-// 1024 threads.  `ids` may be global or LDS memory.
-__device__ void permute_block(const int32_t* ids, int n, int E, int32_t* __restrict__ offsets,
-                              int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos, int* cnt,
-                              int* run, int* wsum) {
+// Multi-workgroup stable counting sort for large batches.  Block b owns the
+// assignments [1024 b, 1024 b + 1024).  perm_count writes each block's
+// per-expert histogram; perm_scatter (one workgroup per block again) adds the
+// histograms of the earlier blocks and the per-expert totals to get where its
+// assignments of each expert start, then ranks them stably inside the block
+// (wave ballots, waves in order) and scatters them.
+constexpr int kPermBlock = 1024;
+
+__global__ void __launch_bounds__(1024) perm_count_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                           int32_t* __restrict__ block_hist) {
+    __shared__ int hist[kMaxE];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 1024) hist[e] = 0;
+    __syncthreads();
+    const int a = blockIdx.x * kPermBlock + tid;
+    if (a < n) atomicAdd(&hist[ids[a]], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += 1024) block_hist[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+__global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __restrict__ ids, int n, int E, int nblocks,
+                                                             const int32_t* __restrict__ block_hist,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_assign,
+                                                             int32_t* __restrict__ assign_pos) {
+    __shared__ int run[kMaxE];
+    __shared__ int wsum[16];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    for (int e = tid; e < E; e += 1024) cnt[e] = 0;
-    __syncthreads();
-    for (int a = tid; a < n; a += 1024) atomicAdd(&cnt[ids[a]], 1);
-    __syncthreads();
-    // Exclusive scan of cnt[0..E) (E <= 1024: one entry per thread).
-    int c = tid < E ? cnt[tid] : 0;
-    int incl = c;
+    const int b = blockIdx.x;
+    // per expert (one per thread): total over all blocks, and the part in blocks before b
+    int total = 0, before_b = 0;
+    if (tid < E) {
+        for (int bb = 0; bb < nblocks; ++bb) {
+            const int h = block_hist[(size_t)bb * E + tid];
+            total += h;
+            if (bb < b) before_b += h;
+        }
+    }
+    // exclusive scan of the totals over experts
+    int incl = total;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-        int o = __shfl_up(incl, off, kWave);
+        const int o = __shfl_up(incl, off, kWave);
         if (lane >= off) incl += o;
     }
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int i = 0; i < 16; ++i) {
-            int s = wsum[i];
-            wsum[i] = acc;
-            acc += s;
-        }
-    }
-    __syncthreads();
-    int excl = incl - c + wsum[wave];
+    int wbefore = 0;
+    for (int i = 0; i < wave; ++i) wbefore += wsum[i];
+    const int excl = wbefore + incl - total;
     if (tid < E) {
-        offsets[tid] = excl;
-        run[tid] = excl;
+        run[tid] = excl + before_b;
+        if (b == 0) offsets[tid] = excl;
     }
-    if (tid == 0) offsets[E] = n;
+    if (b == 0 && tid == 0) offsets[E] = n;
     __syncthreads();
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < n; base += 1024) {
-        int a = base + tid;
-        bool valid = a < n;
-        int e = valid ? ids[a] : 0;
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            bool bit = (e >> b) & 1;
-            uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        int rank = __popcll(peers & lt_mask);
-        int cw = __popcll(peers);
-        int last_wave = min(15, (n - base - 1) / kWave);
-        for (int w2 = 0; w2 <= last_wave; ++w2) {
-            if (wave == w2 && valid) {
-                int b0 = run[e];
-                int pos = b0 + rank;
-                if (rank == 0) run[e] = b0 + cw;
-                sorted_assign[pos] = a;
-                assign_pos[a] = pos;
-            }
-            __syncthreads();
-        }
+    const int a = b * kPermBlock + tid;
+    const bool valid = a < n;
+    const int e = valid ? ids[a] : 0;
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool on = (e >> bit) & 1;
+        const uint64_t m = __ballot(on);
+        peers &= on ? m : ~m;
     }
-}
-
-__global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict__ ids, int n, int E,
-                                                        int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ sorted_assign,
-                                                        int32_t* __restrict__ assign_pos) {
-    __shared__ int cnt[kMaxE];
-    __shared__ int run[kMaxE];
-    __shared__ int wsum[16];
-    permute_block(ids, n, E, offsets, sorted_assign, assign_pos, cnt, run, wsum);
+    const int rank = __popcll(peers & lt_mask);
+    const int cw = __popcll(peers);
+    const int last_wave = (min(kPermBlock, n - b * kPermBlock) - 1) / kWave;
+    for (int w2 = 0; w2 <= last_wave; ++w2) {
+        if (wave == w2 && valid) {
+            const int b0 = run[e];
+            const int pos = b0 + rank;
+            if (rank == 0) run[e] = b0 + cw;
+            sorted_assign[pos] = a;
+            assign_pos[a] = pos;
+        }
+        __syncthreads();
+    }
 }
 
 // Decode batches (T <= 16, T*k <= kDirectMaxAssign): one workgroup with one
@@ -210,7 +242,7 @@ __global__ void __launch_bounds__(1024) route_small_kernel(const float* __restri
 
 template <int VPL>
 hipError_t launch_route_vpl(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,
-                            int32_t* sorted_assign, int32_t* assign_pos, hipStream_t s) {
+                            int32_t* sorted_assign, int32_t* assign_pos, int32_t* ws, hipStream_t s) {
     if (T <= 16 && T * k <= kDirectMaxAssign) {
         const int threads = kWave * max(4, T);
         hipLaunchKernelGGL(route_small_kernel<VPL>, dim3(1), dim3(threads), 0, s, logits, T, E, k, ids, w, offsets,
@@ -220,23 +252,31 @@ hipError_t launch_route_vpl(const float* logits, int T, int E, int k, int32_t* i
     hipLaunchKernelGGL(topk_kernel<VPL>, dim3(ceil_div(T, 4)), dim3(256), 0, s, logits, T, E, k, ids, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, ids, T * k, E, offsets, sorted_assign,
-                       assign_pos);
+    const int n = T * k, nblocks = ceil_div(n, kPermBlock);
+    hipLaunchKernelGGL(perm_count_kernel, dim3(nblocks), dim3(1024), 0, s, ids, n, E, ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nblocks), dim3(1024), 0, s, ids, n, E, nblocks,
+                       static_cast<const int32_t*>(ws), offsets, sorted_assign, assign_pos);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t route_ws_bytes(int, int, int) { return 0; }
+size_t route_ws_bytes(int T, int E, int k) {
+    // per-block expert histograms of the multi-workgroup permutation
+    const long n = (long)T * k;
+    return (size_t)((n + kPermBlock - 1) / kPermBlock) * (size_t)E * 4;
+}
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,
-                        int32_t* sorted_assign, int32_t* assign_pos, void*, hipStream_t s) {
+                        int32_t* sorted_assign, int32_t* assign_pos, void* ws_v, hipStream_t s) {
+    int32_t* ws = static_cast<int32_t*>(ws_v);
     const int vpl = ceil_div(E, kWave);
-    if (vpl <= 1) return launch_route_vpl<1>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, s);
-    if (vpl <= 2) return launch_route_vpl<2>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, s);
-    if (vpl <= 4) return launch_route_vpl<4>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, s);
-    if (vpl <= 8) return launch_route_vpl<8>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, s);
-    return launch_route_vpl<16>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, s);
+    if (vpl <= 1) return launch_route_vpl<1>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, ws, s);
+    if (vpl <= 2) return launch_route_vpl<2>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, ws, s);
+    if (vpl <= 4) return launch_route_vpl<4>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, ws, s);
+    if (vpl <= 8) return launch_route_vpl<8>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, ws, s);
+    return launch_route_vpl<16>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, ws, s);
 }
 
 }  // namespace moe
