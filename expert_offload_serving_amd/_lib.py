@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_slice_bank.restype = _i
         L.moe_nvfp4_slice_bank.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp]
         L.moe_nvfp4_dequant.restype = _i
-        L.moe_nvfp4_dequant.argtypes = [_vp, _vp, _vp, _i, _i, _vp, _vp]
+        L.moe_nvfp4_dequant.argtypes = [_vp, _i, _i, _i, _vp, _vp]
         _lib = L
     return _lib
 
@@ -151,8 +151,8 @@ def moe_nvfp4_slice_bank(src_bank, num_slots, H, I, r, n, dst_bank, stream=None)
     return lib().moe_nvfp4_slice_bank(_ptr(src_bank), num_slots, H, I, r, n, _ptr(dst_bank), _stream(stream))
 
 
-def moe_nvfp4_dequant(codes, scales, globals_, rows, K, out, stream=None) -> int:
-    return lib().moe_nvfp4_dequant(_ptr(codes), _ptr(scales), _ptr(globals_), rows, K, _ptr(out), _stream(stream))
+def moe_nvfp4_dequant(slot, H, I, matrix, out, stream=None) -> int:
+    return lib().moe_nvfp4_dequant(_ptr(slot), H, I, matrix, _ptr(out), _stream(stream))
 
 
 class ExpertCache:

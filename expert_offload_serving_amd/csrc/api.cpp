@@ -49,7 +49,8 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool shape_ok(int H, int I) { return H > 0 && I > 0 && H % 32 == 0 && I % 32 == 0; }
+// The slot format's tile: H % 128 == 0, I % 32 == 0 (the fp4 scale-block guard of issue #62).
+bool shape_ok(int H, int I) { return H > 0 && I > 0 && H % 128 == 0 && I % 32 == 0; }
 
 int check_route_shape(int T, int E, int k) {
     if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 (got %d)", T);
@@ -104,7 +105,8 @@ int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, 
     if (!layer) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_nvfp4_forward: layer is NULL");
     const moe_nvfp4_layer_t& L = *layer;
     if (!shape_ok(L.H, L.I))
-        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H and I must be positive multiples of 32 (got H=%d, I=%d)", L.H, L.I);
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H must be a positive multiple of 128 and I of 32 (got H=%d, I=%d)",
+                    L.H, L.I);
     int rc = check_route_shape(T, L.E, L.k);
     if (rc != MOE_OK) return rc;
     if (accumulate != 0 && accumulate != 1) return fail(MOE_ERR_INVALID_ARGUMENT, "accumulate must be 0 or 1");
@@ -131,9 +133,7 @@ int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, 
     moe::Layer ml{L.H, L.I, L.E, L.k, static_cast<const uint8_t*>(L.bank_base), L.slot_bytes, L.slot_of_expert,
                   static_cast<const uint8_t*>(L.shared_slot), L.shared_gate_w};
     hipError_t e;
-    if (T <= moe::kDecodeMaxT) {
-        if (!moe::decode_shape_supported(L.H, L.I))
-            return fail(MOE_ERR_UNSUPPORTED_SHAPE, "decode path does not support H=%d, I=%d", L.H, L.I);
+    if (moe::decode_path(T, L.H, L.I)) {
         e = moe::launch_decode(ml, x, T, topk_w, topk_ids, expert_offsets, sorted_assign, assign_pos, y, accumulate,
                                ws, stream);
     } else {
@@ -179,7 +179,8 @@ int expert_cache_fill(void* cache_base, size_t slot_bytes, int num_slots, const 
 
 int moe_nvfp4_slice_bank(const void* src_bank, int num_slots, int H, int I, int r, int n, void* dst_bank,
                          hipStream_t stream) {
-    if (!shape_ok(H, I)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H and I must be positive multiples of 32");
+    if (!shape_ok(H, I))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H must be a positive multiple of 128 and I of 32");
     if (n < 1 || r < 0 || r >= n || I % n != 0 || (I / n) % 32 != 0)
         return fail(MOE_ERR_UNSUPPORTED_SHAPE, "slice %d of %d: I/n must be a multiple of 32 (I=%d)", r, n, I);
     if (num_slots < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_slots must be >= 0");
@@ -191,13 +192,14 @@ int moe_nvfp4_slice_bank(const void* src_bank, int num_slots, int H, int I, int 
     return MOE_OK;
 }
 
-int moe_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* globals, int rows, int K,
-                      float* out, hipStream_t stream) {
-    if (rows < 0 || K <= 0 || K % 32 != 0)
-        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "dequant needs rows >= 0 and K a positive multiple of 32");
-    if (rows == 0) return MOE_OK;
-    if (!codes || !scales || !globals || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
-    hipError_t e = moe::launch_dequant(codes, scales, globals, rows, K, out, stream);
+int moe_nvfp4_dequant(const void* slot, int H, int I, int matrix, float* out, hipStream_t stream) {
+    if (!shape_ok(H, I))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H must be a positive multiple of 128 and I of 32");
+    if (matrix != 0 && matrix != 1) return fail(MOE_ERR_INVALID_ARGUMENT, "matrix must be 0 (gate_up) or 1 (down)");
+    if (!slot || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (reinterpret_cast<uintptr_t>(slot) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "slot and out must be 16-byte aligned");
+    hipError_t e = moe::launch_dequant(static_cast<const uint8_t*>(slot), H, I, matrix, out, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_dequant launch");
     return MOE_OK;
 }

@@ -1,40 +1,40 @@
 // Decode path (T <= 16) of the NVFP4 routed-MoE layer for gfx950.
 //
-// The layer (PR #385 "What this adds"; issue #62 "What it touches"):
-//   h = silu(W_gate x) * (W_up x)   with gate rows [0, I) and up rows [I, 2I) of gate_up [2I, H]
-//   o = W_dn h                      with down [H, I]
-//   y_t = sum_j w_tj o_{e_tj}(x_t) + sigmoid(x_t . w_g) o_shared(x_t)
-// At decode batch sizes this is a set of GEMVs over the distinct routed
-// experts, bound by the HBM bytes of their NVFP4 weights.  Three kernels:
+// The expert FFN is cut along the intermediate axis, exactly as the pages cut
+// it across GPUs (issue #62 "The fix that fits": a slice of I turns gate_up
+// into a row range and down into a column range whose outputs are partial
+// sums).  One work item is (expert, 32-row slice of I):
+//   phase A  gate rows and up rows of the slice against the expert's tokens
+//            (K = H), reduced across the workgroup's waves, SwiGLU;
+//   phase B  the down columns of the slice against the 32 hidden values,
+//            giving a partial sum over all H outputs, times the routing weight.
+// Both phases stream their weights with one 16-byte load per lane per record,
+// and the down records are in flight while phase A computes, so one kernel
+// moves all of an item's bytes.  A second kernel adds the partial outputs of
+// every (expert, slice) of a token in a fixed order and the shared expert's
+// sigmoid-gated term (PR #385 "What this adds": routed + sigmoid(gate) *
+// shared before one reduction).
 //
-// gate_up: one workgroup per (active expert, block of gate rows).  Each wave
-//   owns RW gate rows and the RW matching up rows; LPR lanes share a row and
-//   each owns CPL 16-byte code chunks (32 elements, two scale blocks), so
-//   every load instruction reads whole row segments with 128-bit loads and a
-//   lane's activation chunks serve the gate pass and the up pass.  Codes are
-//   decoded to bf16 (exact) and dotted with the bf16 activations by v_dot2c
-//   (exact products, f32 sums); each 16-block's sum is scaled by its E4M3
-//   scale, the lanes of a row are reduced with cross-lane shuffles, the row
-//   globals are applied, and silu(gate) * up is written as the fp32 hidden
-//   state of that (token, expert) assignment.  The shared expert's first
-//   block also computes the shared gate sigmoid(x_t . w_g).
-//
-// down: one workgroup per (active expert, block of output rows).  CPR = I/32
-//   lanes share a row (one 16-byte chunk each) and keep their 32-element
-//   slice of the fp32 hidden state in registers across the rows they
-//   process; the row sum is a segmented shuffle reduction.  Outputs go to a
-//   per-assignment buffer.
-//
-// combine: y_t = sum_j w_tj o_tj + s_t o_shared, summed in a fixed order, so
-//   results are bit-reproducible.  Each kernel's inputs were completed by the
-//   previous launch, so no workgroup ever waits on another.
+// Arithmetic: v_mfma_f32_16x16x32_f16 with the weights as the 16-row operand
+// and up to 16 tokens as the 16 columns.  Weights decode exactly to fp16
+// (frag_f16).  Activations enter as fp16 times a power of two per (wave,
+// token) that puts the wave's largest magnitude in [2^14, 2^15), so the
+// bf16 -> fp16 conversion is exact in the fp16 normal range; the scale is
+// undone exactly on the fp32 result.  The hidden slice is rescaled the same
+// way before phase B.  Accumulation is fp32 and every sum runs in a fixed
+// order, so results are bit-reproducible.
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
 namespace moe {
 namespace {
 
-struct DecodeArgs {
+constexpr int kDW = 8;              // waves per work item
+constexpr int kDT = kDW * kWave;    // threads per work item
+constexpr int kSl = 32;             // intermediate rows per work item
+constexpr int kMaxChunks = 16;      // E <= 1024 experts, 64 per ballot
+
+struct DecArgs {
     const uint8_t* bank;
     size_t slot_bytes;
     const int32_t* slot_of_expert;
@@ -43,419 +43,338 @@ struct DecodeArgs {
     const uint16_t* x;
     int T, H, I, E, k;
     const float* w;
-    const int32_t* ids;
     const int32_t* offsets;
     const int32_t* sorted_assign;
-    const int32_t* assign_pos;
-    float* hbuf;    // f32 [(T*k + T), I]: row p = sorted assignment p; row T*k + t = shared expert, token t
-    float* obuf;    // f32 [(T*k + T), H]: expert outputs, same row order
-    float* sbuf;    // f32 [T]: shared gate sigmoid(x_t . w_g)
+    float* part;   // [(T*k + T) * nsl, H]: row (assignment or T*k + token) * nsl + slice
     float* y;
     int accumulate;
     size_t gu_codes, gu_scales, gu_glob, dn_codes, dn_scales, dn_glob;
 };
 
-__device__ __forceinline__ uint64_t lanes_below(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
-
-// The workgroup's expert: the ai-th active routed expert in ascending order
-// (count > 0 and a slot), then the shared expert (returned as E).  One pass of
-// parallel loads of the offsets and the slot map; the winner publishes
-// (expert, slot, first sorted row, token count) through LDS.
-struct ExpertInfo {
-    int e, slot, p0, ne, n_total;
+struct ItemExpert {
+    int e;       // expert, E for the shared expert, -1 for no work
+    int begin;   // first position in sorted_assign (routed experts)
+    int count;   // assignments of the expert
 };
 
-template <int NT>
-__device__ ExpertInfo find_expert(const DecodeArgs& a, int ai, int* sh /* LDS, >= NT/64 + 5 ints */) {
-    constexpr int NW = NT / kWave;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    if (tid == 0) sh[NW] = -1;
-    int base = 0;
-    for (int e0 = 0; e0 < a.E; e0 += NT) {
-        const int e = e0 + tid;
-        int o0 = 0, o1 = 0, sl = -1;
-        if (e < a.E) {
-            o0 = a.offsets[e];
-            o1 = a.offsets[e + 1];
-            sl = a.slot_of_expert[e];
-        }
-        const bool act = e < a.E && o1 > o0 && sl >= 0;
-        const uint64_t m = __ballot(act);
-        if (lane == 0) sh[wave] = __popcll(m);
-        __syncthreads();
-        int before = 0, tot = 0;
+// Item u -> the u-th expert (ascending) that has assignments; u equal to the
+// number of such experts is the shared expert.  All lanes agree.
+__device__ ItemExpert item_expert(const DecArgs& a, int u, int lane) {
+    int lo[kMaxChunks], hi[kMaxChunks];
 #pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            const int c = sh[i];
-            before += i < wave ? c : 0;
-            tot += c;
-        }
-        if (act && base + before + __popcll(m & lanes_below(lane)) == ai) {
-            sh[NW] = e;
-            sh[NW + 1] = sl;
-            sh[NW + 2] = o0;
-            sh[NW + 3] = o1 - o0;
-        }
-        base += tot;
-        __syncthreads();
+    for (int c = 0; c < kMaxChunks; ++c) {
+        const int e = 64 * c + lane;
+        lo[c] = e < a.E ? a.offsets[e] : 0;
+        hi[c] = e < a.E ? a.offsets[e + 1] : 0;
     }
-    ExpertInfo r;
-    const bool has_shared = a.shared != nullptr;
-    r.n_total = __builtin_amdgcn_readfirstlane(base) + (has_shared ? 1 : 0);
-    r.e = __builtin_amdgcn_readfirstlane(sh[NW]);
-    if (r.e >= 0) {
-        r.slot = __builtin_amdgcn_readfirstlane(sh[NW + 1]);
-        r.p0 = __builtin_amdgcn_readfirstlane(sh[NW + 2]);
-        r.ne = __builtin_amdgcn_readfirstlane(sh[NW + 3]);
-    } else if (has_shared && ai == r.n_total - 1) {
-        r.e = a.E;
-        r.slot = -1;
-        r.p0 = a.T * a.k;
-        r.ne = a.T;
-    } else {
-        r.slot = -1;
-        r.p0 = 0;
-        r.ne = 0;
+    ItemExpert r{-1, 0, 0};
+    int base = 0;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        const bool act = hi[c] > lo[c];
+        const uint64_t m = __ballot(act);
+        const int n = __popcll(m);
+        if (r.e < 0 && u < base + n) {
+            const uint64_t hit = __ballot(act && __popcll(m & below) == u - base);
+            const int li = __ffsll((unsigned long long)hit) - 1;
+            r.e = 64 * c + li;
+            r.begin = __builtin_amdgcn_readlane(lo[c], li);
+            r.count = __builtin_amdgcn_readlane(hi[c], li) - r.begin;
+        }
+        base += n;
     }
+    if (r.e < 0 && u == base) r.e = a.E;
     return r;
 }
 
-__device__ __forceinline__ const uint8_t* slot_ptr(const DecodeArgs& a, const ExpertInfo& x) {
-    return x.e == a.E ? a.shared : a.bank + (size_t)x.slot * a.slot_bytes;
-}
+// One work item per workgroup.  KQW: most 128-column steps of K = H per wave
+// (steps wave, wave + 8, ...); NRGW: most 64-row down groups per wave.
+template <int KQW, int NRGW>
+__global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
+    __shared__ __attribute__((aligned(16))) f32x4_t red[kDW][4][kWave];
+    __shared__ float hmax[kDW][16];
+    __shared__ __attribute__((aligned(16))) _Float16 hs[16][kSl];
 
-// ------------------------------------------------------------------ gate_up + SwiGLU
-// Dynamic LDS: two activation rows of H bf16 (double-buffered over tokens).
-template <int CPL, int LPR>
-__global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a, int NB) {
-    constexpr int RW = kWave / LPR;  // gate rows (and up rows) per wave
-    constexpr int RG = 4 * RW;       // gate rows per workgroup
-    __shared__ int sh[16];
-    __shared__ int tok[kDecodeMaxT];
-    __shared__ float red[4];
-    extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
-
-    const int ai = blockIdx.x / NB, nb = blockIdx.x % NB;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int u = blockIdx.x / nsl, s = blockIdx.x % nsl;
     const int H = a.H, I = a.I, T = a.T, k = a.k;
-    const int nvec = H / 8;  // 16-byte vectors per activation row
-    auto stage_x = [&](int t, int buf) {
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * H);
-        u32x4_t* dst = reinterpret_cast<u32x4_t*>(xlds + (size_t)buf * H * 2);
-        for (int v = tid; v < nvec; v += 256) dst[v] = src[v];
-    };
-        if (T == 1) stage_x(0, 0);  // the only token: no need to wait for the plan
-    const ExpertInfo ex = find_expert<256>(a, ai, sh);
-    if (ex.e < 0) return;
-    const uint8_t* slot = slot_ptr(a, ex);
-    const bool is_shared = ex.e == a.E;
-    // A token routes to an expert at most once, so ne <= T <= 16; the clamp
-    // only guards the LDS arrays against routing not made by moe_route_topk.
-    const int ne = min(ex.ne, kDecodeMaxT), p0 = ex.p0;
+    const ItemExpert it = item_expert(a, u, lane);
+    if (it.e < 0 || (it.e == a.E && a.shared == nullptr)) return;  // uniform
 
-    const int lir = lane % LPR, rsub = lane / LPR;
-    const int i = nb * RG + wave * RW + rsub;  // gate row; its up row is I + i
-    const bool valid = i < I;
-    const int ig = valid ? i : 0;
-    const uint8_t* gcodes = slot + a.gu_codes + (size_t)ig * (H / 2);
-    const uint8_t* ucodes = slot + a.gu_codes + (size_t)(I + ig) * (H / 2);
-    const uint8_t* gsc = slot + a.gu_scales + (size_t)ig * (H / 16);
-    const uint8_t* usc = slot + a.gu_scales + (size_t)(I + ig) * (H / 16);
-    const float* glob = reinterpret_cast<const float*>(slot + a.gu_glob);
-
-    u32x4_t cg[CPL], cu[CPL];
-    uint32_t sg[CPL], su[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int c = lir + LPR * j;
-        cg[j] = *reinterpret_cast<const u32x4_t*>(gcodes + c * 16);
-        cu[j] = *reinterpret_cast<const u32x4_t*>(ucodes + c * 16);
-        sg[j] = *reinterpret_cast<const uint16_t*>(gsc + c * 2);
-        su[j] = *reinterpret_cast<const uint16_t*>(usc + c * 2);
-    }
-    const float g_gate = glob[ig], g_up = glob[I + ig];
-    if (tid < ne) tok[tid] = (is_shared || T == 1) ? tid : a.sorted_assign[p0 + tid] / k;
-
-    // Shared gate s_t = sigmoid(x_t . w_g): the first block of the shared expert
-    // dots each staged activation row with w_g (16-byte vectors, block reduction).
-    const bool do_gate = is_shared && nb == 0;
-    u32x4_t wgv[4];
-    const int nvec_wg = H / 8;  // <= 1024 for H <= 8192
-    if (do_gate) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int v = tid + 256 * q;
-            wgv[q] = v < nvec_wg ? reinterpret_cast<const u32x4_t*>(a.wg)[v] : u32x4_t{0, 0, 0, 0};
+    // Column c of the MFMA is the item's c-th token.
+    const int c = lane & 15, g = lane >> 4;
+    int ne, tok = -1, prow = 0;
+    float wc = 0.0f;
+    const uint8_t* slot;
+    if (it.e < a.E) {
+        ne = it.count;
+        if (c < ne) {
+            const int as = a.sorted_assign[it.begin + c];
+            tok = as / k;
+            prow = as;
+            wc = a.w[as];
         }
+        const int sl = __builtin_amdgcn_readfirstlane(a.slot_of_expert[it.e]);
+        slot = sl >= 0 ? a.bank + (size_t)sl * a.slot_bytes : nullptr;
+    } else {
+        ne = T;
+        if (c < ne) tok = c, prow = T * k + c, wc = 1.0f;
+        slot = a.shared;
+    }
+    float* prow_ptr = a.part + ((size_t)prow * nsl + s) * H;
+
+    if (slot == nullptr) {  // expert left out of this call: its partial outputs are zero
+        for (int cc = 0; cc < ne; ++cc) {
+            const int pr = a.sorted_assign[it.begin + cc];
+            f32x4_t* dst = reinterpret_cast<f32x4_t*>(a.part + ((size_t)pr * nsl + s) * H);
+            for (int v = tid; v < H / 4; v += kDT) dst[v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        return;
+    }
+
+    const int KQ = H / 128, NT = 2 * I / 16, NG = H / 64;
+    const rsrc_t xres = make_rsrc(a.x, (uint32_t)T * H * 2);
+    const rsrc_t sres = make_rsrc(slot, (uint32_t)a.slot_bytes);
+    const int gcodes = (int)a.gu_codes, gscales = (int)a.gu_scales, gglob = (int)a.gu_glob;
+    const int dcodes = (int)a.dn_codes, dscales = (int)a.dn_scales, dglob = (int)a.dn_glob;
+    const int tiles[4] = {2 * s, 2 * s + 1, I / 16 + 2 * s, I / 16 + 2 * s + 1};  // gate, gate, up, up
+    const int soff = lane_scale_off(lane);
+
+    // ---- issue every load of the item in one straight line: activations
+    // first, then gate_up records, then down records (absent ones read as 0)
+    u32x4_t xr[KQW][4];
+#pragma unroll
+    for (int i = 0; i < KQW; ++i) {
+        const int kq = wave + kDW * i;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            xr[i][m] = buf_load16(xres, (kq < KQ && tok >= 0) ? 2 * (tok * H + 128 * kq + 32 * m + 8 * g) : kOob);
+    }
+    u32x4_t ar[KQW][4];
+    uint32_t asc[KQW][4];
+#pragma unroll
+    for (int i = 0; i < KQW; ++i) {
+        const int kq = wave + kDW * i;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int rec = kq * NT + tiles[tt];
+            ar[i][tt] = buf_load16(sres, kq < KQ ? gcodes + rec * kRecBytes + 16 * lane : kOob);
+            asc[i][tt] = buf_load4(sres, kq < KQ ? gscales + rec * kRecScaleBytes + soff : kOob);
+        }
+    }
+    u32x4_t br[NRGW];
+    uint32_t bsc[NRGW];
+#pragma unroll
+    for (int i = 0; i < NRGW; ++i) {
+        const int rg = wave + kDW * i;
+        const int rec = s * NG + rg;
+        br[i] = buf_load16(sres, rg < NG ? dcodes + rec * kRecBytes + 16 * lane : kOob);
+        bsc[i] = buf_load4(sres, rg < NG ? dscales + rec * kRecScaleBytes + soff : kOob);
+    }
+    // SwiGLU thread (hi, ht): hidden row hi of the slice, token column ht
+    const int hi = tid >> 4, ht = tid & 15;
+    const float g_glob = __uint_as_float(buf_load4(sres, gglob + 4 * (kSl * s + hi)));
+    const float u_glob = __uint_as_float(buf_load4(sres, gglob + 4 * (I + kSl * s + hi)));
+    // keep the scheduler from sinking loads towards their uses: all of them
+    // must be in flight before the first wait
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- activations: per-(wave, token) power-of-two scale, exact fp16
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KQW; ++i)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t wv = word_of(xr[i][m], d);
+                amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(wv << 16)), fabsf(__uint_as_float(wv & 0xFFFF0000u))));
+            }
+    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    const int xsh = fp16_shift(amax);
+    const float xsc = ldexpf(1.0f, xsh), xinv = ldexpf(1.0f, -xsh);
+
+    // ---- phase A: gate and up rows of the slice, this wave's share of K
+    f32x4_t acc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < KQW; ++i) {
+        if (wave + kDW * i >= KQ) break;  // uniform per wave
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            uint32_t xh[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t wv = word_of(xr[i][m], d);
+                const f16x2_t p = {(_Float16)(__uint_as_float(wv << 16) * xsc),
+                                   (_Float16)(__uint_as_float(wv & 0xFFFF0000u) * xsc)};
+                xh[d] = __builtin_bit_cast(uint32_t, p);
+            }
+            const f16x8_t X = __builtin_bit_cast(f16x8_t, u32x4_t{xh[0], xh[1], xh[2], xh[3]});
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                f16x2_t S;
+                if (m == 0) S = scale_f16x2<0>(asc[i][tt]);
+                else if (m == 1) S = scale_f16x2<1>(asc[i][tt]);
+                else if (m == 2) S = scale_f16x2<2>(asc[i][tt]);
+                else S = scale_f16x2<3>(asc[i][tt]);
+                const f16x8_t A = frag_f16(word_of(ar[i][tt], m), S);
+                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, X, acc[tt], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) red[wave][tt][lane] = acc[tt] * xinv;
+
+    // down globals of this wave's output rows (lane rows 16j + 4g + [0, 4) of each group)
+    f32x4_t dg[NRGW][4];
+#pragma unroll
+    for (int i = 0; i < NRGW; ++i) {
+        const int rg = wave + kDW * i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            dg[i][j] = __builtin_bit_cast(f32x4_t, buf_load16(sres, rg < NG ? dglob + 4 * (64 * rg + 16 * j + 4 * g)
+                                                                          : kOob));
     }
     __syncthreads();
-    if (T > 1) stage_x(tok[0], 0);
-    for (int ti = 0; ti < ne; ++ti) {
-        __syncthreads();
-        if (ti + 1 < ne) stage_x(tok[ti + 1], (ti + 1) & 1);
-        const uint8_t* xb = xlds + (size_t)(ti & 1) * H * 2;
-        if (do_gate) {
-            float d = 0.0f;
-            #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int v = tid + 256 * q;
-                if (v < nvec_wg) {
-                    const u32x4_t xv = reinterpret_cast<const u32x4_t*>(xb)[v];
-                    const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-                    const uint32_t ws[4] = {wgv[q].x, wgv[q].y, wgv[q].z, wgv[q].w};
+
+    // ---- SwiGLU: thread (hi, ht) sums its gate and up values over the waves in order
+    float hv;
+    {
+        const int tt = hi >> 4, r = hi & 15, L = 16 * (r >> 2) + ht, ii = r & 3;
+        float gs = 0.0f, us = 0.0f;
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) d = dot2_bf16(as_bf16x2(xs[m]), as_bf16x2(ws[m]), d);
-                }
-            }
-            d = wave_sum(d);
-            if (lane == 0) red[wave] = d;
+        for (int w = 0; w < kDW; ++w) {
+            gs += red[w][tt][L][ii];
+            us += red[w][2 + tt][L][ii];
         }
-        float accg = 0.0f, accu = 0.0f;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int c = lir + LPR * j;
-            const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xb + c * 64);
-            uint32_t xw[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4_t v = xp[q];
-                xw[4 * q + 0] = v.x; xw[4 * q + 1] = v.y; xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
-            }
-            accg += e4m3_f32<0>(sg[j]) * block16_dot_bf16(cg[j].x, cg[j].y, xw) +
-                    e4m3_f32<1>(sg[j]) * block16_dot_bf16(cg[j].z, cg[j].w, xw + 8);
-            accu += e4m3_f32<0>(su[j]) * block16_dot_bf16(cu[j].x, cu[j].y, xw) +
-                    e4m3_f32<1>(su[j]) * block16_dot_bf16(cu[j].z, cu[j].w, xw + 8);
-        }
-        accg = group_sum<LPR>(accg);
-        accu = group_sum<LPR>(accu);
-        if (lir == 0 && valid) {
-            const float gate = accg * g_gate, up = accu * g_up;
-            a.hbuf[(size_t)(p0 + ti) * I + i] = gate * sigmoidf_(gate) * up;
-        }
-        if (do_gate) {
-            __syncthreads();
-            if (tid == 0) a.sbuf[ti] = sigmoidf_(red[0] + red[1] + red[2] + red[3]);
-        }
+        const float gv = gs * g_glob, uv = us * u_glob;
+        hv = gv / (1.0f + expf(-gv)) * uv;
+        float hm = fabsf(hv);
+        hm = fmaxf(hm, __shfl_xor(hm, 16, kWave));
+        hm = fmaxf(hm, __shfl_xor(hm, 32, kWave));
+        if (lane < 16) hmax[wave][lane] = hm;
     }
-}
-
-// ------------------------------------------------------------------ down + combine
-constexpr int kDownPW = 4;  // row passes per wave
-
-// Segmented sum over the LEN consecutive lanes of a segment (c = lane index
-// inside the segment, segments start at multiples of LEN); the total ends in
-// the lane with c == 0.  Lanes only add values from their own segment.
-template <int LEN>
-__device__ __forceinline__ float segment_sum(float v, int c) {
-    int len = LEN;
-#pragma unroll
-    for (int it = 0; it < 7; ++it) {
-        if (len <= 1) break;
-        const int half = (len + 1) / 2;
-        const float other = __shfl_down(v, half, kWave);
-        if (c + half < len) v += other;
-        len = half;
-    }
-    return v;
-}
-
-// One workgroup = one active expert x RBD output rows.  CPR = I/32 lanes per
-// row, RPP = 64/CPR rows per pass, kDownPW passes per wave, 4 waves.
-template <int CPR>
-__global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a, int NB) {
-    constexpr int RPP = kWave / CPR;
-    constexpr int RBD = RPP * kDownPW * 4;
-    __shared__ int sh[16];
-    const int ai = blockIdx.x / NB, rb = blockIdx.x % NB;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int H = a.H, I = a.I;
-    const int r0 = rb * RBD;
-    const int g = lane / CPR, c = lane % CPR;
-    const bool lane_on = g < RPP;
-    const ExpertInfo ex = find_expert<256>(a, ai, sh);
-
-    if (ex.e >= 0) {
-        const uint8_t* slot = slot_ptr(a, ex);
-        const float* dglob = reinterpret_cast<const float*>(slot + a.dn_glob);
-        u32x4_t cw[kDownPW];
-        uint32_t sc[kDownPW];
-        float grow[kDownPW];
-        int rows[kDownPW];
-#pragma unroll
-        for (int q = 0; q < kDownPW; ++q) {
-            const int row = r0 + (q * 4 + wave) * RPP + g;
-            rows[q] = (lane_on && row < H) ? row : -1;
-            const int rr = rows[q] < 0 ? 0 : rows[q];
-            cw[q] = *reinterpret_cast<const u32x4_t*>(slot + a.dn_codes + (size_t)rr * (I / 2) + c * 16);
-            sc[q] = *reinterpret_cast<const uint16_t*>(slot + a.dn_scales + (size_t)rr * (I / 16) + c * 2);
-            grow[q] = dglob[rr];
-        }
-        for (int ti = 0; ti < ex.ne; ++ti) {
-            const int p = ex.p0 + ti;
-            const f32x4_t* hp = reinterpret_cast<const f32x4_t*>(a.hbuf + (size_t)p * I + c * 32);
-            f32x4_t h[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) h[q] = hp[q];
-#pragma unroll
-            for (int q = 0; q < kDownPW; ++q) {
-                const uint32_t words[4] = {cw[q].x, cw[q].y, cw[q].z, cw[q].w};
-                float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-                for (int wd = 0; wd < 4; ++wd) {
-                    const f32x2_t v0 = e2m1x2_f32<0>(words[wd]), v1 = e2m1x2_f32<1>(words[wd]);
-                    const f32x2_t v2 = e2m1x2_f32<2>(words[wd]), v3 = e2m1x2_f32<3>(words[wd]);
-                    const f32x4_t ha = h[2 * wd], hb = h[2 * wd + 1];
-                    float s = v0.x * ha.x;
-                    s += v0.y * ha.y;
-                    s += v1.x * ha.z;
-                    s += v1.y * ha.w;
-                    s += v2.x * hb.x;
-                    s += v2.y * hb.y;
-                    s += v3.x * hb.z;
-                    s += v3.y * hb.w;
-                    if (wd < 2) lo += s; else hi += s;
-                }
-                const float part = e4m3_f32<0>(sc[q]) * lo + e4m3_f32<1>(sc[q]) * hi;
-                const float sum = segment_sum<CPR>(part, c);
-                if (c == 0 && rows[q] >= 0) a.obuf[(size_t)p * H + rows[q]] = sum * grow[q];
-            }
-        }
-    }
-}
-
-// y_t (=|+=) sum_j w_tj o[pos(t,j)] + s_t o[shared row t], summed in a fixed
-// order (j ascending, then the shared expert).  One workgroup per (token,
-// 256 output rows); the token's routing and the slot map are staged in LDS.
-constexpr int kCombineMaxK = 1024;
-
-__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a, int nchunk) {
-    __shared__ int pos_s[kCombineMaxK];
-    __shared__ float w_s[kCombineMaxK];
-    const int t = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
-    const int tid = threadIdx.x;
-    const int H = a.H, T = a.T, k = a.k;
-    for (int j = tid; j < k; j += 256) {
-        const int aidx = t * k + j;
-        const bool ok = a.slot_of_expert[a.ids[aidx]] >= 0;
-        pos_s[j] = ok ? a.assign_pos[aidx] : -1;
-        w_s[j] = a.w[aidx];
-    }
-    const float st = a.shared != nullptr ? a.sbuf[t] : 0.0f;
     __syncthreads();
-    const int row = chunk * 256 + tid;
-    if (row >= H) return;
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        const int p = pos_s[j];
-        if (p >= 0) acc += w_s[j] * a.obuf[(size_t)p * H + row];
+    float hm_t = 0.0f, hm_c = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDW; ++w) hm_t = fmaxf(hm_t, hmax[w][ht]), hm_c = fmaxf(hm_c, hmax[w][c]);
+    hs[ht][hi] = (_Float16)(hv * ldexpf(1.0f, fp16_shift(hm_t)));
+    __syncthreads();
+
+    // ---- phase B: the slice's 32 down columns for this wave's row groups
+    const f16x8_t B = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(&hs[c][8 * g]));
+    const float oscale = ldexpf(1.0f, -fp16_shift(hm_c)) * wc;
+#pragma unroll
+    for (int i = 0; i < NRGW; ++i) {
+        const int rg = wave + kDW * i;
+        if (rg >= NG) break;  // uniform per wave
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f16x2_t S;
+            if (j == 0) S = scale_f16x2<0>(bsc[i]);
+            else if (j == 1) S = scale_f16x2<1>(bsc[i]);
+            else if (j == 2) S = scale_f16x2<2>(bsc[i]);
+            else S = scale_f16x2<3>(bsc[i]);
+            const f16x8_t A = frag_f16(word_of(br[i], j), S);
+            const f32x4_t D =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            if (c < ne) {
+                const f32x4_t o = (D * oscale) * dg[i][j];
+                *reinterpret_cast<f32x4_t*>(prow_ptr + 64 * rg + 16 * j + 4 * g) = o;
+            }
+        }
     }
-    if (a.shared != nullptr) acc += st * a.obuf[(size_t)(T * k + t) * H + row];
-    float* yp = a.y + (size_t)t * H + row;
-    *yp = a.accumulate ? *yp + acc : acc;
 }
 
-struct GateupCfg {
-    int cpl, lpr;
-};
-
-GateupCfg gateup_cfg(int H) {
-    const int cpr = H / 32;
-    int lpr = 1;
-    while (lpr < 64 && cpr % (lpr * 2) == 0) lpr *= 2;
-    return {cpr / lpr, lpr};
-}
-
-template <int CPL>
-hipError_t launch_gateup_cpl(int lpr, const DecodeArgs& a, int nb, int grid, hipStream_t s) {
-    const size_t lds = (size_t)2 * a.H * 2;
-    switch (lpr) {
-#define CASE(L)                                                                                      \
-    case L:                                                                                          \
-        hipLaunchKernelGGL((decode_gateup_kernel<CPL, L>), dim3(grid), dim3(256), lds, s, a, nb);    \
-        return hipGetLastError();
-        CASE(1) CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
-#undef CASE
+// y_t = sum over (j, slice) of the routed partials of token t, plus
+// sigmoid(x_t . w_g) times the shared expert's partials, in a fixed order.
+// Workgroup: one token and 64 output columns; thread (q, cl) sums partial
+// rows q, q + 16, ... of columns [4 cl, 4 cl + 4).
+__global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int nch) {
+    __shared__ f32x4_t rr[16][16], rsh[16][16];
+    __shared__ float dots[4];
+    const int t = blockIdx.x / nch, ch = blockIdx.x % nch;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, cl = tid & 15, q = tid >> 4;
+    const int H = a.H, k = a.k, T = a.T;
+    const int col = 64 * ch + 4 * cl;
+    const int nr = k * nsl;
+    const float* base_r = a.part + (size_t)t * k * nsl * H + col;
+    f32x4_t sr = {0.0f, 0.0f, 0.0f, 0.0f}, ss = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = q; r < nr; r += 16) sr += *reinterpret_cast<const f32x4_t*>(base_r + (size_t)r * H);
+    float gd = 0.0f;
+    if (a.shared != nullptr) {
+        const float* base_s = a.part + (size_t)(T * k + t) * nsl * H + col;
+        for (int r = q; r < nsl; r += 16) ss += *reinterpret_cast<const f32x4_t*>(base_s + (size_t)r * H);
+        const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * H);
+        const u32x4_t* wv = reinterpret_cast<const u32x4_t*>(a.wg);
+        for (int v = tid; v < H / 8; v += 256) {
+            const u32x4_t xx = xv[v], ww = wv[v];
+            gd = dot2_bf16(as_bf16x2(xx.x), as_bf16x2(ww.x), gd);
+            gd = dot2_bf16(as_bf16x2(xx.y), as_bf16x2(ww.y), gd);
+            gd = dot2_bf16(as_bf16x2(xx.z), as_bf16x2(ww.z), gd);
+            gd = dot2_bf16(as_bf16x2(xx.w), as_bf16x2(ww.w), gd);
+        }
+        gd = wave_sum(gd);
     }
-    return hipErrorInvalidValue;
+    rr[q][cl] = sr;
+    rsh[q][cl] = ss;
+    if (lane == 0) dots[wave] = gd;
+    __syncthreads();
+    if (tid >= 16) return;
+    f32x4_t tr = {0.0f, 0.0f, 0.0f, 0.0f}, ts = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tr += rr[i][tid], ts += rsh[i][tid];
+    f32x4_t out = tr;
+    if (a.shared != nullptr) out += sigmoidf_(((dots[0] + dots[1]) + dots[2]) + dots[3]) * ts;
+    f32x4_t* yp = reinterpret_cast<f32x4_t*>(a.y + (size_t)t * H + 64 * ch + 4 * tid);
+    if (a.accumulate) out += *yp;
+    *yp = out;
 }
 
-template <int CPR>
-hipError_t launch_down_cpr(const DecodeArgs& a, int na_max, hipStream_t s) {
-    constexpr int RBD = (kWave / CPR) * kDownPW * 4;
-    const int nb = ceil_div(a.H, RBD);
-    hipLaunchKernelGGL((decode_down_kernel<CPR>), dim3(max(1, na_max) * nb), dim3(256), 0, s, a, nb);
+template <int KQW, int NRGW>
+hipError_t launch_fused(const DecArgs& a, int items, int nsl, hipStream_t s) {
+    hipLaunchKernelGGL((fused_kernel<KQW, NRGW>), dim3(items * nsl), dim3(kDT), 0, s, a, nsl);
     return hipGetLastError();
-}
-
-hipError_t launch_down(const DecodeArgs& a, int na_max, hipStream_t s) {
-    switch (a.I / 32) {
-#define CASE(C) \
-    case C: return launch_down_cpr<C>(a, na_max, s);
-        CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8) CASE(9) CASE(10) CASE(11) CASE(12)
-        CASE(13) CASE(14) CASE(15) CASE(16) CASE(17) CASE(18) CASE(19) CASE(20) CASE(21) CASE(22) CASE(23) CASE(24)
-        CASE(25) CASE(26) CASE(27) CASE(28) CASE(29) CASE(30) CASE(31) CASE(32) CASE(40) CASE(48) CASE(64)
-#undef CASE
-    }
-    return hipErrorInvalidValue;
-}
-
-bool down_supported(int I) {
-    const int c = I / 32;
-    return (c >= 1 && c <= 32) || c == 40 || c == 48 || c == 64;
 }
 
 }  // namespace
 
-bool decode_shape_supported(int H, int I) {
-    GateupCfg c = gateup_cfg(H);
-    return c.cpl >= 1 && c.cpl <= 8 && down_supported(I) && H <= 8192;
-}
+// Per-wave register budget: the kernel keeps all of an item's loads in
+// flight at once, sized for H up to 3072 (larger H runs the prefill path).
+bool decode_shape_supported(int H, int I) { return H % 128 == 0 && I % kSl == 0 && H <= 3072; }
+
+size_t decode_part_bytes(int T, int H, int I, int k) { return (size_t)(T * k + T) * (I / kSl) * H * 4; }
 
 hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                          const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
                          int accumulate, void* ws, hipStream_t s) {
+    (void)ids;
+    (void)assign_pos;
     const int H = L.H, I = L.I, E = L.E, k = L.k;
-    uint8_t* p = static_cast<uint8_t*>(ws);
     const WsLayout wl = ws_layout(T, H, I, E, k);
-    DecodeArgs a;
-    a.bank = L.bank;
-    a.slot_bytes = L.slot_bytes;
-    a.slot_of_expert = L.slot_of_expert;
-    a.shared = L.shared;
-    a.wg = L.wg;
-    a.x = x;
+    DecArgs a;
+    a.bank = L.bank; a.slot_bytes = L.slot_bytes; a.slot_of_expert = L.slot_of_expert;
+    a.shared = L.shared; a.wg = L.wg; a.x = x;
     a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
-    a.w = w; a.ids = ids; a.offsets = offsets; a.sorted_assign = sorted_assign; a.assign_pos = assign_pos;
-    a.hbuf = reinterpret_cast<float*>(p + wl.h);
-    a.obuf = reinterpret_cast<float*>(p + wl.o);
-    a.sbuf = reinterpret_cast<float*>(p + wl.s);
-    a.y = y;
-    a.accumulate = accumulate;
-    SlotGeom gm = slot_geom(H, I);
+    a.w = w; a.offsets = offsets; a.sorted_assign = sorted_assign;
+    a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + wl.part);
+    a.y = y; a.accumulate = accumulate;
+    const SlotGeom gm = slot_geom(H, I);
     a.gu_codes = gm.gu_codes; a.gu_scales = gm.gu_scales; a.gu_glob = gm.gu_glob;
     a.dn_codes = gm.dn_codes; a.dn_scales = gm.dn_scales; a.dn_glob = gm.dn_glob;
 
-    const int na_max = min(E, T * k) + (L.shared ? 1 : 0);
-    GateupCfg c = gateup_cfg(H);
-    const int rg = 4 * (64 / c.lpr);
-    const int nb_gu = ceil_div(I, rg);
-    hipError_t err = hipSuccess;
-    const int grid = max(1, na_max) * nb_gu;
-    switch (c.cpl) {
-        case 1: err = launch_gateup_cpl<1>(c.lpr, a, nb_gu, grid, s); break;
-        case 2: err = launch_gateup_cpl<2>(c.lpr, a, nb_gu, grid, s); break;
-        case 3: err = launch_gateup_cpl<3>(c.lpr, a, nb_gu, grid, s); break;
-        case 4: err = launch_gateup_cpl<4>(c.lpr, a, nb_gu, grid, s); break;
-        case 5: err = launch_gateup_cpl<5>(c.lpr, a, nb_gu, grid, s); break;
-        case 6: err = launch_gateup_cpl<6>(c.lpr, a, nb_gu, grid, s); break;
-        case 7: err = launch_gateup_cpl<7>(c.lpr, a, nb_gu, grid, s); break;
-        case 8: err = launch_gateup_cpl<8>(c.lpr, a, nb_gu, grid, s); break;
-        default: return hipErrorInvalidValue;
-    }
-    if (err != hipSuccess) return err;
-    if ((err = launch_down(a, na_max, s)) != hipSuccess) return err;
-    const int nchunk = ceil_div(H, 256);
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(T * nchunk), dim3(256), 0, s, a, nchunk);
+    const int nsl = I / kSl;
+    const int items = (T * k < E ? T * k : E) + 1;
+    hipError_t e;
+    if (H <= 2560) e = launch_fused<3, 5>(a, items, nsl, s);
+    else e = launch_fused<3, 6>(a, items, nsl, s);
+    if (e != hipSuccess) return e;
+    const int nch = H / 64;
+    hipLaunchKernelGGL(dcombine_kernel, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);
     return hipGetLastError();
 }
 

@@ -30,22 +30,35 @@ struct SlotGeom {
 };
 SlotGeom slot_geom(int H, int I);
 
+// Decode path, T <= 16 (decode.hip): shapes it covers and the bytes of its
+// per-(row, slice) partial outputs.  Other shapes run the prefill path.
+constexpr int kDecodeMaxT = 16;
+bool decode_shape_supported(int H, int I);
+size_t decode_part_bytes(int T, int H, int I, int k);
+inline bool decode_path(int T, int H, int I) { return T <= kDecodeMaxT && decode_shape_supported(H, I); }
+
 // Forward workspace: byte offsets of its regions (each 256-byte aligned).
-//   h      hidden state, (T*k + T) rows of I values (f32 on the decode path, f16 on prefill)
+// The decode path uses only `part`; the prefill path uses the others:
+//   h      hidden state, (T*k + T) rows of I fp16 values
 //   o      per-assignment expert outputs, (T*k + T) rows of H f32
 //   s      shared-gate sigmoid per token, T f32
-//   x16    prefill: scaled fp16 activations [T, H]; xinv: their inverse scales [T]
-//   tiles  prefill work lists: 4 counts, then 3 classes x tile_cap (group, m0) pairs
+//   x16    scaled fp16 activations [T, H]; xinv: their inverse scales [T]
+//   tiles  work lists: 4 counts, then 3 classes x tile_cap (group, m0) pairs
 struct WsLayout {
-    size_t h, o, s, x16, xinv, tiles, total;
+    size_t part, h, o, s, x16, xinv, tiles, total;
     int tile_cap;
 };
 inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
+    WsLayout L{};
+    if (decode_path(T, H, I)) {
+        L.part = 0;
+        L.total = align256(decode_part_bytes(T, H, I, k));
+        return L;
+    }
     const size_t rows = (size_t)T * k + T;
-    WsLayout L;
     L.h = 0;
-    L.o = L.h + align256(rows * I * 4);
+    L.o = L.h + align256(rows * I * 2);
     L.s = L.o + align256(rows * H * 4);
     L.x16 = L.s + align256((size_t)T * 4);
     L.xinv = L.x16 + align256((size_t)T * H * 2);
@@ -56,9 +69,6 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
 }
 inline size_t forward_ws_bytes(int T, int H, int I, int E, int k) { return ws_layout(T, H, I, E, k).total; }
 
-// Decode path, T <= 16 (decode.hip)
-constexpr int kDecodeMaxT = 16;
-bool decode_shape_supported(int H, int I);
 hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                          const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
                          int accumulate, void* ws, hipStream_t s);
@@ -70,8 +80,7 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
                           int accumulate, void* ws, hipStream_t s);
 
 // Utilities (util.hip)
-hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* globals, int rows, int K,
-                          float* out, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* slot, int H, int I, int matrix, float* out, hipStream_t s);
 hipError_t launch_slice_bank(const uint8_t* src, int num_slots, int H, int I, int r, int n, uint8_t* dst,
                              hipStream_t s);
 

@@ -1,13 +1,22 @@
 // Device-side helpers shared by the gfx950 kernels of the NVFP4 MoE library.
 //
 // Number formats (PR #385 "What this adds": packed 4-bit codes with 16-wide
-// FP8 scale blocks and per-row fp32 globals): codes are E2M1, element 2j of
-// a row in the low nibble of byte j; scales are OCP E4M3FN.  gfx950 decodes
-// both in hardware: v_cvt_f32_fp8 follows OCP E4M3FN (all 256 bytes checked
-// exhaustively by the dequant test), and v_cvt_scalef32_pk_{f32,bf16}_fp4
-// decodes two E2M1 codes exactly when the scale operand is 1.0 (the
-// instruction only uses the scale's exponent, so block scales are applied
-// separately).
+// FP8 scale blocks and per-row fp32 globals): codes are E2M1, of two columns
+// sharing a byte the even one in the low nibble; scales are OCP E4M3FN.
+// gfx950 decodes both in hardware: v_cvt_f32_fp8 follows OCP E4M3FN (all 256
+// bytes checked exhaustively by the dequant test), and
+// v_cvt_scalef32_pk_{f32,f16,bf16}_fp4 decodes two E2M1 codes exactly when
+// the scale operand is 1.0 (the instruction only uses the scale's exponent,
+// so block scales are applied separately).
+//
+// Slot records (byte formulas in moe_nvfp4.h): a record is 1 KiB of codes
+// and 128 bytes of scales.  Lane L = 16*g + i of a wave reads the 16 code
+// bytes at 16*L (dword d = one 16x16x32 MFMA operand fragment: row i of a
+// 16-row tile, columns [8g, 8g+8) of a 32-column chunk) and the scale dword
+// at lane_scale_off(L) (byte d = the E4M3 scale of that fragment).  For
+// gate_up the dwords d of a record are four consecutive 32-column chunks of
+// one 16-row tile; for down they are four consecutive 16-row tiles of one
+// 32-column chunk.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,8 +30,61 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
+constexpr int kRecBytes = 1024;     // codes per record
+constexpr int kRecScaleBytes = 128; // scales per record
+
+__device__ __forceinline__ int lane_scale_off(int lane) { return 64 * (lane >> 5) + 4 * (lane & 15); }
+
+// Raw buffer loads (gfx9 buffer resource, stride 0): a byte offset at or past
+// the resource's size returns zeros without touching memory, so optional
+// loads need no branch and every load of a kernel stays in one straight
+// line (exact vmcnt accounting, nothing forces an early wait).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kOob = 0x7FFFFF00;  // an offset past every resource used here (< 2 GiB each)
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// E4M3 byte SEL of a scale dword as an fp16 pair (exact: E4M3 values fit fp16).
+template <int SEL>
+__device__ __forceinline__ f16x2_t scale_f16x2(uint32_t sdw) {
+    const _Float16 v = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sdw, SEL);
+    return f16x2_t{v, v};
+}
+
+// One dword of codes (8 E2M1 values, column order) times the block scale S:
+// an fp16 MFMA operand fragment.  Exact: e2m1 * e4m3 has at most 6
+// significant bits and lies within [2^-10, 2688].
+__device__ __forceinline__ f16x8_t frag_f16(uint32_t c, f16x2_t S) {
+    const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0) * S;
+    const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1) * S;
+    const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2) * S;
+    const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3) * S;
+    const u32x4_t u = {__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                       __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
+    return __builtin_bit_cast(f16x8_t, u);
+}
+
+__device__ __forceinline__ uint32_t word_of(const u32x4_t& v, int d) {
+    return d == 0 ? v.x : (d == 1 ? v.y : (d == 2 ? v.z : v.w));
+}
+
+// Power-of-two exponent that puts a row maximum amax in [2^14, 2^15) (0 for amax == 0).
+__device__ __forceinline__ int fp16_shift(float amax) {
+    int e = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &e);
+    return amax > 0.0f ? 15 - e : 0;
+}
 
 // E4M3FN byte SEL of `word` -> f32 (exact).
 template <int SEL>

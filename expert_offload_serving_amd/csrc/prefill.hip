@@ -18,10 +18,13 @@
 //    the scale exactly.
 //  - hidden state: silu(gate) * up is stored in fp16 (11-bit significand,
 //    saturated at the fp16 maximum) as the A operand of the down GEMM.
-// K is consumed in steps of 128: quarter q of the wave holds k in
-// [32q, 32q + 32) of the step, so each lane loads 16 contiguous code bytes and
-// MFMA j uses elements [8j, 8j + 8) of that slice; the activation tile in LDS
-// is read with the same permutation.
+// K is consumed in steps of 128 (four 32-column MFMA chunks).  Weight
+// fragments come straight from the slot's operand-order records: a gate_up
+// record holds one 16-row tile for all four chunks of a step, a down record
+// holds four 16-row tiles for one chunk, so each lane loads 16 bytes per
+// record and every byte feeds an MFMA.  The activation tile in LDS is read as
+// the matching operand: lane (row i, group g) takes columns [32m + 8g, +8) of
+// the step for chunk m.
 //
 //   prep:     per-token scale, fp16 activations, shared gate sigmoid(x_t . w_g)
 //   plan:     (group, m0) tiles of 128 rows plus one 32/64/128-row remainder
@@ -34,9 +37,6 @@
 
 namespace moe {
 namespace {
-
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int BK = 128;           // contraction step
 constexpr int APITCH = BK + 8;    // LDS row pitch of the activation tile, in fp16 elements
@@ -198,35 +198,16 @@ __device__ __forceinline__ f16x8_t lds_frag(const _Float16* p) {
     return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(p));
 }
 
-// 32 consecutive weights of one row (16 code bytes, 2 scale bytes) -> 16 words
-// of fp16 pairs, exact: e2m1 decoded with unit scale, times the E4M3 block scale.
-__device__ __forceinline__ void dequant32_f16(u32x4_t cw, uint32_t s16, uint32_t* out) {
-    const _Float16 s0 = (_Float16)e4m3_f32<0>(s16), s1 = (_Float16)e4m3_f32<1>(s16);
-    const f16x2_t S0 = {s0, s0}, S1 = {s1, s1};
-    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const f16x2_t S = q < 2 ? S0 : S1;
-        const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[q], 1.0f, 0) * S;
-        const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[q], 1.0f, 1) * S;
-        const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[q], 1.0f, 2) * S;
-        const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(words[q], 1.0f, 3) * S;
-        out[4 * q + 0] = __builtin_bit_cast(uint32_t, v0);
-        out[4 * q + 1] = __builtin_bit_cast(uint32_t, v1);
-        out[4 * q + 2] = __builtin_bit_cast(uint32_t, v2);
-        out[4 * q + 3] = __builtin_bit_cast(uint32_t, v3);
-    }
-}
-
-// One workgroup = one (tile, 64 h-columns) for gate_up or (tile, 128 output
+// One workgroup = one (tile, 64 h-columns) for gate_up or (tile, 64*WNW output
 // rows) for down.  4 waves as WMW (rows) x WNW (columns); each wave owns
-// MB = BM/WMW/16 row blocks and NBW column blocks of 16.
+// MB = BM/WMW/16 row blocks and NBW column blocks of 16 (for down, the four
+// tiles of one 64-row record group).
 template <int BM, bool GATEUP>
 __global__ void __launch_bounds__(256) gemm_kernel(PrefillArgs a, int cls, int n_tiles_n) {
     constexpr int WMW = BM == 32 ? 1 : 2;
     constexpr int WNW = 4 / WMW;
     constexpr int MB = BM / WMW / 16;
-    constexpr int NCOLS = GATEUP ? 64 : 128;       // h columns (gate_up) or output rows (down) per tile
+    constexpr int NCOLS = GATEUP ? 64 : 64 * WNW;  // h columns (gate_up) or output rows (down) per tile
     constexpr int CW = NCOLS / WNW;                 // columns per wave
     constexpr int NBW = GATEUP ? 2 * (CW / 16) : CW / 16;  // column blocks per wave (gate and up for gate_up)
     __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * APITCH];
@@ -256,27 +237,28 @@ __global__ void __launch_bounds__(256) gemm_kernel(PrefillArgs a, int cls, int n
         __syncthreads();
     }
 
-    // B rows of this wave: column block b of the wave -> weight row
-    const uint8_t* bcodes[NBW];
-    const uint8_t* bscales[NBW];
+    // B records of this wave.  gate_up: block b is one 16-row tile (b < NBW/2
+    // gate, then up), one record per step.  down: the wave's 64 output rows are
+    // record group p, four records (one per 32-column chunk) per step.
+    const int soff = lane_scale_off(lane);
+    const uint8_t* codes = slot + (GATEUP ? a.gu_codes : a.dn_codes);
+    const uint8_t* scales = slot + (GATEUP ? a.gu_scales : a.dn_scales);
+    int btile[NBW];
     bool bok[NBW];
+    bool gok = true;
+    int grp = 0;
+    if (GATEUP) {
 #pragma unroll
-    for (int b = 0; b < NBW; ++b) {
-        int wrow;
-        if (GATEUP) {
+        for (int b = 0; b < NBW; ++b) {
             const int half = b / (NBW / 2), cb = b % (NBW / 2);   // half 0 = gate, 1 = up
-            const int hc = nt * 64 + wn * CW + cb * 16 + l16;
-            bok[b] = hc < I;
-            wrow = half * I + (hc < I ? hc : 0);
-        } else {
-            const int oc = nt * 128 + wn * CW + b * 16 + l16;
-            bok[b] = oc < H;
-            wrow = oc < H ? oc : 0;
+            const int hc0 = nt * 64 + wn * CW + cb * 16;
+            bok[b] = hc0 < I;
+            btile[b] = half * (I / 16) + (hc0 < I ? hc0 / 16 : 0);
         }
-        bcodes[b] = slot + (GATEUP ? a.gu_codes : a.dn_codes) + (size_t)wrow * (K / 2);
-        bscales[b] = slot + (GATEUP ? a.gu_scales : a.dn_scales) + (size_t)wrow * (K / 16);
+    } else {
+        grp = (nt * NCOLS + wn * CW) / 64;
+        gok = 64 * grp < H;
     }
-
     // A tile loader: 16 threads per row, 16 bytes (8 fp16) each
     constexpr int ROWS_PER_PASS = 256 / 16;
     constexpr int APASSES = (BM + ROWS_PER_PASS - 1) / ROWS_PER_PASS;
@@ -304,20 +286,39 @@ __global__ void __launch_bounds__(256) gemm_kernel(PrefillArgs a, int cls, int n
             if (m < BM) *reinterpret_cast<u32x4_t*>(&sA[buf][m * APITCH + apiece * 8]) = areg[ps];
         }
     };
-    u32x4_t bcw[NBW];
-    uint32_t bsc[NBW];
+    u32x4_t bcw[4];
+    uint32_t bsc[4];
     auto load_b = [&](int k0) {
-        const int kc = k0 + 32 * q4;
+        const int step = k0 / BK;
 #pragma unroll
-        for (int b = 0; b < NBW; ++b) {
-            if (bok[b] && kc < K) {
-                bcw[b] = *reinterpret_cast<const u32x4_t*>(bcodes[b] + kc / 2);
-                bsc[b] = *reinterpret_cast<const uint16_t*>(bscales[b] + kc / 16);
+        for (int r = 0; r < 4; ++r) {
+            bcw[r] = u32x4_t{0, 0, 0, 0};
+            bsc[r] = 0;
+            size_t rec = 0;
+            bool ok;
+            if (GATEUP) {
+                ok = r < NBW && bok[r];
+                rec = (size_t)step * (2 * I / 16) + btile[r < NBW ? r : 0];
             } else {
-                bcw[b] = u32x4_t{0, 0, 0, 0};
-                bsc[b] = 0;
+                const int kc = 4 * step + r;
+                ok = gok && kc < I / 32;
+                rec = (size_t)kc * (H / 64) + grp;
+            }
+            if (ok) {
+                bcw[r] = *reinterpret_cast<const u32x4_t*>(codes + rec * kRecBytes + 16 * lane);
+                bsc[r] = *reinterpret_cast<const uint32_t*>(scales + rec * kRecScaleBytes + soff);
             }
         }
+    };
+    // fragment (block b, chunk m) of the current step
+    auto frag = [&](int b, int m) -> f16x8_t {
+        const int r = GATEUP ? b : m, d = GATEUP ? m : b;
+        f16x2_t S;
+        if (d == 0) S = scale_f16x2<0>(bsc[r]);
+        else if (d == 1) S = scale_f16x2<1>(bsc[r]);
+        else if (d == 2) S = scale_f16x2<2>(bsc[r]);
+        else S = scale_f16x2<3>(bsc[r]);
+        return frag_f16(word_of(bcw[r], d), S);
     };
 
     f32x4_t acc[MB][NBW];
@@ -334,27 +335,26 @@ __global__ void __launch_bounds__(256) gemm_kernel(PrefillArgs a, int cls, int n
     for (int s = 0; s < nsteps; ++s) {
         const int buf = s & 1;
         // dequantise this step's B fragments, then prefetch the next step
-        uint32_t bw[NBW][16];
+        f16x8_t bw[NBW][4];
 #pragma unroll
-        for (int b = 0; b < NBW; ++b) dequant32_f16(bcw[b], bsc[b], bw[b]);
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) bw[b][m] = frag(b, m);
         if (s + 1 < nsteps) {
             load_a((s + 1) * BK);
             load_b((s + 1) * BK);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int m = 0; m < 4; ++m) {
             f16x8_t fa[MB];
 #pragma unroll
             for (int i = 0; i < MB; ++i)
-                fa[i] = lds_frag(&sA[buf][(wm * MB * 16 + i * 16 + l16) * APITCH + 32 * q4 + 8 * j]);
+                fa[i] = lds_frag(&sA[buf][(wm * MB * 16 + i * 16 + l16) * APITCH + 32 * m + 8 * q4]);
 #pragma unroll
-            for (int b = 0; b < NBW; ++b) {
-                const u32x4_t bv = u32x4_t{bw[b][4 * j], bw[b][4 * j + 1], bw[b][4 * j + 2], bw[b][4 * j + 3]};
-                const f16x8_t fb = __builtin_bit_cast(f16x8_t, bv);
+            for (int b = 0; b < NBW; ++b)
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
-                    acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[i][b], 0, 0, 0);
-            }
+                    acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], bw[b][m], acc[i][b], 0, 0, 0);
         }
         if (s + 1 < nsteps) {
             store_a(buf ^ 1);
@@ -388,7 +388,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(PrefillArgs a, int cls, int n
         const float* gl = reinterpret_cast<const float*>(slot + a.dn_glob);
 #pragma unroll
         for (int b = 0; b < NBW; ++b) {
-            const int oc = nt * 128 + wn * CW + b * 16 + l16;
+            const int oc = nt * NCOLS + wn * CW + b * 16 + l16;
             if (oc >= H) continue;
             const float gd = gl[oc];
 #pragma unroll
@@ -437,7 +437,7 @@ hipError_t launch_gemm(const PrefillArgs& a, int cls, int max_tiles, int ntn, hi
 
 }  // namespace
 
-bool prefill_shape_supported(int H, int I) { return H % 32 == 0 && I % 32 == 0 && H <= 8192; }
+bool prefill_shape_supported(int H, int I) { return H % 128 == 0 && I % 32 == 0 && H <= 8192; }
 
 hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                           const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
@@ -471,13 +471,13 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int ntn_gu = ceil_div(I, 64), ntn_dn = ceil_div(H, 128);
+    const int ntn_gu = ceil_div(I, 64);
     if ((e = launch_gemm<128, true>(a, 0, max128, ntn_gu, s)) != hipSuccess) return e;
     if ((e = launch_gemm<64, true>(a, 1, maxsmall, ntn_gu, s)) != hipSuccess) return e;
     if ((e = launch_gemm<32, true>(a, 2, maxsmall, ntn_gu, s)) != hipSuccess) return e;
-    if ((e = launch_gemm<128, false>(a, 0, max128, ntn_dn, s)) != hipSuccess) return e;
-    if ((e = launch_gemm<64, false>(a, 1, maxsmall, ntn_dn, s)) != hipSuccess) return e;
-    if ((e = launch_gemm<32, false>(a, 2, maxsmall, ntn_dn, s)) != hipSuccess) return e;
+    if ((e = launch_gemm<128, false>(a, 0, max128, ceil_div(H, 128), s)) != hipSuccess) return e;
+    if ((e = launch_gemm<64, false>(a, 1, maxsmall, ceil_div(H, 128), s)) != hipSuccess) return e;
+    if ((e = launch_gemm<32, false>(a, 2, maxsmall, ceil_div(H, 256), s)) != hipSuccess) return e;
     const int nchunk = ceil_div(H, 256);
     hipLaunchKernelGGL(combine_kernel, dim3(T * nchunk), dim3(256), 0, s, a, nchunk);
     return hipGetLastError();

@@ -105,10 +105,11 @@ def forward(layer: DeviceLayer, x: torch.Tensor, r: Routing, y: torch.Tensor | N
     return y
 
 
-def dequant(codes: torch.Tensor, scales: torch.Tensor, globals_: torch.Tensor, stream=None) -> torch.Tensor:
-    rows, half = codes.shape
-    out = torch.empty((rows, 2 * half), dtype=torch.float32, device=codes.device)
-    check(_lib.moe_nvfp4_dequant(codes, scales, globals_, rows, 2 * half, out, stream))
+def dequant(slot: torch.Tensor, H: int, I: int, matrix: int, stream=None) -> torch.Tensor:
+    """fp32 gate_up (matrix 0, [2I, H]) or down (matrix 1, [H, I]) of one device slot."""
+    shape = (2 * I, H) if matrix == 0 else (H, I)
+    out = torch.empty(shape, dtype=torch.float32, device=slot.device)
+    check(_lib.moe_nvfp4_dequant(slot, H, I, matrix, out, stream))
     return out
 
 

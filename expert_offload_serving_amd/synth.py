@@ -19,7 +19,9 @@ g = amax/(6*448) (1 when the row is all zero); per 16-block,
 s = E4M3(amax_blk/(6*g)) rounded to nearest even and saturated at 448;
 each element becomes the E2M1 code nearest to w/(s*g), ties to the even
 mantissa, saturated at 6; a block whose scale rounds to 0 gets all-zero
-codes.  Element 2j of a row sits in the low nibble of byte j.
+codes.  Element 2j of a row sits in the low nibble of byte j of the
+row-major code array; pack_slot then stores codes and scales in the slot's
+matrix-core operand order (the byte formulas of the library header).
 """
 from __future__ import annotations
 
@@ -28,18 +30,18 @@ import dataclasses
 import numpy as np
 
 # ----------------------------------------------------------------------------
-# Slot byte layout: [gu_codes | gu_scales | gu_globals | dn_codes | dn_scales | dn_globals]
+# Slot regions: [gu_codes | gu_scales | gu_globals | dn_codes | dn_scales | dn_globals]
 # ----------------------------------------------------------------------------
 
 
 def slot_regions(H: int, I: int):
     """Byte (offset, size) of the six regions of one expert slot, in order."""
     sizes = [
-        2 * I * H // 2,   # gate_up codes   u8 [2I, H/2]
-        2 * I * H // 16,  # gate_up scales  u8 [2I, H/16]
+        2 * I * H // 2,   # gate_up codes   (operand order)
+        2 * I * H // 16,  # gate_up scales  (operand order)
         2 * I * 4,        # gate_up globals f32 [2I]
-        H * I // 2,       # down codes      u8 [H, I/2]
-        H * I // 16,      # down scales     u8 [H, I/16]
+        H * I // 2,       # down codes      (operand order)
+        H * I // 16,      # down scales     (operand order)
         H * 4,            # down globals    f32 [H]
     ]
     out, off = [], 0
@@ -106,10 +108,36 @@ def quantize_nvfp4(W: np.ndarray):
     return packed, s_byte.reshape(rows, K // 16), g
 
 
+def _frag_gate_up(codes, scales, N: int, K: int):
+    """Row-major gate_up parts -> the slot's column-grouped operand order.
+
+    codes [N, K/2] byte b = 64q + 16m + 4g + e/2 of row r = 16t + i goes to lane
+    record (q, t, 16g + i), dword m; scales [N, K/16] block 8q + 2m + h goes to
+    (q, t, h, i), byte m."""
+    NT, KQ = N // 16, K // 128
+    c = codes.reshape(NT, 16, KQ, 4, 4, 4).transpose(2, 0, 4, 1, 3, 5)
+    s = scales.reshape(NT, 16, KQ, 4, 2).transpose(2, 0, 4, 1, 3)
+    return np.ascontiguousarray(c).reshape(-1), np.ascontiguousarray(s).reshape(-1)
+
+
+def _frag_down(codes, scales, N: int, K: int):
+    """Row-major down parts -> the slot's row-grouped operand order.
+
+    Row r = 64p + 16j + i, codes byte b = 16k + 4g + e/2 goes to lane record
+    (k, p, 16g + i), dword j; scale block 2k + h goes to (k, p, h, i), byte j."""
+    NG, KC = N // 64, K // 32
+    c = codes.reshape(NG, 4, 16, KC, 4, 4).transpose(3, 0, 4, 2, 1, 5)
+    s = scales.reshape(NG, 4, 16, KC, 2).transpose(3, 0, 4, 2, 1)
+    return np.ascontiguousarray(c).reshape(-1), np.ascontiguousarray(s).reshape(-1)
+
+
 def pack_slot(gu, dn, H: int, I: int) -> np.ndarray:
-    """Concatenate the quantized gate_up and down parts into one slot (u8 vector)."""
+    """One slot from the quantized row-major parts (codes, scales, globals) of gate_up and down."""
+    assert H % 128 == 0 and I % 32 == 0, (H, I)
+    gc, gs = _frag_gate_up(np.asarray(gu[0], np.uint8), np.asarray(gu[1], np.uint8), 2 * I, H)
+    dc, ds = _frag_down(np.asarray(dn[0], np.uint8), np.asarray(dn[1], np.uint8), H, I)
     out = np.empty(slot_nbytes(H, I), dtype=np.uint8)
-    parts = [gu[0], gu[1], gu[2], dn[0], dn[1], dn[2]]
+    parts = [gc, gs, np.asarray(gu[2], np.float32), dc, ds, np.asarray(dn[2], np.float32)]
     for (off, size), p in zip(slot_regions(H, I), parts):
         b = np.ascontiguousarray(p).view(np.uint8).reshape(-1)
         assert b.size == size, (b.size, size)

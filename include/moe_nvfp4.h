@@ -19,8 +19,8 @@
  *  - Work is enqueued on the given stream and the call returns; device faults
  *    surface at the caller's next synchronisation.  moe_route_topk and
  *    moe_nvfp4_forward make no host synchronisation and no allocation.
- *  - Shapes: H % 32 == 0, I % 32 == 0 (the fp4 scale-block guard of issue #62
- *    "What it touches"), 1 <= k <= E <= 1024, T >= 0 (T == 0 is a no-op).
+ *  - Shapes: H % 128 == 0, I % 32 == 0 (see the slot format below),
+ *    1 <= k <= E <= 1024, T >= 0 (T == 0 is a no-op).
  *  - bf16 values are passed as their uint16 bit patterns.
  */
 #ifndef MOE_NVFP4_H
@@ -48,17 +48,33 @@ enum {
 const char* moe_last_error(void);
 
 /* ------------------------------------------------------------------ slots
- * One expert slot holds, in this order and without padding:
- *   gate_up codes   u8  [2I, H/2]   element 2j of a row in the low nibble of byte j
- *   gate_up scales  u8  [2I, H/16]  E4M3FN (OCP), one per 16 consecutive elements of a row
- *   gate_up globals f32 [2I]        one per row
- *   down codes      u8  [H, I/2]
- *   down scales     u8  [H, I/16]
- *   down globals    f32 [H]
- * The weight is W[r,c] = e2m1(code) * e4m3(scale[r, c/16]) * global[r]
- * (PR #385 "What this adds": packed codes, 16-wide scale blocks, per-row
- * globals).  Returns the slot size in bytes, or 0 if H or I is not a
- * positive multiple of 32. */
+ * An expert is two NVFP4 matrices (PR #385 "What this adds": packed 4-bit
+ * E2M1 codes, one E4M3FN scale per 16 consecutive elements along the
+ * contraction axis, one fp32 global per row; issue #62 "What it touches":
+ * gate_up is [2I, H] with gate rows [0, I) and up rows [I, 2I), down is
+ * [H, I]).  Element (r, c) of a matrix with N rows is
+ *     W[r,c] = e2m1(code(r,c)) * e4m3(scale(r, c/16)) * global[r].
+ * One slot holds, in this order and without padding:
+ *     gate_up codes   2I*H/2 bytes      gate_up scales  2I*H/16 bytes
+ *     gate_up globals f32 [2I]          down codes      H*I/2 bytes
+ *     down scales     H*I/16 bytes      down globals    f32 [H]
+ * Codes and scales are stored in matrix-core operand order, so that one
+ * 16-byte load per lane of a 64-lane wave brings whole operand fragments of
+ * the 16x16x32 MFMA (lane L = 16*g + i holds row i of a 16-row tile and the
+ * 8 columns [8g, 8g+8) of a 32-column chunk; two codes per byte, the even
+ * column in the low nibble).  With e = c % 8, g = (c / 8) % 4, i = r % 16:
+ *   gate_up (N = 2I, "column-grouped": a 16-row x 128-column tile per 1 KiB),
+ *     q = c / 128, m = (c / 32) % 4, t = r / 16, T = N / 16:
+ *       code byte  = 16*(64*(q*T + t) + 16*g + i) + 4*m + e/2
+ *       scale byte = 4*(16*(2*(q*T + t) + g/2) + i) + m      (block c/16)
+ *   down (N = H, "row-grouped": a 64-row x 32-column tile per 1 KiB),
+ *     k = c / 32, p = r / 64, j = (r / 16) % 4, P = N / 64:
+ *       code byte  = 16*(64*(k*P + p) + 16*g + i) + 4*j + e/2
+ *       scale byte = 4*(16*(2*(k*P + p) + g/2) + i) + j      (block c/16)
+ *   globals: row r at byte 4*r of its region.
+ * Requires H % 128 == 0 and I % 32 == 0 (I/tp a multiple of 32 is the
+ * fp4 scale-block guard of issue #62 "What it touches"; H % 128 is this
+ * format's tile).  Returns the slot size in bytes, or 0 for other shapes. */
 size_t moe_nvfp4_slot_bytes(int H, int I);
 
 /* ------------------------------------------------------------------ routing
@@ -165,11 +181,10 @@ int moe_nvfp4_slice_bank(const void* src_bank, int num_slots, int H, int I, int 
                          hipStream_t stream);
 
 /* ------------------------------------------------------------------ test hook
- * Dequantise an NVFP4 matrix [rows, K] to fp32 with the same decode the
- * forward kernels use: out[r,c] = f32(f32(e2m1 * e4m3) * globals[r]).
- * K % 32 == 0. */
-int moe_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* globals, int rows, int K,
-                      float* out, hipStream_t stream);
+ * Dequantise one matrix of one slot to fp32, row-major, with the same decode
+ * the forward kernels use: out[r,c] = f32(f32(e2m1 * e4m3) * global[r]).
+ * matrix 0 is gate_up (out [2I, H]), matrix 1 is down (out [H, I]). */
+int moe_nvfp4_dequant(const void* slot, int H, int I, int matrix, float* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -49,6 +49,12 @@ def lib():
         L.oracle_e4m3.argtypes = [ctypes.c_int]
         L.oracle_dequant.restype = None
         L.oracle_dequant.argtypes = [_u8p, _u8p, _f32p, ctypes.c_int, ctypes.c_int, _f32p]
+        L.oracle_shape_ok.restype = ctypes.c_int
+        L.oracle_shape_ok.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.oracle_dequant_slot.restype = ctypes.c_int
+        L.oracle_dequant_slot.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f32p]
+        L.oracle_unpack_slot.restype = ctypes.c_int
+        L.oracle_unpack_slot.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _u8p, _f32p]
         L.oracle_route.restype = ctypes.c_int
         L.oracle_route.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _f32p]
         L.oracle_permute.restype = None
@@ -91,6 +97,32 @@ def dequant(codes, scales, globals_) -> np.ndarray:
     out = np.empty((rows, K), dtype=np.float32)
     lib().oracle_dequant(codes, scales, g, rows, K, out)
     return out
+
+
+def _matrix_shape(H: int, I: int, matrix: int):
+    if not lib().oracle_shape_ok(H, I) or matrix not in (0, 1):
+        raise ValueError(f"bad slot shape H={H} I={I} matrix={matrix}")
+    return (2 * I, H) if matrix == 0 else (H, I)
+
+
+def dequant_slot(slot, H: int, I: int, matrix: int) -> np.ndarray:
+    """fp32 [N, K] of gate_up (matrix 0, [2I, H]) or down (matrix 1, [H, I]) of one slot."""
+    N, K = _matrix_shape(H, I, matrix)
+    slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
+    out = np.empty((N, K), dtype=np.float32)
+    lib().oracle_dequant_slot(slot, H, I, matrix, out)
+    return out
+
+
+def unpack_slot(slot, H: int, I: int, matrix: int):
+    """Row-major (codes [N, K/2], scales [N, K/16], globals [N]) of one matrix of a slot."""
+    N, K = _matrix_shape(H, I, matrix)
+    slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
+    codes = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((N, K // 16), dtype=np.uint8)
+    g = np.empty(N, dtype=np.float32)
+    lib().oracle_unpack_slot(slot, H, I, matrix, codes, scales, g)
+    return codes, scales, g
 
 
 def route(logits, k: int):
@@ -148,7 +180,7 @@ def slice_slot(slot, H: int, I: int, r: int, n: int) -> np.ndarray:
     slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
     out = np.empty(slot_bytes(H, I // n), dtype=np.uint8)
     if lib().oracle_slice_slot(slot, H, I, r, n, out) != 0:
-        raise ValueError("slice does not fall on whole scale blocks")
+        raise ValueError("slice is not a valid slot shape (I/n must be a multiple of 32)")
     return out
 
 

@@ -18,7 +18,10 @@
  * are the OCP 8-bit / microscaling element formats.
  *
  * Readings where the pages are silent (each one is listed in the design doc):
- *  - code nibble order: element 2j is the low nibble of byte j;
+ *  - code nibble order: of two columns sharing a byte, the even one is the
+ *    low nibble;
+ *  - slot byte order: the library header's operand-order formulas (a storage
+ *    choice; the pages fix no byte order), read here element by element;
  *  - scale blocks run along the contraction axis (H for gate_up, I for down);
  *  - dequant: W = f32( f32(e2m1 * e4m3) * global ), the inner product exact;
  *  - routing weights: softmax over the k selected logits (the same as a full
@@ -139,28 +142,101 @@ void oracle_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets, i
 
 /* ---------------------------------------------------------------- layer */
 
+/* Byte offset of code (r, c) and of scale (r, block b) of a matrix with N
+ * rows, in the slot's operand order (see the library header):
+ * gate_up keeps a 16-row x 128-column tile per 1 KiB, down a 64-row x
+ * 32-column tile; inside a tile, lane record 16*g + i holds row i (of the
+ * 16-row group) and columns [8g, 8g+8) of each 32-column chunk. */
+static size_t gu_code_at(int N, int r, int c) {
+    size_t q = c / 128, m = (c / 32) % 4, g = (c / 8) % 4, e = c % 8, t = r / 16, i = r % 16;
+    return 16 * (64 * (q * (N / 16) + t) + 16 * g + i) + 4 * m + e / 2;
+}
+static size_t gu_scale_at(int N, int r, int b) {
+    size_t q = b / 8, m = (b / 2) % 4, h = b % 2, t = r / 16, i = r % 16;
+    return 4 * (16 * (2 * (q * (N / 16) + t) + h) + i) + m;
+}
+static size_t dn_code_at(int N, int r, int c) {
+    size_t k = c / 32, g = (c / 8) % 4, e = c % 8, p = r / 64, j = (r / 16) % 4, i = r % 16;
+    return 16 * (64 * (k * (N / 64) + p) + 16 * g + i) + 4 * j + e / 2;
+}
+static size_t dn_scale_at(int N, int r, int b) {
+    size_t k = b / 2, h = b % 2, p = r / 64, j = (r / 16) % 4, i = r % 16;
+    return 4 * (16 * (2 * (k * (N / 64) + p) + h) + i) + j;
+}
+
+/* One matrix of a slot: N rows of K columns. */
 typedef struct {
-    const uint8_t *gu_codes, *gu_scales, *dn_codes, *dn_scales;
-    const float *gu_glob, *dn_glob;
-} slot_view;
+    const uint8_t *codes, *scales;
+    const float* glob;
+    int N, K, down;
+} mat_view;
 
 /* Region order in a slot: gate_up codes, gate_up scales, gate_up globals,
- * down codes, down scales, down globals (row-major, no padding). */
-static slot_view view_slot(const uint8_t* slot, int H, int I) {
-    slot_view v;
-    size_t off = 0;
-    v.gu_codes = slot + off; off += (size_t)2 * I * H / 2;
-    v.gu_scales = slot + off; off += (size_t)2 * I * H / 16;
-    v.gu_glob = (const float*)(slot + off); off += (size_t)2 * I * 4;
-    v.dn_codes = slot + off; off += (size_t)H * I / 2;
-    v.dn_scales = slot + off; off += (size_t)H * I / 16;
-    v.dn_glob = (const float*)(slot + off);
+ * down codes, down scales, down globals, without padding. */
+static mat_view view_matrix(const uint8_t* slot, int H, int I, int down) {
+    size_t gc = (size_t)2 * I * H / 2, gs = (size_t)2 * I * H / 16, gg = (size_t)2 * I * 4;
+    size_t dc = (size_t)H * I / 2, ds = (size_t)H * I / 16;
+    mat_view v;
+    if (!down) {
+        v.codes = slot;
+        v.scales = slot + gc;
+        v.glob = (const float*)(slot + gc + gs);
+        v.N = 2 * I, v.K = H;
+    } else {
+        v.codes = slot + gc + gs + gg;
+        v.scales = v.codes + dc;
+        v.glob = (const float*)(v.scales + ds);
+        v.N = H, v.K = I;
+    }
+    v.down = down;
     return v;
 }
+
+static int code_of(const mat_view* v, int r, int c) {
+    size_t o = v->down ? dn_code_at(v->N, r, c) : gu_code_at(v->N, r, c);
+    return (v->codes[o] >> (4 * (c & 1))) & 0xF;
+}
+
+static int scale_of(const mat_view* v, int r, int b) {
+    return v->scales[v->down ? dn_scale_at(v->N, r, b) : gu_scale_at(v->N, r, b)];
+}
+
+/* Row r of a slot matrix, dequantised: out[c] = f32( f32(e2m1 * e4m3) * g ). */
+static void dequant_view_row(const mat_view* v, int r, float* out) {
+    for (int c = 0; c < v->K; ++c) {
+        float q = (float)(oracle_e2m1(code_of(v, r, c)) * oracle_e4m3(scale_of(v, r, c / 16)));
+        out[c] = q * v->glob[r];
+    }
+}
+
+int oracle_shape_ok(int H, int I) { return H > 0 && I > 0 && H % 128 == 0 && I % 32 == 0; }
 
 size_t oracle_slot_bytes(int H, int I) {
     return (size_t)2 * I * H / 2 + (size_t)2 * I * H / 16 + (size_t)2 * I * 4 + (size_t)H * I / 2 +
            (size_t)H * I / 16 + (size_t)H * 4;
+}
+
+/* Dequantise matrix 0 (gate_up, [2I, H]) or 1 (down, [H, I]) of a slot. */
+int oracle_dequant_slot(const uint8_t* slot, int H, int I, int matrix, float* out) {
+    if (!oracle_shape_ok(H, I) || matrix < 0 || matrix > 1) return -1;
+    mat_view v = view_matrix(slot, H, I, matrix);
+    for (int r = 0; r < v.N; ++r) dequant_view_row(&v, r, out + (size_t)r * v.K);
+    return 0;
+}
+
+/* Read matrix 0 or 1 of a slot back into row-major arrays: codes [N, K/2]
+ * (even column in the low nibble), scales [N, K/16], globals [N]. */
+int oracle_unpack_slot(const uint8_t* slot, int H, int I, int matrix, uint8_t* codes, uint8_t* scales,
+                       float* globals) {
+    if (!oracle_shape_ok(H, I) || matrix < 0 || matrix > 1) return -1;
+    mat_view v = view_matrix(slot, H, I, matrix);
+    for (int r = 0; r < v.N; ++r) {
+        for (int c = 0; c < v.K; c += 2)
+            codes[(size_t)r * (v.K / 2) + c / 2] = (uint8_t)(code_of(&v, r, c) | (code_of(&v, r, c + 1) << 4));
+        for (int b = 0; b < v.K / 16; ++b) scales[(size_t)r * (v.K / 16) + b] = (uint8_t)scale_of(&v, r, b);
+        globals[r] = v.glob[r];
+    }
+    return 0;
 }
 
 /* silu(z) * up with silu(z) = z / (1 + exp(-z)). */
@@ -169,16 +245,16 @@ static double swiglu(double gate, double up) { return gate / (1.0 + exp(-gate)) 
 /* Expert FFN for one token: a = W_gu x; h = silu(a[:I]) * a[I:]; o = W_dn h. */
 static void expert_ffn(const uint8_t* slot, int H, int I, const double* x, double* a, double* h, float* row,
                        double* o) {
-    slot_view v = view_slot(slot, H, I);
+    mat_view gu = view_matrix(slot, H, I, 0), dn = view_matrix(slot, H, I, 1);
     for (int r = 0; r < 2 * I; ++r) {
-        dequant_row(v.gu_codes + (size_t)r * (H / 2), v.gu_scales + (size_t)r * (H / 16), v.gu_glob[r], H, row);
+        dequant_view_row(&gu, r, row);
         double acc = 0.0;
         for (int c = 0; c < H; ++c) acc += (double)row[c] * x[c];
         a[r] = acc;
     }
     for (int i = 0; i < I; ++i) h[i] = swiglu(a[i], a[I + i]);
     for (int r = 0; r < H; ++r) {
-        dequant_row(v.dn_codes + (size_t)r * (I / 2), v.dn_scales + (size_t)r * (I / 16), v.dn_glob[r], I, row);
+        dequant_view_row(&dn, r, row);
         double acc = 0.0;
         for (int c = 0; c < I; ++c) acc += (double)row[c] * h[c];
         o[r] = acc;
@@ -202,7 +278,7 @@ void oracle_shared_gate(const uint16_t* x, int T, int H, const uint16_t* wg, dou
 int oracle_forward(int H, int I, int E, int k, const uint8_t* bank, size_t slot_bytes, const int32_t* slot_of_expert,
                    long shared_slot, const uint16_t* wg, const uint16_t* x, int T, const int32_t* ids, const float* w,
                    const int32_t* tokens, int n_tokens, float* y, int nthreads) {
-    if (slot_bytes != oracle_slot_bytes(H, I) || H % 16 || I % 16) return -1;
+    if (!oracle_shape_ok(H, I) || slot_bytes != oracle_slot_bytes(H, I)) return -1;
     if (tokens == NULL) n_tokens = T;
     int bad = 0;
 #ifdef _OPENMP
@@ -249,44 +325,35 @@ int oracle_forward(int H, int I, int E, int k, const uint8_t* bank, size_t slot_
 
 /* ---------------------------------------------------------------- slicing */
 
-/* Slice r of n along the intermediate axis, I_l = I / n: gate rows
- * [r*I_l, (r+1)*I_l) followed by up rows [I + r*I_l, I + (r+1)*I_l) with
- * their scales and globals; down columns [r*I_l, (r+1)*I_l) of every one of
- * the H rows (code bytes and scale columns cut to match, all H globals
- * kept).  dst is a slot of shape (H, I_l).  Returns 0, or -1 if the slice
- * does not fall on whole scale blocks. */
+/* Slice r of n along the intermediate axis, I_l = I / n: the gate_up of
+ * the result has gate rows [r*I_l, (r+1)*I_l) followed by up rows
+ * [I + r*I_l, I + (r+1)*I_l), each with its codes, scales and global; its
+ * down has columns [r*I_l, (r+1)*I_l) of every one of the H rows, with the
+ * matching scale blocks and all H globals.  dst is a slot of shape (H, I_l),
+ * written element by element through the format's byte formulas.  Returns 0,
+ * or -1 if the slice is not a valid slot shape (I_l % 32 != 0). */
 int oracle_slice_slot(const uint8_t* src, int H, int I, int r, int n, uint8_t* dst) {
-    if (n <= 0 || r < 0 || r >= n || I % n) return -1;
+    if (n <= 0 || r < 0 || r >= n || I % n || !oracle_shape_ok(H, I)) return -1;
     int Il = I / n;
-    if (Il % 16) return -1;
-    slot_view s = view_slot(src, H, I);
-    uint8_t* p = dst;
-    /* gate_up codes, then scales, then globals: the gate range then the up range */
-    const int rows0[2] = {r * Il, I + r * Il};
-    for (int part = 0; part < 2; ++part)
-        for (int i = 0; i < Il; ++i) {
-            memcpy(p, s.gu_codes + (size_t)(rows0[part] + i) * (H / 2), (size_t)H / 2);
-            p += H / 2;
-        }
-    for (int part = 0; part < 2; ++part)
-        for (int i = 0; i < Il; ++i) {
-            memcpy(p, s.gu_scales + (size_t)(rows0[part] + i) * (H / 16), (size_t)H / 16);
-            p += H / 16;
-        }
-    for (int part = 0; part < 2; ++part)
-        for (int i = 0; i < Il; ++i) {
-            memcpy(p, &s.gu_glob[rows0[part] + i], 4);
-            p += 4;
-        }
-    for (int row = 0; row < H; ++row) {
-        memcpy(p, s.dn_codes + (size_t)row * (I / 2) + (size_t)r * (Il / 2), (size_t)Il / 2);
-        p += Il / 2;
+    if (!oracle_shape_ok(H, Il)) return -1;
+    memset(dst, 0, oracle_slot_bytes(H, Il));
+    mat_view sg = view_matrix(src, H, I, 0), sd = view_matrix(src, H, I, 1);
+    mat_view dg = view_matrix(dst, H, Il, 0), dd = view_matrix(dst, H, Il, 1);
+    uint8_t *dgc = (uint8_t*)dg.codes, *dgs = (uint8_t*)dg.scales, *ddc = (uint8_t*)dd.codes,
+            *dds = (uint8_t*)dd.scales;
+    float *dgg = (float*)dg.glob, *ddg = (float*)dd.glob;
+    for (int rr = 0; rr < 2 * Il; ++rr) {
+        int from = rr < Il ? r * Il + rr : I + r * Il + (rr - Il);
+        for (int c = 0; c < H; ++c) dgc[gu_code_at(2 * Il, rr, c)] |= (uint8_t)(code_of(&sg, from, c) << (4 * (c & 1)));
+        for (int b = 0; b < H / 16; ++b) dgs[gu_scale_at(2 * Il, rr, b)] = (uint8_t)scale_of(&sg, from, b);
+        dgg[rr] = sg.glob[from];
     }
     for (int row = 0; row < H; ++row) {
-        memcpy(p, s.dn_scales + (size_t)row * (I / 16) + (size_t)r * (Il / 16), (size_t)Il / 16);
-        p += Il / 16;
+        for (int c = 0; c < Il; ++c)
+            ddc[dn_code_at(H, row, c)] |= (uint8_t)(code_of(&sd, row, r * Il + c) << (4 * (c & 1)));
+        for (int b = 0; b < Il / 16; ++b) dds[dn_scale_at(H, row, b)] = (uint8_t)scale_of(&sd, row, r * Il / 16 + b);
+        ddg[row] = sd.glob[row];
     }
-    memcpy(p, s.dn_glob, (size_t)H * 4);
     return 0;
 }
 

@@ -34,9 +34,9 @@ def test_slot_bytes():
     assert _lib.moe_nvfp4_slot_bytes(2560, 640) == 2_780_160
     assert _lib.moe_nvfp4_slot_bytes(2560, 320) == 1_395_200
     assert _lib.moe_nvfp4_slot_bytes(256, 64) == 29_184
-    for H, I in [(2560, 641), (2576, 640), (0, 64), (-32, 64), (256, 16)]:
+    for H, I in [(2560, 641), (2576, 640), (0, 64), (-32, 64), (256, 16), (96, 32), (320, 64)]:
         assert _lib.moe_nvfp4_slot_bytes(H, I) == 0
-    for H, I in [(96, 32), (2560, 640), (7168, 2048)]:
+    for H, I in [(128, 32), (2560, 640), (7168, 2048)]:
         assert _lib.moe_nvfp4_slot_bytes(H, I) == oracle.slot_bytes(H, I)
 
 
@@ -83,8 +83,11 @@ def test_forward_validation_without_gpu():
 
 
 def test_other_entry_points_validate():
-    assert _lib.moe_nvfp4_dequant(1, 1, 1, 4, 48, 1, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
-    assert _lib.moe_nvfp4_dequant(1, 1, 1, 0, 64, 1, 0) == _lib.MOE_OK
+    assert _lib.moe_nvfp4_dequant(0x100, 96, 32, 0, 0x100, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE   # H % 128
+    assert _lib.moe_nvfp4_dequant(0x100, 128, 48, 0, 0x100, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE  # I % 32
+    assert _lib.moe_nvfp4_dequant(0x100, 128, 32, 2, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT   # matrix
+    assert _lib.moe_nvfp4_dequant(0x101, 128, 32, 0, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT   # misaligned
+    assert _lib.moe_nvfp4_dequant(None, 128, 32, 0, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT
     assert _lib.moe_nvfp4_slice_bank(1, 4, 2560, 640, 0, 8, 1, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE  # 80 % 32 != 0
     assert _lib.moe_nvfp4_slice_bank(1, 4, 2560, 640, 2, 2, 1, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
     assert _lib.moe_nvfp4_slice_bank(1, 0, 2560, 640, 0, 2, 1, 0) == _lib.MOE_OK

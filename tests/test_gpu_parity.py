@@ -34,35 +34,39 @@ def _announce(msg):
 # ---------------------------------------------------------------- dequant
 
 def test_dequant_bitexact_all_code_scale_pairs():
-    """Every (code, scale byte) pair under several globals, against oracle_dequant bit for bit."""
-    _announce("dequant 16 codes x 256 scales x 5 globals")
-    K = 256
-    codes_row = np.array([((2 * j) % 16) | (((2 * j + 1) % 16) << 4) for j in range(K // 2)], dtype=np.uint8)
-    gl = [1.0, 0.5, 3.7e-5, -2.25, 1.0e30]
-    rows = 256 * len(gl)
-    codes = np.tile(codes_row, (rows, 1))
-    scales = np.repeat(np.tile(np.arange(256, dtype=np.uint8), len(gl))[:, None], K // 16, axis=1)
-    globals_ = np.repeat(np.array(gl, dtype=np.float32), 256)
-    want = oracle.dequant(codes, scales, globals_)
-    got = dl.dequant(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
-                     torch.from_numpy(globals_).cuda()).cpu().numpy()
-    nan_w, nan_g = np.isnan(want), np.isnan(got)
-    assert np.array_equal(nan_w, nan_g)
-    assert np.array_equal(want[~nan_w].view(np.uint32), got[~nan_g].view(np.uint32))
+    """Every (code, scale byte) pair under several globals, in both matrices of a slot, bit for bit against the
+    oracle's dequant of the same row-major values."""
+    _announce("dequant 16 codes x 256 scales x 5 globals (H=256, I=640)")
+    H, I = 256, 640
+    gl = np.array([1.0, 0.5, 3.7e-5, -2.25, 1.0e30], dtype=np.float32)
+    def all_pairs(N, K, shift):
+        codes_row = np.array([((2 * j + shift) % 16) | (((2 * j + 1 + shift) % 16) << 4) for j in range(K // 2)],
+                             dtype=np.uint8)
+        codes = np.tile(codes_row, (N, 1))
+        blocks = np.arange(N * (K // 16)).reshape(N, K // 16)
+        scales = ((blocks + shift) % 256).astype(np.uint8)
+        globals_ = gl[(np.arange(N) * 7 + shift) % len(gl)]
+        return codes, scales, globals_
+    gu, dn = all_pairs(2 * I, H, 0), all_pairs(H, I, 3)
+    slot = synth.pack_slot(gu, dn, H, I)
+    dslot = torch.from_numpy(slot).cuda()
+    for m, parts in enumerate((gu, dn)):
+        want = oracle.dequant(*parts)
+        assert np.array_equal(np.isnan(want), np.isnan(oracle.dequant_slot(slot, H, I, m)))
+        got = dl.dequant(dslot, H, I, m).cpu().numpy()
+        nan_w, nan_g = np.isnan(want), np.isnan(got)
+        assert np.array_equal(nan_w, nan_g)
+        assert np.array_equal(want[~nan_w].view(np.uint32), got[~nan_g].view(np.uint32))
 
 
 def test_dequant_bitexact_real_bank():
     _announce("dequant real expert slot (H=2560, I=640)")
     H, I = 2560, 640
     slot = synth.random_expert_slot(np.random.default_rng(7), H, I)
-    reg = synth.slot_regions(H, I)
-    def part(i, shape, dt=np.uint8):
-        off, size = reg[i]
-        return np.ascontiguousarray(slot[off:off + size].view(dt).reshape(shape))
-    for (ci, si, gi, rows, K) in [(0, 1, 2, 2 * I, H), (3, 4, 5, H, I)]:
-        c, s, g = part(ci, (rows, K // 2)), part(si, (rows, K // 16)), part(gi, (rows,), np.float32)
-        want = oracle.dequant(c, s, g)
-        got = dl.dequant(torch.from_numpy(c).cuda(), torch.from_numpy(s).cuda(), torch.from_numpy(g).cuda())
+    dslot = torch.from_numpy(slot).cuda()
+    for m in (0, 1):
+        want = oracle.dequant_slot(slot, H, I, m)
+        got = dl.dequant(dslot, H, I, m)
         assert np.array_equal(want.view(np.uint32), got.cpu().numpy().view(np.uint32))
 
 
@@ -159,8 +163,10 @@ def test_forward_decode_bs1_config():
 
 
 def test_forward_small_shapes_and_ragged():
-    """Odd sizes exercising partial row blocks and tiles: H=96 (3 chunks per row), I=32, E=5."""
-    for (H, I, E, k, T) in [(96, 32, 5, 2, 3), (96, 32, 5, 2, 17), (320, 96, 7, 3, 40), (256, 64, 8, 8, 16)]:
+    """Small and odd sizes: H=128 (one 128-column step, fewer steps than waves), I=32 (one slice), I=96 (a partial
+    128-column step of down), E=5/7, T across both paths."""
+    for (H, I, E, k, T) in [(128, 32, 5, 2, 3), (128, 32, 5, 2, 17), (384, 96, 7, 3, 40), (384, 96, 7, 3, 11),
+                            (256, 64, 8, 8, 16)]:
         _announce(f"forward H={H} I={I} E={E} k={k} T={T}")
         rng = np.random.default_rng(H + I + T)
         bank = np.stack([synth.random_expert_slot(rng, H, I) for _ in range(E + 1)])

@@ -154,14 +154,93 @@ def test_permute_matches_stable_argsort():
 
 # ---------------------------------------------------------------- layer
 
-def _dense_dequant_slot(slot, H, I):
+def _byte_offsets(N, K, down):
+    """Code and scale byte offsets of every (row, column) / (row, block) of a slot matrix, computed directly from
+    the format's formulas (numpy broadcasting; no reshapes shared with the packer or the oracle)."""
+    r = np.arange(N)[:, None]
+    c = np.arange(K)[None, :]
+    b = np.arange(K // 16)[None, :]
+    i, g, e = r % 16, (c // 8) % 4, c % 8
+    if not down:
+        T, t = N // 16, r // 16
+        code = 16 * (64 * ((c // 128) * T + t) + 16 * g + i) + 4 * ((c // 32) % 4) + e // 2
+        scale = 4 * (16 * (2 * ((b // 8) * T + t) + b % 2) + i) + (b // 2) % 4
+    else:
+        P, p, j = N // 64, r // 64, (r // 16) % 4
+        code = 16 * (64 * ((c // 32) * P + p) + 16 * g + i) + 4 * j + e // 2
+        scale = 4 * (16 * (2 * ((b // 2) * P + p) + b % 2) + i) + j
+    return code, scale
+
+
+def _formula_unpack(slot, H, I, matrix):
+    """(nibbles [N, K], scale bytes [N, K/16], globals [N]) of one slot matrix via _byte_offsets."""
     reg = synth.slot_regions(H, I)
-    def part(i, shape, dt=np.uint8):
-        off, size = reg[i]
-        return slot[off:off + size].view(dt).reshape(shape)
-    Wgu = _independent_dequant(part(0, (2 * I, H // 2)), part(1, (2 * I, H // 16)), part(2, (2 * I,), np.float32))
-    Wdn = _independent_dequant(part(3, (H, I // 2)), part(4, (H, I // 16)), part(5, (H,), np.float32))
-    return Wgu.astype(np.float64), Wdn.astype(np.float64)
+    N, K = (2 * I, H) if matrix == 0 else (H, I)
+    base = 3 * matrix
+    def region(idx):
+        off, size = reg[base + idx]
+        return slot[off:off + size]
+    code_off, scale_off = _byte_offsets(N, K, matrix == 1)
+    nib = (region(0)[code_off] >> (4 * (np.arange(K)[None, :] & 1))) & 0xF
+    return nib.astype(np.uint8), region(1)[scale_off], region(2).view(np.float32)
+
+
+def _pack_nibbles(nib):
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _dense_dequant_slot(slot, H, I):
+    mats = []
+    for m in (0, 1):
+        nib, sc, g = _formula_unpack(slot, H, I, m)
+        mats.append(_independent_dequant(_pack_nibbles(nib), sc, g).astype(np.float64))
+    return mats[0], mats[1]
+
+
+def test_slot_operand_order_matches_formulas():
+    """The packer writes, and the oracle reads, every code nibble, scale byte and global where the format's byte
+    formulas put them (plain Python loops over every element of a small slot)."""
+    H, I = 256, 32
+    rng = np.random.default_rng(21)
+    parts = []
+    for N, K in ((2 * I, H), (H, I)):
+        parts.append((rng.integers(0, 256, (N, K // 2), dtype=np.uint8),
+                      rng.integers(0, 256, (N, K // 16), dtype=np.uint8),
+                      rng.standard_normal(N).astype(np.float32)))
+        parts[-1][1][(parts[-1][1] & 0x7F) == 0x7F] = 0x38    # no NaN scales (the encoder never makes them)
+    slot = synth.pack_slot(parts[0], parts[1], H, I)
+    reg = synth.slot_regions(H, I)
+    for m, (N, K) in enumerate(((2 * I, H), (H, I))):
+        codes, scales, g = parts[m]
+        c_reg = slot[reg[3 * m][0]:][:reg[3 * m][1]]
+        s_reg = slot[reg[3 * m + 1][0]:][:reg[3 * m + 1][1]]
+        for r in range(N):
+            for c in range(K):
+                if m == 0:
+                    off = 16 * (64 * ((c // 128) * (N // 16) + r // 16) + 16 * ((c // 8) % 4) + r % 16) \
+                        + 4 * ((c // 32) % 4) + (c % 8) // 2
+                else:
+                    off = 16 * (64 * ((c // 32) * (N // 64) + r // 64) + 16 * ((c // 8) % 4) + r % 16) \
+                        + 4 * ((r // 16) % 4) + (c % 8) // 2
+                assert (c_reg[off] >> (4 * (c % 2))) & 0xF == (codes[r, c // 2] >> (4 * (c % 2))) & 0xF, (m, r, c)
+            for bk in range(K // 16):
+                if m == 0:
+                    off = 4 * (16 * (2 * ((bk // 8) * (N // 16) + r // 16) + bk % 2) + r % 16) + (bk // 2) % 4
+                else:
+                    off = 4 * (16 * (2 * ((bk // 2) * (N // 64) + r // 64) + bk % 2) + r % 16) + (r // 16) % 4
+                assert s_reg[off] == scales[r, bk], (m, r, bk)
+        uc, us, ug = oracle.unpack_slot(slot, H, I, m)
+        assert np.array_equal(uc, codes) and np.array_equal(us, scales)
+        assert np.array_equal(ug.view(np.uint32), g.view(np.uint32))
+        want = _independent_dequant(codes, scales, g)
+        assert np.array_equal(oracle.dequant_slot(slot, H, I, m).view(np.uint32), want.view(np.uint32))
+
+
+def test_slot_shape_guard():
+    assert oracle.slot_bytes(128, 32) > 0
+    for H, I in ((96, 32), (320, 64), (128, 48)):
+        with pytest.raises(ValueError):
+            oracle.dequant_slot(np.zeros(oracle.slot_bytes(H, I), np.uint8), H, I, 0)
 
 
 def _bruteforce_layer(L, ids, w, shared=True):
@@ -237,7 +316,7 @@ def test_forward_special_cases():
 def test_forward_closed_form_all_ones_expert():
     """One expert whose every weight is 1 (codes 2 = 1.0, scale 0x38 = 1.0, globals 1): with x = 0.5 everywhere,
     a_r = H/2 for every row, h_i = silu(H/2) * H/2, o_r = I * h; k=1 gives w=1 and y = o."""
-    H, I, E = 32, 16, 1
+    H, I, E = 128, 32, 1
     sb = synth.slot_nbytes(H, I)
     slot = np.zeros(sb, dtype=np.uint8)
     reg = synth.slot_regions(H, I)
@@ -269,7 +348,7 @@ def test_slot_geometry_matches_pages():
 
 
 def test_slice_dequant_equals_dequant_slice():
-    H, I = 64, 64
+    H, I = 128, 128
     slot = synth.random_expert_slot(np.random.default_rng(2), H, I)
     Wgu, Wdn = _dense_dequant_slot(slot, H, I)
     for n in (2, 4):
@@ -297,7 +376,7 @@ def test_slice_partials_sum_to_full():
 
 def test_slice_rejects_partial_blocks():
     with pytest.raises(ValueError):
-        oracle.slice_slot(np.zeros(synth.slot_nbytes(64, 32), np.uint8), 64, 32, 0, 4)
+        oracle.slice_slot(np.zeros(synth.slot_nbytes(128, 64), np.uint8), 128, 64, 0, 4)
 
 
 # ---------------------------------------------------------------- LRU model
