@@ -293,7 +293,9 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
 // y_t = sum over (j, slice) of the routed partials of token t, plus
 // sigmoid(x_t . w_g) times the shared expert's partials, in a fixed order.
 // Workgroup: one token and 64 output columns; thread (q, cl) sums partial
-// rows q, q + 16, ... of columns [4 cl, 4 cl + 4).
+// rows q, q + 16, ... of columns [4 cl, 4 cl + 4).  Each pass issues all of
+// its loads before the first add (partial rows past the end read as zero).
+constexpr int kCR = 16;  // partial rows per thread per pass
 __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int nch) {
     __shared__ f32x4_t rr[16][16], rsh[16][16];
     __shared__ float dots[4];
@@ -302,17 +304,56 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
     const int H = a.H, k = a.k, T = a.T;
     const int col = 64 * ch + 4 * cl;
     const int nr = k * nsl;
-    const float* base_r = a.part + (size_t)t * k * nsl * H + col;
+    const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
+    const int rbase = t * k * nsl, sbase = (T * k + t) * nsl;
+    const bool has_shared = a.shared != nullptr;
     f32x4_t sr = {0.0f, 0.0f, 0.0f, 0.0f}, ss = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int r = q; r < nr; r += 16) sr += *reinterpret_cast<const f32x4_t*>(base_r + (size_t)r * H);
     float gd = 0.0f;
-    if (a.shared != nullptr) {
-        const float* base_s = a.part + (size_t)(T * k + t) * nsl * H + col;
-        for (int r = q; r < nsl; r += 16) ss += *reinterpret_cast<const f32x4_t*>(base_s + (size_t)r * H);
-        const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * H);
-        const u32x4_t* wv = reinterpret_cast<const u32x4_t*>(a.wg);
-        for (int v = tid; v < H / 8; v += 256) {
-            const u32x4_t xx = xv[v], ww = wv[v];
+    {
+        f32x4_t v[kCR], vs[2];
+        u32x4_t xv[2], wv[2];
+#pragma unroll
+        for (int i = 0; i < kCR; ++i) {
+            const int r = q + 16 * i;
+            v[i] = __builtin_bit_cast(f32x4_t, buf_load16(pres, r < nr ? 4 * ((rbase + r) * H + col) : kOob));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = q + 16 * i;
+            vs[i] = __builtin_bit_cast(f32x4_t,
+                                       buf_load16(pres, has_shared && r < nsl ? 4 * ((sbase + r) * H + col) : kOob));
+        }
+        const rsrc_t xres = make_rsrc(a.x + (size_t)t * H, (uint32_t)H * 2);
+        const rsrc_t gres = make_rsrc(a.wg, has_shared ? (uint32_t)H * 2 : 0u);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int vv = tid + 256 * i;
+            xv[i] = buf_load16(xres, has_shared && vv < H / 8 ? 16 * vv : kOob);
+            wv[i] = buf_load16(gres, has_shared && vv < H / 8 ? 16 * vv : kOob);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kCR; ++i) sr += v[i];
+        ss = vs[0] + vs[1];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            gd = dot2_bf16(as_bf16x2(xv[i].x), as_bf16x2(wv[i].x), gd);
+            gd = dot2_bf16(as_bf16x2(xv[i].y), as_bf16x2(wv[i].y), gd);
+            gd = dot2_bf16(as_bf16x2(xv[i].z), as_bf16x2(wv[i].z), gd);
+            gd = dot2_bf16(as_bf16x2(xv[i].w), as_bf16x2(wv[i].w), gd);
+        }
+    }
+    // rare shapes: more partial rows, or more of the shared expert / H, than one pass covers
+    for (int r0 = 16 * kCR; r0 < nr; r0 += 16 * kCR)
+        for (int r = r0 + q; r < nr && r < r0 + 16 * kCR; r += 16)
+            sr += __builtin_bit_cast(f32x4_t, buf_load16(pres, 4 * ((rbase + r) * H + col)));
+    if (has_shared) {
+        for (int r = q + 32; r < nsl; r += 16)
+            ss += __builtin_bit_cast(f32x4_t, buf_load16(pres, 4 * ((sbase + r) * H + col)));
+        const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * H);
+        const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(a.wg);
+        for (int vv = tid + 512; vv < H / 8; vv += 256) {
+            const u32x4_t xx = xp[vv], ww = wp[vv];
             gd = dot2_bf16(as_bf16x2(xx.x), as_bf16x2(ww.x), gd);
             gd = dot2_bf16(as_bf16x2(xx.y), as_bf16x2(ww.y), gd);
             gd = dot2_bf16(as_bf16x2(xx.z), as_bf16x2(ww.z), gd);
@@ -329,7 +370,7 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
 #pragma unroll
     for (int i = 0; i < 16; ++i) tr += rr[i][tid], ts += rsh[i][tid];
     f32x4_t out = tr;
-    if (a.shared != nullptr) out += sigmoidf_(((dots[0] + dots[1]) + dots[2]) + dots[3]) * ts;
+    if (has_shared) out += sigmoidf_(((dots[0] + dots[1]) + dots[2]) + dots[3]) * ts;
     f32x4_t* yp = reinterpret_cast<f32x4_t*>(a.y + (size_t)t * H + 64 * ch + 4 * tid);
     if (a.accumulate) out += *yp;
     *yp = out;

@@ -19,96 +19,105 @@ namespace {
 constexpr int kMaxE = 1024;
 constexpr int kVPL = kMaxE / kWave;  // logits held per lane
 
-// (va, ia) ranks before (vb, ib): larger logit first, lower index on ties.
-// With a NaN operand neither comparison holds and the index decides, so the
-// result is always a valid, untaken expert.
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-    if (ia < 0) return false;
-    if (ib < 0) return true;
-    if (va > vb) return true;
-    if (va < vb) return false;
-    return ia < ib;
+// Selection order as one unsigned 64-bit key per (logit, expert): the high
+// word maps the logit monotonically onto uint32 (-0 folded onto +0, so equal
+// logits tie), the low word is ~index, so a larger key ranks first and ties
+// go to the lower index.  Key 0 means "no candidate" (every real key has a
+// nonzero low word).  A NaN logit maps to some key; NaN input is a
+// precondition violation and only has to leave a valid, untaken expert.
+__device__ __forceinline__ uint64_t rank_key(float v, int idx) {
+    uint32_t u = __float_as_uint(v + 0.0f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)idx;
+}
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)~(uint32_t)key; }
+// The logit of a key (a -0 logit comes back as +0, which no later step can tell apart).
+__device__ __forceinline__ float key_value(uint64_t key) {
+    const uint32_t u = (uint32_t)(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
 // DPP row operations of the GCN/CDNA ISA (gfx9 encodings).
 constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr3 = 0x113, kDppRowShr4 = 0x114,
               kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
 
-// One step of a wave arg-max: combine each lane's (v, i) with the pair DPP
-// control CTRL brings in; lanes the masks disable or whose source is out of
-// range keep their own pair.
+// One branch-free step of a wave max over 64-bit keys: take the key DPP
+// control CTRL brings in when it is larger; lanes the masks disable keep
+// their own (old operand = own key).
 template <int CTRL, int ROW_MASK, int BANK_MASK>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK,
-                                                                BANK_MASK, false));
-    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, BANK_MASK, false);
-    if (ranks_before(ov, oi, v, i)) v = ov, i = oi;
+__device__ __forceinline__ uint64_t kmax_step(uint64_t key) {
+    const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, BANK_MASK, false);
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, BANK_MASK, false);
+    const uint64_t other = ((uint64_t)ohi << 32) | olo;
+    return other > key ? other : key;
 }
 
-// Wave-wide best (v, i) by ranks_before, returned to every lane.  The DPP
-// sequence leaves the result in lane 63 (shifts within each 16-lane row,
-// then the row broadcasts); max-like merges tolerate the overlaps.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-    argmax_step<kDppRowShr1, 0xF, 0xF>(v, i);
-    argmax_step<kDppRowShr2, 0xF, 0xF>(v, i);
-    argmax_step<kDppRowShr3, 0xF, 0xF>(v, i);
-    argmax_step<kDppRowShr4, 0xF, 0xE>(v, i);
-    argmax_step<kDppRowShr8, 0xF, 0xC>(v, i);
-    argmax_step<kDppRowBcast15, 0xA, 0xF>(v, i);
-    argmax_step<kDppRowBcast31, 0xC, 0xF>(v, i);
-    v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-    i = __builtin_amdgcn_readlane(i, 63);
+// Wave-wide maximum key, returned to every lane.  The DPP sequence leaves
+// the result in lane 63 (shifts within each 16-lane row, then the row
+// broadcasts); max tolerates the overlapping inputs.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
+    key = kmax_step<kDppRowShr1, 0xF, 0xF>(key);
+    key = kmax_step<kDppRowShr2, 0xF, 0xF>(key);
+    key = kmax_step<kDppRowShr3, 0xF, 0xF>(key);
+    key = kmax_step<kDppRowShr4, 0xF, 0xE>(key);
+    key = kmax_step<kDppRowShr8, 0xF, 0xC>(key);
+    key = kmax_step<kDppRowBcast15, 0xA, 0xF>(key);
+    key = kmax_step<kDppRowBcast31, 0xC, 0xF>(key);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)key, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
-// One wave selects the top-k of row `l` (E <= 64 * VPL logits) and writes ids and weights.
+// One wave selects the top-k of row `l` (E <= 64 * VPL logits) and writes
+// ids and weights.  Selection: k rounds of a wave maximum over each lane's
+// best remaining key.  Weights: softmax over the k selected logits in
+// double (exp(l_j - l_max) / sum), summed in selection order, rounded to f32.
 template <int VPL>
 __device__ void topk_one_token(const float* __restrict__ l, int E, int k, int32_t* __restrict__ ids,
                                float* __restrict__ w, int lane) {
     static_assert(VPL <= kVPL, "too many logits per lane");
-    float v[VPL];
-    uint32_t taken = 0;
+    uint64_t key[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        int idx = lane + kWave * i;
-        v[i] = idx < E ? l[idx] : 0.0f;
+        const int idx = lane + kWave * i;
+        key[i] = idx < E ? rank_key(l[idx], idx) : 0ull;
     }
-    float held_v[VPL];  // logit of selection j is kept by lane j % 64 in slot j / 64
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) held_v[i] = 0.0f;
+    float held = 0.0f;  // selection j's logit, kept by lane j (j < 64)
     float m = 0.0f;
     for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int bi = -1;
+        uint64_t best = key[0];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            int idx = lane + kWave * i;
-            bool ok = idx < E && !((taken >> i) & 1u);
-            if (ok && ranks_before(v[i], idx, bv, bi)) bv = v[i], bi = idx;
-        }
-        wave_argmax(bv, bi);
-        if (bi >= 0 && (bi % kWave) == lane) taken |= 1u << (bi / kWave);
+        for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_key(best);
+        const int bi = key_index(best);
+        const int owner_slot = bi / kWave, owner_lane = bi % kWave;
+        const float bv = key_value(best);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) key[i] = (i == owner_slot && lane == owner_lane) ? 0ull : key[i];
         if (j == 0) m = bv;
-        if ((j % kWave) == lane) {
-            held_v[j / kWave] = bv;
-            ids[j] = bi;
+        if ((j % kWave) == lane) ids[j] = bi;
+        if (j == lane) held = bv;
+        if (j >= kWave && (j % kWave) == lane) w[j] = bv;  // parked logit, replaced below
+    }
+    // exp of each selected logit relative to the largest, in double
+    if (k <= kWave) {
+        const double ex = lane < k ? exp((double)held - (double)m) : 0.0;
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) {
+            const int lo = __builtin_amdgcn_readlane((int)(uint32_t)__double_as_longlong(ex), j);
+            const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(__double_as_longlong(ex) >> 32), j);
+            sum += __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
         }
-    }
-    // Softmax over the selected logits in double, summed in selection order.
-    double ex[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) ex[i] = (lane + kWave * i < k) ? exp((double)held_v[i] - (double)m) : 0.0;
-    double sum = 0.0;
-    for (int j = 0; j < k; ++j) {
-        double e = 0.0;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if (i == j / kWave) e = ex[i];
-        sum += __shfl(e, j % kWave, kWave);
-    }
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        int j = lane + kWave * i;
-        if (j < k) w[j] = (float)(ex[i] / sum);
+        if (lane < k) w[lane] = (float)(ex / sum);
+    } else {
+        // rare: more selections than lanes; logits of selections >= 64 were parked in w
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) sum += exp((double)(j < kWave ? __shfl(held, j, kWave) : w[j]) - (double)m);
+        for (int j = lane; j < k; j += kWave) {
+            const float lj = j < kWave ? held : w[j];
+            w[j] = (float)(exp((double)lj - (double)m) / sum);
+        }
     }
 }
 
@@ -217,25 +226,34 @@ __global__ void __launch_bounds__(1024) route_small_kernel(const float* __restri
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ sorted_assign,
                                                             int32_t* __restrict__ assign_pos) {
-    __shared__ int32_t ids_lds[kDirectMaxAssign];
+    __shared__ __attribute__((aligned(16))) int32_t ids_lds[kDirectMaxAssign + 4];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     if (wave < T) topk_one_token<VPL>(logits + (size_t)wave * E, E, k, ids_lds + wave * k, w + (size_t)wave * k, lane);
+    const int n = T * k, n4 = (n + 3) / 4;
+    if ((int)threadIdx.x < 4 * n4 - n) ids_lds[n + threadIdx.x] = 0x7FFFFFFF;  // pad: ranks after every expert
     __syncthreads();
-    const int n = T * k;
+    const int4* ids4 = reinterpret_cast<const int4*>(ids_lds);
+    // pos(a) = #{b : (e_b, b) < (e_a, a)}, scanned four assignments per LDS read
     for (int a = threadIdx.x; a < n; a += blockDim.x) {
         const int e = ids_lds[a];
         int pos = 0;
-        for (int b = 0; b < n; ++b) {
-            const int eb = ids_lds[b];
-            pos += (eb < e || (eb == e && b < a)) ? 1 : 0;
+        for (int q = 0; q < n4; ++q) {
+            const int4 v = ids4[q];
+            const int b = 4 * q;
+            pos += (v.x < e || (v.x == e && b < a)) + (v.y < e || (v.y == e && b + 1 < a)) +
+                   (v.z < e || (v.z == e && b + 2 < a)) + (v.w < e || (v.w == e && b + 3 < a));
         }
         ids[a] = e;
         sorted_assign[pos] = a;
         assign_pos[a] = pos;
     }
+    // offsets[e] = #{b : e_b < e}
     for (int e = threadIdx.x; e <= E; e += blockDim.x) {
         int c = 0;
-        for (int b = 0; b < n; ++b) c += ids_lds[b] < e ? 1 : 0;
+        for (int q = 0; q < n4; ++q) {
+            const int4 v = ids4[q];
+            c += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
+        }
         offsets[e] = c;
     }
 }
