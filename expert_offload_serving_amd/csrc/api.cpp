@@ -133,7 +133,7 @@ int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, 
     moe::Layer ml{L.H, L.I, L.E, L.k, static_cast<const uint8_t*>(L.bank_base), L.slot_bytes, L.slot_of_expert,
                   static_cast<const uint8_t*>(L.shared_slot), L.shared_gate_w};
     hipError_t e;
-    if (moe::decode_path(T, L.H, L.I)) {
+    if (moe::decode_path(T, L.H, L.I, L.k)) {
         e = moe::launch_decode(ml, x, T, topk_w, topk_ids, expert_offsets, sorted_assign, assign_pos, y, accumulate,
                                ws, stream);
     } else {

@@ -8,12 +8,13 @@
 //            (K = H), reduced across the workgroup's waves, SwiGLU;
 //   phase B  the down columns of the slice against the 32 hidden values,
 //            giving a partial sum over all H outputs, times the routing weight.
-// Both phases stream their weights with one 16-byte load per lane per record,
-// and the down records are in flight while phase A computes, so one kernel
-// moves all of an item's bytes.  A second kernel adds the partial outputs of
-// every (expert, slice) of a token in a fixed order and the shared expert's
-// sigmoid-gated term (PR #385 "What this adds": routed + sigmoid(gate) *
-// shared before one reduction).
+// Both phases stream their weights with one 16-byte load per lane per record.
+// The kernel is persistent (one workgroup per CU): while an item reduces,
+// runs SwiGLU and its down phase, the next item's loads are already in
+// flight.  A second kernel scales each row's slice sum by the expert's
+// down-row globals and adds the rows of a token in a fixed order with the
+// shared expert's sigmoid-gated term (PR #385 "What this adds": routed +
+// sigmoid(gate) * shared before one reduction).
 //
 // Arithmetic: v_mfma_f32_16x16x32_f16 with the weights as the 16-row operand
 // and up to 16 tokens as the 16 columns.  Weights decode exactly to fp16
@@ -29,10 +30,10 @@
 namespace moe {
 namespace {
 
-constexpr int kDW = 8;              // waves per work item
-constexpr int kDT = kDW * kWave;    // threads per work item
+constexpr int kDW = 8;              // waves per workgroup
+constexpr int kDT = kDW * kWave;    // threads per workgroup
 constexpr int kSl = 32;             // intermediate rows per work item
-constexpr int kMaxChunks = 16;      // E <= 1024 experts, 64 per ballot
+constexpr int kMaxE = 1024;         // experts (64 per ballot chunk)
 
 struct DecArgs {
     const uint8_t* bank;
@@ -45,229 +46,213 @@ struct DecArgs {
     const float* w;
     const int32_t* offsets;
     const int32_t* sorted_assign;
-    float* part;   // [(T*k + T) * nsl, H]: row (assignment or T*k + token) * nsl + slice
+    float* part;   // [(T*k + T) * nsl, H]: row (assignment or T*k + token) * nsl + slice, times the row's weight
+    int32_t* rowslot;  // [(T*k + T)]: slot of each row's expert (-1 left out, -2 shared)
     float* y;
     int accumulate;
-    size_t gu_codes, gu_scales, gu_glob, dn_codes, dn_scales, dn_glob;
+    int gu_codes, gu_scales, gu_glob, dn_codes, dn_scales, dn_glob;  // region offsets in a slot
 };
 
-struct ItemExpert {
-    int e;       // expert, E for the shared expert, -1 for no work
-    int begin;   // first position in sorted_assign (routed experts)
-    int count;   // assignments of the expert
+// Routing tables staged in LDS once per workgroup.
+struct Tables {
+    int off[kMaxE + 1];          // expert_offsets
+    int slot[kMaxE];             // slot_of_expert
+    int sorted[kDecodeMaxAssign];
+    float w[kDecodeMaxAssign];
+    int act[kMaxE];              // experts with assignments, ascending
+    int n_act;
 };
 
-// Item u -> the u-th expert (ascending) that has assignments; u equal to the
-// number of such experts is the shared expert.  All lanes agree.
-__device__ ItemExpert item_expert(const DecArgs& a, int u, int lane) {
-    int lo[kMaxChunks], hi[kMaxChunks];
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-        const int e = 64 * c + lane;
-        lo[c] = e < a.E ? a.offsets[e] : 0;
-        hi[c] = e < a.E ? a.offsets[e + 1] : 0;
-    }
-    ItemExpert r{-1, 0, 0};
-    int base = 0;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-        const bool act = hi[c] > lo[c];
-        const uint64_t m = __ballot(act);
-        const int n = __popcll(m);
-        if (r.e < 0 && u < base + n) {
-            const uint64_t hit = __ballot(act && __popcll(m & below) == u - base);
-            const int li = __ffsll((unsigned long long)hit) - 1;
-            r.e = 64 * c + li;
-            r.begin = __builtin_amdgcn_readlane(lo[c], li);
-            r.count = __builtin_amdgcn_readlane(hi[c], li) - r.begin;
-        }
-        base += n;
-    }
-    if (r.e < 0 && u == base) r.e = a.E;
-    return r;
+// A work item as seen by one lane: its slice, its tokens (the MFMA's 16
+// columns) and the expert's slot as a buffer resource (0 bytes when the
+// expert is left out or there is no item, so every load reads zeros).
+struct Item {
+    int s, ne, begin;
+    bool shared;     // the shared expert (rows T*k + token) rather than a routed one
+    int slot_index;  // the expert's slot, -1 when left out, -2 for the shared expert
+    int tok, prow;   // this lane's column: token (-1: none) and output row
+    float wc;        // this lane's column weight
+    rsrc_t sres;
+};
+
+// Branch-free on purpose: with a divergent branch (c < ne) inside the
+// routed/shared choice, the compiler would treat the slot as divergent and
+// wrap every buffer load in a readfirstlane loop.  n_act must be
+// wave-uniform (read with readfirstlane).
+__device__ __forceinline__ Item decode_item(const DecArgs& a, const Tables& tb, int n_act, int nsl, int u, bool valid,
+                                            int c) {
+    Item it;
+    const int ui = u / nsl;
+    it.s = u % nsl;
+    const bool routed = valid && ui < n_act;
+    const bool shared = valid && !routed;
+    const int e = __builtin_amdgcn_readfirstlane(tb.act[routed ? ui : 0]);
+    const int e_ok = routed ? e : 0;
+    const int b0 = __builtin_amdgcn_readfirstlane(tb.off[e_ok]);
+    const int b1 = __builtin_amdgcn_readfirstlane(tb.off[e_ok + 1]);
+    const int sl = __builtin_amdgcn_readfirstlane(tb.slot[e_ok]);
+    it.shared = shared;
+    it.begin = routed ? b0 : 0;
+    it.ne = routed ? b1 - b0 : (shared ? a.T : 0);
+    it.slot_index = routed ? sl : (shared ? -2 : -1);
+    const uint8_t* slot = routed ? (sl >= 0 ? a.bank + (size_t)sl * a.slot_bytes : nullptr) : (shared ? a.shared : nullptr);
+    it.sres = make_rsrc(slot != nullptr ? slot : a.bank, slot != nullptr ? (uint32_t)a.slot_bytes : 0u);
+    const bool has_col = c < it.ne;
+    const int as = tb.sorted[it.begin + (routed && has_col ? c : 0)];
+    const float ws = tb.w[routed && has_col ? as : 0];
+    it.tok = !has_col ? -1 : (routed ? as / a.k : c);
+    it.prow = !has_col ? 0 : (routed ? as : a.T * a.k + c);
+    it.wc = !has_col ? 0.0f : (routed ? ws : 1.0f);
+    return it;
 }
 
-// One work item per workgroup.  KQW: most 128-column steps of K = H per wave
-// (steps wave, wave + 8, ...); NRGW: most 64-row down groups per wave.
-template <int KQW, int NRGW>
-__global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
-    __shared__ __attribute__((aligned(16))) f32x4_t red[kDW][4][kWave];
-    __shared__ float hmax[kDW][16];
-    __shared__ __attribute__((aligned(16))) _Float16 hs[16][kSl];
-
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int u = blockIdx.x / nsl, s = blockIdx.x % nsl;
-    const int H = a.H, I = a.I, T = a.T, k = a.k;
-    const ItemExpert it = item_expert(a, u, lane);
-    if (it.e < 0 || (it.e == a.E && a.shared == nullptr)) return;  // uniform
-
-    // Column c of the MFMA is the item's c-th token.
-    const int c = lane & 15, g = lane >> 4;
-    int ne, tok = -1, prow = 0;
-    float wc = 0.0f;
-    const uint8_t* slot;
-    if (it.e < a.E) {
-        ne = it.count;
-        if (c < ne) {
-            const int as = a.sorted_assign[it.begin + c];
-            tok = as / k;
-            prow = as;
-            wc = a.w[as];
-        }
-        const int sl = __builtin_amdgcn_readfirstlane(a.slot_of_expert[it.e]);
-        slot = sl >= 0 ? a.bank + (size_t)sl * a.slot_bytes : nullptr;
-    } else {
-        ne = T;
-        if (c < ne) tok = c, prow = T * k + c, wc = 1.0f;
-        slot = a.shared;
-    }
-    float* prow_ptr = a.part + ((size_t)prow * nsl + s) * H;
-
-    if (slot == nullptr) {  // expert left out of this call: its partial outputs are zero
-        for (int cc = 0; cc < ne; ++cc) {
-            const int pr = a.sorted_assign[it.begin + cc];
-            f32x4_t* dst = reinterpret_cast<f32x4_t*>(a.part + ((size_t)pr * nsl + s) * H);
-            for (int v = tid; v < H / 4; v += kDT) dst[v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-        return;
-    }
-
-    const int KQ = H / 128, NT = 2 * I / 16, NG = H / 64;
-    const rsrc_t xres = make_rsrc(a.x, (uint32_t)T * H * 2);
-    const rsrc_t sres = make_rsrc(slot, (uint32_t)a.slot_bytes);
-    const int gcodes = (int)a.gu_codes, gscales = (int)a.gu_scales, gglob = (int)a.gu_glob;
-    const int dcodes = (int)a.dn_codes, dscales = (int)a.dn_scales, dglob = (int)a.dn_glob;
-    const int tiles[4] = {2 * s, 2 * s + 1, I / 16 + 2 * s, I / 16 + 2 * s + 1};  // gate, gate, up, up
-    const int soff = lane_scale_off(lane);
-
-    // ---- issue every load of the item in one straight line: activations
-    // first, then gate_up records, then down records (absent ones read as 0)
-    u32x4_t xr[KQW][4];
-#pragma unroll
-    for (int i = 0; i < KQW; ++i) {
-        const int kq = wave + kDW * i;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            xr[i][m] = buf_load16(xres, (kq < KQ && tok >= 0) ? 2 * (tok * H + 128 * kq + 32 * m + 8 * g) : kOob);
-    }
-    u32x4_t ar[KQW][4];
-    uint32_t asc[KQW][4];
-#pragma unroll
-    for (int i = 0; i < KQW; ++i) {
-        const int kq = wave + kDW * i;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int rec = kq * NT + tiles[tt];
-            ar[i][tt] = buf_load16(sres, kq < KQ ? gcodes + rec * kRecBytes + 16 * lane : kOob);
-            asc[i][tt] = buf_load4(sres, kq < KQ ? gscales + rec * kRecScaleBytes + soff : kOob);
-        }
-    }
+// Per-lane loads of one item: phase A (gate/up records, their scales and the
+// SwiGLU thread's two row globals) and phase B (down records and scales).
+template <int KQW>
+struct ALoads {
+    u32x4_t ar[KQW][2];
+    uint32_t asc[KQW][2];
+    float glob;  // lane l < 32: gate global of slice row l; lane l >= 32: up global of slice row l - 32
+};
+template <int NRGW>
+struct BLoads {
     u32x4_t br[NRGW];
     uint32_t bsc[NRGW];
+};
+
+// Phase A split: wave w takes the two gate tiles (w < 4) or the two up tiles
+// (w >= 4) of the slice, over the 128-column steps kq = w % 4 + 4 i.
+template <int KQW>
+__device__ __forceinline__ void issue_a(const DecArgs& a, const Item& it, int wave, int lane, int tid,
+                                        ALoads<KQW>& L) {
+    const int H = a.H, I = a.I, KQ = H / 128, NT = 2 * I / 16;
+    const int s = it.s;
+    const int t0 = (wave >> 2) * (I / 16) + 2 * s;  // first of this wave's two tiles
+    const int soff = lane_scale_off(lane);
+#pragma unroll
+    for (int i = 0; i < KQW; ++i) {
+        const int kq = (wave & 3) + 4 * i;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int rec = kq * NT + t0 + tt;
+            L.ar[i][tt] = buf_load16(it.sres, kq < KQ ? a.gu_codes + rec * kRecBytes + 16 * lane : kOob);
+            L.asc[i][tt] = buf_load4(it.sres, kq < KQ ? a.gu_scales + rec * kRecScaleBytes + soff : kOob);
+        }
+    }
+    (void)tid;
+    L.glob = __uint_as_float(buf_load4(it.sres, a.gu_glob + 4 * ((lane >> 5) * I + kSl * s + (lane & 31))));
+}
+
+template <int NRGW>
+__device__ __forceinline__ void issue_b(const DecArgs& a, const Item& it, int wave, int lane, BLoads<NRGW>& L) {
+    const int NG = a.H / 64, soff = lane_scale_off(lane);
 #pragma unroll
     for (int i = 0; i < NRGW; ++i) {
         const int rg = wave + kDW * i;
-        const int rec = s * NG + rg;
-        br[i] = buf_load16(sres, rg < NG ? dcodes + rec * kRecBytes + 16 * lane : kOob);
-        bsc[i] = buf_load4(sres, rg < NG ? dscales + rec * kRecScaleBytes + soff : kOob);
+        const int rec = it.s * NG + rg;
+        L.br[i] = buf_load16(it.sres, rg < NG ? a.dn_codes + rec * kRecBytes + 16 * lane : kOob);
+        L.bsc[i] = buf_load4(it.sres, rg < NG ? a.dn_scales + rec * kRecScaleBytes + soff : kOob);
     }
-    // SwiGLU thread (hi, ht): hidden row hi of the slice, token column ht
-    const int hi = tid >> 4, ht = tid & 15;
-    const float g_glob = __uint_as_float(buf_load4(sres, gglob + 4 * (kSl * s + hi)));
-    const float u_glob = __uint_as_float(buf_load4(sres, gglob + 4 * (I + kSl * s + hi)));
-    // keep the scheduler from sinking loads towards their uses: all of them
-    // must be in flight before the first wait
-    __builtin_amdgcn_sched_barrier(0);
+}
 
-    // ---- activations: per-(wave, token) power-of-two scale, exact fp16
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < KQW; ++i)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t wv = word_of(xr[i][m], d);
-                amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(wv << 16)), fabsf(__uint_as_float(wv & 0xFFFF0000u))));
-            }
-    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-    const int xsh = fp16_shift(amax);
-    const float xsc = ldexpf(1.0f, xsh), xinv = ldexpf(1.0f, -xsh);
+// Workgroup LDS besides the activations.
+struct DecShared {
+    f32x4_t red[2][kDW][2][kWave];  // phase A partial sums of every wave, double-buffered by item parity
+    int xsh[kDecodeMaxT + 1];       // per-token activation exponent shift (row T: the zero row)
+    Tables tb;
+};
 
-    // ---- phase A: gate and up rows of the slice, this wave's share of K
-    f32x4_t acc[4];
+// One work item.  Consumes LA (phase A) and LB (phase B) of `cur`; refills
+// LA with the loads of item na and, after phase B, LB with those of item nb.
+template <int KQW, int NRGW>
+__device__ __forceinline__ void run_item(const DecArgs& a, DecShared& sh, const _Float16* x16, int XP, int nsl,
+                                         const rsrc_t& pres, const Item& cur, ALoads<KQW>& LA, BLoads<NRGW>& LB,
+                                         const Item& na, const Item& nb, int tid, int lane, int wave, int par) {
+    const int H = a.H, T = a.T, k = a.k, KQ = H / 128, NG = H / 64;
+    const int c = lane & 15, g = lane >> 4;
+    const int xrow = cur.tok >= 0 ? cur.tok : T;  // this lane's activation row (T: zeros)
+    const _Float16* xr = x16 + xrow * XP + 8 * g;
+
+    // ---- phase A: this wave's two tiles of the slice over its share of K
+    f32x4_t acc[2];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int tt = 0; tt < 2; ++tt) acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < KQW; ++i) {
-        if (wave + kDW * i >= KQ) break;  // uniform per wave
+        const int kq = (wave & 3) + 4 * i;
+        if (kq >= KQ) break;  // uniform per wave
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            uint32_t xh[4];
+            const f16x8_t X = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(xr + 128 * kq + 32 * m));
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t wv = word_of(xr[i][m], d);
-                const f16x2_t p = {(_Float16)(__uint_as_float(wv << 16) * xsc),
-                                   (_Float16)(__uint_as_float(wv & 0xFFFF0000u) * xsc)};
-                xh[d] = __builtin_bit_cast(uint32_t, p);
-            }
-            const f16x8_t X = __builtin_bit_cast(f16x8_t, u32x4_t{xh[0], xh[1], xh[2], xh[3]});
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
+            for (int tt = 0; tt < 2; ++tt) {
                 f16x2_t S;
-                if (m == 0) S = scale_f16x2<0>(asc[i][tt]);
-                else if (m == 1) S = scale_f16x2<1>(asc[i][tt]);
-                else if (m == 2) S = scale_f16x2<2>(asc[i][tt]);
-                else S = scale_f16x2<3>(asc[i][tt]);
-                const f16x8_t A = frag_f16(word_of(ar[i][tt], m), S);
+                if (m == 0) S = scale_f16x2<0>(LA.asc[i][tt]);
+                else if (m == 1) S = scale_f16x2<1>(LA.asc[i][tt]);
+                else if (m == 2) S = scale_f16x2<2>(LA.asc[i][tt]);
+                else S = scale_f16x2<3>(LA.asc[i][tt]);
+                const f16x8_t A = frag_f16(word_of(LA.ar[i][tt], m), S);
                 acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, X, acc[tt], 0, 0, 0);
             }
         }
     }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) red[wave][tt][lane] = acc[tt] * xinv;
+    const float glob = LA.glob;
+    // slice 0 records, per output row of the item, where the expert's down globals live
+    if (cur.s == 0)
+        for (int cc = tid; cc < cur.ne; cc += kDT)
+            a.rowslot[cur.shared ? T * k + cc : sh.tb.sorted[cur.begin + cc]] = cur.slot_index;
 
-    // down globals of this wave's output rows (lane rows 16j + 4g + [0, 4) of each group)
-    f32x4_t dg[NRGW][4];
+    // ---- the registers of phase A are free: item na's phase A loads stream from here on
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a<KQW>(a, na, wave, lane, tid, LA);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const float xinv = ldexpf(1.0f, -sh.xsh[xrow]);
 #pragma unroll
-    for (int i = 0; i < NRGW; ++i) {
-        const int rg = wave + kDW * i;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dg[i][j] = __builtin_bit_cast(f32x4_t, buf_load16(sres, rg < NG ? dglob + 4 * (64 * rg + 16 * j + 4 * g)
-                                                                          : kOob));
-    }
+    for (int tt = 0; tt < 2; ++tt) sh.red[par][wave][tt][lane] = acc[tt] * xinv;
     __syncthreads();
 
-    // ---- SwiGLU: thread (hi, ht) sums its gate and up values over the waves in order
-    float hv;
+    // ---- SwiGLU, computed by every wave for exactly the values its phase B
+    // operand needs: lane (c, g) takes hidden rows 8g + [0, 8) of token c.
+    // Gate sums come from waves 0-3 and up sums from waves 4-7, added in order.
+    f16x8_t B;
+    float oscale;
     {
-        const int tt = hi >> 4, r = hi & 15, L = 16 * (r >> 2) + ht, ii = r & 3;
-        float gs = 0.0f, us = 0.0f;
+        const int tt = g >> 1, L0 = 32 * (g & 1) + c;  // rows 8(g & 1) + [0,4) and + [4,8) of tile tt
+        f32x4_t gs0 = {0.0f, 0.0f, 0.0f, 0.0f}, gs1 = gs0, us0 = gs0, us1 = gs0;
 #pragma unroll
-        for (int w = 0; w < kDW; ++w) {
-            gs += red[w][tt][L][ii];
-            us += red[w][2 + tt][L][ii];
+        for (int w = 0; w < 4; ++w) {
+            gs0 += sh.red[par][w][tt][L0];
+            gs1 += sh.red[par][w][tt][L0 + 16];
+            us0 += sh.red[par][4 + w][tt][L0];
+            us1 += sh.red[par][4 + w][tt][L0 + 16];
         }
-        const float gv = gs * g_glob, uv = us * u_glob;
-        hv = gv / (1.0f + expf(-gv)) * uv;
-        float hm = fabsf(hv);
+        float h[8];
+        float hm = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float gsum = e < 4 ? gs0[e] : gs1[e - 4], usum = e < 4 ? us0[e] : us1[e - 4];
+            const float gv = gsum * __shfl(glob, 8 * g + e, kWave);
+            const float uv = usum * __shfl(glob, 32 + 8 * g + e, kWave);
+            h[e] = gv / (1.0f + expf(-gv)) * uv;
+            hm = fmaxf(hm, fabsf(h[e]));
+        }
         hm = fmaxf(hm, __shfl_xor(hm, 16, kWave));
         hm = fmaxf(hm, __shfl_xor(hm, 32, kWave));
-        if (lane < 16) hmax[wave][lane] = hm;
-    }
-    __syncthreads();
-    float hm_t = 0.0f, hm_c = 0.0f;
+        const int hsh = fp16_shift(hm);
+        const float hsc = ldexpf(1.0f, hsh);
+        uint32_t hw[4];
 #pragma unroll
-    for (int w = 0; w < kDW; ++w) hm_t = fmaxf(hm_t, hmax[w][ht]), hm_c = fmaxf(hm_c, hmax[w][c]);
-    hs[ht][hi] = (_Float16)(hv * ldexpf(1.0f, fp16_shift(hm_t)));
-    __syncthreads();
+        for (int d = 0; d < 4; ++d) {
+            const f16x2_t q = {(_Float16)(h[2 * d] * hsc), (_Float16)(h[2 * d + 1] * hsc)};
+            hw[d] = __builtin_bit_cast(uint32_t, q);
+        }
+        B = __builtin_bit_cast(f16x8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
+        oscale = ldexpf(1.0f, -hsh) * cur.wc;
+    }
 
     // ---- phase B: the slice's 32 down columns for this wave's row groups
-    const f16x8_t B = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(&hs[c][8 * g]));
-    const float oscale = ldexpf(1.0f, -fp16_shift(hm_c)) * wc;
+    const int pbase = c < cur.ne ? 4 * ((cur.prow * nsl + cur.s) * H + 4 * g) : kOob;
 #pragma unroll
     for (int i = 0; i < NRGW; ++i) {
         const int rg = wave + kDW * i;
@@ -275,27 +260,175 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             f16x2_t S;
-            if (j == 0) S = scale_f16x2<0>(bsc[i]);
-            else if (j == 1) S = scale_f16x2<1>(bsc[i]);
-            else if (j == 2) S = scale_f16x2<2>(bsc[i]);
-            else S = scale_f16x2<3>(bsc[i]);
-            const f16x8_t A = frag_f16(word_of(br[i], j), S);
-            const f32x4_t D =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            if (c < ne) {
-                const f32x4_t o = (D * oscale) * dg[i][j];
-                *reinterpret_cast<f32x4_t*>(prow_ptr + 64 * rg + 16 * j + 4 * g) = o;
+            if (j == 0) S = scale_f16x2<0>(LB.bsc[i]);
+            else if (j == 1) S = scale_f16x2<1>(LB.bsc[i]);
+            else if (j == 2) S = scale_f16x2<2>(LB.bsc[i]);
+            else S = scale_f16x2<3>(LB.bsc[i]);
+            const f16x8_t A = frag_f16(word_of(LB.br[i], j), S);
+            const f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            buf_store16(pres, pbase + 4 * (64 * rg + 16 * j), D * oscale);
+        }
+    }
+
+    // ---- item nb's phase B loads
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b<NRGW>(a, nb, wave, lane, LB);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Persistent over work items u = blockIdx.x + j * gridDim.x; item u is
+// (expert act[u / nsl], or the shared expert, slice u % nsl).  Every token's
+// activations are staged in LDS once, as fp16 times a per-token power of two.
+// Phase A loads run two items ahead and phase B loads one item ahead, so the
+// next items stream while this one reduces, runs SwiGLU and finishes.
+// KQW: most 128-column steps of K = H per wave (steps wave % 4 + 4 i);
+// NRGW: most 64-row down groups per wave (groups wave + 8 i).
+template <int KQW, int NRGW>
+__global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
+    extern __shared__ __attribute__((aligned(16))) _Float16 x16[];  // (T + 1) rows of XP halves; row T is zero
+    __shared__ DecShared sh;
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int H = a.H, T = a.T, k = a.k, E = a.E;
+    const int XP = H + 8;  // padded row: rows of different tokens start 16 bytes apart modulo the LDS banks
+    Tables& tb = sh.tb;
+
+    // ---- stage the routing tables (issued first, so waiting for them waits for nothing else)
+    const int n = T * k;
+    constexpr int R = (kMaxE + 1 + kDT - 1) / kDT;
+    constexpr int XC = 2560 / 8 / kWave;  // 16-byte chunks of a token row per lane (H <= 2560)
+    uint32_t vo[R], vs[R], va[2], vw[2];
+    u32x4_t xv[2][XC];
+    {
+        const rsrc_t ro = make_rsrc(a.offsets, (uint32_t)(E + 1) * 4);
+        const rsrc_t rs = make_rsrc(a.slot_of_expert, (uint32_t)E * 4);
+        const rsrc_t ra = make_rsrc(a.sorted_assign, (uint32_t)n * 4);
+        const rsrc_t rw = make_rsrc(a.w, (uint32_t)n * 4);
+        const rsrc_t rx = make_rsrc(a.x, (uint32_t)T * H * 2);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = tid + kDT * r;
+            vo[r] = buf_load4(ro, i <= E ? 4 * i : kOob);
+            vs[r] = buf_load4(rs, i < E ? 4 * i : kOob);
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int i = tid + kDT * r;
+            va[r] = buf_load4(ra, i < n ? 4 * i : kOob);
+            vw[r] = buf_load4(rw, i < n ? 4 * i : kOob);
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {  // activations: wave w stages tokens w and w + 8
+            const int t = wave + kDW * p;
+#pragma unroll
+            for (int i = 0; i < XC; ++i) {
+                const int ch = lane + kWave * i;
+                xv[p][i] = buf_load16(rx, t < T && ch < H / 8 ? 2 * (t * H + 8 * ch) : kOob);
             }
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = tid + kDT * r;
+        if (i <= E) tb.off[i] = (int)vo[r];
+        if (i < E) tb.slot[i] = (int)vs[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int i = tid + kDT * r;
+        if (i < n) tb.sorted[i] = (int)va[r], tb.w[i] = __uint_as_float(vw[r]);
+    }
+    __syncthreads();
+    if (wave == 0) {  // compaction of the experts with assignments, ascending
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        int base = 0;
+        for (int e0 = 0; e0 < E; e0 += kWave) {
+            const int e = e0 + lane;
+            const bool act = e < E && tb.off[e + 1] > tb.off[e];
+            const uint64_t m = __ballot(act);
+            if (act) tb.act[base + __popcll(m & below)] = e;
+            base += __popcll(m);
+        }
+        if (lane == 0) tb.n_act = base;
+    }
+    __syncthreads();
+    const int n_act = __builtin_amdgcn_readfirstlane(tb.n_act);
+    const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
+    int u = blockIdx.x;
+    if (u >= n_items) return;  // uniform
+
+    // ---- activations: fp16 times a per-token power of two, into LDS
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int t = wave + kDW * p;
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < XC; ++i)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t wv = word_of(xv[p][i], d);
+                amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(wv << 16)), fabsf(__uint_as_float(wv & 0xFFFF0000u))));
+            }
+        amax = wave_max(amax);
+        const int sh_t = fp16_shift(amax);
+        const float sc = ldexpf(1.0f, sh_t);
+        if (t < T) {
+            if (lane == 0) sh.xsh[t] = sh_t;
+#pragma unroll
+            for (int i = 0; i < XC; ++i) {
+                const int ch = lane + kWave * i;
+                if (ch >= H / 8) continue;
+                uint32_t hw[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t wv = word_of(xv[p][i], d);
+                    const f16x2_t q = {(_Float16)(__uint_as_float(wv << 16) * sc),
+                                       (_Float16)(__uint_as_float(wv & 0xFFFF0000u) * sc)};
+                    hw[d] = __builtin_bit_cast(uint32_t, q);
+                }
+                *reinterpret_cast<u32x4_t*>(x16 + t * XP + 8 * ch) = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+            }
+        }
+    }
+    for (int ch = tid; ch < XP / 8; ch += kDT)  // the zero row
+        *reinterpret_cast<u32x4_t*>(x16 + T * XP + 8 * ch) = u32x4_t{0, 0, 0, 0};
+    if (tid == 0) sh.xsh[T] = 0;
+    // ---- the first items' weights start streaming (the activations arrived first)
+    const int G = (int)gridDim.x, c = lane & 15;
+    const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
+    Item it0 = decode_item(a, tb, n_act, nsl, u, true, c);
+    Item it1 = decode_item(a, tb, n_act, nsl, u + G, u + G < n_items, c);
+    ALoads<KQW> LA0, LA1;
+    BLoads<NRGW> LB;
+    issue_a<KQW>(a, it0, wave, lane, tid, LA0);
+    issue_b<NRGW>(a, it0, wave, lane, LB);
+    issue_a<KQW>(a, it1, wave, lane, tid, LA1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    __syncthreads();
+
+    for (;;) {
+        const Item it2 = decode_item(a, tb, n_act, nsl, u + 2 * G, u + 2 * G < n_items, c);
+        run_item<KQW, NRGW>(a, sh, x16, XP, nsl, pres, it0, LA0, LB, it2, it1, tid, lane, wave, 0);
+        if (u + G >= n_items) break;
+        const Item it3 = decode_item(a, tb, n_act, nsl, u + 3 * G, u + 3 * G < n_items, c);
+        run_item<KQW, NRGW>(a, sh, x16, XP, nsl, pres, it1, LA1, LB, it3, it2, tid, lane, wave, 1);
+        if (u + 2 * G >= n_items) break;
+        u += 2 * G;
+        it0 = it2;
+        it1 = it3;
+    }
 }
 
-// y_t = sum over (j, slice) of the routed partials of token t, plus
-// sigmoid(x_t . w_g) times the shared expert's partials, in a fixed order.
-// Workgroup: one token and 64 output columns; thread (q, cl) sums partial
-// rows q, q + 16, ... of columns [4 cl, 4 cl + 4).  Each pass issues all of
-// its loads before the first add (partial rows past the end read as zero).
-constexpr int kCR = 16;  // partial rows per thread per pass
+// y_t = sum_j dg_j * (sum over slices of row j's partials) over the routed
+// rows j of token t, plus sigmoid(x_t . w_g) * dg_sh * (shared partials), in a
+// fixed order; dg_j are the down-row globals of row j's expert, found through
+// the slot the forward kernel recorded for the row.  Workgroup: one token and 64 output columns; thread (q, cl)
+// handles row q (q < k: assignment t*k + q; q == k: the shared expert) of
+// columns [4 cl, 4 cl + 4).  The first pass issues all of its loads before
+// the first add (rows and slices past the end read as zero).
+constexpr int kCS = 32;  // slices per row loaded in the first pass
 __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int nch) {
     __shared__ f32x4_t rr[16][16], rsh[16][16];
     __shared__ float dots[4];
@@ -303,57 +436,35 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, cl = tid & 15, q = tid >> 4;
     const int H = a.H, k = a.k, T = a.T;
     const int col = 64 * ch + 4 * cl;
-    const int nr = k * nsl;
-    const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
-    const int rbase = t * k * nsl, sbase = (T * k + t) * nsl;
     const bool has_shared = a.shared != nullptr;
+    const int nrows = k + (has_shared ? 1 : 0);
+    const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
     f32x4_t sr = {0.0f, 0.0f, 0.0f, 0.0f}, ss = {0.0f, 0.0f, 0.0f, 0.0f};
     float gd = 0.0f;
-    {
-        f32x4_t v[kCR], vs[2];
-        u32x4_t xv[2], wv[2];
+    for (int j = q; j < nrows; j += 16) {
+        const int row = j < k ? t * k + j : T * k + t;
+        f32x4_t v[kCS];
 #pragma unroll
-        for (int i = 0; i < kCR; ++i) {
-            const int r = q + 16 * i;
-            v[i] = __builtin_bit_cast(f32x4_t, buf_load16(pres, r < nr ? 4 * ((rbase + r) * H + col) : kOob));
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = q + 16 * i;
-            vs[i] = __builtin_bit_cast(f32x4_t,
-                                       buf_load16(pres, has_shared && r < nsl ? 4 * ((sbase + r) * H + col) : kOob));
-        }
-        const rsrc_t xres = make_rsrc(a.x + (size_t)t * H, (uint32_t)H * 2);
-        const rsrc_t gres = make_rsrc(a.wg, has_shared ? (uint32_t)H * 2 : 0u);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int vv = tid + 256 * i;
-            xv[i] = buf_load16(xres, has_shared && vv < H / 8 ? 16 * vv : kOob);
-            wv[i] = buf_load16(gres, has_shared && vv < H / 8 ? 16 * vv : kOob);
-        }
+        for (int i = 0; i < kCS; ++i)
+            v[i] = __builtin_bit_cast(f32x4_t, buf_load16(pres, i < nsl ? 4 * ((row * nsl + i) * H + col) : kOob));
+        const int rs = a.rowslot[row];
+        const uint8_t* slot = rs >= 0 ? a.bank + (size_t)rs * a.slot_bytes : (rs == -2 ? a.shared : a.bank);
+        const rsrc_t gsr = make_rsrc(slot, rs == -1 ? 0u : (uint32_t)a.slot_bytes);
+        const f32x4_t dg = __builtin_bit_cast(f32x4_t, buf_load16(gsr, a.dn_glob + 4 * col));
         __builtin_amdgcn_sched_barrier(0);
+        f32x4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < kCR; ++i) sr += v[i];
-        ss = vs[0] + vs[1];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            gd = dot2_bf16(as_bf16x2(xv[i].x), as_bf16x2(wv[i].x), gd);
-            gd = dot2_bf16(as_bf16x2(xv[i].y), as_bf16x2(wv[i].y), gd);
-            gd = dot2_bf16(as_bf16x2(xv[i].z), as_bf16x2(wv[i].z), gd);
-            gd = dot2_bf16(as_bf16x2(xv[i].w), as_bf16x2(wv[i].w), gd);
-        }
+        for (int i = 0; i < kCS; ++i) sum += v[i];
+        for (int i = kCS; i < nsl; ++i)
+            sum += __builtin_bit_cast(f32x4_t, buf_load16(pres, 4 * ((row * nsl + i) * H + col)));
+        if (j < k) sr += sum * dg;
+        else ss = sum * dg;
     }
-    // rare shapes: more partial rows, or more of the shared expert / H, than one pass covers
-    for (int r0 = 16 * kCR; r0 < nr; r0 += 16 * kCR)
-        for (int r = r0 + q; r < nr && r < r0 + 16 * kCR; r += 16)
-            sr += __builtin_bit_cast(f32x4_t, buf_load16(pres, 4 * ((rbase + r) * H + col)));
     if (has_shared) {
-        for (int r = q + 32; r < nsl; r += 16)
-            ss += __builtin_bit_cast(f32x4_t, buf_load16(pres, 4 * ((sbase + r) * H + col)));
-        const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * H);
-        const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(a.wg);
-        for (int vv = tid + 512; vv < H / 8; vv += 256) {
-            const u32x4_t xx = xp[vv], ww = wp[vv];
+        const rsrc_t xres = make_rsrc(a.x + (size_t)t * H, (uint32_t)H * 2);
+        const rsrc_t gres = make_rsrc(a.wg, (uint32_t)H * 2);
+        for (int vv = tid; vv < H / 8; vv += 256) {
+            const u32x4_t xx = buf_load16(xres, 16 * vv), ww = buf_load16(gres, 16 * vv);
             gd = dot2_bf16(as_bf16x2(xx.x), as_bf16x2(ww.x), gd);
             gd = dot2_bf16(as_bf16x2(xx.y), as_bf16x2(ww.y), gd);
             gd = dot2_bf16(as_bf16x2(xx.z), as_bf16x2(ww.z), gd);
@@ -376,19 +487,38 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
     *yp = out;
 }
 
+int g_num_cu = 0;
+
+constexpr size_t kXLdsMax = (size_t)(kDecodeMaxT + 1) * (2560 + 8) * 2;
+
 template <int KQW, int NRGW>
-hipError_t launch_fused(const DecArgs& a, int items, int nsl, hipStream_t s) {
-    hipLaunchKernelGGL((fused_kernel<KQW, NRGW>), dim3(items * nsl), dim3(kDT), 0, s, a, nsl);
+hipError_t launch_fused(const DecArgs& a, int items_max, int nsl, hipStream_t s) {
+    static bool attr_set = false;
+    if (g_num_cu == 0 || !attr_set) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&g_num_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int grid = items_max < g_num_cu ? items_max : g_num_cu;
+    const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
+    hipLaunchKernelGGL((fused_kernel<KQW, NRGW>), dim3(grid), dim3(kDT), lds, s, a, nsl);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Per-wave register budget: the kernel keeps all of an item's loads in
-// flight at once, sized for H up to 3072 (larger H runs the prefill path).
-bool decode_shape_supported(int H, int I) { return H % 128 == 0 && I % kSl == 0 && H <= 3072; }
+// Per-wave register budget: the kernel keeps an item's loads in flight at
+// once (up to 5 steps of 128 columns and 5 row groups of 64 per wave), sized
+// for H up to 2560; larger H runs the prefill path.
+bool decode_shape_supported(int H, int I) { return H % 128 == 0 && I % kSl == 0 && H <= 2560; }
 
 size_t decode_part_bytes(int T, int H, int I, int k) { return (size_t)(T * k + T) * (I / kSl) * H * 4; }
+size_t decode_rowslot_bytes(int T, int k) { return (size_t)(T * k + T) * 4; }
 
 hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                          const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
@@ -403,16 +533,15 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
     a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
     a.w = w; a.offsets = offsets; a.sorted_assign = sorted_assign;
     a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + wl.part);
+    a.rowslot = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + wl.dg);
     a.y = y; a.accumulate = accumulate;
     const SlotGeom gm = slot_geom(H, I);
-    a.gu_codes = gm.gu_codes; a.gu_scales = gm.gu_scales; a.gu_glob = gm.gu_glob;
-    a.dn_codes = gm.dn_codes; a.dn_scales = gm.dn_scales; a.dn_glob = gm.dn_glob;
+    a.gu_codes = (int)gm.gu_codes; a.gu_scales = (int)gm.gu_scales; a.gu_glob = (int)gm.gu_glob;
+    a.dn_codes = (int)gm.dn_codes; a.dn_scales = (int)gm.dn_scales; a.dn_glob = (int)gm.dn_glob;
 
     const int nsl = I / kSl;
-    const int items = (T * k < E ? T * k : E) + 1;
-    hipError_t e;
-    if (H <= 2560) e = launch_fused<3, 5>(a, items, nsl, s);
-    else e = launch_fused<3, 6>(a, items, nsl, s);
+    const int items_max = ((T * k < E ? T * k : E) + 1) * nsl;
+    hipError_t e = launch_fused<5, 5>(a, items_max, nsl, s);
     if (e != hipSuccess) return e;
     const int nch = H / 64;
     hipLaunchKernelGGL(dcombine_kernel, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);

@@ -33,27 +33,33 @@ SlotGeom slot_geom(int H, int I);
 // Decode path, T <= 16 (decode.hip): shapes it covers and the bytes of its
 // per-(row, slice) partial outputs.  Other shapes run the prefill path.
 constexpr int kDecodeMaxT = 16;
+constexpr int kDecodeMaxAssign = 1024;  // T*k
 bool decode_shape_supported(int H, int I);
 size_t decode_part_bytes(int T, int H, int I, int k);
-inline bool decode_path(int T, int H, int I) { return T <= kDecodeMaxT && decode_shape_supported(H, I); }
+size_t decode_rowslot_bytes(int T, int k);
+inline bool decode_path(int T, int H, int I, int k) {
+    return T <= kDecodeMaxT && T * k <= kDecodeMaxAssign && decode_shape_supported(H, I);
+}
 
 // Forward workspace: byte offsets of its regions (each 256-byte aligned).
-// The decode path uses only `part`; the prefill path uses the others:
+// The decode path uses `part` (per-(row, slice) partial outputs) and `dg`
+// (per-row slot of the row's expert); the prefill path uses the others:
 //   h      hidden state, (T*k + T) rows of I fp16 values
 //   o      per-assignment expert outputs, (T*k + T) rows of H f32
 //   s      shared-gate sigmoid per token, T f32
 //   x16    scaled fp16 activations [T, H]; xinv: their inverse scales [T]
 //   tiles  work lists: 4 counts, then 3 classes x tile_cap (group, m0) pairs
 struct WsLayout {
-    size_t part, h, o, s, x16, xinv, tiles, total;
+    size_t part, dg, h, o, s, x16, xinv, tiles, total;
     int tile_cap;
 };
 inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
     WsLayout L{};
-    if (decode_path(T, H, I)) {
+    if (decode_path(T, H, I, k)) {
         L.part = 0;
-        L.total = align256(decode_part_bytes(T, H, I, k));
+        L.dg = align256(decode_part_bytes(T, H, I, k));
+        L.total = L.dg + align256(decode_rowslot_bytes(T, k));
         return L;
     }
     const size_t rows = (size_t)T * k + T;

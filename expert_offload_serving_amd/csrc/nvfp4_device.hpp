@@ -54,6 +54,10 @@ __device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, int off) {
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, int off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
+// A store at an offset past the resource's size is dropped.
+__device__ __forceinline__ void buf_store16(rsrc_t r, int off, f32x4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
+}
 
 // E4M3 byte SEL of a scale dword as an fp16 pair (exact: E4M3 values fit fp16).
 template <int SEL>
@@ -138,6 +142,12 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<kWave>(v); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
 
 // Opaque to the optimiser: keeps code words from being decoded once and held
 // decoded across a loop (which would multiply their register footprint).
