@@ -402,31 +402,255 @@ __global__ void __launch_bounds__(256) gemm_kernel(PrefillArgs a, int cls, int n
     }
 }
 
-// ------------------------------------------------------------------ combine
-__global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a, int nchunk) {
-    __shared__ int pos_s[1024];
-    __shared__ float w_s[1024];
-    const int t = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
-    const int tid = threadIdx.x;
-    const int H = a.H, T = a.T, k = a.k;
-    for (int j = tid; j < k; j += 256) {
-        const int aidx = t * k + j;
-        const bool ok = a.slot_of_expert[a.ids[aidx]] >= 0;
-        pos_s[j] = ok ? a.assign_pos[aidx] : -1;
-        w_s[j] = a.w[aidx];
+// ------------------------------------------------------------------ big-tile GEMM (128-row tiles)
+// One workgroup computes a 128-token x 256-weight-row tile: gate_up: 128
+// h-columns (their 128 gate rows and 128 up rows); down: 256 output rows.
+// Wave (wm, wn) owns tokens [64 wm, 64 wm + 64) and 16 NB weight rows
+// (NB 16-row blocks: gate_up: NB/2 gate tiles and the matching up tiles;
+// down: NB/4 record groups), so each dequantised weight fragment feeds 4
+// MFMAs.  NB = 4 (8 waves, two per SIMD) measured faster than NB = 8 (4
+// waves with 512 registers each), whose single wave per SIMD could not hide
+// its dequantisation behind the matrix cores.  Per
+// 128-column step the activation tile (128 x 128 fp16) sits in LDS, written
+// from registers one step ahead; each wave's weight records are loaded two
+// steps ahead into a register ping-pong.  Load order per step end:
+// activations of step s + 2, then weights of step s + 2, so waiting for
+// either never waits for the other's newer loads.
+template <bool GATEUP, int NB>
+__global__ void __launch_bounds__(32 * kWave / NB) big_gemm_kernel(PrefillArgs a, int n_tiles_n) {
+    constexpr int BM = 128;
+    constexpr int NWN = 16 / NB;            // waves along the weight rows (2 along the tokens)
+    constexpr int NT = 2 * NWN * kWave;      // threads
+    constexpr int AQ = BM * 16 / NT;         // activation chunks per thread per step
+    __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * APITCH];
+    __shared__ int tok[BM];
+
+    const int tile = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
+    if (tile >= a.tiles[0]) return;
+    const int* te = a.tiles + 4 + 2 * tile;
+    const int g = te[0], m0 = te[1];
+    const int gb = group_begin(a, g), cnt = min(BM, group_end(a, g) - gb - m0);
+    const uint8_t* slot = group_slot(a, g);
+    const int H = a.H, I = a.I, T = a.T, k = a.k;
+    const int K = GATEUP ? H : I;
+    const int nsteps = (K + BK - 1) / BK;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / NWN, wn = wave % NWN;
+    const int l16 = lane & 15, q4 = lane >> 4;
+
+    if (GATEUP) {
+        for (int m = tid; m < BM; m += NT) {
+            int t = -1;
+            if (m < cnt) {
+                const int p = gb + m0 + m;
+                t = g < a.E ? a.sorted_assign[p] / k : p - T * k;
+            }
+            tok[m] = t;
+        }
+        __syncthreads();
     }
-    const float st = a.shared != nullptr ? a.sbuf[t] : 0.0f;
+
+    // ---- activation loader: thread -> 16-byte chunk (tid & 15) of rows (tid >> 4) + (NT / 16) q
+    const int ach = tid & 15, arow0 = tid >> 4;
+    const rsrc_t ares = GATEUP ? make_rsrc(a.x16, (uint32_t)T * H * 2)
+                               : make_rsrc(a.hbuf, (uint32_t)((size_t)(T * k + T) * I * 2));
+    int aoff[AQ];
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+        const int m = arow0 + (NT / 16) * q;
+        const int mm = m < cnt ? m : 0;  // rows past the group read a valid row; their outputs are dropped
+        aoff[q] = GATEUP ? 2 * tok[mm] * H : 2 * (gb + m0 + mm) * I;
+    }
+    u32x4_t ra[AQ];
+    auto load_a = [&](int step) {
+        const int kk = step * BK + 8 * ach;
+        const bool ok = step < nsteps && kk < K;
+#pragma unroll
+        for (int q = 0; q < AQ; ++q) ra[q] = buf_load16(ares, ok ? aoff[q] + 2 * kk : kOob);
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < AQ; ++q)
+            *reinterpret_cast<u32x4_t*>(&sA[buf][(arow0 + (NT / 16) * q) * APITCH + 8 * ach]) = ra[q];
+    };
+
+    // ---- weight records of this wave
+    const rsrc_t sres = make_rsrc(slot, (uint32_t)a.slot_bytes);
+    const int soff = lane_scale_off(lane);
+    const int codes = (int)(GATEUP ? a.gu_codes : a.dn_codes), scales = (int)(GATEUP ? a.gu_scales : a.dn_scales);
+    const int hc0 = 128 * nt + 8 * NB * wn;         // gate_up: first h-column of the wave (NB / 2 tiles)
+    const int grp0 = 4 * nt + (NB / 4) * wn;        // down: first record group of the wave (NB / 4 groups)
+    struct BRegs {
+        u32x4_t c[NB];
+        uint32_t s[NB];
+    };
+    // gate_up: record b < NB/2 is gate tile hc0/16 + b, b >= NB/2 the matching up tile (one 128-column step each).
+    // down: record 4 gi + m is group grp0 + gi at 32-column chunk 4 step + m.
+    auto load_b = [&](int step, BRegs& r) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            int rec;
+            bool ok = step < nsteps;
+            if (GATEUP) {
+                const int hcb = hc0 + 16 * (b % (NB / 2));
+                ok = ok && hcb < I;
+                rec = step * (2 * I / 16) + (b / (NB / 2)) * (I / 16) + hcb / 16;
+            } else {
+                const int gi = b >> 2, kc = 4 * step + (b & 3);
+                ok = ok && kc < I / 32 && 64 * (grp0 + gi) < H;
+                rec = kc * (H / 64) + grp0 + gi;
+            }
+            r.c[b] = buf_load16(sres, ok ? codes + rec * kRecBytes + 16 * lane : kOob);
+            r.s[b] = buf_load4(sres, ok ? scales + rec * kRecScaleBytes + soff : kOob);
+        }
+    };
+
+    f32x4_t acc[4][NB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[i][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](int buf, const BRegs& r) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f16x8_t fa[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                fa[i] = lds_frag(&sA[buf][(64 * wm + 16 * i + l16) * APITCH + 32 * m + 8 * q4]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                // gate_up: record b holds chunk m in dword m; down: record 4 gi + m holds tile j in dword j
+                const int ri = GATEUP ? b : 4 * (b >> 2) + m;
+                const int d = GATEUP ? m : (b & 3);
+                const uint32_t cw = word_of(r.c[ri], d);
+                f16x2_t S;
+                if (d == 0) S = scale_f16x2<0>(r.s[ri]);
+                else if (d == 1) S = scale_f16x2<1>(r.s[ri]);
+                else if (d == 2) S = scale_f16x2<2>(r.s[ri]);
+                else S = scale_f16x2<3>(r.s[ri]);
+                const f16x8_t fb = frag_f16(cw, S);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[i][b], 0, 0, 0);
+            }
+        }
+    };
+
+    // the issue order of the loads is part of the design (see above): pin it
+#define MOE_PIN() __builtin_amdgcn_sched_barrier(0)
+    BRegs rb0, rb1;
+    load_a(0);
+    MOE_PIN();
+    load_b(0, rb0);
+    MOE_PIN();
+    store_a(0);
+    MOE_PIN();
+    load_a(1);
+    MOE_PIN();
+    load_b(1, rb1);
+    MOE_PIN();
     __syncthreads();
-    const int n = chunk * 256 + tid;
-    if (n >= H) return;
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        const int p = pos_s[j];
-        if (p >= 0) acc += w_s[j] * a.obuf[(size_t)p * H + n];
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {  // one exit: keeps the loop-carried loads' wait counts exact
+        compute(0, rb0);
+        MOE_PIN();
+        store_a(1);           // activations of step s + 1
+        MOE_PIN();
+        load_a(s + 2);
+        MOE_PIN();
+        load_b(s + 2, rb0);
+        MOE_PIN();
+        __syncthreads();
+        compute(1, rb1);
+        MOE_PIN();
+        store_a(0);           // activations of step s + 2
+        MOE_PIN();
+        load_a(s + 3);
+        MOE_PIN();
+        load_b(s + 3, rb1);
+        MOE_PIN();
+        __syncthreads();
     }
-    if (a.shared != nullptr) acc += st * a.obuf[(size_t)(T * k + t) * H + n];
-    float* yp = a.y + (size_t)t * H + n;
-    *yp = a.accumulate ? *yp + acc : acc;
+    if (s < nsteps) compute(0, rb0);  // odd number of steps: the last one sits in buffer 0
+#undef MOE_PIN
+
+    // ---- epilogue: lane holds token rows 4 q4 + [0, 4) of column l16 of each 16x16 block
+    if (GATEUP) {
+        const float* gl = reinterpret_cast<const float*>(slot + a.gu_glob);
+#pragma unroll
+        for (int cb = 0; cb < NB / 2; ++cb) {
+            const int hc = hc0 + 16 * cb + l16;
+            if (hc >= I) continue;
+            const float gg = gl[hc], gu = gl[I + hc];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 64 * wm + 16 * i + 4 * q4 + r;
+                    if (m >= cnt) continue;
+                    const float inv = a.xinv[tok[m]];
+                    const float gate = acc[i][cb][r] * inv * gg;
+                    const float up = acc[i][NB / 2 + cb][r] * inv * gu;
+                    float h = gate * sigmoidf_(gate) * up;
+                    h = fminf(fmaxf(h, -65504.0f), 65504.0f);
+                    a.hbuf[(size_t)(gb + m0 + m) * I + hc] = (_Float16)h;
+                }
+        }
+    } else {
+        const float* gl = reinterpret_cast<const float*>(slot + a.dn_glob);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int oc = 64 * (grp0 + (b >> 2)) + 16 * (b & 3) + l16;
+            if (oc >= H) continue;
+            const float gd = gl[oc];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 64 * wm + 16 * i + 4 * q4 + r;
+                    if (m < cnt) a.obuf[(size_t)(gb + m0 + m) * H + oc] = acc[i][b][r] * gd;
+                }
+        }
+    }
+}
+
+constexpr int kBigNB = 4;
+
+// ------------------------------------------------------------------ combine
+// One thread per 4 output columns of token t; the k expert rows are read in
+// groups of 8 with every load of a group in flight before the first add
+// (rows past k read as zero), and added in assignment order.
+__global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a, int nchunk) {
+    const int t = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+    const int H = a.H, T = a.T, k = a.k, H4 = H / 4;
+    const int c4 = chunk * 256 + (int)threadIdx.x;
+    if (c4 >= H4) return;
+    const rsrc_t ores = make_rsrc(a.obuf, (uint32_t)((size_t)(T * k + T) * H * 4));
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        f32x4_t v[8];
+        float wj[8];
+        bool ok[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = j0 + i, aidx = t * k + j;
+            const bool valid = j < k;
+            const int p = valid ? a.assign_pos[aidx] : 0;
+            v[i] = __builtin_bit_cast(f32x4_t, buf_load16(ores, valid ? 16 * (p * H4 + c4) : kOob));
+            wj[i] = valid ? a.w[aidx] : 0.0f;
+            ok[i] = valid && a.slot_of_expert[a.ids[aidx]] >= 0;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (ok[i]) acc += wj[i] * v[i];
+    }
+    if (a.shared != nullptr) {
+        const f32x4_t vs = __builtin_bit_cast(f32x4_t, buf_load16(ores, 16 * ((T * k + t) * H4 + c4)));
+        acc += a.sbuf[t] * vs;
+    }
+    f32x4_t* yp = reinterpret_cast<f32x4_t*>(a.y + (size_t)t * H) + c4;
+    if (a.accumulate) acc += *yp;
+    *yp = acc;
 }
 
 template <int BM, bool GATEUP>
@@ -472,13 +696,17 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int ntn_gu = ceil_div(I, 64);
-    if ((e = launch_gemm<128, true>(a, 0, max128, ntn_gu, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL((big_gemm_kernel<true, kBigNB>), dim3(max128 * ceil_div(I, 128)), dim3(32 * kWave / kBigNB), 0,
+                       s, a, ceil_div(I, 128));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_gemm<64, true>(a, 1, maxsmall, ntn_gu, s)) != hipSuccess) return e;
     if ((e = launch_gemm<32, true>(a, 2, maxsmall, ntn_gu, s)) != hipSuccess) return e;
-    if ((e = launch_gemm<128, false>(a, 0, max128, ceil_div(H, 128), s)) != hipSuccess) return e;
+    hipLaunchKernelGGL((big_gemm_kernel<false, kBigNB>), dim3(max128 * ceil_div(H, 256)), dim3(32 * kWave / kBigNB), 0,
+                       s, a, ceil_div(H, 256));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_gemm<64, false>(a, 1, maxsmall, ceil_div(H, 128), s)) != hipSuccess) return e;
     if ((e = launch_gemm<32, false>(a, 2, maxsmall, ceil_div(H, 256), s)) != hipSuccess) return e;
-    const int nchunk = ceil_div(H, 256);
+    const int nchunk = ceil_div(H / 4, 256);
     hipLaunchKernelGGL(combine_kernel, dim3(T * nchunk), dim3(256), 0, s, a, nchunk);
     return hipGetLastError();
 }
