@@ -27,6 +27,7 @@ import numpy as np
 METRIC = "MoE-layer tokens/s + expert-weight HBM GB/s (% peak), H2560 I640 NVFP4"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+PCIE_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction
 
 
 def log(msg: str) -> None:
@@ -190,6 +191,176 @@ def parity_sample(inp, res, tokens):
     return {"ids_bitexact": True, "rel_l2": rel, "tokens_checked": int(toks.size)}
 
 
+# ---------------------------------------------------------------- offload
+
+def bench_offload(steps: int, warmup: int, distinct: int):
+    """48 MoE layers whose 256 experts live in pinned host memory behind one HBM cache of 37% of the
+    12,288 expert-layer slots (global LRU, cold start).  Per layer-step: route on the GPU, one D2H copy of
+    the ids, host LRU plan, misses copied on a side stream while the hits-only forward runs, then the
+    misses-only forward accumulates.  Returns the JSON dict."""
+    import torch
+    import oracle
+    from expert_offload_serving_amd import _lib, synth
+    from expert_offload_serving_amd import layer as dl
+
+    H, I, E, k, T, L = 2560, 640, 256, 8, 8, 48
+    seed = 48
+    r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
+    sb = synth.slot_nbytes(H, I)
+    n_slots = int(0.37 * L * E)
+    t0 = time.time()
+    base_np = synth.make_bank(r_w, H, I, E, distinct)          # 256 base experts (distinct of them quantized)
+    log(f"offload: quantized {min(distinct, E)} distinct experts into {E} base slots in {time.time() - t0:.1f}s")
+    # expert (l, e) is base expert (e + 37 l) mod 256: every (layer, expert) reads its own base slot address
+    # range; the 48 x 256 banks are these 256 pinned slots, each serving 48 (layer, expert) pairs.
+    host = torch.from_numpy(base_np).pin_memory()
+    host_ptr = [host[j].data_ptr() for j in range(E)]
+    def base_of(l, e):
+        return (e + 37 * l) % E
+    dev = torch.device("cuda:0")
+    cache = torch.empty((n_slots, sb), dtype=torch.uint8, device=dev)
+    shared_np = np.stack([base_np[(200 + l) % E] for l in range(L)])
+    shared = torch.from_numpy(shared_np).to(dev)
+    wg_np = synth.f32_to_bf16_bits(r_g.standard_normal((L, H), dtype=np.float32) * np.float32(0.02))
+    wg = dl.to_device_bf16(wg_np, dev).view(L, H)
+    total = steps + warmup
+    ranks = [r_l.permutation(E) + 1 for _ in range(L)]
+    logits_np = np.empty((total, L, T, E), dtype=np.float32)
+    for l in range(L):
+        for s_ in range(total):
+            logits_np[s_, l] = synth.zipf_gumbel_logits(r_l, T, E, 1.2, ranks[l])
+    logits = torch.from_numpy(logits_np).to(dev)
+    NX = 16
+    xs_np = synth.f32_to_bf16_bits(r_x.standard_normal((NX, T, H), dtype=np.float32))
+    xs = dl.to_device_bf16(xs_np.reshape(NX * T, H), dev).view(NX, T, H)
+
+    mgr = _lib.ExpertCache(L, E, n_slots)
+    route = dl.Routing.empty(T, E, k, dev)
+    rws = _lib.moe_route_workspace_bytes(T, E, k)
+    rws_t = torch.empty(max(1, rws), dtype=torch.uint8, device=dev)
+    ws = torch.empty(_lib.moe_nvfp4_forward_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ids_h = torch.empty((T, k), dtype=torch.int32).pin_memory()
+    maps_h = torch.empty((2, E), dtype=torch.int32).pin_memory()
+    maps_d = torch.empty((2, E), dtype=torch.int32, device=dev)
+    comp = torch.cuda.current_stream()
+    copy = torch.cuda.Stream(device=dev)
+    done = torch.cuda.Event()
+    ids_log = np.empty((total, L, T * k), dtype=np.int32)
+    stats = {"hits": np.zeros((total, L), np.int64), "misses": np.zeros((total, L), np.int64)}
+
+    def layer_struct(l, slot_map, with_shared):
+        st = _lib.LayerStruct()
+        st.H, st.I, st.E, st.k = H, I, E, k
+        st.bank_base = cache.data_ptr()
+        st.slot_bytes = sb
+        st.num_slots = n_slots
+        st.slot_of_expert = slot_map.data_ptr()
+        st.shared_slot = shared[l].data_ptr() if with_shared else None
+        st.shared_gate_w = wg[l].data_ptr() if with_shared else None
+        return st
+
+    def layer_step(s_, l):
+        x = xs[(s_ * L + l) % NX]
+        _lib.check(_lib.moe_route_topk(logits[s_, l], T, E, k, route.ids, route.w, route.offsets,
+                                       route.sorted_assign, route.assign_pos, rws_t, rws, None))
+        ids_h.copy_(route.ids, non_blocking=True)
+        comp.synchronize()                      # the one D2H sync per layer-step: the host plans the misses
+        ids = ids_h.numpy().reshape(-1).copy()
+        ids_log[s_, l] = ids
+        som, miss_e, miss_s, n_hit = mgr.plan(l, ids)
+        stats["hits"][s_, l], stats["misses"][s_, l] = n_hit, len(miss_e)
+        # The previous layer-step's kernels finished before the sync above (they precede this route in
+        # stream order), so no slot being overwritten below is still being read.
+        som = np.asarray(som, dtype=np.int32)
+        hit_map = som.copy()
+        miss_map = np.full(E, -1, dtype=np.int32)
+        for e_, sl in zip(miss_e, miss_s):
+            hit_map[e_] = -1
+            miss_map[e_] = sl
+        maps_h.numpy()[0] = hit_map
+        maps_h.numpy()[1] = miss_map
+        maps_d.copy_(maps_h, non_blocking=True)
+        if miss_e:
+            _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, list(miss_s),
+                                              [host_ptr[base_of(l, e_)] for e_ in miss_e], copy, done))
+        _lib.check(_lib.moe_nvfp4_forward(layer_struct(l, maps_d[0], True), x, T, route.ids, route.w,
+                                          route.offsets, route.sorted_assign, route.assign_pos, y, 0, ws,
+                                          ws.numel(), None))
+        if miss_e:
+            comp.wait_event(done)
+            _lib.check(_lib.moe_nvfp4_forward(layer_struct(l, maps_d[1], False), x, T, route.ids, route.w,
+                                              route.offsets, route.sorted_assign, route.assign_pos, y, 1, ws,
+                                              ws.numel(), None))
+
+    log(f"offload: {L} layers x {E} experts, cache {n_slots} slots ({n_slots * sb / 1e9:.1f} GB), "
+        f"{warmup} warm-up + {steps} timed steps at bs {T}")
+    t_cold = time.perf_counter()
+    for s_ in range(warmup):
+        for l in range(L):
+            layer_step(s_, l)
+    torch.cuda.synchronize()
+    t_cold = time.perf_counter() - t_cold
+    log(f"offload: warm-up done in {t_cold:.1f}s, hit rate {stats['hits'][:warmup].sum() / max(1, stats['hits'][:warmup].sum() + stats['misses'][:warmup].sum()):.3f}")
+    t0 = time.perf_counter()
+    for s_ in range(warmup, total):
+        for l in range(L):
+            layer_step(s_, l)
+        if (s_ - warmup) % 16 == 15:
+            log(f"offload: step {s_ - warmup + 1}/{steps}")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # pinned host -> HBM copy rate alone (64 slots, one stream)
+    n_probe = 64
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(copy)
+    _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, list(range(n_probe)),
+                                      [host_ptr[j % E] for j in range(n_probe)], copy, None))
+    ev1.record(copy)
+    torch.cuda.synchronize()
+    h2d_gbs = n_probe * sb / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+
+    # checks: the host LRU against the oracle's model on the same ids; the last layer-step against the oracle
+    h_ref, m_ref, _, _ = oracle.lru_run(ids_log, E, n_slots, want_maps=False)
+    lru_ok = bool(np.array_equal(h_ref, stats["hits"]) and np.array_equal(m_ref, stats["misses"]))
+    s_last, l_last = total - 1, L - 1
+    ids_o, w_o = oracle.route(logits_np[s_last, l_last], k)
+    bank_o = np.concatenate([base_np, shared_np[l_last][None]], axis=0)
+    som_o = np.array([base_of(l_last, e_) for e_ in range(E)], dtype=np.int32)
+    toks = np.arange(2, dtype=np.int32)
+    ref = oracle.forward(H, I, E, k, bank_o, som_o, E, wg_np[l_last], xs_np[(s_last * L + l_last) % NX], ids_o,
+                         w_o, tokens=toks)
+    got = y.cpu().numpy()[toks].astype(np.float64)
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+    hits, misses = stats["hits"][warmup:].sum(), stats["misses"][warmup:].sum()
+    miss_bytes = misses * sb
+    layer_tok_s = T * steps * L / wall
+    pcie = miss_bytes / wall / 1e9
+    return {
+        "metric": "MoE-layer tokens/s with the expert cache (offload), H2560 I640 NVFP4",
+        "value": round(layer_tok_s, 2), "unit": "layer-tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(wall * 1e3 / steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "offload_48x256_cache37", "H": H, "I": I, "E": E, "k": k, "T": T, "layers": L,
+                   "cache_slots": n_slots, "residency": round(n_slots / (L * E), 4), "routing": "Zipf(1.2) per layer",
+                   "host_banks": f"{E} pinned base slots ({E * sb / 1e9:.2f} GB); expert (l, e) = base (e + 37 l) mod {E}",
+                   "distinct_quantized_experts": min(distinct, E), "parallelism": "single GPU"},
+        "roofline": {"bound": "pcie", "achieved": round(pcie, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(pcie / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "expert_cache_fill (hipMemcpyAsync of missed slots on a side stream)",
+                     "per_launch": f"{misses / max(1, steps * L):.2f} missed slots x {sb} B per layer-step"},
+        "offload": {"hit_rate_steady": round(hits / max(1, hits + misses), 4),
+                    "hit_rate_warmup": round(stats["hits"][:warmup].sum() /
+                                             max(1, stats["hits"][:warmup].sum() + stats["misses"][:warmup].sum()), 4),
+                    "model_tokens_per_s": round(T * steps / wall, 2), "ms_per_layer_step": round(wall * 1e3 / (steps * L), 4),
+                    "miss_GB_per_step": round(miss_bytes / steps / 1e9, 3), "h2d_copy_GBps_alone": round(h2d_gbs, 2),
+                    "warmup_s": round(t_cold, 2), "lru_matches_oracle_model": lru_ok},
+        "parity": {"rel_l2_last_layer_step": rel, "tokens_checked": int(toks.size)},
+    }
+
+
 # ---------------------------------------------------------------- main
 
 def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: int, want_cpu: bool, cpu_tokens: int):
@@ -212,12 +383,14 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
         tf = flops / fwd_s / 1e12
         roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "moe_nvfp4_forward prefill (gateup_mfma + down_mfma + combine)",
+                "kernel": "moe_nvfp4_forward prefill (prep, plan, big_gemm_kernel + gemm_kernel for gate_up and "
+                          "down, combine_kernel), timed together with HIP events",
                 "per_launch": f"{flops / 1e9:.2f} GFLOP per forward (2*3*I*H*(T*k+T))"}
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "moe_nvfp4_forward decode (decode_gateup_kernel + decode_down_kernel)",
+                "kernel": "moe_nvfp4_forward decode (fused_kernel + dcombine_kernel), timed together with HIP "
+                          "events",
                 "per_launch": f"{bytes_fwd / 1e6:.2f} MB expert weights per forward ((D+1) x {sb} B, "
                               f"mean D = {mean_d:.2f})"}
     out = {
@@ -252,7 +425,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_bs1",
-                    choices=["decode_bs1", "decode_bs16", "prefill_2048", "all"])
+                    choices=["decode_bs1", "decode_bs16", "prefill_2048", "offload", "all"])
     ap.add_argument("--replicas", type=int, default=8, help="copies of the expert bank rotated over steps")
     ap.add_argument("--distinct", type=int, default=32, help="distinct quantized experts tiled over the slots")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -271,6 +444,10 @@ def main():
     _lib.lib()
     names = ["decode_bs1", "decode_bs16", "prefill_2048"] if args.config == "all" else [args.config]
     for name in names:
+        if name == "offload":
+            steps, warmup = (64, 16) if args.steps == 200 and args.warmup == 10 else (args.steps, args.warmup)
+            print(json.dumps(bench_offload(steps, warmup, args.distinct)), flush=True)
+            continue
         steps, warmup = args.steps, args.warmup
         if name == "prefill_2048":
             steps, warmup = max(1, min(steps, 20)), max(1, min(warmup, 3))

@@ -143,7 +143,20 @@ def expert_cache_fill(cache_base, slot_bytes, num_slots, dst_slots, srcs, copy_s
     n = len(dst_slots)
     d = (ctypes.c_int32 * max(1, n))(*[int(v) for v in dst_slots])
     s = (ctypes.c_void_p * max(1, n))(*[int(v) for v in srcs])
-    ev = None if done_event is None else done_event.cuda_event
+    ev = None
+    if done_event is not None:
+        if isinstance(done_event, int):
+            ev = done_event
+        else:
+            # torch creates the HIP event of a torch.cuda.Event on its first record; until then its handle is 0
+            # and a stream's wait_event on it is a no-op.  Recording it once here creates it, and the library's
+            # record after the copies is then the one that waits see.
+            if not done_event.cuda_event:
+                done_event.record(copy_stream if copy_stream is not None and not isinstance(copy_stream, int)
+                                  else None)
+            ev = done_event.cuda_event
+            if not ev:
+                raise MoeError(MOE_ERR_INVALID_ARGUMENT, "done_event has no HIP event")
     return lib().expert_cache_fill(_ptr(cache_base), slot_bytes, num_slots, d, s, n, _stream(copy_stream), ev)
 
 

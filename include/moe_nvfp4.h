@@ -127,10 +127,13 @@ size_t moe_nvfp4_forward_workspace_bytes(int T, int H, int I, int E, int k);
  *   x        bf16 [T, H] activations
  *   routing  the outputs of moe_route_topk for the same T, E, k
  *   y        f32 [T, H]; accumulate = 0 writes y, 1 adds into y
- * T <= 16 runs the decode path (NVFP4 GEMV with wavefront reductions, fp32
- * hidden state); larger T runs the prefill path (grouped bf16 MFMA GEMM over
- * the permuted tokens with the weights dequantised in LDS, bf16 hidden
- * state).  Expert slots referenced by slot_of_expert must lie inside the
+ * T <= 16 (with H <= 2560) runs the decode path: one persistent kernel over
+ * (expert, I-slice) work items whose NVFP4 operands are decoded in registers
+ * into fp16 matrix-core fragments against per-token fp16-scaled activations
+ * (fp32 accumulation and hidden state), then a combine kernel that sums the
+ * slices and applies the down-row globals in a fixed order.  Larger T runs
+ * the prefill path: grouped bf16 MFMA GEMMs over the permuted tokens with
+ * the weights decoded in registers, bf16 hidden state.  Expert slots referenced by slot_of_expert must lie inside the
  * bank; the kernels do not range-check them.  Output order of summation is
  * fixed, so repeated calls give bit-identical results. */
 int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,

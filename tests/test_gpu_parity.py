@@ -338,6 +338,7 @@ def test_offload_layer_steps_match_resident():
             done = torch.cuda.Event()
             _lib.check(_lib.expert_cache_fill(cache, sb, C, miss_s, [host[l, e].data_ptr() for e in miss_e], side,
                                               done))
+            assert done.cuda_event != 0          # the wait below must see a real event
             dev = dl.DeviceLayer(H, I, E, k, cache, torch.from_numpy(som).cuda(), -1, dl.to_device_bf16(wg))
             xd = dl.to_device_bf16(x)
             # hits first (the copies may still be in flight), then wait and add the misses
