@@ -30,6 +30,34 @@ BF16_PEAK_TFLOPS = 2500.0
 PCIE_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction
 
 
+# HBM bytes per forward call from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, summed over the call's
+# kernels and scaled by what the same counters read for a plain copy of known size), with a digest of the kernel
+# sources they were taken on.  Reported as roofline.traffic only while those sources are unchanged.
+COUNTED_TRAFFIC = {
+    "decode_bs1": (29_278_069, "3ad5bb5983649fd6"),
+    "decode_bs16": (348_102_580, "3ad5bb5983649fd6"),
+    "prefill_2048": (1_890_454_916, "7ae170f188708718"),
+}
+KERNEL_SOURCES = {"decode": ["decode.hip", "nvfp4_device.hpp"], "prefill": ["prefill.hip", "nvfp4_device.hpp"]}
+
+
+def kernel_digest(kind: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "expert_offload_serving_amd", "csrc")
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(base, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(name: str, kind: str):
+    ent = COUNTED_TRAFFIC.get(name)
+    if ent is None or kernel_digest(kind) != ent[1]:
+        return None
+    return ent[0]
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -382,13 +410,13 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     if prefill:
         tf = flops / fwd_s / 1e12
         roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": counted_traffic(name, "prefill"),
                 "kernel": "moe_nvfp4_forward prefill (prep, plan, big_gemm_kernel + gemm_kernel for gate_up and "
                           "down, combine_kernel), timed together with HIP events",
                 "per_launch": f"{flops / 1e9:.2f} GFLOP per forward (2*3*I*H*(T*k+T))"}
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic(name, "decode"),
                 "kernel": "moe_nvfp4_forward decode (fused_kernel + dcombine_kernel), timed together with HIP "
                           "events",
                 "per_launch": f"{bytes_fwd / 1e6:.2f} MB expert weights per forward ((D+1) x {sb} B, "
@@ -419,6 +447,21 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     return out
 
 
+def copy_calibration(nbytes: int, reps: int) -> None:
+    """A plain device copy of known size (torch's elementwise negation of an fp32 buffer: reads and writes
+    nbytes each), launched reps times; its FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters."""
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"kernel": "torch.neg fp32 (vectorized_elementwise_kernel)",
+                                           "read_bytes": n * 4, "write_bytes": n * 4, "dispatches": reps}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -429,7 +472,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=8, help="copies of the expert bank rotated over steps")
     ap.add_argument("--distinct", type=int, default=32, help="distinct quantized experts tiled over the slots")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--cpu-tokens", type=int, default=320)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (for calibrating HBM byte counters) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -440,6 +485,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 4)
+        return
     from expert_offload_serving_amd import _lib
     _lib.lib()
     names = ["decode_bs1", "decode_bs16", "prefill_2048"] if args.config == "all" else [args.config]
