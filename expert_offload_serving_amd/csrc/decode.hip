@@ -276,29 +276,29 @@ __device__ __forceinline__ void run_item(const DecArgs& a, DecShared& sh, const 
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Persistent over work items u = blockIdx.x + j * gridDim.x; item u is
-// (expert act[u / nsl], or the shared expert, slice u % nsl).  Every token's
-// activations are staged in LDS once, as fp16 times a per-token power of two.
-// Phase A loads run two items ahead and phase B loads one item ahead, so the
-// next items stream while this one reduces, runs SwiGLU and finishes.
-// KQW: most 128-column steps of K = H per wave (steps wave % 4 + 4 i);
-// NRGW: most 64-row down groups per wave (groups wave + 8 i).
-template <int KQW, int NRGW>
-__global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
-    extern __shared__ __attribute__((aligned(16))) _Float16 x16[];  // (T + 1) rows of XP halves; row T is zero
-    __shared__ DecShared sh;
+// Prologue shared by the decode kernels (NW waves per workgroup), in two
+// parts so that a kernel can start its first weight loads in between.
+// stage_tables issues the routing-table and activation loads in one batch
+// (tables first, so waiting for them waits for nothing else), puts the
+// tables in LDS and lists the experts that have assignments (ascending); it
+// ends with a workgroup barrier and returns their number (wave-uniform).
+// stage_x then writes every token's activations to LDS as fp16 times a
+// per-token power of two (xsh); the caller synchronises before reading them.
+template <int NW>
+struct XRegs {
+    static constexpr int XT = (kDecodeMaxT + NW - 1) / NW;  // token rows staged per wave
+    static constexpr int XC = 2560 / 8 / kWave;             // 16-byte chunks of a token row per lane (H <= 2560)
+    u32x4_t v[XT][XC];
+};
 
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int H = a.H, T = a.T, k = a.k, E = a.E;
-    const int XP = H + 8;  // padded row: rows of different tokens start 16 bytes apart modulo the LDS banks
-    Tables& tb = sh.tb;
-
-    // ---- stage the routing tables (issued first, so waiting for them waits for nothing else)
-    const int n = T * k;
-    constexpr int R = (kMaxE + 1 + kDT - 1) / kDT;
-    constexpr int XC = 2560 / 8 / kWave;  // 16-byte chunks of a token row per lane (H <= 2560)
-    uint32_t vo[R], vs[R], va[2], vw[2];
-    u32x4_t xv[2][XC];
+template <int NW>
+__device__ __forceinline__ int stage_tables(const DecArgs& a, Tables& tb, XRegs<NW>& xr, int tid, int lane,
+                                            int wave) {
+    constexpr int NT = NW * kWave;
+    const int H = a.H, T = a.T, k = a.k, E = a.E, n = T * k;
+    constexpr int R = (kMaxE + 1 + NT - 1) / NT;
+    constexpr int RA = (kDecodeMaxAssign + NT - 1) / NT;
+    uint32_t vo[R], vs[R], va[RA], vw[RA];
     {
         const rsrc_t ro = make_rsrc(a.offsets, (uint32_t)(E + 1) * 4);
         const rsrc_t rs = make_rsrc(a.slot_of_expert, (uint32_t)E * 4);
@@ -307,36 +307,36 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
         const rsrc_t rx = make_rsrc(a.x, (uint32_t)T * H * 2);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int i = tid + kDT * r;
+            const int i = tid + NT * r;
             vo[r] = buf_load4(ro, i <= E ? 4 * i : kOob);
             vs[r] = buf_load4(rs, i < E ? 4 * i : kOob);
         }
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int i = tid + kDT * r;
+        for (int r = 0; r < RA; ++r) {
+            const int i = tid + NT * r;
             va[r] = buf_load4(ra, i < n ? 4 * i : kOob);
             vw[r] = buf_load4(rw, i < n ? 4 * i : kOob);
         }
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {  // activations: wave w stages tokens w and w + 8
-            const int t = wave + kDW * p;
+        for (int p = 0; p < XRegs<NW>::XT; ++p) {  // wave w stages tokens w, w + NW, ...
+            const int t = wave + NW * p;
 #pragma unroll
-            for (int i = 0; i < XC; ++i) {
+            for (int i = 0; i < XRegs<NW>::XC; ++i) {
                 const int ch = lane + kWave * i;
-                xv[p][i] = buf_load16(rx, t < T && ch < H / 8 ? 2 * (t * H + 8 * ch) : kOob);
+                xr.v[p][i] = buf_load16(rx, t < T && ch < H / 8 ? 2 * (t * H + 8 * ch) : kOob);
             }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int i = tid + kDT * r;
+        const int i = tid + NT * r;
         if (i <= E) tb.off[i] = (int)vo[r];
         if (i < E) tb.slot[i] = (int)vs[r];
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int i = tid + kDT * r;
+    for (int r = 0; r < RA; ++r) {
+        const int i = tid + NT * r;
         if (i < n) tb.sorted[i] = (int)va[r], tb.w[i] = __uint_as_float(vw[r]);
     }
     __syncthreads();
@@ -353,36 +353,37 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
         if (lane == 0) tb.n_act = base;
     }
     __syncthreads();
-    const int n_act = __builtin_amdgcn_readfirstlane(tb.n_act);
-    const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
-    int u = blockIdx.x;
-    if (u >= n_items) return;  // uniform
+    return __builtin_amdgcn_readfirstlane(tb.n_act);
+}
 
-    // ---- activations: fp16 times a per-token power of two, into LDS
+template <int NW>
+__device__ __forceinline__ void stage_x(const DecArgs& a, const XRegs<NW>& xr, int* xsh, _Float16* x16, int XP,
+                                        int tid, int lane, int wave) {
+    const int H = a.H, T = a.T;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int t = wave + kDW * p;
+    for (int p = 0; p < XRegs<NW>::XT; ++p) {
+        const int t = wave + NW * p;
         float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < XC; ++i)
+        for (int i = 0; i < XRegs<NW>::XC; ++i)
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const uint32_t wv = word_of(xv[p][i], d);
+                const uint32_t wv = word_of(xr.v[p][i], d);
                 amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(wv << 16)), fabsf(__uint_as_float(wv & 0xFFFF0000u))));
             }
         amax = wave_max(amax);
         const int sh_t = fp16_shift(amax);
         const float sc = ldexpf(1.0f, sh_t);
         if (t < T) {
-            if (lane == 0) sh.xsh[t] = sh_t;
+            if (lane == 0) xsh[t] = sh_t;
 #pragma unroll
-            for (int i = 0; i < XC; ++i) {
+            for (int i = 0; i < XRegs<NW>::XC; ++i) {
                 const int ch = lane + kWave * i;
                 if (ch >= H / 8) continue;
                 uint32_t hw[4];
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    const uint32_t wv = word_of(xv[p][i], d);
+                    const uint32_t wv = word_of(xr.v[p][i], d);
                     const f16x2_t q = {(_Float16)(__uint_as_float(wv << 16) * sc),
                                        (_Float16)(__uint_as_float(wv & 0xFFFF0000u) * sc)};
                     hw[d] = __builtin_bit_cast(uint32_t, q);
@@ -391,10 +392,35 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
             }
         }
     }
-    for (int ch = tid; ch < XP / 8; ch += kDT)  // the zero row
+    for (int ch = tid; ch < XP / 8; ch += NW * kWave)  // the zero row
         *reinterpret_cast<u32x4_t*>(x16 + T * XP + 8 * ch) = u32x4_t{0, 0, 0, 0};
-    if (tid == 0) sh.xsh[T] = 0;
-    // ---- the first items' weights start streaming (the activations arrived first)
+    if (tid == 0) xsh[T] = 0;
+}
+
+// Persistent over work items u = blockIdx.x + j * gridDim.x; item u is
+// (expert act[u / nsl], or the shared expert, slice u % nsl).  Every token's
+// activations are staged in LDS once, as fp16 times a per-token power of two.
+// Phase A loads run two items ahead and phase B loads one item ahead, so the
+// next items stream while this one reduces, runs SwiGLU and finishes.
+// KQW: most 128-column steps of K = H per wave (steps wave % 4 + 4 i);
+// NRGW: most 64-row down groups per wave (groups wave + 8 i).
+template <int KQW, int NRGW>
+__global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
+    extern __shared__ __attribute__((aligned(16))) _Float16 x16[];  // (T + 1) rows of XP halves; row T is zero
+    __shared__ DecShared sh;
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int H = a.H, T = a.T, k = a.k;
+    const int XP = H + 8;  // padded row: rows of different tokens start 16 bytes apart modulo the LDS banks
+    Tables& tb = sh.tb;
+
+    XRegs<kDW> xv;
+    const int n_act = stage_tables<kDW>(a, tb, xv, tid, lane, wave);
+    const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
+    int u = blockIdx.x;
+    if (u >= n_items) return;  // uniform
+
+    // ---- the first items' weights start streaming, then the activations go to LDS
     const int G = (int)gridDim.x, c = lane & 15;
     const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
     Item it0 = decode_item(a, tb, n_act, nsl, u, true, c);
@@ -405,7 +431,7 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
     issue_b<NRGW>(a, it0, wave, lane, LB);
     issue_a<KQW>(a, it1, wave, lane, tid, LA1);
     __builtin_amdgcn_sched_barrier(0);
-
+    stage_x<kDW>(a, xv, sh.xsh, x16, XP, tid, lane, wave);
     __syncthreads();
 
     for (;;) {
@@ -419,6 +445,250 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
         it0 = it2;
         it1 = it3;
     }
+}
+
+// ------------------------------------------------------------------ wave-item kernel
+// For batches with many active experts the items outnumber the workgroups
+// several times over, and the per-item barrier of the fused kernel leaves
+// each CU waiting on its slowest wave.  Here each wave runs whole items on
+// its own (same items, same partial outputs, same combine): phase A
+// accumulates the slice's four tiles over all of K in registers, SwiGLU is
+// wave-local, phase B follows, and no barrier is taken after the prologue.
+// A wave streams its item as groups of records through a two-slot register
+// ring (one group in flight while the other is consumed; a third slot
+// measured slower): a gate_up group is two 128-column steps of the four
+// tiles, a down group four 64-row record groups of the slice's 32 columns.
+// The last groups of an item prefetch the first groups of the wave's next
+// item.  Group counts are padded to even numbers with zero records (reads
+// past the slot return zeros, stores past the partials are dropped, padded
+// K steps are skipped).
+constexpr int kWW = 8;             // waves per workgroup
+constexpr int kWT = kWW * kWave;   // threads per workgroup
+#ifndef MOE_WAVE_MIN_ITEMS
+#define MOE_WAVE_MIN_ITEMS 600     // work items from which decode runs the wave-item kernel (about T >= 4)
+#endif
+
+struct WaveShared {
+    int xsh[kDecodeMaxT + 1];
+    Tables tb;
+};
+
+struct Ring8 {
+    u32x4_t cd[8];
+    uint32_t sc[8];
+};
+
+__device__ __forceinline__ f16x2_t scale_of(uint32_t sdw, int m) {
+    return m == 0 ? scale_f16x2<0>(sdw) : (m == 1 ? scale_f16x2<1>(sdw) : (m == 2 ? scale_f16x2<2>(sdw) : scale_f16x2<3>(sdw)));
+}
+
+// gate_up group ga: steps 2 ga and 2 ga + 1 of tiles (gate 2s, 2s + 1, up I/16 + 2s, I/16 + 2s + 1).
+__device__ __forceinline__ void wv_issue_a(const DecArgs& a, const Item& it, int ga, int lane, Ring8& R) {
+    const int KQ = a.H / 128, NT = 2 * a.I / 16, up = a.I / 16, soff = lane_scale_off(lane);
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+        const int q = 2 * ga + qq;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rec = q * NT + (r < 2 ? 0 : up) + 2 * it.s + (r & 1);
+            R.cd[4 * qq + r] = buf_load16(it.sres, q < KQ ? a.gu_codes + rec * kRecBytes + 16 * lane : kOob);
+            R.sc[4 * qq + r] = buf_load4(it.sres, q < KQ ? a.gu_scales + rec * kRecScaleBytes + soff : kOob);
+        }
+    }
+}
+
+// down group gb: record groups p = 4 gb + [0, 4) of column chunk s.
+__device__ __forceinline__ void wv_issue_b(const DecArgs& a, const Item& it, int gb, int lane, Ring8& R) {
+    const int NG = a.H / 64, soff = lane_scale_off(lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int p = 4 * gb + r;
+        const int rec = it.s * NG + p;
+        R.cd[r] = buf_load16(it.sres, p < NG ? a.dn_codes + rec * kRecBytes + 16 * lane : kOob);
+        R.sc[r] = buf_load4(it.sres, p < NG ? a.dn_scales + rec * kRecScaleBytes + soff : kOob);
+    }
+}
+
+// Row globals of this lane's accumulator rows 4g + [0, 4) of the four tiles.
+__device__ __forceinline__ void wv_issue_glob(const DecArgs& a, const Item& it, int lane, f32x4_t (&gl)[4]) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = (r < 2 ? 0 : a.I) + kSl * it.s + 16 * (r & 1) + 4 * g;
+        gl[r] = __builtin_bit_cast(f32x4_t, buf_load16(it.sres, a.gu_glob + 4 * row));
+    }
+}
+
+__device__ __forceinline__ void wv_compute_a(const DecArgs& a, const Ring8& R, int ga, const _Float16* xr,
+                                             f32x4_t (&acc)[4]) {
+    const int KQ = a.H / 128;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+        const int q = 2 * ga + qq;
+        if (q >= KQ) continue;  // uniform: a padded step (its activations would lie past the row)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f16x8_t X = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(xr + 128 * q + 32 * m));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f16x8_t A = frag_f16(word_of(R.cd[4 * qq + r], m), scale_of(R.sc[4 * qq + r], m));
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, X, acc[r], 0, 0, 0);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void wv_compute_b(const DecArgs& a, const Ring8& R, int gb, f16x8_t B, float oscale,
+                                             const rsrc_t& pres, int pbase) {
+    const int NG = a.H / 64;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int p = 4 * gb + r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f16x8_t A = frag_f16(word_of(R.cd[r], j), scale_of(R.sc[r], j));
+            const f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            buf_store16(pres, p < NG ? pbase + 4 * (64 * p + 16 * j) : kOob, D * oscale);
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
+    extern __shared__ __attribute__((aligned(16))) _Float16 x16[];  // (T + 1) rows of XP halves; row T is zero
+    __shared__ WaveShared sh;
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int H = a.H, T = a.T, k = a.k;
+    const int XP = H + 8;
+    XRegs<kWW> xv;
+    const int n_act = stage_tables<kWW>(a, sh.tb, xv, tid, lane, wave);
+    const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
+    const int stride = (int)gridDim.x * kWW;
+    // consecutive items go to different CUs; readfirstlane tells the compiler the item is wave-uniform
+    int v = __builtin_amdgcn_readfirstlane(wave * (int)gridDim.x + (int)blockIdx.x);
+
+    const int c = lane & 15, g = lane >> 4;
+    const int KQ = H / 128, NG = H / 64;
+    const int NGA = 2 * ((KQ + 3) / 4);  // gate_up groups of two steps, an even number
+    const int NGB = 2 * ((NG + 7) / 8);  // down groups of four record groups, an even number
+    const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
+    const rsrc_t rres = make_rsrc(a.rowslot, (uint32_t)(T * k + T) * 4);
+
+    // the first item's weights start streaming (a wave without items loads nothing), then the activations go
+    // to LDS; after the barrier a wave without items leaves
+    Item cur = decode_item(a, sh.tb, n_act, nsl, v, v < n_items, c);
+    Ring8 R0, R1;
+    f32x4_t gl[4];
+    wv_issue_glob(a, cur, lane, gl);
+    wv_issue_a(a, cur, 0, lane, R0);
+    wv_issue_a(a, cur, 1, lane, R1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_x<kWW>(a, xv, sh.xsh, x16, XP, tid, lane, wave);
+    __syncthreads();
+    if (v >= n_items) return;  // uniform per wave; no barrier follows
+    do {
+        const Item nxt = decode_item(a, sh.tb, n_act, nsl, v + stride, v + stride < n_items, c);
+        const int xrow = cur.tok >= 0 ? cur.tok : T;
+        const _Float16* xr = x16 + xrow * XP + 8 * g;
+
+        // ---- phase A: the slice's gate and up tiles over all of K
+        f32x4_t acc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        int ga = 0;
+        for (; ga + 2 < NGA; ga += 2) {
+            wv_compute_a(a, R0, ga, xr, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            wv_issue_a(a, cur, ga + 2, lane, R0);
+            __builtin_amdgcn_sched_barrier(0);
+            wv_compute_a(a, R1, ga + 1, xr, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            wv_issue_a(a, cur, ga + 3, lane, R1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wv_compute_a(a, R0, ga, xr, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        wv_issue_b(a, cur, 0, lane, R0);
+        __builtin_amdgcn_sched_barrier(0);
+        wv_compute_a(a, R1, ga + 1, xr, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        wv_issue_b(a, cur, 1, lane, R1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- SwiGLU on this lane's rows 4g + [0, 4) of the two tile pairs, then the phase B operand:
+        // lane (c, g') takes slice rows 8g' + [0, 8) of token c from lanes (c, 2(g' & 1)) and (c, 2(g' & 1) + 1)
+        f16x8_t B;
+        float oscale;
+        {
+            const float xinv = ldexpf(1.0f, -sh.xsh[xrow]);
+            float h[2][4];
+            float hm = 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float gv = acc[tt][r] * xinv * gl[tt][r];
+                    const float uv = acc[2 + tt][r] * xinv * gl[2 + tt][r];
+                    h[tt][r] = gv / (1.0f + expf(-gv)) * uv;
+                    hm = fmaxf(hm, fabsf(h[tt][r]));
+                }
+            hm = fmaxf(hm, __shfl_xor(hm, 16, kWave));
+            hm = fmaxf(hm, __shfl_xor(hm, 32, kWave));
+            const int hsh = fp16_shift(hm);
+            const float hsc = ldexpf(1.0f, hsh);
+            uint32_t P[2][2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const f16x2_t q = {(_Float16)(h[tt][2 * d] * hsc), (_Float16)(h[tt][2 * d + 1] * hsc)};
+                    P[tt][d] = __builtin_bit_cast(uint32_t, q);
+                }
+            const int src0 = c + 32 * (g & 1), src1 = src0 + 16;
+            const bool hi = g >= 2;
+            uint32_t bw[4];
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const uint32_t a0 = (uint32_t)__shfl((int)P[0][d], src0, kWave);
+                const uint32_t a1 = (uint32_t)__shfl((int)P[1][d], src0, kWave);
+                const uint32_t b0 = (uint32_t)__shfl((int)P[0][d], src1, kWave);
+                const uint32_t b1 = (uint32_t)__shfl((int)P[1][d], src1, kWave);
+                bw[d] = hi ? a1 : a0;
+                bw[2 + d] = hi ? b1 : b0;
+            }
+            B = __builtin_bit_cast(f16x8_t, u32x4_t{bw[0], bw[1], bw[2], bw[3]});
+            oscale = ldexpf(1.0f, -hsh) * cur.wc;
+        }
+        // slice 0 records, per output row of the item, where the expert's down globals live
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)cur.slot_index, rres,
+                                              cur.s == 0 && g == 0 && c < cur.ne ? 4 * cur.prow : kOob, 0, 0);
+
+        // ---- phase B: the slice's 32 down columns for all H outputs
+        const int pbase = c < cur.ne ? 4 * ((cur.prow * nsl + cur.s) * H + 4 * g) : kOob;
+        int gb = 0;
+        for (; gb + 2 < NGB; gb += 2) {
+            wv_compute_b(a, R0, gb, B, oscale, pres, pbase);
+            __builtin_amdgcn_sched_barrier(0);
+            wv_issue_b(a, cur, gb + 2, lane, R0);
+            __builtin_amdgcn_sched_barrier(0);
+            wv_compute_b(a, R1, gb + 1, B, oscale, pres, pbase);
+            __builtin_amdgcn_sched_barrier(0);
+            wv_issue_b(a, cur, gb + 3, lane, R1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- the next item's first groups start streaming
+        wv_compute_b(a, R0, gb, B, oscale, pres, pbase);
+        __builtin_amdgcn_sched_barrier(0);
+        wv_issue_glob(a, nxt, lane, gl);
+        wv_issue_a(a, nxt, 0, lane, R0);
+        __builtin_amdgcn_sched_barrier(0);
+        wv_compute_b(a, R1, gb + 1, B, oscale, pres, pbase);
+        __builtin_amdgcn_sched_barrier(0);
+        wv_issue_a(a, nxt, 1, lane, R1);
+        __builtin_amdgcn_sched_barrier(0);
+        cur = nxt;
+        v += stride;
+    } while (v < n_items);
 }
 
 // y_t = sum_j dg_j * (sum over slices of row j's partials) over the routed
@@ -491,22 +761,40 @@ int g_num_cu = 0;
 
 constexpr size_t kXLdsMax = (size_t)(kDecodeMaxT + 1) * (2560 + 8) * 2;
 
+hipError_t init_device_info() {
+    if (g_num_cu != 0) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&g_num_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    return e;
+}
+
 template <int KQW, int NRGW>
 hipError_t launch_fused(const DecArgs& a, int items_max, int nsl, hipStream_t s) {
     static bool attr_set = false;
-    if (g_num_cu == 0 || !attr_set) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&g_num_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int grid = items_max < g_num_cu ? items_max : g_num_cu;
     const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
     hipLaunchKernelGGL((fused_kernel<KQW, NRGW>), dim3(grid), dim3(kDT), lds, s, a, nsl);
+    return hipGetLastError();
+}
+
+hipError_t launch_wave(const DecArgs& a, int items_max, int nsl, hipStream_t s) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wave_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int grid = items_max < g_num_cu ? items_max : g_num_cu;
+    const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
+    hipLaunchKernelGGL(wave_kernel, dim3(grid), dim3(kWT), lds, s, a, nsl);
     return hipGetLastError();
 }
 
@@ -541,7 +829,9 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
 
     const int nsl = I / kSl;
     const int items_max = ((T * k < E ? T * k : E) + 1) * nsl;
-    hipError_t e = launch_fused<5, 5>(a, items_max, nsl, s);
+    hipError_t e = init_device_info();
+    if (e != hipSuccess) return e;
+    e = items_max >= MOE_WAVE_MIN_ITEMS ? launch_wave(a, items_max, nsl, s) : launch_fused<5, 5>(a, items_max, nsl, s);
     if (e != hipSuccess) return e;
     const int nch = H / 64;
     hipLaunchKernelGGL(dcombine_kernel, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);
