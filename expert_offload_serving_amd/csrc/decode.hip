@@ -482,78 +482,111 @@ __device__ __forceinline__ f16x2_t scale_of(uint32_t sdw, int m) {
     return m == 0 ? scale_f16x2<0>(sdw) : (m == 1 ? scale_f16x2<1>(sdw) : (m == 2 ? scale_f16x2<2>(sdw) : scale_f16x2<3>(sdw)));
 }
 
-// gate_up group ga: steps 2 ga and 2 ga + 1 of tiles (gate 2s, 2s + 1, up I/16 + 2s, I/16 + 2s + 1).
+// SL: intermediate rows per item (32 or 64).  A slice has NTT = SL/16 gate
+// tiles (rows SL*s + [0, SL)) and the NTT matching up tiles; a gate_up group
+// is 8 records: 8/(2 NTT) steps of the 2 NTT tiles.  A down group is 4 row
+// groups p of the slice's SL/32 column chunks.
+template <int SL>
+struct WaveGeom {
+    static constexpr int NTT = SL / 16;           // gate (and up) tiles per slice
+    static constexpr int SPG = 8 / (2 * NTT);     // 128-column steps per gate_up group
+    static constexpr int NB = SL / 32;            // 32-column chunks (phase B operands) per slice
+};
+
+template <int SL>
 __device__ __forceinline__ void wv_issue_a(const DecArgs& a, const Item& it, int ga, int lane, Ring8& R) {
+    using W = WaveGeom<SL>;
     const int KQ = a.H / 128, NT = 2 * a.I / 16, up = a.I / 16, soff = lane_scale_off(lane);
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        const int q = 2 * ga + qq;
+    for (int qq = 0; qq < W::SPG; ++qq) {
+        const int q = W::SPG * ga + qq;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int rec = q * NT + (r < 2 ? 0 : up) + 2 * it.s + (r & 1);
-            R.cd[4 * qq + r] = buf_load16(it.sres, q < KQ ? a.gu_codes + rec * kRecBytes + 16 * lane : kOob);
-            R.sc[4 * qq + r] = buf_load4(it.sres, q < KQ ? a.gu_scales + rec * kRecScaleBytes + soff : kOob);
+        for (int r = 0; r < 2 * W::NTT; ++r) {
+            const int rec = q * NT + (r < W::NTT ? 0 : up) + W::NTT * it.s + r % W::NTT;
+            R.cd[2 * W::NTT * qq + r] = buf_load16(it.sres, q < KQ ? a.gu_codes + rec * kRecBytes + 16 * lane : kOob);
+            R.sc[2 * W::NTT * qq + r] = buf_load4(it.sres, q < KQ ? a.gu_scales + rec * kRecScaleBytes + soff : kOob);
         }
     }
 }
 
-// down group gb: record groups p = 4 gb + [0, 4) of column chunk s.
+// down group gb: records (column chunk NB s + f, row group 4 gb + r) in entry NB r + f.
+template <int SL>
 __device__ __forceinline__ void wv_issue_b(const DecArgs& a, const Item& it, int gb, int lane, Ring8& R) {
+    using W = WaveGeom<SL>;
     const int NG = a.H / 64, soff = lane_scale_off(lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int p = 4 * gb + r;
-        const int rec = it.s * NG + p;
-        R.cd[r] = buf_load16(it.sres, p < NG ? a.dn_codes + rec * kRecBytes + 16 * lane : kOob);
-        R.sc[r] = buf_load4(it.sres, p < NG ? a.dn_scales + rec * kRecScaleBytes + soff : kOob);
+#pragma unroll
+        for (int f = 0; f < W::NB; ++f) {
+            const int rec = (W::NB * it.s + f) * NG + p;
+            R.cd[W::NB * r + f] = buf_load16(it.sres, p < NG ? a.dn_codes + rec * kRecBytes + 16 * lane : kOob);
+            R.sc[W::NB * r + f] = buf_load4(it.sres, p < NG ? a.dn_scales + rec * kRecScaleBytes + soff : kOob);
+        }
     }
 }
 
-// Row globals of this lane's accumulator rows 4g + [0, 4) of the four tiles.
-__device__ __forceinline__ void wv_issue_glob(const DecArgs& a, const Item& it, int lane, f32x4_t (&gl)[4]) {
+// Row globals of this lane's accumulator rows 4g + [0, 4) of the slice's gate and up tiles.
+template <int SL>
+__device__ __forceinline__ void wv_issue_glob(const DecArgs& a, const Item& it, int lane,
+                                              f32x4_t (&gl)[2 * WaveGeom<SL>::NTT]) {
+    using W = WaveGeom<SL>;
     const int g = lane >> 4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = (r < 2 ? 0 : a.I) + kSl * it.s + 16 * (r & 1) + 4 * g;
+    for (int r = 0; r < 2 * W::NTT; ++r) {
+        const int row = (r < W::NTT ? 0 : a.I) + SL * it.s + 16 * (r % W::NTT) + 4 * g;
         gl[r] = __builtin_bit_cast(f32x4_t, buf_load16(it.sres, a.gu_glob + 4 * row));
     }
 }
 
+template <int SL>
 __device__ __forceinline__ void wv_compute_a(const DecArgs& a, const Ring8& R, int ga, const _Float16* xr,
-                                             f32x4_t (&acc)[4]) {
+                                             f32x4_t (&acc)[2 * WaveGeom<SL>::NTT]) {
+    using W = WaveGeom<SL>;
     const int KQ = a.H / 128;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        const int q = 2 * ga + qq;
+    for (int qq = 0; qq < W::SPG; ++qq) {
+        const int q = W::SPG * ga + qq;
         if (q >= KQ) continue;  // uniform: a padded step (its activations would lie past the row)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const f16x8_t X = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(xr + 128 * q + 32 * m));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const f16x8_t A = frag_f16(word_of(R.cd[4 * qq + r], m), scale_of(R.sc[4 * qq + r], m));
+            for (int r = 0; r < 2 * W::NTT; ++r) {
+                const int e = 2 * W::NTT * qq + r;
+                const f16x8_t A = frag_f16(word_of(R.cd[e], m), scale_of(R.sc[e], m));
                 acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, X, acc[r], 0, 0, 0);
             }
         }
     }
 }
 
-__device__ __forceinline__ void wv_compute_b(const DecArgs& a, const Ring8& R, int gb, f16x8_t B, float oscale,
-                                             const rsrc_t& pres, int pbase) {
+template <int SL>
+__device__ __forceinline__ void wv_compute_b(const DecArgs& a, const Ring8& R, int gb,
+                                             const f16x8_t (&B)[WaveGeom<SL>::NB], float oscale, const rsrc_t& pres,
+                                             int pbase) {
+    using W = WaveGeom<SL>;
     const int NG = a.H / 64;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int p = 4 * gb + r;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const f16x8_t A = frag_f16(word_of(R.cd[r], j), scale_of(R.sc[r], j));
-            const f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            f32x4_t D = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int f = 0; f < W::NB; ++f) {
+                const int e = W::NB * r + f;
+                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(frag_f16(word_of(R.cd[e], j), scale_of(R.sc[e], j)), B[f],
+                                                           D, 0, 0, 0);
+            }
             buf_store16(pres, p < NG ? pbase + 4 * (64 * p + 16 * j) : kOob, D * oscale);
         }
     }
 }
 
+template <int SL>
 __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
+    using W = WaveGeom<SL>;
     extern __shared__ __attribute__((aligned(16))) _Float16 x16[];  // (T + 1) rows of XP halves; row T is zero
     __shared__ WaveShared sh;
 
@@ -569,8 +602,8 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
 
     const int c = lane & 15, g = lane >> 4;
     const int KQ = H / 128, NG = H / 64;
-    const int NGA = 2 * ((KQ + 3) / 4);  // gate_up groups of two steps, an even number
-    const int NGB = 2 * ((NG + 7) / 8);  // down groups of four record groups, an even number
+    const int NGA = 2 * ((KQ + 2 * W::SPG - 1) / (2 * W::SPG));  // gate_up groups, an even number
+    const int NGB = 2 * ((NG + 7) / 8);                          // down groups, an even number
     const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
     const rsrc_t rres = make_rsrc(a.rowslot, (uint32_t)(T * k + T) * 4);
 
@@ -578,10 +611,10 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
     // to LDS; after the barrier a wave without items leaves
     Item cur = decode_item(a, sh.tb, n_act, nsl, v, v < n_items, c);
     Ring8 R0, R1;
-    f32x4_t gl[4];
-    wv_issue_glob(a, cur, lane, gl);
-    wv_issue_a(a, cur, 0, lane, R0);
-    wv_issue_a(a, cur, 1, lane, R1);
+    f32x4_t gl[2 * W::NTT];
+    wv_issue_glob<SL>(a, cur, lane, gl);
+    wv_issue_a<SL>(a, cur, 0, lane, R0);
+    wv_issue_a<SL>(a, cur, 1, lane, R1);
     __builtin_amdgcn_sched_barrier(0);
     stage_x<kWW>(a, xv, sh.xsh, x16, XP, tid, lane, wave);
     __syncthreads();
@@ -592,43 +625,44 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
         const _Float16* xr = x16 + xrow * XP + 8 * g;
 
         // ---- phase A: the slice's gate and up tiles over all of K
-        f32x4_t acc[4];
+        f32x4_t acc[2 * W::NTT];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int r = 0; r < 2 * W::NTT; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         int ga = 0;
         for (; ga + 2 < NGA; ga += 2) {
-            wv_compute_a(a, R0, ga, xr, acc);
+            wv_compute_a<SL>(a, R0, ga, xr, acc);
             __builtin_amdgcn_sched_barrier(0);
-            wv_issue_a(a, cur, ga + 2, lane, R0);
+            wv_issue_a<SL>(a, cur, ga + 2, lane, R0);
             __builtin_amdgcn_sched_barrier(0);
-            wv_compute_a(a, R1, ga + 1, xr, acc);
+            wv_compute_a<SL>(a, R1, ga + 1, xr, acc);
             __builtin_amdgcn_sched_barrier(0);
-            wv_issue_a(a, cur, ga + 3, lane, R1);
+            wv_issue_a<SL>(a, cur, ga + 3, lane, R1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        wv_compute_a(a, R0, ga, xr, acc);
+        wv_compute_a<SL>(a, R0, ga, xr, acc);
         __builtin_amdgcn_sched_barrier(0);
-        wv_issue_b(a, cur, 0, lane, R0);
+        wv_issue_b<SL>(a, cur, 0, lane, R0);
         __builtin_amdgcn_sched_barrier(0);
-        wv_compute_a(a, R1, ga + 1, xr, acc);
+        wv_compute_a<SL>(a, R1, ga + 1, xr, acc);
         __builtin_amdgcn_sched_barrier(0);
-        wv_issue_b(a, cur, 1, lane, R1);
+        wv_issue_b<SL>(a, cur, 1, lane, R1);
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- SwiGLU on this lane's rows 4g + [0, 4) of the two tile pairs, then the phase B operand:
-        // lane (c, g') takes slice rows 8g' + [0, 8) of token c from lanes (c, 2(g' & 1)) and (c, 2(g' & 1) + 1)
-        f16x8_t B;
+        // ---- SwiGLU on this lane's rows 4g + [0, 4) of each gate/up tile pair, then the phase B operands:
+        // operand f of lane (c, g') holds slice rows 32f + 8g' + [0, 8) of token c, taken from lanes
+        // (c, 2(g' & 1)) and (c, 2(g' & 1) + 1) of tile 2f + (g' >> 1)
+        f16x8_t B[W::NB];
         float oscale;
         {
             const float xinv = ldexpf(1.0f, -sh.xsh[xrow]);
-            float h[2][4];
+            float h[W::NTT][4];
             float hm = 0.0f;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < W::NTT; ++tt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float gv = acc[tt][r] * xinv * gl[tt][r];
-                    const float uv = acc[2 + tt][r] * xinv * gl[2 + tt][r];
+                    const float uv = acc[W::NTT + tt][r] * xinv * gl[W::NTT + tt][r];
                     h[tt][r] = gv / (1.0f + expf(-gv)) * uv;
                     hm = fmaxf(hm, fabsf(h[tt][r]));
                 }
@@ -636,9 +670,9 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
             hm = fmaxf(hm, __shfl_xor(hm, 32, kWave));
             const int hsh = fp16_shift(hm);
             const float hsc = ldexpf(1.0f, hsh);
-            uint32_t P[2][2];
+            uint32_t P[W::NTT][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < W::NTT; ++tt)
 #pragma unroll
                 for (int d = 0; d < 2; ++d) {
                     const f16x2_t q = {(_Float16)(h[tt][2 * d] * hsc), (_Float16)(h[tt][2 * d + 1] * hsc)};
@@ -646,45 +680,48 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
                 }
             const int src0 = c + 32 * (g & 1), src1 = src0 + 16;
             const bool hi = g >= 2;
-            uint32_t bw[4];
 #pragma unroll
-            for (int d = 0; d < 2; ++d) {
-                const uint32_t a0 = (uint32_t)__shfl((int)P[0][d], src0, kWave);
-                const uint32_t a1 = (uint32_t)__shfl((int)P[1][d], src0, kWave);
-                const uint32_t b0 = (uint32_t)__shfl((int)P[0][d], src1, kWave);
-                const uint32_t b1 = (uint32_t)__shfl((int)P[1][d], src1, kWave);
-                bw[d] = hi ? a1 : a0;
-                bw[2 + d] = hi ? b1 : b0;
+            for (int f = 0; f < W::NB; ++f) {
+                uint32_t bw[4];
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const uint32_t a0 = (uint32_t)__shfl((int)P[2 * f][d], src0, kWave);
+                    const uint32_t a1 = (uint32_t)__shfl((int)P[2 * f + 1][d], src0, kWave);
+                    const uint32_t b0 = (uint32_t)__shfl((int)P[2 * f][d], src1, kWave);
+                    const uint32_t b1 = (uint32_t)__shfl((int)P[2 * f + 1][d], src1, kWave);
+                    bw[d] = hi ? a1 : a0;
+                    bw[2 + d] = hi ? b1 : b0;
+                }
+                B[f] = __builtin_bit_cast(f16x8_t, u32x4_t{bw[0], bw[1], bw[2], bw[3]});
             }
-            B = __builtin_bit_cast(f16x8_t, u32x4_t{bw[0], bw[1], bw[2], bw[3]});
             oscale = ldexpf(1.0f, -hsh) * cur.wc;
         }
         // slice 0 records, per output row of the item, where the expert's down globals live
         __builtin_amdgcn_raw_buffer_store_b32((uint32_t)cur.slot_index, rres,
                                               cur.s == 0 && g == 0 && c < cur.ne ? 4 * cur.prow : kOob, 0, 0);
 
-        // ---- phase B: the slice's 32 down columns for all H outputs
+        // ---- phase B: the slice's SL down columns for all H outputs
         const int pbase = c < cur.ne ? 4 * ((cur.prow * nsl + cur.s) * H + 4 * g) : kOob;
         int gb = 0;
         for (; gb + 2 < NGB; gb += 2) {
-            wv_compute_b(a, R0, gb, B, oscale, pres, pbase);
+            wv_compute_b<SL>(a, R0, gb, B, oscale, pres, pbase);
             __builtin_amdgcn_sched_barrier(0);
-            wv_issue_b(a, cur, gb + 2, lane, R0);
+            wv_issue_b<SL>(a, cur, gb + 2, lane, R0);
             __builtin_amdgcn_sched_barrier(0);
-            wv_compute_b(a, R1, gb + 1, B, oscale, pres, pbase);
+            wv_compute_b<SL>(a, R1, gb + 1, B, oscale, pres, pbase);
             __builtin_amdgcn_sched_barrier(0);
-            wv_issue_b(a, cur, gb + 3, lane, R1);
+            wv_issue_b<SL>(a, cur, gb + 3, lane, R1);
             __builtin_amdgcn_sched_barrier(0);
         }
         // ---- the next item's first groups start streaming
-        wv_compute_b(a, R0, gb, B, oscale, pres, pbase);
+        wv_compute_b<SL>(a, R0, gb, B, oscale, pres, pbase);
         __builtin_amdgcn_sched_barrier(0);
-        wv_issue_glob(a, nxt, lane, gl);
-        wv_issue_a(a, nxt, 0, lane, R0);
+        wv_issue_glob<SL>(a, nxt, lane, gl);
+        wv_issue_a<SL>(a, nxt, 0, lane, R0);
         __builtin_amdgcn_sched_barrier(0);
-        wv_compute_b(a, R1, gb + 1, B, oscale, pres, pbase);
+        wv_compute_b<SL>(a, R1, gb + 1, B, oscale, pres, pbase);
         __builtin_amdgcn_sched_barrier(0);
-        wv_issue_a(a, nxt, 1, lane, R1);
+        wv_issue_a<SL>(a, nxt, 1, lane, R1);
         __builtin_amdgcn_sched_barrier(0);
         cur = nxt;
         v += stride;
@@ -784,17 +821,18 @@ hipError_t launch_fused(const DecArgs& a, int items_max, int nsl, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int SL>
 hipError_t launch_wave(const DecArgs& a, int items_max, int nsl, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wave_kernel),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wave_kernel<SL>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int grid = items_max < g_num_cu ? items_max : g_num_cu;
     const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
-    hipLaunchKernelGGL(wave_kernel, dim3(grid), dim3(kWT), lds, s, a, nsl);
+    hipLaunchKernelGGL((wave_kernel<SL>), dim3(grid), dim3(kWT), lds, s, a, nsl);
     return hipGetLastError();
 }
 
@@ -827,11 +865,19 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
     a.gu_codes = (int)gm.gu_codes; a.gu_scales = (int)gm.gu_scales; a.gu_glob = (int)gm.gu_glob;
     a.dn_codes = (int)gm.dn_codes; a.dn_scales = (int)gm.dn_scales; a.dn_glob = (int)gm.dn_glob;
 
-    const int nsl = I / kSl;
-    const int items_max = ((T * k < E ? T * k : E) + 1) * nsl;
     hipError_t e = init_device_info();
     if (e != hipSuccess) return e;
-    e = items_max >= MOE_WAVE_MIN_ITEMS ? launch_wave(a, items_max, nsl, s) : launch_fused<5, 5>(a, items_max, nsl, s);
+    // 32-row items; when they would outnumber the waves of one pass, 64-row items (half the partials)
+    int nsl = I / kSl;
+    const int rows_max = (T * k < E ? T * k : E) + 1;
+    if (rows_max * nsl < MOE_WAVE_MIN_ITEMS) {
+        e = launch_fused<5, 5>(a, rows_max * nsl, nsl, s);
+    } else if (rows_max * nsl > g_num_cu * kWW && I % 64 == 0) {
+        nsl = I / 64;
+        e = launch_wave<64>(a, rows_max * nsl, nsl, s);
+    } else {
+        e = launch_wave<32>(a, rows_max * nsl, nsl, s);
+    }
     if (e != hipSuccess) return e;
     const int nch = H / 64;
     hipLaunchKernelGGL(dcombine_kernel, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);

@@ -166,9 +166,11 @@ def test_forward_small_shapes_and_ragged():
     """Small and odd sizes: H=128 (one 128-column step, fewer steps than waves), I=32 (one slice), I=96 (a partial
     128-column step of down), E=5/7, T across both paths."""
     for (H, I, E, k, T) in [(128, 32, 5, 2, 3), (128, 32, 5, 2, 17), (384, 96, 7, 3, 40), (384, 96, 7, 3, 11),
-                            (256, 64, 8, 8, 16), (384, 320, 256, 8, 16), (128, 640, 64, 8, 16)]:
-        # the last two have enough (expert, slice) items for the wave-item decode kernel, with padded
-        # gate_up steps (H/128 = 3 and 1) and padded down record groups (H/64 = 6 and 2)
+                            (256, 64, 8, 8, 16), (384, 320, 256, 8, 16), (128, 640, 64, 8, 16),
+                            (384, 640, 256, 8, 16), (128, 640, 256, 8, 16)]:
+        # the last four have enough (expert, slice) items for the wave-item decode kernel (32-row items for
+        # the first two, 64-row items for the last two), with padded gate_up steps (H/128 = 3 and 1) and
+        # padded down record groups (H/64 = 6 and 2)
         _announce(f"forward H={H} I={I} E={E} k={k} T={T}")
         rng = np.random.default_rng(H + I + T)
         distinct = [synth.random_expert_slot(rng, H, I) for _ in range(min(E + 1, 9))]
