@@ -32,6 +32,9 @@
 //             epilogue h = silu(gate) * up -> fp16
 //   down:     O = h W_dn^T over 128 output rows per tile -> fp32
 //   combine:  y_t = sum_j w_tj O[pos(t,j)] + s_t O[shared row t] (fixed order)
+#include <map>
+#include <mutex>
+
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -659,6 +662,37 @@ hipError_t launch_gemm(const PrefillArgs& a, int cls, int max_tiles, int ntn, hi
     return hipGetLastError();
 }
 
+// The 128-row tiles (matrix-core bound) and the 32/64-row remainder tiles
+// (bound by streaming their experts' weights) are independent until the
+// combine, so the remainder GEMMs run on a second stream forked from and
+// joined back to the caller's stream with events: the two kinds of work share
+// the chip instead of following each other.  One side stream and event pair
+// per caller stream (calls on one stream are ordered, so their events can be
+// reused); default priority.
+struct Fork {
+    hipStream_t side = nullptr;
+    hipEvent_t forked = nullptr, joined = nullptr;
+};
+
+hipError_t fork_for(hipStream_t s, Fork& out) {
+    static std::mutex mu;
+    static std::map<hipStream_t, Fork> forks;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = forks.find(s);
+    if (it != forks.end()) {
+        out = it->second;
+        return hipSuccess;
+    }
+    Fork f;
+    hipError_t e = hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f.forked, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f.joined, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    forks[s] = f;
+    out = f;
+    return hipSuccess;
+}
+
 }  // namespace
 
 bool prefill_shape_supported(int H, int I) { return H % 128 == 0 && I % 32 == 0 && H <= 8192; }
@@ -695,17 +729,24 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // remainder tiles on the side stream, 128-row tiles on the caller's stream
+    Fork f;
+    if ((e = fork_for(s, f)) != hipSuccess) return e;
+    if ((e = hipEventRecord(f.forked, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(f.side, f.forked, 0)) != hipSuccess) return e;
     const int ntn_gu = ceil_div(I, 64);
+    if ((e = launch_gemm<64, true>(a, 1, maxsmall, ntn_gu, f.side)) != hipSuccess) return e;
+    if ((e = launch_gemm<32, true>(a, 2, maxsmall, ntn_gu, f.side)) != hipSuccess) return e;
+    if ((e = launch_gemm<64, false>(a, 1, maxsmall, ceil_div(H, 128), f.side)) != hipSuccess) return e;
+    if ((e = launch_gemm<32, false>(a, 2, maxsmall, ceil_div(H, 256), f.side)) != hipSuccess) return e;
+    if ((e = hipEventRecord(f.joined, f.side)) != hipSuccess) return e;
     hipLaunchKernelGGL((big_gemm_kernel<true, kBigNB>), dim3(max128 * ceil_div(I, 128)), dim3(32 * kWave / kBigNB), 0,
                        s, a, ceil_div(I, 128));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_gemm<64, true>(a, 1, maxsmall, ntn_gu, s)) != hipSuccess) return e;
-    if ((e = launch_gemm<32, true>(a, 2, maxsmall, ntn_gu, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((big_gemm_kernel<false, kBigNB>), dim3(max128 * ceil_div(H, 256)), dim3(32 * kWave / kBigNB), 0,
                        s, a, ceil_div(H, 256));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_gemm<64, false>(a, 1, maxsmall, ceil_div(H, 128), s)) != hipSuccess) return e;
-    if ((e = launch_gemm<32, false>(a, 2, maxsmall, ceil_div(H, 256), s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s, f.joined, 0)) != hipSuccess) return e;
     const int nchunk = ceil_div(H / 4, 256);
     hipLaunchKernelGGL(combine_kernel, dim3(T * nchunk), dim3(256), 0, s, a, nchunk);
     return hipGetLastError();

@@ -133,7 +133,9 @@ size_t moe_nvfp4_forward_workspace_bytes(int T, int H, int I, int E, int k);
  * (fp32 accumulation and hidden state), then a combine kernel that sums the
  * slices and applies the down-row globals in a fixed order.  Larger T runs
  * the prefill path: grouped bf16 MFMA GEMMs over the permuted tokens with
- * the weights decoded in registers, bf16 hidden state.  Expert slots referenced by slot_of_expert must lie inside the
+ * the weights decoded in registers, fp16 hidden state; its remainder tiles run
+ * on a library-owned side stream forked from and joined back to `stream`, so
+ * the call stays ordered on `stream` (and capturable in a graph).  Expert slots referenced by slot_of_expert must lie inside the
  * bank; the kernels do not range-check them.  Output order of summation is
  * fixed, so repeated calls give bit-identical results. */
 int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
