@@ -103,16 +103,22 @@ def run_gpu(inp, steps: int, warmup: int):
     logits = torch.from_numpy(np.ascontiguousarray(inp["logits"][:total])).to(dev)
     routes = [dl.Routing.empty(T, E, k, dev) for _ in range(total)]
     ws = dl.workspace(T, layers[0])
+    rf_bytes = _lib.moe_nvfp4_route_forward_workspace_bytes(T, H, I, E, k)
+    ws_rf = torch.empty(rf_bytes, dtype=torch.uint8, device=dev)
     y = torch.empty((total, T, H), dtype=torch.float32, device=dev)
     rws = _lib.moe_route_workspace_bytes(T, E, k)
     rws_t = torch.empty(max(1, rws), dtype=torch.uint8, device=dev)
 
     def step(s: int, do_route: bool = True, do_forward: bool = True):
+        """A step is one moe_nvfp4_route_forward call; do_route / do_forward select the separate calls."""
         r = routes[s]
-        if do_route:
+        if do_route and do_forward:
+            _lib.check(_lib.moe_nvfp4_route_forward(structs[s % R], logits[s], xs[s], T, r.ids, r.w, r.offsets,
+                                                    r.sorted_assign, r.assign_pos, y[s], 0, ws_rf, rf_bytes, None))
+        elif do_route:
             _lib.check(_lib.moe_route_topk(logits[s], T, E, k, r.ids, r.w, r.offsets, r.sorted_assign,
                                            r.assign_pos, rws_t, rws, None))
-        if do_forward:
+        else:
             _lib.check(_lib.moe_nvfp4_forward(structs[s % R], xs[s], T, r.ids, r.w, r.offsets, r.sorted_assign,
                                               r.assign_pos, y[s], 0, ws, ws.numel(), None))
 
@@ -149,8 +155,14 @@ def run_gpu(inp, steps: int, warmup: int):
     wall = time.perf_counter() - t0
     replay_ok = torch.equal(y[total - 1], y_eager)
 
-    # forward kernels only, HIP events on the stream they run on
+    # the step's calls, HIP events on the stream they run on
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(cur)
+    g_step.replay()
+    ev1.record(cur)
+    torch.cuda.synchronize()
+    call_ms = ev0.elapsed_time(ev1) / steps
+    # forward kernels only (routing given), HIP events
     ev0.record(cur)
     g_fwd.replay()
     ev1.record(cur)
@@ -175,7 +187,7 @@ def run_gpu(inp, steps: int, warmup: int):
         off = routes[i].offsets.cpu().numpy()
         distinct.append(int(np.count_nonzero(np.diff(off))))
     counts = np.diff(routes[total - 1].offsets.cpu().numpy())
-    return dict(wall=wall, fwd_ms=fwd_ms, route_ms=route_ms, distinct=distinct, replay_ok=replay_ok,
+    return dict(wall=wall, fwd_ms=fwd_ms, call_ms=call_ms, route_ms=route_ms, distinct=distinct, replay_ok=replay_ok,
                 y_last=y[total - 1].cpu().numpy(), ids_last=routes[total - 1].ids.cpu().numpy(),
                 counts_max=int(counts.max()), counts_min=int(counts.min()))
 
@@ -403,9 +415,11 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     tokens_s = T * steps / res["wall"]
     mean_d = float(np.mean(res["distinct"]))
     bytes_fwd = (mean_d + 1) * sb                       # touched expert slots incl. the shared expert
-    fwd_s = res["fwd_ms"] * 1e-3
-    gbs = bytes_fwd / fwd_s / 1e9
     prefill = T > 16
+    # roofline unit: decode routes inside its first kernel, so the unit is the step's route_forward call;
+    # prefill routes in kernels of its own, so the unit is the forward call
+    fwd_s = (res["fwd_ms"] if prefill else res["call_ms"]) * 1e-3
+    gbs = bytes_fwd / fwd_s / 1e9
     flops = synth.prefill_flops(T, H, I, k)
     if prefill:
         tf = flops / fwd_s / 1e12
@@ -417,8 +431,8 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic(name, "decode"),
-                "kernel": "moe_nvfp4_forward decode (fused_kernel + dcombine_kernel), timed together with HIP "
-                          "events",
+                "kernel": "moe_nvfp4_route_forward decode call (fused_kernel or wave_kernel with the routing in "
+                          "its prologue, then dcombine_kernel), timed together with HIP events",
                 "per_launch": f"{bytes_fwd / 1e6:.2f} MB expert weights per forward ((D+1) x {sb} B, "
                               f"mean D = {mean_d:.2f})"}
     out = {
@@ -430,6 +444,7 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
                    "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"route_us": round(res["route_ms"] * 1e3, 2), "forward_us": round(res["fwd_ms"] * 1e3, 2),
+                  "route_forward_us": round(res["call_ms"] * 1e3, 2),
                   "step_us": round(ms_step * 1e3, 2), "expert_weight_GBps_forward": round(gbs, 1),
                   "expert_weight_GBps_step": round(bytes_fwd / (ms_step * 1e-3) / 1e9, 1),
                   "graph_replay_matches_eager": bool(res["replay_ok"])},

@@ -24,6 +24,7 @@ EXPORTED = [
     "moe_last_error", "moe_nvfp4_slot_bytes", "moe_route_workspace_bytes", "moe_route_topk",
     "moe_nvfp4_forward_workspace_bytes", "moe_nvfp4_forward", "expert_cache_fill", "moe_cache_create",
     "moe_cache_destroy", "moe_cache_plan", "moe_nvfp4_slice_bank", "moe_nvfp4_dequant",
+    "moe_nvfp4_route_forward_workspace_bytes", "moe_nvfp4_route_forward",
 ]
 
 
@@ -67,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_forward.restype = _i
         L.moe_nvfp4_forward.argtypes = [ctypes.POINTER(LayerStruct), _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                                         _vp, _sz, _vp]
+        L.moe_nvfp4_route_forward_workspace_bytes.restype = _sz
+        L.moe_nvfp4_route_forward_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+        L.moe_nvfp4_route_forward.restype = _i
+        L.moe_nvfp4_route_forward.argtypes = [ctypes.POINTER(LayerStruct), _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _i, _vp, _sz, _vp]
         L.expert_cache_fill.restype = _i
         L.expert_cache_fill.argtypes = [_vp, _sz, _i, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(_vp), _i, _vp,
                                         _vp]
@@ -137,6 +143,17 @@ def moe_nvfp4_forward(layer: LayerStruct, x, T, topk_ids, topk_w, expert_offsets
     return lib().moe_nvfp4_forward(ctypes.byref(layer), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w),
                                    _ptr(expert_offsets), _ptr(sorted_assign), _ptr(assign_pos), _ptr(y),
                                    int(accumulate), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_nvfp4_route_forward_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(lib().moe_nvfp4_route_forward_workspace_bytes(T, H, I, E, k))
+
+
+def moe_nvfp4_route_forward(layer: LayerStruct, logits, x, T, topk_ids, topk_w, expert_offsets, sorted_assign,
+                            assign_pos, y, accumulate, ws, ws_bytes, stream=None) -> int:
+    return lib().moe_nvfp4_route_forward(ctypes.byref(layer), _ptr(logits), _ptr(x), T, _ptr(topk_ids),
+                                         _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_assign), _ptr(assign_pos),
+                                         _ptr(y), int(accumulate), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def expert_cache_fill(cache_base, slot_bytes, num_slots, dst_slots, srcs, copy_stream=None, done_event=None) -> int:

@@ -60,6 +60,11 @@ int check_route_shape(int T, int E, int k) {
     return MOE_OK;
 }
 
+int forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
+                 const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
+                 const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream,
+                 const moe::RouteOut* route);
+
 }  // namespace
 
 extern "C" {
@@ -102,6 +107,58 @@ int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, 
                       const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
                       const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
                       hipStream_t stream) {
+    return forward_impl(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y, accumulate, ws,
+                        ws_bytes, stream, nullptr);
+}
+
+size_t moe_nvfp4_route_forward_workspace_bytes(int T, int H, int I, int E, int k) {
+    if (!shape_ok(H, I) || check_route_shape(T, E, k) != MOE_OK) return 0;
+    return moe::align256(moe::forward_ws_bytes(T, H, I, E, k)) + moe::route_ws_bytes(T, E, k);
+}
+
+int moe_nvfp4_route_forward(const moe_nvfp4_layer_t* layer, const float* logits, const uint16_t* x, int T,
+                            int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_assign,
+                            int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    if (!layer) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_nvfp4_route_forward: layer is NULL");
+    const moe_nvfp4_layer_t& L = *layer;
+    int rc = check_route_shape(T, L.E, L.k);
+    if (rc != MOE_OK) return rc;
+    if (T == 0) return forward_impl(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y,
+                                    accumulate, ws, ws_bytes, stream, nullptr);
+    if (!logits) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_nvfp4_route_forward: logits is NULL");
+    if (!shape_ok(L.H, L.I))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H must be a positive multiple of 128 and I of 32 (got H=%d, I=%d)",
+                    L.H, L.I);
+    const size_t fws = moe::align256(moe::forward_ws_bytes(T, L.H, L.I, L.E, L.k));
+    const size_t need = fws + moe::route_ws_bytes(T, L.E, L.k);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "route_forward workspace %zu < %zu bytes", ws_bytes, need);
+    if (moe::decode_path(T, L.H, L.I, L.k) && moe::decode_routes_in_kernel(T, L.E)) {
+        const moe::RouteOut ro{logits, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos};
+        return forward_impl(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y, accumulate,
+                            ws, fws, stream, &ro);
+    }
+    // routing as its own launch (its workspace after the forward's), then the forward
+    if (!topk_ids || !topk_w || !expert_offsets || !sorted_assign || !assign_pos)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_nvfp4_route_forward: null routing output");
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    hipError_t e = moe::launch_route(logits, T, L.E, L.k, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos,
+                                     static_cast<uint8_t*>(ws) + fws, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_route_forward routing launch");
+    return forward_impl(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y, accumulate, ws,
+                        fws, stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
+                 const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
+                 const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream,
+                 const moe::RouteOut* route) {
     if (!layer) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_nvfp4_forward: layer is NULL");
     const moe_nvfp4_layer_t& L = *layer;
     if (!shape_ok(L.H, L.I))
@@ -135,7 +192,7 @@ int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, 
     hipError_t e;
     if (moe::decode_path(T, L.H, L.I, L.k)) {
         e = moe::launch_decode(ml, x, T, topk_w, topk_ids, expert_offsets, sorted_assign, assign_pos, y, accumulate,
-                               ws, stream);
+                               ws, stream, route);
     } else {
         if (!moe::prefill_shape_supported(L.H, L.I))
             return fail(MOE_ERR_UNSUPPORTED_SHAPE, "prefill path does not support H=%d, I=%d", L.H, L.I);
@@ -145,6 +202,10 @@ int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, 
     if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_forward launch");
     return MOE_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int expert_cache_fill(void* cache_base, size_t slot_bytes, int num_slots, const int32_t* dst_slots,
                       const void* const* src, int n, hipStream_t copy_stream, hipEvent_t done) {

@@ -26,6 +26,7 @@
 // order, so results are bit-reproducible.
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
+#include "route_device.hpp"
 
 namespace moe {
 namespace {
@@ -51,6 +52,10 @@ struct DecArgs {
     float* y;
     int accumulate;
     int gu_codes, gu_scales, gu_glob, dn_codes, dn_scales, dn_glob;  // region offsets in a slot
+    // routing inside the kernel (route_forward): the logits in, the routing outputs (written by workgroup 0)
+    const float* logits;
+    int32_t *r_ids, *r_offsets, *r_sorted, *r_pos;
+    float* r_w;
 };
 
 // Routing tables staged in LDS once per workgroup.
@@ -59,9 +64,11 @@ struct Tables {
     int slot[kMaxE];             // slot_of_expert
     int sorted[kDecodeMaxAssign];
     float w[kDecodeMaxAssign];
+    int ids[kDecodeMaxAssign];   // top-k ids, when the kernel routes
     int act[kMaxE];              // experts with assignments, ascending
     int n_act;
 };
+constexpr int kRouteInKernelMaxE = 256;  // experts the decode kernels route themselves (4 logits per lane)
 
 // A work item as seen by one lane: its slice, its tokens (the MFMA's 16
 // columns) and the expert's slot as a buffer resource (0 bytes when the
@@ -356,6 +363,85 @@ __device__ __forceinline__ int stage_tables(const DecArgs& a, Tables& tb, XRegs<
     return __builtin_amdgcn_readfirstlane(tb.n_act);
 }
 
+// The same prologue for a kernel that routes itself (E <= 256): each wave
+// selects the top-k of its tokens straight from the logits (T <= 16, so one
+// or two tokens per wave), then every assignment is ranked directly,
+//   offsets[e] = #{b : e_b < e},  pos(a) = #{b : (e_b, b) < (e_a, a)},
+// the same stable grouping the routing kernels produce.  Workgroup 0 writes
+// the routing outputs.
+template <int NW>
+__device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<NW>& xr, int tid, int lane,
+                                           int wave) {
+    constexpr int NT = NW * kWave;
+    const int H = a.H, T = a.T, k = a.k, E = a.E, n = T * k;
+    constexpr int R = (kMaxE + NT - 1) / NT;
+    uint32_t vs[R];
+    {
+        const rsrc_t rs = make_rsrc(a.slot_of_expert, (uint32_t)E * 4);
+        const rsrc_t rx = make_rsrc(a.x, (uint32_t)T * H * 2);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = tid + NT * r;
+            vs[r] = buf_load4(rs, i < E ? 4 * i : kOob);
+        }
+#pragma unroll
+        for (int p = 0; p < XRegs<NW>::XT; ++p) {
+            const int t = wave + NW * p;
+#pragma unroll
+            for (int i = 0; i < XRegs<NW>::XC; ++i) {
+                const int ch = lane + kWave * i;
+                xr.v[p][i] = buf_load16(rx, t < T && ch < H / 8 ? 2 * (t * H + 8 * ch) : kOob);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    for (int t = wave; t < T; t += NW)
+        topk_one_token<kRouteInKernelMaxE / kWave>(a.logits + (size_t)t * E, E, k, tb.ids + t * k, tb.w + t * k, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = tid + NT * r;
+        if (i < E) tb.slot[i] = (int)vs[r];
+    }
+    __syncthreads();
+    const bool out = blockIdx.x == 0;
+    for (int as = tid; as < n; as += NT) {
+        const int e = tb.ids[as];
+        int pos = 0;
+        for (int b = 0; b < n; ++b) {
+            const int eb = tb.ids[b];
+            pos += (eb < e || (eb == e && b < as)) ? 1 : 0;
+        }
+        tb.sorted[pos] = as;
+        if (out) {
+            a.r_ids[as] = e;
+            a.r_w[as] = tb.w[as];
+            a.r_sorted[pos] = as;
+            a.r_pos[as] = pos;
+        }
+    }
+    for (int e = tid; e <= E; e += NT) {
+        int c = 0;
+        for (int b = 0; b < n; ++b) c += tb.ids[b] < e ? 1 : 0;
+        tb.off[e] = c;
+        if (out) a.r_offsets[e] = c;
+    }
+    __syncthreads();
+    if (wave == 0) {  // compaction of the experts with assignments, ascending
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        int base = 0;
+        for (int e0 = 0; e0 < E; e0 += kWave) {
+            const int e = e0 + lane;
+            const bool act = e < E && tb.off[e + 1] > tb.off[e];
+            const uint64_t m = __ballot(act);
+            if (act) tb.act[base + __popcll(m & below)] = e;
+            base += __popcll(m);
+        }
+        if (lane == 0) tb.n_act = base;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(tb.n_act);
+}
+
 template <int NW>
 __device__ __forceinline__ void stage_x(const DecArgs& a, const XRegs<NW>& xr, int* xsh, _Float16* x16, int XP,
                                         int tid, int lane, int wave) {
@@ -404,7 +490,7 @@ __device__ __forceinline__ void stage_x(const DecArgs& a, const XRegs<NW>& xr, i
 // next items stream while this one reduces, runs SwiGLU and finishes.
 // KQW: most 128-column steps of K = H per wave (steps wave % 4 + 4 i);
 // NRGW: most 64-row down groups per wave (groups wave + 8 i).
-template <int KQW, int NRGW>
+template <int KQW, int NRGW, bool ROUTE>
 __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
     extern __shared__ __attribute__((aligned(16))) _Float16 x16[];  // (T + 1) rows of XP halves; row T is zero
     __shared__ DecShared sh;
@@ -415,7 +501,7 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
     Tables& tb = sh.tb;
 
     XRegs<kDW> xv;
-    const int n_act = stage_tables<kDW>(a, tb, xv, tid, lane, wave);
+    const int n_act = ROUTE ? stage_route<kDW>(a, tb, xv, tid, lane, wave) : stage_tables<kDW>(a, tb, xv, tid, lane, wave);
     const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
     int u = blockIdx.x;
     if (u >= n_items) return;  // uniform
@@ -584,7 +670,7 @@ __device__ __forceinline__ void wv_compute_b(const DecArgs& a, const Ring8& R, i
     }
 }
 
-template <int SL>
+template <int SL, bool ROUTE>
 __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
     using W = WaveGeom<SL>;
     extern __shared__ __attribute__((aligned(16))) _Float16 x16[];  // (T + 1) rows of XP halves; row T is zero
@@ -594,7 +680,8 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
     const int H = a.H, T = a.T, k = a.k;
     const int XP = H + 8;
     XRegs<kWW> xv;
-    const int n_act = stage_tables<kWW>(a, sh.tb, xv, tid, lane, wave);
+    const int n_act = ROUTE ? stage_route<kWW>(a, sh.tb, xv, tid, lane, wave)
+                            : stage_tables<kWW>(a, sh.tb, xv, tid, lane, wave);
     const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
     const int stride = (int)gridDim.x * kWW;
     // consecutive items go to different CUs; readfirstlane tells the compiler the item is wave-uniform
@@ -806,34 +893,48 @@ hipError_t init_device_info() {
     return e;
 }
 
-template <int KQW, int NRGW>
+template <int KQW, int NRGW, bool ROUTE>
 hipError_t launch_fused(const DecArgs& a, int items_max, int nsl, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW, ROUTE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
+    // a kernel that routes itself has every workgroup route; workgroup 0 must exist to write the routing
     const int grid = items_max < g_num_cu ? items_max : g_num_cu;
     const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
-    hipLaunchKernelGGL((fused_kernel<KQW, NRGW>), dim3(grid), dim3(kDT), lds, s, a, nsl);
+    hipLaunchKernelGGL((fused_kernel<KQW, NRGW, ROUTE>), dim3(grid), dim3(kDT), lds, s, a, nsl);
     return hipGetLastError();
 }
 
-template <int SL>
+template <int SL, bool ROUTE>
 hipError_t launch_wave(const DecArgs& a, int items_max, int nsl, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wave_kernel<SL>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int grid = items_max < g_num_cu ? items_max : g_num_cu;
     const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
-    hipLaunchKernelGGL((wave_kernel<SL>), dim3(grid), dim3(kWT), lds, s, a, nsl);
+    hipLaunchKernelGGL((wave_kernel<SL, ROUTE>), dim3(grid), dim3(kWT), lds, s, a, nsl);
     return hipGetLastError();
+}
+
+template <bool ROUTE>
+hipError_t launch_main(const DecArgs& a, int I, int T, int k, int E, int& nsl, hipStream_t s) {
+    // 32-row items; when they would outnumber the waves of one pass, 64-row items (half the partials)
+    nsl = I / kSl;
+    const int rows_max = (T * k < E ? T * k : E) + 1;
+    if (rows_max * nsl < MOE_WAVE_MIN_ITEMS) return launch_fused<5, 5, ROUTE>(a, rows_max * nsl, nsl, s);
+    if (rows_max * nsl > g_num_cu * kWW && I % 64 == 0) {
+        nsl = I / 64;
+        return launch_wave<64, ROUTE>(a, rows_max * nsl, nsl, s);
+    }
+    return launch_wave<32, ROUTE>(a, rows_max * nsl, nsl, s);
 }
 
 }  // namespace
@@ -846,9 +947,12 @@ bool decode_shape_supported(int H, int I) { return H % 128 == 0 && I % kSl == 0 
 size_t decode_part_bytes(int T, int H, int I, int k) { return (size_t)(T * k + T) * (I / kSl) * H * 4; }
 size_t decode_rowslot_bytes(int T, int k) { return (size_t)(T * k + T) * 4; }
 
+// In-kernel routing pays off while every wave routes at most one token.
+bool decode_routes_in_kernel(int T, int E) { return E <= kRouteInKernelMaxE && T <= kDW && T <= kWW; }
+
 hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                          const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
-                         int accumulate, void* ws, hipStream_t s) {
+                         int accumulate, void* ws, hipStream_t s, const RouteOut* route) {
     (void)ids;
     (void)assign_pos;
     const int H = L.H, I = L.I, E = L.E, k = L.k;
@@ -865,19 +969,16 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
     a.gu_codes = (int)gm.gu_codes; a.gu_scales = (int)gm.gu_scales; a.gu_glob = (int)gm.gu_glob;
     a.dn_codes = (int)gm.dn_codes; a.dn_scales = (int)gm.dn_scales; a.dn_glob = (int)gm.dn_glob;
 
+    a.logits = route ? route->logits : nullptr;
+    a.r_ids = route ? route->ids : nullptr;
+    a.r_w = route ? route->w : nullptr;
+    a.r_offsets = route ? route->offsets : nullptr;
+    a.r_sorted = route ? route->sorted_assign : nullptr;
+    a.r_pos = route ? route->assign_pos : nullptr;
     hipError_t e = init_device_info();
     if (e != hipSuccess) return e;
-    // 32-row items; when they would outnumber the waves of one pass, 64-row items (half the partials)
-    int nsl = I / kSl;
-    const int rows_max = (T * k < E ? T * k : E) + 1;
-    if (rows_max * nsl < MOE_WAVE_MIN_ITEMS) {
-        e = launch_fused<5, 5>(a, rows_max * nsl, nsl, s);
-    } else if (rows_max * nsl > g_num_cu * kWW && I % 64 == 0) {
-        nsl = I / 64;
-        e = launch_wave<64>(a, rows_max * nsl, nsl, s);
-    } else {
-        e = launch_wave<32>(a, rows_max * nsl, nsl, s);
-    }
+    int nsl = 0;
+    e = route ? launch_main<true>(a, I, T, k, E, nsl, s) : launch_main<false>(a, I, T, k, E, nsl, s);
     if (e != hipSuccess) return e;
     const int nch = H / 64;
     hipLaunchKernelGGL(dcombine_kernel, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);

@@ -75,9 +75,23 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
 }
 inline size_t forward_ws_bytes(int T, int H, int I, int E, int k) { return ws_layout(T, H, I, E, k).total; }
 
+// Routing computed inside the decode kernels (route_forward): the logits and
+// the routing outputs, which the kernels fill as moe_route_topk would.
+struct RouteOut {
+    const float* logits;
+    int32_t* ids;
+    float* w;
+    int32_t* offsets;
+    int32_t* sorted_assign;
+    int32_t* assign_pos;
+};
+bool decode_routes_in_kernel(int T, int E);
+
+// route == nullptr: the routing tensors are inputs; otherwise the kernels
+// route from route->logits and write the routing tensors.
 hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                          const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
-                         int accumulate, void* ws, hipStream_t s);
+                         int accumulate, void* ws, hipStream_t s, const RouteOut* route = nullptr);
 
 // Prefill path, T > 16 (prefill.hip)
 bool prefill_shape_supported(int H, int I);

@@ -1,125 +1,17 @@
-// Top-k routing with renormalised weights and the deterministic permutation
-// of assignments by expert, for gfx950.
-//
-// Routing follows the replicated router with norm_topk_prob of the pages
-// (issue #62, R9700 interim report: "norm_topk_prob defaults True and the
-// router is replicated"): the k largest logits are selected and their
-// weights are the softmax over those k logits, which equals a full softmax
-// renormalised over the selected experts.  Selection order is (logit
-// descending, expert index ascending).  The permutation groups the T*k
-// assignments by expert with a stable counting sort (per-expert counts,
-// exclusive scan, then stable ranks from wave ballots), so the grouping is
-// bit-reproducible: no atomic operation decides an order (atomics only count).
+// Top-k routing with renormalised weights (route_device.hpp) and the
+// deterministic permutation of assignments by expert, for gfx950.  The
+// permutation groups the T*k assignments by expert with a stable counting
+// sort (per-expert counts, exclusive scan, then stable ranks from wave
+// ballots), so the grouping is bit-reproducible: no atomic operation decides
+// an order (atomics only count).
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
+#include "route_device.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kMaxE = 1024;
-constexpr int kVPL = kMaxE / kWave;  // logits held per lane
-
-// Selection order as one unsigned 64-bit key per (logit, expert): the high
-// word maps the logit monotonically onto uint32 (-0 folded onto +0, so equal
-// logits tie), the low word is ~index, so a larger key ranks first and ties
-// go to the lower index.  Key 0 means "no candidate" (every real key has a
-// nonzero low word).  A NaN logit maps to some key; NaN input is a
-// precondition violation and only has to leave a valid, untaken expert.
-__device__ __forceinline__ uint64_t rank_key(float v, int idx) {
-    uint32_t u = __float_as_uint(v + 0.0f);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)idx;
-}
-__device__ __forceinline__ int key_index(uint64_t key) { return (int)~(uint32_t)key; }
-// The logit of a key (a -0 logit comes back as +0, which no later step can tell apart).
-__device__ __forceinline__ float key_value(uint64_t key) {
-    const uint32_t u = (uint32_t)(key >> 32);
-    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-
-// DPP row operations of the GCN/CDNA ISA (gfx9 encodings).
-constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr3 = 0x113, kDppRowShr4 = 0x114,
-              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
-
-// One branch-free step of a wave max over 64-bit keys: take the key DPP
-// control CTRL brings in when it is larger; lanes the masks disable keep
-// their own (old operand = own key).
-template <int CTRL, int ROW_MASK, int BANK_MASK>
-__device__ __forceinline__ uint64_t kmax_step(uint64_t key) {
-    const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
-    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, BANK_MASK, false);
-    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, BANK_MASK, false);
-    const uint64_t other = ((uint64_t)ohi << 32) | olo;
-    return other > key ? other : key;
-}
-
-// Wave-wide maximum key, returned to every lane.  The DPP sequence leaves
-// the result in lane 63 (shifts within each 16-lane row, then the row
-// broadcasts); max tolerates the overlapping inputs.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
-    key = kmax_step<kDppRowShr1, 0xF, 0xF>(key);
-    key = kmax_step<kDppRowShr2, 0xF, 0xF>(key);
-    key = kmax_step<kDppRowShr3, 0xF, 0xF>(key);
-    key = kmax_step<kDppRowShr4, 0xF, 0xE>(key);
-    key = kmax_step<kDppRowShr8, 0xF, 0xC>(key);
-    key = kmax_step<kDppRowBcast15, 0xA, 0xF>(key);
-    key = kmax_step<kDppRowBcast31, 0xC, 0xF>(key);
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)key, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// One wave selects the top-k of row `l` (E <= 64 * VPL logits) and writes
-// ids and weights.  Selection: k rounds of a wave maximum over each lane's
-// best remaining key.  Weights: softmax over the k selected logits in
-// double (exp(l_j - l_max) / sum), summed in selection order, rounded to f32.
-template <int VPL>
-__device__ void topk_one_token(const float* __restrict__ l, int E, int k, int32_t* __restrict__ ids,
-                               float* __restrict__ w, int lane) {
-    static_assert(VPL <= kVPL, "too many logits per lane");
-    uint64_t key[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int idx = lane + kWave * i;
-        key[i] = idx < E ? rank_key(l[idx], idx) : 0ull;
-    }
-    float held = 0.0f;  // selection j's logit, kept by lane j (j < 64)
-    float m = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_key(best);
-        const int bi = key_index(best);
-        const int owner_slot = bi / kWave, owner_lane = bi % kWave;
-        const float bv = key_value(best);
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) key[i] = (i == owner_slot && lane == owner_lane) ? 0ull : key[i];
-        if (j == 0) m = bv;
-        if ((j % kWave) == lane) ids[j] = bi;
-        if (j == lane) held = bv;
-        if (j >= kWave && (j % kWave) == lane) w[j] = bv;  // parked logit, replaced below
-    }
-    // exp of each selected logit relative to the largest, in double
-    if (k <= kWave) {
-        const double ex = lane < k ? exp((double)held - (double)m) : 0.0;
-        double sum = 0.0;
-        for (int j = 0; j < k; ++j) {
-            const int lo = __builtin_amdgcn_readlane((int)(uint32_t)__double_as_longlong(ex), j);
-            const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(__double_as_longlong(ex) >> 32), j);
-            sum += __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
-        }
-        if (lane < k) w[lane] = (float)(ex / sum);
-    } else {
-        // rare: more selections than lanes; logits of selections >= 64 were parked in w
-        double sum = 0.0;
-        for (int j = 0; j < k; ++j) sum += exp((double)(j < kWave ? __shfl(held, j, kWave) : w[j]) - (double)m);
-        for (int j = lane; j < k; j += kWave) {
-            const float lj = j < kWave ? held : w[j];
-            w[j] = (float)(exp((double)lj - (double)m) / sum);
-        }
-    }
-}
+constexpr int kMaxE = kRouteMaxE;
 
 template <int VPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int T, int E, int k,

@@ -105,6 +105,23 @@ def forward(layer: DeviceLayer, x: torch.Tensor, r: Routing, y: torch.Tensor | N
     return y
 
 
+def route_forward(layer: DeviceLayer, logits: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None,
+                  accumulate: bool = False, out: Routing | None = None, ws: torch.Tensor | None = None,
+                  slot_of_expert: torch.Tensor | None = None, shared: bool = True, stream=None):
+    """Routing and forward in one call; returns (y, routing)."""
+    T, E = logits.shape
+    r = Routing.empty(T, E, layer.k, x.device) if out is None else out
+    if y is None:
+        y = torch.empty((T, layer.H), dtype=torch.float32, device=x.device)
+    if ws is None:
+        nb = _lib.moe_nvfp4_route_forward_workspace_bytes(T, layer.H, layer.I, layer.E, layer.k)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=x.device)
+    st = layer.struct(slot_of_expert, shared)
+    check(_lib.moe_nvfp4_route_forward(st, logits, x, T, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y,
+                                       int(accumulate), ws, ws.numel(), stream))
+    return y, r
+
+
 def dequant(slot: torch.Tensor, H: int, I: int, matrix: int, stream=None) -> torch.Tensor:
     """fp32 gate_up (matrix 0, [2I, H]) or down (matrix 1, [H, I]) of one device slot."""
     shape = (2 * I, H) if matrix == 0 else (H, I)

@@ -135,13 +135,32 @@ size_t moe_nvfp4_forward_workspace_bytes(int T, int H, int I, int E, int k);
  * the prefill path: grouped bf16 MFMA GEMMs over the permuted tokens with
  * the weights decoded in registers, fp16 hidden state; its remainder tiles run
  * on a library-owned side stream forked from and joined back to `stream`, so
- * the call stays ordered on `stream` (and capturable in a graph).  Expert slots referenced by slot_of_expert must lie inside the
- * bank; the kernels do not range-check them.  Output order of summation is
- * fixed, so repeated calls give bit-identical results. */
+ * the call stays ordered on `stream` (and capturable in a graph).  Expert
+ * slots referenced by slot_of_expert must lie inside the bank; the kernels do
+ * not range-check them.  Output order of summation is fixed, so repeated
+ * calls give bit-identical results. */
 int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
                       const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
                       const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
                       hipStream_t stream);
+
+/* Workspace moe_nvfp4_route_forward needs for T tokens; 0 on bad shapes. */
+size_t moe_nvfp4_route_forward_workspace_bytes(int T, int H, int I, int E, int k);
+
+/* moe_route_topk followed by moe_nvfp4_forward in one call, with the same
+ * results: the routing outputs (topk_ids, topk_w, expert_offsets,
+ * sorted_assign, assign_pos, device buffers sized as for moe_route_topk) are
+ * written, and y is the layer output for the routing of `logits` (device f32
+ * [T, E]).  On the decode path with T <= 8 and E <= 256 the forward's first
+ * kernel routes by itself in its prologue (one launch less on the critical
+ * path of a decode step); otherwise the routing is its own launch on
+ * `stream`.  The
+ * workspace holds both calls' workspaces; the other arguments and errors are
+ * those of the two calls. */
+int moe_nvfp4_route_forward(const moe_nvfp4_layer_t* layer, const float* logits, const uint16_t* x, int T,
+                            int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_assign,
+                            int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* ------------------------------------------------------------------ expert cache
  * Copy n expert slots from pinned host banks into GPU cache slots

@@ -82,6 +82,23 @@ def test_forward_validation_without_gpu():
     assert f(_layer(), T=0) == _lib.MOE_OK
 
 
+def test_route_forward_validation_without_gpu():
+    d = 0x3000
+    f = lambda L, lg=d, T=1, ws=0x200000, nb=1 << 30: _lib.moe_nvfp4_route_forward(L, lg, d, T, d, d, d, d, d, d, 0,
+                                                                                  ws, nb, 0)
+    assert f(_layer(I=650)) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert f(_layer(), lg=None) == _lib.MOE_ERR_INVALID_ARGUMENT
+    assert "logits" in _lib.last_error()
+    assert f(_layer(k=300)) == _lib.MOE_ERR_INVALID_ARGUMENT
+    need = _lib.moe_nvfp4_route_forward_workspace_bytes(16, 2560, 640, 256, 8)
+    assert need >= _lib.moe_nvfp4_forward_workspace_bytes(16, 2560, 640, 256, 8)
+    assert f(_layer(), T=16, nb=need - 1) == _lib.MOE_ERR_WORKSPACE_TOO_SMALL
+    big = _lib.moe_nvfp4_route_forward_workspace_bytes(4096, 2560, 640, 256, 8)
+    assert big >= _lib.moe_nvfp4_forward_workspace_bytes(4096, 2560, 640, 256, 8) + \
+        _lib.moe_route_workspace_bytes(4096, 256, 8)
+    assert f(_layer(), T=0) == _lib.MOE_OK
+
+
 def test_other_entry_points_validate():
     assert _lib.moe_nvfp4_dequant(0x100, 96, 32, 0, 0x100, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE   # H % 128
     assert _lib.moe_nvfp4_dequant(0x100, 128, 48, 0, 0x100, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE  # I % 32

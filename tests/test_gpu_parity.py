@@ -183,6 +183,64 @@ def test_forward_small_shapes_and_ragged():
         assert_close(y.cpu().numpy(), _oracle_forward(L), f"H={H} I={I} T={T}")
 
 
+def _route_forward_vs_separate(L, what, slot_map=None, shared=True):
+    """moe_nvfp4_route_forward against moe_route_topk + moe_nvfp4_forward on the same inputs: routing outputs bit
+    for bit, y bit for bit (the same kernels after the prologue), and y against the oracle."""
+    dev = device_layer(L)
+    x = device_x(L)
+    lg = device_logits(L)
+    sm = None if slot_map is None else torch.from_numpy(np.ascontiguousarray(slot_map, dtype=np.int32)).cuda()
+    r_sep = dl.route(lg, L.k)
+    y_sep = dl.forward(dev, x, r_sep, slot_of_expert=sm, shared=shared)
+    y_one, r_one = dl.route_forward(dev, lg, x, slot_of_expert=sm, shared=shared)
+    torch.cuda.synchronize()
+    for name in ("ids", "w", "offsets", "sorted_assign", "assign_pos"):
+        a, b = getattr(r_sep, name).cpu().numpy(), getattr(r_one, name).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{what}: routing output {name} differs"
+    assert np.array_equal(y_sep.cpu().numpy().view(np.uint32), y_one.cpu().numpy().view(np.uint32)), what
+    assert_close(y_one.cpu().numpy(), _oracle_forward(L, slot_map=slot_map, shared=shared), what)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 16])
+def test_route_forward_decode(T):
+    """Routing inside the decode kernels (E <= 256, T <= 8: one wave per token); T = 16 routes in its own launch."""
+    _announce(f"route_forward decode T={T}")
+    L = synth.make_layer("decode_bs16", T=T, n_distinct=8, seed=300 + T)
+    _route_forward_vs_separate(L, f"route_forward T={T}")
+
+
+def test_route_forward_ties_skips_and_fallbacks():
+    rng = np.random.default_rng(9)
+    # heavy ties and -0/+0 at decode size, with skipped experts and no shared expert
+    L = synth.make_layer("decode_bs16", T=5, n_distinct=6, seed=9)
+    L.logits = rng.integers(0, 3, L.logits.shape).astype(np.float32)
+    L.logits[:, 5] = -0.0
+    L.logits[:, 6] = 0.0
+    ids, w = oracle.route(L.logits, L.k)
+    sm = L.slot_of_expert.copy()
+    sm[np.unique(ids)[::3]] = -1
+    _announce("route_forward ties, skipped experts, no shared expert")
+    _route_forward_vs_separate(L, "route_forward ties", slot_map=sm, shared=False)
+    lg = device_logits(L)
+    _, r = dl.route_forward(device_layer(L), lg, device_x(L))
+    torch.cuda.synchronize()
+    off, srt, pos = oracle.permute(ids, L.E)
+    assert np.array_equal(r.ids.cpu().numpy(), ids) and np.array_equal(r.offsets.cpu().numpy(), off)
+    assert np.array_equal(r.sorted_assign.cpu().numpy(), srt) and np.array_equal(r.assign_pos.cpu().numpy(), pos)
+    # the separate-routing fallbacks: prefill size, and more experts than the kernels route themselves
+    _announce("route_forward prefill T=40 (separate routing launch)")
+    _route_forward_vs_separate(synth.make_layer("prefill_2048", T=40, n_distinct=6), "route_forward T=40")
+    _announce("route_forward E=300 decode (separate routing launch)")
+    H, I, E, k, T = 256, 64, 300, 4, 3
+    base = [synth.random_expert_slot(rng, H, I) for _ in range(5)]
+    bank = np.stack([base[e % 5] for e in range(E + 1)])
+    L2 = synth.LayerInputs(H, I, E, k, T, bank, np.arange(E, dtype=np.int32), E,
+                           synth.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32) * 0.02),
+                           synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)),
+                           rng.standard_normal((T, E)).astype(np.float32))
+    _route_forward_vs_separate(L2, "route_forward E=300")
+
+
 def test_forward_no_shared_and_skipped_experts():
     _announce("forward without shared expert; slot map with skipped experts")
     L = synth.make_layer("tiny", T=6)
