@@ -30,15 +30,16 @@ BF16_PEAK_TFLOPS = 2500.0
 PCIE_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction
 
 
-# HBM bytes per forward call from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, summed over the call's
+# HBM bytes per call of the roofline unit from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, summed over the call's
 # kernels and scaled by what the same counters read for a plain copy of known size), with a digest of the kernel
 # sources they were taken on.  Reported as roofline.traffic only while those sources are unchanged.
 COUNTED_TRAFFIC = {
-    "decode_bs1": (29_278_069, "3ad5bb5983649fd6"),
-    "decode_bs16": (348_102_580, "3ad5bb5983649fd6"),
-    "prefill_2048": (1_890_454_916, "7ae170f188708718"),
+    "decode_bs1": (29_338_746, "7e17130ffd60a9c0"),
+    "decode_bs16": (318_901_035, "7e17130ffd60a9c0"),
+    "prefill_2048": (1_889_557_113, "25eda71ee2dd28ba"),
 }
-KERNEL_SOURCES = {"decode": ["decode.hip", "nvfp4_device.hpp"], "prefill": ["prefill.hip", "nvfp4_device.hpp"]}
+KERNEL_SOURCES = {"decode": ["decode.hip", "route_device.hpp", "nvfp4_device.hpp"],
+                  "prefill": ["prefill.hip", "nvfp4_device.hpp"]}
 
 
 def kernel_digest(kind: str) -> str:
