@@ -241,6 +241,56 @@ def test_route_forward_ties_skips_and_fallbacks():
     _route_forward_vs_separate(L2, "route_forward E=300")
 
 
+def _small_layer(rng, H, I, E, k, T, n_distinct=9):
+    distinct = [synth.random_expert_slot(rng, H, I) for _ in range(min(E + 1, n_distinct))]
+    bank = np.stack([distinct[(7 * e) % len(distinct)] for e in range(E + 1)])
+    return synth.LayerInputs(H, I, E, k, T, bank, np.arange(E, dtype=np.int32), E,
+                             synth.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32) * 0.02),
+                             synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)),
+                             rng.standard_normal((T, E)).astype(np.float32))
+
+
+def test_forward_limits():
+    """The decode path at its limits: 1024 experts with top-64 (T*k = 1024 assignments, the most it takes; 64-row
+    items), one token with top-64, and the smallest prefill batch (T = 17)."""
+    rng = np.random.default_rng(17)
+    for (H, I, E, k, T) in [(256, 64, 1024, 64, 16), (256, 64, 1024, 64, 1), (256, 64, 64, 8, 17)]:
+        _announce(f"forward limits H={H} I={I} E={E} k={k} T={T}")
+        L = _small_layer(rng, H, I, E, k, T)
+        y, _ = _gpu_forward(L)
+        assert_close(y.cpu().numpy(), _oracle_forward(L), f"limits E={E} k={k} T={T}")
+        _route_forward_vs_separate(L, f"route_forward limits E={E} k={k} T={T}")
+
+
+def test_route_forward_graph_replays():
+    """route_forward captured in a HIP graph: every replay (with eager work in between) equals the eager call."""
+    for name, T in [("decode_bs1", 1), ("decode_bs16", 16), ("prefill_2048", 96)]:
+        _announce(f"route_forward graph replays {name} T={T}")
+        L = synth.make_layer(name, T=T, n_distinct=6)
+        dev = device_layer(L)
+        x, lg = device_x(L), device_logits(L)
+        r = dl.Routing.empty(T, L.E, L.k)
+        nb = _lib.moe_nvfp4_route_forward_workspace_bytes(T, L.H, L.I, L.E, L.k)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        y = torch.empty((T, L.H), dtype=torch.float32, device="cuda")
+        y_eager, _ = dl.route_forward(dev, lg, x, y=y, out=r, ws=ws)
+        want = y_eager.clone()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                dl.route_forward(dev, lg, x, y=y, out=r, ws=ws)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            y.zero_()
+            dl.route_forward(dev, lg, x, y=torch.empty_like(y), out=dl.Routing.empty(T, L.E, L.k))  # eager work
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), want.cpu().numpy().view(np.uint32)), (name, rep)
+
+
 def test_forward_no_shared_and_skipped_experts():
     _announce("forward without shared expert; slot map with skipped experts")
     L = synth.make_layer("tiny", T=6)
