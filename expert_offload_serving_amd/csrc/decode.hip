@@ -363,9 +363,9 @@ __device__ __forceinline__ int stage_tables(const DecArgs& a, Tables& tb, XRegs<
     return __builtin_amdgcn_readfirstlane(tb.n_act);
 }
 
-// The same prologue for a kernel that routes itself (E <= 256): each wave
-// selects the top-k of its tokens straight from the logits (T <= 16, so one
-// or two tokens per wave), then every assignment is ranked directly,
+// The same prologue for a kernel that routes itself (E <= 256, T <= NW):
+// wave t selects the top-k of token t straight from the logits, then every
+// assignment is ranked directly,
 //   offsets[e] = #{b : e_b < e},  pos(a) = #{b : (e_b, b) < (e_a, a)},
 // the same stable grouping the routing kernels produce.  Workgroup 0 writes
 // the routing outputs.
@@ -395,8 +395,9 @@ __device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<N
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    for (int t = wave; t < T; t += NW)
-        topk_one_token<kRouteInKernelMaxE / kWave>(a.logits + (size_t)t * E, E, k, tb.ids + t * k, tb.w + t * k, lane);
+    if (wave < T)  // T <= NW (checked by the launcher): one token per wave
+        topk_one_token<kRouteInKernelMaxE / kWave>(a.logits + (size_t)wave * E, E, k, tb.ids + wave * k,
+                                                    tb.w + wave * k, lane);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int i = tid + NT * r;
@@ -513,12 +514,15 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
     Item it1 = decode_item(a, tb, n_act, nsl, u + G, u + G < n_items, c);
     ALoads<KQW> LA0, LA1;
     BLoads<NRGW> LB;
+    // the first item's loads, the activations to LDS, then the second item's loads (issuing loads is paced
+    // by the CU's address units, so loads the first item does not need would delay the staging)
     issue_a<KQW>(a, it0, wave, lane, tid, LA0);
     issue_b<NRGW>(a, it0, wave, lane, LB);
-    issue_a<KQW>(a, it1, wave, lane, tid, LA1);
     __builtin_amdgcn_sched_barrier(0);
     stage_x<kDW>(a, xv, sh.xsh, x16, XP, tid, lane, wave);
     __syncthreads();
+    issue_a<KQW>(a, it1, wave, lane, tid, LA1);
+    __builtin_amdgcn_sched_barrier(0);
 
     for (;;) {
         const Item it2 = decode_item(a, tb, n_act, nsl, u + 2 * G, u + 2 * G < n_items, c);

@@ -56,7 +56,8 @@ __device__ __forceinline__ uint32_t wave_umax_dpp(uint32_t v) {
 }
 
 // One wave selects the top-k of row `l` (E <= 64 * VPL logits; lane L holds
-// experts L + 64 i) and writes ids and weights (global or LDS pointers).
+// experts L + 64 i; every lane passes the same row) and writes ids and weights
+// (global or LDS pointers).
 // Each of the k rounds takes the wave maximum of the remaining keys, then the
 // lowest expert index holding it: the first slot i whose ballot of "equals
 // the maximum" is non-empty, at its lowest lane.  A selected key becomes 0.
@@ -67,12 +68,19 @@ template <int VPL>
 __device__ void topk_one_token(const float* __restrict__ l, int E, int k, int32_t* __restrict__ ids,
                                float* __restrict__ w, int lane) {
     static_assert(VPL <= kRouteVPL, "too many logits per lane");
+    // every logit load is issued before any is used, with no branch around them (buffer loads past the row
+    // return zeros, masked to "no candidate" below), so they wait for one another only once
+    // the row is the same for the whole wave; readfirstlane lets the compiler keep its resource scalar
+    const uint64_t lp = reinterpret_cast<uint64_t>(l);
+    const uint32_t lp_lo = __builtin_amdgcn_readfirstlane((uint32_t)lp);
+    const uint32_t lp_hi = __builtin_amdgcn_readfirstlane((uint32_t)(lp >> 32));
+    const rsrc_t lres = make_rsrc(reinterpret_cast<const float*>(((uint64_t)lp_hi << 32) | lp_lo), (uint32_t)E * 4);
+    uint32_t lv[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) lv[i] = buf_load4(lres, 4 * (lane + kWave * i));
     uint32_t v[VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int idx = lane + kWave * i;
-        v[i] = idx < E ? order_key(l[idx]) : 0u;
-    }
+    for (int i = 0; i < VPL; ++i) v[i] = order_key(__uint_as_float(lv[i])) & (lane + kWave * i < E ? ~0u : 0u);
     float held = 0.0f;  // selection j's logit, kept by lane j (j < 64)
     float m = 0.0f;
     for (int j = 0; j < k; ++j) {
