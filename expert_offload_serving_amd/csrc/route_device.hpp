@@ -59,8 +59,8 @@ __device__ __forceinline__ uint32_t wave_umax_dpp(uint32_t v) {
 // experts L + 64 i; every lane passes the same row) and writes ids and weights
 // (global or LDS pointers).
 // Each of the k rounds takes the wave maximum of the remaining keys, then the
-// lowest expert index holding it: the first slot i whose ballot of "equals
-// the maximum" is non-empty, at its lowest lane.  A selected key becomes 0.
+// lowest expert index holding it (a second wave maximum, over ~index of the
+// entries equal to the first).  A selected key becomes 0.
 // A NaN logit (a precondition violation) only changes which valid, distinct
 // experts come out.  Weights: softmax over the k selected logits in double
 // (exp(l_j - l_max) / sum), summed in selection order, rounded to f32.
@@ -88,14 +88,14 @@ __device__ void topk_one_token(const float* __restrict__ l, int E, int k, int32_
 #pragma unroll
         for (int i = 1; i < VPL; ++i) lm = v[i] > lm ? v[i] : lm;
         const uint32_t M = wave_umax_dpp(lm);
-        int bi = -1;
+        // lowest index holding M: each lane offers its lowest slot holding M as ~index, the wave takes the
+        // largest (all on the vector units: with many waves per CU the shared scalar unit would be the limit)
+        uint32_t cand = 0;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const uint64_t b = __ballot(v[i] == M);
-            if (bi < 0 && b != 0) bi = kWave * i + __ffsll((unsigned long long)b) - 1;
-        }
-        // M is a key some lane holds, so bi >= 0; the clamp only keeps the index in range
-        bi = __builtin_amdgcn_readfirstlane(bi < 0 ? 0 : bi);
+        for (int i = VPL - 1; i >= 0; --i) cand = v[i] == M ? ~(uint32_t)(lane + kWave * i) : cand;
+        const uint32_t best = wave_umax_dpp(cand);
+        // M is a key some lane holds, so best != 0; the clamp only keeps the index in range
+        const int bi = best != 0 ? (int)~best : 0;
         const int owner_slot = bi / kWave, owner_lane = bi % kWave;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) v[i] = (i == owner_slot && lane == owner_lane) ? 0u : v[i];
