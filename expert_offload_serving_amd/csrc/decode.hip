@@ -363,9 +363,9 @@ __device__ __forceinline__ int stage_tables(const DecArgs& a, Tables& tb, XRegs<
     return __builtin_amdgcn_readfirstlane(tb.n_act);
 }
 
-// The same prologue for a kernel that routes itself (E <= 256, T <= NW):
-// wave t selects the top-k of token t straight from the logits, then every
-// assignment is ranked directly,
+// The same prologue for a kernel that routes itself (E <= 256): wave w
+// selects the top-k of tokens w and w + NW straight from the logits, then
+// every assignment is ranked directly,
 //   offsets[e] = #{b : e_b < e},  pos(a) = #{b : (e_b, b) < (e_a, a)},
 // the same stable grouping the routing kernels produce.  Workgroup 0 writes
 // the routing outputs.
@@ -395,9 +395,13 @@ __device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<N
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (wave < T)  // T <= NW (checked by the launcher): one token per wave
-        topk_one_token<kRouteInKernelMaxE / kWave>(a.logits + (size_t)wave * E, E, k, tb.ids + wave * k,
-                                                    tb.w + wave * k, lane);
+#pragma unroll
+    for (int p = 0; p < (kDecodeMaxT + NW - 1) / NW; ++p) {  // wave w: tokens w, w + NW
+        const int t = wave + NW * p;
+        if (t < T)
+            topk_one_token<kRouteInKernelMaxE / kWave>(a.logits + (size_t)t * E, E, k, tb.ids + t * k, tb.w + t * k,
+                                                        lane);
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int i = tid + NT * r;
@@ -951,8 +955,11 @@ bool decode_shape_supported(int H, int I) { return H % 128 == 0 && I % kSl == 0 
 size_t decode_part_bytes(int T, int H, int I, int k) { return (size_t)(T * k + T) * (I / kSl) * H * 4; }
 size_t decode_rowslot_bytes(int T, int k) { return (size_t)(T * k + T) * 4; }
 
-// In-kernel routing pays off while every wave routes at most one token.
-bool decode_routes_in_kernel(int T, int E) { return E <= kRouteInKernelMaxE && T <= kDW && T <= kWW; }
+// In-kernel routing (the prologue handles up to two tokens per wave).
+#ifndef MOE_ROUTE_IN_KERNEL_MAX_T
+#define MOE_ROUTE_IN_KERNEL_MAX_T 8   // two tokens per wave (T = 12, 16) measured slower than a routing launch
+#endif
+bool decode_routes_in_kernel(int T, int E) { return E <= kRouteInKernelMaxE && T <= MOE_ROUTE_IN_KERNEL_MAX_T; }
 
 hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                          const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
