@@ -234,7 +234,7 @@ def parity_sample(inp, res, tokens):
 
 # ---------------------------------------------------------------- offload
 
-def bench_offload(steps: int, warmup: int, distinct: int):
+def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2):
     """48 MoE layers whose 256 experts live in pinned host memory behind one HBM cache of 37% of the
     12,288 expert-layer slots (global LRU, cold start).  Per layer-step: route on the GPU, one D2H copy of
     the ids, host LRU plan, misses copied on a side stream while the hits-only forward runs, then the
@@ -285,8 +285,10 @@ def bench_offload(steps: int, warmup: int, distinct: int):
     maps_h = torch.empty((2, E), dtype=torch.int32).pin_memory()
     maps_d = torch.empty((2, E), dtype=torch.int32, device=dev)
     comp = torch.cuda.current_stream()
-    copy = torch.cuda.Stream(device=dev)
-    done = torch.cuda.Event()
+    # misses are split over ncopy side streams (each stream can drive its own copy engine; 2 measured best)
+    copies = [torch.cuda.Stream(device=dev) for _ in range(ncopy)]
+    dones = [torch.cuda.Event() for _ in range(ncopy)]
+    copy = copies[0]
     ids_log = np.empty((total, L, T * k), dtype=np.int32)
     stats = {"hits": np.zeros((total, L), np.int64), "misses": np.zeros((total, L), np.int64)}
 
@@ -322,14 +324,20 @@ def bench_offload(steps: int, warmup: int, distinct: int):
         maps_h.numpy()[0] = hit_map
         maps_h.numpy()[1] = miss_map
         maps_d.copy_(maps_h, non_blocking=True)
-        if miss_e:
-            _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, list(miss_s),
-                                              [host_ptr[base_of(l, e_)] for e_ in miss_e], copy, done))
+        used = []
+        for c_ in range(ncopy):
+            part = list(range(c_, len(miss_e), ncopy))
+            if part:
+                _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, [miss_s[i] for i in part],
+                                                  [host_ptr[base_of(l, miss_e[i])] for i in part], copies[c_],
+                                                  dones[c_]))
+                used.append(c_)
         _lib.check(_lib.moe_nvfp4_forward(layer_struct(l, maps_d[0], True), x, T, route.ids, route.w,
                                           route.offsets, route.sorted_assign, route.assign_pos, y, 0, ws,
                                           ws.numel(), None))
         if miss_e:
-            comp.wait_event(done)
+            for c_ in used:
+                comp.wait_event(dones[c_])
             _lib.check(_lib.moe_nvfp4_forward(layer_struct(l, maps_d[1], False), x, T, route.ids, route.w,
                                               route.offsets, route.sorted_assign, route.assign_pos, y, 1, ws,
                                               ws.numel(), None))
@@ -352,15 +360,15 @@ def bench_offload(steps: int, warmup: int, distinct: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # pinned host -> HBM copy rate alone (64 slots, one stream)
+    # pinned host -> HBM copy rate alone (64 slots over the same copy streams, host clock)
     n_probe = 64
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(copy)
-    _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, list(range(n_probe)),
-                                      [host_ptr[j % E] for j in range(n_probe)], copy, None))
-    ev1.record(copy)
     torch.cuda.synchronize()
-    h2d_gbs = n_probe * sb / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    tp = time.perf_counter()
+    for c_ in range(ncopy):
+        part = list(range(c_, n_probe, ncopy))
+        _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, part, [host_ptr[j % E] for j in part], copies[c_], None))
+    torch.cuda.synchronize()
+    h2d_gbs = n_probe * sb / (time.perf_counter() - tp) / 1e9
 
     # checks: the host LRU against the oracle's model on the same ids; the last layer-step against the oracle
     h_ref, m_ref, _, _ = oracle.lru_run(ids_log, E, n_slots, want_maps=False)
@@ -390,7 +398,7 @@ def bench_offload(steps: int, warmup: int, distinct: int):
                    "distinct_quantized_experts": min(distinct, E), "parallelism": "single GPU"},
         "roofline": {"bound": "pcie", "achieved": round(pcie, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                      "frac": round(pcie / PCIE_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "expert_cache_fill (hipMemcpyAsync of missed slots on a side stream)",
+                     "kernel": f"expert_cache_fill (hipMemcpyAsync of missed slots on {ncopy} side streams)",
                      "per_launch": f"{misses / max(1, steps * L):.2f} missed slots x {sb} B per layer-step"},
         "offload": {"hit_rate_steady": round(hits / max(1, hits + misses), 4),
                     "hit_rate_warmup": round(stats["hits"][:warmup].sum() /
@@ -489,6 +497,7 @@ def main():
     ap.add_argument("--distinct", type=int, default=32, help="distinct quantized experts tiled over the slots")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=320)
+    ap.add_argument("--copy-streams", type=int, default=2, help="offload: side streams the misses are copied on")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (for calibrating HBM byte counters) and exit")
     args = ap.parse_args()
@@ -510,7 +519,7 @@ def main():
     for name in names:
         if name == "offload":
             steps, warmup = (64, 16) if args.steps == 200 and args.warmup == 10 else (args.steps, args.warmup)
-            print(json.dumps(bench_offload(steps, warmup, args.distinct)), flush=True)
+            print(json.dumps(bench_offload(steps, warmup, args.distinct, args.copy_streams)), flush=True)
             continue
         steps, warmup = args.steps, args.warmup
         if name == "prefill_2048":
