@@ -241,7 +241,7 @@ __device__ __forceinline__ void run_item(const DecArgs& a, DecShared& sh, const 
             const float gsum = e < 4 ? gs0[e] : gs1[e - 4], usum = e < 4 ? us0[e] : us1[e - 4];
             const float gv = gsum * __shfl(glob, 8 * g + e, kWave);
             const float uv = usum * __shfl(glob, 32 + 8 * g + e, kWave);
-            h[e] = gv / (1.0f + expf(-gv)) * uv;
+            h[e] = silu_fast(gv) * uv;
             hm = fmaxf(hm, fabsf(h[e]));
         }
         hm = fmaxf(hm, __shfl_xor(hm, 16, kWave));
@@ -758,7 +758,7 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
                 for (int r = 0; r < 4; ++r) {
                     const float gv = acc[tt][r] * xinv * gl[tt][r];
                     const float uv = acc[W::NTT + tt][r] * xinv * gl[W::NTT + tt][r];
-                    h[tt][r] = gv / (1.0f + expf(-gv)) * uv;
+                    h[tt][r] = silu_fast(gv) * uv;
                     hm = fmaxf(hm, fabsf(h[tt][r]));
                 }
             hm = fmaxf(hm, __shfl_xor(hm, 16, kWave));

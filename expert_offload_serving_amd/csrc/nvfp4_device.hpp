@@ -156,4 +156,11 @@ __device__ __forceinline__ void keep_packed(uint32_t& v) { asm volatile("" : "+v
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// silu(g) = g / (1 + e^-g) with the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32: about 1 ulp each, far inside the layer's tolerance).
+// Large |g| saturates correctly: e^-g -> inf gives -0, e^-g -> 0 gives g.
+__device__ __forceinline__ float silu_fast(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+}
+
 }  // namespace moe

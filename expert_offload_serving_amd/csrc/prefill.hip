@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(PrefillArgs a, int cls, int n
                     const float inv = a.xinv[tok[m]];
                     const float gate = acc[i][cb][r] * inv * gg;
                     const float up = acc[i][NBW / 2 + cb][r] * inv * gu;
-                    float h = gate * sigmoidf_(gate) * up;
+                    float h = silu_fast(gate) * up;
                     h = fminf(fmaxf(h, -65504.0f), 65504.0f);
                     a.hbuf[(size_t)(gb + m0 + m) * I + hc] = (_Float16)h;
                 }
@@ -594,7 +594,7 @@ __global__ void __launch_bounds__(32 * kWave / NB) big_gemm_kernel(PrefillArgs a
                     const float inv = a.xinv[tok[m]];
                     const float gate = acc[i][cb][r] * inv * gg;
                     const float up = acc[i][NB / 2 + cb][r] * inv * gu;
-                    float h = gate * sigmoidf_(gate) * up;
+                    float h = silu_fast(gate) * up;
                     h = fminf(fmaxf(h, -65504.0f), 65504.0f);
                     a.hbuf[(size_t)(gb + m0 + m) * I + hc] = (_Float16)h;
                 }
