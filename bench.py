@@ -34,9 +34,9 @@ PCIE_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction
 # kernels and scaled by what the same counters read for a plain copy of known size), with a digest of the kernel
 # sources they were taken on.  Reported as roofline.traffic only while those sources are unchanged.
 COUNTED_TRAFFIC = {
-    "decode_bs1": (29_338_746, "7e17130ffd60a9c0"),
-    "decode_bs16": (318_901_035, "7e17130ffd60a9c0"),
-    "prefill_2048": (1_889_557_113, "25eda71ee2dd28ba"),
+    "decode_bs1": (29_320_187, "391798333bd40a9a"),
+    "decode_bs16": (318_866_993, "391798333bd40a9a"),
+    "prefill_2048": (1_889_232_033, "54a2ca4b423b0895"),
 }
 KERNEL_SOURCES = {"decode": ["decode.hip", "route_device.hpp", "nvfp4_device.hpp"],
                   "prefill": ["prefill.hip", "nvfp4_device.hpp"]}
