@@ -49,6 +49,8 @@ struct DecArgs {
     const int32_t* sorted_assign;
     float* part;   // [(T*k + T) * nsl, H]: row (assignment or T*k + token) * nsl + slice, times the row's weight
     int32_t* rowslot;  // [(T*k + T)]: slot of each row's expert (-1 left out, -2 shared)
+    float* dgrow;      // [(T*k + T), H]: the rows' down-row globals, when spare workgroups copy them (else null)
+    int n_spare;       // spare workgroups at the end of the grid
     float* y;
     int accumulate;
     int gu_codes, gu_scales, gu_glob, dn_codes, dn_scales, dn_glob;  // region offsets in a slot
@@ -488,6 +490,54 @@ __device__ __forceinline__ void stage_x(const DecArgs& a, const XRegs<NW>& xr, i
     if (tid == 0) xsh[T] = 0;
 }
 
+// Spare workgroups (launched past the items when CUs are free) copy the
+// down-row globals of every output row into dgrow, so the combine reads them
+// at its start instead of first reading the row's slot.  Row p in sorted
+// order: p < T*k is assignment sorted[p] of the last active expert whose
+// group starts at or before p; p >= T*k is shared row p.  Each spare
+// workgroup takes rows j, j + n_spare, ... in batches of 8, every load of a
+// batch issued before its stores.
+constexpr int kDgBatch = 8;
+__device__ void copy_down_globals(const DecArgs& a, const Tables& tb, int n_act, int j, int n_spare, int tid) {
+    const int T = a.T, k = a.k, n = T * k, rows = n + T, H4 = a.H / 4;
+    const rsrc_t dres = make_rsrc(a.dgrow, (uint32_t)((size_t)rows * a.H * 4));
+    for (int p0 = j; p0 < rows; p0 += kDgBatch * n_spare) {
+        f32x4_t v[kDgBatch][2];
+        int row[kDgBatch];
+#pragma unroll
+        for (int b = 0; b < kDgBatch; ++b) {
+            const int p = p0 + b * n_spare;
+            rsrc_t res = make_rsrc(a.bank, 0u);
+            row[b] = -1;
+            if (p < n) {
+                int lo = 0, hi = n_act - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) / 2;
+                    if (tb.off[tb.act[mid]] <= p) lo = mid; else hi = mid - 1;
+                }
+                const int sl = tb.slot[tb.act[lo]];
+                row[b] = tb.sorted[p];
+                if (sl >= 0) res = make_rsrc(a.bank + (size_t)sl * a.slot_bytes, (uint32_t)a.slot_bytes);
+            } else if (p < rows) {
+                row[b] = p;
+                if (a.shared != nullptr) res = make_rsrc(a.shared, (uint32_t)a.slot_bytes);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int c4 = tid + kDT * i;
+                v[b][i] = __builtin_bit_cast(f32x4_t, buf_load16(res, c4 < H4 ? a.dn_glob + 16 * c4 : kOob));
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kDgBatch; ++b)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int c4 = tid + kDT * i;
+                buf_store16(dres, row[b] >= 0 && c4 < H4 ? 16 * (row[b] * H4 + c4) : kOob, v[b][i]);
+            }
+    }
+}
+
 // Persistent over work items u = blockIdx.x + j * gridDim.x; item u is
 // (expert act[u / nsl], or the shared expert, slice u % nsl).  Every token's
 // activations are staged in LDS once, as fp16 times a per-token power of two.
@@ -509,7 +559,11 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
     const int n_act = ROUTE ? stage_route<kDW>(a, tb, xv, tid, lane, wave) : stage_tables<kDW>(a, tb, xv, tid, lane, wave);
     const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
     int u = blockIdx.x;
-    if (u >= n_items) return;  // uniform
+    if (u >= n_items) {  // uniform: a workgroup without items; spare ones copy the down-row globals
+        if (a.dgrow != nullptr && u >= (int)gridDim.x - a.n_spare)
+            copy_down_globals(a, tb, n_act, u - ((int)gridDim.x - a.n_spare), a.n_spare, tid);
+        return;
+    }
 
     // ---- the first items' weights start streaming, then the activations go to LDS
     const int G = (int)gridDim.x, c = lane & 15;
@@ -841,6 +895,7 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
     const bool has_shared = a.shared != nullptr;
     const int nrows = k + (has_shared ? 1 : 0);
     const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
+    const rsrc_t dgres = make_rsrc(a.dgrow, (uint32_t)((size_t)(T * k + T) * H * 4));
     f32x4_t sr = {0.0f, 0.0f, 0.0f, 0.0f}, ss = {0.0f, 0.0f, 0.0f, 0.0f};
     float gd = 0.0f;
     for (int j = q; j < nrows; j += 16) {
@@ -849,10 +904,15 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
 #pragma unroll
         for (int i = 0; i < kCS; ++i)
             v[i] = __builtin_bit_cast(f32x4_t, buf_load16(pres, i < nsl ? 4 * ((row * nsl + i) * H + col) : kOob));
-        const int rs = a.rowslot[row];
-        const uint8_t* slot = rs >= 0 ? a.bank + (size_t)rs * a.slot_bytes : (rs == -2 ? a.shared : a.bank);
-        const rsrc_t gsr = make_rsrc(slot, rs == -1 ? 0u : (uint32_t)a.slot_bytes);
-        const f32x4_t dg = __builtin_bit_cast(f32x4_t, buf_load16(gsr, a.dn_glob + 4 * col));
+        f32x4_t dg;
+        if (a.dgrow != nullptr) {  // uniform: the rows' globals were copied by the item kernel
+            dg = __builtin_bit_cast(f32x4_t, buf_load16(dgres, 4 * (row * H + col)));
+        } else {
+            const int rs = a.rowslot[row];
+            const uint8_t* slot = rs >= 0 ? a.bank + (size_t)rs * a.slot_bytes : (rs == -2 ? a.shared : a.bank);
+            const rsrc_t gsr = make_rsrc(slot, rs == -1 ? 0u : (uint32_t)a.slot_bytes);
+            dg = __builtin_bit_cast(f32x4_t, buf_load16(gsr, a.dn_glob + 4 * col));
+        }
         __builtin_amdgcn_sched_barrier(0);
         f32x4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -902,7 +962,7 @@ hipError_t init_device_info() {
 }
 
 template <int KQW, int NRGW, bool ROUTE>
-hipError_t launch_fused(const DecArgs& a, int items_max, int nsl, hipStream_t s) {
+hipError_t launch_fused(DecArgs& a, int items_max, int nsl, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW, ROUTE>),
@@ -910,8 +970,18 @@ hipError_t launch_fused(const DecArgs& a, int items_max, int nsl, hipStream_t s)
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    // a kernel that routes itself has every workgroup route; workgroup 0 must exist to write the routing
-    const int grid = items_max < g_num_cu ? items_max : g_num_cu;
+    // a kernel that routes itself has every workgroup route; workgroup 0 must exist to write the routing.
+    // CUs the items leave free get spare workgroups that copy the down-row globals for the combine.
+    // (a.dgrow stays set only when they run, which tells the combine where to read the globals)
+    int grid = items_max < g_num_cu ? items_max : g_num_cu;
+    a.n_spare = 0;
+    if (grid < g_num_cu && a.dgrow != nullptr) {
+        const int rows = a.T * a.k + a.T;
+        a.n_spare = min(g_num_cu - grid, (rows + kDgBatch - 1) / kDgBatch);
+        grid += a.n_spare;
+    } else {
+        a.dgrow = nullptr;
+    }
     const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
     hipLaunchKernelGGL((fused_kernel<KQW, NRGW, ROUTE>), dim3(grid), dim3(kDT), lds, s, a, nsl);
     return hipGetLastError();
@@ -933,11 +1003,12 @@ hipError_t launch_wave(const DecArgs& a, int items_max, int nsl, hipStream_t s) 
 }
 
 template <bool ROUTE>
-hipError_t launch_main(const DecArgs& a, int I, int T, int k, int E, int& nsl, hipStream_t s) {
+hipError_t launch_main(DecArgs& a, int I, int T, int k, int E, int& nsl, hipStream_t s) {
     // 32-row items; when they would outnumber the waves of one pass, 64-row items (half the partials)
     nsl = I / kSl;
     const int rows_max = (T * k < E ? T * k : E) + 1;
     if (rows_max * nsl < MOE_WAVE_MIN_ITEMS) return launch_fused<5, 5, ROUTE>(a, rows_max * nsl, nsl, s);
+    a.dgrow = nullptr;  // the wave-item kernel leaves the combine to read the globals through the row slots
     if (rows_max * nsl > g_num_cu * kWW && I % 64 == 0) {
         nsl = I / 64;
         return launch_wave<64, ROUTE>(a, rows_max * nsl, nsl, s);
@@ -954,6 +1025,7 @@ bool decode_shape_supported(int H, int I) { return H % 128 == 0 && I % kSl == 0 
 
 size_t decode_part_bytes(int T, int H, int I, int k) { return (size_t)(T * k + T) * (I / kSl) * H * 4; }
 size_t decode_rowslot_bytes(int T, int k) { return (size_t)(T * k + T) * 4; }
+size_t decode_dgrow_bytes(int T, int H, int k) { return (size_t)(T * k + T) * H * 4; }
 
 // In-kernel routing (the prologue handles up to two tokens per wave).
 #ifndef MOE_ROUTE_IN_KERNEL_MAX_T
@@ -975,6 +1047,8 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
     a.w = w; a.offsets = offsets; a.sorted_assign = sorted_assign;
     a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + wl.part);
     a.rowslot = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + wl.dg);
+    a.dgrow = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + wl.dgrow);
+    a.n_spare = 0;
     a.y = y; a.accumulate = accumulate;
     const SlotGeom gm = slot_geom(H, I);
     a.gu_codes = (int)gm.gu_codes; a.gu_scales = (int)gm.gu_scales; a.gu_glob = (int)gm.gu_glob;

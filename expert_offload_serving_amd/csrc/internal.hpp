@@ -37,20 +37,22 @@ constexpr int kDecodeMaxAssign = 1024;  // T*k
 bool decode_shape_supported(int H, int I);
 size_t decode_part_bytes(int T, int H, int I, int k);
 size_t decode_rowslot_bytes(int T, int k);
+size_t decode_dgrow_bytes(int T, int H, int k);
 inline bool decode_path(int T, int H, int I, int k) {
     return T <= kDecodeMaxT && T * k <= kDecodeMaxAssign && decode_shape_supported(H, I);
 }
 
 // Forward workspace: byte offsets of its regions (each 256-byte aligned).
-// The decode path uses `part` (per-(row, slice) partial outputs) and `dg`
-// (per-row slot of the row's expert); the prefill path uses the others:
+// The decode path uses `part` (per-(row, slice) partial outputs), `dg`
+// (per-row slot of the row's expert) and `dgrow` (per-row copies of the
+// expert's down-row globals); the prefill path uses the others:
 //   h      hidden state, (T*k + T) rows of I fp16 values
 //   o      per-assignment expert outputs, (T*k + T) rows of H f32
 //   s      shared-gate sigmoid per token, T f32
 //   x16    scaled fp16 activations [T, H]; xinv: their inverse scales [T]
 //   tiles  work lists: 4 counts, then 3 classes x tile_cap (group, m0) pairs
 struct WsLayout {
-    size_t part, dg, h, o, s, x16, xinv, tiles, total;
+    size_t part, dg, dgrow, h, o, s, x16, xinv, tiles, total;
     int tile_cap;
 };
 inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -59,7 +61,8 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
     if (decode_path(T, H, I, k)) {
         L.part = 0;
         L.dg = align256(decode_part_bytes(T, H, I, k));
-        L.total = L.dg + align256(decode_rowslot_bytes(T, k));
+        L.dgrow = L.dg + align256(decode_rowslot_bytes(T, k));
+        L.total = L.dgrow + align256(decode_dgrow_bytes(T, H, k));
         return L;
     }
     const size_t rows = (size_t)T * k + T;
