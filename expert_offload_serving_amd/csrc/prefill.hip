@@ -406,24 +406,25 @@ __global__ void __launch_bounds__(256) gemm_kernel(PrefillArgs a, int cls, int n
 }
 
 // ------------------------------------------------------------------ big-tile GEMM (128-row tiles)
-// One workgroup computes a 128-token x 256-weight-row tile: gate_up: 128
-// h-columns (their 128 gate rows and 128 up rows); down: 256 output rows.
-// Wave (wm, wn) owns tokens [64 wm, 64 wm + 64) and 16 NB weight rows
-// (NB 16-row blocks: gate_up: NB/2 gate tiles and the matching up tiles;
-// down: NB/4 record groups), so each dequantised weight fragment feeds 4
-// MFMAs.  NB = 4 (8 waves, two per SIMD) measured faster than NB = 8 (4
-// waves with 512 registers each), whose single wave per SIMD could not hide
-// its dequantisation behind the matrix cores.  Per
+// One workgroup (8 waves, two per SIMD) computes a 128-token x 256-weight-row
+// tile: gate_up: 128 h-columns (their 128 gate rows and 128 up rows); down:
+// 256 output rows.  Wave (wm, wn) owns tokens [128/WM wm, +128/WM) and NB
+// 16-row weight blocks (gate_up: NB/2 gate tiles and the matching up tiles;
+// down: NB/4 record groups), so each dequantised weight fragment feeds
+// 8/WM MFMAs.  Four waves with 512 registers each (twice the weight rows per
+// wave) measured slower: a single wave per SIMD could not hide its
+// dequantisation behind the matrix cores.  Per
 // 128-column step the activation tile (128 x 128 fp16) sits in LDS, written
 // from registers one step ahead; each wave's weight records are loaded two
 // steps ahead into a register ping-pong.  Load order per step end:
 // activations of step s + 2, then weights of step s + 2, so waiting for
 // either never waits for the other's newer loads.
-template <bool GATEUP, int NB>
-__global__ void __launch_bounds__(32 * kWave / NB) big_gemm_kernel(PrefillArgs a, int n_tiles_n) {
+template <bool GATEUP, int WM, int NB>
+__global__ void __launch_bounds__(8 * kWave) big_gemm_kernel(PrefillArgs a, int n_tiles_n) {
     constexpr int BM = 128;
-    constexpr int NWN = 16 / NB;            // waves along the weight rows (2 along the tokens)
-    constexpr int NT = 2 * NWN * kWave;      // threads
+    constexpr int NWN = 8 / WM;              // waves along the weight rows (WM along the tokens)
+    constexpr int MI = BM / 16 / WM;         // 16-row token blocks per wave
+    constexpr int NT = 8 * kWave;            // threads
     constexpr int AQ = BM * 16 / NT;         // activation chunks per thread per step
     __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * APITCH];
     __shared__ int tok[BM];
@@ -481,8 +482,8 @@ __global__ void __launch_bounds__(32 * kWave / NB) big_gemm_kernel(PrefillArgs a
     const rsrc_t sres = make_rsrc(slot, (uint32_t)a.slot_bytes);
     const int soff = lane_scale_off(lane);
     const int codes = (int)(GATEUP ? a.gu_codes : a.dn_codes), scales = (int)(GATEUP ? a.gu_scales : a.dn_scales);
-    const int hc0 = 128 * nt + 8 * NB * wn;         // gate_up: first h-column of the wave (NB / 2 tiles)
-    const int grp0 = 4 * nt + (NB / 4) * wn;        // down: first record group of the wave (NB / 4 groups)
+    const int hc0 = 8 * NB * (NWN * nt + wn);      // gate_up: first h-column of the wave (NB / 2 tiles)
+    const int grp0 = (NB / 4) * (NWN * nt + wn);   // down: first record group of the wave (NB / 4 groups)
     struct BRegs {
         u32x4_t c[NB];
         uint32_t s[NB];
@@ -508,19 +509,19 @@ __global__ void __launch_bounds__(32 * kWave / NB) big_gemm_kernel(PrefillArgs a
         }
     };
 
-    f32x4_t acc[4][NB];
+    f32x4_t acc[MI][NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[i][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     auto compute = [&](int buf, const BRegs& r) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            f16x8_t fa[4];
+            f16x8_t fa[MI];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                fa[i] = lds_frag(&sA[buf][(64 * wm + 16 * i + l16) * APITCH + 32 * m + 8 * q4]);
+            for (int i = 0; i < MI; ++i)
+                fa[i] = lds_frag(&sA[buf][(16 * MI * wm + 16 * i + l16) * APITCH + 32 * m + 8 * q4]);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 // gate_up: record b holds chunk m in dword m; down: record 4 gi + m holds tile j in dword j
@@ -534,7 +535,7 @@ __global__ void __launch_bounds__(32 * kWave / NB) big_gemm_kernel(PrefillArgs a
                 else S = scale_f16x2<3>(r.s[ri]);
                 const f16x8_t fb = frag_f16(cw, S);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[i][b], 0, 0, 0);
+                for (int i = 0; i < MI; ++i) acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[i][b], 0, 0, 0);
             }
         }
     };
@@ -586,10 +587,10 @@ __global__ void __launch_bounds__(32 * kWave / NB) big_gemm_kernel(PrefillArgs a
             if (hc >= I) continue;
             const float gg = gl[hc], gu = gl[I + hc];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int m = 64 * wm + 16 * i + 4 * q4 + r;
+                    const int m = 16 * MI * wm + 16 * i + 4 * q4 + r;
                     if (m >= cnt) continue;
                     const float inv = a.xinv[tok[m]];
                     const float gate = acc[i][cb][r] * inv * gg;
@@ -607,17 +608,23 @@ __global__ void __launch_bounds__(32 * kWave / NB) big_gemm_kernel(PrefillArgs a
             if (oc >= H) continue;
             const float gd = gl[oc];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int m = 64 * wm + 16 * i + 4 * q4 + r;
+                    const int m = 16 * MI * wm + 16 * i + 4 * q4 + r;
                     if (m < cnt) a.obuf[(size_t)(gb + m0 + m) * H + oc] = acc[i][b][r] * gd;
                 }
         }
     }
 }
 
-constexpr int kBigNB = 4;
+// gate_up: one wave per 128 tokens (each dequantised weight fragment feeds 8
+// MFMAs, no weight record loaded twice) measured faster than two; down keeps
+// two waves along the tokens and whole 64-row record groups per wave.
+constexpr int kBigGuWM = 1, kBigGuNB = 2;   // gate_up: waves along the tokens, 16-row weight blocks per wave
+constexpr int kBigDnWM = 2, kBigDnNB = 4;   // down
+constexpr int kBigGuCols = (8 / kBigGuWM) * 8 * kBigGuNB;    // h-columns per gate_up tile
+constexpr int kBigDnRows = (8 / kBigDnWM) * 16 * kBigDnNB;   // output rows per down tile
 
 // ------------------------------------------------------------------ combine
 // One thread per 4 output columns of token t; the k expert rows are read in
@@ -740,11 +747,11 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     if ((e = launch_gemm<64, false>(a, 1, maxsmall, ceil_div(H, 128), f.side)) != hipSuccess) return e;
     if ((e = launch_gemm<32, false>(a, 2, maxsmall, ceil_div(H, 256), f.side)) != hipSuccess) return e;
     if ((e = hipEventRecord(f.joined, f.side)) != hipSuccess) return e;
-    hipLaunchKernelGGL((big_gemm_kernel<true, kBigNB>), dim3(max128 * ceil_div(I, 128)), dim3(32 * kWave / kBigNB), 0,
-                       s, a, ceil_div(I, 128));
+    hipLaunchKernelGGL((big_gemm_kernel<true, kBigGuWM, kBigGuNB>), dim3(max128 * ceil_div(I, kBigGuCols)),
+                       dim3(8 * kWave), 0, s, a, ceil_div(I, kBigGuCols));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((big_gemm_kernel<false, kBigNB>), dim3(max128 * ceil_div(H, 256)), dim3(32 * kWave / kBigNB), 0,
-                       s, a, ceil_div(H, 256));
+    hipLaunchKernelGGL((big_gemm_kernel<false, kBigDnWM, kBigDnNB>), dim3(max128 * ceil_div(H, kBigDnRows)),
+                       dim3(8 * kWave), 0, s, a, ceil_div(H, kBigDnRows));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s, f.joined, 0)) != hipSuccess) return e;
     const int nchunk = ceil_div(H / 4, 256);
