@@ -201,227 +201,23 @@ __device__ __forceinline__ f16x8_t lds_frag(const _Float16* p) {
     return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(p));
 }
 
-// One workgroup = one (tile, 64 h-columns) for gate_up or (tile, 64*WNW output
-// rows) for down.  4 waves as WMW (rows) x WNW (columns); each wave owns
-// MB = BM/WMW/16 row blocks and NBW column blocks of 16 (for down, the four
-// tiles of one 64-row record group).
-template <int BM, bool GATEUP>
-__global__ void __launch_bounds__(256) gemm_kernel(PrefillArgs a, int cls, int n_tiles_n) {
-    constexpr int WMW = BM == 32 ? 1 : 2;
-    constexpr int WNW = 4 / WMW;
-    constexpr int MB = BM / WMW / 16;
-    constexpr int NCOLS = GATEUP ? 64 : 64 * WNW;  // h columns (gate_up) or output rows (down) per tile
-    constexpr int CW = NCOLS / WNW;                 // columns per wave
-    constexpr int NBW = GATEUP ? 2 * (CW / 16) : CW / 16;  // column blocks per wave (gate and up for gate_up)
-    __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * APITCH];
-    __shared__ int tok[BM];
-
-    const int tile = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
-    if (tile >= a.tiles[cls]) return;
-    const int* te = a.tiles + 4 + 2 * (cls * a.cap + tile);
-    const int g = te[0], m0 = te[1];
-    const int gb = group_begin(a, g), cnt = min(BM, group_end(a, g) - gb - m0);
-    const uint8_t* slot = group_slot(a, g);
-    const int H = a.H, I = a.I, T = a.T, k = a.k;
-    const int K = GATEUP ? H : I;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int wm = wave / WNW, wn = wave % WNW;
-    const int l16 = lane % 16, q4 = lane / 16;
-
-    if (GATEUP) {
-        for (int m = tid; m < BM; m += 256) {
-            int t = -1;
-            if (m < cnt) {
-                const int p = gb + m0 + m;
-                t = g < a.E ? a.sorted_assign[p] / k : p - T * k;
-            }
-            tok[m] = t;
-        }
-        __syncthreads();
-    }
-
-    // B records of this wave.  gate_up: block b is one 16-row tile (b < NBW/2
-    // gate, then up), one record per step.  down: the wave's 64 output rows are
-    // record group p, four records (one per 32-column chunk) per step.
-    const int soff = lane_scale_off(lane);
-    const uint8_t* codes = slot + (GATEUP ? a.gu_codes : a.dn_codes);
-    const uint8_t* scales = slot + (GATEUP ? a.gu_scales : a.dn_scales);
-    int btile[NBW];
-    bool bok[NBW];
-    bool gok = true;
-    int grp = 0;
-    if (GATEUP) {
-#pragma unroll
-        for (int b = 0; b < NBW; ++b) {
-            const int half = b / (NBW / 2), cb = b % (NBW / 2);   // half 0 = gate, 1 = up
-            const int hc0 = nt * 64 + wn * CW + cb * 16;
-            bok[b] = hc0 < I;
-            btile[b] = half * (I / 16) + (hc0 < I ? hc0 / 16 : 0);
-        }
-    } else {
-        grp = (nt * NCOLS + wn * CW) / 64;
-        gok = 64 * grp < H;
-    }
-    // A tile loader: 16 threads per row, 16 bytes (8 fp16) each
-    constexpr int ROWS_PER_PASS = 256 / 16;
-    constexpr int APASSES = (BM + ROWS_PER_PASS - 1) / ROWS_PER_PASS;
-    const int arow0 = tid / 16, apiece = tid % 16;
-    u32x4_t areg[APASSES];
-    auto load_a = [&](int k0) {
-#pragma unroll
-        for (int ps = 0; ps < APASSES; ++ps) {
-            const int m = arow0 + ps * ROWS_PER_PASS;
-            const int kk = k0 + apiece * 8;
-            u32x4_t v = u32x4_t{0, 0, 0, 0};
-            if (m < BM && m < cnt && kk < K) {
-                const _Float16* src;
-                if (GATEUP) src = a.x16 + (size_t)tok[m] * H + kk;
-                else src = a.hbuf + (size_t)(gb + m0 + m) * I + kk;
-                v = *reinterpret_cast<const u32x4_t*>(src);
-            }
-            areg[ps] = v;
-        }
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int ps = 0; ps < APASSES; ++ps) {
-            const int m = arow0 + ps * ROWS_PER_PASS;
-            if (m < BM) *reinterpret_cast<u32x4_t*>(&sA[buf][m * APITCH + apiece * 8]) = areg[ps];
-        }
-    };
-    u32x4_t bcw[4];
-    uint32_t bsc[4];
-    auto load_b = [&](int k0) {
-        const int step = k0 / BK;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            bcw[r] = u32x4_t{0, 0, 0, 0};
-            bsc[r] = 0;
-            size_t rec = 0;
-            bool ok;
-            if (GATEUP) {
-                ok = r < NBW && bok[r];
-                rec = (size_t)step * (2 * I / 16) + btile[r < NBW ? r : 0];
-            } else {
-                const int kc = 4 * step + r;
-                ok = gok && kc < I / 32;
-                rec = (size_t)kc * (H / 64) + grp;
-            }
-            if (ok) {
-                bcw[r] = *reinterpret_cast<const u32x4_t*>(codes + rec * kRecBytes + 16 * lane);
-                bsc[r] = *reinterpret_cast<const uint32_t*>(scales + rec * kRecScaleBytes + soff);
-            }
-        }
-    };
-    // fragment (block b, chunk m) of the current step
-    auto frag = [&](int b, int m) -> f16x8_t {
-        const int r = GATEUP ? b : m, d = GATEUP ? m : b;
-        f16x2_t S;
-        if (d == 0) S = scale_f16x2<0>(bsc[r]);
-        else if (d == 1) S = scale_f16x2<1>(bsc[r]);
-        else if (d == 2) S = scale_f16x2<2>(bsc[r]);
-        else S = scale_f16x2<3>(bsc[r]);
-        return frag_f16(word_of(bcw[r], d), S);
-    };
-
-    f32x4_t acc[MB][NBW];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int b = 0; b < NBW; ++b) acc[i][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int nsteps = (K + BK - 1) / BK;
-    load_a(0);
-    load_b(0);
-    store_a(0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        // dequantise this step's B fragments, then prefetch the next step
-        f16x8_t bw[NBW][4];
-#pragma unroll
-        for (int b = 0; b < NBW; ++b)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) bw[b][m] = frag(b, m);
-        if (s + 1 < nsteps) {
-            load_a((s + 1) * BK);
-            load_b((s + 1) * BK);
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f16x8_t fa[MB];
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-                fa[i] = lds_frag(&sA[buf][(wm * MB * 16 + i * 16 + l16) * APITCH + 32 * m + 8 * q4]);
-#pragma unroll
-            for (int b = 0; b < NBW; ++b)
-#pragma unroll
-                for (int i = 0; i < MB; ++i)
-                    acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], bw[b][m], acc[i][b], 0, 0, 0);
-        }
-        if (s + 1 < nsteps) {
-            store_a(buf ^ 1);
-            __syncthreads();
-        }
-    }
-
-    // epilogue: lane holds rows 4*q4 + r (r < 4) of column l16 of each 16x16 block
-    if (GATEUP) {
-        const float* gl = reinterpret_cast<const float*>(slot + a.gu_glob);
-#pragma unroll
-        for (int cb = 0; cb < NBW / 2; ++cb) {
-            const int hc = nt * 64 + wn * CW + cb * 16 + l16;
-            if (hc >= I) continue;
-            const float gg = gl[hc], gu = gl[I + hc];
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = wm * MB * 16 + i * 16 + 4 * q4 + r;
-                    if (m >= cnt) continue;
-                    const float inv = a.xinv[tok[m]];
-                    const float gate = acc[i][cb][r] * inv * gg;
-                    const float up = acc[i][NBW / 2 + cb][r] * inv * gu;
-                    float h = silu_fast(gate) * up;
-                    h = fminf(fmaxf(h, -65504.0f), 65504.0f);
-                    a.hbuf[(size_t)(gb + m0 + m) * I + hc] = (_Float16)h;
-                }
-        }
-    } else {
-        const float* gl = reinterpret_cast<const float*>(slot + a.dn_glob);
-#pragma unroll
-        for (int b = 0; b < NBW; ++b) {
-            const int oc = nt * NCOLS + wn * CW + b * 16 + l16;
-            if (oc >= H) continue;
-            const float gd = gl[oc];
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = wm * MB * 16 + i * 16 + 4 * q4 + r;
-                    if (m < cnt) a.obuf[(size_t)(gb + m0 + m) * H + oc] = acc[i][b][r] * gd;
-                }
-        }
-    }
-}
-
-// ------------------------------------------------------------------ big-tile GEMM (128-row tiles)
-// One workgroup (8 waves, two per SIMD) computes a 128-token x 256-weight-row
-// tile: gate_up: 128 h-columns (their 128 gate rows and 128 up rows); down:
-// 256 output rows.  Wave (wm, wn) owns tokens [128/WM wm, +128/WM) and NB
-// 16-row weight blocks (gate_up: NB/2 gate tiles and the matching up tiles;
-// down: NB/4 record groups), so each dequantised weight fragment feeds
-// 8/WM MFMAs.  Four waves with 512 registers each (twice the weight rows per
-// wave) measured slower: a single wave per SIMD could not hide its
-// dequantisation behind the matrix cores.  Per
-// 128-column step the activation tile (128 x 128 fp16) sits in LDS, written
-// from registers one step ahead; each wave's weight records are loaded two
-// steps ahead into a register ping-pong.  Load order per step end:
-// activations of step s + 2, then weights of step s + 2, so waiting for
-// either never waits for the other's newer loads.
-template <bool GATEUP, int WM, int NB>
-__global__ void __launch_bounds__(8 * kWave) big_gemm_kernel(PrefillArgs a, int n_tiles_n) {
-    constexpr int BM = 128;
+// ------------------------------------------------------------------ grouped GEMM tiles
+// One workgroup (8 waves) computes a BM-token tile (BM = 128, 64 or 32)
+// against a block of weight rows: gate_up: matching gate and up rows, down:
+// output rows.  Wave (wm, wn) owns tokens [BM/WM wm, +BM/WM) and NB 16-row
+// weight blocks (gate_up: NB/2 gate tiles and the matching up tiles; down:
+// NB/4 record groups), so each dequantised weight fragment feeds BM/16/WM
+// MFMAs.  Four waves with 512 registers each (twice the weight rows per
+// wave) measured slower for 128-row tiles: a single wave per SIMD could not
+// hide its dequantisation behind the matrix cores.  Per 128-column step the
+// activation tile (BM x 128 fp16) sits in LDS, written from registers one
+// step ahead; each wave's weight records are loaded two steps ahead into a
+// register ping-pong.  Load order per step end: activations of step s + 2,
+// then weights of step s + 2, so waiting for either never waits for the
+// other's newer loads.  Every load is an unconditional buffer load (past
+// the end it reads zeros), which keeps the compiler's wait counts exact.
+template <bool GATEUP, int BM, int WM, int NB, int MINW>
+__global__ void __launch_bounds__(8 * kWave, MINW) tile_gemm_kernel(PrefillArgs a, int cls, int n_tiles_n) {
     constexpr int NWN = 8 / WM;              // waves along the weight rows (WM along the tokens)
     constexpr int MI = BM / 16 / WM;         // 16-row token blocks per wave
     constexpr int NT = 8 * kWave;            // threads
@@ -430,8 +226,8 @@ __global__ void __launch_bounds__(8 * kWave) big_gemm_kernel(PrefillArgs a, int 
     __shared__ int tok[BM];
 
     const int tile = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
-    if (tile >= a.tiles[0]) return;
-    const int* te = a.tiles + 4 + 2 * tile;
+    if (tile >= a.tiles[cls]) return;
+    const int* te = a.tiles + 4 + 2 * (cls * a.cap + tile);
     const int g = te[0], m0 = te[1];
     const int gb = group_begin(a, g), cnt = min(BM, group_end(a, g) - gb - m0);
     const uint8_t* slot = group_slot(a, g);
@@ -621,10 +417,27 @@ __global__ void __launch_bounds__(8 * kWave) big_gemm_kernel(PrefillArgs a, int 
 // gate_up: one wave per 128 tokens (each dequantised weight fragment feeds 8
 // MFMAs, no weight record loaded twice) measured faster than two; down keeps
 // two waves along the tokens and whole 64-row record groups per wave.
-constexpr int kBigGuWM = 1, kBigGuNB = 2;   // gate_up: waves along the tokens, 16-row weight blocks per wave
-constexpr int kBigDnWM = 2, kBigDnNB = 4;   // down
-constexpr int kBigGuCols = (8 / kBigGuWM) * 8 * kBigGuNB;    // h-columns per gate_up tile
-constexpr int kBigDnRows = (8 / kBigDnWM) * 16 * kBigDnNB;   // output rows per down tile
+// Remainder tiles (32 and 64 rows) run the same kernel with one wave along
+// the tokens; their smaller register and LDS footprint lets several
+// workgroups share a CU.
+template <bool GATEUP, int BM>
+struct TileCfg;
+template <> struct TileCfg<true, 128> { static constexpr int WM = 1, NB = 2, MINW = 2; };
+template <> struct TileCfg<false, 128> { static constexpr int WM = 2, NB = 4, MINW = 2; };
+template <> struct TileCfg<true, 64> { static constexpr int WM = 1, NB = 2, MINW = 4; };
+template <> struct TileCfg<false, 64> { static constexpr int WM = 1, NB = 4, MINW = 2; };
+template <> struct TileCfg<true, 32> { static constexpr int WM = 1, NB = 2, MINW = 6; };
+template <> struct TileCfg<false, 32> { static constexpr int WM = 1, NB = 4, MINW = 4; };
+
+template <bool GATEUP, int BM>
+hipError_t launch_tiles(const PrefillArgs& a, int cls, int max_tiles, hipStream_t s) {
+    using C = TileCfg<GATEUP, BM>;
+    const int cols = GATEUP ? (8 / C::WM) * 8 * C::NB : (8 / C::WM) * 16 * C::NB;  // h-columns or output rows
+    const int ntn = ceil_div(GATEUP ? a.I : a.H, cols);
+    hipLaunchKernelGGL((tile_gemm_kernel<GATEUP, BM, C::WM, C::NB, C::MINW>), dim3(max_tiles * ntn), dim3(8 * kWave), 0,
+                       s, a, cls, ntn);
+    return hipGetLastError();
+}
 
 // ------------------------------------------------------------------ combine
 // One thread per 4 output columns of token t; the k expert rows are read in
@@ -661,12 +474,6 @@ __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a, int nchunk)
     f32x4_t* yp = reinterpret_cast<f32x4_t*>(a.y + (size_t)t * H) + c4;
     if (a.accumulate) acc += *yp;
     *yp = acc;
-}
-
-template <int BM, bool GATEUP>
-hipError_t launch_gemm(const PrefillArgs& a, int cls, int max_tiles, int ntn, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_kernel<BM, GATEUP>), dim3(max_tiles * ntn), dim3(256), 0, s, a, cls, ntn);
-    return hipGetLastError();
 }
 
 // The 128-row tiles (matrix-core bound) and the 32/64-row remainder tiles
@@ -741,18 +548,13 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     if ((e = fork_for(s, f)) != hipSuccess) return e;
     if ((e = hipEventRecord(f.forked, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(f.side, f.forked, 0)) != hipSuccess) return e;
-    const int ntn_gu = ceil_div(I, 64);
-    if ((e = launch_gemm<64, true>(a, 1, maxsmall, ntn_gu, f.side)) != hipSuccess) return e;
-    if ((e = launch_gemm<32, true>(a, 2, maxsmall, ntn_gu, f.side)) != hipSuccess) return e;
-    if ((e = launch_gemm<64, false>(a, 1, maxsmall, ceil_div(H, 128), f.side)) != hipSuccess) return e;
-    if ((e = launch_gemm<32, false>(a, 2, maxsmall, ceil_div(H, 256), f.side)) != hipSuccess) return e;
+    if ((e = launch_tiles<true, 64>(a, 1, maxsmall, f.side)) != hipSuccess) return e;
+    if ((e = launch_tiles<true, 32>(a, 2, maxsmall, f.side)) != hipSuccess) return e;
+    if ((e = launch_tiles<false, 64>(a, 1, maxsmall, f.side)) != hipSuccess) return e;
+    if ((e = launch_tiles<false, 32>(a, 2, maxsmall, f.side)) != hipSuccess) return e;
     if ((e = hipEventRecord(f.joined, f.side)) != hipSuccess) return e;
-    hipLaunchKernelGGL((big_gemm_kernel<true, kBigGuWM, kBigGuNB>), dim3(max128 * ceil_div(I, kBigGuCols)),
-                       dim3(8 * kWave), 0, s, a, ceil_div(I, kBigGuCols));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((big_gemm_kernel<false, kBigDnWM, kBigDnNB>), dim3(max128 * ceil_div(H, kBigDnRows)),
-                       dim3(8 * kWave), 0, s, a, ceil_div(H, kBigDnRows));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_tiles<true, 128>(a, 0, max128, s)) != hipSuccess) return e;
+    if ((e = launch_tiles<false, 128>(a, 0, max128, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s, f.joined, 0)) != hipSuccess) return e;
     const int nchunk = ceil_div(H / 4, 256);
     hipLaunchKernelGGL(combine_kernel, dim3(T * nchunk), dim3(256), 0, s, a, nchunk);
