@@ -34,9 +34,9 @@ PCIE_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction
 # kernels and scaled by what the same counters read for a plain copy of known size), with a digest of the kernel
 # sources they were taken on.  Reported as roofline.traffic only while those sources are unchanged.
 COUNTED_TRAFFIC = {
-    "decode_bs1": (29_320_187, "391798333bd40a9a"),
-    "decode_bs16": (318_866_993, "391798333bd40a9a"),
-    "prefill_2048": (1_889_232_033, "54a2ca4b423b0895"),
+    "decode_bs1": (29_566_515, "27be0bdfe5e46959"),
+    "decode_bs16": (318_870_622, "27be0bdfe5e46959"),
+    "prefill_2048": (1_833_153_831, "dd5b874c466c11c5"),
 }
 KERNEL_SOURCES = {"decode": ["decode.hip", "route_device.hpp", "nvfp4_device.hpp"],
                   "prefill": ["prefill.hip", "nvfp4_device.hpp"]}
