@@ -434,7 +434,7 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
         tf = flops / fwd_s / 1e12
         roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": counted_traffic(name, "prefill"),
-                "kernel": "moe_nvfp4_forward prefill (prep, plan, tile_gemm_kernel over 128/64/32-row tiles for gate_up and "
+                "kernel": "moe_nvfp4_forward prefill (prep_plan_kernel, tile_gemm_kernel over 128/64/32-row tiles for gate_up and "
                           "down, combine_kernel), timed together with HIP events",
                 "per_launch": f"{flops / 1e9:.2f} GFLOP per forward (2*3*I*H*(T*k+T))"}
     else:

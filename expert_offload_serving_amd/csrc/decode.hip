@@ -411,26 +411,40 @@ __device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<N
     }
     __syncthreads();
     const bool out = blockIdx.x == 0;
-    for (int as = tid; as < n; as += NT) {
+    // P consecutive lanes (a power of two, up to 16) share one assignment's count
+    int P = 1;
+    while (P < 16 && 2 * P * n <= NT) P *= 2;
+    for (int idx = tid; idx < n * P; idx += NT) {
+        const int as = idx / P, part = idx % P;
         const int e = tb.ids[as];
         int pos = 0;
-        for (int b = 0; b < n; ++b) {
+#pragma unroll 4
+        for (int b = part; b < n; b += P) {
             const int eb = tb.ids[b];
             pos += (eb < e || (eb == e && b < as)) ? 1 : 0;
         }
-        tb.sorted[pos] = as;
-        if (out) {
-            a.r_ids[as] = e;
-            a.r_w[as] = tb.w[as];
-            a.r_sorted[pos] = as;
-            a.r_pos[as] = pos;
+        for (int o = 1; o < P; o <<= 1) pos += __shfl_xor(pos, o, kWave);
+        if (part == 0) {
+            tb.sorted[pos] = as;
+            if (out) {
+                a.r_ids[as] = e;
+                a.r_w[as] = tb.w[as];
+                a.r_sorted[pos] = as;
+                a.r_pos[as] = pos;
+            }
         }
     }
+    __syncthreads();
+    // offsets[e]: the first sorted position whose expert is >= e
     for (int e = tid; e <= E; e += NT) {
-        int c = 0;
-        for (int b = 0; b < n; ++b) c += tb.ids[b] < e ? 1 : 0;
-        tb.off[e] = c;
-        if (out) a.r_offsets[e] = c;
+        int lo = 0, hi = n;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (tb.ids[tb.sorted[mid]] < e) lo = mid + 1;
+            else hi = mid;
+        }
+        tb.off[e] = lo;
+        if (out) a.r_offsets[e] = lo;
     }
     __syncthreads();
     if (wave == 0) {  // compaction of the experts with assignments, ascending

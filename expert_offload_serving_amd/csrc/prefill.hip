@@ -26,8 +26,9 @@
 // the matching operand: lane (row i, group g) takes columns [32m + 8g, +8) of
 // the step for chunk m.
 //
-//   prep:     per-token scale, fp16 activations, shared gate sigmoid(x_t . w_g)
-//   plan:     (group, m0) tiles of 128 rows plus one 32/64/128-row remainder
+//   prep:     per-token scale, fp16 activations, shared gate sigmoid(x_t . w_g);
+//             in the same launch, the plan: (group, m0) tiles of 128 rows plus
+//             one 32/64/128-row remainder per group
 //   gate_up:  C = x W_gu^T over 64 gate and the 64 matching up rows per tile,
 //             epilogue h = silu(gate) * up -> fp16
 //   down:     O = h W_dn^T over 128 output rows per tile -> fp32
@@ -87,9 +88,9 @@ __device__ __forceinline__ const uint8_t* group_slot(const PrefillArgs& a, int g
 }
 
 // ------------------------------------------------------------------ prep
-__global__ void __launch_bounds__(256) prep_kernel(PrefillArgs a) {
-    __shared__ float red[2][4];
-    const int t = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+// One 256-thread workgroup per token t.
+__device__ __forceinline__ void prep_token(const PrefillArgs& a, int t, float (&red)[2][4]) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int H = a.H, nvec = H / 8;
     const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * H);
     const u32x4_t* wr = reinterpret_cast<const u32x4_t*>(a.wg);
@@ -146,8 +147,8 @@ __global__ void __launch_bounds__(256) prep_kernel(PrefillArgs a) {
 // ------------------------------------------------------------------ plan
 __device__ __forceinline__ int tile_class(int rows) { return rows > 64 ? 0 : (rows > 32 ? 1 : 2); }
 
-__global__ void __launch_bounds__(256) plan_kernel(PrefillArgs a) {
-    __shared__ int wsum[kClasses][4];
+// One 256-thread workgroup lists every tile.
+__device__ __forceinline__ void plan_tiles(const PrefillArgs& a, int (&wsum)[kClasses][4]) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int G = a.E + 1;
     const int per = (G + 255) / 256;
@@ -195,6 +196,15 @@ __global__ void __launch_bounds__(256) plan_kernel(PrefillArgs a) {
     }
 }
 
+// Workgroup 0 plans the tiles (it reads only the routing offsets), workgroups
+// 1..T prepare the tokens: one launch, and the plan overlaps the preparation.
+__global__ void __launch_bounds__(256) prep_plan_kernel(PrefillArgs a) {
+    __shared__ float red[2][4];
+    __shared__ int wsum[kClasses][4];
+    if (blockIdx.x == 0) plan_tiles(a, wsum);
+    else prep_token(a, (int)blockIdx.x - 1, red);
+}
+
 // ------------------------------------------------------------------ grouped GEMM (gate_up and down)
 
 __device__ __forceinline__ f16x8_t lds_frag(const _Float16* p) {
@@ -202,7 +212,7 @@ __device__ __forceinline__ f16x8_t lds_frag(const _Float16* p) {
 }
 
 // ------------------------------------------------------------------ grouped GEMM tiles
-// One workgroup (8 waves) computes a BM-token tile (BM = 128, 64 or 32)
+// One workgroup (NW waves) computes a BM-token tile (BM = 128, 64 or 32)
 // against a block of weight rows: gate_up: matching gate and up rows, down:
 // output rows.  Wave (wm, wn) owns tokens [BM/WM wm, +BM/WM) and NB 16-row
 // weight blocks (gate_up: NB/2 gate tiles and the matching up tiles; down:
@@ -216,17 +226,24 @@ __device__ __forceinline__ f16x8_t lds_frag(const _Float16* p) {
 // then weights of step s + 2, so waiting for either never waits for the
 // other's newer loads.  Every load is an unconditional buffer load (past
 // the end it reads zeros), which keeps the compiler's wait counts exact.
-template <bool GATEUP, int BM, int WM, int NB, int MINW>
-__global__ void __launch_bounds__(8 * kWave, MINW) tile_gemm_kernel(PrefillArgs a, int cls, int n_tiles_n) {
-    constexpr int NWN = 8 / WM;              // waves along the weight rows (WM along the tokens)
+template <bool GATEUP, int BM, int NW, int WM, int NB, int MINW>
+__global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs a, int cls, int n_tiles_n) {
+    constexpr int NWN = NW / WM;             // waves along the weight rows (WM along the tokens)
     constexpr int MI = BM / 16 / WM;         // 16-row token blocks per wave
-    constexpr int NT = 8 * kWave;            // threads
+    constexpr int NT = NW * kWave;           // threads
     constexpr int AQ = BM * 16 / NT;         // activation chunks per thread per step
     __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * APITCH];
     __shared__ int tok[BM];
 
-    const int tile = blockIdx.x / n_tiles_n, nt = blockIdx.x % n_tiles_n;
-    if (tile >= a.tiles[cls]) return;
+    // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs (block b to XCD b % 8), so the active
+    // blocks of XCD x take one contiguous range of (tile, column tile) pairs.  The column tiles of a row tile,
+    // and the tiles of one expert, then share that XCD's L2: the activation tile and the expert's weights are
+    // fetched from HBM once per XCD instead of once per workgroup.
+    const int n_active = a.tiles[cls] * n_tiles_n;
+    if ((int)blockIdx.x >= n_active) return;
+    const int per_xcd = n_active / 8, extra = n_active % 8, xcd = (int)blockIdx.x % 8;
+    const int lb = xcd * per_xcd + min(xcd, extra) + (int)blockIdx.x / 8;
+    const int tile = lb / n_tiles_n, nt = lb % n_tiles_n;
     const int* te = a.tiles + 4 + 2 * (cls * a.cap + tile);
     const int g = te[0], m0 = te[1];
     const int gb = group_begin(a, g), cnt = min(BM, group_end(a, g) - gb - m0);
@@ -419,23 +436,25 @@ __global__ void __launch_bounds__(8 * kWave, MINW) tile_gemm_kernel(PrefillArgs 
 // two waves along the tokens and whole 64-row record groups per wave.
 // Remainder tiles (32 and 64 rows) run the same kernel with one wave along
 // the tokens; their smaller register and LDS footprint lets several
-// workgroups share a CU.
+// workgroups share a CU.  Four-wave workgroups (two per CU) made the 128-row
+// gate_up faster in isolation but the whole forward slower, as they leave
+// no room on a CU for the remainder tiles of the side stream.
 template <bool GATEUP, int BM>
 struct TileCfg;
-template <> struct TileCfg<true, 128> { static constexpr int WM = 1, NB = 2, MINW = 2; };
-template <> struct TileCfg<false, 128> { static constexpr int WM = 2, NB = 4, MINW = 2; };
-template <> struct TileCfg<true, 64> { static constexpr int WM = 1, NB = 2, MINW = 4; };
-template <> struct TileCfg<false, 64> { static constexpr int WM = 1, NB = 4, MINW = 2; };
-template <> struct TileCfg<true, 32> { static constexpr int WM = 1, NB = 2, MINW = 6; };
-template <> struct TileCfg<false, 32> { static constexpr int WM = 1, NB = 4, MINW = 4; };
+template <> struct TileCfg<true, 128> { static constexpr int NW = 8, WM = 1, NB = 2, MINW = 2; };
+template <> struct TileCfg<false, 128> { static constexpr int NW = 8, WM = 2, NB = 4, MINW = 2; };
+template <> struct TileCfg<true, 64> { static constexpr int NW = 8, WM = 1, NB = 2, MINW = 4; };
+template <> struct TileCfg<false, 64> { static constexpr int NW = 8, WM = 1, NB = 4, MINW = 2; };
+template <> struct TileCfg<true, 32> { static constexpr int NW = 8, WM = 1, NB = 2, MINW = 6; };
+template <> struct TileCfg<false, 32> { static constexpr int NW = 8, WM = 1, NB = 4, MINW = 4; };
 
 template <bool GATEUP, int BM>
 hipError_t launch_tiles(const PrefillArgs& a, int cls, int max_tiles, hipStream_t s) {
     using C = TileCfg<GATEUP, BM>;
-    const int cols = GATEUP ? (8 / C::WM) * 8 * C::NB : (8 / C::WM) * 16 * C::NB;  // h-columns or output rows
+    const int cols = GATEUP ? (C::NW / C::WM) * 8 * C::NB : (C::NW / C::WM) * 16 * C::NB;  // h-columns or output rows
     const int ntn = ceil_div(GATEUP ? a.I : a.H, cols);
-    hipLaunchKernelGGL((tile_gemm_kernel<GATEUP, BM, C::WM, C::NB, C::MINW>), dim3(max_tiles * ntn), dim3(8 * kWave), 0,
-                       s, a, cls, ntn);
+    hipLaunchKernelGGL((tile_gemm_kernel<GATEUP, BM, C::NW, C::WM, C::NB, C::MINW>), dim3(max_tiles * ntn),
+                       dim3(C::NW * kWave), 0, s, a, cls, ntn);
     return hipGetLastError();
 }
 
@@ -538,11 +557,9 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     const int G = E + 1;
     const int max128 = min(a.cap, rows / 128 + G);
     const int maxsmall = min(a.cap, G);
-    hipLaunchKernelGGL(prep_kernel, dim3(T), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prep_plan_kernel, dim3(T + 1), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     // remainder tiles on the side stream, 128-row tiles on the caller's stream
     Fork f;
     if ((e = fork_for(s, f)) != hipSuccess) return e;

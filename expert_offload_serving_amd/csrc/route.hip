@@ -107,9 +107,12 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __res
 
 // Decode batches (T <= 16, T*k <= kDirectMaxAssign): one workgroup with one
 // wave per token selects the top-k, then ranks every assignment directly:
-//   offsets[e] = #{assignments with expert < e}
 //   pos(a)     = #{a' : (e', a') < (e, a)}   (expert, then flat index)
+//   offsets[e] = #{assignments with expert < e}
 // which is the same stable grouping as the counting sort, in one launch.
+// P threads (a power of two, up to 16) share one assignment's count, each
+// scanning every P-th group of four ids, and add their parts with lane
+// shuffles; the offsets are then a binary search of the sorted expert list.
 constexpr int kDirectMaxAssign = 256;
 
 template <int VPL>
@@ -119,34 +122,46 @@ __global__ void __launch_bounds__(1024) route_small_kernel(const float* __restri
                                                             int32_t* __restrict__ sorted_assign,
                                                             int32_t* __restrict__ assign_pos) {
     __shared__ __attribute__((aligned(16))) int32_t ids_lds[kDirectMaxAssign + 4];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    __shared__ int32_t sorted_e[kDirectMaxAssign];
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int wave = tid / kWave, lane = tid % kWave;
     if (wave < T) topk_one_token<VPL>(logits + (size_t)wave * E, E, k, ids_lds + wave * k, w + (size_t)wave * k, lane);
     const int n = T * k, n4 = (n + 3) / 4;
-    if ((int)threadIdx.x < 4 * n4 - n) ids_lds[n + threadIdx.x] = 0x7FFFFFFF;  // pad: ranks after every expert
+    if (tid < 4 * n4 - n) ids_lds[n + tid] = 0x7FFFFFFF;  // pad: ranks after every expert
     __syncthreads();
+    int P = 1;
+    while (P < 16 && 2 * P * n <= nthr) P *= 2;
     const int4* ids4 = reinterpret_cast<const int4*>(ids_lds);
-    // pos(a) = #{b : (e_b, b) < (e_a, a)}, scanned four assignments per LDS read
-    for (int a = threadIdx.x; a < n; a += blockDim.x) {
+    // the P threads of an assignment are consecutive lanes of one wave, all active together
+    for (int idx = tid; idx < n * P; idx += nthr) {
+        const int a = idx / P, part = idx % P;
         const int e = ids_lds[a];
         int pos = 0;
-        for (int q = 0; q < n4; ++q) {
+#pragma unroll 4
+        for (int q = part; q < n4; q += P) {
             const int4 v = ids4[q];
             const int b = 4 * q;
             pos += (v.x < e || (v.x == e && b < a)) + (v.y < e || (v.y == e && b + 1 < a)) +
                    (v.z < e || (v.z == e && b + 2 < a)) + (v.w < e || (v.w == e && b + 3 < a));
         }
-        ids[a] = e;
-        sorted_assign[pos] = a;
-        assign_pos[a] = pos;
-    }
-    // offsets[e] = #{b : e_b < e}
-    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
-        int c = 0;
-        for (int q = 0; q < n4; ++q) {
-            const int4 v = ids4[q];
-            c += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
+        for (int off = 1; off < P; off <<= 1) pos += __shfl_xor(pos, off, kWave);
+        if (part == 0) {
+            ids[a] = e;
+            sorted_assign[pos] = a;
+            assign_pos[a] = pos;
+            sorted_e[pos] = e;
         }
-        offsets[e] = c;
+    }
+    __syncthreads();
+    // offsets[e] = #{b : e_b < e}: the first sorted position holding an expert >= e
+    for (int e = tid; e <= E; e += nthr) {
+        int lo = 0, hi = n;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (sorted_e[mid] < e) lo = mid + 1;
+            else hi = mid;
+        }
+        offsets[e] = lo;
     }
 }
 
