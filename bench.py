@@ -34,9 +34,9 @@ PCIE_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction
 # kernels and scaled by what the same counters read for a plain copy of known size), with a digest of the kernel
 # sources they were taken on.  Reported as roofline.traffic only while those sources are unchanged.
 COUNTED_TRAFFIC = {
-    "decode_bs1": (29_566_515, "27be0bdfe5e46959"),
-    "decode_bs16": (318_870_622, "27be0bdfe5e46959"),
-    "prefill_2048": (1_833_153_831, "dd5b874c466c11c5"),
+    "decode_bs1": (29_552_752, "8d681a667bd63f91"),
+    "decode_bs16": (318_923_524, "8d681a667bd63f91"),
+    "prefill_2048": (1_394_893_546, "52b117e61e3109c2"),
 }
 KERNEL_SOURCES = {"decode": ["decode.hip", "route_device.hpp", "nvfp4_device.hpp"],
                   "prefill": ["prefill.hip", "nvfp4_device.hpp"]}
