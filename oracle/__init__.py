@@ -57,6 +57,8 @@ def lib():
         L.oracle_unpack_slot.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _u8p, _f32p]
         L.oracle_route.restype = ctypes.c_int
         L.oracle_route.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _f32p]
+        L.oracle_router_logits.restype = None
+        L.oracle_router_logits.argtypes = [_u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f32p]
         L.oracle_permute.restype = None
         L.oracle_permute.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p, _i32p]
         L.oracle_shared_gate.restype = None
@@ -133,6 +135,18 @@ def route(logits, k: int):
     if lib().oracle_route(logits, T, E, k, ids, w) != 0:
         raise ValueError("NaN router logit")
     return ids, w
+
+
+def router_logits(x, w_router) -> np.ndarray:
+    """logits [T, E] = x [T, H] . w_router [E, H]^T (bf16 bit patterns in), double accumulation, f32 out."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w_router = np.ascontiguousarray(w_router, dtype=np.uint16)
+    T, H = x.shape
+    E = w_router.shape[0]
+    assert w_router.shape[1] == H
+    out = np.empty((T, E), dtype=np.float32)
+    lib().oracle_router_logits(x, w_router, T, H, E, out)
+    return out
 
 
 def permute(ids, E: int):

@@ -121,6 +121,19 @@ int oracle_route(const float* logits, int T, int E, int k, int32_t* ids, float* 
     return rc;
 }
 
+/* Router projection (the replicated router of the R9700 interim report on
+ * #62, whose outputs the top-k above selects from): logits[t, e] =
+ * sum_h x[t, h] * w[e, h] over bf16 activations x [T, H] and bf16 router
+ * weights w [E, H], accumulated in double and rounded to f32 once. */
+void oracle_router_logits(const uint16_t* x, const uint16_t* w, int T, int H, int E, float* logits) {
+    for (int t = 0; t < T; ++t)
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h) acc += bf16_to_double(x[(size_t)t * H + h]) * bf16_to_double(w[(size_t)e * H + h]);
+            logits[(size_t)t * E + e] = (float)acc;
+        }
+}
+
 /* Counting sort of the T*k assignments by expert.  offsets[E+1] is the
  * exclusive scan of the per-expert counts; sorted_assign lists flat indices
  * t*k+j ordered by (expert, t, j); assign_pos is its inverse. */

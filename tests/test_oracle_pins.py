@@ -140,6 +140,54 @@ def test_route_rejects_nan():
         oracle.route(np.array([[0.0, np.nan]], dtype=np.float32), 1)
 
 
+# ---------------------------------------------------------------- router projection
+
+def _bf16(v):
+    return synth.f32_to_bf16_bits(np.asarray(v, dtype=np.float32))
+
+
+def test_router_logits_hand_worked_values():
+    # x = [1, 2, -0.5], rows of w: [1, 1, 1] -> 2.5; [3, -1, 4] -> 3 - 2 - 2 = -1; [0.25, 0.125, 8] -> 0.5 - 4 = -3.5
+    x = _bf16([[1.0, 2.0, -0.5]])
+    w = _bf16([[1.0, 1.0, 1.0], [3.0, -1.0, 4.0], [0.25, 0.125, 8.0]])
+    assert oracle.router_logits(x, w).tolist() == [[2.5, -1.0, -3.5]]
+
+
+def test_router_logits_one_hot_picks_a_weight_column():
+    rng = np.random.default_rng(5)
+    w = _bf16(rng.standard_normal((7, 24)) * 0.02)
+    for h in (0, 11, 23):
+        x = np.zeros((1, 24), dtype=np.uint16)
+        x[0, h] = 0x3F80  # bf16 1.0
+        got = oracle.router_logits(x, w)[0]
+        assert np.array_equal(got, synth.bf16_bits_to_f32(w[:, h]))
+
+
+def test_router_logits_round_once_after_exact_accumulation():
+    # 1 + 2^-24 + 2^-24 = 1 + 2^-23 exactly (a float32); accumulating in float32 would lose both small terms
+    # (1 + 2^-24 is a tie that rounds to even, i.e. back to 1).
+    x = _bf16([[1.0, 1.0, 1.0]])
+    w = _bf16([[1.0, 2.0 ** -24, 2.0 ** -24], [1.0, 2.0 ** -24, 0.0], [1.0, 1.5 * 2.0 ** -24, 0.0]])
+    got = oracle.router_logits(x, w)[0]
+    assert got[0] == np.float32(1.0 + 2.0 ** -23)
+    assert got[1] == np.float32(1.0)                       # exact tie -> even
+    assert got[2] == np.float32(1.0 + 2.0 ** -23)          # above the tie -> up
+
+
+def test_router_logits_match_exact_rational_sum():
+    from fractions import Fraction
+    rng = np.random.default_rng(9)
+    x = _bf16(rng.standard_normal((3, 40)))
+    w = _bf16(rng.standard_normal((5, 40)) * 0.02)
+    got = oracle.router_logits(x, w)
+    xf, wf = synth.bf16_bits_to_f32(x), synth.bf16_bits_to_f32(w)
+    for t in range(3):
+        for e in range(5):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xf[t], wf[e]))
+            # the double accumulation can round; it stays within 40 double roundings of the exact sum
+            assert abs(Fraction(float(got[t, e])) - exact) <= abs(exact) * Fraction(1, 2 ** 23) + Fraction(1, 2 ** 60)
+
+
 def test_permute_matches_stable_argsort():
     rng = np.random.default_rng(3)
     for T, E, k in [(1, 256, 8), (16, 256, 8), (300, 32, 4), (7, 5, 5)]:
