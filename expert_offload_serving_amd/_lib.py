@@ -24,7 +24,7 @@ EXPORTED = [
     "moe_last_error", "moe_nvfp4_slot_bytes", "moe_route_workspace_bytes", "moe_route_topk",
     "moe_nvfp4_forward_workspace_bytes", "moe_nvfp4_forward", "expert_cache_fill", "moe_cache_create",
     "moe_cache_destroy", "moe_cache_plan", "moe_nvfp4_slice_bank", "moe_nvfp4_dequant",
-    "moe_nvfp4_route_forward_workspace_bytes", "moe_nvfp4_route_forward",
+    "moe_nvfp4_route_forward_workspace_bytes", "moe_nvfp4_route_forward", "moe_router_logits", "moe_router_topk",
 ]
 
 
@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.moe_route_workspace_bytes.argtypes = [_i, _i, _i]
         L.moe_route_topk.restype = _i
         L.moe_route_topk.argtypes = [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_router_logits.restype = _i
+        L.moe_router_logits.argtypes = [_vp, _vp, _i, _i, _i, _vp, _vp]
+        L.moe_router_topk.restype = _i
+        L.moe_router_topk.argtypes = [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_nvfp4_forward_workspace_bytes.restype = _sz
         L.moe_nvfp4_forward_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
         L.moe_nvfp4_forward.restype = _i
@@ -132,6 +136,17 @@ def moe_route_topk(logits, T, E, k, topk_ids, topk_w, expert_offsets, sorted_ass
                    ws_bytes=0, stream=None) -> int:
     return lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
                                 _ptr(sorted_assign), _ptr(assign_pos), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_router_logits(x, w_router, T, H, E, logits, stream=None) -> int:
+    return lib().moe_router_logits(_ptr(x), _ptr(w_router), T, H, E, _ptr(logits), _stream(stream))
+
+
+def moe_router_topk(x, w_router, T, H, E, k, logits, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos,
+                    ws=None, ws_bytes=0, stream=None) -> int:
+    return lib().moe_router_topk(_ptr(x), _ptr(w_router), T, H, E, k, _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                 _ptr(expert_offsets), _ptr(sorted_assign), _ptr(assign_pos), _ptr(ws), ws_bytes,
+                                 _stream(stream))
 
 
 def moe_nvfp4_forward_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:

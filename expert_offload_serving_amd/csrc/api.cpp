@@ -98,6 +98,42 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, 
     return MOE_OK;
 }
 
+int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int H, int E, float* logits,
+                      hipStream_t stream) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 (got %d)", T);
+    if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E must be in [1, 1024] (got %d)", E);
+    if (!moe::router_shape_supported(T, H, E))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "router shape T=%d H=%d E=%d unsupported (H %% 256 == 0, H <= 16384)",
+                    T, H, E);
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !logits) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_router_logits: null pointer argument");
+    hipError_t e = moe::launch_router(x, w_router, T, H, E, logits, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_router_logits launch");
+    return MOE_OK;
+}
+
+int moe_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int H, int E, int k, float* logits,
+                    int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_assign,
+                    int32_t* assign_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
+    // every argument is checked before anything is enqueued
+    int rc = check_route_shape(T, E, k);
+    if (rc != MOE_OK) return rc;
+    if (!moe::router_shape_supported(T, H, E))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "router shape T=%d H=%d E=%d unsupported (H %% 256 == 0, H <= 16384)",
+                    T, H, E);
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !logits || !topk_ids || !topk_w || !expert_offsets || !sorted_assign || !assign_pos)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_router_topk: null pointer argument");
+    const size_t need = moe::route_ws_bytes(T, E, k);
+    if (ws_bytes < need || (need > 0 && !ws))
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "route workspace %zu < %zu bytes", ws_bytes, need);
+    hipError_t e = moe::launch_router(x, w_router, T, H, E, logits, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_router_topk: router launch");
+    e = moe::launch_route(logits, T, E, k, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_router_topk: routing launch");
+    return MOE_OK;
+}
+
 size_t moe_nvfp4_forward_workspace_bytes(int T, int H, int I, int E, int k) {
     if (!shape_ok(H, I) || check_route_shape(T, E, k) != MOE_OK) return 0;
     return moe::forward_ws_bytes(T, H, I, E, k);

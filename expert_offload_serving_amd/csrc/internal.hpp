@@ -14,6 +14,10 @@ size_t route_ws_bytes(int T, int E, int k);
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_assign, int32_t* assign_pos, void* ws, hipStream_t s);
 
+// Router projection (router.hip): logits [T, E] = x [T, H] . w_r [E, H]^T.
+bool router_shape_supported(int T, int H, int E);
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, int T, int H, int E, float* logits, hipStream_t s);
+
 // Layer description after validation.
 struct Layer {
     int H, I, E, k;

@@ -86,6 +86,30 @@ def route(logits: torch.Tensor, k: int, out: Routing | None = None, stream=None)
     return r
 
 
+def router_logits(x: torch.Tensor, w_router: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """logits [T, E] f32 = x [T, H] bf16 . w_router [E, H] bf16^T on the matrix cores."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if out is None else out
+    check(_lib.moe_router_logits(x, w_router, T, H, E, logits, stream))
+    return logits
+
+
+def router_route(x: torch.Tensor, w_router: torch.Tensor, k: int, out: Routing | None = None,
+                 logits: torch.Tensor | None = None, stream=None):
+    """Router projection and top-k routing in one call; returns (logits, routing)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    r = Routing.empty(T, E, k, x.device) if out is None else out
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    nb = _lib.moe_route_workspace_bytes(T, E, k)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=x.device) if nb else None
+    check(_lib.moe_router_topk(x, w_router, T, H, E, k, logits, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos,
+                               ws, nb, stream))
+    return logits, r
+
+
 def workspace(T: int, layer: DeviceLayer) -> torch.Tensor:
     nb = _lib.moe_nvfp4_forward_workspace_bytes(T, layer.H, layer.I, layer.E, layer.k)
     return torch.empty(nb, dtype=torch.uint8, device=layer.bank.device)

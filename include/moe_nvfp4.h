@@ -94,6 +94,32 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, 
                    int32_t* expert_offsets, int32_t* sorted_assign, int32_t* assign_pos, void* ws, size_t ws_bytes,
                    hipStream_t stream);
 
+/* ------------------------------------------------------------------ router
+ * The replicated router's projection (issue #62, R9700 interim report: the
+ * router is replicated and its top-k weights renormalised), the step just
+ * before the top-k above:
+ *   logits[t, e] = sum_h x[t, h] * w_router[e, h]
+ *   x          device bf16 [T, H] activations (row-major)
+ *   w_router   device bf16 [E, H] router weights (row-major, one row per expert)
+ *   logits     device f32 [T, E] out
+ * bf16 products are exact in fp32; the sum is accumulated in fp32 on the
+ * matrix cores in a fixed order, so repeated calls give identical bits.
+ * Shapes: T >= 0 (0 is a no-op), 1 <= E <= 1024, H % 256 == 0, H <= 16384,
+ * T*H*2 and E*H*2 below 2^31 bytes; others return MOE_ERR_UNSUPPORTED_SHAPE
+ * with nothing enqueued.  Buffers are owned by the caller. */
+int moe_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int H, int E, float* logits,
+                      hipStream_t stream);
+
+/* moe_router_logits followed by moe_route_topk on its logits, in one call
+ * on `stream` (the router fused into routing): logits is written (f32
+ * [T, E], the values the selection was made on) and the routing outputs are
+ * those of moe_route_topk.  ws, ws_bytes: at least
+ * moe_route_workspace_bytes(T, E, k).  All arguments are validated before
+ * anything is enqueued. */
+int moe_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int H, int E, int k, float* logits,
+                    int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_assign,
+                    int32_t* assign_pos, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ layer
  * A layer's expert storage: E routed experts addressed through a slot map
  * into a bank of equally sized slots, plus an optional shared expert.

@@ -118,6 +118,81 @@ def test_route_ties_zero_counts_and_extremes():
     _check_route(rng.standard_normal((16, 1024)).astype(np.float32), 300, "k=300 fused path")
 
 
+# ---------------------------------------------------------------- router projection
+
+def _router_inputs(T, H, E, seed):
+    rng = np.random.default_rng(seed)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    w = synth.f32_to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.02))
+    return x, w
+
+
+def _check_router_logits(got, x, w, what):
+    """fp32 accumulation of H exact bf16 products: |err| <= H * 2^-24 * sum_h |x_h w_h| (plus the final rounding)."""
+    ref = oracle.router_logits(x, w).astype(np.float64)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    wf = synth.bf16_bits_to_f32(w).astype(np.float64)
+    bound = (x.shape[1] + 1) * 2.0 ** -24 * (np.abs(xf) @ np.abs(wf).T)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert (err <= bound).all(), f"{what}: max err/bound {(err / np.maximum(bound, 1e-300)).max():.3g}"
+    return ref
+
+
+@pytest.mark.parametrize("T,H,E", [(1, 2560, 256), (3, 2560, 256), (16, 2560, 256), (17, 2560, 256),
+                                   (300, 2560, 256), (5, 256, 8), (20, 512, 1000), (33, 768, 40)])
+def test_router_logits_vs_oracle(T, H, E):
+    _announce(f"router logits T={T} H={H} E={E}")
+    x, w = _router_inputs(T, H, E, 100 + T)
+    got = dl.router_logits(torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    _check_router_logits(got.cpu().numpy(), x, w, f"T={T} H={H} E={E}")
+
+
+def test_router_logits_prefill_2048_sampled_rows_and_repeatable():
+    T, H, E = 2048, 2560, 256
+    _announce(f"router logits T={T} H={H} E={E} (sampled rows, repeat)")
+    x, w = _router_inputs(T, H, E, 7)
+    xd, wd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+    a = dl.router_logits(xd, wd)
+    b = dl.router_logits(xd, wd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "router logits not bit-identical between calls"
+    rows = np.array([0, 1, 31, 32, 33, 1000, 2015, 2047])
+    _check_router_logits(a.cpu().numpy()[rows], x[rows], w, "T=2048 sampled")
+
+
+def test_router_topk_selects_on_its_logits():
+    # the top-k decision is taken on the kernel's fp32 logits: the oracle's routing of those same logits must match
+    for T, H, E, k in [(1, 2560, 256, 8), (16, 2560, 256, 8), (300, 2560, 256, 8), (4, 256, 8, 2)]:
+        _announce(f"router topk T={T} H={H} E={E} k={k}")
+        x, w = _router_inputs(T, H, E, 11 + T)
+        logits, r = dl.router_route(torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda(), k)
+        torch.cuda.synchronize()
+        lg = logits.cpu().numpy()
+        _check_router_logits(lg, x, w, f"topk T={T}")
+        ids, wt = oracle.route(lg, k)
+        off, srt, pos = oracle.permute(ids, E)
+        assert np.array_equal(r.ids.cpu().numpy(), ids)
+        assert np.array_equal(r.offsets.cpu().numpy(), off)
+        assert np.array_equal(r.sorted_assign.cpu().numpy(), srt)
+        assert np.array_equal(r.assign_pos.cpu().numpy(), pos)
+        ulps = np.abs(r.w.cpu().numpy().view(np.int32).astype(np.int64) - wt.view(np.int32).astype(np.int64))
+        assert ulps.max() <= 1
+
+
+def test_router_rejects_bad_shapes_and_empty_is_noop():
+    x, w = _router_inputs(4, 2560, 16, 3)
+    xd, wd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+    out = torch.full((4, 16), 7.0, device="cuda")
+    assert _lib.moe_router_logits(xd, wd, 4, 2000, 16, out, None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE  # H % 256
+    assert _lib.moe_router_logits(xd, wd, 4, 2560, 2000, out, None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE  # E > 1024
+    assert _lib.moe_router_logits(xd, wd, -1, 2560, 16, out, None) == _lib.MOE_ERR_INVALID_ARGUMENT
+    assert _lib.moe_router_logits(None, wd, 4, 2560, 16, out, None) == _lib.MOE_ERR_INVALID_ARGUMENT
+    assert _lib.moe_router_logits(xd, wd, 0, 2560, 16, out, None) == _lib.MOE_OK
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()), "a refused or empty call wrote its output"
+
+
 # ---------------------------------------------------------------- forward
 
 def _gpu_forward(L, T=None, slot_map=None, shared=True, y=None, accumulate=False):
