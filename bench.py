@@ -234,13 +234,13 @@ def parity_sample(inp, res, tokens):
 
 # ---------------------------------------------------------------- offload
 
-def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2):
+def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_cpu: bool = True):
     """48 MoE layers whose 256 experts live in pinned host memory behind one HBM cache of 37% of the
     12,288 expert-layer slots (global LRU, cold start).  Per layer-step: route on the GPU, one D2H copy of
     the ids, host LRU plan, misses copied on a side stream while the hits-only forward runs, then the
-    misses-only forward accumulates.  Returns the JSON dict."""
+    misses-only forward accumulates.  With want_cpu, the CPU leg checks the host LRU and the last layer-step
+    against the oracle.  Returns the JSON dict."""
     import torch
-    import oracle
     from expert_offload_serving_amd import _lib, synth
     from expert_offload_serving_amd import layer as dl
 
@@ -370,18 +370,24 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2):
     torch.cuda.synchronize()
     h2d_gbs = n_probe * sb / (time.perf_counter() - tp) / 1e9
 
-    # checks: the host LRU against the oracle's model on the same ids; the last layer-step against the oracle
-    h_ref, m_ref, _, _ = oracle.lru_run(ids_log, E, n_slots, want_maps=False)
-    lru_ok = bool(np.array_equal(h_ref, stats["hits"]) and np.array_equal(m_ref, stats["misses"]))
-    s_last, l_last = total - 1, L - 1
-    ids_o, w_o = oracle.route(logits_np[s_last, l_last], k)
-    bank_o = np.concatenate([base_np, shared_np[l_last][None]], axis=0)
-    som_o = np.array([base_of(l_last, e_) for e_ in range(E)], dtype=np.int32)
-    toks = np.arange(2, dtype=np.int32)
-    ref = oracle.forward(H, I, E, k, bank_o, som_o, E, wg_np[l_last], xs_np[(s_last * L + l_last) % NX], ids_o,
-                         w_o, tokens=toks)
-    got = y.cpu().numpy()[toks].astype(np.float64)
-    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    cpu_checks = None
+    if want_cpu:
+        # the CPU leg: the host LRU against the oracle's model on the same ids; the last layer-step against the
+        # oracle
+        import oracle
+        h_ref, m_ref, _, _ = oracle.lru_run(ids_log, E, n_slots, want_maps=False)
+        lru_ok = bool(np.array_equal(h_ref, stats["hits"]) and np.array_equal(m_ref, stats["misses"]))
+        s_last, l_last = total - 1, L - 1
+        ids_o, w_o = oracle.route(logits_np[s_last, l_last], k)
+        bank_o = np.concatenate([base_np, shared_np[l_last][None]], axis=0)
+        som_o = np.array([base_of(l_last, e_) for e_ in range(E)], dtype=np.int32)
+        toks = np.arange(2, dtype=np.int32)
+        ref = oracle.forward(H, I, E, k, bank_o, som_o, E, wg_np[l_last], xs_np[(s_last * L + l_last) % NX], ids_o,
+                             w_o, tokens=toks)
+        got = y.cpu().numpy()[toks].astype(np.float64)
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        cpu_checks = {"lru_matches_oracle_model": lru_ok, "rel_l2_last_layer_step": rel,
+                      "tokens_checked": int(toks.size)}
 
     hits, misses = stats["hits"][warmup:].sum(), stats["misses"][warmup:].sum()
     miss_bytes = misses * sb
@@ -405,8 +411,8 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2):
                                              max(1, stats["hits"][:warmup].sum() + stats["misses"][:warmup].sum()), 4),
                     "model_tokens_per_s": round(T * steps / wall, 2), "ms_per_layer_step": round(wall * 1e3 / (steps * L), 4),
                     "miss_GB_per_step": round(miss_bytes / steps / 1e9, 3), "h2d_copy_GBps_alone": round(h2d_gbs, 2),
-                    "warmup_s": round(t_cold, 2), "lru_matches_oracle_model": lru_ok},
-        "parity": {"rel_l2_last_layer_step": rel, "tokens_checked": int(toks.size)},
+                    "warmup_s": round(t_cold, 2)},
+        **({"parity": cpu_checks} if cpu_checks is not None else {}),
     }
 
 
@@ -461,14 +467,90 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     if prefill:
         out["layer"]["forward_TFLOPs"] = round(flops / fwd_s / 1e12, 2)
         out["layer"]["expert_count_range"] = [res["counts_min"], res["counts_max"]]
-    try:
-        out["parity"] = parity_sample(inp, res, 4)
-    except Exception as e:  # the parity sample is a report, not the measurement
-        out["parity"] = {"error": str(e)}
     if want_cpu:
+        # the CPU-baseline leg (the only part of the benchmark that runs the oracle): the oracle timed on a
+        # sample of this workload, and the last timed step's output checked against it
         log(f"{name}: timing the oracle on {cpu_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(inp, cpu_tokens, "tokens/s")
+        try:
+            out["parity"] = parity_sample(inp, res, 4)
+        except Exception as e:  # the parity sample is a report, not the measurement
+            out["parity"] = {"error": str(e)}
     return out
+
+
+ROUTER_CONFIGS = {"router_bs1": 1, "router_bs16": 16, "router_2048": 2048}
+
+
+def bench_router(name: str, steps: int, warmup: int, replicas: int) -> dict:
+    """Router projection (moe_router_logits) and router + top-k (moe_router_topk) at H=2560, E=256, k=8.
+
+    The weights rotate over `replicas` copies (R x 1.31 MB, more than the Infinity Cache holds) so every step
+    reads them from HBM, as a decode step does after the other layers have streamed through."""
+    import torch
+    from expert_offload_serving_amd import _lib, synth
+    from expert_offload_serving_amd import layer as dl
+    T, H, E, k = ROUTER_CONFIGS[name], 2560, 256, 8
+    rng = np.random.default_rng(77 + T)
+    x = torch.from_numpy(synth.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))).cuda()
+    base = synth.f32_to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.02))
+    wr = torch.from_numpy(base).cuda().unsqueeze(0).repeat(replicas, 1, 1).contiguous()
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    r = dl.Routing.empty(T, E, k)
+    nb = _lib.moe_route_workspace_bytes(T, E, k)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+
+    def call(i: int, topk: bool):
+        w = wr[i % replicas]
+        if topk:
+            _lib.check(_lib.moe_router_topk(x, w, T, H, E, k, logits, r.ids, r.w, r.offsets, r.sorted_assign,
+                                            r.assign_pos, ws, nb, None))
+        else:
+            _lib.check(_lib.moe_router_logits(x, w, T, H, E, logits, None))
+
+    def timed(topk: bool) -> float:
+        for i in range(warmup):
+            call(i, topk)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                call(i, topk)
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3  # us per call
+
+    us_logits = timed(False)
+    us_topk = timed(True)
+    wbytes = E * H * 2
+    decode = T <= 16
+    flops = 2.0 * T * E * H
+    if decode:
+        gbs = (wbytes + T * H * 2 + T * E * 4) / (us_logits * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "router_logits_kernel<1, 1> (moe_router_logits), HIP events around a graph of calls",
+                "per_launch": f"{(wbytes + T * H * 2 + T * E * 4) / 1e6:.3f} MB (router weights, x, logits)"}
+    else:
+        tf = flops / (us_logits * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "router_logits_kernel<2, 4> (moe_router_logits), HIP events around a graph of calls",
+                "per_launch": f"{flops / 1e9:.3f} GFLOP (2*T*E*H)"}
+    return {"metric": "router projection + top-k tokens/s, bf16 W_r [E, H]", "value": round(T / (us_topk * 1e-6), 2),
+            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(us_topk / 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": name, "H": H, "E": E, "k": k, "T": T, "weight_copies": replicas,
+                       "parallelism": "single GPU"},
+            "roofline": roof,
+            "router": {"logits_us": round(us_logits, 2), "router_topk_us": round(us_topk, 2)}}
 
 
 def copy_calibration(nbytes: int, reps: int) -> None:
@@ -492,7 +574,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_bs1",
-                    choices=["decode_bs1", "decode_bs16", "prefill_2048", "offload", "all"])
+                    choices=["decode_bs1", "decode_bs16", "prefill_2048", "offload", "all", *ROUTER_CONFIGS])
     ap.add_argument("--replicas", type=int, default=8, help="copies of the expert bank rotated over steps")
     ap.add_argument("--distinct", type=int, default=32, help="distinct quantized experts tiled over the slots")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -517,9 +599,13 @@ def main():
     _lib.lib()
     names = ["decode_bs1", "decode_bs16", "prefill_2048"] if args.config == "all" else [args.config]
     for name in names:
+        if name in ROUTER_CONFIGS:
+            print(json.dumps(bench_router(name, args.steps, args.warmup, 256)), flush=True)
+            continue
         if name == "offload":
             steps, warmup = (64, 16) if args.steps == 200 and args.warmup == 10 else (args.steps, args.warmup)
-            print(json.dumps(bench_offload(steps, warmup, args.distinct, args.copy_streams)), flush=True)
+            print(json.dumps(bench_offload(steps, warmup, args.distinct, args.copy_streams,
+                                           not args.no_cpu_baseline)), flush=True)
             continue
         steps, warmup = args.steps, args.warmup
         if name == "prefill_2048":
