@@ -13,7 +13,8 @@
 // not depend on timing.  Rows past T or E read zeros and are not written.
 //   decode (T <= 16): MI = NJ = 1, one workgroup per 16 experts: the weights
 //                     are the traffic (E*H*2 bytes), streamed by E/16 CUs.
-//   larger T:         MI = 2, NJ = 4 (32 tokens x 64 experts per workgroup).
+//   larger T:         MI = 2, NJ = 4 (32 tokens x 64 experts per workgroup),
+//                     loads in two groups of five 32-column chunks.
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -54,7 +55,7 @@ __global__ void __launch_bounds__(kRW * kWave) router_logits_kernel(const uint16
     // G chunks of 32 columns per group: every load of a group is issued before its first MFMA (decode: the
     // whole range at once).  Chunks past the range, and lanes past T or E, load zeros (an offset past the
     // resource), which add nothing.
-    constexpr int G = (MI + NJ <= 2) ? 10 : 4;
+    constexpr int G = (MI + NJ <= 2) ? 10 : 5;
     for (int c0 = 0; c0 < kw; c0 += 32 * G) {
         u32x4_t a[G][MI], b[G][NJ];
 #pragma unroll
