@@ -26,8 +26,10 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
 // assignments [1024 b, 1024 b + 1024).  perm_count writes each block's
 // per-expert histogram; perm_scatter (one workgroup per block again) adds the
 // histograms of the earlier blocks and the per-expert totals to get where its
-// assignments of each expert start, then ranks them stably inside the block
-// (wave ballots, waves in order) and scatters them.
+// assignments of each expert start, then ranks them stably inside the block:
+// wave ballots give each assignment's rank among its wave's assignments of
+// the same expert, and a per-(wave, expert) count table scanned over the
+// waves gives each wave's start, so all waves scatter at once.
 constexpr int kPermBlock = 1024;
 
 __global__ void __launch_bounds__(1024) perm_count_kernel(const int32_t* __restrict__ ids, int n, int E,
@@ -49,6 +51,7 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __res
                                                              int32_t* __restrict__ assign_pos) {
     __shared__ int run[kMaxE];
     __shared__ int wsum[16];
+    __shared__ int wcnt[16][kMaxE];  // per wave: its assignments of each expert, then where they start
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int b = blockIdx.x;
     // per expert (one per thread): total over all blocks, and the part in blocks before b
@@ -77,7 +80,7 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __res
         if (b == 0) offsets[tid] = excl;
     }
     if (b == 0 && tid == 0) offsets[E] = n;
-    __syncthreads();
+    for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -91,17 +94,22 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __res
         peers &= on ? m : ~m;
     }
     const int rank = __popcll(peers & lt_mask);
-    const int cw = __popcll(peers);
-    const int last_wave = (min(kPermBlock, n - b * kPermBlock) - 1) / kWave;
-    for (int w2 = 0; w2 <= last_wave; ++w2) {
-        if (wave == w2 && valid) {
-            const int b0 = run[e];
-            const int pos = b0 + rank;
-            if (rank == 0) run[e] = b0 + cw;
-            sorted_assign[pos] = a;
-            assign_pos[a] = pos;
+    __syncthreads();  // wcnt cleared, run set
+    if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (tid < E) {  // each wave's start for expert tid: run[tid] plus the counts of the waves before it
+        int acc = run[tid];
+        for (int w2 = 0; w2 < 16; ++w2) {
+            const int c = wcnt[w2][tid];
+            wcnt[w2][tid] = acc;
+            acc += c;
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    if (valid) {
+        const int pos = wcnt[wave][e] + rank;
+        sorted_assign[pos] = a;
+        assign_pos[a] = pos;
     }
 }
 
