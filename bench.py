@@ -234,9 +234,10 @@ def parity_sample(inp, res, tokens):
 
 # ---------------------------------------------------------------- offload
 
-def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_cpu: bool = True):
-    """48 MoE layers whose 256 experts live in pinned host memory behind one HBM cache of 37% of the
-    12,288 expert-layer slots (global LRU, cold start).  Per layer-step: route on the GPU, one D2H copy of
+def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_cpu: bool = True,
+                  residency: float = 0.37):
+    """48 MoE layers whose 256 experts live in pinned host memory behind one HBM cache holding `residency`
+    (default 37%) of the 12,288 expert-layer slots (global LRU, cold start).  Per layer-step: route on the GPU, one D2H copy of
     the ids, host LRU plan, misses copied on a side stream while the hits-only forward runs, then the
     misses-only forward accumulates.  With want_cpu, the CPU leg checks the host LRU and the last layer-step
     against the oracle.  Returns the JSON dict."""
@@ -248,7 +249,7 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
     seed = 48
     r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
     sb = synth.slot_nbytes(H, I)
-    n_slots = int(0.37 * L * E)
+    n_slots = max(1, min(L * E, int(residency * L * E)))
     t0 = time.time()
     base_np = synth.make_bank(r_w, H, I, E, distinct)          # 256 base experts (distinct of them quantized)
     log(f"offload: quantized {min(distinct, E)} distinct experts into {E} base slots in {time.time() - t0:.1f}s")
@@ -398,7 +399,7 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
         "value": round(layer_tok_s, 2), "unit": "layer-tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(wall * 1e3 / steps, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "offload_48x256_cache37", "H": H, "I": I, "E": E, "k": k, "T": T, "layers": L,
+        "config": {"workload": f"offload_48x256_cache{round(100 * n_slots / (L * E))}", "H": H, "I": I, "E": E, "k": k, "T": T, "layers": L,
                    "cache_slots": n_slots, "residency": round(n_slots / (L * E), 4), "routing": "Zipf(1.2) per layer",
                    "host_banks": f"{E} pinned base slots ({E * sb / 1e9:.2f} GB); expert (l, e) = base (e + 37 l) mod {E}",
                    "distinct_quantized_experts": min(distinct, E), "parallelism": "single GPU"},
@@ -580,6 +581,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=320)
     ap.add_argument("--copy-streams", type=int, default=2, help="offload: side streams the misses are copied on")
+    ap.add_argument("--residency", type=float, default=0.37,
+                    help="offload: fraction of the 48 x 256 expert-layers the HBM cache holds")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (for calibrating HBM byte counters) and exit")
     args = ap.parse_args()
@@ -605,7 +608,7 @@ def main():
         if name == "offload":
             steps, warmup = (64, 16) if args.steps == 200 and args.warmup == 10 else (args.steps, args.warmup)
             print(json.dumps(bench_offload(steps, warmup, args.distinct, args.copy_streams,
-                                           not args.no_cpu_baseline)), flush=True)
+                                           not args.no_cpu_baseline, args.residency)), flush=True)
             continue
         steps, warmup = args.steps, args.warmup
         if name == "prefill_2048":
