@@ -139,7 +139,8 @@ def _check_router_logits(got, x, w, what):
 
 
 @pytest.mark.parametrize("T,H,E", [(1, 2560, 256), (3, 2560, 256), (16, 2560, 256), (17, 2560, 256),
-                                   (300, 2560, 256), (5, 256, 8), (20, 512, 1000), (33, 768, 40)])
+                                   (300, 2560, 256), (5, 256, 8), (20, 512, 1000), (33, 768, 40), (2, 256, 1),
+                                   (16, 4096, 1024)])
 def test_router_logits_vs_oracle(T, H, E):
     _announce(f"router logits T={T} H={H} E={E}")
     x, w = _router_inputs(T, H, E, 100 + T)
