@@ -17,8 +17,11 @@
  *    enqueued; a failed call enqueues nothing and returns a nonzero status.
  *    moe_last_error() then returns a message for the calling thread.
  *  - Work is enqueued on the given stream and the call returns; device faults
- *    surface at the caller's next synchronisation.  moe_route_topk and
- *    moe_nvfp4_forward make no host synchronisation and no allocation.
+ *    surface at the caller's next synchronisation.  moe_route_topk,
+ *    moe_nvfp4_forward, moe_nvfp4_route_forward, moe_router_logits and
+ *    moe_router_topk make no host synchronisation and allocate no memory
+ *    (the prefill path creates its side stream and two events on its first
+ *    call for a given caller stream, and reuses them afterwards).
  *  - Shapes: H % 128 == 0, I % 32 == 0 (see the slot format below),
  *    1 <= k <= E <= 1024, T >= 0 (T == 0 is a no-op).
  *  - bf16 values are passed as their uint16 bit patterns.
