@@ -181,6 +181,39 @@ def test_router_topk_selects_on_its_logits():
         assert ulps.max() <= 1
 
 
+def test_router_topk_graph_replays():
+    """moe_router_topk captured in a HIP graph: every replay (with eager work in between) equals the eager call."""
+    for T in (1, 16, 300):
+        _announce(f"router_topk graph replays T={T}")
+        H, E, k = 2560, 256, 8
+        x, w = _router_inputs(T, H, E, 40 + T)
+        xd, wd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+        r = dl.Routing.empty(T, E, k)
+        logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        dl.router_route(xd, wd, k, out=r, logits=logits)
+        torch.cuda.synchronize()
+        want = [t.clone() for t in (logits, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos)]
+        nb = _lib.moe_route_workspace_bytes(T, E, k)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                _lib.check(_lib.moe_router_topk(xd, wd, T, H, E, k, logits, r.ids, r.w, r.offsets, r.sorted_assign,
+                                                r.assign_pos, ws, nb, None))
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for t in (logits, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos):
+                t.zero_()
+            dl.router_route(xd, wd, k)  # eager work between replays
+            g.replay()
+            torch.cuda.synchronize()
+            got = (logits, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos)
+            for a_, b_ in zip(got, want):
+                assert torch.equal(a_, b_), (T, rep)
+
+
 def test_router_rejects_bad_shapes_and_empty_is_noop():
     x, w = _router_inputs(4, 2560, 16, 3)
     xd, wd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
