@@ -64,6 +64,10 @@ int forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const
                  const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
                  const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream,
                  const moe::RouteOut* route);
+int validate_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
+                     const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
+                     const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes);
+moe::Layer layer_of(const moe_nvfp4_layer_t& L);
 
 }  // namespace
 
@@ -175,26 +179,36 @@ int moe_nvfp4_route_forward(const moe_nvfp4_layer_t* layer, const float* logits,
         return forward_impl(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y, accumulate,
                             ws, fws, stream, &ro);
     }
-    // routing as its own launch (its workspace after the forward's), then the forward
+    // routing as its own launch (its workspace after the forward's), then the forward; every argument is checked
+    // before the first launch
     if (!topk_ids || !topk_w || !expert_offsets || !sorted_assign || !assign_pos)
         return fail(MOE_ERR_INVALID_ARGUMENT, "moe_nvfp4_route_forward: null routing output");
-    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-    hipError_t e = moe::launch_route(logits, T, L.E, L.k, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos,
-                                     static_cast<uint8_t*>(ws) + fws, stream);
-    if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_route_forward routing launch");
-    return forward_impl(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y, accumulate, ws,
-                        fws, stream, nullptr);
+    rc = validate_forward(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y, accumulate, ws,
+                          fws);
+    if (rc != MOE_OK) return rc;
+    const moe::Layer ml = layer_of(L);
+    hipError_t e = moe::launch_route(logits, T, L.E, L.k, topk_ids, topk_w, expert_offsets, sorted_assign,
+                                     assign_pos, static_cast<uint8_t*>(ws) + fws, stream);
+    if (e == hipSuccess) {
+        if (moe::decode_path(T, L.H, L.I, L.k))
+            e = moe::launch_decode(ml, x, T, topk_w, topk_ids, expert_offsets, sorted_assign, assign_pos, y,
+                                   accumulate, ws, stream, nullptr);
+        else
+            e = moe::launch_prefill(ml, x, T, topk_w, topk_ids, expert_offsets, sorted_assign, assign_pos, y,
+                                    accumulate, ws, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_route_forward launch");
+    return MOE_OK;
 }
 
 }  // extern "C"
 
 namespace {
 
-int forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
-                 const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
-                 const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream,
-                 const moe::RouteOut* route) {
+// Every check of a forward call (nothing is enqueued here).
+int validate_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
+                     const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
+                     const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes) {
     if (!layer) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_nvfp4_forward: layer is NULL");
     const moe_nvfp4_layer_t& L = *layer;
     if (!shape_ok(L.H, L.I))
@@ -223,18 +237,31 @@ int forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const
         return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "forward workspace %zu < %zu bytes", ws_bytes, need);
     if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
         return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-    moe::Layer ml{L.H, L.I, L.E, L.k, static_cast<const uint8_t*>(L.bank_base), L.slot_bytes, L.slot_of_expert,
-                  static_cast<const uint8_t*>(L.shared_slot), L.shared_gate_w};
+    if (!moe::decode_path(T, L.H, L.I, L.k) && !moe::prefill_shape_supported(L.H, L.I))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "prefill path does not support H=%d, I=%d", L.H, L.I);
+    return MOE_OK;
+}
+
+moe::Layer layer_of(const moe_nvfp4_layer_t& L) {
+    return moe::Layer{L.H, L.I, L.E, L.k, static_cast<const uint8_t*>(L.bank_base), L.slot_bytes, L.slot_of_expert,
+                      static_cast<const uint8_t*>(L.shared_slot), L.shared_gate_w};
+}
+
+int forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
+                 const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
+                 const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream,
+                 const moe::RouteOut* route) {
+    int rc = validate_forward(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y, accumulate,
+                              ws, ws_bytes);
+    if (rc != MOE_OK || T == 0) return rc;
+    const moe::Layer ml = layer_of(*layer);
     hipError_t e;
-    if (moe::decode_path(T, L.H, L.I, L.k)) {
+    if (moe::decode_path(T, ml.H, ml.I, ml.k))
         e = moe::launch_decode(ml, x, T, topk_w, topk_ids, expert_offsets, sorted_assign, assign_pos, y, accumulate,
                                ws, stream, route);
-    } else {
-        if (!moe::prefill_shape_supported(L.H, L.I))
-            return fail(MOE_ERR_UNSUPPORTED_SHAPE, "prefill path does not support H=%d, I=%d", L.H, L.I);
+    else
         e = moe::launch_prefill(ml, x, T, topk_w, topk_ids, expert_offsets, sorted_assign, assign_pos, y, accumulate,
                                 ws, stream);
-    }
     if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_forward launch");
     return MOE_OK;
 }

@@ -359,6 +359,30 @@ def _small_layer(rng, H, I, E, k, T, n_distinct=9):
                              rng.standard_normal((T, E)).astype(np.float32))
 
 
+def test_route_forward_bad_layer_enqueues_nothing():
+    """A layer argument the forward refuses is caught before the routing is enqueued (nothing written)."""
+    for name, T in [("decode_bs16", 12), ("prefill_2048", 64)]:
+        _announce(f"route_forward refusal {name} T={T}")
+        L = synth.make_layer(name, T=T, n_distinct=4)
+        dev = device_layer(L)
+        x, lg = device_x(L), device_logits(L)
+        r = dl.Routing.empty(T, L.E, L.k)
+        for t in (r.ids, r.offsets, r.sorted_assign, r.assign_pos):
+            t.fill_(-7)
+        nb = _lib.moe_nvfp4_route_forward_workspace_bytes(T, L.H, L.I, L.E, L.k)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        y = torch.full((T, L.H), 3.0, dtype=torch.float32, device="cuda")
+        st = dev.struct()
+        st.slot_bytes = st.slot_bytes + 256  # does not match H and I
+        rc = _lib.moe_nvfp4_route_forward(st, lg, x, T, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y, 0,
+                                          ws, nb, None)
+        torch.cuda.synchronize()
+        assert rc == _lib.MOE_ERR_INVALID_ARGUMENT
+        for t in (r.ids, r.offsets, r.sorted_assign, r.assign_pos):
+            assert bool((t == -7).all()), "routing was enqueued before the refusal"
+        assert bool((y == 3.0).all())
+
+
 def test_forward_limits():
     """The decode path at its limits: 1024 experts with top-64 (T*k = 1024 assignments, the most it takes; 64-row
     items), one token with top-64, and the smallest prefill batch (T = 17)."""
