@@ -171,9 +171,11 @@ struct DecShared {
     Tables tb;
 };
 
-// One work item.  Consumes LA (phase A) and LB (phase B) of `cur`; refills
-// LA with the loads of item na and, after phase B, LB with those of item nb.
-template <int KQW, int NRGW>
+// One work item.  Consumes LA (phase A) and LB (phase B) of `cur`; with PF,
+// refills LA with the loads of item na and, after phase B, LB with those of
+// item nb (without PF, when no workgroup has a next item, nothing is
+// prefetched: even out-of-range loads take the CU's address units).
+template <int KQW, int NRGW, bool PF>
 __device__ __forceinline__ void run_item(const DecArgs& a, DecShared& sh, const _Float16* x16, int XP, int nsl,
                                          const rsrc_t& pres, const Item& cur, ALoads<KQW>& LA, BLoads<NRGW>& LB,
                                          const Item& na, const Item& nb, int tid, int lane, int wave, int par) {
@@ -212,9 +214,11 @@ __device__ __forceinline__ void run_item(const DecArgs& a, DecShared& sh, const 
             a.rowslot[cur.shared ? T * k + cc : sh.tb.sorted[cur.begin + cc]] = cur.slot_index;
 
     // ---- the registers of phase A are free: item na's phase A loads stream from here on
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a<KQW>(a, na, wave, lane, tid, LA);
-    __builtin_amdgcn_sched_barrier(0);
+    if (PF) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a<KQW>(a, na, wave, lane, tid, LA);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     const float xinv = ldexpf(1.0f, -sh.xsh[xrow]);
 #pragma unroll
@@ -280,9 +284,11 @@ __device__ __forceinline__ void run_item(const DecArgs& a, DecShared& sh, const 
     }
 
     // ---- item nb's phase B loads
-    __builtin_amdgcn_sched_barrier(0);
-    issue_b<NRGW>(a, nb, wave, lane, LB);
-    __builtin_amdgcn_sched_barrier(0);
+    if (PF) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b<NRGW>(a, nb, wave, lane, LB);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // Prologue shared by the decode kernels (NW waves per workgroup), in two
@@ -559,7 +565,8 @@ __device__ void copy_down_globals(const DecArgs& a, const Tables& tb, int n_act,
 // next items stream while this one reduces, runs SwiGLU and finishes.
 // KQW: most 128-column steps of K = H per wave (steps wave % 4 + 4 i);
 // NRGW: most 64-row down groups per wave (groups wave + 8 i).
-template <int KQW, int NRGW, bool ROUTE>
+// MULTI: a workgroup may have several items (items beyond the grid); otherwise each has at most one.
+template <int KQW, int NRGW, bool ROUTE, bool MULTI>
 __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
     extern __shared__ __attribute__((aligned(16))) _Float16 x16[];  // (T + 1) rows of XP halves; row T is zero
     __shared__ DecShared sh;
@@ -583,7 +590,6 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
     const int G = (int)gridDim.x, c = lane & 15;
     const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
     Item it0 = decode_item(a, tb, n_act, nsl, u, true, c);
-    Item it1 = decode_item(a, tb, n_act, nsl, u + G, u + G < n_items, c);
     ALoads<KQW> LA0, LA1;
     BLoads<NRGW> LB;
     // the first item's loads, the activations to LDS, then the second item's loads (issuing loads is paced
@@ -593,15 +599,20 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
     __builtin_amdgcn_sched_barrier(0);
     stage_x<kDW>(a, xv, sh.xsh, x16, XP, tid, lane, wave);
     __syncthreads();
+    if (!MULTI) {
+        run_item<KQW, NRGW, false>(a, sh, x16, XP, nsl, pres, it0, LA0, LB, it0, it0, tid, lane, wave, 0);
+        return;
+    }
+    Item it1 = decode_item(a, tb, n_act, nsl, u + G, u + G < n_items, c);
     issue_a<KQW>(a, it1, wave, lane, tid, LA1);
     __builtin_amdgcn_sched_barrier(0);
 
     for (;;) {
         const Item it2 = decode_item(a, tb, n_act, nsl, u + 2 * G, u + 2 * G < n_items, c);
-        run_item<KQW, NRGW>(a, sh, x16, XP, nsl, pres, it0, LA0, LB, it2, it1, tid, lane, wave, 0);
+        run_item<KQW, NRGW, true>(a, sh, x16, XP, nsl, pres, it0, LA0, LB, it2, it1, tid, lane, wave, 0);
         if (u + G >= n_items) break;
         const Item it3 = decode_item(a, tb, n_act, nsl, u + 3 * G, u + 3 * G < n_items, c);
-        run_item<KQW, NRGW>(a, sh, x16, XP, nsl, pres, it1, LA1, LB, it3, it2, tid, lane, wave, 1);
+        run_item<KQW, NRGW, true>(a, sh, x16, XP, nsl, pres, it1, LA1, LB, it3, it2, tid, lane, wave, 1);
         if (u + 2 * G >= n_items) break;
         u += 2 * G;
         it0 = it2;
@@ -979,11 +990,15 @@ template <int KQW, int NRGW, bool ROUTE>
 hipError_t launch_fused(DecArgs& a, int items_max, int nsl, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW, ROUTE>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW, ROUTE, true>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW, ROUTE, false>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
+    const bool multi = items_max > g_num_cu;  // otherwise every workgroup has at most one item
     // a kernel that routes itself has every workgroup route; workgroup 0 must exist to write the routing.
     // CUs the items leave free get spare workgroups that copy the down-row globals for the combine.
     // (a.dgrow stays set only when they run, which tells the combine where to read the globals)
@@ -997,7 +1012,10 @@ hipError_t launch_fused(DecArgs& a, int items_max, int nsl, hipStream_t s) {
         a.dgrow = nullptr;
     }
     const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
-    hipLaunchKernelGGL((fused_kernel<KQW, NRGW, ROUTE>), dim3(grid), dim3(kDT), lds, s, a, nsl);
+    if (multi)
+        hipLaunchKernelGGL((fused_kernel<KQW, NRGW, ROUTE, true>), dim3(grid), dim3(kDT), lds, s, a, nsl);
+    else
+        hipLaunchKernelGGL((fused_kernel<KQW, NRGW, ROUTE, false>), dim3(grid), dim3(kDT), lds, s, a, nsl);
     return hipGetLastError();
 }
 
