@@ -757,7 +757,9 @@ __device__ __forceinline__ void wv_compute_b(const DecArgs& a, const Ring8& R, i
     }
 }
 
-template <int SL, bool ROUTE>
+// MULTI: a wave may have several items (more items than waves); otherwise each wave has at most one and
+// nothing of a next item is prefetched (even out-of-range loads take the CU's address units).
+template <int SL, bool ROUTE, bool MULTI>
 __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
     using W = WaveGeom<SL>;
     extern __shared__ __attribute__((aligned(16))) _Float16 x16[];  // (T + 1) rows of XP halves; row T is zero
@@ -794,7 +796,7 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
     __syncthreads();
     if (v >= n_items) return;  // uniform per wave; no barrier follows
     do {
-        const Item nxt = decode_item(a, sh.tb, n_act, nsl, v + stride, v + stride < n_items, c);
+        const Item nxt = decode_item(a, sh.tb, n_act, nsl, v + stride, MULTI && v + stride < n_items, c);
         const int xrow = cur.tok >= 0 ? cur.tok : T;
         const _Float16* xr = x16 + xrow * XP + 8 * g;
 
@@ -889,6 +891,10 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
         }
         // ---- the next item's first groups start streaming
         wv_compute_b<SL>(a, R0, gb, B, oscale, pres, pbase);
+        if (!MULTI) {
+            wv_compute_b<SL>(a, R1, gb + 1, B, oscale, pres, pbase);
+            break;
+        }
         __builtin_amdgcn_sched_barrier(0);
         wv_issue_glob<SL>(a, nxt, lane, gl);
         wv_issue_a<SL>(a, nxt, 0, lane, R0);
@@ -1023,14 +1029,20 @@ template <int SL, bool ROUTE>
 hipError_t launch_wave(const DecArgs& a, int items_max, int nsl, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE, true>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE, false>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int grid = items_max < g_num_cu ? items_max : g_num_cu;
     const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
-    hipLaunchKernelGGL((wave_kernel<SL, ROUTE>), dim3(grid), dim3(kWT), lds, s, a, nsl);
+    if (items_max > grid * kWW)  // some wave has a second item
+        hipLaunchKernelGGL((wave_kernel<SL, ROUTE, true>), dim3(grid), dim3(kWT), lds, s, a, nsl);
+    else
+        hipLaunchKernelGGL((wave_kernel<SL, ROUTE, false>), dim3(grid), dim3(kWT), lds, s, a, nsl);
     return hipGetLastError();
 }
 
