@@ -387,10 +387,12 @@ __device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<N
     {
         const rsrc_t rs = make_rsrc(a.slot_of_expert, (uint32_t)E * 4);
         const rsrc_t rx = make_rsrc(a.x, (uint32_t)T * H * 2);
+        // groups of loads that no lane needs are skipped (uniform conditions), so that the routing's logit
+        // loads do not queue behind out-of-range ones in the address units
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int i = tid + NT * r;
-            vs[r] = buf_load4(rs, i < E ? 4 * i : kOob);
+            vs[r] = NT * r < E ? buf_load4(rs, i < E ? 4 * i : kOob) : 0u;
         }
 #pragma unroll
         for (int p = 0; p < XRegs<NW>::XT; ++p) {
@@ -398,7 +400,7 @@ __device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<N
 #pragma unroll
             for (int i = 0; i < XRegs<NW>::XC; ++i) {
                 const int ch = lane + kWave * i;
-                xr.v[p][i] = buf_load16(rx, t < T && ch < H / 8 ? 2 * (t * H + 8 * ch) : kOob);
+                xr.v[p][i] = t < T ? buf_load16(rx, ch < H / 8 ? 2 * (t * H + 8 * ch) : kOob) : u32x4_t{0, 0, 0, 0};
             }
         }
     }
