@@ -917,7 +917,9 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
 // handles row q (q < k: assignment t*k + q; q == k: the shared expert) of
 // columns [4 cl, 4 cl + 4).  The first pass issues all of its loads before
 // the first add (rows and slices past the end read as zero).
-constexpr int kCS = 32;  // slices per row loaded in the first pass
+// CS: slices per row loaded in the first pass, the smallest instantiated
+// batch that covers nsl (out-of-range loads still take the address units).
+template <int CS>
 __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int nch) {
     __shared__ f32x4_t rr[16][16], rsh[16][16];
     __shared__ float dots[4];
@@ -933,9 +935,9 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
     float gd = 0.0f;
     for (int j = q; j < nrows; j += 16) {
         const int row = j < k ? t * k + j : T * k + t;
-        f32x4_t v[kCS];
+        f32x4_t v[CS];
 #pragma unroll
-        for (int i = 0; i < kCS; ++i)
+        for (int i = 0; i < CS; ++i)
             v[i] = __builtin_bit_cast(f32x4_t, buf_load16(pres, i < nsl ? 4 * ((row * nsl + i) * H + col) : kOob));
         f32x4_t dg;
         if (a.dgrow != nullptr) {  // uniform: the rows' globals were copied by the item kernel
@@ -949,8 +951,8 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
         __builtin_amdgcn_sched_barrier(0);
         f32x4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < kCS; ++i) sum += v[i];
-        for (int i = kCS; i < nsl; ++i)
+        for (int i = 0; i < CS; ++i) sum += v[i];
+        for (int i = CS; i < nsl; ++i)
             sum += __builtin_bit_cast(f32x4_t, buf_load16(pres, 4 * ((row * nsl + i) * H + col)));
         if (j < k) sr += sum * dg;
         else ss = sum * dg;
@@ -1112,7 +1114,9 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
     e = route ? launch_main<true>(a, I, T, k, E, nsl, s) : launch_main<false>(a, I, T, k, E, nsl, s);
     if (e != hipSuccess) return e;
     const int nch = H / 64;
-    hipLaunchKernelGGL(dcombine_kernel, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);
+    if (nsl <= 10) hipLaunchKernelGGL(dcombine_kernel<10>, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);
+    else if (nsl <= 20) hipLaunchKernelGGL(dcombine_kernel<20>, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);
+    else hipLaunchKernelGGL(dcombine_kernel<32>, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);
     return hipGetLastError();
 }
 
