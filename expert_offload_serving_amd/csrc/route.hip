@@ -57,6 +57,8 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __res
     // per expert (one per thread): total over all blocks, and the part in blocks before b
     int total = 0, before_b = 0;
     if (tid < E) {
+        // unrolled so that the histogram loads are in flight together rather than one round trip each
+#pragma unroll 8
         for (int bb = 0; bb < nblocks; ++bb) {
             const int h = block_hist[(size_t)bb * E + tid];
             total += h;
