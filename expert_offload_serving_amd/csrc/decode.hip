@@ -933,6 +933,19 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
     const rsrc_t dgres = make_rsrc(a.dgrow, (uint32_t)((size_t)(T * k + T) * H * 4));
     f32x4_t sr = {0.0f, 0.0f, 0.0f, 0.0f}, ss = {0.0f, 0.0f, 0.0f, 0.0f};
     float gd = 0.0f;
+    // this thread's chunks (tid, tid + 256) of x_t and w_g for the shared gate, loaded first so that their
+    // latency overlaps the partials' (H <= 2560: at most 320 chunks)
+    u32x4_t gx[2], gw[2];
+    {
+        const rsrc_t xres = make_rsrc(a.x + (size_t)t * H, has_shared ? (uint32_t)H * 2 : 0u);
+        const rsrc_t gres = make_rsrc(a.wg, has_shared ? (uint32_t)H * 2 : 0u);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int vv = tid + 256 * r;
+            gx[r] = buf_load16(xres, vv < H / 8 ? 16 * vv : kOob);
+            gw[r] = buf_load16(gres, vv < H / 8 ? 16 * vv : kOob);
+        }
+    }
     for (int j = q; j < nrows; j += 16) {
         const int row = j < k ? t * k + j : T * k + t;
         f32x4_t v[CS];
@@ -958,14 +971,13 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
         else ss = sum * dg;
     }
     if (has_shared) {
-        const rsrc_t xres = make_rsrc(a.x + (size_t)t * H, (uint32_t)H * 2);
-        const rsrc_t gres = make_rsrc(a.wg, (uint32_t)H * 2);
-        for (int vv = tid; vv < H / 8; vv += 256) {
-            const u32x4_t xx = buf_load16(xres, 16 * vv), ww = buf_load16(gres, 16 * vv);
-            gd = dot2_bf16(as_bf16x2(xx.x), as_bf16x2(ww.x), gd);
-            gd = dot2_bf16(as_bf16x2(xx.y), as_bf16x2(ww.y), gd);
-            gd = dot2_bf16(as_bf16x2(xx.z), as_bf16x2(ww.z), gd);
-            gd = dot2_bf16(as_bf16x2(xx.w), as_bf16x2(ww.w), gd);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            if (tid + 256 * r >= H / 8) break;  // the chunks in order, as the sum always ran
+            gd = dot2_bf16(as_bf16x2(gx[r].x), as_bf16x2(gw[r].x), gd);
+            gd = dot2_bf16(as_bf16x2(gx[r].y), as_bf16x2(gw[r].y), gd);
+            gd = dot2_bf16(as_bf16x2(gx[r].z), as_bf16x2(gw[r].z), gd);
+            gd = dot2_bf16(as_bf16x2(gx[r].w), as_bf16x2(gw[r].w), gd);
         }
         gd = wave_sum(gd);
     }
