@@ -34,9 +34,9 @@ PCIE_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction
 # kernels and scaled by what the same counters read for a plain copy of known size), with a digest of the kernel
 # sources they were taken on.  Reported as roofline.traffic only while those sources are unchanged.
 COUNTED_TRAFFIC = {
-    "decode_bs1": (29_486_757, "c37d000f2ddcb7bd"),
-    "decode_bs16": (318_853_449, "c37d000f2ddcb7bd"),
-    "prefill_2048": (1_394_842_045, "52b117e61e3109c2"),
+    "decode_bs1": (29_485_120, "55fb154bdad41245"),
+    "decode_bs16": (318_853_215, "55fb154bdad41245"),
+    "prefill_2048": (1_394_877_674, "52b117e61e3109c2"),
 }
 KERNEL_SOURCES = {"decode": ["decode.hip", "route_device.hpp", "nvfp4_device.hpp"],
                   "prefill": ["prefill.hip", "nvfp4_device.hpp"]}
