@@ -255,19 +255,20 @@ int oracle_unpack_slot(const uint8_t* slot, int H, int I, int matrix, uint8_t* c
 /* silu(z) * up with silu(z) = z / (1 + exp(-z)). */
 static double swiglu(double gate, double up) { return gate / (1.0 + exp(-gate)) * up; }
 
-/* Expert FFN for one token: a = W_gu x; h = silu(a[:I]) * a[I:]; o = W_dn h. */
-static void expert_ffn(const uint8_t* slot, int H, int I, const double* x, double* a, double* h, float* row,
+/* Expert FFN for one token from the expert's dequantised matrices:
+ * a = W_gu x; h = silu(a[:I]) * a[I:]; o = W_dn h, every sum in double in
+ * column order. */
+static void expert_ffn(const float* Wgu, const float* Wdn, int H, int I, const double* x, double* a, double* h,
                        double* o) {
-    mat_view gu = view_matrix(slot, H, I, 0), dn = view_matrix(slot, H, I, 1);
     for (int r = 0; r < 2 * I; ++r) {
-        dequant_view_row(&gu, r, row);
+        const float* row = Wgu + (size_t)r * H;
         double acc = 0.0;
         for (int c = 0; c < H; ++c) acc += (double)row[c] * x[c];
         a[r] = acc;
     }
     for (int i = 0; i < I; ++i) h[i] = swiglu(a[i], a[I + i]);
     for (int r = 0; r < H; ++r) {
-        dequant_view_row(&dn, r, row);
+        const float* row = Wdn + (size_t)r * I;
         double acc = 0.0;
         for (int c = 0; c < I; ++c) acc += (double)row[c] * h[c];
         o[r] = acc;
@@ -283,57 +284,107 @@ void oracle_shared_gate(const uint16_t* x, int T, int H, const uint16_t* wg, dou
     }
 }
 
+static int cmp_long(const void* a, const void* b) {
+    long x = *(const long*)a, y = *(const long*)b;
+    return (x > y) - (x < y);
+}
+
 /* y_t = sum_j w_tj * FFN_{ids[t,j]}(x_t) + s_t * FFN_shared(x_t), in double,
  * rounded once to f32.  Experts are found through slot_of_expert in the
  * bank (slot index, or -1 to leave that expert out); shared_slot < 0 means
  * no shared term.  Computes the n_tokens rows listed in tokens (all T when
- * tokens is NULL), y laid out in list order.  Returns 0 or -1 on bad input. */
+ * tokens is NULL), y laid out in list order.  Returns 0 or -1 on bad input.
+ *
+ * Each slot that some listed token uses is dequantised once into dense fp32
+ * matrices (the definition of the weights), every (token, expert) output
+ * o_tj is formed from them and kept in double, and each token's outputs are
+ * then added in the order j = 0..k-1, shared last. */
 int oracle_forward(int H, int I, int E, int k, const uint8_t* bank, size_t slot_bytes, const int32_t* slot_of_expert,
                    long shared_slot, const uint16_t* wg, const uint16_t* x, int T, const int32_t* ids, const float* w,
                    const int32_t* tokens, int n_tokens, float* y, int nthreads) {
     if (!oracle_shape_ok(H, I) || slot_bytes != oracle_slot_bytes(H, I)) return -1;
     if (tokens == NULL) n_tokens = T;
-    int bad = 0;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel reduction(| : bad)
+#else
+    (void)nthreads;
 #endif
-    {
-        double* xd = (double*)malloc(sizeof(double) * (size_t)H);
-        double* a = (double*)malloc(sizeof(double) * (size_t)2 * I);
-        double* h = (double*)malloc(sizeof(double) * (size_t)I);
-        double* o = (double*)malloc(sizeof(double) * (size_t)H);
-        double* acc = (double*)malloc(sizeof(double) * (size_t)H);
-        float* row = (float*)malloc(sizeof(float) * (size_t)(H > I ? H : I));
+    const int K1 = k + 1; /* per token: k routed outputs, then the shared one */
+    /* the slot of each (listed token, j) pair, -1 if it contributes nothing */
+    long* use = (long*)malloc(sizeof(long) * (size_t)n_tokens * K1);
+    for (int n = 0; n < n_tokens; ++n) {
+        int t = tokens ? tokens[n] : n;
+        if (t < 0 || t >= T) { free(use); return -1; }
+        for (int j = 0; j < k; ++j) {
+            int e = ids[(size_t)t * k + j];
+            if (e < 0 || e >= E) { free(use); return -1; }
+            use[(size_t)n * K1 + j] = slot_of_expert[e];
+        }
+        use[(size_t)n * K1 + k] = shared_slot >= 0 ? shared_slot : -1;
+    }
+    /* the distinct slots used, ascending */
+    size_t npairs = (size_t)n_tokens * K1, nd = 0;
+    long* slots = (long*)malloc(sizeof(long) * (npairs + 1));
+    for (size_t i = 0; i < npairs; ++i)
+        if (use[i] >= 0) slots[nd++] = use[i];
+    qsort(slots, nd, sizeof(long), cmp_long);
+    size_t nu = 0;
+    for (size_t i = 0; i < nd; ++i)
+        if (nu == 0 || slots[i] != slots[nu - 1]) slots[nu++] = slots[i];
+
+    double* out = (double*)calloc(npairs * (size_t)H, sizeof(double)); /* o_tj for every used pair */
+    float* Wgu = (float*)malloc(sizeof(float) * (size_t)2 * I * H);
+    float* Wdn = (float*)malloc(sizeof(float) * (size_t)H * I);
+    for (size_t u = 0; u < nu; ++u) {
+        const uint8_t* slot = bank + (size_t)slots[u] * slot_bytes;
+        mat_view gu = view_matrix(slot, H, I, 0), dn = view_matrix(slot, H, I, 1);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+        for (int r = 0; r < 2 * I + H; ++r) {
+            if (r < 2 * I) dequant_view_row(&gu, r, Wgu + (size_t)r * H);
+            else dequant_view_row(&dn, r - 2 * I, Wdn + (size_t)(r - 2 * I) * I);
+        }
+#ifdef _OPENMP
+#pragma omp parallel
+#endif
+        {
+            double* xd = (double*)malloc(sizeof(double) * (size_t)H);
+            double* a = (double*)malloc(sizeof(double) * (size_t)2 * I);
+            double* h = (double*)malloc(sizeof(double) * (size_t)I);
 #ifdef _OPENMP
 #pragma omp for schedule(dynamic, 1)
 #endif
-        for (int n = 0; n < n_tokens; ++n) {
-            int t = tokens ? tokens[n] : n;
-            if (t < 0 || t >= T) { bad = 1; continue; }
-            for (int c = 0; c < H; ++c) xd[c] = bf16_to_double(x[(size_t)t * H + c]);
-            for (int c = 0; c < H; ++c) acc[c] = 0.0;
-            for (int j = 0; j < k; ++j) {
-                int e = ids[(size_t)t * k + j];
-                if (e < 0 || e >= E) { bad = 1; continue; }
-                int s = slot_of_expert[e];
-                if (s < 0) continue;
-                expert_ffn(bank + (size_t)s * slot_bytes, H, I, xd, a, h, row, o);
-                double wj = (double)w[(size_t)t * k + j];
-                for (int c = 0; c < H; ++c) acc[c] += wj * o[c];
+            for (long i = 0; i < (long)npairs; ++i) {
+                if (use[i] != slots[u]) continue;
+                int n = (int)(i / K1), t = tokens ? tokens[n] : n;
+                for (int c = 0; c < H; ++c) xd[c] = bf16_to_double(x[(size_t)t * H + c]);
+                expert_ffn(Wgu, Wdn, H, I, xd, a, h, out + (size_t)i * H);
             }
-            if (shared_slot >= 0) {
-                double g = 0.0;
-                for (int c = 0; c < H; ++c) g += xd[c] * bf16_to_double(wg[c]);
-                double st = 1.0 / (1.0 + exp(-g));
-                expert_ffn(bank + (size_t)shared_slot * slot_bytes, H, I, xd, a, h, row, o);
-                for (int c = 0; c < H; ++c) acc[c] += st * o[c];
-            }
-            for (int c = 0; c < H; ++c) y[(size_t)n * H + c] = (float)acc[c];
+            free(xd); free(a); free(h);
         }
-        free(xd); free(a); free(h); free(o); free(acc); free(row);
     }
-    return bad ? -1 : 0;
+    for (int n = 0; n < n_tokens; ++n) {
+        int t = tokens ? tokens[n] : n;
+        double* acc = (double*)calloc((size_t)H, sizeof(double));
+        for (int j = 0; j < k; ++j) {
+            if (use[(size_t)n * K1 + j] < 0) continue;
+            double wj = (double)w[(size_t)t * k + j];
+            const double* o = out + ((size_t)n * K1 + j) * H;
+            for (int c = 0; c < H; ++c) acc[c] += wj * o[c];
+        }
+        if (shared_slot >= 0) {
+            double g = 0.0;
+            for (int c = 0; c < H; ++c) g += bf16_to_double(x[(size_t)t * H + c]) * bf16_to_double(wg[c]);
+            double st = 1.0 / (1.0 + exp(-g));
+            const double* o = out + ((size_t)n * K1 + k) * H;
+            for (int c = 0; c < H; ++c) acc[c] += st * o[c];
+        }
+        for (int c = 0; c < H; ++c) y[(size_t)n * H + c] = (float)acc[c];
+        free(acc);
+    }
+    free(use); free(slots); free(out); free(Wgu); free(Wdn);
+    return 0;
 }
 
 /* ---------------------------------------------------------------- slicing */
