@@ -23,8 +23,9 @@ MOE_ERR_HIP = 5
 EXPORTED = [
     "moe_last_error", "moe_nvfp4_slot_bytes", "moe_route_workspace_bytes", "moe_route_topk",
     "moe_nvfp4_forward_workspace_bytes", "moe_nvfp4_forward", "expert_cache_fill", "moe_cache_create",
-    "moe_cache_destroy", "moe_cache_plan", "moe_nvfp4_slice_bank", "moe_nvfp4_dequant",
+    "moe_cache_destroy", "moe_cache_plan", "moe_nvfp4_slice_bank", "moe_nvfp4_dequant", "moe_nvfp4_dequant_slot",
     "moe_nvfp4_route_forward_workspace_bytes", "moe_nvfp4_route_forward", "moe_router_logits", "moe_router_topk",
+    "moe_release_streams",
 ]
 
 
@@ -91,7 +92,11 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_slice_bank.restype = _i
         L.moe_nvfp4_slice_bank.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp]
         L.moe_nvfp4_dequant.restype = _i
-        L.moe_nvfp4_dequant.argtypes = [_vp, _i, _i, _i, _vp, _vp]
+        L.moe_nvfp4_dequant.argtypes = [_vp, _vp, _vp, _i, _i, _vp, _vp]
+        L.moe_nvfp4_dequant_slot.restype = _i
+        L.moe_nvfp4_dequant_slot.argtypes = [_vp, _i, _i, _i, _vp, _vp]
+        L.moe_release_streams.restype = _i
+        L.moe_release_streams.argtypes = []
         _lib = L
     return _lib
 
@@ -196,8 +201,16 @@ def moe_nvfp4_slice_bank(src_bank, num_slots, H, I, r, n, dst_bank, stream=None)
     return lib().moe_nvfp4_slice_bank(_ptr(src_bank), num_slots, H, I, r, n, _ptr(dst_bank), _stream(stream))
 
 
-def moe_nvfp4_dequant(slot, H, I, matrix, out, stream=None) -> int:
-    return lib().moe_nvfp4_dequant(_ptr(slot), H, I, matrix, _ptr(out), _stream(stream))
+def moe_nvfp4_dequant(codes, scales, globals_, rows, K, out, stream=None) -> int:
+    return lib().moe_nvfp4_dequant(_ptr(codes), _ptr(scales), _ptr(globals_), rows, K, _ptr(out), _stream(stream))
+
+
+def moe_nvfp4_dequant_slot(slot, H, I, matrix, out, stream=None) -> int:
+    return lib().moe_nvfp4_dequant_slot(_ptr(slot), H, I, matrix, _ptr(out), _stream(stream))
+
+
+def moe_release_streams() -> int:
+    return lib().moe_release_streams()
 
 
 class ExpertCache:

@@ -49,6 +49,9 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Largest buffer the kernels address (32-bit byte offsets in buffer resources).
+constexpr size_t kMaxBuffer = (size_t)1 << 31;
+
 // The slot format's tile: H % 128 == 0, I % 32 == 0 (the fp4 scale-block guard of issue #62).
 bool shape_ok(int H, int I) { return H > 0 && I > 0 && H % 128 == 0 && I % 32 == 0; }
 
@@ -221,6 +224,11 @@ int validate_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, c
     if (L.slot_bytes != sb)
         return fail(MOE_ERR_INVALID_ARGUMENT, "slot_bytes %zu does not match H=%d, I=%d (%zu bytes)", L.slot_bytes,
                     L.H, L.I, sb);
+    // the kernels address every buffer through 32-bit offsets: each must stay below 2 GiB
+    if (sb >= kMaxBuffer || (size_t)T * L.H * 4 >= kMaxBuffer ||
+        moe::forward_ws_bytes(T, L.H, L.I, L.E, L.k) >= kMaxBuffer)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T=%d H=%d I=%d k=%d: a slot, x, y or the workspace reaches 2 GiB", T,
+                    L.H, L.I, L.k);
     if (T == 0) return MOE_OK;
     if (!L.bank_base || !L.slot_of_expert || L.num_slots < 1)
         return fail(MOE_ERR_INVALID_ARGUMENT, "layer bank, slot map and num_slots are required");
@@ -243,8 +251,8 @@ int validate_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, c
 }
 
 moe::Layer layer_of(const moe_nvfp4_layer_t& L) {
-    return moe::Layer{L.H, L.I, L.E, L.k, static_cast<const uint8_t*>(L.bank_base), L.slot_bytes, L.slot_of_expert,
-                      static_cast<const uint8_t*>(L.shared_slot), L.shared_gate_w};
+    return moe::Layer{L.H, L.I, L.E, L.k, static_cast<const uint8_t*>(L.bank_base), L.slot_bytes, L.num_slots,
+                      L.slot_of_expert, static_cast<const uint8_t*>(L.shared_slot), L.shared_gate_w};
 }
 
 int forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
@@ -316,7 +324,21 @@ int moe_nvfp4_slice_bank(const void* src_bank, int num_slots, int H, int I, int 
     return MOE_OK;
 }
 
-int moe_nvfp4_dequant(const void* slot, int H, int I, int matrix, float* out, hipStream_t stream) {
+int moe_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* globals, int rows, int K, float* out,
+                      hipStream_t stream) {
+    if (rows < 0 || K <= 0 || K % 16 != 0)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "rows must be >= 0 and K a positive multiple of 16 (rows=%d, K=%d)", rows,
+                    K);
+    if (rows == 0) return MOE_OK;
+    if (!codes || !scales || !globals || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (reinterpret_cast<uintptr_t>(codes) % 4 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "codes must be 4-byte and out 16-byte aligned");
+    hipError_t e = moe::launch_dequant_rows(codes, scales, globals, rows, K, out, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_dequant launch");
+    return MOE_OK;
+}
+
+int moe_nvfp4_dequant_slot(const void* slot, int H, int I, int matrix, float* out, hipStream_t stream) {
     if (!shape_ok(H, I))
         return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H must be a positive multiple of 128 and I of 32");
     if (matrix != 0 && matrix != 1) return fail(MOE_ERR_INVALID_ARGUMENT, "matrix must be 0 (gate_up) or 1 (down)");
@@ -324,7 +346,13 @@ int moe_nvfp4_dequant(const void* slot, int H, int I, int matrix, float* out, hi
     if (reinterpret_cast<uintptr_t>(slot) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
         return fail(MOE_ERR_INVALID_ARGUMENT, "slot and out must be 16-byte aligned");
     hipError_t e = moe::launch_dequant(static_cast<const uint8_t*>(slot), H, I, matrix, out, stream);
-    if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_dequant launch");
+    if (e != hipSuccess) return hip_fail(e, "moe_nvfp4_dequant_slot launch");
+    return MOE_OK;
+}
+
+int moe_release_streams(void) {
+    hipError_t e = moe::release_side_streams();
+    if (e != hipSuccess) return hip_fail(e, "moe_release_streams");
     return MOE_OK;
 }
 

@@ -24,6 +24,11 @@
 // undone exactly on the fp32 result.  The hidden slice is rescaled the same
 // way before phase B.  Accumulation is fp32 and every sum runs in a fixed
 // order, so results are bit-reproducible.
+#include <map>
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 #include "route_device.hpp"
@@ -39,6 +44,7 @@ constexpr int kMaxE = 1024;         // experts (64 per ballot chunk)
 struct DecArgs {
     const uint8_t* bank;
     size_t slot_bytes;
+    int num_slots;
     const int32_t* slot_of_expert;
     const uint8_t* shared;
     const uint16_t* wg;
@@ -59,6 +65,10 @@ struct DecArgs {
     int32_t *r_ids, *r_offsets, *r_sorted, *r_pos;
     float* r_w;
 };
+
+// A slot index outside [0, num_slots) leaves its expert out (-1), like a
+// negative one: the kernels never address memory outside the bank.
+__device__ __forceinline__ int slot_or_skip(int sl, int num_slots) { return sl >= 0 && sl < num_slots ? sl : -1; }
 
 // Routing tables staged in LDS once per workgroup.
 struct Tables {
@@ -347,7 +357,7 @@ __device__ __forceinline__ int stage_tables(const DecArgs& a, Tables& tb, XRegs<
     for (int r = 0; r < R; ++r) {
         const int i = tid + NT * r;
         if (i <= E) tb.off[i] = (int)vo[r];
-        if (i < E) tb.slot[i] = (int)vs[r];
+        if (i < E) tb.slot[i] = slot_or_skip((int)vs[r], a.num_slots);
     }
 #pragma unroll
     for (int r = 0; r < RA; ++r) {
@@ -415,7 +425,7 @@ __device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<N
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int i = tid + NT * r;
-        if (i < E) tb.slot[i] = (int)vs[r];
+        if (i < E) tb.slot[i] = slot_or_skip((int)vs[r], a.num_slots);
     }
     __syncthreads();
     const bool out = blockIdx.x == 0;
@@ -996,39 +1006,54 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
     *yp = out;
 }
 
-int g_num_cu = 0;
-
 constexpr size_t kXLdsMax = (size_t)(kDecodeMaxT + 1) * (2560 + 8) * 2;
 
-hipError_t init_device_info() {
-    if (g_num_cu != 0) return hipSuccess;
+// Compute units of the current device (queried once per device; thread-safe).
+hipError_t device_cus(int& ncu) {
+    static std::mutex mu;
+    static std::map<int, int> cus;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&g_num_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cus.find(dev);
+    if (it != cus.end()) {
+        ncu = it->second;
+        return hipSuccess;
+    }
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) cus[dev] = ncu;
+    return e;
+}
+
+// The dynamic LDS limit of a kernel raised to what the activations need, once per (kernel, device); thread-safe.
+hipError_t allow_lds(const void* fn) {
+    static std::mutex mu;
+    static std::set<std::pair<const void*, int>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({fn, dev})) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
+    if (e == hipSuccess) done.insert({fn, dev});
     return e;
 }
 
 template <int KQW, int NRGW, bool ROUTE>
-hipError_t launch_fused(DecArgs& a, int items_max, int nsl, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW, ROUTE, true>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW, ROUTE, false>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    const bool multi = items_max > g_num_cu;  // otherwise every workgroup has at most one item
+hipError_t launch_fused(DecArgs& a, int items_max, int nsl, int ncu, hipStream_t s) {
+    hipError_t e = allow_lds(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW, ROUTE, true>));
+    if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void*>(&fused_kernel<KQW, NRGW, ROUTE, false>));
+    if (e != hipSuccess) return e;
+    const bool multi = items_max > ncu;  // otherwise every workgroup has at most one item
     // a kernel that routes itself has every workgroup route; workgroup 0 must exist to write the routing.
     // CUs the items leave free get spare workgroups that copy the down-row globals for the combine.
     // (a.dgrow stays set only when they run, which tells the combine where to read the globals)
-    int grid = items_max < g_num_cu ? items_max : g_num_cu;
+    int grid = items_max < ncu ? items_max : ncu;
     a.n_spare = 0;
-    if (grid < g_num_cu && a.dgrow != nullptr) {
+    if (grid < ncu && a.dgrow != nullptr) {
         const int rows = a.T * a.k + a.T;
-        a.n_spare = min(g_num_cu - grid, (rows + kDgBatch - 1) / kDgBatch);
+        a.n_spare = min(ncu - grid, (rows + kDgBatch - 1) / kDgBatch);
         grid += a.n_spare;
     } else {
         a.dgrow = nullptr;
@@ -1042,18 +1067,11 @@ hipError_t launch_fused(DecArgs& a, int items_max, int nsl, hipStream_t s) {
 }
 
 template <int SL, bool ROUTE>
-hipError_t launch_wave(const DecArgs& a, int items_max, int nsl, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE, true>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE, false>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXLdsMax);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    const int grid = items_max < g_num_cu ? items_max : g_num_cu;
+hipError_t launch_wave(const DecArgs& a, int items_max, int nsl, int ncu, hipStream_t s) {
+    hipError_t e = allow_lds(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE, true>));
+    if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE, false>));
+    if (e != hipSuccess) return e;
+    const int grid = items_max < ncu ? items_max : ncu;
     const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
     if (items_max > grid * kWW)  // some wave has a second item
         hipLaunchKernelGGL((wave_kernel<SL, ROUTE, true>), dim3(grid), dim3(kWT), lds, s, a, nsl);
@@ -1063,17 +1081,17 @@ hipError_t launch_wave(const DecArgs& a, int items_max, int nsl, hipStream_t s) 
 }
 
 template <bool ROUTE>
-hipError_t launch_main(DecArgs& a, int I, int T, int k, int E, int& nsl, hipStream_t s) {
+hipError_t launch_main(DecArgs& a, int I, int T, int k, int E, int& nsl, int ncu, hipStream_t s) {
     // 32-row items; when they would outnumber the waves of one pass, 64-row items (half the partials)
     nsl = I / kSl;
     const int rows_max = (T * k < E ? T * k : E) + 1;
-    if (rows_max * nsl < MOE_WAVE_MIN_ITEMS) return launch_fused<5, 5, ROUTE>(a, rows_max * nsl, nsl, s);
+    if (rows_max * nsl < MOE_WAVE_MIN_ITEMS) return launch_fused<5, 5, ROUTE>(a, rows_max * nsl, nsl, ncu, s);
     a.dgrow = nullptr;  // the wave-item kernel leaves the combine to read the globals through the row slots
-    if (rows_max * nsl > g_num_cu * kWW && I % 64 == 0) {
+    if (rows_max * nsl > ncu * kWW && I % 64 == 0) {
         nsl = I / 64;
-        return launch_wave<64, ROUTE>(a, rows_max * nsl, nsl, s);
+        return launch_wave<64, ROUTE>(a, rows_max * nsl, nsl, ncu, s);
     }
-    return launch_wave<32, ROUTE>(a, rows_max * nsl, nsl, s);
+    return launch_wave<32, ROUTE>(a, rows_max * nsl, nsl, ncu, s);
 }
 
 }  // namespace
@@ -1101,7 +1119,7 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
     const int H = L.H, I = L.I, E = L.E, k = L.k;
     const WsLayout wl = ws_layout(T, H, I, E, k);
     DecArgs a;
-    a.bank = L.bank; a.slot_bytes = L.slot_bytes; a.slot_of_expert = L.slot_of_expert;
+    a.bank = L.bank; a.slot_bytes = L.slot_bytes; a.num_slots = L.num_slots; a.slot_of_expert = L.slot_of_expert;
     a.shared = L.shared; a.wg = L.wg; a.x = x;
     a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
     a.w = w; a.offsets = offsets; a.sorted_assign = sorted_assign;
@@ -1120,10 +1138,11 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
     a.r_offsets = route ? route->offsets : nullptr;
     a.r_sorted = route ? route->sorted_assign : nullptr;
     a.r_pos = route ? route->assign_pos : nullptr;
-    hipError_t e = init_device_info();
+    int ncu = 0;
+    hipError_t e = device_cus(ncu);
     if (e != hipSuccess) return e;
     int nsl = 0;
-    e = route ? launch_main<true>(a, I, T, k, E, nsl, s) : launch_main<false>(a, I, T, k, E, nsl, s);
+    e = route ? launch_main<true>(a, I, T, k, E, nsl, ncu, s) : launch_main<false>(a, I, T, k, E, nsl, ncu, s);
     if (e != hipSuccess) return e;
     const int nch = H / 64;
     if (nsl <= 10) hipLaunchKernelGGL(dcombine_kernel<10>, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);

@@ -9,6 +9,8 @@
 
 namespace moe {
 
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
 // Routing (route.hip)
 size_t route_ws_bytes(int T, int E, int k);
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,
@@ -23,6 +25,7 @@ struct Layer {
     int H, I, E, k;
     const uint8_t* bank;
     size_t slot_bytes;
+    int num_slots;              // slot indices outside [0, num_slots) leave their expert out
     const int32_t* slot_of_expert;
     const uint8_t* shared;      // nullptr: no shared expert
     const uint16_t* wg;         // bf16 [H]
@@ -51,12 +54,13 @@ inline bool decode_path(int T, int H, int I, int k) {
 // (per-row slot of the row's expert) and `dgrow` (per-row copies of the
 // expert's down-row globals); the prefill path uses the others:
 //   h      hidden state, (T*k + T) rows of I fp16 values
+//   hx     the exponent of each 128-column tile of h, (T*k + T) rows of ceil(I/128) i32
 //   o      per-assignment expert outputs, (T*k + T) rows of H f32
 //   s      shared-gate sigmoid per token, T f32
 //   x16    scaled fp16 activations [T, H]; xinv: their inverse scales [T]
 //   tiles  work lists: 4 counts, then 3 classes x tile_cap (group, m0) pairs
 struct WsLayout {
-    size_t part, dg, dgrow, h, o, s, x16, xinv, tiles, total;
+    size_t part, dg, dgrow, h, hx, o, s, x16, xinv, tiles, total;
     int tile_cap;
 };
 inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -71,7 +75,8 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
     }
     const size_t rows = (size_t)T * k + T;
     L.h = 0;
-    L.o = L.h + align256(rows * I * 2);
+    L.hx = L.h + align256(rows * I * 2);
+    L.o = L.hx + align256(rows * (size_t)ceil_div(I, 128) * 4);
     L.s = L.o + align256(rows * H * 4);
     L.x16 = L.s + align256((size_t)T * 4);
     L.xinv = L.x16 + align256((size_t)T * H * 2);
@@ -102,15 +107,17 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
 
 // Prefill path, T > 16 (prefill.hip)
 bool prefill_shape_supported(int H, int I);
+hipError_t release_side_streams();
 hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                           const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
                           int accumulate, void* ws, hipStream_t s);
 
 // Utilities (util.hip)
 hipError_t launch_dequant(const uint8_t* slot, int H, int I, int matrix, float* out, hipStream_t s);
+hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, const float* globals, int rows, int K,
+                               float* out, hipStream_t s);
 hipError_t launch_slice_bank(const uint8_t* src, int num_slots, int H, int I, int r, int n, uint8_t* dst,
                              hipStream_t s);
 
-__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace moe

@@ -16,8 +16,15 @@
 //    conversion exact in the fp16 normal range (values more than 28 binades
 //    below the row maximum round to fp16 subnormals); the epilogue undoes
 //    the scale exactly.
-//  - hidden state: silu(gate) * up is stored in fp16 (11-bit significand,
-//    saturated at the fp16 maximum) as the A operand of the down GEMM.
+//  - hidden state: silu(gate) * up is stored in fp16 as the A operand of
+//    the down GEMM, each (token row, 128-column tile) times its own power of
+//    two that puts the tile's largest magnitude in [2^14, 2^15) (the tile's
+//    exponent is kept beside it).  The down GEMM, whose 128-column K steps
+//    are exactly those tiles, brings a row's tiles to the row's smallest
+//    exponent while staging them (exact unless a value falls below the fp16
+//    range relative to the row maximum) and undoes that exponent on the fp32
+//    result, so the hidden state neither saturates nor loses precision to
+//    fp16 subnormals whatever its magnitude.
 // K is consumed in steps of 128 (four 32-column MFMA chunks).  Weight
 // fragments come straight from the slot's operand-order records: a gate_up
 // record holds one 16-row tile for all four chunks of a step, a down record
@@ -49,6 +56,7 @@ constexpr int kClasses = 3;       // row-tile classes: 128, 64, 32 rows
 struct PrefillArgs {
     const uint8_t* bank;
     size_t slot_bytes;
+    int num_slots;
     const int32_t* slot_of_expert;
     const uint8_t* shared;
     const uint16_t* wg;
@@ -59,7 +67,9 @@ struct PrefillArgs {
     const int32_t* offsets;
     const int32_t* sorted_assign;
     const int32_t* assign_pos;
-    _Float16* hbuf;   // fp16 [(T*k + T), I]
+    _Float16* hbuf;   // fp16 [(T*k + T), I], tile (row, c) scaled by 2^hexp[row, c]
+    int* hexp;        // i32  [(T*k + T), KT]: exponent of each 128-column tile of hbuf (kNoExp: all zero)
+    int KT;           // 128-column tiles of I
     float* obuf;      // f32  [(T*k + T), H]
     _Float16* x16;    // fp16 [T, H] scaled activations
     float* xinv;      // f32  [T] inverse activation scale
@@ -79,9 +89,11 @@ __device__ __forceinline__ int group_begin(const PrefillArgs& a, int g) {
 __device__ __forceinline__ int group_end(const PrefillArgs& a, int g) {
     return g < a.E ? a.offsets[g + 1] : a.T * a.k + a.T;
 }
+// An expert whose slot index is negative or not below num_slots is left out.
+__device__ __forceinline__ bool slot_in_bank(const PrefillArgs& a, int sl) { return sl >= 0 && sl < a.num_slots; }
 __device__ __forceinline__ bool group_active(const PrefillArgs& a, int g) {
     if (g == a.E) return a.shared != nullptr;
-    return a.offsets[g + 1] > a.offsets[g] && a.slot_of_expert[g] >= 0;
+    return a.offsets[g + 1] > a.offsets[g] && slot_in_bank(a, a.slot_of_expert[g]);
 }
 __device__ __forceinline__ const uint8_t* group_slot(const PrefillArgs& a, int g) {
     return g == a.E ? a.shared : a.bank + (size_t)a.slot_of_expert[g] * a.slot_bytes;
@@ -211,6 +223,34 @@ __device__ __forceinline__ f16x8_t lds_frag(const _Float16* p) {
     return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(p));
 }
 
+// Exponent of a hidden-state tile that is all zero: larger than any real one,
+// so it never is a row's minimum, and aligning to a real one gives zeros.
+constexpr int kNoExp = 1 << 20;
+
+__device__ __forceinline__ int tile_shift(float amax) { return amax > 0.0f ? fp16_shift(amax) : kNoExp; }
+
+// 2^n as an fp16 pair for n in [-24, 0] (subnormal below -14); 0 below -24.
+__device__ __forceinline__ f16x2_t pow2_f16x2(int n) {
+    const uint16_t b = n < -24 ? 0 : (n < -14 ? (uint16_t)(1u << (n + 24)) : (uint16_t)((n + 15) << 10));
+    const _Float16 v = __builtin_bit_cast(_Float16, b);
+    return f16x2_t{v, v};
+}
+
+// Eight fp16 values times 2^d (d <= 0), in two exact power-of-two steps
+// (the second rounds only results below the fp16 normal range).
+__device__ __forceinline__ u32x4_t scale_h8(u32x4_t v, int d) {
+    const int d1 = d > -14 ? d : -14;
+    const f16x2_t f1 = pow2_f16x2(d1), f2 = pow2_f16x2(d - d1);
+    u32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f16x2_t h = __builtin_bit_cast(f16x2_t, word_of(v, i)) * f1 * f2;
+        const uint32_t u = __builtin_bit_cast(uint32_t, h);
+        if (i == 0) o.x = u; else if (i == 1) o.y = u; else if (i == 2) o.z = u; else o.w = u;
+    }
+    return o;
+}
+
 // ------------------------------------------------------------------ grouped GEMM tiles
 // One workgroup (NW waves) computes a BM-token tile (BM = 128, 64 or 32)
 // against a block of weight rows: gate_up: matching gate and up rows, down:
@@ -232,8 +272,13 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
     constexpr int MI = BM / 16 / WM;         // 16-row token blocks per wave
     constexpr int NT = NW * kWave;           // threads
     constexpr int AQ = BM * 16 / NT;         // activation chunks per thread per step
+    // a gate_up workgroup's h-columns are exactly one 128-column K step of the down GEMM (one exponent tile)
+    static_assert(!GATEUP || NWN * 8 * NB == BK, "gate_up column tile must match the down K step");
     __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * APITCH];
     __shared__ int tok[BM];
+    // gate_up: per-(row, wave along the weight rows) maximum of |h|; down: each row's smallest tile exponent
+    __shared__ float smax[GATEUP ? NWN : 1][BM];
+    __shared__ int semin[BM];
 
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs (block b to XCD b % 8), so the active
     // blocks of XCD x take one contiguous range of (tile, column tile) pairs.  The column tiles of a row tile,
@@ -278,17 +323,47 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
         const int mm = m < cnt ? m : 0;  // rows past the group read a valid row; their outputs are dropped
         aoff[q] = GATEUP ? 2 * tok[mm] * H : 2 * (gb + m0 + mm) * I;
     }
+    // down: the hidden-state tiles of a row carry their own exponents; each is brought to the row's smallest
+    // (the exponent of its largest tile) while staged, and that one is undone in the epilogue
+    const rsrc_t xres = make_rsrc(a.hexp, GATEUP ? 0u : (uint32_t)((size_t)(T * k + T) * a.KT * 4));
+    int emin[GATEUP ? 1 : AQ], eoff[GATEUP ? 1 : AQ];
+    if (!GATEUP) {
+        int ev[AQ][4];
+#pragma unroll
+        for (int q = 0; q < AQ; ++q) {
+            const int m = arow0 + (NT / 16) * q;
+            eoff[q] = 4 * (gb + m0 + (m < cnt ? m : 0)) * a.KT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ev[q][j] = (int)buf_load4(xres, j < a.KT ? eoff[q] + 4 * j : kOob);
+        }
+#pragma unroll
+        for (int q = 0; q < AQ; ++q) {
+            int e = kNoExp;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e = j < a.KT ? min(e, ev[q][j]) : e;
+            for (int j = 4; j < a.KT; ++j) e = min(e, (int)buf_load4(xres, eoff[q] + 4 * j));
+            emin[q] = e;
+            if (ach == 0) semin[arow0 + (NT / 16) * q] = e;
+        }
+    }
     u32x4_t ra[AQ];
+    int rex[GATEUP ? 1 : AQ];
     auto load_a = [&](int step) {
         const int kk = step * BK + 8 * ach;
         const bool ok = step < nsteps && kk < K;
+        if (!GATEUP) {
+#pragma unroll
+            for (int q = 0; q < AQ; ++q) rex[q] = (int)buf_load4(xres, step < nsteps ? eoff[q] + 4 * step : kOob);
+        }
 #pragma unroll
         for (int q = 0; q < AQ; ++q) ra[q] = buf_load16(ares, ok ? aoff[q] + 2 * kk : kOob);
     };
     auto store_a = [&](int buf) {
 #pragma unroll
-        for (int q = 0; q < AQ; ++q)
-            *reinterpret_cast<u32x4_t*>(&sA[buf][(arow0 + (NT / 16) * q) * APITCH + 8 * ach]) = ra[q];
+        for (int q = 0; q < AQ; ++q) {
+            const u32x4_t v = GATEUP ? ra[q] : scale_h8(ra[q], emin[GATEUP ? 0 : q] - rex[GATEUP ? 0 : q]);
+            *reinterpret_cast<u32x4_t*>(&sA[buf][(arow0 + (NT / 16) * q) * APITCH + 8 * ach]) = v;
+        }
     };
 
     // ---- weight records of this wave
@@ -392,40 +467,82 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
 #undef MOE_PIN
 
     // ---- epilogue: lane holds token rows 4 q4 + [0, 4) of column l16 of each 16x16 block
+    const rsrc_t gres = make_rsrc(slot, (uint32_t)a.slot_bytes);
     if (GATEUP) {
-        const float* gl = reinterpret_cast<const float*>(slot + a.gu_glob);
+        // h = silu(gate) * up in fp32; the tile's 128 columns are this workgroup's: its largest |h| per row
+        // (over the 16 lanes of a column block, the wave's blocks, then the waves) sets the row's exponent
+        constexpr int NC = NB / 2;
+        float hv[NC][MI][4];
+        float rmax[MI][4];
 #pragma unroll
-        for (int cb = 0; cb < NB / 2; ++cb) {
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rmax[i][r] = 0.0f;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
             const int hc = hc0 + 16 * cb + l16;
-            if (hc >= I) continue;
-            const float gg = gl[hc], gu = gl[I + hc];
+            const bool cok = hc < I;
+            const float gg = __uint_as_float(buf_load4(gres, cok ? (int)a.gu_glob + 4 * hc : kOob));
+            const float gu = __uint_as_float(buf_load4(gres, cok ? (int)a.gu_glob + 4 * (I + hc) : kOob));
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = 16 * MI * wm + 16 * i + 4 * q4 + r;
-                    if (m >= cnt) continue;
-                    const float inv = a.xinv[tok[m]];
+                    const bool ok = cok && m < cnt;
+                    const float inv = a.xinv[tok[ok ? m : 0] >= 0 ? tok[ok ? m : 0] : 0];
                     const float gate = acc[i][cb][r] * inv * gg;
                     const float up = acc[i][NB / 2 + cb][r] * inv * gu;
-                    float h = silu_fast(gate) * up;
-                    h = fminf(fmaxf(h, -65504.0f), 65504.0f);
-                    a.hbuf[(size_t)(gb + m0 + m) * I + hc] = (_Float16)h;
+                    const float h = ok ? silu_fast(gate) * up : 0.0f;
+                    hv[cb][i][r] = h;
+                    rmax[i][r] = fmaxf(rmax[i][r], fabsf(h));
                 }
         }
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = rmax[i][r];
+                v = fmaxf(v, __shfl_xor(v, 1, kWave));
+                v = fmaxf(v, __shfl_xor(v, 2, kWave));
+                v = fmaxf(v, __shfl_xor(v, 4, kWave));
+                v = fmaxf(v, __shfl_xor(v, 8, kWave));
+                if (l16 == 0) smax[wn][16 * MI * wm + 16 * i + 4 * q4 + r] = v;
+            }
+        __syncthreads();
+        const int KT = a.KT;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * MI * wm + 16 * i + 4 * q4 + r;
+                float tmax = 0.0f;
+#pragma unroll
+                for (int w = 0; w < NWN; ++w) tmax = fmaxf(tmax, smax[w][m]);
+                const int e = tile_shift(tmax);
+                if (m < cnt && wn == 0 && l16 == 0) a.hexp[(size_t)(gb + m0 + m) * KT + nt] = e;
+                const float sc = ldexpf(1.0f, e == kNoExp ? 0 : e);
+#pragma unroll
+                for (int cb = 0; cb < NC; ++cb) {
+                    const int hc = hc0 + 16 * cb + l16;
+                    if (hc < I && m < cnt) a.hbuf[(size_t)(gb + m0 + m) * I + hc] = (_Float16)(hv[cb][i][r] * sc);
+                }
+            }
     } else {
-        const float* gl = reinterpret_cast<const float*>(slot + a.dn_glob);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int oc = 64 * (grp0 + (b >> 2)) + 16 * (b & 3) + l16;
             if (oc >= H) continue;
-            const float gd = gl[oc];
+            const float gd = __uint_as_float(buf_load4(gres, (int)a.dn_glob + 4 * oc));
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = 16 * MI * wm + 16 * i + 4 * q4 + r;
-                    if (m < cnt) a.obuf[(size_t)(gb + m0 + m) * H + oc] = acc[i][b][r] * gd;
+                    if (m < cnt) {
+                        const int e = semin[m];
+                        a.obuf[(size_t)(gb + m0 + m) * H + oc] = ldexpf(acc[i][b][r], e == kNoExp ? 0 : -e) * gd;
+                    }
                 }
         }
     }
@@ -480,7 +597,7 @@ __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a, int nchunk)
             const int p = valid ? a.assign_pos[aidx] : 0;
             v[i] = __builtin_bit_cast(f32x4_t, buf_load16(ores, valid ? 16 * (p * H4 + c4) : kOob));
             wj[i] = valid ? a.w[aidx] : 0.0f;
-            ok[i] = valid && a.slot_of_expert[a.ids[aidx]] >= 0;
+            ok[i] = valid && slot_in_bank(a, a.slot_of_expert[a.ids[aidx]]);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -507,12 +624,13 @@ struct Fork {
     hipEvent_t forked = nullptr, joined = nullptr;
 };
 
+std::mutex g_fork_mu;
+std::map<hipStream_t, Fork> g_forks;
+
 hipError_t fork_for(hipStream_t s, Fork& out) {
-    static std::mutex mu;
-    static std::map<hipStream_t, Fork> forks;
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = forks.find(s);
-    if (it != forks.end()) {
+    std::lock_guard<std::mutex> lock(g_fork_mu);
+    auto it = g_forks.find(s);
+    if (it != g_forks.end()) {
         out = it->second;
         return hipSuccess;
     }
@@ -520,13 +638,34 @@ hipError_t fork_for(hipStream_t s, Fork& out) {
     hipError_t e = hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&f.forked, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&f.joined, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
-    forks[s] = f;
+    if (e != hipSuccess) {  // nothing half-made is kept
+        if (f.joined) (void)hipEventDestroy(f.joined);
+        if (f.forked) (void)hipEventDestroy(f.forked);
+        if (f.side) (void)hipStreamDestroy(f.side);
+        return e;
+    }
+    g_forks[s] = f;
     out = f;
     return hipSuccess;
 }
 
 }  // namespace
+
+// Every side stream and event pair the prefill path created: each side stream is synchronised, then destroyed.
+hipError_t release_side_streams() {
+    std::lock_guard<std::mutex> lock(g_fork_mu);
+    hipError_t first = hipSuccess;
+    for (auto& kv : g_forks) {
+        Fork& f = kv.second;
+        hipError_t e = hipStreamSynchronize(f.side);
+        if (e == hipSuccess) e = hipEventDestroy(f.forked);
+        if (e == hipSuccess) e = hipEventDestroy(f.joined);
+        if (e == hipSuccess) e = hipStreamDestroy(f.side);
+        if (e != hipSuccess && first == hipSuccess) first = e;
+    }
+    g_forks.clear();
+    return first;
+}
 
 bool prefill_shape_supported(int H, int I) { return H % 128 == 0 && I % 32 == 0 && H <= 8192; }
 
@@ -537,11 +676,13 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     uint8_t* p = static_cast<uint8_t*>(ws);
     const WsLayout wl = ws_layout(T, H, I, E, k);
     PrefillArgs a;
-    a.bank = L.bank; a.slot_bytes = L.slot_bytes; a.slot_of_expert = L.slot_of_expert;
+    a.bank = L.bank; a.slot_bytes = L.slot_bytes; a.num_slots = L.num_slots; a.slot_of_expert = L.slot_of_expert;
     a.shared = L.shared; a.wg = L.wg; a.x = x;
     a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
     a.w = w; a.ids = ids; a.offsets = offsets; a.sorted_assign = sorted_assign; a.assign_pos = assign_pos;
     a.hbuf = reinterpret_cast<_Float16*>(p + wl.h);
+    a.hexp = reinterpret_cast<int*>(p + wl.hx);
+    a.KT = ceil_div(I, BK);
     a.obuf = reinterpret_cast<float*>(p + wl.o);
     a.x16 = reinterpret_cast<_Float16*>(p + wl.x16);
     a.xinv = reinterpret_cast<float*>(p + wl.xinv);
@@ -557,12 +698,13 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     const int G = E + 1;
     const int max128 = min(a.cap, rows / 128 + G);
     const int maxsmall = min(a.cap, G);
-    hipLaunchKernelGGL(prep_plan_kernel, dim3(T + 1), dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // remainder tiles on the side stream, 128-row tiles on the caller's stream
+    // the side stream and its events exist before anything is enqueued, so a failure here enqueues nothing
     Fork f;
-    if ((e = fork_for(s, f)) != hipSuccess) return e;
+    hipError_t e = fork_for(s, f);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prep_plan_kernel, dim3(T + 1), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // remainder tiles on the side stream, 128-row tiles on the caller's stream
     if ((e = hipEventRecord(f.forked, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(f.side, f.forked, 0)) != hipSuccess) return e;
     if ((e = launch_tiles<true, 64>(a, 1, maxsmall, f.side)) != hipSuccess) return e;

@@ -47,6 +47,29 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
     }
 }
 
+// Row-major matrix: one thread per code dword (8 consecutive columns of a
+// row, element 2j in the low nibble of byte j), decoded by frag_f16 with
+// the scale of its 16-column block, then times the row's global.
+__global__ void __launch_bounds__(256) dequant_rows_kernel(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           const float* __restrict__ globals, int rows, int K,
+                                                           float* __restrict__ out) {
+    const long per_row = K / 8;
+    const long q = (long)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (long)rows * per_row) return;
+    const long r = q / per_row;
+    const int c0 = (int)(q % per_row) * 8;
+    const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + r * (K / 2) + c0 / 2);
+    const uint32_t sb = scales[r * (K / 16) + c0 / 16];
+    const f16x8_t v = frag_f16(cw, scale_f16x2<0>(sb));
+    const float gl = globals[r];
+    f32x4_t lo, hi;
+    for (int e = 0; e < 4; ++e) lo[e] = (float)v[e] * gl, hi[e] = (float)v[4 + e] * gl;
+    f32x4_t* o = reinterpret_cast<f32x4_t*>(out + r * K + c0);
+    o[0] = lo;
+    o[1] = hi;
+}
+
 // Copy records of every slot: dst record o*per + i of a region <- src record
 // o*src_per + (i < split ? a + i : b + (i - split)), rb bytes each.
 __global__ void __launch_bounds__(256) copy_records_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
@@ -87,6 +110,14 @@ hipError_t launch_dequant(const uint8_t* slot, int H, int I, int matrix, float* 
         hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)((lanes / 2 + 255) / 256)), dim3(256), 0, s, slot, H,
                            I, gm.dn_codes, gm.dn_scales, gm.dn_glob, out);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, const float* globals, int rows, int K,
+                               float* out, hipStream_t s) {
+    const long n = (long)rows * (K / 8);
+    hipLaunchKernelGGL(dequant_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, scales,
+                       globals, rows, K, out);
     return hipGetLastError();
 }
 

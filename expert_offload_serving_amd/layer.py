@@ -146,11 +146,19 @@ def route_forward(layer: DeviceLayer, logits: torch.Tensor, x: torch.Tensor, y: 
     return y, r
 
 
-def dequant(slot: torch.Tensor, H: int, I: int, matrix: int, stream=None) -> torch.Tensor:
+def dequant(codes: torch.Tensor, scales: torch.Tensor, globals_: torch.Tensor, stream=None) -> torch.Tensor:
+    """fp32 [rows, K] of a row-major NVFP4 matrix: codes u8 [rows, K/2], scales u8 [rows, K/16], globals f32 [rows]."""
+    rows, K = codes.shape[0], 2 * codes.shape[1]
+    out = torch.empty((rows, K), dtype=torch.float32, device=codes.device)
+    check(_lib.moe_nvfp4_dequant(codes, scales, globals_, rows, K, out, stream))
+    return out
+
+
+def dequant_slot(slot: torch.Tensor, H: int, I: int, matrix: int, stream=None) -> torch.Tensor:
     """fp32 gate_up (matrix 0, [2I, H]) or down (matrix 1, [H, I]) of one device slot."""
     shape = (2 * I, H) if matrix == 0 else (H, I)
     out = torch.empty(shape, dtype=torch.float32, device=slot.device)
-    check(_lib.moe_nvfp4_dequant(slot, H, I, matrix, out, stream))
+    check(_lib.moe_nvfp4_dequant_slot(slot, H, I, matrix, out, stream))
     return out
 
 

@@ -212,17 +212,50 @@ CONFIGS = {
 }
 
 
+def flip_code_signs(slot: np.ndarray, H: int, I: int, rng: np.random.Generator) -> np.ndarray:
+    """A copy of `slot` whose E2M1 codes have their sign bits flipped by a random mask.
+
+    The quantizer is sign-symmetric (scales and globals come from magnitudes), so the result is exactly the
+    quantization of the base weights with those signs flipped: another properly quantized expert whose
+    weights, for the symmetric N(0, std) draw, have the same distribution."""
+    out = slot.copy()
+    regions = slot_regions(H, I)
+    for r in (0, 3):  # gate_up codes, down codes
+        off, size = regions[r]
+        out[off:off + size] ^= rng.integers(0, 256, size, dtype=np.uint8) & np.uint8(0x88)
+    return out
+
+
 def make_bank(rng: np.random.Generator, H: int, I: int, n_slots: int, n_distinct: int | None = None) -> np.ndarray:
-    """n_slots quantized expert slots.  With n_distinct < n_slots, slot j repeats base expert j % n_distinct
-    (every slot keeps its own address; values stay those of properly quantized experts)."""
+    """n_slots quantized expert slots, every one distinct.  With n_distinct < n_slots only n_distinct experts
+    are quantized; slot j >= n_distinct is base expert j % n_distinct with the signs of its codes flipped by a
+    mask of its own (flip_code_signs), which keeps generation fast while no two slots hold the same weights."""
     nd = n_slots if n_distinct is None else max(1, min(n_distinct, n_slots))
     sb = slot_nbytes(H, I)
     bank = np.empty((n_slots, sb), dtype=np.uint8)
     for j in range(nd):
         bank[j] = random_expert_slot(rng, H, I)
+    flips = rng.spawn(1)[0] if n_slots > nd else None
     for j in range(nd, n_slots):
-        bank[j] = bank[j % nd]
+        bank[j] = flip_code_signs(bank[j % nd], H, I, flips)
     return bank
+
+
+def permute_slots(L: "LayerInputs", rng: np.random.Generator, spare: int = 40) -> "LayerInputs":
+    """The same layer stored in a larger bank at random positions: E + 1 + spare slots, expert e at a random
+    slot, the shared expert at another, and the spare slots filled with random bytes (whose scale bytes include
+    the E4M3 NaN codes, so reading one shows up in the output).  The layer's values are unchanged."""
+    n = L.E + 1 + spare
+    order = rng.permutation(n)
+    bank = rng.integers(0, 256, (n, L.slot_bytes), dtype=np.uint8)
+    for e in range(L.E):
+        bank[order[e]] = L.bank[L.slot_of_expert[e]]
+    shared = -1
+    if L.shared_slot >= 0:
+        shared = int(order[L.E])
+        bank[shared] = L.bank[L.shared_slot]
+    som = order[:L.E].astype(np.int32)
+    return LayerInputs(L.H, L.I, L.E, L.k, L.T, bank, som, shared, L.wg, L.x, L.logits)
 
 
 def make_logits(rng: np.random.Generator, T: int, E: int, kind: str) -> np.ndarray:

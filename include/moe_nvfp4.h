@@ -21,9 +21,12 @@
  *    moe_nvfp4_forward, moe_nvfp4_route_forward, moe_router_logits and
  *    moe_router_topk make no host synchronisation and allocate no memory
  *    (the prefill path creates its side stream and two events on its first
- *    call for a given caller stream, and reuses them afterwards).
+ *    call for a given caller stream, and reuses them afterwards;
+ *    moe_release_streams destroys them).
  *  - Shapes: H % 128 == 0, I % 32 == 0 (see the slot format below),
- *    1 <= k <= E <= 1024, T >= 0 (T == 0 is a no-op).
+ *    1 <= k <= E <= 1024, T >= 0 (T == 0 is a no-op).  The kernels address
+ *    buffers through 32-bit byte offsets: a slot, x, y or a workspace of
+ *    2 GiB or more is refused with MOE_ERR_UNSUPPORTED_SHAPE.
  *  - bf16 values are passed as their uint16 bit patterns.
  */
 #ifndef MOE_NVFP4_H
@@ -130,7 +133,9 @@ int moe_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int H, i
  *   slot_bytes      must equal moe_nvfp4_slot_bytes(H, I)
  *   slot_of_expert  device i32 [E]: slot index of each expert, or -1 to leave it
  *                   out of this call (its assignments then contribute nothing)
- *   num_slots       number of slots at bank_base (slot indices must be below it)
+ *   num_slots       number of slots at bank_base; an index outside [0, num_slots)
+ *                   leaves its expert out exactly like -1 (no memory outside the
+ *                   bank is read)
  *   shared_slot     device pointer to the shared expert's slot (same layout,
  *                   same H and I), or NULL for no shared expert
  *   shared_gate_w   device bf16 [H]: the shared expert's scalar gate
@@ -156,18 +161,21 @@ size_t moe_nvfp4_forward_workspace_bytes(int T, int H, int I, int E, int k);
  *   x        bf16 [T, H] activations
  *   routing  the outputs of moe_route_topk for the same T, E, k
  *   y        f32 [T, H]; accumulate = 0 writes y, 1 adds into y
+ * Arithmetic: every contraction runs on the fp16 matrix cores
+ * (v_mfma_f32_16x16x32_f16) with fp32 accumulation.  NVFP4 weights decode
+ * exactly to fp16 (e2m1 * e4m3 has at most 6 significant bits); bf16
+ * activations enter as fp16 times a per-token power of two, which is exact
+ * in the fp16 normal range; the hidden state goes back into fp16 with a
+ * power-of-two scale per (token, slice or 128-column tile); every scale is
+ * undone exactly on the fp32 results.
  * T <= 16 (with H <= 2560) runs the decode path: one persistent kernel over
- * (expert, I-slice) work items whose NVFP4 operands are decoded in registers
- * into fp16 matrix-core fragments against per-token fp16-scaled activations
- * (fp32 accumulation and hidden state), then a combine kernel that sums the
- * slices and applies the down-row globals in a fixed order.  Larger T runs
- * the prefill path: grouped bf16 MFMA GEMMs over the permuted tokens with
- * the weights decoded in registers, fp16 hidden state; its remainder tiles run
- * on a library-owned side stream forked from and joined back to `stream`, so
- * the call stays ordered on `stream` (and capturable in a graph).  Expert
- * slots referenced by slot_of_expert must lie inside the bank; the kernels do
- * not range-check them.  Output order of summation is fixed, so repeated
- * calls give bit-identical results. */
+ * (expert, I-slice) work items whose operands are decoded in registers,
+ * then a combine kernel that sums the slices and applies the down-row
+ * globals in a fixed order.  Larger T runs the prefill path: grouped GEMMs
+ * over the permuted tokens; its remainder tiles run on a library-owned side
+ * stream forked from and joined back to `stream`, so the call stays ordered
+ * on `stream` (and capturable in a graph).  Output order of summation is
+ * fixed, so repeated calls give bit-identical results. */
 int moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
                       const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
                       const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
@@ -233,11 +241,31 @@ int moe_cache_plan(moe_expert_cache_t* cache, int layer, const int32_t* ids, int
 int moe_nvfp4_slice_bank(const void* src_bank, int num_slots, int H, int I, int r, int n, void* dst_bank,
                          hipStream_t stream);
 
-/* ------------------------------------------------------------------ test hook
- * Dequantise one matrix of one slot to fp32, row-major, with the same decode
- * the forward kernels use: out[r,c] = f32(f32(e2m1 * e4m3) * global[r]).
- * matrix 0 is gate_up (out [2I, H]), matrix 1 is down (out [H, I]). */
-int moe_nvfp4_dequant(const void* slot, int H, int I, int matrix, float* out, hipStream_t stream);
+/* ------------------------------------------------------------------ dequant
+ * The NVFP4 decode of one row-major matrix (PR #385 "What this adds": packed
+ * 4-bit codes, 16-wide FP8 scale blocks, per-row fp32 globals), with the
+ * decode the forward kernels use:
+ *     out[r, c] = f32(f32(e2m1(code(r, c)) * e4m3(scales[r, c/16])) * globals[r])
+ *   codes    device u8 [rows, K/2]: element 2j of a row in the low nibble of byte j
+ *   scales   device u8 [rows, K/16]: OCP E4M3FN bytes
+ *   globals  device f32 [rows]
+ *   out      device f32 [rows, K], 16-byte aligned (codes 4-byte aligned)
+ * K must be a positive multiple of 16; rows == 0 is a no-op.  E4M3 NaN
+ * scale bytes give NaN. */
+int moe_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* globals, int rows, int K, float* out,
+                      hipStream_t stream);
+
+/* The same decode of one matrix of one slot (the operand-order layout
+ * above) to fp32, row-major: matrix 0 is gate_up (out [2I, H]), matrix 1 is
+ * down (out [H, I]). */
+int moe_nvfp4_dequant_slot(const void* slot, int H, int I, int matrix, float* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------ streams
+ * Synchronise and destroy the side streams and events the prefill path
+ * created for its callers' streams (the next prefill call creates them
+ * again).  The caller must not have prefill work in flight or being captured
+ * on any stream when calling this. */
+int moe_release_streams(void);
 
 #ifdef __cplusplus
 }

@@ -99,12 +99,33 @@ def test_route_forward_validation_without_gpu():
     assert f(_layer(), T=0) == _lib.MOE_OK
 
 
+def test_forward_refuses_buffers_of_2gib():
+    """Every buffer the kernels address through 32-bit offsets must stay below 2 GiB: shapes whose workspace or
+    output would reach it are refused before anything is enqueued (no GPU needed)."""
+    d = 0x3000
+    f = lambda L, T: _lib.moe_nvfp4_forward(L, d, T, d, d, d, d, d, d, 0, 0x200000, 1 << 62, 0)
+    assert _lib.moe_nvfp4_forward_workspace_bytes(23_000, 2560, 640, 256, 8) >= 1 << 31
+    assert f(_layer(), 23_000) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert "2 GiB" in _lib.last_error()
+    assert f(_layer(), 200_000) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert f(_layer(), 0) == _lib.MOE_OK  # T = 0 stays a valid no-op
+
+
 def test_other_entry_points_validate():
-    assert _lib.moe_nvfp4_dequant(0x100, 96, 32, 0, 0x100, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE   # H % 128
-    assert _lib.moe_nvfp4_dequant(0x100, 128, 48, 0, 0x100, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE  # I % 32
-    assert _lib.moe_nvfp4_dequant(0x100, 128, 32, 2, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT   # matrix
-    assert _lib.moe_nvfp4_dequant(0x101, 128, 32, 0, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT   # misaligned
-    assert _lib.moe_nvfp4_dequant(None, 128, 32, 0, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT
+    ds = _lib.moe_nvfp4_dequant_slot
+    assert ds(0x100, 96, 32, 0, 0x100, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE   # H % 128
+    assert ds(0x100, 128, 48, 0, 0x100, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE  # I % 32
+    assert ds(0x100, 128, 32, 2, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT   # matrix
+    assert ds(0x101, 128, 32, 0, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT   # misaligned
+    assert ds(None, 128, 32, 0, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT
+    dq = _lib.moe_nvfp4_dequant
+    assert dq(0x100, 0x100, 0x100, 4, 40, 0x100, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE   # K % 16
+    assert dq(0x100, 0x100, 0x100, -1, 32, 0x100, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE  # rows < 0
+    assert dq(0x102, 0x100, 0x100, 4, 32, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT    # codes misaligned
+    assert dq(0x100, 0x100, 0x100, 4, 32, 0x108, 0) == _lib.MOE_ERR_INVALID_ARGUMENT    # out misaligned
+    assert dq(0x100, None, 0x100, 4, 32, 0x100, 0) == _lib.MOE_ERR_INVALID_ARGUMENT
+    assert dq(None, None, None, 0, 32, None, 0) == _lib.MOE_OK                          # rows == 0: no-op
+    assert _lib.moe_release_streams() == _lib.MOE_OK                                    # nothing created yet
     assert _lib.moe_nvfp4_slice_bank(1, 4, 2560, 640, 0, 8, 1, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE  # 80 % 32 != 0
     assert _lib.moe_nvfp4_slice_bank(1, 4, 2560, 640, 2, 2, 1, 0) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
     assert _lib.moe_nvfp4_slice_bank(1, 0, 2560, 640, 0, 2, 1, 0) == _lib.MOE_OK

@@ -53,7 +53,7 @@ def test_dequant_bitexact_all_code_scale_pairs():
     for m, parts in enumerate((gu, dn)):
         want = oracle.dequant(*parts)
         assert np.array_equal(np.isnan(want), np.isnan(oracle.dequant_slot(slot, H, I, m)))
-        got = dl.dequant(dslot, H, I, m).cpu().numpy()
+        got = dl.dequant_slot(dslot, H, I, m).cpu().numpy()
         nan_w, nan_g = np.isnan(want), np.isnan(got)
         assert np.array_equal(nan_w, nan_g)
         assert np.array_equal(want[~nan_w].view(np.uint32), got[~nan_g].view(np.uint32))
@@ -66,8 +66,37 @@ def test_dequant_bitexact_real_bank():
     dslot = torch.from_numpy(slot).cuda()
     for m in (0, 1):
         want = oracle.dequant_slot(slot, H, I, m)
-        got = dl.dequant(dslot, H, I, m)
+        got = dl.dequant_slot(dslot, H, I, m)
         assert np.array_equal(want.view(np.uint32), got.cpu().numpy().view(np.uint32))
+
+
+def _bits_equal(got: np.ndarray, want: np.ndarray):
+    """Equal bit patterns, with every NaN position matching (NaN payloads are not compared)."""
+    nan_w, nan_g = np.isnan(want), np.isnan(got)
+    assert np.array_equal(nan_w, nan_g)
+    assert np.array_equal(want[~nan_w].view(np.uint32), got[~nan_g].view(np.uint32))
+
+
+def test_dequant_rowmajor_bitexact_all_code_scale_pairs():
+    """The row-major decode entry (no slot layout involved): every (code, scale byte) pair under several globals,
+    ragged row counts and K from one scale block up, bit for bit against the oracle's dequant."""
+    gl = np.array([1.0, 0.5, 3.7e-5, -2.25, 1.0e30, 2.0 ** -126, 0.0], dtype=np.float32)
+    # rows x K = 16 codes in every position of a 16-block, 256 scale bytes, each (code, scale) pair present
+    codes_row = np.array([(2 * j % 16) | (((2 * j + 1) % 16) << 4) for j in range(8)], dtype=np.uint8)
+    for rows, K, what in [(256 * 7, 16, "all pairs x globals"), (37, 48, "ragged"), (1, 4096, "one long row"),
+                          (1000, 32, "many rows")]:
+        _announce(f"dequant row-major rows={rows} K={K} ({what})")
+        codes = np.tile(codes_row, (rows, K // 16))
+        r_ = np.arange(rows)[:, None]
+        blocks = np.arange(K // 16)[None, :]
+        scales = ((r_ + 37 * blocks) % 256).astype(np.uint8)
+        if what.startswith("all pairs"):
+            scales = (np.arange(rows)[:, None] % 256).astype(np.uint8).repeat(K // 16, axis=1)
+        globals_ = gl[(np.arange(rows) // 256 + np.arange(rows)) % len(gl)]
+        want = oracle.dequant(codes, scales, globals_)
+        got = dl.dequant(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                         torch.from_numpy(globals_).cuda()).cpu().numpy()
+        _bits_equal(got, want)
 
 
 # ---------------------------------------------------------------- routing
@@ -282,8 +311,7 @@ def test_forward_small_shapes_and_ragged():
         # padded down record groups (H/64 = 6 and 2)
         _announce(f"forward H={H} I={I} E={E} k={k} T={T}")
         rng = np.random.default_rng(H + I + T)
-        distinct = [synth.random_expert_slot(rng, H, I) for _ in range(min(E + 1, 9))]
-        bank = np.stack([distinct[(7 * e) % len(distinct)] for e in range(E + 1)])
+        bank = synth.make_bank(rng, H, I, E + 1, 9)  # every slot distinct
         L = synth.LayerInputs(H, I, E, k, T, bank, np.arange(E, dtype=np.int32), E,
                               synth.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32) * 0.02),
                               synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)),
@@ -341,8 +369,7 @@ def test_route_forward_ties_skips_and_fallbacks():
     _route_forward_vs_separate(synth.make_layer("prefill_2048", T=40, n_distinct=6), "route_forward T=40")
     _announce("route_forward E=300 decode (separate routing launch)")
     H, I, E, k, T = 256, 64, 300, 4, 3
-    base = [synth.random_expert_slot(rng, H, I) for _ in range(5)]
-    bank = np.stack([base[e % 5] for e in range(E + 1)])
+    bank = synth.make_bank(rng, H, I, E + 1, 5)
     L2 = synth.LayerInputs(H, I, E, k, T, bank, np.arange(E, dtype=np.int32), E,
                            synth.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32) * 0.02),
                            synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)),
@@ -351,8 +378,7 @@ def test_route_forward_ties_skips_and_fallbacks():
 
 
 def _small_layer(rng, H, I, E, k, T, n_distinct=9):
-    distinct = [synth.random_expert_slot(rng, H, I) for _ in range(min(E + 1, n_distinct))]
-    bank = np.stack([distinct[(7 * e) % len(distinct)] for e in range(E + 1)])
+    bank = synth.make_bank(rng, H, I, E + 1, n_distinct)  # every slot distinct
     return synth.LayerInputs(H, I, E, k, T, bank, np.arange(E, dtype=np.int32), E,
                              synth.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32) * 0.02),
                              synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)),
