@@ -8,9 +8,16 @@ in HBM before timing; every step uses fresh routing and, to keep the 256 MB
 Infinity Cache from serving repeated experts, one of several copies of the
 expert bank in turn.  The steps are captured in a HIP graph and replayed.
 
-Default workload (the decode shape the metric is quoted on): H=2560,
-I=640, 256 experts top-8 with uniform-random logits, one shared expert,
-batch 1.  Prints one JSON line.
+Default run: every workload, printed as ONE JSON line whose top level is the
+decode shape the metric is quoted on (H=2560, I=640, 256 experts top-8 with
+uniform-random logits, one shared expert, batch 1) and whose "configs" entry
+holds the full result of decode batch 16, the 2048-token prefill chunk and
+the offloaded 48-layer run, each with its own roofline and CPU baseline.
+`--config NAME` prints that workload's line alone.
+
+The arithmetic (dtype field): NVFP4 weights decoded exactly to fp16, bf16
+activations entered as fp16 times a per-token power of two, fp16 matrix-core
+products accumulated in fp32.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME|all]
 """
@@ -19,6 +26,8 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -28,6 +37,7 @@ METRIC = "MoE-layer tokens/s + expert-weight HBM GB/s (% peak), H2560 I640 NVFP4
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 PCIE_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction
+DTYPE = "nvfp4w-fp16mfma-fp32acc"
 
 
 # HBM bytes per call of the roofline unit from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, summed over the call's
@@ -195,22 +205,96 @@ def run_gpu(inp, steps: int, warmup: int):
 
 # ---------------------------------------------------------------- CPU baseline (the oracle)
 
-def cpu_baseline(inp, n_tokens: int, unit: str):
+def oracle_threads():
+    """Threads for the oracle: the host's physical cores (lscpu), capped by the CPUs this process may run on and
+    by its cgroup CPU quota (an oversubscribed OpenMP pool would measure spin-waiting, not the oracle)."""
+    phys = None
+    try:
+        out = subprocess.run(["lscpu", "-p=core,socket"], capture_output=True, text=True, timeout=20).stdout
+        phys = len({ln for ln in out.splitlines() if ln and not ln.startswith("#")}) or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    avail = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()
+        if q != "max":
+            quota = max(1, int(int(q) // int(per)))
+    except (OSError, ValueError):
+        pass
+    n = min(v for v in (phys, avail, quota) if v)
+    return n, {"lscpu_physical_cores": phys, "affinity_cpus": avail, "cgroup_cpu_quota": quota}
+
+
+# Per-repetition sample of each workload for the oracle (one oracle call per step, as the GPU runs them).
+CPU_SAMPLES = {"decode_bs1": 4, "decode_bs16": 1, "prefill_2048": 128, "offload": 2}
+
+
+def cpu_leg(name: str, reps: int = 5) -> dict:
+    """Runs in a child process (OMP_NUM_THREADS / OMP_PROC_BIND set before the OpenMP runtime starts): the oracle
+    (routing + the whole layer forward, fp64 accumulation) timed on a sample of the workload, one warm-up then the
+    median of `reps` repetitions."""
     import oracle
     from expert_offload_serving_amd import synth
-    H, I, E, k, T = inp["H"], inp["I"], inp["E"], inp["k"], inp["T"]
-    x = inp["xs"].reshape(-1, H)[:n_tokens]
-    logits = inp["logits"].reshape(-1, E)[:n_tokens]
-    ids, w = oracle.route(logits, k)
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
-    threads = min(threads, n_tokens)
+    threads = int(os.environ["OMP_NUM_THREADS"])
+    n = CPU_SAMPLES[name]
+    if name == "offload":
+        H, I, E, k, T, seed = 2560, 640, 256, 8, 8, 48
+        r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
+        bank = synth.make_bank(r_w, H, I, E + 1, 32)
+        ranks = r_l.permutation(E) + 1
+        steps = [(synth.f32_to_bf16_bits(r_x.standard_normal((T, H), dtype=np.float32)),
+                  synth.zipf_gumbel_logits(r_l, T, E, 1.2, ranks)) for _ in range(n)]
+        what = f"{n} layer-steps of bs {T} (Zipf(1.2) routing), one oracle call each"
+        per_rep_tokens = n * T
+    else:
+        H, I, E, k, T, seed, kind = synth.CONFIGS[name]
+        r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
+        bank = synth.make_bank(r_w, H, I, E + 1, 32)
+        if T > 16:  # the prefill chunk: its first n tokens, routed and computed as one call
+            x = synth.f32_to_bf16_bits(r_x.standard_normal((T, H), dtype=np.float32))
+            lg = synth.make_logits(r_l, T, E, kind)
+            steps = [(x[:n], lg[:n])]
+            what = f"the first {n} tokens of the {T}-token chunk in one oracle call"
+            per_rep_tokens = n
+        else:
+            steps = [(synth.f32_to_bf16_bits(r_x.standard_normal((T, H), dtype=np.float32)),
+                      synth.make_logits(r_l, T, E, kind)) for _ in range(n)]
+            what = f"{n} step(s) of {T} token(s), one oracle call each"
+            per_rep_tokens = n * T
+    wg = synth.f32_to_bf16_bits(r_g.standard_normal(H, dtype=np.float32) * np.float32(0.02))
+    som = np.arange(E, dtype=np.int32)
+
+    def once():
+        t0 = time.perf_counter()
+        for x, lg in steps:
+            ids, w = oracle.route(lg, k)
+            oracle.forward(H, I, E, k, bank, som, E, wg, x, ids, w, nthreads=threads)
+        return time.perf_counter() - t0
+
+    once()
+    times = [once() for _ in range(reps)]
+    med = statistics.median(times)
+    return {"value": round(per_rep_tokens / med, 3), "seconds_per_rep": [round(t, 3) for t in times],
+            "sample": f"{what}: routing and the whole layer forward (all expert FFNs, shared expert, combine) "
+                      f"through the oracle, fp64 accumulation; 1 warm-up then the median of {reps} repetitions of "
+                      f"{per_rep_tokens} tokens"}
+
+
+def cpu_baseline(name: str, unit: str) -> dict:
+    """The oracle timed on the host's cores in a child process, so that OMP_NUM_THREADS and OMP_PROC_BIND=close
+    are in force when its OpenMP runtime starts."""
+    threads, how = oracle_threads()
+    env = dict(os.environ, OMP_NUM_THREADS=str(threads), OMP_PROC_BIND="close", OMP_PLACES="cores")
     t0 = time.perf_counter()
-    oracle.forward(H, I, E, k, inp["bank"], np.arange(E, dtype=np.int32), E, inp["wg"], x, ids, w,
-                   nthreads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": round(n_tokens / dt, 3), "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"{n_tokens} tokens of the same workload (routing, all expert FFNs, shared expert, combine) "
-                      f"through oracle_forward, fp64 accumulation, {dt:.1f} s"}
+    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-leg", name], capture_output=True,
+                         text=True, env=env, timeout=900)
+    if res.returncode != 0:
+        return {"error": res.stderr[-500:], "kind": "oracle"}
+    leg = json.loads(res.stdout.strip().splitlines()[-1])
+    return {"value": leg["value"], "unit": unit, "cores": threads, "kind": "oracle", "sample": leg["sample"],
+            "threads_from": how, "omp": "OMP_PROC_BIND=close OMP_PLACES=cores",
+            "seconds_per_rep": leg["seconds_per_rep"], "wall_s": round(time.perf_counter() - t0, 1)}
 
 
 def parity_sample(inp, res, tokens):
@@ -235,12 +319,13 @@ def parity_sample(inp, res, tokens):
 # ---------------------------------------------------------------- offload
 
 def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_cpu: bool = True,
-                  residency: float = 0.37):
+                  residency: float = 0.37, distinct_banks: bool = True):
     """48 MoE layers whose 256 experts live in pinned host memory behind one HBM cache holding `residency`
     (default 37%) of the 12,288 expert-layer slots (global LRU, cold start).  Per layer-step: route on the GPU, one D2H copy of
     the ids, host LRU plan, misses copied on a side stream while the hits-only forward runs, then the
     misses-only forward accumulates.  With want_cpu, the CPU leg checks the host LRU and the last layer-step
-    against the oracle.  Returns the JSON dict."""
+    against the oracle.  With distinct_banks (the default) every one of the 48 x 256 experts has its own pinned
+    host slot (34.16 GB); otherwise the experts alias 256 pinned base slots.  Returns the JSON dict."""
     import torch
     from expert_offload_serving_amd import _lib, synth
     from expert_offload_serving_amd import layer as dl
@@ -253,12 +338,41 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
     t0 = time.time()
     base_np = synth.make_bank(r_w, H, I, E, distinct)          # 256 base experts (distinct of them quantized)
     log(f"offload: quantized {min(distinct, E)} distinct experts into {E} base slots in {time.time() - t0:.1f}s")
-    # expert (l, e) is base expert (e + 37 l) mod 256: every (layer, expert) reads its own base slot address
-    # range; the 48 x 256 banks are these 256 pinned slots, each serving 48 (layer, expert) pairs.
-    host = torch.from_numpy(base_np).pin_memory()
-    host_ptr = [host[j].data_ptr() for j in range(E)]
+    # expert (l, e) is base expert (e + 37 l) mod 256 with its code signs flipped by layer l's own mask, so every
+    # (layer, expert) has distinct weights and its own pinned slot
     def base_of(l, e):
         return (e + 37 * l) % E
+    banks_note = None
+    host = None
+    if distinct_banks:
+        t0 = time.time()
+        try:
+            host = torch.empty((L, E, sb), dtype=torch.uint8, pin_memory=True)
+        except RuntimeError as err:  # page-locking 34 GB refused: fall back to the aliased banks, and say so
+            banks_note = f"distinct pinned banks refused ({err}); aliased base slots used"
+            log(f"offload: {banks_note}")
+            host = None
+        if host is not None:
+            base_t = torch.from_numpy(base_np)
+            mrng = np.random.default_rng(4800)
+            regions = synth.slot_regions(H, I)
+            for l in range(L):
+                mask = np.zeros(sb, dtype=np.uint8)
+                for r_ in (0, 3):  # code regions: sign bits only
+                    off, size = regions[r_]
+                    mask[off:off + size] = mrng.integers(0, 256, size, dtype=np.uint8) & np.uint8(0x88)
+                idx = torch.tensor([base_of(l, e) for e in range(E)])
+                torch.bitwise_xor(base_t[idx], torch.from_numpy(mask), out=host[l])
+            host_ptr = [[host[l, e].data_ptr() for e in range(E)] for l in range(L)]
+            log(f"offload: {L} x {E} distinct expert slots pinned ({L * E * sb / 1e9:.2f} GB) in "
+                f"{time.time() - t0:.1f}s")
+    if host is None:
+        # the 48 x 256 banks alias 256 pinned base slots, each serving 48 (layer, expert) pairs
+        host_base = torch.from_numpy(base_np).pin_memory()
+        host_ptr = [[host_base[base_of(l, e)].data_ptr() for e in range(E)] for l in range(L)]
+
+    def host_slot_np(l, e):
+        return host[l, e].numpy() if host is not None else base_np[base_of(l, e)]
     dev = torch.device("cuda:0")
     cache = torch.empty((n_slots, sb), dtype=torch.uint8, device=dev)
     shared_np = np.stack([base_np[(200 + l) % E] for l in range(L)])
@@ -330,7 +444,7 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
             part = list(range(c_, len(miss_e), ncopy))
             if part:
                 _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, [miss_s[i] for i in part],
-                                                  [host_ptr[base_of(l, miss_e[i])] for i in part], copies[c_],
+                                                  [host_ptr[l][miss_e[i]] for i in part], copies[c_],
                                                   dones[c_]))
                 used.append(c_)
         _lib.check(_lib.moe_nvfp4_forward(layer_struct(l, maps_d[0], True), x, T, route.ids, route.w,
@@ -367,7 +481,8 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
     tp = time.perf_counter()
     for c_ in range(ncopy):
         part = list(range(c_, n_probe, ncopy))
-        _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, part, [host_ptr[j % E] for j in part], copies[c_], None))
+        _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, part, [host_ptr[j // E % L][j % E] for j in part],
+                                          copies[c_], None))
     torch.cuda.synchronize()
     h2d_gbs = n_probe * sb / (time.perf_counter() - tp) / 1e9
 
@@ -380,15 +495,19 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
         lru_ok = bool(np.array_equal(h_ref, stats["hits"]) and np.array_equal(m_ref, stats["misses"]))
         s_last, l_last = total - 1, L - 1
         ids_o, w_o = oracle.route(logits_np[s_last, l_last], k)
-        bank_o = np.concatenate([base_np, shared_np[l_last][None]], axis=0)
-        som_o = np.array([base_of(l_last, e_) for e_ in range(E)], dtype=np.int32)
         toks = np.arange(2, dtype=np.int32)
-        ref = oracle.forward(H, I, E, k, bank_o, som_o, E, wg_np[l_last], xs_np[(s_last * L + l_last) % NX], ids_o,
-                             w_o, tokens=toks)
+        routed = np.unique(ids_o[toks])
+        bank_o = np.stack([host_slot_np(l_last, int(e_)) for e_ in routed] + [shared_np[l_last]])
+        som_o = np.full(E, -1, dtype=np.int32)
+        som_o[routed] = np.arange(routed.size, dtype=np.int32)
+        ref = oracle.forward(H, I, E, k, bank_o, som_o, routed.size, wg_np[l_last],
+                             xs_np[(s_last * L + l_last) % NX], ids_o, w_o, tokens=toks)
         got = y.cpu().numpy()[toks].astype(np.float64)
         rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
         cpu_checks = {"lru_matches_oracle_model": lru_ok, "rel_l2_last_layer_step": rel,
                       "tokens_checked": int(toks.size)}
+        log("offload: timing the oracle (child process)")
+        cpu_checks["cpu_baseline"] = cpu_baseline("offload", "layer-tokens/s")
 
     hits, misses = stats["hits"][warmup:].sum(), stats["misses"][warmup:].sum()
     miss_bytes = misses * sb
@@ -398,10 +517,12 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
         "metric": "MoE-layer tokens/s with the expert cache (offload), H2560 I640 NVFP4",
         "value": round(layer_tok_s, 2), "unit": "layer-tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(wall * 1e3 / steps, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": f"offload_48x256_cache{round(100 * n_slots / (L * E))}", "H": H, "I": I, "E": E, "k": k, "T": T, "layers": L,
                    "cache_slots": n_slots, "residency": round(n_slots / (L * E), 4), "routing": "Zipf(1.2) per layer",
-                   "host_banks": f"{E} pinned base slots ({E * sb / 1e9:.2f} GB); expert (l, e) = base (e + 37 l) mod {E}",
+                   "host_banks": (f"{L} x {E} distinct pinned expert slots ({L * E * sb / 1e9:.2f} GB)" if host is not None
+                                  else f"{E} pinned base slots ({E * sb / 1e9:.2f} GB); expert (l, e) = base "
+                                       f"(e + 37 l) mod {E}" + (f" [{banks_note}]" if banks_note else "")),
                    "distinct_quantized_experts": min(distinct, E), "parallelism": "single GPU"},
         "roofline": {"bound": "pcie", "achieved": round(pcie, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                      "frac": round(pcie / PCIE_PEAK_GBS, 4), "traffic": None,
@@ -413,13 +534,13 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
                     "model_tokens_per_s": round(T * steps / wall, 2), "ms_per_layer_step": round(wall * 1e3 / (steps * L), 4),
                     "miss_GB_per_step": round(miss_bytes / steps / 1e9, 3), "h2d_copy_GBps_alone": round(h2d_gbs, 2),
                     "warmup_s": round(t_cold, 2)},
-        **({"parity": cpu_checks} if cpu_checks is not None else {}),
+        **({"cpu_baseline": cpu_checks.pop("cpu_baseline"), "parity": cpu_checks} if cpu_checks is not None else {}),
     }
 
 
 # ---------------------------------------------------------------- main
 
-def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: int, want_cpu: bool, cpu_tokens: int):
+def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: int, want_cpu: bool):
     from expert_offload_serving_amd import synth
     inp = build_inputs(name, steps + warmup, replicas, distinct)
     H, I, E, k, T = inp["H"], inp["I"], inp["E"], inp["k"], inp["T"]
@@ -454,7 +575,7 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     out = {
         "metric": METRIC, "value": round(tokens_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if prefill else "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": name, "H": H, "I": I, "E": E, "k": k, "T": T, "shared_expert": True,
                    "bank_copies": replicas, "distinct_quantized_experts": min(distinct, E + 1),
                    "parallelism": "single GPU"},
@@ -471,8 +592,8 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     if want_cpu:
         # the CPU-baseline leg (the only part of the benchmark that runs the oracle): the oracle timed on a
         # sample of this workload, and the last timed step's output checked against it
-        log(f"{name}: timing the oracle on {cpu_tokens} tokens")
-        out["cpu_baseline"] = cpu_baseline(inp, cpu_tokens, "tokens/s")
+        log(f"{name}: timing the oracle (child process)")
+        out["cpu_baseline"] = cpu_baseline(name, "tokens/s")
         try:
             out["parity"] = parity_sample(inp, res, 4)
         except Exception as e:  # the parity sample is a report, not the measurement
@@ -569,23 +690,33 @@ def copy_calibration(nbytes: int, reps: int) -> None:
           flush=True)
 
 
+REPLICAS = {"decode_bs1": 16, "decode_bs16": 8, "prefill_2048": 4}  # bank copies rotated over steps
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode_bs1",
+    ap.add_argument("--config", default="all",
                     choices=["decode_bs1", "decode_bs16", "prefill_2048", "offload", "all", *ROUTER_CONFIGS])
-    ap.add_argument("--replicas", type=int, default=8, help="copies of the expert bank rotated over steps")
-    ap.add_argument("--distinct", type=int, default=32, help="distinct quantized experts tiled over the slots")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="copies of the expert bank rotated over steps (default 16 at bs 1, 8 at bs 16, 4 prefill)")
+    ap.add_argument("--distinct", type=int, default=32, help="experts quantized; the other slots are sign-flipped "
+                                                              "copies of them (every slot distinct)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=320)
     ap.add_argument("--copy-streams", type=int, default=2, help="offload: side streams the misses are copied on")
     ap.add_argument("--residency", type=float, default=0.37,
                     help="offload: fraction of the 48 x 256 expert-layers the HBM cache holds")
+    ap.add_argument("--aliased-banks", action="store_true",
+                    help="offload: 256 pinned base slots aliased by the 48 layers instead of 48 x 256 distinct ones")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (for calibrating HBM byte counters) and exit")
+    ap.add_argument("--cpu-leg", default=None, help=argparse.SUPPRESS)  # internal: the oracle timing child process
     args = ap.parse_args()
+    if args.cpu_leg:
+        print(json.dumps(cpu_leg(args.cpu_leg)), flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: the layer runs on a single MI355X here (--gpus {args.gpus}, "
@@ -600,22 +731,31 @@ def main():
         return
     from expert_offload_serving_amd import _lib
     _lib.lib()
-    names = ["decode_bs1", "decode_bs16", "prefill_2048"] if args.config == "all" else [args.config]
-    for name in names:
+    want_cpu = not args.no_cpu_baseline
+
+    def run(name):
         if name in ROUTER_CONFIGS:
-            print(json.dumps(bench_router(name, args.steps, args.warmup, 256)), flush=True)
-            continue
+            return bench_router(name, args.steps, args.warmup, 256)
         if name == "offload":
             steps, warmup = (64, 16) if args.steps == 200 and args.warmup == 10 else (args.steps, args.warmup)
-            print(json.dumps(bench_offload(steps, warmup, args.distinct, args.copy_streams,
-                                           not args.no_cpu_baseline, args.residency)), flush=True)
-            continue
+            return bench_offload(steps, warmup, args.distinct, args.copy_streams, want_cpu, args.residency,
+                                 not args.aliased_banks)
         steps, warmup = args.steps, args.warmup
         if name == "prefill_2048":
             steps, warmup = max(1, min(steps, 20)), max(1, min(warmup, 3))
-        reps = args.replicas if name != "prefill_2048" else min(args.replicas, 4)
-        out = bench_config(name, steps, warmup, reps, args.distinct, not args.no_cpu_baseline, args.cpu_tokens)
-        print(json.dumps(out), flush=True)
+        reps = args.replicas or REPLICAS[name]
+        return bench_config(name, steps, warmup, reps, args.distinct, want_cpu)
+
+    if args.config != "all":
+        print(json.dumps(run(args.config)), flush=True)
+        return
+    # every workload, one line: the headline decode batch 1 at the top level, the others under "configs"
+    head = run("decode_bs1")
+    head["configs"] = {}
+    for name in ("decode_bs16", "prefill_2048", "offload"):
+        head["configs"][name] = run(name)
+        torch.cuda.empty_cache()
+    print(json.dumps(head), flush=True)
 
 
 if __name__ == "__main__":
