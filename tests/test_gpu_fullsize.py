@@ -149,7 +149,8 @@ def _scale_gate_up_globals(L: synth.LayerInputs, row_exp) -> synth.LayerInputs:
     off, size = synth.slot_regions(L.H, L.I)[2]
     bank = L.bank.copy()
     g = bank[:, off:off + size].view(np.float32).reshape(bank.shape[0], 2 * L.I)
-    g *= np.exp2(np.asarray(row_exp, dtype=np.float64)).astype(np.float32)[None, :]
+    used = list(L.slot_of_expert) + ([L.shared_slot] if L.shared_slot >= 0 else [])
+    g[used] *= np.exp2(np.asarray(row_exp, dtype=np.float64)).astype(np.float32)[None, :]  # spare slots hold noise
     return synth.LayerInputs(L.H, L.I, L.E, L.k, L.T, bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, L.logits)
 
 
