@@ -25,7 +25,7 @@ EXPORTED = [
     "moe_nvfp4_forward_workspace_bytes", "moe_nvfp4_forward", "expert_cache_fill", "moe_cache_create",
     "moe_cache_destroy", "moe_cache_plan", "moe_nvfp4_slice_bank", "moe_nvfp4_dequant", "moe_nvfp4_dequant_slot",
     "moe_nvfp4_route_forward_workspace_bytes", "moe_nvfp4_route_forward", "moe_router_logits", "moe_router_topk",
-    "moe_release_streams",
+    "moe_release_streams", "moe_nvfp4_noalloc_scratch_bytes", "moe_nvfp4_route_forward_noalloc",
 ]
 
 
@@ -97,6 +97,11 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_dequant_slot.argtypes = [_vp, _i, _i, _i, _vp, _vp]
         L.moe_release_streams.restype = _i
         L.moe_release_streams.argtypes = []
+        L.moe_nvfp4_noalloc_scratch_bytes.restype = _sz
+        L.moe_nvfp4_noalloc_scratch_bytes.argtypes = []
+        L.moe_nvfp4_route_forward_noalloc.restype = _i
+        L.moe_nvfp4_route_forward_noalloc.argtypes = [ctypes.POINTER(LayerStruct), _vp, _vp, _i, _vp, _vp, _vp, _vp,
+                                                      _vp, _vp, _i, _vp]
         _lib = L
     return _lib
 
@@ -174,6 +179,17 @@ def moe_nvfp4_route_forward(layer: LayerStruct, logits, x, T, topk_ids, topk_w, 
     return lib().moe_nvfp4_route_forward(ctypes.byref(layer), _ptr(logits), _ptr(x), T, _ptr(topk_ids),
                                          _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_assign), _ptr(assign_pos),
                                          _ptr(y), int(accumulate), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_nvfp4_noalloc_scratch_bytes() -> int:
+    return int(lib().moe_nvfp4_noalloc_scratch_bytes())
+
+
+def moe_nvfp4_route_forward_noalloc(layer: LayerStruct, logits, x, T, topk_ids, topk_w, expert_offsets,
+                                    sorted_assign, assign_pos, y, accumulate, stream=None) -> int:
+    return lib().moe_nvfp4_route_forward_noalloc(ctypes.byref(layer), _ptr(logits), _ptr(x), T, _ptr(topk_ids),
+                                                 _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_assign),
+                                                 _ptr(assign_pos), _ptr(y), int(accumulate), _stream(stream))
 
 
 def expert_cache_fill(cache_base, slot_bytes, num_slots, dst_slots, srcs, copy_stream=None, done_event=None) -> int:

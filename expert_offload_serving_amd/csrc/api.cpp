@@ -74,6 +74,20 @@ moe::Layer layer_of(const moe_nvfp4_layer_t& L);
 
 }  // namespace
 
+namespace moe {
+
+int set_error(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }

@@ -11,6 +11,9 @@ namespace moe {
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Records the calling thread's last-error message (api.cpp) and returns code.
+int set_error(int code, const char* fmt, ...);
+
 // Routing (route.hip)
 size_t route_ws_bytes(int T, int E, int k);
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,

@@ -199,6 +199,25 @@ int moe_nvfp4_route_forward(const moe_nvfp4_layer_t* layer, const float* logits,
                             int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* ------------------------------------------------------------------ without allocation
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * call as moe_nvfp4_route_forward with the same arguments, results and
+ * errors, except that its workspace is a fixed array inside the library
+ * (moe_nvfp4_noalloc_scratch_bytes() bytes, 32 MiB, held on each GPU the
+ * library runs on until the process ends) instead of ws/ws_bytes.  It covers
+ * the decode path (T <= 16, H <= 2560, T*k <= 1024) whose workspace fits
+ * that array (T = 16, H = 2560, I = 640, k = 8 needs 29.6 MiB); other shapes
+ * return MOE_ERR_UNSUPPORTED_SHAPE or MOE_ERR_WORKSPACE_TOO_SMALL with nothing
+ * enqueued.  It calls no allocation routine.  All calls on one GPU share its
+ * array: calls that can overlap on one GPU (different streams without
+ * ordering between them) race and must be serialised by the caller. */
+size_t moe_nvfp4_noalloc_scratch_bytes(void);
+int moe_nvfp4_route_forward_noalloc(const moe_nvfp4_layer_t* layer, const float* logits, const uint16_t* x, int T,
+                                    int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                                    int32_t* sorted_assign, int32_t* assign_pos, float* y, int accumulate,
+                                    hipStream_t stream);
+
 /* ------------------------------------------------------------------ expert cache
  * Copy n expert slots from pinned host banks into GPU cache slots
  * (issue #62 "Why TP=2 loses today" and PR #385 "What this adds": the GPU
