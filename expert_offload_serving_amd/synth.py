@@ -145,11 +145,77 @@ def pack_slot(gu, dn, H: int, I: int) -> np.ndarray:
     return out
 
 
-def random_expert_slot(rng: np.random.Generator, H: int, I: int, std: float = 0.02) -> np.ndarray:
+def random_expert_slot(rng: np.random.Generator, H: int, I: int, std: float = 0.02, fmt: str = "nvfp4") -> np.ndarray:
     """One expert: W_gu ~ N(0, std) [2I, H] and W_dn ~ N(0, std) [H, I], quantized and packed."""
     Wgu = rng.standard_normal((2 * I, H), dtype=np.float32) * np.float32(std)
     Wdn = rng.standard_normal((H, I), dtype=np.float32) * np.float32(std)
+    if fmt == "mxfp4":
+        return pack_mx_slot(mx_transposed(*quantize_mxfp4(Wgu)), mx_transposed(*quantize_mxfp4(Wdn)), H, I)
     return pack_slot(quantize_nvfp4(Wgu), quantize_nvfp4(Wdn), H, I)
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 (OCP MX FP4: E2M1 elements, one E8M0 scale per 32 along the contraction axis, no global).
+# Checkpoints store each matrix transposed: blocks_t [K/2, N] and scales_t [K/32, N].
+# ----------------------------------------------------------------------------
+
+
+def mx_slot_regions(H: int, I: int):
+    """Byte (offset, size) of the four regions of one MXFP4 slot: gate_up codes, gate_up scales, down codes,
+    down scales (no globals)."""
+    sizes = [2 * I * H // 2, 2 * I * H // 32, H * I // 2, H * I // 32]
+    out, off = [], 0
+    for sz in sizes:
+        out.append((off, sz))
+        off += sz
+    return out
+
+
+def mx_slot_nbytes(H: int, I: int) -> int:
+    off, size = mx_slot_regions(H, I)[-1]
+    return off + size
+
+
+def quantize_mxfp4(W: np.ndarray):
+    """OCP MX recipe: per 32-block, shared exponent floor(log2(amax)) - 2 (E2M1's largest exponent), stored as
+    E8M0 (bias 127, clamped to [0, 254]); elements the nearest E2M1 code of w / 2^e, ties to the even mantissa,
+    saturating at 6; an all-zero block gets scale byte 127.  Returns row-major codes [N, K/2] (even column in the
+    low nibble) and scales [N, K/32]."""
+    W = np.asarray(W, dtype=np.float32)
+    N, K = W.shape
+    assert K % 32 == 0
+    blk = np.abs(W).reshape(N, K // 32, 32).max(axis=2).astype(np.float64)
+    e = np.where(blk > 0, np.floor(np.log2(np.where(blk > 0, blk, 1.0))) - 2, 0).astype(np.int64)
+    sbyte = np.clip(e + 127, 0, 254)
+    scale = np.exp2((sbyte - 127).astype(np.float64))
+    r = (W.reshape(N, K // 32, 32).astype(np.float64) / scale[..., None]).astype(np.float32)
+    codes = encode_e2m1(r).reshape(N, K)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sbyte.astype(np.uint8)
+
+
+def mx_transposed(codes: np.ndarray, scales: np.ndarray):
+    """Row-major (codes [N, K/2], scales [N, K/32]) -> the checkpoints' (blocks_t [K/2, N], scales_t [K/32, N])."""
+    return np.ascontiguousarray(codes.T), np.ascontiguousarray(scales.T)
+
+
+def pack_mx_slot(gu_t, dn_t, H: int, I: int) -> np.ndarray:
+    """One MXFP4 slot from the transposed checkpoint tensors of gate_up (blocks_t [H/2, 2I], scales_t [H/32, 2I])
+    and down (blocks_t [I/2, H], scales_t [I/32, H]), in the slot's matrix-core operand order (the byte formulas
+    of the library header)."""
+    assert H % 128 == 0 and I % 32 == 0, (H, I)
+    N, K = 2 * I, H
+    gc = np.ascontiguousarray(gu_t[0]).T.reshape(N // 16, 16, K // 128, 4, 16).transpose(2, 0, 3, 1, 4)
+    gs = np.ascontiguousarray(gu_t[1]).T.reshape(N // 16, 16, K // 128, 4).transpose(2, 0, 3, 1)
+    N, K = H, I
+    dc = np.ascontiguousarray(dn_t[0]).T.reshape(N // 64, 4, 16, K // 32, 4, 4).transpose(3, 0, 4, 2, 1, 5)
+    ds = np.ascontiguousarray(dn_t[1]).T.reshape(N // 64, 4, 16, K // 32).transpose(3, 0, 2, 1)
+    out = np.empty(mx_slot_nbytes(H, I), dtype=np.uint8)
+    for (off, size), part in zip(mx_slot_regions(H, I), (gc, gs, dc, ds)):
+        b = np.ascontiguousarray(part).reshape(-1)
+        assert b.size == size, (b.size, size)
+        out[off:off + size] = b
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -212,32 +278,33 @@ CONFIGS = {
 }
 
 
-def flip_code_signs(slot: np.ndarray, H: int, I: int, rng: np.random.Generator) -> np.ndarray:
+def flip_code_signs(slot: np.ndarray, H: int, I: int, rng: np.random.Generator, fmt: str = "nvfp4") -> np.ndarray:
     """A copy of `slot` whose E2M1 codes have their sign bits flipped by a random mask.
 
     The quantizer is sign-symmetric (scales and globals come from magnitudes), so the result is exactly the
     quantization of the base weights with those signs flipped: another properly quantized expert whose
     weights, for the symmetric N(0, std) draw, have the same distribution."""
     out = slot.copy()
-    regions = slot_regions(H, I)
-    for r in (0, 3):  # gate_up codes, down codes
+    regions = slot_regions(H, I) if fmt == "nvfp4" else mx_slot_regions(H, I)
+    for r in ((0, 3) if fmt == "nvfp4" else (0, 2)):  # gate_up codes, down codes
         off, size = regions[r]
         out[off:off + size] ^= rng.integers(0, 256, size, dtype=np.uint8) & np.uint8(0x88)
     return out
 
 
-def make_bank(rng: np.random.Generator, H: int, I: int, n_slots: int, n_distinct: int | None = None) -> np.ndarray:
+def make_bank(rng: np.random.Generator, H: int, I: int, n_slots: int, n_distinct: int | None = None,
+              fmt: str = "nvfp4") -> np.ndarray:
     """n_slots quantized expert slots, every one distinct.  With n_distinct < n_slots only n_distinct experts
     are quantized; slot j >= n_distinct is base expert j % n_distinct with the signs of its codes flipped by a
     mask of its own (flip_code_signs), which keeps generation fast while no two slots hold the same weights."""
     nd = n_slots if n_distinct is None else max(1, min(n_distinct, n_slots))
-    sb = slot_nbytes(H, I)
+    sb = slot_nbytes(H, I) if fmt == "nvfp4" else mx_slot_nbytes(H, I)
     bank = np.empty((n_slots, sb), dtype=np.uint8)
     for j in range(nd):
-        bank[j] = random_expert_slot(rng, H, I)
+        bank[j] = random_expert_slot(rng, H, I, fmt=fmt)
     flips = rng.spawn(1)[0] if n_slots > nd else None
     for j in range(nd, n_slots):
-        bank[j] = flip_code_signs(bank[j % nd], H, I, flips)
+        bank[j] = flip_code_signs(bank[j % nd], H, I, flips, fmt)
     return bank
 
 
@@ -270,14 +337,15 @@ def make_logits(rng: np.random.Generator, T: int, E: int, kind: str) -> np.ndarr
 
 
 def make_layer(name: str, T: int | None = None, n_distinct: int | None = None, seed: int | None = None,
-               shared: bool = True) -> LayerInputs:
-    """Build one configuration's inputs from its seed: streams (weights, x, logits, w_g)."""
+               shared: bool = True, fmt: str = "nvfp4") -> LayerInputs:
+    """Build one configuration's inputs from its seed: streams (weights, x, logits, w_g).  fmt: the bank's slot
+    format, "nvfp4" or "mxfp4"."""
     H, I, E, k, T0, seed0, kind = CONFIGS[name]
     T = T0 if T is None else T
     seed = seed0 if seed is None else seed
     r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
     n_slots = E + 1
-    bank = make_bank(r_w, H, I, n_slots, n_distinct)
+    bank = make_bank(r_w, H, I, n_slots, n_distinct, fmt)
     x = f32_to_bf16_bits(r_x.standard_normal((T, H), dtype=np.float32))
     logits = make_logits(r_l, T, E, kind)
     wg = f32_to_bf16_bits(r_g.standard_normal(H, dtype=np.float32) * np.float32(0.02))

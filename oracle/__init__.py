@@ -71,6 +71,20 @@ def lib():
                                      ctypes.c_void_p, ctypes.c_int, _f32p, ctypes.c_int]
         L.oracle_slice_slot.restype = ctypes.c_int
         L.oracle_slice_slot.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p]
+        L.oracle_e8m0.restype = ctypes.c_double
+        L.oracle_e8m0.argtypes = [ctypes.c_int]
+        L.oracle_mx_dequant_t.restype = None
+        L.oracle_mx_dequant_t.argtypes = [_u8p, _u8p, ctypes.c_int, ctypes.c_int, _f32p]
+        L.oracle_mx_slot_bytes.restype = ctypes.c_size_t
+        L.oracle_mx_slot_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.oracle_mx_dequant_slot.restype = ctypes.c_int
+        L.oracle_mx_dequant_slot.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f32p]
+        L.oracle_mx_unpack_slot.restype = ctypes.c_int
+        L.oracle_mx_unpack_slot.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _u8p]
+        L.oracle_mx_slice_slot.restype = ctypes.c_int
+        L.oracle_mx_slice_slot.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p]
+        L.oracle_mx_forward.restype = ctypes.c_int
+        L.oracle_mx_forward.argtypes = L.oracle_forward.argtypes
         L.oracle_lru_run.restype = ctypes.c_int
         L.oracle_lru_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, _i32p, _i32p, _i32p, ctypes.c_void_p, ctypes.c_void_p]
@@ -167,8 +181,10 @@ def shared_gate(x, wg) -> np.ndarray:
     return s
 
 
-def forward(H, I, E, k, bank, slot_of_expert, shared_slot, wg, x, ids, w, tokens=None, nthreads: int = 0):
-    """Layer output y (f32) for all tokens, or for the listed tokens in list order."""
+def forward(H, I, E, k, bank, slot_of_expert, shared_slot, wg, x, ids, w, tokens=None, nthreads: int = 0,
+            fmt: str = "nvfp4"):
+    """Layer output y (f32) for all tokens, or for the listed tokens in list order.  fmt: "nvfp4" or "mxfp4"
+    (the bank's slot format)."""
     bank = np.ascontiguousarray(bank, dtype=np.uint8)
     x = np.ascontiguousarray(x, dtype=np.uint16)
     T = x.shape[0]
@@ -181,7 +197,9 @@ def forward(H, I, E, k, bank, slot_of_expert, shared_slot, wg, x, ids, w, tokens
         keep = np.ascontiguousarray(tokens, dtype=np.int32)
         tok_ptr, n = keep.ctypes.data, keep.size
     y = np.empty((n, H), dtype=np.float32)
-    rc = lib().oracle_forward(H, I, E, k, bank.reshape(-1), bank.shape[-1] if bank.ndim == 2 else slot_bytes(H, I),
+    fn = {"nvfp4": lib().oracle_forward, "mxfp4": lib().oracle_mx_forward}[fmt]
+    sb = bank.shape[-1] if bank.ndim == 2 else (slot_bytes(H, I) if fmt == "nvfp4" else mx_slot_bytes(H, I))
+    rc = fn(H, I, E, k, bank.reshape(-1), sb,
                               np.ascontiguousarray(slot_of_expert, dtype=np.int32), int(shared_slot),
                               np.ascontiguousarray(wg, dtype=np.uint16), x, T, ids, w, tok_ptr, n, y, int(nthreads))
     if rc != 0:
@@ -211,3 +229,50 @@ def lru_run(ids, E: int, C: int, want_maps: bool = True):
     if rc != 0:
         raise ValueError("cache smaller than one layer-step's distinct experts")
     return hits, misses, smap, mslots
+
+
+# ---------------------------------------------------------------- MXFP4
+
+def e8m0(byte: int) -> float:
+    return lib().oracle_e8m0(int(byte))
+
+
+def mx_slot_bytes(H: int, I: int) -> int:
+    return int(lib().oracle_mx_slot_bytes(H, I))
+
+
+def mx_dequant_t(blocks_t, scales_t) -> np.ndarray:
+    """fp32 W [N, K] of an MXFP4 matrix stored transposed: blocks_t u8 [K/2, N], scales_t u8 [K/32, N]."""
+    blocks_t = np.ascontiguousarray(blocks_t, dtype=np.uint8)
+    scales_t = np.ascontiguousarray(scales_t, dtype=np.uint8)
+    K, N = blocks_t.shape[0] * 2, blocks_t.shape[1]
+    assert scales_t.shape == (K // 32, N)
+    out = np.empty((N, K), dtype=np.float32)
+    lib().oracle_mx_dequant_t(blocks_t, scales_t, N, K, out)
+    return out
+
+
+def mx_dequant_slot(slot, H: int, I: int, matrix: int) -> np.ndarray:
+    N, K = _matrix_shape(H, I, matrix)
+    slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
+    out = np.empty((N, K), dtype=np.float32)
+    lib().oracle_mx_dequant_slot(slot, H, I, matrix, out)
+    return out
+
+
+def mx_unpack_slot(slot, H: int, I: int, matrix: int):
+    """The transposed checkpoint tensors (blocks_t [K/2, N], scales_t [K/32, N]) of one matrix of an MXFP4 slot."""
+    N, K = _matrix_shape(H, I, matrix)
+    slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
+    blocks_t = np.empty((K // 2, N), dtype=np.uint8)
+    scales_t = np.empty((K // 32, N), dtype=np.uint8)
+    lib().oracle_mx_unpack_slot(slot, H, I, matrix, blocks_t, scales_t)
+    return blocks_t, scales_t
+
+
+def mx_slice_slot(slot, H: int, I: int, r: int, n: int) -> np.ndarray:
+    slot = np.ascontiguousarray(slot, dtype=np.uint8).reshape(-1)
+    out = np.empty(mx_slot_bytes(H, I // n), dtype=np.uint8)
+    if lib().oracle_mx_slice_slot(slot, H, I, r, n, out) != 0:
+        raise ValueError("slice is not a valid slot shape (I/n must be a multiple of 32)")
+    return out

@@ -28,7 +28,12 @@
  *    softmax followed by renormalisation over the top k), ties in selection
  *    broken by the lower expert index;
  *  - activation: SwiGLU, silu(gate) * up, no clamp;
- *  - shared gate: s_t = sigmoid(x_t . w_g), applied after the shared expert.
+ *  - shared gate: s_t = sigmoid(x_t . w_g), applied after the shared expert;
+ *  - the MXFP4 bank format (issue #62 "What it touches" names it, its
+ *    transposed blocks_t [K//2, N] and its 32-wide fp4 scale blocks): E2M1
+ *    elements times one OCP E8M0 scale per 32 consecutive elements along
+ *    the contraction axis, no per-row global; the scales are stored
+ *    transposed like the blocks, scales_t [K/32, N]; W = f32(e2m1 * e8m0).
  *
  * Arithmetic: fp32 dequant, double accumulation, one rounding to f32 at the
  * output.  Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp.
@@ -299,10 +304,37 @@ static int cmp_long(const void* a, const void* b) {
  * matrices (the definition of the weights), every (token, expert) output
  * o_tj is formed from them and kept in double, and each token's outputs are
  * then added in the order j = 0..k-1, shared last. */
+/* Dequantises both matrices of a slot: Wgu [2I, H] and Wdn [H, I], fp32 row-major. */
+typedef void (*slot_dequant_fn)(const uint8_t* slot, int H, int I, float* Wgu, float* Wdn);
+
+static void nvfp4_slot_dequant(const uint8_t* slot, int H, int I, float* Wgu, float* Wdn) {
+    mat_view gu = view_matrix(slot, H, I, 0), dn = view_matrix(slot, H, I, 1);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int r = 0; r < 2 * I + H; ++r) {
+        if (r < 2 * I) dequant_view_row(&gu, r, Wgu + (size_t)r * H);
+        else dequant_view_row(&dn, r - 2 * I, Wdn + (size_t)(r - 2 * I) * I);
+    }
+}
+
+static int forward_core(int H, int I, int E, int k, const uint8_t* bank, size_t slot_bytes,
+                        const int32_t* slot_of_expert, long shared_slot, const uint16_t* wg, const uint16_t* x, int T,
+                        const int32_t* ids, const float* w, const int32_t* tokens, int n_tokens, float* y,
+                        int nthreads, slot_dequant_fn dequant_slot_matrices);
+
 int oracle_forward(int H, int I, int E, int k, const uint8_t* bank, size_t slot_bytes, const int32_t* slot_of_expert,
                    long shared_slot, const uint16_t* wg, const uint16_t* x, int T, const int32_t* ids, const float* w,
                    const int32_t* tokens, int n_tokens, float* y, int nthreads) {
     if (!oracle_shape_ok(H, I) || slot_bytes != oracle_slot_bytes(H, I)) return -1;
+    return forward_core(H, I, E, k, bank, slot_bytes, slot_of_expert, shared_slot, wg, x, T, ids, w, tokens, n_tokens,
+                        y, nthreads, nvfp4_slot_dequant);
+}
+
+static int forward_core(int H, int I, int E, int k, const uint8_t* bank, size_t slot_bytes,
+                        const int32_t* slot_of_expert, long shared_slot, const uint16_t* wg, const uint16_t* x, int T,
+                        const int32_t* ids, const float* w, const int32_t* tokens, int n_tokens, float* y,
+                        int nthreads, slot_dequant_fn dequant_slot_matrices) {
     if (tokens == NULL) n_tokens = T;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -336,15 +368,7 @@ int oracle_forward(int H, int I, int E, int k, const uint8_t* bank, size_t slot_
     float* Wgu = (float*)malloc(sizeof(float) * (size_t)2 * I * H);
     float* Wdn = (float*)malloc(sizeof(float) * (size_t)H * I);
     for (size_t u = 0; u < nu; ++u) {
-        const uint8_t* slot = bank + (size_t)slots[u] * slot_bytes;
-        mat_view gu = view_matrix(slot, H, I, 0), dn = view_matrix(slot, H, I, 1);
-#ifdef _OPENMP
-#pragma omp parallel for schedule(static)
-#endif
-        for (int r = 0; r < 2 * I + H; ++r) {
-            if (r < 2 * I) dequant_view_row(&gu, r, Wgu + (size_t)r * H);
-            else dequant_view_row(&dn, r - 2 * I, Wdn + (size_t)(r - 2 * I) * I);
-        }
+        dequant_slot_matrices(bank + (size_t)slots[u] * slot_bytes, H, I, Wgu, Wdn);
 #ifdef _OPENMP
 #pragma omp parallel
 #endif
@@ -385,6 +409,167 @@ int oracle_forward(int H, int I, int E, int k, const uint8_t* bank, size_t slot_
     }
     free(use); free(slots); free(out); free(Wgu); free(Wdn);
     return 0;
+}
+
+/* ---------------------------------------------------------------- MXFP4 */
+
+/* The second fp4 bank format of issue #62 "What it touches": OCP MX FP4,
+ * E2M1 elements with one shared E8M0 scale per 32 consecutive elements along
+ * the contraction axis (the fp4 scale-block size of that section) and no
+ * per-row global.  E8M0: 8 exponent bits, bias 127, no sign or mantissa;
+ * 0xFF is NaN. */
+double oracle_e8m0(int byte) { return (byte & 0xFF) == 0xFF ? NAN : ldexp(1.0, (byte & 0xFF) - 127); }
+
+/* An MXFP4 matrix W [N, K] as its checkpoints store it, transposed
+ * (issue #62 "What it touches": blocks_t [K//2, N]): byte (j, n) of
+ * blocks_t holds W[n, 2j] in its low nibble and W[n, 2j+1] in its high
+ * nibble; the scales are transposed the same way, scales_t [K/32, N].
+ *     W[n, c] = f32( e2m1(code(n, c)) * e8m0(scales_t[c/32, n]) )
+ * (the product is exact in double; one rounding to f32). */
+void oracle_mx_dequant_t(const uint8_t* blocks_t, const uint8_t* scales_t, int N, int K, float* out) {
+    for (int n = 0; n < N; ++n)
+        for (int c = 0; c < K; ++c) {
+            int code = (blocks_t[(size_t)(c / 2) * N + n] >> (4 * (c & 1))) & 0xF;
+            out[(size_t)n * K + c] = (float)(oracle_e2m1(code) * oracle_e8m0(scales_t[(size_t)(c / 32) * N + n]));
+        }
+}
+
+/* Byte offsets in an MXFP4 slot (the library header's formulas):
+ * gate_up [2I, H] keeps a 16-row x 128-column tile per 1 KiB, lane record
+ * 16*a + i holding row i and the 32 columns [32a, 32a+32) of the tile; its
+ * scales are one byte per (row, 32-column block), the byte of lane record
+ * 16*a + i in a 64-byte record per tile.  down [H, I] keeps a 64-row x
+ * 32-column tile per 1 KiB exactly like the NVFP4 down matrix; its scales
+ * are 64 bytes per tile, byte 4*i + j for row 16*j + i of the tile. */
+static size_t mx_gu_code_at(int N, int r, int c) {
+    size_t q = c / 128, a = (c / 32) % 4, e = c % 32, t = r / 16, i = r % 16;
+    return 16 * (64 * (q * (N / 16) + t) + 16 * a + i) + e / 2;
+}
+static size_t mx_gu_scale_at(int N, int r, int b) {
+    size_t q = b / 4, a = b % 4, t = r / 16, i = r % 16;
+    return 64 * (q * (N / 16) + t) + 16 * a + i;
+}
+static size_t mx_dn_code_at(int N, int r, int c) {
+    size_t kc = c / 32, g = (c / 8) % 4, e = c % 8, p = r / 64, j = (r / 16) % 4, i = r % 16;
+    return 16 * (64 * (kc * (N / 64) + p) + 16 * g + i) + 4 * j + e / 2;
+}
+static size_t mx_dn_scale_at(int N, int r, int b) {
+    size_t p = r / 64, j = (r / 16) % 4, i = r % 16;
+    return 64 * ((size_t)b * (N / 64) + p) + 4 * i + j;
+}
+
+/* Region order in an MXFP4 slot: gate_up codes, gate_up scales, down
+ * codes, down scales, without padding. */
+size_t oracle_mx_slot_bytes(int H, int I) {
+    return (size_t)2 * I * H / 2 + (size_t)2 * I * H / 32 + (size_t)H * I / 2 + (size_t)H * I / 32;
+}
+
+typedef struct {
+    const uint8_t *codes, *scales;
+    int N, K, down;
+} mx_view;
+
+static mx_view mx_view_matrix(const uint8_t* slot, int H, int I, int down) {
+    size_t gc = (size_t)2 * I * H / 2, gs = (size_t)2 * I * H / 32, dc = (size_t)H * I / 2;
+    mx_view v;
+    if (!down) {
+        v.codes = slot;
+        v.scales = slot + gc;
+        v.N = 2 * I, v.K = H;
+    } else {
+        v.codes = slot + gc + gs;
+        v.scales = v.codes + dc;
+        v.N = H, v.K = I;
+    }
+    v.down = down;
+    return v;
+}
+
+static int mx_code_of(const mx_view* v, int r, int c) {
+    size_t o = v->down ? mx_dn_code_at(v->N, r, c) : mx_gu_code_at(v->N, r, c);
+    return (v->codes[o] >> (4 * (c & 1))) & 0xF;
+}
+
+static int mx_scale_of(const mx_view* v, int r, int b) {
+    return v->scales[v->down ? mx_dn_scale_at(v->N, r, b) : mx_gu_scale_at(v->N, r, b)];
+}
+
+/* Row r of an MXFP4 slot matrix, dequantised: out[c] = f32(e2m1 * e8m0). */
+static void mx_dequant_view_row(const mx_view* v, int r, float* out) {
+    for (int c = 0; c < v->K; ++c)
+        out[c] = (float)(oracle_e2m1(mx_code_of(v, r, c)) * oracle_e8m0(mx_scale_of(v, r, c / 32)));
+}
+
+/* Dequantise matrix 0 (gate_up, [2I, H]) or 1 (down, [H, I]) of an MXFP4 slot. */
+int oracle_mx_dequant_slot(const uint8_t* slot, int H, int I, int matrix, float* out) {
+    if (!oracle_shape_ok(H, I) || matrix < 0 || matrix > 1) return -1;
+    mx_view v = mx_view_matrix(slot, H, I, matrix);
+    for (int r = 0; r < v.N; ++r) mx_dequant_view_row(&v, r, out + (size_t)r * v.K);
+    return 0;
+}
+
+/* Read matrix 0 or 1 of an MXFP4 slot back into the checkpoints' transposed
+ * tensors: blocks_t [K/2, N] and scales_t [K/32, N]. */
+int oracle_mx_unpack_slot(const uint8_t* slot, int H, int I, int matrix, uint8_t* blocks_t, uint8_t* scales_t) {
+    if (!oracle_shape_ok(H, I) || matrix < 0 || matrix > 1) return -1;
+    mx_view v = mx_view_matrix(slot, H, I, matrix);
+    for (int r = 0; r < v.N; ++r) {
+        for (int c = 0; c < v.K; c += 2)
+            blocks_t[(size_t)(c / 2) * v.N + r] = (uint8_t)(mx_code_of(&v, r, c) | (mx_code_of(&v, r, c + 1) << 4));
+        for (int b = 0; b < v.K / 32; ++b) scales_t[(size_t)b * v.N + r] = (uint8_t)mx_scale_of(&v, r, b);
+    }
+    return 0;
+}
+
+/* Slice r of n along the intermediate axis of an MXFP4 slot, I_l = I / n.
+ * In the checkpoints' transposed tensors this is (issue #62 "What it
+ * touches": mxfp4's slice runs along N and its scales slice differently):
+ * gate_up blocks_t [H/2, 2I] and scales_t [H/32, 2I] keep the columns
+ * [r*I_l, (r+1)*I_l) and [I + r*I_l, I + (r+1)*I_l); down blocks_t [I/2, H]
+ * keeps the rows [r*I_l/2, (r+1)*I_l/2) and scales_t [I/32, H] the rows
+ * [r*I_l/32, (r+1)*I_l/32).  Written element by element through the byte
+ * formulas.  Returns 0, or -1 unless I_l is a multiple of 32. */
+int oracle_mx_slice_slot(const uint8_t* src, int H, int I, int r, int n, uint8_t* dst) {
+    if (n <= 0 || r < 0 || r >= n || I % n || !oracle_shape_ok(H, I)) return -1;
+    int Il = I / n;
+    if (!oracle_shape_ok(H, Il)) return -1;
+    memset(dst, 0, oracle_mx_slot_bytes(H, Il));
+    mx_view sg = mx_view_matrix(src, H, I, 0), sd = mx_view_matrix(src, H, I, 1);
+    mx_view dg = mx_view_matrix(dst, H, Il, 0), dd = mx_view_matrix(dst, H, Il, 1);
+    uint8_t *dgc = (uint8_t*)dg.codes, *dgs = (uint8_t*)dg.scales, *ddc = (uint8_t*)dd.codes,
+            *dds = (uint8_t*)dd.scales;
+    for (int rr = 0; rr < 2 * Il; ++rr) {
+        int from = rr < Il ? r * Il + rr : I + r * Il + (rr - Il);
+        for (int c = 0; c < H; ++c) dgc[mx_gu_code_at(2 * Il, rr, c)] |= (uint8_t)(mx_code_of(&sg, from, c) << (4 * (c & 1)));
+        for (int b = 0; b < H / 32; ++b) dgs[mx_gu_scale_at(2 * Il, rr, b)] = (uint8_t)mx_scale_of(&sg, from, b);
+    }
+    for (int row = 0; row < H; ++row) {
+        for (int c = 0; c < Il; ++c)
+            ddc[mx_dn_code_at(H, row, c)] |= (uint8_t)(mx_code_of(&sd, row, r * Il + c) << (4 * (c & 1)));
+        for (int b = 0; b < Il / 32; ++b) dds[mx_dn_scale_at(H, row, b)] = (uint8_t)mx_scale_of(&sd, row, r * Il / 32 + b);
+    }
+    return 0;
+}
+
+static void mxfp4_slot_dequant(const uint8_t* slot, int H, int I, float* Wgu, float* Wdn) {
+    mx_view gu = mx_view_matrix(slot, H, I, 0), dn = mx_view_matrix(slot, H, I, 1);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int r = 0; r < 2 * I + H; ++r) {
+        if (r < 2 * I) mx_dequant_view_row(&gu, r, Wgu + (size_t)r * H);
+        else mx_dequant_view_row(&dn, r - 2 * I, Wdn + (size_t)(r - 2 * I) * I);
+    }
+}
+
+/* The layer of oracle_forward with MXFP4 expert slots (same routing,
+ * shared expert, SwiGLU and combine; only the weight decode differs). */
+int oracle_mx_forward(int H, int I, int E, int k, const uint8_t* bank, size_t slot_bytes,
+                      const int32_t* slot_of_expert, long shared_slot, const uint16_t* wg, const uint16_t* x, int T,
+                      const int32_t* ids, const float* w, const int32_t* tokens, int n_tokens, float* y, int nthreads) {
+    if (!oracle_shape_ok(H, I) || slot_bytes != oracle_mx_slot_bytes(H, I)) return -1;
+    return forward_core(H, I, E, k, bank, slot_bytes, slot_of_expert, shared_slot, wg, x, T, ids, w, tokens, n_tokens,
+                        y, nthreads, mxfp4_slot_dequant);
 }
 
 /* ---------------------------------------------------------------- slicing */

@@ -463,3 +463,163 @@ def test_lru_invariants():
     h2, m2, _, _ = oracle.lru_run(ids, E=E, C=L * E)
     first = sum(len(set(ids[:, l].reshape(-1).tolist())) for l in range(L))
     assert int(m2.sum()) == first
+
+
+# ---------------------------------------------------------------- MXFP4 (the second fp4 bank format)
+
+def test_e8m0_all_bytes_match_torch_decoder_and_closed_form():
+    """E8M0 (OCP MX shared scale): 2^(byte - 127), 0xFF is NaN; every byte against torch's float8_e8m0fnu
+    decoder and spot values of the closed form."""
+    lib_vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    for b in range(256):
+        got = oracle.e8m0(b)
+        if b == 255:
+            assert math.isnan(got) and math.isnan(lib_vals[b])
+        else:
+            assert got == lib_vals[b] == 2.0 ** (b - 127), b
+    assert oracle.e8m0(127) == 1.0 and oracle.e8m0(0) == 2.0 ** -127 and oracle.e8m0(254) == 2.0 ** 127
+
+
+def _independent_mx_dequant_t(blocks_t, scales_t):
+    """numpy decode of the transposed layout: W[n, c] from nibble c%2 of blocks_t[c//2, n] and scales_t[c//32, n],
+    element values from the OCP E2M1 table, scales from torch's E8M0 decoder."""
+    e2m1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
+    e8m0 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    K2, N = blocks_t.shape
+    codes = np.empty((N, 2 * K2), dtype=np.int64)
+    codes[:, 0::2] = (blocks_t.T & 15)
+    codes[:, 1::2] = (blocks_t.T >> 4)
+    scale = np.repeat(e8m0[scales_t.T.astype(np.int64)], 32, axis=1)
+    with np.errstate(over="ignore", invalid="ignore"):
+        return (e2m1[codes] * scale).astype(np.float32)
+
+
+def _bits_equal(a, b):
+    nan_a, nan_b = np.isnan(a), np.isnan(b)
+    assert np.array_equal(nan_a, nan_b)
+    assert np.array_equal(a[~nan_a].view(np.uint32), b[~nan_b].view(np.uint32))
+
+
+def test_mx_dequant_every_code_and_scale_byte_bitexact():
+    """Every (code, E8M0 byte) pair, including 0 (2^-127: f32 subnormal products), 254 (6 * 2^127 overflows f32
+    to inf) and 255 (NaN), against the independent decode."""
+    N, K = 256, 512
+    codes_row = np.array([(2 * j % 16) | (((2 * j + 1) % 16) << 4) for j in range(K // 2)], dtype=np.uint8)
+    blocks_t = np.tile(codes_row[:, None], (1, N))                 # [K/2, N], every code in every block
+    scales_t = np.tile(np.arange(N, dtype=np.uint8)[None, :], (K // 32, 1))  # column n uses scale byte n
+    scales_t[1::2] = ((scales_t[1::2].astype(np.int64) + 101) % 256).astype(np.uint8)  # other bytes, odd blocks
+    _bits_equal(oracle.mx_dequant_t(blocks_t, scales_t), _independent_mx_dequant_t(blocks_t, scales_t))
+
+
+def test_mx_dequant_transposed_layout_hand_case():
+    """One hand-worked element per layout rule: blocks_t[j, n] holds W[n, 2j] low and W[n, 2j+1] high;
+    scales_t[b, n] scales W[n, 32b .. 32b+31]."""
+    N, K = 3, 64
+    blocks_t = np.zeros((K // 2, N), dtype=np.uint8)
+    scales_t = np.full((K // 32, N), 127, dtype=np.uint8)
+    blocks_t[5, 2] = 0x7A          # W[2, 10] = e2m1(0xA) = -1.0, W[2, 11] = e2m1(0x7) = 6.0
+    scales_t[0, 2] = 129           # block 0 of row 2 scaled by 4
+    blocks_t[20, 1] = 0x03         # W[1, 40] = 1.5 in block 1
+    scales_t[1, 1] = 120           # times 2^-7
+    W = oracle.mx_dequant_t(blocks_t, scales_t)
+    want = np.zeros((N, K), dtype=np.float32)
+    want[2, 10], want[2, 11], want[1, 40] = -4.0, 24.0, 1.5 * 2.0 ** -7
+    assert np.array_equal(W, want)
+
+
+def _mx_formula_offsets(N, K, down):
+    """The MXFP4 slot's byte formulas re-derived in plain loops: code byte and scale byte of every element."""
+    code = np.empty((N, K), dtype=np.int64)
+    scale = np.empty((N, K // 32), dtype=np.int64)
+    for r in range(N):
+        i = r % 16
+        for c in range(K):
+            if not down:   # 16-row x 128-column tile per KiB; lane 16a + i holds columns [32a, 32a + 32)
+                q, a, e, t = c // 128, (c // 32) % 4, c % 32, r // 16
+                code[r, c] = 16 * (64 * (q * (N // 16) + t) + 16 * a + i) + e // 2
+            else:          # 64-row x 32-column tile per KiB, as the NVFP4 down matrix
+                kc, g, e, p, j = c // 32, (c // 8) % 4, c % 8, r // 64, (r // 16) % 4
+                code[r, c] = 16 * (64 * (kc * (N // 64) + p) + 16 * g + i) + 4 * j + e // 2
+        for b in range(K // 32):
+            if not down:
+                q, a, t = b // 4, b % 4, r // 16
+                scale[r, b] = 64 * (q * (N // 16) + t) + 16 * a + i
+            else:
+                p, j = r // 64, (r // 16) % 4
+                scale[r, b] = 64 * (b * (N // 64) + p) + 4 * i + j
+    return code, scale
+
+
+def test_mx_slot_operand_order_matches_formulas():
+    """The packer writes, and the oracle reads back, exactly the byte formulas: the formulas re-derived in
+    plain loops place every element, the oracle's unpacking returns the checkpoint tensors, and the slot
+    dequant equals the transposed-layout dequant bit for bit."""
+    H, I = 256, 64
+    rng = np.random.default_rng(21)
+    gu = (rng.integers(0, 256, (H // 2, 2 * I), dtype=np.uint8), rng.integers(100, 150, (H // 32, 2 * I), dtype=np.uint8))
+    dn = (rng.integers(0, 256, (I // 2, H), dtype=np.uint8), rng.integers(100, 150, (I // 32, H), dtype=np.uint8))
+    slot = synth.pack_mx_slot(gu, dn, H, I)
+    regions = synth.mx_slot_regions(H, I)
+    for m, ((bt, st), (creg, sreg)) in enumerate(zip((gu, dn), ((0, 1), (2, 3)))):
+        N, K = bt.shape[1], bt.shape[0] * 2
+        code_off, scale_off = _mx_formula_offsets(N, K, m == 1)
+        cbase, sbase = regions[creg][0], regions[sreg][0]
+        nib = np.empty((N, K), dtype=np.int64)
+        nib[:, 0::2], nib[:, 1::2] = bt.T & 15, bt.T >> 4
+        got_nib = (slot[cbase + code_off] >> (4 * (np.arange(K)[None, :] % 2))) & 15
+        assert np.array_equal(got_nib, nib)
+        assert np.array_equal(slot[sbase + scale_off], st.T)
+        b2, s2 = oracle.mx_unpack_slot(slot, H, I, m)
+        assert np.array_equal(b2, bt) and np.array_equal(s2, st)
+        _bits_equal(oracle.mx_dequant_slot(slot, H, I, m), _independent_mx_dequant_t(bt, st))
+    assert slot.size == oracle.mx_slot_bytes(H, I) == 3 * I * H // 2 + 3 * I * H // 32
+
+
+def test_mx_slice_along_n_and_k_equals_slice_of_dequant():
+    """Slicing I (issue #62: mxfp4's slice runs along N of the transposed gate_up and along K of down): the
+    dequant of each slice is the matching slice of the full dequant, and the checkpoint tensors of the slice are
+    column / row slices of the full ones."""
+    H, I, n = 256, 128, 2
+    slot = synth.random_expert_slot(np.random.default_rng(8), H, I, fmt="mxfp4")
+    Wgu, Wdn = oracle.mx_dequant_slot(slot, H, I, 0), oracle.mx_dequant_slot(slot, H, I, 1)
+    (gb, gs), (db, ds) = oracle.mx_unpack_slot(slot, H, I, 0), oracle.mx_unpack_slot(slot, H, I, 1)
+    Il = I // n
+    for r in range(n):
+        sl = oracle.mx_slice_slot(slot, H, I, r, n)
+        rows = np.r_[r * Il:(r + 1) * Il, I + r * Il:I + (r + 1) * Il]
+        _bits_equal(oracle.mx_dequant_slot(sl, H, Il, 0), Wgu[rows])
+        _bits_equal(oracle.mx_dequant_slot(sl, H, Il, 1), Wdn[:, r * Il:(r + 1) * Il])
+        sgb, sgs = oracle.mx_unpack_slot(sl, H, Il, 0)
+        sdb, sds = oracle.mx_unpack_slot(sl, H, Il, 1)
+        assert np.array_equal(sgb, gb[:, rows]) and np.array_equal(sgs, gs[:, rows])          # along N
+        assert np.array_equal(sdb, db[r * Il // 2:(r + 1) * Il // 2])                         # along K/2
+        assert np.array_equal(sds, ds[r * Il // 32:(r + 1) * Il // 32])
+    with pytest.raises(ValueError):
+        oracle.mx_slice_slot(slot, H, I, 0, 8)  # I/n = 16: not a whole scale block
+
+
+def test_mx_forward_matches_dense_bruteforce():
+    """The MXFP4 layer (tiny shape) against a float64 numpy brute force over the independently decoded weights."""
+    H, I, E, k, T = 256, 64, 8, 2, 5
+    rng = np.random.default_rng(31)
+    bank = synth.make_bank(rng, H, I, E + 1, None, fmt="mxfp4")
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wg = synth.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32) * 0.02)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w = oracle.route(logits, k)
+    got = oracle.forward(H, I, E, k, bank, np.arange(E, dtype=np.int32), E, wg, x, ids, w, fmt="mxfp4")
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    gf = synth.bf16_bits_to_f32(wg).astype(np.float64)
+    def ffn(slot, xv):
+        (gb, gs), (db, ds) = oracle.mx_unpack_slot(slot, H, I, 0), oracle.mx_unpack_slot(slot, H, I, 1)
+        Wgu = _independent_mx_dequant_t(gb, gs).astype(np.float64)
+        Wdn = _independent_mx_dequant_t(db, ds).astype(np.float64)
+        a = Wgu @ xv
+        h = a[:I] / (1.0 + np.exp(-a[:I])) * a[I:]
+        return Wdn @ h
+    want = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            want[t] += float(w[t, j]) * ffn(bank[ids[t, j]], xf[t])
+        want[t] += 1.0 / (1.0 + np.exp(-(xf[t] @ gf))) * ffn(bank[E], xf[t])
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6 * np.abs(want).max())
