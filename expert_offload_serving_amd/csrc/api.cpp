@@ -372,6 +372,116 @@ int moe_release_streams(void) {
 
 }  // extern "C"
 
+// ------------------------------------------------------------------ MXFP4 bank format
+
+namespace {
+
+// Every check of an MXFP4 forward call (nothing is enqueued here).
+int validate_mx_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
+                        const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
+                        const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes) {
+    if (!layer) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_mxfp4_forward: layer is NULL");
+    const moe_nvfp4_layer_t& L = *layer;
+    if (!shape_ok(L.H, L.I))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H must be a positive multiple of 128 and I of 32 (got H=%d, I=%d)",
+                    L.H, L.I);
+    int rc = check_route_shape(T, L.E, L.k);
+    if (rc != MOE_OK) return rc;
+    if (accumulate != 0 && accumulate != 1) return fail(MOE_ERR_INVALID_ARGUMENT, "accumulate must be 0 or 1");
+    const size_t sb = moe::mx_slot_geom(L.H, L.I).total;
+    if (L.slot_bytes != sb)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "slot_bytes %zu does not match an MXFP4 slot at H=%d, I=%d (%zu bytes)",
+                    L.slot_bytes, L.H, L.I, sb);
+    if (T == 0) return MOE_OK;
+    if (!moe::decode_path(T, L.H, L.I, L.k) || !moe::mx_decode_shape_supported(L.H, L.I))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                    "MXFP4 layers run the decode path only (T <= %d, T*k <= %d, H <= 2560; got T=%d H=%d k=%d)",
+                    moe::kDecodeMaxT, moe::kDecodeMaxAssign, T, L.H, L.k);
+    if (!L.bank_base || !L.slot_of_expert || L.num_slots < 1)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "layer bank, slot map and num_slots are required");
+    if (reinterpret_cast<uintptr_t>(L.bank_base) % 256 != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "bank_base must be 256-byte aligned");
+    if (L.shared_slot && (reinterpret_cast<uintptr_t>(L.shared_slot) % 64 != 0))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "shared_slot must be 64-byte aligned");
+    if (L.shared_slot && !L.shared_gate_w)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "shared_gate_w is required with a shared expert");
+    if (!x || !topk_ids || !topk_w || !expert_offsets || !sorted_assign || !assign_pos || !y)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_mxfp4_forward: null pointer argument");
+    const size_t need = moe::forward_ws_bytes(T, L.H, L.I, L.E, L.k);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "forward workspace %zu < %zu bytes", ws_bytes, need);
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_mxfp4_slot_bytes(int H, int I) {
+    if (!shape_ok(H, I)) return 0;
+    return moe::mx_slot_geom(H, I).total;
+}
+
+size_t moe_mxfp4_forward_workspace_bytes(int T, int H, int I, int E, int k) {
+    if (!shape_ok(H, I) || check_route_shape(T, E, k) != MOE_OK || !moe::decode_path(T, H, I, k)) return 0;
+    return moe::forward_ws_bytes(T, H, I, E, k);
+}
+
+int moe_mxfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
+                      const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
+                      const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+    int rc = validate_mx_forward(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y,
+                                 accumulate, ws, ws_bytes);
+    if (rc != MOE_OK || T == 0) return rc;
+    hipError_t e = moe::launch_mx_decode(layer_of(*layer), x, T, topk_w, expert_offsets, sorted_assign, y, accumulate,
+                                         ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_mxfp4_forward launch");
+    return MOE_OK;
+}
+
+int moe_mxfp4_dequant(const uint8_t* blocks_t, const uint8_t* scales_t, int N, int K, float* out,
+                      hipStream_t stream) {
+    if (N < 0 || K <= 0 || K % 32 != 0)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "N must be >= 0 and K a positive multiple of 32 (N=%d, K=%d)", N, K);
+    if (N == 0) return MOE_OK;
+    if (!blocks_t || !scales_t || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+    hipError_t e = moe::launch_mx_dequant_t(blocks_t, scales_t, N, K, out, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_mxfp4_dequant launch");
+    return MOE_OK;
+}
+
+int moe_mxfp4_dequant_slot(const void* slot, int H, int I, int matrix, float* out, hipStream_t stream) {
+    if (!shape_ok(H, I))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H must be a positive multiple of 128 and I of 32");
+    if (matrix != 0 && matrix != 1) return fail(MOE_ERR_INVALID_ARGUMENT, "matrix must be 0 (gate_up) or 1 (down)");
+    if (!slot || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer argument");
+    if (reinterpret_cast<uintptr_t>(slot) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "slot and out must be 16-byte aligned");
+    hipError_t e = moe::launch_mx_dequant_slot(static_cast<const uint8_t*>(slot), H, I, matrix, out, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_mxfp4_dequant_slot launch");
+    return MOE_OK;
+}
+
+int moe_mxfp4_slice_bank(const void* src_bank, int num_slots, int H, int I, int r, int n, void* dst_bank,
+                         hipStream_t stream) {
+    if (!shape_ok(H, I))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H must be a positive multiple of 128 and I of 32");
+    if (n < 1 || r < 0 || r >= n || I % n != 0 || (I / n) % 32 != 0)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "slice %d of %d: I/n must be a multiple of 32 (I=%d)", r, n, I);
+    if (num_slots < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_slots must be >= 0");
+    if (num_slots == 0) return MOE_OK;
+    if (!src_bank || !dst_bank) return fail(MOE_ERR_INVALID_ARGUMENT, "null bank pointer");
+    hipError_t e = moe::launch_mx_slice_bank(static_cast<const uint8_t*>(src_bank), num_slots, H, I, r, n,
+                                             static_cast<uint8_t*>(dst_bank), stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_mxfp4_slice_bank launch");
+    return MOE_OK;
+}
+
+}  // extern "C"
+
 // ------------------------------------------------------------------ host cache slot manager
 
 struct moe_expert_cache {

@@ -115,6 +115,18 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
                           const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
                           int accumulate, void* ws, hipStream_t s);
 
+// MXFP4 bank format (mxfp4.hip, slicer in util.hip): slot regions (globals empty), the decode path (T <= 16), the
+// dequant hooks (checkpoint-transposed matrix; one matrix of a slot through the forward's own decode).
+SlotGeom mx_slot_geom(int H, int I);
+bool mx_decode_shape_supported(int H, int I);
+hipError_t launch_mx_decode(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* offsets,
+                            const int32_t* sorted_assign, float* y, int accumulate, void* ws, hipStream_t s);
+hipError_t launch_mx_dequant_t(const uint8_t* blocks_t, const uint8_t* scales_t, int N, int K, float* out,
+                               hipStream_t s);
+hipError_t launch_mx_dequant_slot(const uint8_t* slot, int H, int I, int matrix, float* out, hipStream_t s);
+hipError_t launch_mx_slice_bank(const uint8_t* src, int num_slots, int H, int I, int r, int n, uint8_t* dst,
+                                hipStream_t s);
+
 // Utilities (util.hip)
 hipError_t launch_dequant(const uint8_t* slot, int H, int I, int matrix, float* out, hipStream_t s);
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, const float* globals, int rows, int K,

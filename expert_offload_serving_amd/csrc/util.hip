@@ -147,4 +147,28 @@ hipError_t launch_slice_bank(const uint8_t* src, int num_slots, int H, int I, in
     return copy_records(src, dst, num_slots, S.total, D.total, S.dn_glob, D.dn_glob, 1, 1, 0, 4 * H, 1, 0, 0, s);
 }
 
+// The same slice of an MXFP4 bank.  In the checkpoints' transposed tensors
+// it runs along N of gate_up (blocks_t [H/2, 2I]: two column ranges) and
+// along K of down (blocks_t [I/2, H]: a row range), with the scales sliced to
+// match (issue #62 "What it touches"); in the slot's operand order both are
+// whole records: gate_up 16-row tiles per 128-column step (64 scale bytes
+// each), down 32-column chunks of 64-row groups (64 scale bytes each).
+hipError_t launch_mx_slice_bank(const uint8_t* src, int num_slots, int H, int I, int r, int n, uint8_t* dst,
+                                hipStream_t s) {
+    const int Il = I / n;
+    const SlotGeom S = mx_slot_geom(H, I), D = mx_slot_geom(H, Il);
+    const int KQ = H / 128, NTs = 2 * I / 16, NTd = 2 * Il / 16, NG = H / 64;
+    const int gt = r * Il / 16, ut = I / 16 + r * Il / 16;
+    hipError_t e;
+    if ((e = copy_records(src, dst, num_slots, S.total, D.total, S.gu_codes, D.gu_codes, KQ, NTd, NTs, 1024,
+                          Il / 16, gt, ut, s)) != hipSuccess) return e;
+    if ((e = copy_records(src, dst, num_slots, S.total, D.total, S.gu_scales, D.gu_scales, KQ, NTd, NTs, 64,
+                          Il / 16, gt, ut, s)) != hipSuccess) return e;
+    const int nrec = (Il / 32) * NG, first = (r * Il / 32) * NG;
+    if ((e = copy_records(src, dst, num_slots, S.total, D.total, S.dn_codes, D.dn_codes, 1, nrec, 0, 1024, nrec,
+                          first, 0, s)) != hipSuccess) return e;
+    return copy_records(src, dst, num_slots, S.total, D.total, S.dn_scales, D.dn_scales, 1, nrec, 0, 64, nrec, first,
+                        0, s);
+}
+
 }  // namespace moe

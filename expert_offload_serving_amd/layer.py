@@ -37,10 +37,12 @@ class DeviceLayer:
     shared_slot: int
     wg: torch.Tensor              # bf16 [H]
 
+    fmt: str = "nvfp4"            # slot format: "nvfp4" or "mxfp4"
+
     def __post_init__(self):
-        sb = _lib.moe_nvfp4_slot_bytes(self.H, self.I)
+        sb = (_lib.moe_nvfp4_slot_bytes if self.fmt == "nvfp4" else _lib.moe_mxfp4_slot_bytes)(self.H, self.I)
         if sb == 0 or self.bank.dim() != 2 or self.bank.shape[1] != sb:
-            raise ValueError(f"bank must be [slots, {sb}] bytes for H={self.H}, I={self.I}")
+            raise ValueError(f"bank must be [slots, {sb}] bytes for H={self.H}, I={self.I} ({self.fmt})")
 
     @property
     def slot_bytes(self) -> int:
@@ -111,8 +113,9 @@ def router_route(x: torch.Tensor, w_router: torch.Tensor, k: int, out: Routing |
 
 
 def workspace(T: int, layer: DeviceLayer) -> torch.Tensor:
-    nb = _lib.moe_nvfp4_forward_workspace_bytes(T, layer.H, layer.I, layer.E, layer.k)
-    return torch.empty(nb, dtype=torch.uint8, device=layer.bank.device)
+    f = _lib.moe_nvfp4_forward_workspace_bytes if layer.fmt == "nvfp4" else _lib.moe_mxfp4_forward_workspace_bytes
+    nb = f(T, layer.H, layer.I, layer.E, layer.k)
+    return torch.empty(max(nb, 1), dtype=torch.uint8, device=layer.bank.device)
 
 
 def forward(layer: DeviceLayer, x: torch.Tensor, r: Routing, y: torch.Tensor | None = None, accumulate: bool = False,
@@ -124,8 +127,9 @@ def forward(layer: DeviceLayer, x: torch.Tensor, r: Routing, y: torch.Tensor | N
     if ws is None:
         ws = workspace(T, layer)
     st = layer.struct(slot_of_expert, shared)
-    check(_lib.moe_nvfp4_forward(st, x, T, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y, int(accumulate),
-                                 ws, ws.numel(), stream))
+    f = _lib.moe_nvfp4_forward if layer.fmt == "nvfp4" else _lib.moe_mxfp4_forward
+    check(f(st, x, T, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y, int(accumulate), ws, ws.numel(),
+            stream))
     return y
 
 
@@ -166,4 +170,26 @@ def slice_bank(bank: torch.Tensor, H: int, I: int, r: int, n: int, stream=None) 
     sb = _lib.moe_nvfp4_slot_bytes(H, I // n)
     out = torch.empty((bank.shape[0], sb), dtype=torch.uint8, device=bank.device)
     check(_lib.moe_nvfp4_slice_bank(bank, bank.shape[0], H, I, r, n, out, stream))
+    return out
+
+
+def mx_dequant(blocks_t: torch.Tensor, scales_t: torch.Tensor, stream=None) -> torch.Tensor:
+    """fp32 [N, K] of an MXFP4 matrix in the checkpoints' transposed layout (blocks_t u8 [K/2, N], scales_t [K/32, N])."""
+    K, N = 2 * blocks_t.shape[0], blocks_t.shape[1]
+    out = torch.empty((N, K), dtype=torch.float32, device=blocks_t.device)
+    check(_lib.moe_mxfp4_dequant(blocks_t, scales_t, N, K, out, stream))
+    return out
+
+
+def mx_dequant_slot(slot: torch.Tensor, H: int, I: int, matrix: int, stream=None) -> torch.Tensor:
+    shape = (2 * I, H) if matrix == 0 else (H, I)
+    out = torch.empty(shape, dtype=torch.float32, device=slot.device)
+    check(_lib.moe_mxfp4_dequant_slot(slot, H, I, matrix, out, stream))
+    return out
+
+
+def mx_slice_bank(bank: torch.Tensor, H: int, I: int, r: int, n: int, stream=None) -> torch.Tensor:
+    sb = _lib.moe_mxfp4_slot_bytes(H, I // n)
+    out = torch.empty((bank.shape[0], sb), dtype=torch.uint8, device=bank.device)
+    check(_lib.moe_mxfp4_slice_bank(bank, bank.shape[0], H, I, r, n, out, stream))
     return out

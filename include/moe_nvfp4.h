@@ -260,6 +260,76 @@ int moe_cache_plan(moe_expert_cache_t* cache, int layer, const int32_t* ids, int
 int moe_nvfp4_slice_bank(const void* src_bank, int num_slots, int H, int I, int r, int n, void* dst_bank,
                          hipStream_t stream);
 
+/* ------------------------------------------------------------------ MXFP4 banks
+ * The second fp4 bank format (issue #62 "What it touches": mxfp4, whose
+ * checkpoints store each matrix transposed, blocks_t [K//2, N], with 32-wide
+ * fp4 scale blocks; "Suggested staging": the last format to add): E2M1 codes
+ * with one E8M0 scale (2^(byte - 127), 0xFF NaN) per 32 consecutive
+ * elements along the contraction axis and no per-row global:
+ *     W[r, c] = e2m1(code(r, c)) * e8m0(scale(r, c / 32)).
+ * One slot holds, in this order and without padding:
+ *     gate_up codes  2I*H/2 bytes     gate_up scales  2I*H/32 bytes
+ *     down codes     H*I/2 bytes      down scales     H*I/32 bytes
+ * in gfx950 matrix-core operand order (lane L = 16*a + i of a wave loads one
+ * 16-byte piece): with i = r % 16,
+ *   gate_up (N = 2I): a 16-row x 128-column tile per 1 KiB whose piece L is
+ *     row i, columns [32a, 32a + 32) (the fp4 operand of
+ *     v_mfma_scale_f32_16x16x128_f8f6f4, one scale block), q = c / 128,
+ *     a = (c / 32) % 4, t = r / 16, T = N / 16:
+ *       code byte  = 16*(64*(q*T + t) + 16*a + i) + (c % 32)/2
+ *       scale byte = 64*(q*T + t) + 16*a + i                   (block c/32)
+ *   down (N = H): the NVFP4 down tiling (64-row x 32-column tile per 1 KiB),
+ *     k = c / 32, p = r / 64, j = (r / 16) % 4, g = (c / 8) % 4, P = N / 64:
+ *       code byte  = 16*(64*(k*P + p) + 16*g + i) + 4*j + (c % 8)/2
+ *       scale byte = 64*(k*P + p) + 4*i + j                    (block k)
+ * The even column of a byte is its low nibble.  Same shape rules as NVFP4
+ * slots (H % 128 == 0, I % 32 == 0); 0 for other shapes. */
+size_t moe_mxfp4_slot_bytes(int H, int I);
+
+/* Workspace moe_mxfp4_forward needs for T tokens; 0 for shapes it does not take. */
+size_t moe_mxfp4_forward_workspace_bytes(int T, int H, int I, int E, int k);
+
+/* The routed-MoE layer of moe_nvfp4_forward over MXFP4 slots (the same
+ * layer struct with slot_bytes = moe_mxfp4_slot_bytes(H, I); the same
+ * routing inputs, combine, accumulate and error rules).  It runs the decode
+ * path only: T <= 16, T*k <= 1024, H <= 2560 (larger T returns
+ * MOE_ERR_UNSUPPORTED_SHAPE with nothing enqueued).  gate_up runs on
+ * v_mfma_scale_f32_16x16x128_f8f6f4 with the fp4 codes and E8M0 scales used
+ * as stored and the activations entered as two fp8 E4M3 terms with their own
+ * E8M0 block scales (the bf16 value exactly, unless a block's values span
+ * more than the fp8 range); down decodes its codes exactly to bf16 with the
+ * scale applied by v_cvt_scalef32_pk_bf16_fp4 and multiplies them on
+ * v_mfma_f32_16x16x32_bf16 against the hidden state as two bf16 terms.
+ * Sums are fp32 in a fixed order (bit-reproducible). */
+int moe_mxfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
+                      const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
+                      const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* MXFP4 decode of one matrix in the checkpoints' transposed layout:
+ *   blocks_t  device u8 [K/2, N]: byte (j, n) = W[n, 2j] (low nibble), W[n, 2j+1]
+ *   scales_t  device u8 [K/32, N]: E8M0 of (n, block)
+ *   out       device f32 [N, K]
+ * K a positive multiple of 32; N == 0 is a no-op.  Decoded by the converter
+ * the forward's down phase uses (fp4 -> bf16 with the scale applied). */
+int moe_mxfp4_dequant(const uint8_t* blocks_t, const uint8_t* scales_t, int N, int K, float* out,
+                      hipStream_t stream);
+
+/* One matrix of an MXFP4 slot to fp32, row-major, through the forward's own
+ * decode: gate_up (matrix 0, out [2I, H]) through the scaled matrix cores
+ * against one-hot fp8 columns, down (matrix 1, out [H, I]) through the bf16
+ * converter. */
+int moe_mxfp4_dequant_slot(const void* slot, int H, int I, int matrix, float* out, hipStream_t stream);
+
+/* Intermediate-axis slice r of n of every MXFP4 slot in a bank.  In the
+ * checkpoints' transposed tensors it runs along N of gate_up (columns
+ * [r*Il, (r+1)*Il) and [I + r*Il, I + (r+1)*Il)) and along K of down (rows
+ * [r*Il/2, (r+1)*Il/2) of blocks_t, [r*Il/32, (r+1)*Il/32) of scales_t),
+ * Il = I/n a multiple of 32 (issue #62 "What it touches": mxfp4's slice is
+ * along N and its scales slice differently). */
+int moe_mxfp4_slice_bank(const void* src_bank, int num_slots, int H, int I, int r, int n, void* dst_bank,
+                         hipStream_t stream);
+
 /* ------------------------------------------------------------------ dequant
  * The NVFP4 decode of one row-major matrix (PR #385 "What this adds": packed
  * 4-bit codes, 16-wide FP8 scale blocks, per-row fp32 globals), with the

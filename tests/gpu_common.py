@@ -40,9 +40,9 @@ def assert_close(y, ref, what=""):
     return rel
 
 
-def device_layer(L: synth.LayerInputs) -> dl.DeviceLayer:
+def device_layer(L: synth.LayerInputs, fmt: str = "nvfp4") -> dl.DeviceLayer:
     return dl.DeviceLayer(L.H, L.I, L.E, L.k, dl.to_device_u8(L.bank), torch.from_numpy(L.slot_of_expert).cuda(),
-                          L.shared_slot, dl.to_device_bf16(L.wg))
+                          L.shared_slot, dl.to_device_bf16(L.wg), fmt)
 
 
 def device_x(L: synth.LayerInputs) -> torch.Tensor:

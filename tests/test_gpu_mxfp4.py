@@ -1,0 +1,165 @@
+"""GPU parity of the MXFP4 bank format against the oracle (marker: gpu).
+
+The decode of MXFP4 weights (E2M1 with E8M0 scales per 32) must be bit-exact
+in fp32 through both of the forward's decode routes (the scaled matrix cores
+for gate_up, the fp4 -> bf16 converter for down); the slicer byte-exact;
+layer outputs within relative L2 2e-3 and max |err| <= 1e-2 * max |ref| at
+every decode batch size's launch configuration, with every slot distinct and
+the experts at random positions of a larger bank.
+"""
+import hashlib
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_offload_serving_amd import _lib
+from expert_offload_serving_amd import layer as dl
+from expert_offload_serving_amd import synth
+from tests.gpu_common import assert_close, device_layer, device_logits, device_x, need_gpu
+
+pytestmark = pytest.mark.gpu
+NTHREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    _lib.lib()
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _bits_equal(got, want, what):
+    nan_w, nan_g = np.isnan(want), np.isnan(got)
+    assert np.array_equal(nan_w, nan_g), f"{what}: NaN positions differ ({nan_w.sum()} vs {nan_g.sum()})"
+    bad = want[~nan_w].view(np.uint32) != got[~nan_g].view(np.uint32)
+    assert not bad.any(), f"{what}: {bad.sum()} values differ, e.g. want {want[~nan_w][bad][:4]} got {got[~nan_g][bad][:4]}"
+
+
+def test_mx_dequant_transposed_every_code_and_scale_byte():
+    """moe_mxfp4_dequant on the checkpoints' transposed layout: every (code, E8M0 byte) pair, bit for bit."""
+    N, K = 256, 512
+    _announce(f"mxfp4 dequant transposed N={N} K={K}, all codes x all scale bytes")
+    codes_row = np.array([(2 * j % 16) | (((2 * j + 1) % 16) << 4) for j in range(K // 2)], dtype=np.uint8)
+    blocks_t = np.ascontiguousarray(np.tile(codes_row[:, None], (1, N)))
+    scales_t = np.tile(np.arange(N, dtype=np.uint8)[None, :], (K // 32, 1))
+    scales_t[1::2] = ((scales_t[1::2].astype(np.int64) + 101) % 256).astype(np.uint8)
+    want = oracle.mx_dequant_t(blocks_t, scales_t)
+    got = dl.mx_dequant(torch.from_numpy(blocks_t).cuda(), torch.from_numpy(np.ascontiguousarray(scales_t)).cuda())
+    _bits_equal(got.cpu().numpy(), want, "mx dequant transposed")
+
+
+@pytest.mark.parametrize("scales", ["realistic", "every_byte"])
+def test_mx_dequant_slot_through_forward_decode(scales):
+    """One MXFP4 slot's gate_up through the scaled matrix cores (one-hot activations) and its down through the
+    bf16 converter: bit for bit against the oracle's slot dequant."""
+    H, I = 2560, 640
+    rng = np.random.default_rng(5)
+    slot = synth.random_expert_slot(rng, H, I, fmt="mxfp4")
+    if scales == "every_byte":  # every E8M0 byte except NaN, in both matrices
+        regs = synth.mx_slot_regions(H, I)
+        for r_ in (1, 3):
+            off, size = regs[r_]
+            slot[off:off + size] = (np.arange(size) % 255).astype(np.uint8)
+    _announce(f"mxfp4 dequant slot H={H} I={I} ({scales} scales)")
+    dslot = torch.from_numpy(slot).cuda()
+    for m in (0, 1):
+        got, want = dl.mx_dequant_slot(dslot, H, I, m).cpu().numpy(), oracle.mx_dequant_slot(slot, H, I, m)
+        if m == 0:
+            # through the matrix cores a -0 weight plus the one-hot's zero products sums to +0 (IEEE -0 + +0);
+            # the sign of zero is the only thing that route does not carry, every other bit must match
+            assert np.all(got[want == 0] == 0)
+            want = np.where(want == 0, np.float32(0.0), want)
+        _bits_equal(got, want, f"mx slot matrix {m}")
+
+
+def test_mx_slice_bank_bytes_and_sum():
+    """The slicer against the oracle's byte for byte; the two I/2 slices' layer outputs add up to the full one."""
+    T = 16
+    L = synth.make_layer("decode_bs16", T=T, n_distinct=6, seed=55, fmt="mxfp4")
+    _announce(f"mxfp4 slice I=640 -> 2 x 320, T={T}")
+    dev = device_layer(L, "mxfp4")
+    x = device_x(L)
+    r = dl.route(device_logits(L), L.k)
+    full = dl.forward(dev, x, r)
+    acc = torch.zeros_like(full)
+    for rr in range(2):
+        sb = dl.mx_slice_bank(dev.bank, L.H, L.I, rr, 2)
+        want = np.stack([oracle.mx_slice_slot(s, L.H, L.I, rr, 2) for s in L.bank[:L.E + 1]])
+        assert np.array_equal(sb.cpu().numpy()[:L.E + 1], want), "sliced bytes differ from the oracle's slicer"
+        part = dl.DeviceLayer(L.H, L.I // 2, L.E, L.k, sb, dev.slot_of_expert, L.shared_slot, dev.wg, "mxfp4")
+        dl.forward(part, x, r, y=acc, accumulate=rr > 0)
+    torch.cuda.synchronize()
+    ids, w = oracle.route(L.logits, L.k)
+    ref = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w,
+                         nthreads=NTHREADS, fmt="mxfp4")
+    assert_close(acc.cpu().numpy(), full.cpu().numpy(), "mx slice sum vs full")
+    assert_close(acc.cpu().numpy(), ref, "mx slice sum vs oracle")
+
+
+def test_mx_forward_tiny():
+    H, I, E, k, T = 256, 64, 8, 2, 4
+    rng = np.random.default_rng(0)
+    bank = synth.make_bank(rng, H, I, E + 1, None, fmt="mxfp4")
+    L = synth.LayerInputs(H, I, E, k, T, bank, np.arange(E, dtype=np.int32), E,
+                          synth.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32) * 0.02),
+                          synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)),
+                          rng.standard_normal((T, E)).astype(np.float32))
+    _announce("mxfp4 forward tiny H=256 I=64 E=8 k=2 T=4")
+    y = dl.forward(device_layer(L, "mxfp4"), device_x(L), dl.route(device_logits(L), k))
+    torch.cuda.synchronize()
+    ids, w = oracle.route(L.logits, k)
+    ref = oracle.forward(H, I, E, k, bank, L.slot_of_expert, E, L.wg, L.x, ids, w, fmt="mxfp4")
+    rel = assert_close(y.cpu().numpy(), ref, "mx tiny")
+    print(f"mx tiny rel L2 {rel:.2e}")
+
+
+@pytest.fixture(scope="module")
+def mx_layer():
+    L = synth.permute_slots(synth.make_layer("decode_bs16", T=16, n_distinct=16, seed=116, fmt="mxfp4"),
+                            np.random.default_rng(117), spare=40)
+    used = [int(s) for s in L.slot_of_expert] + [L.shared_slot]
+    assert len({hashlib.sha1(L.bank[j].tobytes()).digest() for j in used}) == len(used)
+    return L
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 16])
+def test_mx_forward_full_shape_distinct_permuted(mx_layer, T):
+    """MXFP4 layer at H=2560, I=640, 256 experts top-8, every slot distinct, experts at random slots."""
+    xb, lg = synth.fresh_tokens(1200 + T, T, mx_layer.H, mx_layer.E, "uniform")
+    L = synth.LayerInputs(mx_layer.H, mx_layer.I, mx_layer.E, mx_layer.k, T, mx_layer.bank, mx_layer.slot_of_expert,
+                          mx_layer.shared_slot, mx_layer.wg, xb, lg)
+    _announce(f"mxfp4 forward full shape T={T}")
+    dev = device_layer(L, "mxfp4")
+    r = dl.route(device_logits(L), L.k)
+    y = dl.forward(dev, device_x(L), r)
+    y2 = dl.forward(dev, device_x(L), r)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32)), "not bit-reproducible"
+    ids, w = oracle.route(L.logits, L.k)
+    ref = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w,
+                         nthreads=NTHREADS, fmt="mxfp4")
+    rel = assert_close(y.cpu().numpy(), ref, f"mx forward T={T}")
+    print(f"mx T={T} rel L2 {rel:.2e}")
+
+
+def test_mx_forward_refuses_prefill_and_wrong_slot_size(mx_layer):
+    L = mx_layer
+    dev = device_layer(L, "mxfp4")
+    x = torch.zeros((17, L.H), dtype=torch.bfloat16, device="cuda")
+    r = dl.Routing.empty(17, L.E, L.k)
+    y = torch.full((17, L.H), 3.0, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    st = dev.struct()
+    rc = _lib.moe_mxfp4_forward(st, x, 17, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y, 0, ws, ws.numel())
+    assert rc == _lib.MOE_ERR_UNSUPPORTED_SHAPE and "decode path" in _lib.last_error()
+    st.slot_bytes = _lib.moe_nvfp4_slot_bytes(L.H, L.I)  # an NVFP4 slot size
+    rc = _lib.moe_mxfp4_forward(st, x, 4, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y, 0, ws, ws.numel())
+    assert rc == _lib.MOE_ERR_INVALID_ARGUMENT
+    torch.cuda.synchronize()
+    assert bool((y == 3.0).all())
