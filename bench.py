@@ -11,8 +11,9 @@ expert bank in turn.  The steps are captured in a HIP graph and replayed.
 Default run: every workload, printed as ONE JSON line whose top level is the
 decode shape the metric is quoted on (H=2560, I=640, 256 experts top-8 with
 uniform-random logits, one shared expert, batch 1) and whose "configs" entry
-holds the full result of decode batch 16, the 2048-token prefill chunk and
-the offloaded 48-layer run, each with its own roofline and CPU baseline.
+holds the full result of decode batch 16, the 2048-token prefill chunk, the
+offloaded 48-layer run and the MXFP4 bank format at decode batch 1 and 16,
+each with its own roofline and CPU baseline.
 `--config NAME` prints that workload's line alone.
 
 The arithmetic (dtype field): NVFP4 weights decoded exactly to fp16, bf16
@@ -38,6 +39,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 PCIE_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction
 DTYPE = "nvfp4w-fp16mfma-fp32acc"
+METRIC_MX = "MoE-layer tokens/s + expert-weight HBM GB/s (% peak), H2560 I640 MXFP4"
+DTYPE_MX = "mxfp4w-fp8x2scaledmfma-bf16x2mfma-fp32acc"
 
 
 # HBM bytes per call of the roofline unit from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, summed over the call's
@@ -48,7 +51,8 @@ COUNTED_TRAFFIC = {
     "decode_bs16": (318_853_215, "55fb154bdad41245"),
     "prefill_2048": (1_394_877_674, "52b117e61e3109c2"),
 }
-KERNEL_SOURCES = {"decode": ["decode.hip", "route_device.hpp", "nvfp4_device.hpp"],
+KERNEL_SOURCES = {"decode": ["decode.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],
+                  "mxfp4": ["mxfp4.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],
                   "prefill": ["prefill.hip", "nvfp4_device.hpp"]}
 
 
@@ -75,18 +79,24 @@ def log(msg: str) -> None:
 
 # ---------------------------------------------------------------- inputs
 
+def split_name(name: str):
+    """Workload name -> (base config, slot format): "mxfp4_decode_bs1" is decode_bs1 over MXFP4 slots."""
+    return (name[len("mxfp4_"):], "mxfp4") if name.startswith("mxfp4_") else (name, "nvfp4")
+
+
 def build_inputs(name: str, steps: int, replicas: int, distinct: int):
     """Host inputs: the expert bank (E routed + 1 shared slot), per-step activations and logits."""
     from expert_offload_serving_amd import synth
-    H, I, E, k, T, seed, kind = synth.CONFIGS[name]
+    base, fmt = split_name(name)
+    H, I, E, k, T, seed, kind = synth.CONFIGS[base]
     r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
     t0 = time.time()
-    bank = synth.make_bank(r_w, H, I, E + 1, distinct)
+    bank = synth.make_bank(r_w, H, I, E + 1, distinct, fmt)
     log(f"{name}: quantized {min(distinct, E + 1)} distinct experts into {E + 1} slots in {time.time() - t0:.1f}s")
     wg = synth.f32_to_bf16_bits(r_g.standard_normal(H, dtype=np.float32) * np.float32(0.02))
     xs = synth.f32_to_bf16_bits(r_x.standard_normal((steps, T, H), dtype=np.float32))
     logits = np.stack([synth.make_logits(r_l, T, E, kind) for _ in range(steps)])
-    return dict(H=H, I=I, E=E, k=k, T=T, bank=bank, wg=wg, xs=xs, logits=logits, replicas=replicas)
+    return dict(H=H, I=I, E=E, k=k, T=T, bank=bank, wg=wg, xs=xs, logits=logits, replicas=replicas, fmt=fmt)
 
 
 # ---------------------------------------------------------------- GPU run
@@ -107,7 +117,8 @@ def run_gpu(inp, steps: int, warmup: int):
     wg = dl.to_device_bf16(inp["wg"], dev)
     maps = torch.arange(E, dtype=torch.int32, device=dev)[None, :] + nslot * torch.arange(
         R, dtype=torch.int32, device=dev)[:, None]
-    layers = [dl.DeviceLayer(H, I, E, k, bank, maps[r].contiguous(), r * nslot + E, wg) for r in range(R)]
+    fmt = inp["fmt"]
+    layers = [dl.DeviceLayer(H, I, E, k, bank, maps[r].contiguous(), r * nslot + E, wg, fmt) for r in range(R)]
     structs = [l.struct() for l in layers]
     total = steps + warmup
     xs = dl.to_device_bf16(inp["xs"][:total].reshape(total * T, H), dev).view(total, T, H)
@@ -121,8 +132,17 @@ def run_gpu(inp, steps: int, warmup: int):
     rws_t = torch.empty(max(1, rws), dtype=torch.uint8, device=dev)
 
     def step(s: int, do_route: bool = True, do_forward: bool = True):
-        """A step is one moe_nvfp4_route_forward call; do_route / do_forward select the separate calls."""
+        """A step is one moe_nvfp4_route_forward call (MXFP4: moe_route_topk then moe_mxfp4_forward);
+        do_route / do_forward select the separate calls."""
         r = routes[s]
+        if fmt == "mxfp4":
+            if do_route:
+                _lib.check(_lib.moe_route_topk(logits[s], T, E, k, r.ids, r.w, r.offsets, r.sorted_assign,
+                                               r.assign_pos, rws_t, rws, None))
+            if do_forward:
+                _lib.check(_lib.moe_mxfp4_forward(structs[s % R], xs[s], T, r.ids, r.w, r.offsets, r.sorted_assign,
+                                                  r.assign_pos, y[s], 0, ws, ws.numel(), None))
+            return
         if do_route and do_forward:
             _lib.check(_lib.moe_nvfp4_route_forward(structs[s % R], logits[s], xs[s], T, r.ids, r.w, r.offsets,
                                                     r.sorted_assign, r.assign_pos, y[s], 0, ws_rf, rf_bytes, None))
@@ -227,7 +247,8 @@ def oracle_threads():
 
 
 # Per-repetition sample of each workload for the oracle (one oracle call per step, as the GPU runs them).
-CPU_SAMPLES = {"decode_bs1": 4, "decode_bs16": 1, "prefill_2048": 128, "offload": 2}
+CPU_SAMPLES = {"decode_bs1": 4, "decode_bs16": 1, "prefill_2048": 128, "offload": 2, "mxfp4_decode_bs1": 4,
+               "mxfp4_decode_bs16": 1}
 
 
 def cpu_leg(name: str, reps: int = 5) -> dict:
@@ -238,6 +259,7 @@ def cpu_leg(name: str, reps: int = 5) -> dict:
     from expert_offload_serving_amd import synth
     threads = int(os.environ["OMP_NUM_THREADS"])
     n = CPU_SAMPLES[name]
+    fmt = "nvfp4"
     if name == "offload":
         H, I, E, k, T, seed = 2560, 640, 256, 8, 8, 48
         r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
@@ -248,9 +270,10 @@ def cpu_leg(name: str, reps: int = 5) -> dict:
         what = f"{n} layer-steps of bs {T} (Zipf(1.2) routing), one oracle call each"
         per_rep_tokens = n * T
     else:
-        H, I, E, k, T, seed, kind = synth.CONFIGS[name]
+        base, fmt = split_name(name)
+        H, I, E, k, T, seed, kind = synth.CONFIGS[base]
         r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
-        bank = synth.make_bank(r_w, H, I, E + 1, 32)
+        bank = synth.make_bank(r_w, H, I, E + 1, 32, fmt)
         if T > 16:  # the prefill chunk: its first n tokens, routed and computed as one call
             x = synth.f32_to_bf16_bits(r_x.standard_normal((T, H), dtype=np.float32))
             lg = synth.make_logits(r_l, T, E, kind)
@@ -269,7 +292,7 @@ def cpu_leg(name: str, reps: int = 5) -> dict:
         t0 = time.perf_counter()
         for x, lg in steps:
             ids, w = oracle.route(lg, k)
-            oracle.forward(H, I, E, k, bank, som, E, wg, x, ids, w, nthreads=threads)
+            oracle.forward(H, I, E, k, bank, som, E, wg, x, ids, w, nthreads=threads, fmt=fmt)
         return time.perf_counter() - t0
 
     once()
@@ -310,7 +333,7 @@ def parity_sample(inp, res, tokens):
         return {"ids_bitexact": False}
     toks = np.arange(min(tokens, T), dtype=np.int32)
     ref = oracle.forward(H, I, E, k, inp["bank"], np.arange(E, dtype=np.int32), E, inp["wg"], x, ids, w,
-                         tokens=toks)
+                         tokens=toks, fmt=inp["fmt"])
     got = res["y_last"][toks].astype(np.float64)
     rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     return {"ids_bitexact": True, "rel_l2": rel, "tokens_checked": int(toks.size)}
@@ -547,15 +570,16 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     log(f"{name}: running {warmup} warmup + {steps} timed steps, {replicas} bank copies")
     res = run_gpu(inp, steps, warmup)
     res["last_index"] = steps + warmup - 1
-    sb = synth.slot_nbytes(H, I)
+    mx = inp["fmt"] == "mxfp4"
+    sb = synth.mx_slot_nbytes(H, I) if mx else synth.slot_nbytes(H, I)
     ms_step = res["wall"] * 1e3 / steps
     tokens_s = T * steps / res["wall"]
     mean_d = float(np.mean(res["distinct"]))
     bytes_fwd = (mean_d + 1) * sb                       # touched expert slots incl. the shared expert
     prefill = T > 16
-    # roofline unit: decode routes inside its first kernel, so the unit is the step's route_forward call;
-    # prefill routes in kernels of its own, so the unit is the forward call
-    fwd_s = (res["fwd_ms"] if prefill else res["call_ms"]) * 1e-3
+    # roofline unit: NVFP4 decode routes inside its first kernel, so the unit is the step's route_forward call;
+    # prefill and MXFP4 decode route in kernels of their own, so the unit is the forward call
+    fwd_s = (res["fwd_ms"] if prefill or mx else res["call_ms"]) * 1e-3
     gbs = bytes_fwd / fwd_s / 1e9
     flops = synth.prefill_flops(T, H, I, k)
     if prefill:
@@ -565,6 +589,14 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
                 "kernel": "moe_nvfp4_forward prefill (prep_plan_kernel, tile_gemm_kernel over 128/64/32-row tiles for gate_up and "
                           "down, combine_kernel), timed together with HIP events",
                 "per_launch": f"{flops / 1e9:.2f} GFLOP per forward (2*3*I*H*(T*k+T))"}
+    elif mx:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic(name, "mxfp4"),
+                "kernel": "moe_mxfp4_forward decode call (mx_wave_kernel: gate_up on "
+                          "v_mfma_scale_f32_16x16x128_f8f6f4, down on v_mfma_f32_16x16x32_bf16; then "
+                          "dcombine_kernel), timed together with HIP events",
+                "per_launch": f"{bytes_fwd / 1e6:.2f} MB expert weights per forward ((D+1) x {sb} B, "
+                              f"mean D = {mean_d:.2f})"}
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic(name, "decode"),
@@ -573,9 +605,9 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
                 "per_launch": f"{bytes_fwd / 1e6:.2f} MB expert weights per forward ((D+1) x {sb} B, "
                               f"mean D = {mean_d:.2f})"}
     out = {
-        "metric": METRIC, "value": round(tokens_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
+        "metric": METRIC_MX if mx else METRIC, "value": round(tokens_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_MX if mx else DTYPE, "data": "synthetic",
         "config": {"workload": name, "H": H, "I": I, "E": E, "k": k, "T": T, "shared_expert": True,
                    "bank_copies": replicas, "distinct_quantized_experts": min(distinct, E + 1),
                    "parallelism": "single GPU"},
@@ -690,7 +722,8 @@ def copy_calibration(nbytes: int, reps: int) -> None:
           flush=True)
 
 
-REPLICAS = {"decode_bs1": 16, "decode_bs16": 8, "prefill_2048": 4}  # bank copies rotated over steps
+REPLICAS = {"decode_bs1": 16, "decode_bs16": 8, "prefill_2048": 4,  # bank copies rotated over steps
+            "mxfp4_decode_bs1": 16, "mxfp4_decode_bs16": 8}
 
 
 def main():
@@ -699,7 +732,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="all",
-                    choices=["decode_bs1", "decode_bs16", "prefill_2048", "offload", "all", *ROUTER_CONFIGS])
+                    choices=["decode_bs1", "decode_bs16", "prefill_2048", "offload", "mxfp4_decode_bs1",
+                             "mxfp4_decode_bs16", "all", *ROUTER_CONFIGS])
     ap.add_argument("--replicas", type=int, default=0,
                     help="copies of the expert bank rotated over steps (default 16 at bs 1, 8 at bs 16, 4 prefill)")
     ap.add_argument("--distinct", type=int, default=32, help="experts quantized; the other slots are sign-flipped "
@@ -752,7 +786,7 @@ def main():
     # every workload, one line: the headline decode batch 1 at the top level, the others under "configs"
     head = run("decode_bs1")
     head["configs"] = {}
-    for name in ("decode_bs16", "prefill_2048", "offload"):
+    for name in ("decode_bs16", "prefill_2048", "offload", "mxfp4_decode_bs1", "mxfp4_decode_bs16"):
         head["configs"][name] = run(name)
         torch.cuda.empty_cache()
     print(json.dumps(head), flush=True)
