@@ -341,12 +341,13 @@ def parity_sample(inp, res, tokens):
 
 # ---------------------------------------------------------------- offload
 
-def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_cpu: bool = True,
+def bench_offload(steps: int, warmup: int, distinct: int, want_cpu: bool = True,
                   residency: float = 0.37, distinct_banks: bool = True):
     """48 MoE layers whose 256 experts live in pinned host memory behind one HBM cache holding `residency`
-    (default 37%) of the 12,288 expert-layer slots (global LRU, cold start).  Per layer-step: route on the GPU, one D2H copy of
-    the ids, host LRU plan, misses copied on a side stream while the hits-only forward runs, then the
-    misses-only forward accumulates.  With want_cpu, the CPU leg checks the host LRU and the last layer-step
+    (default 37%) of the 12,288 expert-layer slots (global LRU, cold start).  Per layer-step, one
+    moe_offload_layer call: route on the GPU, look the routed experts up in the engine's device-side directory,
+    start the hits-only forward, plan on the host meanwhile (one wait for the small lookup result), copy the misses
+    on two side streams, then the misses-only forward accumulates.  With want_cpu, the CPU leg checks the host LRU and the last layer-step
     against the oracle.  With distinct_banks (the default) every one of the 48 x 256 experts has its own pinned
     host slot (34.16 GB); otherwise the experts alias 256 pinned base slots.  Returns the JSON dict."""
     import torch
@@ -413,72 +414,17 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
     xs_np = synth.f32_to_bf16_bits(r_x.standard_normal((NX, T, H), dtype=np.float32))
     xs = dl.to_device_bf16(xs_np.reshape(NX * T, H), dev).view(NX, T, H)
 
-    mgr = _lib.ExpertCache(L, E, n_slots)
-    route = dl.Routing.empty(T, E, k, dev)
-    rws = _lib.moe_route_workspace_bytes(T, E, k)
-    rws_t = torch.empty(max(1, rws), dtype=torch.uint8, device=dev)
-    ws = torch.empty(_lib.moe_nvfp4_forward_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device=dev)
+    dws = torch.empty(_lib.moe_offload_device_bytes(L, E, k, T, H, I), dtype=torch.uint8, device=dev)
+    eng = _lib.OffloadEngine(L, E, k, H, I, T, cache, [host_ptr[l][e_] for l in range(L) for e_ in range(E)], dws)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ids_h = torch.empty((T, k), dtype=torch.int32).pin_memory()
-    maps_h = torch.empty((2, E), dtype=torch.int32).pin_memory()
-    maps_d = torch.empty((2, E), dtype=torch.int32, device=dev)
-    comp = torch.cuda.current_stream()
-    # misses are split over ncopy side streams (each stream can drive its own copy engine; 2 measured best)
-    copies = [torch.cuda.Stream(device=dev) for _ in range(ncopy)]
-    dones = [torch.cuda.Event() for _ in range(ncopy)]
-    copy = copies[0]
-    ids_log = np.empty((total, L, T * k), dtype=np.int32)
+    copy = torch.cuda.Stream(device=dev)
     stats = {"hits": np.zeros((total, L), np.int64), "misses": np.zeros((total, L), np.int64)}
 
-    def layer_struct(l, slot_map, with_shared):
-        st = _lib.LayerStruct()
-        st.H, st.I, st.E, st.k = H, I, E, k
-        st.bank_base = cache.data_ptr()
-        st.slot_bytes = sb
-        st.num_slots = n_slots
-        st.slot_of_expert = slot_map.data_ptr()
-        st.shared_slot = shared[l].data_ptr() if with_shared else None
-        st.shared_gate_w = wg[l].data_ptr() if with_shared else None
-        return st
-
     def layer_step(s_, l):
-        x = xs[(s_ * L + l) % NX]
-        _lib.check(_lib.moe_route_topk(logits[s_, l], T, E, k, route.ids, route.w, route.offsets,
-                                       route.sorted_assign, route.assign_pos, rws_t, rws, None))
-        ids_h.copy_(route.ids, non_blocking=True)
-        comp.synchronize()                      # the one D2H sync per layer-step: the host plans the misses
-        ids = ids_h.numpy().reshape(-1).copy()
-        ids_log[s_, l] = ids
-        som, miss_e, miss_s, n_hit = mgr.plan(l, ids)
-        stats["hits"][s_, l], stats["misses"][s_, l] = n_hit, len(miss_e)
-        # The previous layer-step's kernels finished before the sync above (they precede this route in
-        # stream order), so no slot being overwritten below is still being read.
-        som = np.asarray(som, dtype=np.int32)
-        hit_map = som.copy()
-        miss_map = np.full(E, -1, dtype=np.int32)
-        for e_, sl in zip(miss_e, miss_s):
-            hit_map[e_] = -1
-            miss_map[e_] = sl
-        maps_h.numpy()[0] = hit_map
-        maps_h.numpy()[1] = miss_map
-        maps_d.copy_(maps_h, non_blocking=True)
-        used = []
-        for c_ in range(ncopy):
-            part = list(range(c_, len(miss_e), ncopy))
-            if part:
-                _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, [miss_s[i] for i in part],
-                                                  [host_ptr[l][miss_e[i]] for i in part], copies[c_],
-                                                  dones[c_]))
-                used.append(c_)
-        _lib.check(_lib.moe_nvfp4_forward(layer_struct(l, maps_d[0], True), x, T, route.ids, route.w,
-                                          route.offsets, route.sorted_assign, route.assign_pos, y, 0, ws,
-                                          ws.numel(), None))
-        if miss_e:
-            for c_ in used:
-                comp.wait_event(dones[c_])
-            _lib.check(_lib.moe_nvfp4_forward(layer_struct(l, maps_d[1], False), x, T, route.ids, route.w,
-                                              route.offsets, route.sorted_assign, route.assign_pos, y, 1, ws,
-                                              ws.numel(), None))
+        """One moe_offload_layer call: route, device-side lookup, hits forward, host LRU plan overlapping it,
+        misses copied on two copy streams, misses forward."""
+        stats["hits"][s_, l], stats["misses"][s_, l] = eng.layer(l, logits[s_, l], xs[(s_ * L + l) % NX], T,
+                                                                  shared[l], wg[l], y, copy_stream=copy)
 
     log(f"offload: {L} layers x {E} experts, cache {n_slots} slots ({n_slots * sb / 1e9:.1f} GB), "
         f"{warmup} warm-up + {steps} timed steps at bs {T}")
@@ -498,12 +444,15 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # pinned host -> HBM copy rate alone (64 slots over the same copy streams, host clock)
+    # pinned host -> HBM copy rate alone (64 slots over two copy streams, host clock)
     n_probe = 64
+    copies = [copy, torch.cuda.Stream(device=dev)]
+    for c_ in range(2):  # a stream's first use sets up its queue: not part of the measurement
+        _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, [c_], [host_ptr[0][c_]], copies[c_], None))
     torch.cuda.synchronize()
     tp = time.perf_counter()
-    for c_ in range(ncopy):
-        part = list(range(c_, n_probe, ncopy))
+    for c_ in range(2):
+        part = list(range(c_, n_probe, 2))
         _lib.check(_lib.expert_cache_fill(cache, sb, n_slots, part, [host_ptr[j // E % L][j % E] for j in part],
                                           copies[c_], None))
     torch.cuda.synchronize()
@@ -514,6 +463,8 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
         # the CPU leg: the host LRU against the oracle's model on the same ids; the last layer-step against the
         # oracle
         import oracle
+        ids_log = np.stack([np.stack([oracle.route(logits_np[s_, l], k)[0].reshape(-1) for l in range(L)])
+                            for s_ in range(total)])
         h_ref, m_ref, _, _ = oracle.lru_run(ids_log, E, n_slots, want_maps=False)
         lru_ok = bool(np.array_equal(h_ref, stats["hits"]) and np.array_equal(m_ref, stats["misses"]))
         s_last, l_last = total - 1, L - 1
@@ -549,7 +500,8 @@ def bench_offload(steps: int, warmup: int, distinct: int, ncopy: int = 2, want_c
                    "distinct_quantized_experts": min(distinct, E), "parallelism": "single GPU"},
         "roofline": {"bound": "pcie", "achieved": round(pcie, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                      "frac": round(pcie / PCIE_PEAK_GBS, 4), "traffic": None,
-                     "kernel": f"expert_cache_fill (hipMemcpyAsync of missed slots on {ncopy} side streams)",
+                     "kernel": "moe_offload_layer (device-side cache lookup, hits forward while the host plans, "
+                               "misses copied on two side streams, misses forward)",
                      "per_launch": f"{misses / max(1, steps * L):.2f} missed slots x {sb} B per layer-step"},
         "offload": {"hit_rate_steady": round(hits / max(1, hits + misses), 4),
                     "hit_rate_warmup": round(stats["hits"][:warmup].sum() /
@@ -739,7 +691,6 @@ def main():
     ap.add_argument("--distinct", type=int, default=32, help="experts quantized; the other slots are sign-flipped "
                                                               "copies of them (every slot distinct)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-streams", type=int, default=2, help="offload: side streams the misses are copied on")
     ap.add_argument("--residency", type=float, default=0.37,
                     help="offload: fraction of the 48 x 256 expert-layers the HBM cache holds")
     ap.add_argument("--aliased-banks", action="store_true",
@@ -772,7 +723,7 @@ def main():
             return bench_router(name, args.steps, args.warmup, 256)
         if name == "offload":
             steps, warmup = (64, 16) if args.steps == 200 and args.warmup == 10 else (args.steps, args.warmup)
-            return bench_offload(steps, warmup, args.distinct, args.copy_streams, want_cpu, args.residency,
+            return bench_offload(steps, warmup, args.distinct, want_cpu, args.residency,
                                  not args.aliased_banks)
         steps, warmup = args.steps, args.warmup
         if name == "prefill_2048":

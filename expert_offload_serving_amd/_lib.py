@@ -27,7 +27,8 @@ EXPORTED = [
     "moe_nvfp4_route_forward_workspace_bytes", "moe_nvfp4_route_forward", "moe_router_logits", "moe_router_topk",
     "moe_release_streams", "moe_nvfp4_noalloc_scratch_bytes", "moe_nvfp4_route_forward_noalloc",
     "moe_mxfp4_slot_bytes", "moe_mxfp4_forward_workspace_bytes", "moe_mxfp4_forward", "moe_mxfp4_dequant",
-    "moe_mxfp4_dequant_slot", "moe_mxfp4_slice_bank",
+    "moe_mxfp4_dequant_slot", "moe_mxfp4_slice_bank", "moe_offload_device_bytes", "moe_offload_create",
+    "moe_offload_destroy", "moe_offload_layer",
 ]
 
 
@@ -112,6 +113,15 @@ def lib() -> ctypes.CDLL:
         L.moe_mxfp4_dequant_slot.argtypes = [_vp, _i, _i, _i, _vp, _vp]
         L.moe_mxfp4_slice_bank.restype = _i
         L.moe_mxfp4_slice_bank.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp]
+        L.moe_offload_device_bytes.restype = _sz
+        L.moe_offload_device_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+        L.moe_offload_create.restype = _vp
+        L.moe_offload_create.argtypes = [_i, _i, _i, _i, _i, _i, _vp, _i, ctypes.POINTER(_vp), _vp, _sz, _vp]
+        L.moe_offload_destroy.restype = None
+        L.moe_offload_destroy.argtypes = [_vp]
+        L.moe_offload_layer.restype = _i
+        L.moe_offload_layer.argtypes = [_vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_i),
+                                        ctypes.POINTER(_i)]
         L.moe_nvfp4_noalloc_scratch_bytes.restype = _sz
         L.moe_nvfp4_noalloc_scratch_bytes.argtypes = []
         L.moe_nvfp4_route_forward_noalloc.restype = _i
@@ -269,6 +279,45 @@ def moe_nvfp4_dequant_slot(slot, H, I, matrix, out, stream=None) -> int:
 
 def moe_release_streams() -> int:
     return lib().moe_release_streams()
+
+
+def moe_offload_device_bytes(num_layers: int, num_experts: int, k: int, T_max: int, H: int, I: int) -> int:
+    return int(lib().moe_offload_device_bytes(num_layers, num_experts, k, T_max, H, I))
+
+
+class OffloadEngine:
+    """moe_offload_create / moe_offload_layer / moe_offload_destroy: the layer-step engine over the expert cache.
+    cache: device u8 [num_slots, slot_bytes]; host_ptrs: layer-major list of pinned slot addresses; dev_ws: a
+    device u8 tensor of at least moe_offload_device_bytes(...) (kept alive by the engine object)."""
+
+    def __init__(self, num_layers, num_experts, k, H, I, T_max, cache, host_ptrs, dev_ws, stream=None):
+        n = num_layers * num_experts
+        assert len(host_ptrs) == n
+        self._ptrs = (ctypes.c_void_p * n)(*[int(p) for p in host_ptrs])
+        self._keep = (cache, dev_ws)
+        self._h = lib().moe_offload_create(num_layers, num_experts, k, H, I, T_max, _ptr(cache), cache.shape[0],
+                                           self._ptrs, _ptr(dev_ws), dev_ws.numel(), _stream(stream))
+        if not self._h:
+            raise MoeError(MOE_ERR_INVALID_ARGUMENT, last_error())
+
+    def layer(self, layer, logits, x, T, shared_slot, shared_gate_w, y, stream=None, copy_stream=None):
+        """Runs one layer-step; returns (n_hit, n_miss)."""
+        nh, nm = ctypes.c_int(), ctypes.c_int()
+        check(lib().moe_offload_layer(self._h, layer, _ptr(logits), _ptr(x), T, _ptr(shared_slot),
+                                      _ptr(shared_gate_w), _ptr(y), _stream(stream), _stream(copy_stream),
+                                      ctypes.byref(nh), ctypes.byref(nm)))
+        return nh.value, nm.value
+
+    def close(self):
+        if self._h:
+            lib().moe_offload_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class ExpertCache:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libmoe_nvfp4.so")
-SOURCES = ["api.cpp", "route.hip", "router.hip", "decode.hip", "prefill.hip", "util.hip", "noalloc.hip", "mxfp4.hip"]
+SOURCES = ["api.cpp", "route.hip", "router.hip", "decode.hip", "prefill.hip", "util.hip", "noalloc.hip", "mxfp4.hip", "offload.hip"]
 ARCH = "gfx950"
 
 

@@ -529,6 +529,15 @@ void moe_cache_destroy(moe_expert_cache_t* cache) { delete cache; }
 
 int moe_cache_plan(moe_expert_cache_t* c, int layer, const int32_t* ids, int n, int32_t* slot_of_expert,
                    int32_t* miss_experts, int32_t* miss_slots, int* n_miss, int* n_hit) {
+    return moe::cache_plan(c, layer, ids, n, slot_of_expert, miss_experts, miss_slots, n_miss, n_hit, nullptr);
+}
+
+}  // extern "C"
+
+// moe_cache_plan; evicted (optional, one entry per miss): the (layer * E + expert) whose slot the miss took, or
+// -1 when the slot had never been used.
+int moe::cache_plan(moe_expert_cache_t* c, int layer, const int32_t* ids, int n, int32_t* slot_of_expert,
+                    int32_t* miss_experts, int32_t* miss_slots, int* n_miss, int* n_hit, int32_t* evicted) {
     if (!c || layer < 0 || layer >= c->L || n < 0 || (n > 0 && !ids) || !slot_of_expert || !n_miss || !n_hit ||
         (n > 0 && (!miss_experts || !miss_slots)))
         return fail(MOE_ERR_INVALID_ARGUMENT, "moe_cache_plan: bad arguments");
@@ -554,14 +563,16 @@ int moe_cache_plan(moe_expert_cache_t* c, int layer, const int32_t* ids, int n, 
     }
     for (int e = 0; e < E; ++e) {  // misses take a never-used slot, else evict the least recent
         if (!c->mark[e] || c->where[base + e] >= 0) continue;
-        int s;
+        int s, prev = -1;
         if (c->never_used < c->C) {
             s = c->never_used++;
         } else {
             s = c->head;
             c->unlink(s);
-            c->where[c->owner[s]] = -1;
+            prev = c->owner[s];
+            c->where[prev] = -1;
         }
+        if (evicted) evicted[misses] = prev;
         c->owner[s] = (int32_t)(base + e);
         c->where[base + e] = s;
         c->push_recent(s);
@@ -574,5 +585,8 @@ int moe_cache_plan(moe_expert_cache_t* c, int layer, const int32_t* ids, int n, 
     *n_hit = hits;
     return MOE_OK;
 }
+
+
+extern "C" {
 
 }  // extern "C"

@@ -7,9 +7,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct moe_expert_cache;  // the host slot manager (api.cpp)
+
 namespace moe {
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// moe_cache_plan with the evicted (layer * E + expert) of each miss, or -1 for a never-used slot (api.cpp).
+int cache_plan(::moe_expert_cache* c, int layer, const int32_t* ids, int n, int32_t* slot_of_expert,
+               int32_t* miss_experts, int32_t* miss_slots, int* n_miss, int* n_hit, int32_t* evicted);
 
 // Records the calling thread's last-error message (api.cpp) and returns code.
 int set_error(int code, const char* fmt, ...);

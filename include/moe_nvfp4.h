@@ -249,6 +249,49 @@ void moe_cache_destroy(moe_expert_cache_t* cache);
 int moe_cache_plan(moe_expert_cache_t* cache, int layer, const int32_t* ids, int n, int32_t* slot_of_expert,
                    int32_t* miss_experts, int32_t* miss_slots, int* n_miss, int* n_hit);
 
+/* ------------------------------------------------------------------ offload engine
+ * One MoE layer-step over the expert cache (issue #62 "Why TP=2 loses
+ * today": the GPU caches a fraction of the experts and streams the rest over
+ * PCIe; PR #385 "Measurements": prefill serves cache hits from device
+ * memory).  The engine keeps a device-side directory of where every
+ * (layer, expert) is cached, so each step routes, looks the routed experts up
+ * on the GPU and starts the hits-only forward (with the shared expert)
+ * before the host sees anything; the host then waits only for the small
+ * lookup result (copied ahead of that forward), plans with the same LRU
+ * policy as moe_cache_plan (one pool of num_slots slots over all layers;
+ * hits refreshed, misses into never-used or least recently used slots, never
+ * a slot this step reads), copies the misses on copy_stream and runs the
+ * misses-only forward accumulating into y.  Steps without misses run one
+ * forward.  NVFP4 slots.
+ *   moe_offload_device_bytes  device workspace the engine needs (directory,
+ *                             routing, lookup, forward workspace); 0 on bad sizes
+ *   moe_offload_create        cache_base: device, num_slots slots of
+ *                             moe_nvfp4_slot_bytes(H, I), 256-byte aligned;
+ *                             host_slots: host array of num_layers*num_experts
+ *                             pointers to page-locked slots (layer-major), not
+ *                             copied; dev_ws: that workspace (256-byte aligned),
+ *                             initialised on `stream`.  Buffers stay owned by
+ *                             the caller and must outlive the engine; the engine
+ *                             itself allocates two small page-locked host
+ *                             buffers, three events and a second copy stream
+ *                             (the misses alternate between copy_stream and
+ *                             it).  NULL on error.
+ *   moe_offload_layer         logits f32 [T, E], x bf16 [T, H], 1 <= T <= T_max;
+ *                             shared_slot / shared_gate_w as in the layer struct
+ *                             (NULL: none); y f32 [T, H] out; n_hit / n_miss:
+ *                             host out.  Synchronises the host with `stream`
+ *                             once per step (after the lookup); not capturable.
+ * Not thread-safe per engine. */
+typedef struct moe_offload moe_offload_t;
+size_t moe_offload_device_bytes(int num_layers, int num_experts, int k, int T_max, int H, int I);
+moe_offload_t* moe_offload_create(int num_layers, int num_experts, int k, int H, int I, int T_max, void* cache_base,
+                                  int num_slots, const void* const* host_slots, void* dev_ws, size_t dev_ws_bytes,
+                                  hipStream_t stream);
+void moe_offload_destroy(moe_offload_t* engine);
+int moe_offload_layer(moe_offload_t* engine, int layer, const float* logits, const uint16_t* x, int T,
+                      const void* shared_slot, const uint16_t* shared_gate_w, float* y, hipStream_t stream,
+                      hipStream_t copy_stream, int* n_hit, int* n_miss);
+
 /* ------------------------------------------------------------------ bank slicing
  * Intermediate-axis slice r of n of every slot in a bank (issue #62 "What it
  * touches": gate_up gives two disjoint row ranges, down a column slice; PR
