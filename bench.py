@@ -342,19 +342,20 @@ def parity_sample(inp, res, tokens):
 # ---------------------------------------------------------------- offload
 
 def bench_offload(steps: int, warmup: int, distinct: int, want_cpu: bool = True,
-                  residency: float = 0.37, distinct_banks: bool = True):
+                  residency: float = 0.37, distinct_banks: bool = True, T: int = 8):
     """48 MoE layers whose 256 experts live in pinned host memory behind one HBM cache holding `residency`
     (default 37%) of the 12,288 expert-layer slots (global LRU, cold start).  Per layer-step, one
     moe_offload_layer call: route on the GPU, look the routed experts up in the engine's device-side directory,
     start the hits-only forward, plan on the host meanwhile (one wait for the small lookup result), copy the misses
     on two side streams, then the misses-only forward accumulates.  With want_cpu, the CPU leg checks the host LRU and the last layer-step
     against the oracle.  With distinct_banks (the default) every one of the 48 x 256 experts has its own pinned
-    host slot (34.16 GB); otherwise the experts alias 256 pinned base slots.  Returns the JSON dict."""
+    host slot (34.16 GB); otherwise the experts alias 256 pinned base slots.  T: tokens per layer-step (8: decode
+    at batch 8; 2048: a prefill chunk, whose cache hits are read in place from HBM).  Returns the JSON dict."""
     import torch
     from expert_offload_serving_amd import _lib, synth
     from expert_offload_serving_amd import layer as dl
 
-    H, I, E, k, T, L = 2560, 640, 256, 8, 8, 48
+    H, I, E, k, L = 2560, 640, 256, 8, 48
     seed = 48
     r_w, r_x, r_l, r_g = np.random.default_rng(seed).spawn(4)
     sb = synth.slot_nbytes(H, I)
@@ -444,6 +445,23 @@ def bench_offload(steps: int, warmup: int, distinct: int, want_cpu: bool = True,
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # a cache that holds every expert-layer never evicts: replaying the last timed steps' routing then hits on
+    # every expert, which times the engine's all-hit layer-step (one forward, no copies)
+    all_hits = None
+    if n_slots >= L * E:
+        replay = list(range(max(warmup, total - 8), total))
+        saved = {key: v.copy() for key, v in stats.items()}
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for s_ in replay:
+            for l in range(L):
+                layer_step(s_, l)
+        torch.cuda.synchronize()
+        ta = time.perf_counter() - ta
+        assert stats["misses"][replay].sum() == 0
+        all_hits = round(ta * 1e3 / (len(replay) * L), 4)
+        stats.update(saved)
+
     # pinned host -> HBM copy rate alone (64 slots over two copy streams, host clock)
     n_probe = 64
     copies = [copy, torch.cuda.Stream(device=dev)]
@@ -481,7 +499,7 @@ def bench_offload(steps: int, warmup: int, distinct: int, want_cpu: bool = True,
         cpu_checks = {"lru_matches_oracle_model": lru_ok, "rel_l2_last_layer_step": rel,
                       "tokens_checked": int(toks.size)}
         log("offload: timing the oracle (child process)")
-        cpu_checks["cpu_baseline"] = cpu_baseline("offload", "layer-tokens/s")
+        cpu_checks["cpu_baseline"] = cpu_baseline("offload" if T <= 16 else "prefill_2048", "layer-tokens/s")
 
     hits, misses = stats["hits"][warmup:].sum(), stats["misses"][warmup:].sum()
     miss_bytes = misses * sb
@@ -492,7 +510,8 @@ def bench_offload(steps: int, warmup: int, distinct: int, want_cpu: bool = True,
         "value": round(layer_tok_s, 2), "unit": "layer-tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(wall * 1e3 / steps, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
-        "config": {"workload": f"offload_48x256_cache{round(100 * n_slots / (L * E))}", "H": H, "I": I, "E": E, "k": k, "T": T, "layers": L,
+        "config": {"workload": f"offload{'' if T <= 16 else '_prefill' + str(T)}_48x256_cache"
+                               f"{round(100 * n_slots / (L * E))}", "H": H, "I": I, "E": E, "k": k, "T": T, "layers": L,
                    "cache_slots": n_slots, "residency": round(n_slots / (L * E), 4), "routing": "Zipf(1.2) per layer",
                    "host_banks": (f"{L} x {E} distinct pinned expert slots ({L * E * sb / 1e9:.2f} GB)" if host is not None
                                   else f"{E} pinned base slots ({E * sb / 1e9:.2f} GB); expert (l, e) = base "
@@ -508,6 +527,7 @@ def bench_offload(steps: int, warmup: int, distinct: int, want_cpu: bool = True,
                                              max(1, stats["hits"][:warmup].sum() + stats["misses"][:warmup].sum()), 4),
                     "model_tokens_per_s": round(T * steps / wall, 2), "ms_per_layer_step": round(wall * 1e3 / (steps * L), 4),
                     "miss_GB_per_step": round(miss_bytes / steps / 1e9, 3), "h2d_copy_GBps_alone": round(h2d_gbs, 2),
+                    **({"ms_per_layer_step_all_hits": all_hits} if all_hits is not None else {}),
                     "warmup_s": round(t_cold, 2)},
         **({"cpu_baseline": cpu_checks.pop("cpu_baseline"), "parity": cpu_checks} if cpu_checks is not None else {}),
     }
@@ -684,7 +704,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="all",
-                    choices=["decode_bs1", "decode_bs16", "prefill_2048", "offload", "mxfp4_decode_bs1",
+                    choices=["decode_bs1", "decode_bs16", "prefill_2048", "offload", "offload_prefill", "mxfp4_decode_bs1",
                              "mxfp4_decode_bs16", "all", *ROUTER_CONFIGS])
     ap.add_argument("--replicas", type=int, default=0,
                     help="copies of the expert bank rotated over steps (default 16 at bs 1, 8 at bs 16, 4 prefill)")
@@ -725,6 +745,8 @@ def main():
             steps, warmup = (64, 16) if args.steps == 200 and args.warmup == 10 else (args.steps, args.warmup)
             return bench_offload(steps, warmup, args.distinct, want_cpu, args.residency,
                                  not args.aliased_banks)
+        if name == "offload_prefill":  # 2048-token chunks through all 48 layers: a few steps
+            return bench_offload(3, 1, args.distinct, want_cpu, args.residency, not args.aliased_banks, T=2048)
         steps, warmup = args.steps, args.warmup
         if name == "prefill_2048":
             steps, warmup = max(1, min(steps, 20)), max(1, min(warmup, 3))
@@ -737,7 +759,8 @@ def main():
     # every workload, one line: the headline decode batch 1 at the top level, the others under "configs"
     head = run("decode_bs1")
     head["configs"] = {}
-    for name in ("decode_bs16", "prefill_2048", "offload", "mxfp4_decode_bs1", "mxfp4_decode_bs16"):
+    for name in ("decode_bs16", "prefill_2048", "offload", "offload_prefill", "mxfp4_decode_bs1",
+                 "mxfp4_decode_bs16"):
         head["configs"][name] = run(name)
         torch.cuda.empty_cache()
     print(json.dumps(head), flush=True)
