@@ -71,16 +71,21 @@ __device__ __forceinline__ void issue_a(const DecArgs& a, const Item& it, int wa
     L.glob = __uint_as_float(buf_load4(it.sres, a.gu_glob + 4 * ((lane >> 5) * I + kSl * s + (lane & 31))));
 }
 
+// Phase B loads of row group wave + 8 i (one record and its scales).
+template <int NRGW>
+__device__ __forceinline__ void issue_b_one(const DecArgs& a, const Item& it, int wave, int lane, BLoads<NRGW>& L,
+                                            int i) {
+    const int NG = a.H / 64, soff = lane_scale_off(lane);
+    const int rg = wave + kDW * i;
+    const int rec = it.s * NG + rg;
+    L.br[i] = buf_load16(it.sres, rg < NG ? a.dn_codes + rec * kRecBytes + 16 * lane : kOob);
+    L.bsc[i] = buf_load4(it.sres, rg < NG ? a.dn_scales + rec * kRecScaleBytes + soff : kOob);
+}
+
 template <int NRGW>
 __device__ __forceinline__ void issue_b(const DecArgs& a, const Item& it, int wave, int lane, BLoads<NRGW>& L) {
-    const int NG = a.H / 64, soff = lane_scale_off(lane);
 #pragma unroll
-    for (int i = 0; i < NRGW; ++i) {
-        const int rg = wave + kDW * i;
-        const int rec = it.s * NG + rg;
-        L.br[i] = buf_load16(it.sres, rg < NG ? a.dn_codes + rec * kRecBytes + 16 * lane : kOob);
-        L.bsc[i] = buf_load4(it.sres, rg < NG ? a.dn_scales + rec * kRecScaleBytes + soff : kOob);
-    }
+    for (int i = 0; i < NRGW; ++i) issue_b_one<NRGW>(a, it, wave, lane, L, i);
 }
 
 // Workgroup LDS besides the activations.
@@ -94,7 +99,12 @@ struct DecShared {
 // refills LA with the loads of item na and, after phase B, LB with those of
 // item nb (without PF, when no workgroup has a next item, nothing is
 // prefetched: even out-of-range loads take the CU's address units).
-template <int KQW, int NRGW, bool PF>
+// With ILB the caller has issued only the phase A loads: phase B's are issued
+// one row group after each 128-column step of phase A.  A CU holds a limited
+// number of loads in flight and a wave that issues past that limit stalls, so
+// this keeps the waves computing phase A on the records that have arrived
+// while the rest stream in.
+template <int KQW, int NRGW, bool PF, bool ILB = false>
 __device__ __forceinline__ void run_item(const DecArgs& a, DecShared& sh, const _Float16* x16, int XP, int nsl,
                                          const rsrc_t& pres, const Item& cur, ALoads<KQW>& LA, BLoads<NRGW>& LB,
                                          const Item& na, const Item& nb, int tid, int lane, int wave, int par) {
@@ -107,23 +117,31 @@ __device__ __forceinline__ void run_item(const DecArgs& a, DecShared& sh, const 
     f32x4_t acc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) acc[tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int NSTEP = KQW > NRGW ? KQW : NRGW;
 #pragma unroll
-    for (int i = 0; i < KQW; ++i) {
+    for (int i = 0; i < NSTEP; ++i) {
         const int kq = (wave & 3) + 4 * i;
-        if (kq >= KQ) break;  // uniform per wave
+        if (i < KQW && kq < KQ) {  // uniform per wave
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f16x8_t X = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(xr + 128 * kq + 32 * m));
+            for (int m = 0; m < 4; ++m) {
+                const f16x8_t X =
+                    __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(xr + 128 * kq + 32 * m));
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                f16x2_t S;
-                if (m == 0) S = scale_f16x2<0>(LA.asc[i][tt]);
-                else if (m == 1) S = scale_f16x2<1>(LA.asc[i][tt]);
-                else if (m == 2) S = scale_f16x2<2>(LA.asc[i][tt]);
-                else S = scale_f16x2<3>(LA.asc[i][tt]);
-                const f16x8_t A = frag_f16(word_of(LA.ar[i][tt], m), S);
-                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, X, acc[tt], 0, 0, 0);
+                for (int tt = 0; tt < 2; ++tt) {
+                    f16x2_t S;
+                    if (m == 0) S = scale_f16x2<0>(LA.asc[i][tt]);
+                    else if (m == 1) S = scale_f16x2<1>(LA.asc[i][tt]);
+                    else if (m == 2) S = scale_f16x2<2>(LA.asc[i][tt]);
+                    else S = scale_f16x2<3>(LA.asc[i][tt]);
+                    const f16x8_t A = frag_f16(word_of(LA.ar[i][tt], m), S);
+                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, X, acc[tt], 0, 0, 0);
+                }
             }
+        }
+        if (ILB && i < NRGW) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_b_one<NRGW>(a, cur, wave, lane, LB, i);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     const float glob = LA.glob;
@@ -300,7 +318,7 @@ __device__ void copy_down_globals(const DecArgs& a, const Tables& tb, int n_act,
 }
 
 // Persistent over work items u = blockIdx.x + j * gridDim.x; item u is
-// (expert act[u / nsl], or the shared expert, slice u % nsl).  Every token's
+// (the shared expert for u < nsl, else expert act[u / nsl - 1]; slice u % nsl).  Every token's
 // activations are staged in LDS once, as fp16 times a per-token power of two.
 // Phase A loads run two items ahead and phase B loads one item ahead, so the
 // next items stream while this one reduces, runs SwiGLU and finishes.
@@ -318,7 +336,21 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
     Tables& tb = sh.tb;
 
     XRegs<kDW> xv;
-    const int n_act = ROUTE ? stage_route<kDW>(a, tb, xv, tid, lane, wave) : stage_tables<kDW>(a, tb, xv, tid, lane, wave);
+    const int G = (int)gridDim.x, c = lane & 15;
+    ALoads<KQW> LA0, LA1;
+    BLoads<NRGW> LB;
+    Item it0;
+    // a workgroup whose one item is the shared expert's (items 0 .. nsl-1) needs no routing for it: its weights
+    // start streaming before the kernel routes
+    const bool early = ROUTE && !MULTI && a.shared != nullptr && (int)blockIdx.x < nsl;  // uniform
+    const auto start_early = [&]() {
+        if (early) {
+            it0 = decode_item(a, tb, 0, nsl, blockIdx.x, true, c);
+            issue_a<KQW>(a, it0, wave, lane, tid, LA0);
+        }
+    };
+    const int n_act = ROUTE ? stage_route<kDW>(a, tb, xv, tid, lane, wave, start_early)
+                            : stage_tables<kDW>(a, tb, xv, tid, lane, wave);
     const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
     int u = blockIdx.x;
     if (u >= n_items) {  // uniform: a workgroup without items; spare ones copy the down-row globals
@@ -328,20 +360,22 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
     }
 
     // ---- the first items' weights start streaming, then the activations go to LDS
-    const int G = (int)gridDim.x, c = lane & 15;
     const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
-    Item it0 = decode_item(a, tb, n_act, nsl, u, true, c);
-    ALoads<KQW> LA0, LA1;
-    BLoads<NRGW> LB;
     // the first item's loads, the activations to LDS, then the second item's loads (issuing loads is paced
     // by the CU's address units, so loads the first item does not need would delay the staging)
-    issue_a<KQW>(a, it0, wave, lane, tid, LA0);
-    issue_b<NRGW>(a, it0, wave, lane, LB);
-    __builtin_amdgcn_sched_barrier(0);
-    stage_x<kDW>(a, xv, sh.xsh, x16, XP, tid, lane, wave);
+    // (a workgroup with one item issues phase B's loads during phase A).  With one item the activations go to
+    // LDS first: they arrived with the routing, and a workgroup that started early has slack to wait for them.
+    if (!MULTI) stage_x<kDW>(a, xv, sh.xsh, x16, XP, tid, lane, wave);
+    if (!early) {
+        it0 = decode_item(a, tb, n_act, nsl, u, true, c);
+        issue_a<KQW>(a, it0, wave, lane, tid, LA0);
+        if (MULTI) issue_b<NRGW>(a, it0, wave, lane, LB);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (MULTI) stage_x<kDW>(a, xv, sh.xsh, x16, XP, tid, lane, wave);
     __syncthreads();
     if (!MULTI) {
-        run_item<KQW, NRGW, false>(a, sh, x16, XP, nsl, pres, it0, LA0, LB, it0, it0, tid, lane, wave, 0);
+        run_item<KQW, NRGW, false, true>(a, sh, x16, XP, nsl, pres, it0, LA0, LB, it0, it0, tid, lane, wave, 0);
         return;
     }
     Item it1 = decode_item(a, tb, n_act, nsl, u + G, u + G < n_items, c);
@@ -510,7 +544,7 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
     const int H = a.H, T = a.T, k = a.k;
     const int XP = H + 8;
     XRegs<kWW> xv;
-    const int n_act = ROUTE ? stage_route<kWW>(a, sh.tb, xv, tid, lane, wave)
+    const int n_act = ROUTE ? stage_route<kWW>(a, sh.tb, xv, tid, lane, wave, [] {})
                             : stage_tables<kWW>(a, sh.tb, xv, tid, lane, wave);
     const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
     const int stride = (int)gridDim.x * kWW;
@@ -701,6 +735,8 @@ hipError_t launch_fused(DecArgs& a, int items_max, int nsl, int ncu, hipStream_t
     } else {
         a.dgrow = nullptr;
     }
+    // the routing outputs come from a spare workgroup when there is one (it has no item to delay)
+    a.route_wg = a.n_spare > 0 ? grid - 1 : 0;
     const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
     if (multi)
         hipLaunchKernelGGL((fused_kernel<KQW, NRGW, ROUTE, true>), dim3(grid), dim3(kDT), lds, s, a, nsl);
@@ -761,6 +797,10 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
     (void)assign_pos;
     const int H = L.H, I = L.I, E = L.E, k = L.k;
     const WsLayout wl = ws_layout(T, H, I, E, k);
+    // the regions must not overlap (a kernel would read another region's data as its own)
+    if (wl.dg < wl.part + decode_part_bytes(T, H, I, k) ||
+        wl.dgrow < wl.dg + decode_rowslot_bytes(T, k) || wl.total < wl.dgrow + decode_dgrow_bytes(T, H, k))
+        return hipErrorInvalidValue;
     DecArgs a;
     a.bank = L.bank; a.slot_bytes = L.slot_bytes; a.num_slots = L.num_slots; a.slot_of_expert = L.slot_of_expert;
     a.shared = L.shared; a.wg = L.wg; a.x = x;
@@ -776,6 +816,7 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
     a.dn_codes = (int)gm.dn_codes; a.dn_scales = (int)gm.dn_scales; a.dn_glob = (int)gm.dn_glob;
     a.no_glob = 0;
 
+    a.route_wg = 0;
     a.logits = route ? route->logits : nullptr;
     a.r_ids = route ? route->ids : nullptr;
     a.r_w = route ? route->w : nullptr;

@@ -40,6 +40,7 @@ struct DecArgs {
     const float* logits;
     int32_t *r_ids, *r_offsets, *r_sorted, *r_pos;
     float* r_w;
+    int route_wg;      // the workgroup that writes the routing outputs
 };
 
 // A slot index outside [0, num_slots) leaves its expert out (-1), like a
@@ -79,9 +80,12 @@ __device__ __forceinline__ Item decode_item(const DecArgs& a, const Tables& tb, 
     Item it;
     const int ui = u / nsl;
     it.s = u % nsl;
-    const bool routed = valid && ui < n_act;
-    const bool shared = valid && !routed;
-    const int e = __builtin_amdgcn_readfirstlane(tb.act[routed ? ui : 0]);
+    // the shared expert's items come first: they need no routing, so a kernel can start them before it routes
+    const bool has_sh = a.shared != nullptr;
+    const int ri = has_sh ? ui - 1 : ui;
+    const bool shared = valid && has_sh && ui == 0;
+    const bool routed = valid && !shared && ri < n_act;
+    const int e = __builtin_amdgcn_readfirstlane(tb.act[routed ? ri : 0]);
     const int e_ok = routed ? e : 0;
     const int b0 = __builtin_amdgcn_readfirstlane(tb.off[e_ok]);
     const int b1 = __builtin_amdgcn_readfirstlane(tb.off[e_ok + 1]);
@@ -185,11 +189,15 @@ __device__ __forceinline__ int stage_tables(const DecArgs& a, Tables& tb, XRegs<
 // selects the top-k of tokens w and w + NW straight from the logits, then
 // every assignment is ranked directly,
 //   offsets[e] = #{b : e_b < e},  pos(a) = #{b : (e_b, b) < (e_a, a)},
-// the same stable grouping the routing kernels produce.  Workgroup 0 writes
-// the routing outputs.
-template <int NW>
+// the same stable grouping the routing kernels produce (for one token, whose
+// k experts are distinct, a single pass over the experts).  Workgroup
+// a.route_wg writes the routing outputs.
+// after_loads() runs once the slot-map and activation loads are issued, before
+// the routing: a caller can start loads that need no routing there, behind the
+// activations (which every path then finds issued before its weight loads).
+template <int NW, class AfterLoads>
 __device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<NW>& xr, int tid, int lane,
-                                           int wave) {
+                                           int wave, AfterLoads&& after_loads) {
     constexpr int NT = NW * kWave;
     const int H = a.H, T = a.T, k = a.k, E = a.E, n = T * k;
     constexpr int R = (kMaxE + NT - 1) / NT;
@@ -215,6 +223,8 @@ __device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<N
         }
     }
     __builtin_amdgcn_sched_barrier(0);
+    after_loads();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < (kDecodeMaxT + NW - 1) / NW; ++p) {  // wave w: tokens w, w + NW
         const int t = wave + NW * p;
@@ -228,7 +238,32 @@ __device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<N
         if (i < E) tb.slot[i] = slot_or_skip((int)vs[r], a.num_slots);
     }
     __syncthreads();
-    const bool out = blockIdx.x == 0;
+    const bool out = (int)blockIdx.x == a.route_wg;
+    if (T == 1) {  // uniform.  One token's k experts are distinct: each expert's group holds at most one assignment,
+                   // so one pass over the experts gives offsets, the active list and the permutation
+        for (int e = tid; e <= E; e += NT) {
+            int lt = 0, at = -1;
+#pragma unroll 8
+            for (int b = 0; b < k; ++b) {
+                const int eb = tb.ids[b];
+                lt += eb < e ? 1 : 0;
+                at = eb == e ? b : at;
+            }
+            tb.off[e] = lt;
+            if (at >= 0) tb.act[lt] = e, tb.sorted[lt] = at;
+            if (out) {
+                a.r_offsets[e] = lt;
+                if (at >= 0) {
+                    a.r_ids[at] = e;
+                    a.r_w[at] = tb.w[at];
+                    a.r_sorted[lt] = at;
+                    a.r_pos[at] = lt;
+                }
+            }
+        }
+        __syncthreads();
+        return k;
+    }
     // P consecutive lanes (a power of two, up to 16) share one assignment's count
     int P = 1;
     while (P < 16 && 2 * P * n <= NT) P *= 2;
@@ -328,9 +363,11 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
         } else if (a.dgrow != nullptr) {  // uniform: the rows' globals were copied by the item kernel
             dg = __builtin_bit_cast(f32x4_t, buf_load16(dgres, 4 * (row * H + col)));
         } else {
-            const int rs = a.rowslot[row];
+            // (an entry outside the bank or the shared marker is read as "left out": never an address)
+            const int rs0 = a.rowslot[row];
+            const int rs = rs0 == -2 ? -2 : slot_or_skip(rs0, a.num_slots);
             const uint8_t* slot = rs >= 0 ? a.bank + (size_t)rs * a.slot_bytes : (rs == -2 ? a.shared : a.bank);
-            const rsrc_t gsr = make_rsrc(slot, rs == -1 ? 0u : (uint32_t)a.slot_bytes);
+            const rsrc_t gsr = make_rsrc(slot, rs == -1 || (rs == -2 && a.shared == nullptr) ? 0u : (uint32_t)a.slot_bytes);
             dg = __builtin_bit_cast(f32x4_t, buf_load16(gsr, a.dn_glob + 4 * col));
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -367,6 +404,8 @@ __global__ void __launch_bounds__(256) dcombine_kernel(DecArgs a, int nsl, int n
     if (a.accumulate) out += *yp;
     *yp = out;
 }
+
+
 
 }  // namespace
 }  // namespace moe

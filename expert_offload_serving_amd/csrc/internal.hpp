@@ -77,7 +77,7 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
     WsLayout L{};
     if (decode_path(T, H, I, k)) {
         L.part = 0;
-        L.dg = align256(decode_part_bytes(T, H, I, k));
+        L.dg = L.part + align256(decode_part_bytes(T, H, I, k));
         L.dgrow = L.dg + align256(decode_rowslot_bytes(T, k));
         L.total = L.dgrow + align256(decode_dgrow_bytes(T, H, k));
         return L;

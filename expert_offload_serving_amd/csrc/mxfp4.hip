@@ -490,6 +490,7 @@ hipError_t launch_mx_decode(const Layer& L, const uint16_t* x, int T, const floa
     a.gu_codes = (int)gm.gu_codes; a.gu_scales = (int)gm.gu_scales; a.gu_glob = 0;
     a.dn_codes = (int)gm.dn_codes; a.dn_scales = (int)gm.dn_scales; a.dn_glob = 0;
     a.no_glob = 1;
+    a.route_wg = 0;
     a.logits = nullptr;
     int ncu = 0;
     hipError_t e = mx_device_cus(ncu);

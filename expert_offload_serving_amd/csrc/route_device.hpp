@@ -21,11 +21,13 @@ constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr3 = 0x113, kDp
 
 // Logits are compared as order-preserving unsigned keys: the float bits with
 // the sign bit set for non-negative values and all bits inverted for negative
-// ones, after folding -0 onto +0.  Key 0 (an all-ones NaN) marks "no
-// candidate": it is never the maximum while a real logit remains.
+// ones, after folding -0 onto +0.  Key 0 marks "no candidate": the one float
+// pattern that would map to it (an all-ones NaN, a precondition violation)
+// takes key 1 instead, so 0 is never the maximum while a logit remains.
 __device__ __forceinline__ uint32_t order_key(float v) {
     const uint32_t u = __float_as_uint(v + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return key > 1u ? key : 1u;
 }
 __device__ __forceinline__ float key_logit(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
@@ -58,12 +60,15 @@ __device__ __forceinline__ uint32_t wave_umax_dpp(uint32_t v) {
 // One wave selects the top-k of row `l` (E <= 64 * VPL logits; lane L holds
 // experts L + 64 i; every lane passes the same row) and writes ids and weights
 // (global or LDS pointers).
-// Each of the k rounds takes the wave maximum of the remaining keys, then the
-// lowest expert index holding it (a second wave maximum, over ~index of the
-// entries equal to the first).  A selected key becomes 0.
-// A NaN logit (a precondition violation) only changes which valid, distinct
-// experts come out.  Weights: softmax over the k selected logits in double
-// (exp(l_j - l_max) / sum), summed in selection order, rounded to f32.
+// Each lane first orders its VPL keys (descending; equal keys keep index
+// order, as the insertion network below is stable), so its head is its best
+// remaining candidate.  Each of the k rounds takes the wave maximum M of the
+// heads; the selection is the lowest expert index holding M, which is the
+// head of the lowest lane among those whose head is M and whose slot i is the
+// smallest (one ballot, or one per slot when heads tie), and that lane drops
+// its head.  Selection j is kept by lane j % 64 and stored after the rounds.
+// Weights: softmax over the k selected logits in double (exp(l_j - l_max) /
+// sum), summed in selection order, rounded to f32.
 template <int VPL>
 __device__ void topk_one_token(const float* __restrict__ l, int E, int k, int32_t* __restrict__ ids,
                                float* __restrict__ w, int lane) {
@@ -78,33 +83,69 @@ __device__ void topk_one_token(const float* __restrict__ l, int E, int k, int32_
     uint32_t lv[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) lv[i] = buf_load4(lres, 4 * (lane + kWave * i));
-    uint32_t v[VPL];
+    uint32_t kk[VPL];  // this lane's remaining keys, best first
+    int ss[VPL];       // their slots i (expert lane + 64 i); VPL once dropped
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) v[i] = order_key(__uint_as_float(lv[i])) & (lane + kWave * i < E ? ~0u : 0u);
+    for (int i = 0; i < VPL; ++i) {
+        kk[i] = order_key(__uint_as_float(lv[i])) & (lane + kWave * i < E ? ~0u : 0u);
+        ss[i] = i;
+    }
+#pragma unroll
+    for (int i = 1; i < VPL; ++i)
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const bool sw = kk[j] > kk[j - 1];
+            const uint32_t ka = kk[j - 1], kb = kk[j];
+            const int sa = ss[j - 1], sb = ss[j];
+            kk[j - 1] = sw ? kb : ka;
+            kk[j] = sw ? ka : kb;
+            ss[j - 1] = sw ? sb : sa;
+            ss[j] = sw ? sa : sb;
+        }
     float held = 0.0f;  // selection j's logit, kept by lane j (j < 64)
+    int held_id = 0;    // and its expert
     float m = 0.0f;
     for (int j = 0; j < k; ++j) {
-        uint32_t lm = v[0];
+        const uint32_t M = wave_umax_dpp(kk[0]);
+        uint64_t hit = __ballot(kk[0] == M);
+        int slot;
+        if (__popcll(hit) == 1) {  // uniform; the usual case
+            slot = __builtin_amdgcn_readlane(ss[0], (int)__builtin_ctzll(hit));
+        } else {  // heads tie on M: the smallest slot holding M, then its lowest lane
+            slot = 0;
+            for (int i = 0; i < VPL; ++i) {
+                const uint64_t b = __ballot(kk[0] == M && ss[0] == i);
+                if (b != 0) {
+                    hit = b;
+                    slot = i;
+                    break;
+                }
+            }
+        }
+        // M >= 1 is the head of some lane (k <= E valid keys), so hit != 0
+        const int owner = (int)__builtin_ctzll(hit);
+        const int bi = min(slot * kWave + owner, E - 1);  // the clamp only keeps the index in range
+        if (lane == owner) {
 #pragma unroll
-        for (int i = 1; i < VPL; ++i) lm = v[i] > lm ? v[i] : lm;
-        const uint32_t M = wave_umax_dpp(lm);
-        // lowest index holding M: each lane offers its lowest slot holding M as ~index, the wave takes the
-        // largest (all on the vector units: with many waves per CU the shared scalar unit would be the limit)
-        uint32_t cand = 0;
-#pragma unroll
-        for (int i = VPL - 1; i >= 0; --i) cand = v[i] == M ? ~(uint32_t)(lane + kWave * i) : cand;
-        const uint32_t best = wave_umax_dpp(cand);
-        // M is a key some lane holds, so best != 0; the clamp only keeps the index in range
-        const int bi = best != 0 ? (int)~best : 0;
-        const int owner_slot = bi / kWave, owner_lane = bi % kWave;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) v[i] = (i == owner_slot && lane == owner_lane) ? 0u : v[i];
+            for (int i = 0; i + 1 < VPL; ++i) {
+                kk[i] = kk[i + 1];
+                ss[i] = ss[i + 1];
+            }
+            kk[VPL - 1] = 0u;
+            ss[VPL - 1] = VPL;
+        }
         const float bv = key_logit(M);
         if (j == 0) m = bv;
-        if ((j % kWave) == lane) ids[j] = bi;
-        if (j == lane) held = bv;
-        if (j >= kWave && (j % kWave) == lane) w[j] = bv;  // parked logit, replaced below
+        if (j == lane) {
+            held = bv;
+            held_id = bi;
+        }
+        if (j >= kWave && (j % kWave) == lane) {  // rare: more selections than lanes; logit parked in w
+            ids[j] = bi;
+            w[j] = bv;
+        }
     }
+    if (lane < k) ids[lane] = held_id;
     // exp of each selected logit relative to the largest, in double
     if (k <= kWave) {
         const double ex = lane < k ? exp((double)held - (double)m) : 0.0;

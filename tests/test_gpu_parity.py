@@ -421,6 +421,34 @@ def test_forward_limits():
         _route_forward_vs_separate(L, f"route_forward limits E={E} k={k} T={T}")
 
 
+def test_one_token_calls_sharing_a_workspace():
+    """One token, up to 16 output rows in the combine: calls that share one workspace (route_forward and forward
+    alternating, accumulate on and off, with and without the shared expert) match the oracle each time; the
+    workspace starts as garbage, since no region of it has to start at any value."""
+    rng = np.random.default_rng(41)
+    for (H, I, E, k) in [(256, 64, 8, 2), (512, 96, 16, 15), (2560, 640, 256, 8)]:
+        _announce(f"one-token calls sharing a workspace H={H} I={I} E={E} k={k}")
+        L = _small_layer(rng, H, I, E, k, 1, n_distinct=min(E + 1, 12))
+        dev = device_layer(L)
+        nb = _lib.moe_nvfp4_route_forward_workspace_bytes(1, H, I, E, k)
+        ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
+        for it in range(4):
+            L.x = synth.f32_to_bf16_bits(rng.standard_normal((1, H)).astype(np.float32))
+            L.logits = rng.standard_normal((1, E)).astype(np.float32)
+            x, lg = device_x(L), device_logits(L)
+            shared = it != 2
+            acc = it == 3
+            y0 = torch.from_numpy(rng.standard_normal((1, H)).astype(np.float32)).cuda()
+            y = y0.clone()
+            if it % 2 == 0:
+                y, _ = dl.route_forward(dev, lg, x, y=y, accumulate=acc, ws=ws, shared=shared)
+            else:
+                y = dl.forward(dev, x, dl.route(lg, k), y=y, accumulate=acc, ws=ws, shared=shared)
+            torch.cuda.synchronize()
+            want = _oracle_forward(L, shared=shared) + (y0.cpu().numpy() if acc else 0.0)
+            assert_close(y.cpu().numpy(), want, f"one token H={H} k={k} call {it}")
+
+
 def test_route_forward_graph_replays():
     """route_forward captured in a HIP graph: every replay (with eager work in between) equals the eager call."""
     for name, T in [("decode_bs1", 1), ("decode_bs16", 16), ("prefill_2048", 96)]:
