@@ -49,11 +49,11 @@ __device__ __forceinline__ int slot_or_skip(int sl, int num_slots) { return sl >
 
 // Routing tables staged in LDS once per workgroup.
 struct Tables {
+    alignas(16) int ids[kDecodeMaxAssign];   // top-k ids, when the kernel routes (first: 16-byte aligned)
     int off[kMaxE + 1];          // expert_offsets
     int slot[kMaxE];             // slot_of_expert
     int sorted[kDecodeMaxAssign];
     float w[kDecodeMaxAssign];
-    int ids[kDecodeMaxAssign];   // top-k ids, when the kernel routes
     int act[kMaxE];              // experts with assignments, ascending
     int n_act;
 };
@@ -241,13 +241,19 @@ __device__ __forceinline__ int stage_route(const DecArgs& a, Tables& tb, XRegs<N
     const bool out = (int)blockIdx.x == a.route_wg;
     if (T == 1) {  // uniform.  One token's k experts are distinct: each expert's group holds at most one assignment,
                    // so one pass over the experts gives offsets, the active list and the permutation
+        const int4* ids4 = reinterpret_cast<const int4*>(tb.ids);  // read four at a time; ids past k are not used
         for (int e = tid; e <= E; e += NT) {
             int lt = 0, at = -1;
-#pragma unroll 8
-            for (int b = 0; b < k; ++b) {
-                const int eb = tb.ids[b];
-                lt += eb < e ? 1 : 0;
-                at = eb == e ? b : at;
+#pragma unroll 2
+            for (int b = 0; b < k; b += 4) {
+                const int4 v = ids4[b / 4];
+                const int eb[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bool in = b + u < k;
+                    lt += in && eb[u] < e ? 1 : 0;
+                    at = in && eb[u] == e ? b + u : at;
+                }
             }
             tb.off[e] = lt;
             if (at >= 0) tb.act[lt] = e, tb.sorted[lt] = at;

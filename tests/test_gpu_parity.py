@@ -338,6 +338,37 @@ def _route_forward_vs_separate(L, what, slot_map=None, shared=True):
     assert_close(y_one.cpu().numpy(), _oracle_forward(L, slot_map=slot_map, shared=shared), what)
 
 
+def test_route_tied_blocks_and_group_shapes():
+    """Selection order under structured ties: 64 keys tied at the top spread over every (16-lane row, slot) group,
+    65 of them, one key above the tie, k = 16 with E = 256, and E = 16 (fewer logits than lanes), each bit-exact
+    against the oracle through the routing launch and through the decode kernel's own routing (one token)."""
+    rng = np.random.default_rng(77)
+    E = 256
+    def grouped(n_tied, above=False):
+        lg = (rng.standard_normal(E) * 0.1 - 5.0).astype(np.float32)
+        # group (row r, slot i) holds experts 64 i + 16 r + [0, 16); 4 tied keys in each of the 16 groups
+        tied = [64 * i + 16 * r + j for i in range(4) for r in range(4) for j in range(4)]
+        extra = [64 * i + 16 * r + 4 for i in range(4) for r in range(4)]
+        for e in (tied + extra)[:n_tied]:
+            lg[e] = 1.0
+        if above:
+            lg[0] = 1.5  # replaces a tied key: still 64 candidates
+        return lg[None, :]
+    cases = [(grouped(64), 8, "64 tied candidates"), (grouped(65), 8, "65 candidates (rounds)"),
+             (grouped(64, above=True), 8, "one key above 64 tied"),
+             (rng.standard_normal((1, E)).astype(np.float32), 16, "k = 16 groups of 16"),
+             (rng.standard_normal((1, 16)).astype(np.float32), 8, "E = 16: fewer groups than k")]
+    for lg, k, what in cases:
+        _check_route(lg, k, what)
+        _check_route(np.repeat(lg, 3, axis=0), k, what + " x3 tokens")
+    # the decode kernel's own routing (one token, E = 256, k = 8) on the tied cases
+    for lg, k, what in cases[:3]:
+        _announce(f"route_forward one token: {what}")
+        L = _small_layer(rng, 256, 64, E, k, 1, n_distinct=12)
+        L.logits = lg
+        _route_forward_vs_separate(L, f"route_forward {what}")
+
+
 @pytest.mark.parametrize("T", [1, 3, 8, 16])
 def test_route_forward_decode(T):
     """Routing inside the decode kernels (E <= 256, T <= 8: one wave per token); T = 16 routes in its own launch."""
