@@ -438,6 +438,133 @@ __global__ void __launch_bounds__(256) mx_dequant_dn_kernel(const uint8_t* __res
     }
 }
 
+// ------------------------------------------------------------------ one item per workgroup
+// When the items fit the CUs one per workgroup (one token at top-8 and
+// I = 640: 180 items), a wave per item leaves most of each CU idle, and one
+// wave's loads in flight are too few to stream an item's ~120 KB in time.
+// Then the eight waves of a workgroup share its item: wave w takes the
+// 128-column gate_up chunks q = w + 8 i (all four tiles of the slice) and the
+// 64-row down groups w + 8 i.  The gate_up partial sums meet in LDS and are
+// added over the waves in a fixed order; every wave forms SwiGLU for exactly
+// the down operand it needs (as the wave kernel does, from the summed tiles).
+// A wave issues its gate_up loads first and one down group after each
+// gate_up chunk, so it computes on the chunks that have arrived while the
+// down records stream in.
+constexpr int kMxQW = 3;  // most gate_up chunks per wave (H <= 2560: 20 chunks over 8 waves)
+constexpr int kMxBW = 5;  // most down groups per wave (H <= 2560: 40 groups over 8 waves)
+
+__global__ void __launch_bounds__(kMT) mx_fused_kernel(DecArgs a, int nsl) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+    __shared__ Tables tb;
+    __shared__ f32x4_t red[kMW][4][kWave];  // gate_up partial sums of every wave
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int H = a.H, T = a.T, k = a.k;
+    const int c = lane & 15, g = lane >> 4;
+    const int KQ = H / 128, NG = H / 64, NB = H / 32;
+    XRegs<kMW> xv;
+    const int n_act = stage_tables<kMW>(a, tb, xv, tid, lane, wave);
+    const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
+    if ((int)blockIdx.x >= n_items) return;  // uniform
+    const Item it = decode_item(a, tb, n_act, nsl, (int)blockIdx.x, true, c);
+
+    // ---- gate_up loads of this wave's chunks: tiles 0, 1 (gate rows 32 s + 16 r), 2, 3 (the matching up rows)
+    const int NTT = 2 * a.I / 16, up = a.I / 16;
+    u32x4_t ac[kMxQW][4];
+    uint32_t as[kMxQW][4];
+#pragma unroll
+    for (int i = 0; i < kMxQW; ++i) {
+        const int q = wave + kMW * i;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rec = q * NTT + (r < 2 ? 0 : up) + 2 * it.s + (r & 1);
+            ac[i][r] = buf_load16(it.sres, q < KQ ? a.gu_codes + rec * kRecBytes + 16 * lane : kOob);
+            as[i][r] = __builtin_amdgcn_raw_buffer_load_b8(it.sres, q < KQ ? a.gu_scales + rec * 64 + lane : kOob, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mx_stage_x(a, xv, xs, tid, lane, wave);
+    __syncthreads();
+
+    // ---- gate_up on the scaled matrix cores; a down group is issued after each chunk
+    const int row = it.tok >= 0 ? it.tok : T;
+    u32x4_t bc[kMxBW];
+    uint32_t bs[kMxBW];
+    f32x4_t acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int NSTEP = kMxQW > kMxBW ? kMxQW : kMxBW;
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+        const int q = wave + kMW * i;
+        if (i < kMxQW && q < KQ) {  // uniform per wave
+            v8i_t bh, bl;
+            int sh, sl;
+            mx_x_operand(xs, T, NB, row, q, g, bh, bl, sh, sl);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const u32x4_t cw = ac[i][r];
+                const v8i_t A = v8i_t{(int)cw.x, (int)cw.y, (int)cw.z, (int)cw.w, 0, 0, 0, 0};
+                const int sa = (int)as[i][r];
+                acc[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, bh, acc[r], 4, 0, 0, sa, 0, sh);
+                acc[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, bl, acc[r], 4, 0, 0, sa, 0, sl);
+            }
+        }
+        if (i < kMxBW) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int rg = wave + kMW * i;
+            const int rec = it.s * NG + rg;
+            bc[i] = buf_load16(it.sres, rg < NG ? a.dn_codes + rec * kRecBytes + 16 * lane : kOob);
+            bs[i] = buf_load4(it.sres, rg < NG ? a.dn_scales + rec * 64 + 4 * (lane & 15) : kOob);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+
+    // ---- SwiGLU for this lane's down operand: lane (c, g) needs slice rows 8 g + [0, 8) of token c, i.e. rows
+    // 8 (g & 1) + [0, 4) and + [4, 8) of tile g >> 1, held by lanes 32 (g & 1) + c and + 16 of each wave's sums
+    bf16x8_t Bh, Bl;
+    {
+        const int tt = g >> 1, L0 = 32 * (g & 1) + c;
+        f32x4_t gs0 = {0.0f, 0.0f, 0.0f, 0.0f}, gs1 = gs0, us0 = gs0, us1 = gs0;
+#pragma unroll
+        for (int w = 0; w < kMW; ++w) {
+            gs0 += red[w][tt][L0];
+            gs1 += red[w][tt][L0 + 16];
+            us0 += red[w][2 + tt][L0];
+            us1 += red[w][2 + tt][L0 + 16];
+        }
+        float h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float gv = e < 4 ? gs0[e] : gs1[e - 4], uv = e < 4 ? us0[e] : us1[e - 4];
+            h[e] = silu_fast(gv) * uv;
+        }
+        uint32_t bh[4], bl[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) split_bf16x2(h[2 * d], h[2 * d + 1], bh[d], bl[d]);
+        Bh = __builtin_bit_cast(bf16x8_t, u32x4_t{bh[0], bh[1], bh[2], bh[3]});
+        Bl = __builtin_bit_cast(bf16x8_t, u32x4_t{bl[0], bl[1], bl[2], bl[3]});
+    }
+
+    // ---- down: this wave's row groups of the slice's 32 columns, partial sums times the routing weight
+    const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
+    const int pbase = c < it.ne ? 4 * ((it.prow * nsl + it.s) * H + 4 * g) : kOob;
+#pragma unroll
+    for (int i = 0; i < kMxBW; ++i) {
+        const int rg = wave + kMW * i;
+        if (rg >= NG) break;  // uniform per wave
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8_t A = mx_down_frag(word_of(bc[i], j), bs[i], j);
+            f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bh, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl, D, 0, 0, 0);
+            buf_store16(pres, pbase + 4 * (64 * rg + 16 * j), D * it.wc);
+        }
+    }
+}
+
 hipError_t allow_mx_lds(const void* fn) {
     static std::mutex mu;
     static std::set<std::pair<const void*, int>> done;
@@ -497,12 +624,15 @@ hipError_t launch_mx_decode(const Layer& L, const uint16_t* x, int T, const floa
     if (e != hipSuccess) return e;
     if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<true>))) != hipSuccess) return e;
     if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<false>))) != hipSuccess) return e;
+    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_fused_kernel))) != hipSuccess) return e;
     const int nsl = I / 32;
     const int rows_max = (T * k < E ? T * k : E) + 1;
     const int items_max = rows_max * nsl;
     const int grid = items_max < ncu ? items_max : ncu;
     const size_t lds = mx_lds_bytes(T, H);
-    if (items_max > grid * kMW)
+    if (items_max <= ncu)  // one item per workgroup, shared by its waves
+        hipLaunchKernelGGL(mx_fused_kernel, dim3(items_max), dim3(kMT), lds, s, a, nsl);
+    else if (items_max > grid * kMW)
         hipLaunchKernelGGL(mx_wave_kernel<true>, dim3(grid), dim3(kMT), lds, s, a, nsl);
     else
         hipLaunchKernelGGL(mx_wave_kernel<false>, dim3(grid), dim3(kMT), lds, s, a, nsl);
