@@ -47,11 +47,11 @@ DTYPE_MX = "mxfp4w-fp8x2scaledmfma-bf16x2mfma-fp32acc"
 # kernels and scaled by what the same counters read for a plain copy of known size), with a digest of the kernel
 # sources they were taken on.  Reported as roofline.traffic only while those sources are unchanged.
 COUNTED_TRAFFIC = {
-    "decode_bs1": (29_486_866, "03924d89112af3c7"),
-    "decode_bs16": (318_848_908, "03924d89112af3c7"),
+    "decode_bs1": (29_536_890, "a0b07b34ca494660"),
+    "decode_bs16": (318_864_941, "a0b07b34ca494660"),
     "prefill_2048": (1_395_470_065, "c93bc6ebc63cd5e1"),
-    "mxfp4_decode_bs1": (27_945_329, "685d544185584219"),
-    "mxfp4_decode_bs16": (330_858_705, "685d544185584219"),
+    "mxfp4_decode_bs1": (27_708_588, "024edebb0eb4b6ea"),
+    "mxfp4_decode_bs16": (330_867_293, "024edebb0eb4b6ea"),
 }
 KERNEL_SOURCES = {"decode": ["decode.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],
                   "mxfp4": ["mxfp4.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],
