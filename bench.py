@@ -127,33 +127,29 @@ def run_gpu(inp, steps: int, warmup: int):
     logits = torch.from_numpy(np.ascontiguousarray(inp["logits"][:total])).to(dev)
     routes = [dl.Routing.empty(T, E, k, dev) for _ in range(total)]
     ws = dl.workspace(T, layers[0])
-    rf_bytes = _lib.moe_nvfp4_route_forward_workspace_bytes(T, H, I, E, k)
+    rf_bytes = (_lib.moe_mxfp4_route_forward_workspace_bytes if fmt == "mxfp4"
+                else _lib.moe_nvfp4_route_forward_workspace_bytes)(T, H, I, E, k)
     ws_rf = torch.empty(rf_bytes, dtype=torch.uint8, device=dev)
     y = torch.empty((total, T, H), dtype=torch.float32, device=dev)
     rws = _lib.moe_route_workspace_bytes(T, E, k)
     rws_t = torch.empty(max(1, rws), dtype=torch.uint8, device=dev)
 
     def step(s: int, do_route: bool = True, do_forward: bool = True):
-        """A step is one moe_nvfp4_route_forward call (MXFP4: moe_route_topk then moe_mxfp4_forward);
-        do_route / do_forward select the separate calls."""
+        """A step is one moe_nvfp4_route_forward call (MXFP4: moe_mxfp4_route_forward); do_route / do_forward
+        select the separate calls (moe_route_topk, moe_nvfp4_forward / moe_mxfp4_forward)."""
         r = routes[s]
-        if fmt == "mxfp4":
-            if do_route:
-                _lib.check(_lib.moe_route_topk(logits[s], T, E, k, r.ids, r.w, r.offsets, r.sorted_assign,
-                                               r.assign_pos, rws_t, rws, None))
-            if do_forward:
-                _lib.check(_lib.moe_mxfp4_forward(structs[s % R], xs[s], T, r.ids, r.w, r.offsets, r.sorted_assign,
-                                                  r.assign_pos, y[s], 0, ws, ws.numel(), None))
-            return
+        mx = fmt == "mxfp4"
         if do_route and do_forward:
-            _lib.check(_lib.moe_nvfp4_route_forward(structs[s % R], logits[s], xs[s], T, r.ids, r.w, r.offsets,
-                                                    r.sorted_assign, r.assign_pos, y[s], 0, ws_rf, rf_bytes, None))
+            f = _lib.moe_mxfp4_route_forward if mx else _lib.moe_nvfp4_route_forward
+            _lib.check(f(structs[s % R], logits[s], xs[s], T, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos,
+                         y[s], 0, ws_rf, rf_bytes, None))
         elif do_route:
             _lib.check(_lib.moe_route_topk(logits[s], T, E, k, r.ids, r.w, r.offsets, r.sorted_assign,
                                            r.assign_pos, rws_t, rws, None))
         else:
-            _lib.check(_lib.moe_nvfp4_forward(structs[s % R], xs[s], T, r.ids, r.w, r.offsets, r.sorted_assign,
-                                              r.assign_pos, y[s], 0, ws, ws.numel(), None))
+            f = _lib.moe_mxfp4_forward if mx else _lib.moe_nvfp4_forward
+            _lib.check(f(structs[s % R], xs[s], T, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y[s], 0,
+                         ws, ws.numel(), None))
 
     # eager warm-up, then an eager reference of the last timed step
     for s in range(warmup):
@@ -551,9 +547,9 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     mean_d = float(np.mean(res["distinct"]))
     bytes_fwd = (mean_d + 1) * sb                       # touched expert slots incl. the shared expert
     prefill = T > 16
-    # roofline unit: NVFP4 decode routes inside its first kernel, so the unit is the step's route_forward call;
-    # prefill and MXFP4 decode route in kernels of their own, so the unit is the forward call
-    fwd_s = (res["fwd_ms"] if prefill or mx else res["call_ms"]) * 1e-3
+    # roofline unit: a decode step is one route_forward call (up to 8 tokens its first kernel routes in its
+    # prologue), so that call is the unit; prefill routes in kernels of its own, so its unit is the forward call
+    fwd_s = (res["fwd_ms"] if prefill else res["call_ms"]) * 1e-3
     gbs = bytes_fwd / fwd_s / 1e9
     flops = synth.prefill_flops(T, H, I, k)
     if prefill:
@@ -566,9 +562,9 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     elif mx:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic(name, "mxfp4"),
-                "kernel": "moe_mxfp4_forward decode call (mx_wave_kernel: gate_up on "
-                          "v_mfma_scale_f32_16x16x128_f8f6f4, down on v_mfma_f32_16x16x32_bf16; then "
-                          "dcombine_kernel), timed together with HIP events",
+                "kernel": "moe_mxfp4_route_forward decode call (mx_fused_kernel or mx_wave_kernel, routing in "
+                          "the prologue up to 8 tokens: gate_up on v_mfma_scale_f32_16x16x128_f8f6f4, down on "
+                          "v_mfma_f32_16x16x32_bf16; then dcombine_kernel), timed together with HIP events",
                 "per_launch": f"{bytes_fwd / 1e6:.2f} MB expert weights per forward ((D+1) x {sb} B, "
                               f"mean D = {mean_d:.2f})"}
     else:

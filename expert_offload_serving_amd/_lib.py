@@ -26,7 +26,8 @@ EXPORTED = [
     "moe_cache_destroy", "moe_cache_plan", "moe_nvfp4_slice_bank", "moe_nvfp4_dequant", "moe_nvfp4_dequant_slot",
     "moe_nvfp4_route_forward_workspace_bytes", "moe_nvfp4_route_forward", "moe_router_logits", "moe_router_topk",
     "moe_release_streams", "moe_nvfp4_noalloc_scratch_bytes", "moe_nvfp4_route_forward_noalloc",
-    "moe_mxfp4_slot_bytes", "moe_mxfp4_forward_workspace_bytes", "moe_mxfp4_forward", "moe_mxfp4_dequant",
+    "moe_mxfp4_slot_bytes", "moe_mxfp4_forward_workspace_bytes", "moe_mxfp4_forward",
+    "moe_mxfp4_route_forward_workspace_bytes", "moe_mxfp4_route_forward", "moe_mxfp4_dequant",
     "moe_mxfp4_dequant_slot", "moe_mxfp4_slice_bank", "moe_offload_device_bytes", "moe_offload_create",
     "moe_offload_destroy", "moe_offload_layer",
 ]
@@ -107,6 +108,11 @@ def lib() -> ctypes.CDLL:
         L.moe_mxfp4_forward.restype = _i
         L.moe_mxfp4_forward.argtypes = [ctypes.POINTER(LayerStruct), _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                                         _vp, _sz, _vp]
+        L.moe_mxfp4_route_forward_workspace_bytes.restype = _sz
+        L.moe_mxfp4_route_forward_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+        L.moe_mxfp4_route_forward.restype = _i
+        L.moe_mxfp4_route_forward.argtypes = [ctypes.POINTER(LayerStruct), _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp,
+                                              _vp, _i, _vp, _sz, _vp]
         L.moe_mxfp4_dequant.restype = _i
         L.moe_mxfp4_dequant.argtypes = [_vp, _vp, _i, _i, _vp, _vp]
         L.moe_mxfp4_dequant_slot.restype = _i
@@ -230,6 +236,17 @@ def moe_mxfp4_forward(layer: LayerStruct, x, T, topk_ids, topk_w, expert_offsets
     return lib().moe_mxfp4_forward(ctypes.byref(layer), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w),
                                    _ptr(expert_offsets), _ptr(sorted_assign), _ptr(assign_pos), _ptr(y),
                                    int(accumulate), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_mxfp4_route_forward_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(lib().moe_mxfp4_route_forward_workspace_bytes(T, H, I, E, k))
+
+
+def moe_mxfp4_route_forward(layer: LayerStruct, logits, x, T, topk_ids, topk_w, expert_offsets, sorted_assign,
+                            assign_pos, y, accumulate, ws, ws_bytes, stream=None) -> int:
+    return lib().moe_mxfp4_route_forward(ctypes.byref(layer), _ptr(logits), _ptr(x), T, _ptr(topk_ids),
+                                         _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_assign), _ptr(assign_pos),
+                                         _ptr(y), int(accumulate), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def moe_mxfp4_dequant(blocks_t, scales_t, N, K, out, stream=None) -> int:

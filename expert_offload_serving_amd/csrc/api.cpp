@@ -442,6 +442,45 @@ int moe_mxfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, 
     return MOE_OK;
 }
 
+size_t moe_mxfp4_route_forward_workspace_bytes(int T, int H, int I, int E, int k) {
+    const size_t f = moe_mxfp4_forward_workspace_bytes(T, H, I, E, k);
+    if (f == 0) return 0;
+    return moe::align256(f) + moe::route_ws_bytes(T, E, k);
+}
+
+int moe_mxfp4_route_forward(const moe_nvfp4_layer_t* layer, const float* logits, const uint16_t* x, int T,
+                            int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_assign,
+                            int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    if (!layer) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_mxfp4_route_forward: layer is NULL");
+    const moe_nvfp4_layer_t& L = *layer;
+    int rc = check_route_shape(T, L.E, L.k);
+    if (rc != MOE_OK) return rc;
+    // every check of the forward, against its share of the workspace (the routing's follows it)
+    const size_t f = moe::forward_ws_bytes(T, L.H, L.I, L.E, L.k);
+    const size_t fws = moe::align256(f);
+    rc = validate_mx_forward(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y, accumulate,
+                             ws, ws_bytes < fws ? ws_bytes : fws);
+    if (rc != MOE_OK || T == 0) return rc;
+    if (!logits) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_mxfp4_route_forward: logits is NULL");
+    const size_t need = fws + moe::route_ws_bytes(T, L.E, L.k);
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "route_forward workspace %zu < %zu bytes", ws_bytes, need);
+    const moe::Layer ml = layer_of(L);
+    hipError_t e;
+    if (moe::decode_routes_in_kernel(T, L.E)) {
+        const moe::RouteOut ro{logits, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos};
+        e = moe::launch_mx_decode(ml, x, T, topk_w, expert_offsets, sorted_assign, y, accumulate, ws, stream, &ro);
+    } else {
+        e = moe::launch_route(logits, T, L.E, L.k, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos,
+                              static_cast<uint8_t*>(ws) + fws, stream);
+        if (e == hipSuccess)
+            e = moe::launch_mx_decode(ml, x, T, topk_w, expert_offsets, sorted_assign, y, accumulate, ws, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "moe_mxfp4_route_forward launch");
+    return MOE_OK;
+}
+
 int moe_mxfp4_dequant(const uint8_t* blocks_t, const uint8_t* scales_t, int N, int K, float* out,
                       hipStream_t stream) {
     if (N < 0 || K <= 0 || K % 32 != 0)

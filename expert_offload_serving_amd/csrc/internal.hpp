@@ -125,8 +125,10 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
 // dequant hooks (checkpoint-transposed matrix; one matrix of a slot through the forward's own decode).
 SlotGeom mx_slot_geom(int H, int I);
 bool mx_decode_shape_supported(int H, int I);
+// route == nullptr: the routing tensors are inputs; otherwise the kernels route from route->logits.
 hipError_t launch_mx_decode(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* offsets,
-                            const int32_t* sorted_assign, float* y, int accumulate, void* ws, hipStream_t s);
+                            const int32_t* sorted_assign, float* y, int accumulate, void* ws, hipStream_t s,
+                            const RouteOut* route = nullptr);
 hipError_t launch_mx_dequant_t(const uint8_t* blocks_t, const uint8_t* scales_t, int N, int K, float* out,
                                hipStream_t s);
 hipError_t launch_mx_dequant_slot(const uint8_t* slot, int H, int I, int matrix, float* out, hipStream_t s);

@@ -261,14 +261,16 @@ __device__ __forceinline__ void mx_compute_b(const DecArgs& a, const MxRing& R, 
 }
 
 // Persistent over items v = wave * grid + block + j * 8 * grid.  MULTI: some wave has more than one item.
-template <bool MULTI>
+// ROUTE: the kernel routes the tokens itself in its prologue (from a.logits) and writes the routing outputs.
+template <bool MULTI, bool ROUTE>
 __global__ void __launch_bounds__(kMT) mx_wave_kernel(DecArgs a, int nsl) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
     __shared__ Tables tb;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int H = a.H, T = a.T, k = a.k;
     XRegs<kMW> xv;
-    const int n_act = stage_tables<kMW>(a, tb, xv, tid, lane, wave);
+    const int n_act = ROUTE ? stage_route<kMW>(a, tb, xv, tid, lane, wave, [] {})
+                            : stage_tables<kMW>(a, tb, xv, tid, lane, wave);
     const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
     const int stride = (int)gridDim.x * kMW;
     int v = __builtin_amdgcn_readfirstlane(wave * (int)gridDim.x + (int)blockIdx.x);
@@ -453,6 +455,7 @@ __global__ void __launch_bounds__(256) mx_dequant_dn_kernel(const uint8_t* __res
 constexpr int kMxQW = 3;  // most gate_up chunks per wave (H <= 2560: 20 chunks over 8 waves)
 constexpr int kMxBW = 5;  // most down groups per wave (H <= 2560: 40 groups over 8 waves)
 
+template <bool ROUTE>
 __global__ void __launch_bounds__(kMT) mx_fused_kernel(DecArgs a, int nsl) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
     __shared__ Tables tb;
@@ -462,7 +465,8 @@ __global__ void __launch_bounds__(kMT) mx_fused_kernel(DecArgs a, int nsl) {
     const int c = lane & 15, g = lane >> 4;
     const int KQ = H / 128, NG = H / 64, NB = H / 32;
     XRegs<kMW> xv;
-    const int n_act = stage_tables<kMW>(a, tb, xv, tid, lane, wave);
+    const int n_act = ROUTE ? stage_route<kMW>(a, tb, xv, tid, lane, wave, [] {})
+                            : stage_tables<kMW>(a, tb, xv, tid, lane, wave);
     const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
     if ((int)blockIdx.x >= n_items) return;  // uniform
     const Item it = decode_item(a, tb, n_act, nsl, (int)blockIdx.x, true, c);
@@ -599,8 +603,27 @@ hipError_t mx_device_cus(int& ncu) {
 
 bool mx_decode_shape_supported(int H, int I) { return H % 128 == 0 && I % 32 == 0 && H <= 2560; }
 
+namespace {
+template <bool ROUTE>
+hipError_t launch_mx_kernels(const DecArgs& a, int items_max, int nsl, int ncu, size_t lds, hipStream_t s) {
+    hipError_t e;
+    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<true, ROUTE>))) != hipSuccess) return e;
+    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<false, ROUTE>))) != hipSuccess) return e;
+    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_fused_kernel<ROUTE>))) != hipSuccess) return e;
+    const int grid = items_max < ncu ? items_max : ncu;
+    if (items_max <= ncu)  // one item per workgroup, shared by its waves
+        hipLaunchKernelGGL(mx_fused_kernel<ROUTE>, dim3(items_max), dim3(kMT), lds, s, a, nsl);
+    else if (items_max > grid * kMW)
+        hipLaunchKernelGGL((mx_wave_kernel<true, ROUTE>), dim3(grid), dim3(kMT), lds, s, a, nsl);
+    else
+        hipLaunchKernelGGL((mx_wave_kernel<false, ROUTE>), dim3(grid), dim3(kMT), lds, s, a, nsl);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_mx_decode(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* offsets,
-                            const int32_t* sorted_assign, float* y, int accumulate, void* ws, hipStream_t s) {
+                            const int32_t* sorted_assign, float* y, int accumulate, void* ws, hipStream_t s,
+                            const RouteOut* route) {
     const int H = L.H, I = L.I, E = L.E, k = L.k;
     const WsLayout wl = ws_layout(T, H, I, E, k);
     DecArgs a{};
@@ -617,26 +640,23 @@ hipError_t launch_mx_decode(const Layer& L, const uint16_t* x, int T, const floa
     a.gu_codes = (int)gm.gu_codes; a.gu_scales = (int)gm.gu_scales; a.gu_glob = 0;
     a.dn_codes = (int)gm.dn_codes; a.dn_scales = (int)gm.dn_scales; a.dn_glob = 0;
     a.no_glob = 1;
-    a.route_wg = 0;
-    a.logits = nullptr;
+    a.route_wg = 0;  // workgroup 0 writes the routing outputs when the kernels route
+    a.logits = route ? route->logits : nullptr;
+    a.r_ids = route ? route->ids : nullptr;
+    a.r_w = route ? route->w : nullptr;
+    a.r_offsets = route ? route->offsets : nullptr;
+    a.r_sorted = route ? route->sorted_assign : nullptr;
+    a.r_pos = route ? route->assign_pos : nullptr;
     int ncu = 0;
     hipError_t e = mx_device_cus(ncu);
     if (e != hipSuccess) return e;
-    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<true>))) != hipSuccess) return e;
-    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<false>))) != hipSuccess) return e;
-    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_fused_kernel))) != hipSuccess) return e;
     const int nsl = I / 32;
     const int rows_max = (T * k < E ? T * k : E) + 1;
     const int items_max = rows_max * nsl;
-    const int grid = items_max < ncu ? items_max : ncu;
     const size_t lds = mx_lds_bytes(T, H);
-    if (items_max <= ncu)  // one item per workgroup, shared by its waves
-        hipLaunchKernelGGL(mx_fused_kernel, dim3(items_max), dim3(kMT), lds, s, a, nsl);
-    else if (items_max > grid * kMW)
-        hipLaunchKernelGGL(mx_wave_kernel<true>, dim3(grid), dim3(kMT), lds, s, a, nsl);
-    else
-        hipLaunchKernelGGL(mx_wave_kernel<false>, dim3(grid), dim3(kMT), lds, s, a, nsl);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = route ? launch_mx_kernels<true>(a, items_max, nsl, ncu, lds, s)
+              : launch_mx_kernels<false>(a, items_max, nsl, ncu, lds, s);
+    if (e != hipSuccess) return e;
     const int nch = H / 64;
     if (nsl <= 10) hipLaunchKernelGGL(dcombine_kernel<10>, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);
     else if (nsl <= 20) hipLaunchKernelGGL(dcombine_kernel<20>, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);

@@ -141,12 +141,15 @@ def route_forward(layer: DeviceLayer, logits: torch.Tensor, x: torch.Tensor, y: 
     r = Routing.empty(T, E, layer.k, x.device) if out is None else out
     if y is None:
         y = torch.empty((T, layer.H), dtype=torch.float32, device=x.device)
+    mx = layer.fmt == "mxfp4"
     if ws is None:
-        nb = _lib.moe_nvfp4_route_forward_workspace_bytes(T, layer.H, layer.I, layer.E, layer.k)
+        f = _lib.moe_mxfp4_route_forward_workspace_bytes if mx else _lib.moe_nvfp4_route_forward_workspace_bytes
+        nb = f(T, layer.H, layer.I, layer.E, layer.k)
         ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=x.device)
     st = layer.struct(slot_of_expert, shared)
-    check(_lib.moe_nvfp4_route_forward(st, logits, x, T, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y,
-                                       int(accumulate), ws, ws.numel(), stream))
+    f = _lib.moe_mxfp4_route_forward if mx else _lib.moe_nvfp4_route_forward
+    check(f(st, logits, x, T, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y, int(accumulate), ws,
+            ws.numel(), stream))
     return y, r
 
 

@@ -349,6 +349,21 @@ int moe_mxfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, 
                       const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
                       hipStream_t stream);
 
+/* Workspace moe_mxfp4_route_forward needs for T tokens; 0 for shapes it does not take. */
+size_t moe_mxfp4_route_forward_workspace_bytes(int T, int H, int I, int E, int k);
+
+/* moe_route_topk followed by moe_mxfp4_forward in one call, with the same
+ * results and the same contract as moe_nvfp4_route_forward (routing outputs
+ * written, y the layer output for the routing of `logits`, device f32
+ * [T, E]).  With T <= 8 and E <= 256 the forward's kernel routes by itself in
+ * its prologue; otherwise the routing is its own launch on `stream`, its
+ * workspace after the forward's.  Every argument is checked before anything
+ * is enqueued. */
+int moe_mxfp4_route_forward(const moe_nvfp4_layer_t* layer, const float* logits, const uint16_t* x, int T,
+                            int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_assign,
+                            int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* MXFP4 decode of one matrix in the checkpoints' transposed layout:
  *   blocks_t  device u8 [K/2, N]: byte (j, n) = W[n, 2j] (low nibble), W[n, 2j+1]
  *   scales_t  device u8 [K/32, N]: E8M0 of (n, block)

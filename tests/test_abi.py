@@ -99,6 +99,23 @@ def test_route_forward_validation_without_gpu():
     assert f(_layer(), T=0) == _lib.MOE_OK
 
 
+def test_mx_route_forward_validation_without_gpu():
+    d = 0x3000
+    mx = _lib.moe_mxfp4_slot_bytes(2560, 640)
+    f = lambda L, lg=d, T=1, ws=0x200000, nb=1 << 30: _lib.moe_mxfp4_route_forward(L, lg, d, T, d, d, d, d, d, d, 0,
+                                                                                  ws, nb, 0)
+    assert f(_layer(slot_bytes=mx), lg=None) == _lib.MOE_ERR_INVALID_ARGUMENT
+    assert "logits" in _lib.last_error()
+    assert f(_layer()) == _lib.MOE_ERR_INVALID_ARGUMENT  # an NVFP4 slot size
+    assert f(_layer(slot_bytes=mx), T=17) == _lib.MOE_ERR_UNSUPPORTED_SHAPE  # decode path only
+    need = _lib.moe_mxfp4_route_forward_workspace_bytes(16, 2560, 640, 256, 8)
+    assert need >= _lib.moe_mxfp4_forward_workspace_bytes(16, 2560, 640, 256, 8) + \
+        _lib.moe_route_workspace_bytes(16, 256, 8)
+    assert f(_layer(slot_bytes=mx), T=16, nb=need - 1) == _lib.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert _lib.moe_mxfp4_route_forward_workspace_bytes(17, 2560, 640, 256, 8) == 0
+    assert f(_layer(slot_bytes=mx), T=0) == _lib.MOE_OK
+
+
 def test_forward_refuses_buffers_of_2gib():
     """Every buffer the kernels address through 32-bit offsets must stay below 2 GiB: shapes whose workspace or
     output would reach it are refused before anything is enqueued (no GPU needed)."""

@@ -148,6 +148,37 @@ def test_mx_forward_full_shape_distinct_permuted(mx_layer, T):
     print(f"mx T={T} rel L2 {rel:.2e}")
 
 
+@pytest.mark.parametrize("T", [1, 3, 8, 12])
+def test_mx_route_forward_matches_route_then_forward(mx_layer, T):
+    """moe_mxfp4_route_forward against moe_route_topk + moe_mxfp4_forward on the same inputs: routing outputs bit
+    for bit and y bit for bit (T <= 8 routes inside the forward's kernel, T = 12 in its own launch), y against the
+    oracle; then run again with the shared expert left out and accumulating into y."""
+    xb, lg = synth.fresh_tokens(1500 + T, T, mx_layer.H, mx_layer.E, "uniform")
+    L = synth.LayerInputs(mx_layer.H, mx_layer.I, mx_layer.E, mx_layer.k, T, mx_layer.bank, mx_layer.slot_of_expert,
+                          mx_layer.shared_slot, mx_layer.wg, xb, lg)
+    _announce(f"mxfp4 route_forward T={T}")
+    dev = device_layer(L, "mxfp4")
+    x, lgd = device_x(L), device_logits(L)
+    r_sep = dl.route(lgd, L.k)
+    y_sep = dl.forward(dev, x, r_sep)
+    y_one, r_one = dl.route_forward(dev, lgd, x)
+    torch.cuda.synchronize()
+    for name in ("ids", "w", "offsets", "sorted_assign", "assign_pos"):
+        a, b = getattr(r_sep, name).cpu().numpy(), getattr(r_one, name).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"T={T}: routing output {name} differs"
+    assert np.array_equal(y_sep.cpu().numpy().view(np.uint32), y_one.cpu().numpy().view(np.uint32)), f"T={T}"
+    ids, w = oracle.route(L.logits, L.k)
+    ref = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w,
+                         nthreads=NTHREADS, fmt="mxfp4")
+    assert_close(y_one.cpu().numpy(), ref, f"mx route_forward T={T}")
+    y0 = torch.from_numpy(np.random.default_rng(T).standard_normal((T, L.H)).astype(np.float32)).cuda()
+    y_acc, _ = dl.route_forward(dev, lgd, x, y=y0.clone(), accumulate=True, shared=False)
+    torch.cuda.synchronize()
+    ref_ns = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, -1, L.wg, L.x, ids, w,
+                            nthreads=NTHREADS, fmt="mxfp4")
+    assert_close(y_acc.cpu().numpy(), ref_ns + y0.cpu().numpy(), f"mx route_forward accumulate T={T}")
+
+
 def test_mx_forward_refuses_prefill_and_wrong_slot_size(mx_layer):
     L = mx_layer
     dev = device_layer(L, "mxfp4")
