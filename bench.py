@@ -50,8 +50,8 @@ COUNTED_TRAFFIC = {
     "decode_bs1": (29_536_890, "a0b07b34ca494660"),
     "decode_bs16": (318_864_941, "a0b07b34ca494660"),
     "prefill_2048": (1_395_470_065, "c93bc6ebc63cd5e1"),
-    "mxfp4_decode_bs1": (27_708_588, "024edebb0eb4b6ea"),
-    "mxfp4_decode_bs16": (330_867_293, "024edebb0eb4b6ea"),
+    "mxfp4_decode_bs1": (27_783_258, "bd608b08969f1eef"),
+    "mxfp4_decode_bs16": (330_865_370, "bd608b08969f1eef"),
 }
 KERNEL_SOURCES = {"decode": ["decode.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],
                   "mxfp4": ["mxfp4.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],
