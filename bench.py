@@ -659,7 +659,7 @@ def bench_router(name: str, steps: int, warmup: int, replicas: int) -> dict:
         gbs = (wbytes + T * H * 2 + T * E * 4) / (us_logits * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "router_logits_kernel<1, 1> (moe_router_logits), HIP events around a graph of calls",
+                "kernel": f"router_gemv_kernel<2, {1 if T == 1 else (2 if T == 2 else 4)}> (moe_router_logits), HIP events around a graph of calls",
                 "per_launch": f"{(wbytes + T * H * 2 + T * E * 4) / 1e6:.3f} MB (router weights, x, logits)"}
     else:
         tf = flops / (us_logits * 1e-6) / 1e12

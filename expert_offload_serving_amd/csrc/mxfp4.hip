@@ -109,8 +109,7 @@ __device__ __forceinline__ void mx_stage_x(const DecArgs& a, const XRegs<kMW>& x
             float am = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
-            am = fmaxf(am, __shfl_xor(am, 1, kWave));
-            am = fmaxf(am, __shfl_xor(am, 2, kWave));
+            am = quad_max(am);
             const int bh = mx_block_exp(am);
             const float inv_h = ldexpf(1.0f, 127 - bh);
             float r[8];
@@ -131,8 +130,7 @@ __device__ __forceinline__ void mx_stage_x(const DecArgs& a, const XRegs<kMW>& x
             float ar = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ar = fmaxf(ar, fabsf(r[e]));
-            ar = fmaxf(ar, __shfl_xor(ar, 1, kWave));
-            ar = fmaxf(ar, __shfl_xor(ar, 2, kWave));
+            ar = quad_max(ar);
             const int bl_rel = mx_block_exp(ar);  // exponent of the residual in units of 2^(bh - 127)
             int bl = bl_rel - 127 + bh;           // as an absolute E8M0 byte
             const bool lo_zero = ar == 0.0f || bl < 0;

@@ -132,21 +132,53 @@ __device__ __forceinline__ float block16_dot_bf16(uint32_t w0, uint32_t w1, cons
     return p;
 }
 
-// Sum over groups of G consecutive lanes (G a power of two <= 64); every lane
-// of a group ends with the group's total.
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+// Wave-wide reductions by DPP moves (VALU only, no LDS round trips), in a
+// fixed order: lane pairs (xor 1), pairs of pairs (xor 2), the two quads of
+// each 8-lane half-row, the two halves of each 16-lane row, then row 0 into
+// row 1 and row 2 into row 3, and rows 0+1 into row 3; the result is lane
+// 63's, returned to every lane.  Lanes a step does not write keep their value
+// (sum: plus 0; max: their own), which only rows 0-2 see.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float add_dpp(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float max_dpp(float v) {
+    const int b = __float_as_int(v);
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, CTRL, ROW_MASK, 0xF, false)));
 }
 
-__device__ __forceinline__ float wave_sum(float v) { return group_sum<kWave>(v); }
+// Maximum over each aligned group of 4 lanes, returned to every lane of it.
+__device__ __forceinline__ float quad_max(float v) {
+    v = max_dpp<0xB1, 0xF>(v);  // quad_perm [1, 0, 3, 2]
+    return max_dpp<0x4E, 0xF>(v);  // quad_perm [2, 3, 0, 1]
+}
+
+// Maximum over each 16-lane row, returned to every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+    v = quad_max(v);
+    v = max_dpp<0x141, 0xF>(v);  // row_half_mirror
+    return max_dpp<0x140, 0xF>(v);  // row_mirror
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = add_dpp<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+    v = add_dpp<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+    v = add_dpp<0x141, 0xF>(v);  // row_half_mirror
+    v = add_dpp<0x140, 0xF>(v);  // row_mirror
+    v = add_dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = add_dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
+    v = max_dpp<0xB1, 0xF>(v);
+    v = max_dpp<0x4E, 0xF>(v);
+    v = max_dpp<0x141, 0xF>(v);
+    v = max_dpp<0x140, 0xF>(v);
+    v = max_dpp<0x142, 0xA>(v);
+    v = max_dpp<0x143, 0xC>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Opaque to the optimiser: keeps code words from being decoded once and held

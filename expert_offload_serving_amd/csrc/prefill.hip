@@ -123,11 +123,8 @@ __device__ __forceinline__ void prep_token(const PrefillArgs& a, int t, float (&
             dot = dot2_bf16(as_bf16x2(ws[m]), as_bf16x2(gs[m]), dot);
         }
     }
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-        dot += __shfl_xor(dot, off, kWave);
-    }
+    amax = wave_max(amax);
+    dot = wave_sum(dot);
     if (lane == 0) red[0][wave] = amax, red[1][wave] = dot;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
@@ -502,11 +499,7 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float v = rmax[i][r];
-                v = fmaxf(v, __shfl_xor(v, 1, kWave));
-                v = fmaxf(v, __shfl_xor(v, 2, kWave));
-                v = fmaxf(v, __shfl_xor(v, 4, kWave));
-                v = fmaxf(v, __shfl_xor(v, 8, kWave));
+                const float v = row16_max(rmax[i][r]);
                 if (l16 == 0) smax[wn][16 * MI * wm + 16 * i + 4 * q4 + r] = v;
             }
         __syncthreads();

@@ -3,18 +3,18 @@
 // router is replicated and its logits feed the top-k of route.hip (issue #62,
 // R9700 interim report: norm_topk_prob over a replicated router).
 //
-// The product is a dense contraction, so it runs on v_mfma_f32_16x16x32_bf16
-// (bf16 x bf16 products are exact in fp32; fp32 accumulation).  A workgroup
-// owns a tile of 16*MI tokens x 16*NJ experts; its 8 waves split H into 8
-// equal ranges and each wave streams its range with 16-byte buffer loads
-// straight into MFMA operands (lane (row i, group g) takes columns
-// [8g, 8g+8) of each 32-column chunk, the same for both operands).  The 8
-// partial tiles meet in LDS and are added in wave order, so the result does
-// not depend on timing.  Rows past T or E read zeros and are not written.
-//   decode (T <= 16): MI = NJ = 1, one workgroup per 16 experts: the weights
-//                     are the traffic (E*H*2 bytes), streamed by E/16 CUs.
-//   larger T:         MI = 2, NJ = 4 (32 tokens x 64 experts per workgroup),
-//                     loads in two groups of five 32-column chunks.
+// With more than 16 tokens the product is a dense contraction, so it runs on
+// v_mfma_f32_16x16x32_bf16 (bf16 x bf16 products are exact in fp32; fp32
+// accumulation).  A workgroup owns a tile of 32 tokens x 64 experts; its 8
+// waves split H into 8 equal ranges and each wave streams its range with
+// 16-byte buffer loads straight into MFMA operands (lane (row i, group g)
+// takes columns [8g, 8g+8) of each 32-column chunk, the same for both
+// operands), in two groups of five 32-column chunks.  The 8 partial tiles
+// meet in LDS and are added in wave order, so the result does not depend on
+// timing.  Rows past T or E read zeros and are not written.
+// Decode batches (T <= 16) take the vector path below instead: the weights
+// are the traffic (E*H*2 bytes), so one workgroup per expert row spreads them
+// over E CUs (a 16-expert matrix tile would leave all but E/16 CUs idle).
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -99,6 +99,76 @@ __global__ void __launch_bounds__(kRW * kWave) router_logits_kernel(const uint16
     }
 }
 
+// Decode batches: one 256-thread workgroup per expert e.  Thread j takes the
+// 16-byte chunks j, j + 256, ... of row e of W_r and of each token row of x
+// (those rows are few and stay in L2 for every workgroup).  bf16 pairs are
+// multiplied exactly and accumulated in fp32 (v_dot2_f32_bf16) in a fixed
+// order: per thread over its chunks in order, then over the wave's lanes
+// (wave_sum), then the four waves in order, so repeated calls give identical bits.
+// C: chunks per thread (H <= 2048 C); TG: tokens per pass.
+template <int C, int TG>
+__global__ void __launch_bounds__(256) router_gemv_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr, int T, int H, int E,
+                                                          float* __restrict__ logits) {
+    __shared__ float red[4][TG];
+    const int e = (int)blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int nch = H / 8;  // 16-byte chunks per row
+    const rsrc_t xres = make_rsrc(x, (uint32_t)((size_t)T * H * 2));
+    const rsrc_t wres = make_rsrc(wr, (uint32_t)((size_t)E * H * 2));
+    u32x4_t wv[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int ch = tid + 256 * c;
+        wv[c] = buf_load16(wres, ch < nch ? 2 * (e * H + 8 * ch) : kOob);
+    }
+    // workgroup e visits the tokens of a pass starting at e mod TG, so the workgroups' first loads spread over
+    // TG different rows of x instead of all asking L2 for the same lines at once
+    const int rot = e % TG;
+    for (int t0 = 0; t0 < T; t0 += TG) {
+        u32x4_t xv[TG][C];
+#pragma unroll
+        for (int q = 0; q < TG; ++q)
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const int t = t0 + (q + rot) % TG, ch = tid + 256 * c;
+                xv[q][c] = buf_load16(xres, t < T && ch < nch ? 2 * (t * H + 8 * ch) : kOob);
+            }
+#pragma unroll
+        for (int q = 0; q < TG; ++q) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) acc = dot2_bf16(as_bf16x2(word_of(xv[q][c], d)), as_bf16x2(word_of(wv[c], d)), acc);
+            acc = wave_sum(acc);
+            if (lane == 0) red[wave][(q + rot) % TG] = acc;
+        }
+        __syncthreads();
+        if (tid < TG && t0 + tid < T)
+            logits[(size_t)(t0 + tid) * E + e] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+        __syncthreads();
+    }
+}
+
+template <int C>
+hipError_t launch_router_gemv(const uint16_t* x, const uint16_t* wr, int T, int H, int E, float* logits,
+                              hipStream_t s) {
+    // as many tokens per pass as the registers allow (TG * C 16-byte chunks per thread, at most 64), so a
+    // batch of up to 16 tokens is one round trip to L2 for x
+    constexpr int kMaxTG = 64 / C < 16 ? 64 / C : 16;
+    if (T == 1)
+        hipLaunchKernelGGL((router_gemv_kernel<C, 1>), dim3(E), dim3(256), 0, s, x, wr, T, H, E, logits);
+    else if (T == 2)
+        hipLaunchKernelGGL((router_gemv_kernel<C, 2>), dim3(E), dim3(256), 0, s, x, wr, T, H, E, logits);
+    else if (T <= 4)
+        hipLaunchKernelGGL((router_gemv_kernel<C, 4>), dim3(E), dim3(256), 0, s, x, wr, T, H, E, logits);
+    else if (T <= 8 || kMaxTG < 16)
+        hipLaunchKernelGGL((router_gemv_kernel<C, 8>), dim3(E), dim3(256), 0, s, x, wr, T, H, E, logits);
+    else
+        hipLaunchKernelGGL((router_gemv_kernel<C, kMaxTG>), dim3(E), dim3(256), 0, s, x, wr, T, H, E, logits);
+    return hipGetLastError();
+}
+
 template <int MI, int NJ>
 hipError_t launch_router_cfg(const uint16_t* x, const uint16_t* wr, int T, int H, int E, float* logits,
                              hipStream_t s) {
@@ -117,7 +187,13 @@ bool router_shape_supported(int T, int H, int E) {
 }
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, int T, int H, int E, float* logits, hipStream_t s) {
-    if (T <= 16) return launch_router_cfg<1, 1>(x, wr, T, H, E, logits, s);
+    if (T <= 16) {
+        const int c = ceil_div(H / 8, 256);  // chunks per thread; H <= 16384 gives c <= 8
+        if (c <= 1) return launch_router_gemv<1>(x, wr, T, H, E, logits, s);
+        if (c <= 2) return launch_router_gemv<2>(x, wr, T, H, E, logits, s);
+        if (c <= 4) return launch_router_gemv<4>(x, wr, T, H, E, logits, s);
+        return launch_router_gemv<8>(x, wr, T, H, E, logits, s);
+    }
     return launch_router_cfg<2, 4>(x, wr, T, H, E, logits, s);
 }
 

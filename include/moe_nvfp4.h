@@ -108,8 +108,9 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, 
  *   x          device bf16 [T, H] activations (row-major)
  *   w_router   device bf16 [E, H] router weights (row-major, one row per expert)
  *   logits     device f32 [T, E] out
- * bf16 products are exact in fp32; the sum is accumulated in fp32 on the
- * matrix cores in a fixed order, so repeated calls give identical bits.
+ * bf16 products are exact in fp32; the sum is accumulated in fp32 in a fixed
+ * order (T <= 16: vector dot products, one workgroup per expert row; larger
+ * T: the matrix cores), so repeated calls give identical bits.
  * Shapes: T >= 0 (0 is a no-op), 1 <= E <= 1024, H % 256 == 0, H <= 16384,
  * T*H*2 and E*H*2 below 2^31 bytes; others return MOE_ERR_UNSUPPORTED_SHAPE
  * with nothing enqueued.  Buffers are owned by the caller. */
