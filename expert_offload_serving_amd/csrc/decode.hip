@@ -412,6 +412,7 @@ __global__ void __launch_bounds__(kDT) fused_kernel(DecArgs a, int nsl) {
 // K steps are skipped).
 constexpr int kWW = 8;             // waves per workgroup
 constexpr int kWT = kWW * kWave;   // threads per workgroup
+constexpr int kWU = 4;             // waves per workgroup that take items of their own under COOP: one per SIMD
 #ifndef MOE_WAVE_MIN_ITEMS
 #define MOE_WAVE_MIN_ITEMS 600     // work items from which decode runs the wave-item kernel (about T >= 4)
 #endif
@@ -532,13 +533,78 @@ __device__ __forceinline__ void wv_compute_b(const DecArgs& a, const Ring8& R, i
     }
 }
 
+// SwiGLU on this lane's rows 4g + [0, 4) of each gate/up tile pair (acc: the slice's gate and up tiles over all
+// of K), then the phase B operands: operand f of lane (c, g') holds slice rows 32f + 8g' + [0, 8) of token c,
+// taken from lanes (c, 2(g' & 1)) and (c, 2(g' & 1) + 1) of tile 2f + (g' >> 1).  The hidden values go to fp16
+// times a power of two that puts the wave's largest one in [2^14, 2^15); oscale undoes it (times the column
+// weight wc) on the down result.
+template <int SL>
+__device__ __forceinline__ void wv_swiglu(const f32x4_t (&acc)[2 * WaveGeom<SL>::NTT],
+                                          const f32x4_t (&gl)[2 * WaveGeom<SL>::NTT], float xinv, float wc, int c,
+                                          int g, f16x8_t (&B)[WaveGeom<SL>::NB], float& oscale) {
+    using W = WaveGeom<SL>;
+    float h[W::NTT][4];
+    float hm = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < W::NTT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float gv = acc[tt][r] * xinv * gl[tt][r];
+            const float uv = acc[W::NTT + tt][r] * xinv * gl[W::NTT + tt][r];
+            h[tt][r] = silu_fast(gv) * uv;
+            hm = fmaxf(hm, fabsf(h[tt][r]));
+        }
+    hm = fmaxf(hm, __shfl_xor(hm, 16, kWave));
+    hm = fmaxf(hm, __shfl_xor(hm, 32, kWave));
+    const int hsh = fp16_shift(hm);
+    const float hsc = ldexpf(1.0f, hsh);
+    uint32_t P[W::NTT][2];
+#pragma unroll
+    for (int tt = 0; tt < W::NTT; ++tt)
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const f16x2_t q = {(_Float16)(h[tt][2 * d] * hsc), (_Float16)(h[tt][2 * d + 1] * hsc)};
+            P[tt][d] = __builtin_bit_cast(uint32_t, q);
+        }
+    const int src0 = c + 32 * (g & 1), src1 = src0 + 16;
+    const bool hi = g >= 2;
+#pragma unroll
+    for (int f = 0; f < W::NB; ++f) {
+        uint32_t bw[4];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const uint32_t a0 = (uint32_t)__shfl((int)P[2 * f][d], src0, kWave);
+            const uint32_t a1 = (uint32_t)__shfl((int)P[2 * f + 1][d], src0, kWave);
+            const uint32_t b0 = (uint32_t)__shfl((int)P[2 * f][d], src1, kWave);
+            const uint32_t b1 = (uint32_t)__shfl((int)P[2 * f + 1][d], src1, kWave);
+            bw[d] = hi ? a1 : a0;
+            bw[2 + d] = hi ? b1 : b0;
+        }
+        B[f] = __builtin_bit_cast(f16x8_t, u32x4_t{bw[0], bw[1], bw[2], bw[3]});
+    }
+    oscale = ldexpf(1.0f, -hsh) * wc;
+}
+
+// Waits until the LDS counter *p reaches target (the waves that raise it never wait on this one).
+__device__ __forceinline__ void lds_wait_count(int* p, int target) {
+    while (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) __builtin_amdgcn_s_sleep(1);
+}
+
 // MULTI: a wave may have several items (more items than waves); otherwise each wave has at most one and
 // nothing of a next item is prefetched (even out-of-range loads take the CU's address units).
-template <int SL, bool ROUTE, bool MULTI>
+// COOP (with !MULTI): only the first kWU waves of a workgroup (one per SIMD) take items of their own; the
+// items past kWU per workgroup (leftovers) are each run by the other kWU waves of one workgroup together,
+// beside the first waves' items from the start: wave kWU + w streams the gate_up groups w, w + kWU, ... and the
+// down groups w, w + kWU, ..., and the gate_up partial sums meet in LDS, added in wave order, before SwiGLU.
+// One wave running a leftover beside an item would share one SIMD's VALU (the fp4 decode) for the whole call
+// with one wave's loads in flight; split over kWU waves it spreads over the four SIMDs.
+template <int SL, bool ROUTE, bool MULTI, bool COOP = false>
 __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
     using W = WaveGeom<SL>;
     extern __shared__ __attribute__((aligned(16))) _Float16 x16[];  // (T + 1) rows of XP halves; row T is zero
     __shared__ WaveShared sh;
+    __shared__ f32x4_t coop_red[COOP ? kWU : 1][COOP ? 2 * W::NTT : 1][kWave];
+    __shared__ int coop_cnt[2];  // partial sums written, partial sums read (counted per wave, never reset)
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int H = a.H, T = a.T, k = a.k;
@@ -549,7 +615,8 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
     const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
     const int stride = (int)gridDim.x * kWW;
     // consecutive items go to different CUs; readfirstlane tells the compiler the item is wave-uniform
-    int v = __builtin_amdgcn_readfirstlane(wave * (int)gridDim.x + (int)blockIdx.x);
+    int v = __builtin_amdgcn_readfirstlane(COOP && wave >= kWU ? n_items : wave * (int)gridDim.x + (int)blockIdx.x);
+    if (COOP && tid < 2) coop_cnt[tid] = 0;
 
     const int c = lane & 15, g = lane >> 4;
     const int KQ = H / 128, NG = H / 64;
@@ -569,8 +636,9 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
     __builtin_amdgcn_sched_barrier(0);
     stage_x<kWW>(a, xv, sh.xsh, x16, XP, tid, lane, wave);
     __syncthreads();
-    if (v >= n_items) return;  // uniform per wave; no barrier follows
-    do {
+    const bool coop_wave = COOP && wave >= kWU;  // runs leftover items, none of its own
+    if (v >= n_items && !coop_wave) return;      // uniform per wave; no barrier follows
+    if (v < n_items) do {
         const Item nxt = decode_item(a, sh.tb, n_act, nsl, v + stride, MULTI && v + stride < n_items, c);
         const int xrow = cur.tok >= 0 ? cur.tok : T;
         const _Float16* xr = x16 + xrow * XP + 8 * g;
@@ -599,54 +667,10 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
         wv_issue_b<SL>(a, cur, 1, lane, R1);
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- SwiGLU on this lane's rows 4g + [0, 4) of each gate/up tile pair, then the phase B operands:
-        // operand f of lane (c, g') holds slice rows 32f + 8g' + [0, 8) of token c, taken from lanes
-        // (c, 2(g' & 1)) and (c, 2(g' & 1) + 1) of tile 2f + (g' >> 1)
+        // ---- SwiGLU, then the phase B operands
         f16x8_t B[W::NB];
         float oscale;
-        {
-            const float xinv = ldexpf(1.0f, -sh.xsh[xrow]);
-            float h[W::NTT][4];
-            float hm = 0.0f;
-#pragma unroll
-            for (int tt = 0; tt < W::NTT; ++tt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float gv = acc[tt][r] * xinv * gl[tt][r];
-                    const float uv = acc[W::NTT + tt][r] * xinv * gl[W::NTT + tt][r];
-                    h[tt][r] = silu_fast(gv) * uv;
-                    hm = fmaxf(hm, fabsf(h[tt][r]));
-                }
-            hm = fmaxf(hm, __shfl_xor(hm, 16, kWave));
-            hm = fmaxf(hm, __shfl_xor(hm, 32, kWave));
-            const int hsh = fp16_shift(hm);
-            const float hsc = ldexpf(1.0f, hsh);
-            uint32_t P[W::NTT][2];
-#pragma unroll
-            for (int tt = 0; tt < W::NTT; ++tt)
-#pragma unroll
-                for (int d = 0; d < 2; ++d) {
-                    const f16x2_t q = {(_Float16)(h[tt][2 * d] * hsc), (_Float16)(h[tt][2 * d + 1] * hsc)};
-                    P[tt][d] = __builtin_bit_cast(uint32_t, q);
-                }
-            const int src0 = c + 32 * (g & 1), src1 = src0 + 16;
-            const bool hi = g >= 2;
-#pragma unroll
-            for (int f = 0; f < W::NB; ++f) {
-                uint32_t bw[4];
-#pragma unroll
-                for (int d = 0; d < 2; ++d) {
-                    const uint32_t a0 = (uint32_t)__shfl((int)P[2 * f][d], src0, kWave);
-                    const uint32_t a1 = (uint32_t)__shfl((int)P[2 * f + 1][d], src0, kWave);
-                    const uint32_t b0 = (uint32_t)__shfl((int)P[2 * f][d], src1, kWave);
-                    const uint32_t b1 = (uint32_t)__shfl((int)P[2 * f + 1][d], src1, kWave);
-                    bw[d] = hi ? a1 : a0;
-                    bw[2 + d] = hi ? b1 : b0;
-                }
-                B[f] = __builtin_bit_cast(f16x8_t, u32x4_t{bw[0], bw[1], bw[2], bw[3]});
-            }
-            oscale = ldexpf(1.0f, -hsh) * cur.wc;
-        }
+        wv_swiglu<SL>(acc, gl, ldexpf(1.0f, -sh.xsh[xrow]), cur.wc, c, g, B, oscale);
         // slice 0 records, per output row of the item, where the expert's down globals live
         __builtin_amdgcn_raw_buffer_store_b32((uint32_t)cur.slot_index, rres,
                                               cur.s == 0 && g == 0 && c < cur.ne ? 4 * cur.prow : kOob, 0, 0);
@@ -681,6 +705,87 @@ __global__ void __launch_bounds__(kWT) wave_kernel(DecArgs a, int nsl) {
         cur = nxt;
         v += stride;
     } while (v < n_items);
+
+    if (coop_wave) {
+        // leftover items kWU * grid + b + grid * r of workgroup b, run by its waves kWU .. 2 kWU - 1 together
+        // (each takes part in every round, so all kWU of them arrive at every count below)
+        const int cw = wave - kWU;
+        const int grid = (int)gridDim.x;
+        for (int r = 0;; ++r) {
+            const int lv = kWU * grid + (int)blockIdx.x + grid * r;
+            if (lv >= n_items) break;  // uniform over the workgroup's leftover waves
+            const Item it = decode_item(a, sh.tb, n_act, nsl, lv, true, c);
+            const int xrow = it.tok >= 0 ? it.tok : T;
+            const _Float16* xr = x16 + xrow * XP + 8 * g;
+            f32x4_t acc[2 * W::NTT];
+#pragma unroll
+            for (int q = 0; q < 2 * W::NTT; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            wv_issue_glob<SL>(a, it, lane, gl);
+            // gate_up groups cw, cw + kWU, ...: groups past NGA load zeros and their steps are skipped
+            int ga = cw;
+            wv_issue_a<SL>(a, it, ga, lane, R0);
+            wv_issue_a<SL>(a, it, ga + kWU, lane, R1);
+            __builtin_amdgcn_sched_barrier(0);
+            for (; ga + 2 * kWU < NGA; ga += 2 * kWU) {
+                wv_compute_a<SL>(a, R0, ga, xr, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                wv_issue_a<SL>(a, it, ga + 2 * kWU, lane, R0);
+                __builtin_amdgcn_sched_barrier(0);
+                wv_compute_a<SL>(a, R1, ga + kWU, xr, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                wv_issue_a<SL>(a, it, ga + 3 * kWU, lane, R1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wv_compute_a<SL>(a, R0, ga, xr, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            wv_compute_a<SL>(a, R1, ga + kWU, xr, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            // the kWU partial sums meet in LDS (the previous round's have all been read)
+            lds_wait_count(&coop_cnt[1], kWU * r);
+#pragma unroll
+            for (int q = 0; q < 2 * W::NTT; ++q) coop_red[cw][q][lane] = acc[q];
+            if (lane == 0) __hip_atomic_fetch_add(&coop_cnt[0], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            lds_wait_count(&coop_cnt[0], kWU * (r + 1));
+#pragma unroll
+            for (int q = 0; q < 2 * W::NTT; ++q) {
+                f32x4_t t = coop_red[0][q][lane];
+#pragma unroll
+                for (int w = 1; w < kWU; ++w) t += coop_red[w][q][lane];
+                acc[q] = t;
+                __builtin_amdgcn_sched_barrier(0);  // a tile at a time
+            }
+            if (lane == 0) __hip_atomic_fetch_add(&coop_cnt[1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            f16x8_t B[W::NB];
+            float oscale;
+            wv_swiglu<SL>(acc, gl, ldexpf(1.0f, -sh.xsh[xrow]), it.wc, c, g, B, oscale);
+            // the down records are issued only now: in flight across the reduction and SwiGLU they would push
+            // the kernel past its registers
+            __builtin_amdgcn_sched_barrier(0);
+            wv_issue_b<SL>(a, it, cw, lane, R0);
+            wv_issue_b<SL>(a, it, cw + kWU, lane, R1);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)it.slot_index, rres,
+                                                  cw == 0 && it.s == 0 && g == 0 && c < it.ne ? 4 * it.prow : kOob,
+                                                  0, 0);
+            // down groups cw, cw + kWU, ...: groups past NGB load zeros and store nothing
+            const int pbase = c < it.ne ? 4 * ((it.prow * nsl + it.s) * H + 4 * g) : kOob;
+            int gb = cw;
+            for (; gb + 2 * kWU < NGB; gb += 2 * kWU) {
+                wv_compute_b<SL>(a, R0, gb, B, oscale, pres, pbase);
+                __builtin_amdgcn_sched_barrier(0);
+                wv_issue_b<SL>(a, it, gb + 2 * kWU, lane, R0);
+                __builtin_amdgcn_sched_barrier(0);
+                wv_compute_b<SL>(a, R1, gb + kWU, B, oscale, pres, pbase);
+                __builtin_amdgcn_sched_barrier(0);
+                wv_issue_b<SL>(a, it, gb + 3 * kWU, lane, R1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wv_compute_b<SL>(a, R0, gb, B, oscale, pres, pbase);
+            __builtin_amdgcn_sched_barrier(0);
+            wv_compute_b<SL>(a, R1, gb + kWU, B, oscale, pres, pbase);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 }
 
 constexpr size_t kXLdsMax = (size_t)(kDecodeMaxT + 1) * (2560 + 8) * 2;
@@ -749,11 +854,14 @@ template <int SL, bool ROUTE>
 hipError_t launch_wave(const DecArgs& a, int items_max, int nsl, int ncu, hipStream_t s) {
     hipError_t e = allow_lds(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE, true>));
     if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE, false>));
+    if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void*>(&wave_kernel<SL, ROUTE, false, true>));
     if (e != hipSuccess) return e;
     const int grid = items_max < ncu ? items_max : ncu;
     const size_t lds = (size_t)(a.T + 1) * (a.H + 8) * 2;
     if (items_max > grid * kWW)  // some wave has a second item
         hipLaunchKernelGGL((wave_kernel<SL, ROUTE, true>), dim3(grid), dim3(kWT), lds, s, a, nsl);
+    else if (items_max > grid * kWU && items_max <= grid * (kWU + 2))  // a few leftovers: up to two rounds
+        hipLaunchKernelGGL((wave_kernel<SL, ROUTE, false, true>), dim3(grid), dim3(kWT), lds, s, a, nsl);
     else
         hipLaunchKernelGGL((wave_kernel<SL, ROUTE, false>), dim3(grid), dim3(kWT), lds, s, a, nsl);
     return hipGetLastError();

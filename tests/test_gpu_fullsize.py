@@ -104,6 +104,31 @@ def test_decode_full_shape_distinct_permuted(decode_layer, T):
     print(f"T={T} rel L2 {rel:.2e}")
 
 
+@pytest.mark.parametrize("T", [14, 16])
+def test_decode_leftover_items_run_together(decode_layer, T):
+    """Every token routed to 8 experts of its own: T*8 active experts plus the shared one, 64-row items (10 per
+    expert): 1,130 items at T=14, 1,290 at T=16, against one item per SIMD (1,024).  The items past that run
+    cooperatively on the four item waves of a workgroup, in one round (T=14) or two (T=16)."""
+    L = _with_tokens(decode_layer, T, 2000 + T)
+    lg = np.random.default_rng(3000 + T).random((T, L.E), dtype=np.float32)
+    for t in range(T):
+        lg[t, 8 * t:8 * t + 8] = 2.0 + np.arange(8, dtype=np.float32) * 0.125
+    L = synth.LayerInputs(L.H, L.I, L.E, L.k, T, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, lg)
+    _announce(f"decode leftover items, T={T}, {T * 8} distinct experts + shared")
+    ids, w, ref = _oracle(L)
+    assert len(np.unique(ids)) == 8 * T
+    dev = device_layer(L)
+    x, dlg = device_x(L), device_logits(L)
+    r = dl.route(dlg, L.k)
+    y = dl.forward(dev, x, r)
+    y_again = dl.forward(dev, x, r)
+    torch.cuda.synchronize()
+    _check_routing(r, ids, w, L.E, f"route T={T}")
+    assert torch.equal(y, y_again), "forward not bit-identical between calls"
+    rel = assert_close(y.cpu().numpy(), ref, f"forward T={T}")
+    print(f"T={T} rel L2 {rel:.2e}")
+
+
 def test_prefill_2048_all_tokens_distinct_permuted():
     """The 2048-token prefill config (Zipf routing, seed 2048) in the benchmark's launch configuration, every
     token against the oracle, with all 257 experts distinct and stored at random slots."""
