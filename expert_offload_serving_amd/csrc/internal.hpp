@@ -64,12 +64,13 @@ inline bool decode_path(int T, int H, int I, int k) {
 // expert's down-row globals); the prefill path uses the others:
 //   h      hidden state, (T*k + T) rows of I fp16 values
 //   hx     the exponent of each 128-column tile of h, (T*k + T) rows of ceil(I/128) i32
-//   o      per-assignment expert outputs, (T*k + T) rows of H f32
+//   o      per-assignment expert outputs, (T*k + T) rows of H fp16, chunk (row, c) scaled by 2^ox[row, c]
+//   ox     the exponent of each 256-column chunk of o, (T*k + T) rows of ceil(H/256) i32
 //   s      shared-gate sigmoid per token, T f32
 //   x16    scaled fp16 activations [T, H]; xinv: their inverse scales [T]
 //   tiles  work lists: 4 counts, then 3 classes x tile_cap (group, m0) pairs
 struct WsLayout {
-    size_t part, dg, dgrow, h, hx, o, s, x16, xinv, tiles, total;
+    size_t part, dg, dgrow, h, hx, o, ox, s, x16, xinv, tiles, total;
     int tile_cap;
 };
 inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -86,7 +87,8 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.h = 0;
     L.hx = L.h + align256(rows * I * 2);
     L.o = L.hx + align256(rows * (size_t)ceil_div(I, 128) * 4);
-    L.s = L.o + align256(rows * H * 4);
+    L.ox = L.o + align256(rows * H * 2);
+    L.s = L.ox + align256(rows * (size_t)ceil_div(H, 256) * 4);
     L.x16 = L.s + align256((size_t)T * 4);
     L.xinv = L.x16 + align256((size_t)T * H * 2);
     L.tiles = L.xinv + align256((size_t)T * 4);

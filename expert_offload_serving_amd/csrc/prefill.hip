@@ -38,8 +38,9 @@
 //             one 32/64/128-row remainder per group
 //   gate_up:  C = x W_gu^T over 64 gate and the 64 matching up rows per tile,
 //             epilogue h = silu(gate) * up -> fp16
-//   down:     O = h W_dn^T over 128 output rows per tile -> fp32
-//   combine:  y_t = sum_j w_tj O[pos(t,j)] + s_t O[shared row t] (fixed order)
+//   down:     O = h W_dn^T over 128 output rows per tile -> fp16, each (row, 256-column chunk) times
+//             its own power of two (the chunk's largest magnitude in [2^14, 2^15)), undone by the combine
+//   combine:  y_t = sum_j w_tj O[pos(t,j)] + s_t O[shared row t] (fixed order, fp32)
 #include <map>
 #include <mutex>
 
@@ -70,7 +71,9 @@ struct PrefillArgs {
     _Float16* hbuf;   // fp16 [(T*k + T), I], tile (row, c) scaled by 2^hexp[row, c]
     int* hexp;        // i32  [(T*k + T), KT]: exponent of each 128-column tile of hbuf (kNoExp: all zero)
     int KT;           // 128-column tiles of I
-    float* obuf;      // f32  [(T*k + T), H]
+    _Float16* obuf;   // fp16 [(T*k + T), H], chunk (row, c) scaled by 2^oexp[row, c]
+    int* oexp;        // i32  [(T*k + T), OT]: exponent of each 256-column chunk of obuf (kNoExp: all zero)
+    int OT;           // 256-column chunks of H
     _Float16* x16;    // fp16 [T, H] scaled activations
     float* xinv;      // f32  [T] inverse activation scale
     float* sbuf;      // f32  [T] shared gate
@@ -273,8 +276,9 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
     static_assert(!GATEUP || NWN * 8 * NB == BK, "gate_up column tile must match the down K step");
     __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * APITCH];
     __shared__ int tok[BM];
-    // gate_up: per-(row, wave along the weight rows) maximum of |h|; down: each row's smallest tile exponent
-    __shared__ float smax[GATEUP ? NWN : 1][BM];
+    // per-(row, wave along the weight rows) maximum of |h| (gate_up) or |o| (down); down: each row's smallest
+    // hidden-state tile exponent
+    __shared__ float smax[NWN][BM];
     __shared__ int semin[BM];
 
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs (block b to XCD b % 8), so the active
@@ -522,22 +526,57 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
                 }
             }
     } else {
+        // o = acc * 2^-emin * gd; a wave's NB / 4 record groups are 64 output columns of one 256-column chunk
+        // (chunk (NWN nt + wn) / 4: column tiles are 256 or 512 wide, so the waves of a chunk share a workgroup).
+        // The chunk's largest |o| per row (16 lanes, the wave's blocks, then the chunk's four waves) sets the
+        // power of two the row's chunk is stored under in fp16.
+        static_assert(GATEUP || (NB == 4 && NWN % 4 == 0), "a down wave covers 64 columns; four make a 256-column chunk");
+        float ov[NB][MI][4];
+        float rmax[MI][4];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rmax[i][r] = 0.0f;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const int oc = 64 * (grp0 + (b >> 2)) + 16 * (b & 3) + l16;
-            if (oc >= H) continue;
-            const float gd = __uint_as_float(buf_load4(gres, (int)a.dn_glob + 4 * oc));
+            const int oc = 64 * grp0 + 16 * b + l16;
+            const bool cok = oc < H;
+            const float gd = __uint_as_float(buf_load4(gres, cok ? (int)a.dn_glob + 4 * oc : kOob));
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = 16 * MI * wm + 16 * i + 4 * q4 + r;
-                    if (m < cnt) {
-                        const int e = semin[m];
-                        a.obuf[(size_t)(gb + m0 + m) * H + oc] = ldexpf(acc[i][b][r], e == kNoExp ? 0 : -e) * gd;
-                    }
+                    const int e = semin[m];
+                    const float o = cok && m < cnt ? ldexpf(acc[i][b][r], e == kNoExp ? 0 : -e) * gd : 0.0f;
+                    ov[b][i][r] = o;
+                    rmax[i][r] = fmaxf(rmax[i][r], fabsf(o));
                 }
         }
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = row16_max(rmax[i][r]);
+                if (l16 == 0) smax[wn][16 * MI * wm + 16 * i + 4 * q4 + r] = v;
+            }
+        __syncthreads();
+        const int OT = a.OT, ch = grp0 / 4, w0 = wn & ~3;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * MI * wm + 16 * i + 4 * q4 + r;
+                const float cmax = fmaxf(fmaxf(smax[w0][m], smax[w0 + 1][m]), fmaxf(smax[w0 + 2][m], smax[w0 + 3][m]));
+                const int e = tile_shift(cmax);
+                if (m < cnt && wn == w0 && l16 == 0 && ch < OT) a.oexp[(size_t)(gb + m0 + m) * OT + ch] = e;
+                const float sc = ldexpf(1.0f, e == kNoExp ? 0 : e);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int oc = 64 * grp0 + 16 * b + l16;
+                    if (oc < H && m < cnt) a.obuf[(size_t)(gb + m0 + m) * H + oc] = (_Float16)(ov[b][i][r] * sc);
+                }
+            }
     }
 }
 
@@ -569,18 +608,38 @@ hipError_t launch_tiles(const PrefillArgs& a, int cls, int max_tiles, hipStream_
 }
 
 // ------------------------------------------------------------------ combine
-// One thread per 4 output columns of token t; the k expert rows are read in
-// groups of 8 with every load of a group in flight before the first add
-// (rows past k read as zero), and added in assignment order.
+// One thread per 8 output columns of token t (one 16-byte load per expert
+// row; 8 columns never straddle a 256-column exponent chunk); the k expert
+// rows are read in groups of 8 with every load of a group in flight before the
+// first add (rows past k read as zero), brought back to fp32 by their chunk's
+// exponent and added in assignment order.
+struct O8 {
+    f32x4_t lo, hi;
+};
+__device__ __forceinline__ O8 load_o8(const rsrc_t& ores, const rsrc_t& xres, int row, int c8, int H8, int OT,
+                                      bool valid) {
+    const int ch = (8 * c8) / 256;
+    const int e = (int)buf_load4(xres, valid ? 4 * (row * OT + ch) : kOob);
+    const u32x4_t h = buf_load16(ores, valid ? 16 * (row * H8 + c8) : kOob);
+    const float sc = e == kNoExp ? 0.0f : ldexpf(1.0f, -e);
+    // word_of, not h.y: __builtin_bit_cast of a vector element (h.y) compiles here to a cast of element 0
+    const f16x2_t h0 = __builtin_bit_cast(f16x2_t, word_of(h, 0)), h1 = __builtin_bit_cast(f16x2_t, word_of(h, 1));
+    const f16x2_t h2 = __builtin_bit_cast(f16x2_t, word_of(h, 2)), h3 = __builtin_bit_cast(f16x2_t, word_of(h, 3));
+    return O8{f32x4_t{(float)h0.x, (float)h0.y, (float)h1.x, (float)h1.y} * sc,
+              f32x4_t{(float)h2.x, (float)h2.y, (float)h3.x, (float)h3.y} * sc};
+}
+
 __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a, int nchunk) {
     const int t = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
-    const int H = a.H, T = a.T, k = a.k, H4 = H / 4;
-    const int c4 = chunk * 256 + (int)threadIdx.x;
-    if (c4 >= H4) return;
-    const rsrc_t ores = make_rsrc(a.obuf, (uint32_t)((size_t)(T * k + T) * H * 4));
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int H = a.H, T = a.T, k = a.k, H8 = H / 8, OT = a.OT;
+    const int c8 = chunk * 256 + (int)threadIdx.x;
+    if (c8 >= H8) return;
+    const int rows = T * k + T;
+    const rsrc_t ores = make_rsrc(a.obuf, (uint32_t)((size_t)rows * H * 2));
+    const rsrc_t xres = make_rsrc(a.oexp, (uint32_t)((size_t)rows * OT * 4));
+    f32x4_t lo = {0.0f, 0.0f, 0.0f, 0.0f}, hi = lo;
     for (int j0 = 0; j0 < k; j0 += 8) {
-        f32x4_t v[8];
+        O8 v[8];
         float wj[8];
         bool ok[8];
 #pragma unroll
@@ -588,21 +647,23 @@ __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a, int nchunk)
             const int j = j0 + i, aidx = t * k + j;
             const bool valid = j < k;
             const int p = valid ? a.assign_pos[aidx] : 0;
-            v[i] = __builtin_bit_cast(f32x4_t, buf_load16(ores, valid ? 16 * (p * H4 + c4) : kOob));
+            v[i] = load_o8(ores, xres, p, c8, H8, OT, valid);
             wj[i] = valid ? a.w[aidx] : 0.0f;
             ok[i] = valid && slot_in_bank(a, a.slot_of_expert[a.ids[aidx]]);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            if (ok[i]) acc += wj[i] * v[i];
+            if (ok[i]) lo += wj[i] * v[i].lo, hi += wj[i] * v[i].hi;
     }
     if (a.shared != nullptr) {
-        const f32x4_t vs = __builtin_bit_cast(f32x4_t, buf_load16(ores, 16 * ((T * k + t) * H4 + c4)));
-        acc += a.sbuf[t] * vs;
+        const O8 vs = load_o8(ores, xres, T * k + t, c8, H8, OT, true);
+        lo += a.sbuf[t] * vs.lo;
+        hi += a.sbuf[t] * vs.hi;
     }
-    f32x4_t* yp = reinterpret_cast<f32x4_t*>(a.y + (size_t)t * H) + c4;
-    if (a.accumulate) acc += *yp;
-    *yp = acc;
+    f32x4_t* yp = reinterpret_cast<f32x4_t*>(a.y + (size_t)t * H) + 2 * c8;
+    if (a.accumulate) lo += yp[0], hi += yp[1];
+    yp[0] = lo;
+    yp[1] = hi;
 }
 
 // The 128-row tiles (matrix-core bound) and the 32/64-row remainder tiles
@@ -676,7 +737,9 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     a.hbuf = reinterpret_cast<_Float16*>(p + wl.h);
     a.hexp = reinterpret_cast<int*>(p + wl.hx);
     a.KT = ceil_div(I, BK);
-    a.obuf = reinterpret_cast<float*>(p + wl.o);
+    a.obuf = reinterpret_cast<_Float16*>(p + wl.o);
+    a.oexp = reinterpret_cast<int*>(p + wl.ox);
+    a.OT = ceil_div(H, 256);
     a.x16 = reinterpret_cast<_Float16*>(p + wl.x16);
     a.xinv = reinterpret_cast<float*>(p + wl.xinv);
     a.sbuf = reinterpret_cast<float*>(p + wl.s);
@@ -708,7 +771,7 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     if ((e = launch_tiles<true, 128>(a, 0, max128, s)) != hipSuccess) return e;
     if ((e = launch_tiles<false, 128>(a, 0, max128, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s, f.joined, 0)) != hipSuccess) return e;
-    const int nchunk = ceil_div(H / 4, 256);
+    const int nchunk = ceil_div(H / 8, 256);
     hipLaunchKernelGGL(combine_kernel, dim3(T * nchunk), dim3(256), 0, s, a, nchunk);
     return hipGetLastError();
 }
