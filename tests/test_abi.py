@@ -121,8 +121,10 @@ def test_forward_refuses_buffers_of_2gib():
     output would reach it are refused before anything is enqueued (no GPU needed)."""
     d = 0x3000
     f = lambda L, T: _lib.moe_nvfp4_forward(L, d, T, d, d, d, d, d, d, 0, 0x200000, 1 << 62, 0)
-    assert _lib.moe_nvfp4_forward_workspace_bytes(23_000, 2560, 640, 256, 8) >= 1 << 31
-    assert f(_layer(), 23_000) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    # the prefill workspace first reaches 2 GiB at T = 33,939 for these shapes
+    assert _lib.moe_nvfp4_forward_workspace_bytes(33_938, 2560, 640, 256, 8) < 1 << 31
+    assert _lib.moe_nvfp4_forward_workspace_bytes(33_939, 2560, 640, 256, 8) >= 1 << 31
+    assert f(_layer(), 33_939) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
     assert "2 GiB" in _lib.last_error()
     assert f(_layer(), 200_000) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
     assert f(_layer(), 0) == _lib.MOE_OK  # T = 0 stays a valid no-op
