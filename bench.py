@@ -47,11 +47,11 @@ DTYPE_MX = "mxfp4w-fp8x2scaledmfma-bf16x2mfma-fp32acc"
 # kernels and scaled by what the same counters read for a plain copy of known size), with a digest of the kernel
 # sources they were taken on.  Reported as roofline.traffic only while those sources are unchanged.
 COUNTED_TRAFFIC = {
-    "decode_bs1": (29_536_890, "a0b07b34ca494660"),
-    "decode_bs16": (318_864_941, "a0b07b34ca494660"),
-    "prefill_2048": (1_395_470_065, "c93bc6ebc63cd5e1"),
-    "mxfp4_decode_bs1": (27_783_258, "bd608b08969f1eef"),
-    "mxfp4_decode_bs16": (330_865_370, "bd608b08969f1eef"),
+    "decode_bs1": (29_530_271, "a4931601b49db091"),
+    "decode_bs16": (319_183_108, "a4931601b49db091"),
+    "prefill_2048": (1_181_113_811, "9c5957eb5128e954"),
+    "mxfp4_decode_bs1": (27_774_362, "1883acdbb16eff3b"),
+    "mxfp4_decode_bs16": (330_863_930, "1883acdbb16eff3b"),
 }
 KERNEL_SOURCES = {"decode": ["decode.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],
                   "mxfp4": ["mxfp4.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],
