@@ -12,8 +12,8 @@ Default run: every workload, printed as ONE JSON line whose top level is the
 decode shape the metric is quoted on (H=2560, I=640, 256 experts top-8 with
 uniform-random logits, one shared expert, batch 1) and whose "configs" entry
 holds the full result of decode batch 16, the 2048-token prefill chunk, the
-offloaded 48-layer run and the MXFP4 bank format at decode batch 1 and 16,
-each with its own roofline and CPU baseline.
+offloaded 48-layer run and the MXFP4 bank format at decode batch 1 and 16 and
+the 2048-token prefill, each with its own roofline and CPU baseline.
 `--config NAME` prints that workload's line alone.
 
 The arithmetic (dtype field): NVFP4 weights decoded exactly to fp16, bf16
@@ -41,6 +41,7 @@ PCIE_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction
 DTYPE = "nvfp4w-fp16mfma-fp32acc"
 METRIC_MX = "MoE-layer tokens/s + expert-weight HBM GB/s (% peak), H2560 I640 MXFP4"
 DTYPE_MX = "mxfp4w-fp8x2scaledmfma-bf16x2mfma-fp32acc"
+DTYPE_MX_PREFILL = "mxfp4w-bf16mfma-bf16x2h-fp32acc"  # MXFP4 prefill: weights decoded exactly to bf16
 
 
 # HBM bytes per call of the roofline unit from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, summed over the call's
@@ -246,7 +247,7 @@ def oracle_threads():
 
 # Per-repetition sample of each workload for the oracle (one oracle call per step, as the GPU runs them).
 CPU_SAMPLES = {"decode_bs1": 4, "decode_bs16": 1, "prefill_2048": 128, "offload": 2, "mxfp4_decode_bs1": 4,
-               "mxfp4_decode_bs16": 1}
+               "mxfp4_decode_bs16": 1, "mxfp4_prefill_2048": 128}
 
 
 def cpu_leg(name: str, reps: int = 5) -> dict:
@@ -556,8 +557,11 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
         tf = flops / fwd_s / 1e12
         roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": counted_traffic(name, "prefill"),
-                "kernel": "moe_nvfp4_forward prefill (prep_plan_kernel, tile_gemm_kernel over 128/64/32-row tiles for gate_up and "
-                          "down, combine_kernel), timed together with HIP events",
+                "kernel": ("moe_mxfp4_forward prefill (prep_plan_kernel, tile_gemm_kernel<..., MX> over 128/64/32-row "
+                           "tiles for gate_up and down on v_mfma_f32_16x16x32_bf16, combine_kernel), timed together "
+                           "with HIP events") if mx else
+                          ("moe_nvfp4_forward prefill (prep_plan_kernel, tile_gemm_kernel over 128/64/32-row tiles for "
+                           "gate_up and down, combine_kernel), timed together with HIP events"),
                 "per_launch": f"{flops / 1e9:.2f} GFLOP per forward (2*3*I*H*(T*k+T))"}
     elif mx:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -577,7 +581,8 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
     out = {
         "metric": METRIC_MX if mx else METRIC, "value": round(tokens_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_MX if mx else DTYPE, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": (DTYPE_MX_PREFILL if prefill else DTYPE_MX) if mx else DTYPE, "data": "synthetic",
         "config": {"workload": name, "H": H, "I": I, "E": E, "k": k, "T": T, "shared_expert": True,
                    "bank_copies": replicas, "distinct_quantized_experts": min(distinct, E + 1),
                    "parallelism": "single GPU"},
@@ -693,7 +698,7 @@ def copy_calibration(nbytes: int, reps: int) -> None:
 
 
 REPLICAS = {"decode_bs1": 16, "decode_bs16": 8, "prefill_2048": 4,  # bank copies rotated over steps
-            "mxfp4_decode_bs1": 16, "mxfp4_decode_bs16": 8}
+            "mxfp4_decode_bs1": 16, "mxfp4_decode_bs16": 8, "mxfp4_prefill_2048": 4}
 
 
 def main():
@@ -703,7 +708,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="all",
                     choices=["decode_bs1", "decode_bs16", "prefill_2048", "offload", "offload_prefill", "mxfp4_decode_bs1",
-                             "mxfp4_decode_bs16", "all", *ROUTER_CONFIGS])
+                             "mxfp4_decode_bs16", "mxfp4_prefill_2048", "all", *ROUTER_CONFIGS])
     ap.add_argument("--replicas", type=int, default=0,
                     help="copies of the expert bank rotated over steps (default 16 at bs 1, 8 at bs 16, 4 prefill)")
     ap.add_argument("--distinct", type=int, default=32, help="experts quantized; the other slots are sign-flipped "
@@ -746,7 +751,7 @@ def main():
         if name == "offload_prefill":  # 2048-token chunks through all 48 layers: a few steps
             return bench_offload(3, 1, args.distinct, want_cpu, args.residency, not args.aliased_banks, T=2048)
         steps, warmup = args.steps, args.warmup
-        if name == "prefill_2048":
+        if name.endswith("prefill_2048"):
             steps, warmup = max(1, min(steps, 20)), max(1, min(warmup, 3))
         reps = args.replicas or REPLICAS[name]
         return bench_config(name, steps, warmup, reps, args.distinct, want_cpu)
@@ -758,7 +763,7 @@ def main():
     head = run("decode_bs1")
     head["configs"] = {}
     for name in ("decode_bs16", "prefill_2048", "offload", "offload_prefill", "mxfp4_decode_bs1",
-                 "mxfp4_decode_bs16"):
+                 "mxfp4_decode_bs16", "mxfp4_prefill_2048"):
         head["configs"][name] = run(name)
         torch.cuda.empty_cache()
     print(json.dumps(head), flush=True)

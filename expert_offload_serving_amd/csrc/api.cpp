@@ -392,11 +392,16 @@ int validate_mx_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T
     if (L.slot_bytes != sb)
         return fail(MOE_ERR_INVALID_ARGUMENT, "slot_bytes %zu does not match an MXFP4 slot at H=%d, I=%d (%zu bytes)",
                     L.slot_bytes, L.H, L.I, sb);
+    const bool decode = moe::decode_path(T, L.H, L.I, L.k);
+    // the kernels address every buffer through 32-bit offsets: each must stay below 2 GiB
+    if (sb >= kMaxBuffer || (size_t)T * L.H * 4 >= kMaxBuffer ||
+        moe::forward_ws_bytes(T, L.H, L.I, L.E, L.k, true) >= kMaxBuffer)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T=%d H=%d I=%d k=%d: a slot, x, y or the workspace reaches 2 GiB", T,
+                    L.H, L.I, L.k);
     if (T == 0) return MOE_OK;
-    if (!moe::decode_path(T, L.H, L.I, L.k) || !moe::mx_decode_shape_supported(L.H, L.I))
-        return fail(MOE_ERR_UNSUPPORTED_SHAPE,
-                    "MXFP4 layers run the decode path only (T <= %d, T*k <= %d, H <= 2560; got T=%d H=%d k=%d)",
-                    moe::kDecodeMaxT, moe::kDecodeMaxAssign, T, L.H, L.k);
+    if (decode ? !moe::mx_decode_shape_supported(L.H, L.I) : !moe::prefill_shape_supported(L.H, L.I))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "MXFP4 %s path does not support H=%d, I=%d",
+                    decode ? "decode" : "prefill", L.H, L.I);
     if (!L.bank_base || !L.slot_of_expert || L.num_slots < 1)
         return fail(MOE_ERR_INVALID_ARGUMENT, "layer bank, slot map and num_slots are required");
     if (reinterpret_cast<uintptr_t>(L.bank_base) % 256 != 0)
@@ -407,7 +412,7 @@ int validate_mx_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T
         return fail(MOE_ERR_INVALID_ARGUMENT, "shared_gate_w is required with a shared expert");
     if (!x || !topk_ids || !topk_w || !expert_offsets || !sorted_assign || !assign_pos || !y)
         return fail(MOE_ERR_INVALID_ARGUMENT, "moe_mxfp4_forward: null pointer argument");
-    const size_t need = moe::forward_ws_bytes(T, L.H, L.I, L.E, L.k);
+    const size_t need = moe::forward_ws_bytes(T, L.H, L.I, L.E, L.k, true);
     if (!ws || ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "forward workspace %zu < %zu bytes", ws_bytes, need);
     if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
@@ -425,8 +430,10 @@ size_t moe_mxfp4_slot_bytes(int H, int I) {
 }
 
 size_t moe_mxfp4_forward_workspace_bytes(int T, int H, int I, int E, int k) {
-    if (!shape_ok(H, I) || check_route_shape(T, E, k) != MOE_OK || !moe::decode_path(T, H, I, k)) return 0;
-    return moe::forward_ws_bytes(T, H, I, E, k);
+    if (!shape_ok(H, I) || check_route_shape(T, E, k) != MOE_OK) return 0;
+    if (moe::decode_path(T, H, I, k) ? !moe::mx_decode_shape_supported(H, I) : !moe::prefill_shape_supported(H, I))
+        return 0;
+    return moe::forward_ws_bytes(T, H, I, E, k, true);
 }
 
 int moe_mxfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
@@ -436,8 +443,12 @@ int moe_mxfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, 
     int rc = validate_mx_forward(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y,
                                  accumulate, ws, ws_bytes);
     if (rc != MOE_OK || T == 0) return rc;
-    hipError_t e = moe::launch_mx_decode(layer_of(*layer), x, T, topk_w, expert_offsets, sorted_assign, y, accumulate,
-                                         ws, stream);
+    const moe::Layer ml = layer_of(*layer);
+    hipError_t e = moe::decode_path(T, ml.H, ml.I, ml.k)
+                       ? moe::launch_mx_decode(ml, x, T, topk_w, expert_offsets, sorted_assign, y, accumulate, ws,
+                                               stream)
+                       : moe::launch_prefill(ml, x, T, topk_w, topk_ids, expert_offsets, sorted_assign, assign_pos, y,
+                                             accumulate, ws, stream, true);
     if (e != hipSuccess) return hip_fail(e, "moe_mxfp4_forward launch");
     return MOE_OK;
 }
@@ -457,7 +468,7 @@ int moe_mxfp4_route_forward(const moe_nvfp4_layer_t* layer, const float* logits,
     int rc = check_route_shape(T, L.E, L.k);
     if (rc != MOE_OK) return rc;
     // every check of the forward, against its share of the workspace (the routing's follows it)
-    const size_t f = moe::forward_ws_bytes(T, L.H, L.I, L.E, L.k);
+    const size_t f = moe::forward_ws_bytes(T, L.H, L.I, L.E, L.k, true);
     const size_t fws = moe::align256(f);
     rc = validate_mx_forward(layer, x, T, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos, y, accumulate,
                              ws, ws_bytes < fws ? ws_bytes : fws);
@@ -475,7 +486,10 @@ int moe_mxfp4_route_forward(const moe_nvfp4_layer_t* layer, const float* logits,
         e = moe::launch_route(logits, T, L.E, L.k, topk_ids, topk_w, expert_offsets, sorted_assign, assign_pos,
                               static_cast<uint8_t*>(ws) + fws, stream);
         if (e == hipSuccess)
-            e = moe::launch_mx_decode(ml, x, T, topk_w, expert_offsets, sorted_assign, y, accumulate, ws, stream);
+            e = moe::decode_path(T, L.H, L.I, L.k)
+                    ? moe::launch_mx_decode(ml, x, T, topk_w, expert_offsets, sorted_assign, y, accumulate, ws, stream)
+                    : moe::launch_prefill(ml, x, T, topk_w, topk_ids, expert_offsets, sorted_assign, assign_pos, y,
+                                          accumulate, ws, stream, true);
     }
     if (e != hipSuccess) return hip_fail(e, "moe_mxfp4_route_forward launch");
     return MOE_OK;

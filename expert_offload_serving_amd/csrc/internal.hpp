@@ -62,8 +62,9 @@ inline bool decode_path(int T, int H, int I, int k) {
 // The decode path uses `part` (per-(row, slice) partial outputs), `dg`
 // (per-row slot of the row's expert) and `dgrow` (per-row copies of the
 // expert's down-row globals); the prefill path uses the others:
-//   h      hidden state, (T*k + T) rows of I fp16 values
-//   hx     the exponent of each 128-column tile of h, (T*k + T) rows of ceil(I/128) i32
+//   h      hidden state, (T*k + T) rows of I fp16 values (MXFP4 bank: the bf16
+//          high terms of all rows, then the bf16 low terms)
+//   hx     the exponent of each 128-column tile of h, (T*k + T) rows of ceil(I/128) i32 (MXFP4: empty)
 //   o      per-assignment expert outputs, (T*k + T) rows of H fp16, chunk (row, c) scaled by 2^ox[row, c]
 //   ox     the exponent of each 256-column chunk of o, (T*k + T) rows of ceil(H/256) i32
 //   s      shared-gate sigmoid per token, T f32
@@ -74,7 +75,7 @@ struct WsLayout {
     int tile_cap;
 };
 inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
-inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
+inline WsLayout ws_layout(int T, int H, int I, int E, int k, bool mx = false) {
     WsLayout L{};
     if (decode_path(T, H, I, k)) {
         L.part = 0;
@@ -85,8 +86,8 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
     }
     const size_t rows = (size_t)T * k + T;
     L.h = 0;
-    L.hx = L.h + align256(rows * I * 2);
-    L.o = L.hx + align256(rows * (size_t)ceil_div(I, 128) * 4);
+    L.hx = L.h + align256(rows * I * (mx ? 4 : 2));
+    L.o = L.hx + (mx ? 0 : align256(rows * (size_t)ceil_div(I, 128) * 4));
     L.ox = L.o + align256(rows * H * 2);
     L.s = L.ox + align256(rows * (size_t)ceil_div(H, 256) * 4);
     L.x16 = L.s + align256((size_t)T * 4);
@@ -96,7 +97,9 @@ inline WsLayout ws_layout(int T, int H, int I, int E, int k) {
     L.total = L.tiles + align256((4 + 3 * 2 * (size_t)L.tile_cap) * 4);
     return L;
 }
-inline size_t forward_ws_bytes(int T, int H, int I, int E, int k) { return ws_layout(T, H, I, E, k).total; }
+inline size_t forward_ws_bytes(int T, int H, int I, int E, int k, bool mx = false) {
+    return ws_layout(T, H, I, E, k, mx).total;
+}
 
 // Routing computed inside the decode kernels (route_forward): the logits and
 // the routing outputs, which the kernels fill as moe_route_topk would.
@@ -119,9 +122,10 @@ hipError_t launch_decode(const Layer& L, const uint16_t* x, int T, const float* 
 // Prefill path, T > 16 (prefill.hip)
 bool prefill_shape_supported(int H, int I);
 hipError_t release_side_streams();
+// mx: the bank holds MXFP4 slots (mx_slot_geom) instead of NVFP4 ones.
 hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                           const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
-                          int accumulate, void* ws, hipStream_t s);
+                          int accumulate, void* ws, hipStream_t s, bool mx = false);
 
 // MXFP4 bank format (mxfp4.hip, slicer in util.hip): slot regions (globals empty), the decode path (T <= 16), the
 // dequant hooks (checkpoint-transposed matrix; one matrix of a slot through the forward's own decode).

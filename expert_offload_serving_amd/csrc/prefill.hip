@@ -41,6 +41,19 @@
 //   down:     O = h W_dn^T over 128 output rows per tile -> fp16, each (row, 256-column chunk) times
 //             its own power of two (the chunk's largest magnitude in [2^14, 2^15)), undone by the combine
 //   combine:  y_t = sum_j w_tj O[pos(t,j)] + s_t O[shared row t] (fixed order, fp32)
+//
+// MXFP4 banks (E2M1 with one E8M0 scale per 32 elements, no globals) run the
+// same kernels with MX set: the weights are decoded exactly to bf16 by
+// v_cvt_scalef32_pk_bf16_fp4, which applies the block's E8M0 scale itself
+// (e2m1 * 2^e is exact in bf16 for every E8M0 value), into
+// v_mfma_f32_16x16x32_bf16.  gate_up takes the bf16 activations as they are
+// (no per-token scale); its records give lane (row i, a) the 32 columns
+// [32a, 32a + 32) of the step (one scale block), so MFMA m of a step uses
+// dword m of every lane's record and the activation columns 32a + 8m + [0, 8)
+// of the same lane position: the four MFMAs still cover the step's 128
+// columns once.  The hidden state is stored as two bf16 terms (h_hi = bf16(h),
+// h_lo = bf16(h - h_hi): 16 significant bits, fp32's range, no exponents) and
+// down multiplies each decoded weight fragment by both.
 #include <map>
 #include <mutex>
 
@@ -69,6 +82,8 @@ struct PrefillArgs {
     const int32_t* sorted_assign;
     const int32_t* assign_pos;
     _Float16* hbuf;   // fp16 [(T*k + T), I], tile (row, c) scaled by 2^hexp[row, c]
+    uint16_t* hmx;    // MXFP4: bf16 [(T*k + T), I] high terms, then the low terms
+    int mx;           // MXFP4 bank (the prep skips the fp16 activations)
     int* hexp;        // i32  [(T*k + T), KT]: exponent of each 128-column tile of hbuf (kNoExp: all zero)
     int KT;           // 128-column tiles of I
     _Float16* obuf;   // fp16 [(T*k + T), H], chunk (row, c) scaled by 2^oexp[row, c]
@@ -140,6 +155,7 @@ __device__ __forceinline__ void prep_token(const PrefillArgs& a, int t, float (&
         a.xinv[t] = ldexpf(1.0f, -shift);
         if (a.shared != nullptr) a.sbuf[t] = sigmoidf_(red[1][0] + red[1][1] + red[1][2] + red[1][3]);
     }
+    if (a.mx) return;  // the MXFP4 GEMMs read the bf16 activations directly
     f16x2_t* dst = reinterpret_cast<f16x2_t*>(a.x16 + (size_t)t * H);
 #pragma unroll
     for (int q = 0; q < kMaxV; ++q) {
@@ -251,6 +267,25 @@ __device__ __forceinline__ u32x4_t scale_h8(u32x4_t v, int d) {
     return o;
 }
 
+// MXFP4: E8M0 byte as an f32 power of two; eight E2M1 codes (one dword) times 2^(e - 127), exactly, in bf16.
+__device__ __forceinline__ float e8m0_f32(uint32_t b) { return __uint_as_float((b & 0xFF) << 23); }
+__device__ __forceinline__ bf16x8_t mx_frag_bf16(uint32_t cw, float sc) {
+    const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0);
+    const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1);
+    const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2);
+    const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3);
+    const u32x4_t u = {__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                       __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+// bf16 bits of the two terms of h: hi = bf16(h), lo = bf16(h - hi) (both round to nearest even)
+__device__ __forceinline__ void split_bf16(float h, uint16_t& hi, uint16_t& lo) {
+    const __bf16 bh = (__bf16)h;
+    const __bf16 bl = (__bf16)(h - (float)bh);
+    hi = __builtin_bit_cast(uint16_t, bh);
+    lo = __builtin_bit_cast(uint16_t, bl);
+}
+
 // ------------------------------------------------------------------ grouped GEMM tiles
 // One workgroup (NW waves) computes a BM-token tile (BM = 128, 64 or 32)
 // against a block of weight rows: gate_up: matching gate and up rows, down:
@@ -266,7 +301,7 @@ __device__ __forceinline__ u32x4_t scale_h8(u32x4_t v, int d) {
 // then weights of step s + 2, so waiting for either never waits for the
 // other's newer loads.  Every load is an unconditional buffer load (past
 // the end it reads zeros), which keeps the compiler's wait counts exact.
-template <bool GATEUP, int BM, int NW, int WM, int NB, int MINW>
+template <bool GATEUP, int BM, int NW, int WM, int NB, int MINW, bool MX>
 __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs a, int cls, int n_tiles_n) {
     constexpr int NWN = NW / WM;             // waves along the weight rows (WM along the tokens)
     constexpr int MI = BM / 16 / WM;         // 16-row token blocks per wave
@@ -274,7 +309,8 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
     constexpr int AQ = BM * 16 / NT;         // activation chunks per thread per step
     // a gate_up workgroup's h-columns are exactly one 128-column K step of the down GEMM (one exponent tile)
     static_assert(!GATEUP || NWN * 8 * NB == BK, "gate_up column tile must match the down K step");
-    __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM * APITCH];
+    constexpr int NA = MX && !GATEUP ? 2 : 1;  // activation tiles per step: MXFP4 down stages h_hi and h_lo
+    __shared__ __attribute__((aligned(16))) _Float16 sA[2][NA * BM * APITCH];
     __shared__ int tok[BM];
     // per-(row, wave along the weight rows) maximum of |h| (gate_up) or |o| (down); down: each row's smallest
     // hidden-state tile exponent
@@ -315,8 +351,11 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
 
     // ---- activation loader: thread -> 16-byte chunk (tid & 15) of rows (tid >> 4) + (NT / 16) q
     const int ach = tid & 15, arow0 = tid >> 4;
-    const rsrc_t ares = GATEUP ? make_rsrc(a.x16, (uint32_t)T * H * 2)
-                               : make_rsrc(a.hbuf, (uint32_t)((size_t)(T * k + T) * I * 2));
+    const int rows = T * k + T;
+    const rsrc_t ares = GATEUP ? make_rsrc(MX ? static_cast<const void*>(a.x) : static_cast<const void*>(a.x16),
+                                           (uint32_t)T * H * 2)
+                               : (MX ? make_rsrc(a.hmx, (uint32_t)((size_t)rows * I * 4))
+                                     : make_rsrc(a.hbuf, (uint32_t)((size_t)rows * I * 2)));
     int aoff[AQ];
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
@@ -326,9 +365,9 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
     }
     // down: the hidden-state tiles of a row carry their own exponents; each is brought to the row's smallest
     // (the exponent of its largest tile) while staged, and that one is undone in the epilogue
-    const rsrc_t xres = make_rsrc(a.hexp, GATEUP ? 0u : (uint32_t)((size_t)(T * k + T) * a.KT * 4));
+    const rsrc_t xres = make_rsrc(a.hexp, GATEUP || MX ? 0u : (uint32_t)((size_t)rows * a.KT * 4));
     int emin[GATEUP ? 1 : AQ], eoff[GATEUP ? 1 : AQ];
-    if (!GATEUP) {
+    if (!GATEUP && !MX) {
         int ev[AQ][4];
 #pragma unroll
         for (int q = 0; q < AQ; ++q) {
@@ -347,29 +386,39 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
             if (ach == 0) semin[arow0 + (NT / 16) * q] = e;
         }
     }
-    u32x4_t ra[AQ];
+    u32x4_t ra[AQ], rl[NA == 2 ? AQ : 1];
     int rex[GATEUP ? 1 : AQ];
     auto load_a = [&](int step) {
         const int kk = step * BK + 8 * ach;
         const bool ok = step < nsteps && kk < K;
-        if (!GATEUP) {
+        if (!GATEUP && !MX) {
 #pragma unroll
             for (int q = 0; q < AQ; ++q) rex[q] = (int)buf_load4(xres, step < nsteps ? eoff[q] + 4 * step : kOob);
         }
 #pragma unroll
         for (int q = 0; q < AQ; ++q) ra[q] = buf_load16(ares, ok ? aoff[q] + 2 * kk : kOob);
+        if (NA == 2) {
+#pragma unroll
+            for (int q = 0; q < AQ; ++q) rl[NA == 2 ? q : 0] = buf_load16(ares, ok ? 2 * rows * I + aoff[q] + 2 * kk : kOob);
+        }
     };
     auto store_a = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < AQ; ++q) {
-            const u32x4_t v = GATEUP ? ra[q] : scale_h8(ra[q], emin[GATEUP ? 0 : q] - rex[GATEUP ? 0 : q]);
+            const u32x4_t v = GATEUP || MX ? ra[q] : scale_h8(ra[q], emin[GATEUP ? 0 : q] - rex[GATEUP ? 0 : q]);
             *reinterpret_cast<u32x4_t*>(&sA[buf][(arow0 + (NT / 16) * q) * APITCH + 8 * ach]) = v;
+            if (NA == 2)
+                *reinterpret_cast<u32x4_t*>(&sA[buf][BM * APITCH + (arow0 + (NT / 16) * q) * APITCH + 8 * ach]) =
+                    rl[NA == 2 ? q : 0];
         }
     };
 
     // ---- weight records of this wave
     const rsrc_t sres = make_rsrc(slot, (uint32_t)a.slot_bytes);
-    const int soff = lane_scale_off(lane);
+    // scales: NVFP4 one dword per lane (its four E4M3 bytes); MXFP4 gate_up one E8M0 byte per lane, down one dword
+    // per lane (the four rows' E8M0 bytes), 64 bytes per record
+    const int soff = MX ? (GATEUP ? lane : 4 * (lane & 15)) : lane_scale_off(lane);
+    const int sstride = MX ? 64 : kRecScaleBytes;
     const int codes = (int)(GATEUP ? a.gu_codes : a.dn_codes), scales = (int)(GATEUP ? a.gu_scales : a.dn_scales);
     const int hc0 = 8 * NB * (NWN * nt + wn);      // gate_up: first h-column of the wave (NB / 2 tiles)
     const int grp0 = (NB / 4) * (NWN * nt + wn);   // down: first record group of the wave (NB / 4 groups)
@@ -394,7 +443,10 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
                 rec = kc * (H / 64) + grp0 + gi;
             }
             r.c[b] = buf_load16(sres, ok ? codes + rec * kRecBytes + 16 * lane : kOob);
-            r.s[b] = buf_load4(sres, ok ? scales + rec * kRecScaleBytes + soff : kOob);
+            if (MX && GATEUP)
+                r.s[b] = __builtin_amdgcn_raw_buffer_load_b8(sres, ok ? scales + rec * sstride + soff : kOob, 0, 0);
+            else
+                r.s[b] = buf_load4(sres, ok ? scales + rec * sstride + soff : kOob);
         }
     };
 
@@ -407,10 +459,36 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
     auto compute = [&](int buf, const BRegs& r) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
+            // MXFP4 gate_up: MFMA m takes dword m of every lane's record, columns 32 q4 + 8 m + [0, 8)
+            const int col = MX && GATEUP ? 32 * q4 + 8 * m : 32 * m + 8 * q4;
             f16x8_t fa[MI];
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-                fa[i] = lds_frag(&sA[buf][(16 * MI * wm + 16 * i + l16) * APITCH + 32 * m + 8 * q4]);
+            for (int i = 0; i < MI; ++i) fa[i] = lds_frag(&sA[buf][(16 * MI * wm + 16 * i + l16) * APITCH + col]);
+            if (MX) {
+                bf16x8_t fl[NA == 2 ? MI : 1];
+                if (NA == 2) {
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+                        fl[NA == 2 ? i : 0] = __builtin_bit_cast(
+                            bf16x8_t, lds_frag(&sA[buf][BM * APITCH + (16 * MI * wm + 16 * i + l16) * APITCH + col]));
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int ri = GATEUP ? b : 4 * (b >> 2) + m;
+                    const int d = GATEUP ? m : (b & 3);
+                    const float sc = e8m0_f32(GATEUP ? r.s[ri] : r.s[ri] >> (8 * d));
+                    const bf16x8_t fb = mx_frag_bf16(word_of(r.c[ri], d), sc);
+#pragma unroll
+                    for (int i = 0; i < MI; ++i) {
+                        acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[i]), fb,
+                                                                            acc[i][b], 0, 0, 0);
+                        if (NA == 2)
+                            acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[NA == 2 ? i : 0], fb, acc[i][b],
+                                                                                0, 0, 0);
+                    }
+                }
+                continue;
+            }
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 // gate_up: record b holds chunk m in dword m; down: record 4 gi + m holds tile j in dword j
@@ -469,7 +547,28 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
 
     // ---- epilogue: lane holds token rows 4 q4 + [0, 4) of column l16 of each 16x16 block
     const rsrc_t gres = make_rsrc(slot, (uint32_t)a.slot_bytes);
-    if (GATEUP) {
+    if (GATEUP && MX) {
+        // h = silu(gate) * up in fp32 (MXFP4 has no globals and the activations no scale), stored as two bf16 terms
+        constexpr int NC = NB / 2;
+        const size_t lo_off = (size_t)rows * I;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+            const int hc = hc0 + 16 * cb + l16;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 16 * MI * wm + 16 * i + 4 * q4 + r;
+                    if (hc < I && m < cnt) {
+                        uint16_t hi, lo;
+                        split_bf16(silu_fast(acc[i][cb][r]) * acc[i][NB / 2 + cb][r], hi, lo);
+                        const size_t at = (size_t)(gb + m0 + m) * I + hc;
+                        a.hmx[at] = hi;
+                        a.hmx[lo_off + at] = lo;
+                    }
+                }
+        }
+    } else if (GATEUP) {
         // h = silu(gate) * up in fp32; the tile's 128 columns are this workgroup's: its largest |h| per row
         // (over the 16 lanes of a column block, the wave's blocks, then the waves) sets the row's exponent
         constexpr int NC = NB / 2;
@@ -541,13 +640,14 @@ __global__ void __launch_bounds__(NW * kWave, MINW) tile_gemm_kernel(PrefillArgs
         for (int b = 0; b < NB; ++b) {
             const int oc = 64 * grp0 + 16 * b + l16;
             const bool cok = oc < H;
-            const float gd = __uint_as_float(buf_load4(gres, cok ? (int)a.dn_glob + 4 * oc : kOob));
+            // MXFP4: no row globals, and the hidden state carries no exponent
+            const float gd = MX ? 1.0f : __uint_as_float(buf_load4(gres, cok ? (int)a.dn_glob + 4 * oc : kOob));
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = 16 * MI * wm + 16 * i + 4 * q4 + r;
-                    const int e = semin[m];
+                    const int e = MX ? 0 : semin[m];
                     const float o = cok && m < cnt ? ldexpf(acc[i][b][r], e == kNoExp ? 0 : -e) * gd : 0.0f;
                     ov[b][i][r] = o;
                     rmax[i][r] = fmaxf(rmax[i][r], fabsf(o));
@@ -597,12 +697,14 @@ template <> struct TileCfg<false, 64> { static constexpr int NW = 8, WM = 1, NB 
 template <> struct TileCfg<true, 32> { static constexpr int NW = 8, WM = 1, NB = 2, MINW = 6; };
 template <> struct TileCfg<false, 32> { static constexpr int NW = 8, WM = 1, NB = 4, MINW = 4; };
 
-template <bool GATEUP, int BM>
+template <bool GATEUP, int BM, bool MX>
 hipError_t launch_tiles(const PrefillArgs& a, int cls, int max_tiles, hipStream_t s) {
     using C = TileCfg<GATEUP, BM>;
     const int cols = GATEUP ? (C::NW / C::WM) * 8 * C::NB : (C::NW / C::WM) * 16 * C::NB;  // h-columns or output rows
     const int ntn = ceil_div(GATEUP ? a.I : a.H, cols);
-    hipLaunchKernelGGL((tile_gemm_kernel<GATEUP, BM, C::NW, C::WM, C::NB, C::MINW>), dim3(max_tiles * ntn),
+    // the MXFP4 32-row down (two activation fragments per MFMA step) needs more registers than four waves per SIMD
+    constexpr int MINW = MX && !GATEUP && BM == 32 ? 3 : C::MINW;
+    hipLaunchKernelGGL((tile_gemm_kernel<GATEUP, BM, C::NW, C::WM, C::NB, MINW, MX>), dim3(max_tiles * ntn),
                        dim3(C::NW * kWave), 0, s, a, cls, ntn);
     return hipGetLastError();
 }
@@ -723,18 +825,53 @@ hipError_t release_side_streams() {
 
 bool prefill_shape_supported(int H, int I) { return H % 128 == 0 && I % 32 == 0 && H <= 8192; }
 
+namespace {
+
+// prep + plan, the grouped GEMMs (remainder tiles on the side stream), the combine
+template <bool MX>
+hipError_t run_prefill(const PrefillArgs& a, hipStream_t s) {
+    const int rows = a.T * a.k + a.T;
+    const int G = a.E + 1;
+    const int max128 = min(a.cap, rows / 128 + G);
+    const int maxsmall = min(a.cap, G);
+    // the side stream and its events exist before anything is enqueued, so a failure here enqueues nothing
+    Fork f;
+    hipError_t e = fork_for(s, f);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prep_plan_kernel, dim3(a.T + 1), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // remainder tiles on the side stream, 128-row tiles on the caller's stream
+    if ((e = hipEventRecord(f.forked, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(f.side, f.forked, 0)) != hipSuccess) return e;
+    if ((e = launch_tiles<true, 64, MX>(a, 1, maxsmall, f.side)) != hipSuccess) return e;
+    if ((e = launch_tiles<true, 32, MX>(a, 2, maxsmall, f.side)) != hipSuccess) return e;
+    if ((e = launch_tiles<false, 64, MX>(a, 1, maxsmall, f.side)) != hipSuccess) return e;
+    if ((e = launch_tiles<false, 32, MX>(a, 2, maxsmall, f.side)) != hipSuccess) return e;
+    if ((e = hipEventRecord(f.joined, f.side)) != hipSuccess) return e;
+    if ((e = launch_tiles<true, 128, MX>(a, 0, max128, s)) != hipSuccess) return e;
+    if ((e = launch_tiles<false, 128, MX>(a, 0, max128, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s, f.joined, 0)) != hipSuccess) return e;
+    const int nchunk = ceil_div(a.H / 8, 256);
+    hipLaunchKernelGGL(combine_kernel, dim3(a.T * nchunk), dim3(256), 0, s, a, nchunk);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float* w, const int32_t* ids,
                           const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos, float* y,
-                          int accumulate, void* ws, hipStream_t s) {
+                          int accumulate, void* ws, hipStream_t s, bool mx) {
     const int H = L.H, I = L.I, E = L.E, k = L.k;
     uint8_t* p = static_cast<uint8_t*>(ws);
-    const WsLayout wl = ws_layout(T, H, I, E, k);
+    const WsLayout wl = ws_layout(T, H, I, E, k, mx);
     PrefillArgs a;
     a.bank = L.bank; a.slot_bytes = L.slot_bytes; a.num_slots = L.num_slots; a.slot_of_expert = L.slot_of_expert;
     a.shared = L.shared; a.wg = L.wg; a.x = x;
     a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
     a.w = w; a.ids = ids; a.offsets = offsets; a.sorted_assign = sorted_assign; a.assign_pos = assign_pos;
     a.hbuf = reinterpret_cast<_Float16*>(p + wl.h);
+    a.hmx = reinterpret_cast<uint16_t*>(p + wl.h);
+    a.mx = mx ? 1 : 0;
     a.hexp = reinterpret_cast<int*>(p + wl.hx);
     a.KT = ceil_div(I, BK);
     a.obuf = reinterpret_cast<_Float16*>(p + wl.o);
@@ -746,34 +883,10 @@ hipError_t launch_prefill(const Layer& L, const uint16_t* x, int T, const float*
     a.tiles = reinterpret_cast<int*>(p + wl.tiles);
     a.cap = wl.tile_cap;
     a.y = y; a.accumulate = accumulate;
-    SlotGeom gm = slot_geom(H, I);
+    const SlotGeom gm = mx ? mx_slot_geom(H, I) : slot_geom(H, I);
     a.gu_codes = gm.gu_codes; a.gu_scales = gm.gu_scales; a.gu_glob = gm.gu_glob;
     a.dn_codes = gm.dn_codes; a.dn_scales = gm.dn_scales; a.dn_glob = gm.dn_glob;
-
-    const int rows = T * k + T;
-    const int G = E + 1;
-    const int max128 = min(a.cap, rows / 128 + G);
-    const int maxsmall = min(a.cap, G);
-    // the side stream and its events exist before anything is enqueued, so a failure here enqueues nothing
-    Fork f;
-    hipError_t e = fork_for(s, f);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prep_plan_kernel, dim3(T + 1), dim3(256), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // remainder tiles on the side stream, 128-row tiles on the caller's stream
-    if ((e = hipEventRecord(f.forked, s)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(f.side, f.forked, 0)) != hipSuccess) return e;
-    if ((e = launch_tiles<true, 64>(a, 1, maxsmall, f.side)) != hipSuccess) return e;
-    if ((e = launch_tiles<true, 32>(a, 2, maxsmall, f.side)) != hipSuccess) return e;
-    if ((e = launch_tiles<false, 64>(a, 1, maxsmall, f.side)) != hipSuccess) return e;
-    if ((e = launch_tiles<false, 32>(a, 2, maxsmall, f.side)) != hipSuccess) return e;
-    if ((e = hipEventRecord(f.joined, f.side)) != hipSuccess) return e;
-    if ((e = launch_tiles<true, 128>(a, 0, max128, s)) != hipSuccess) return e;
-    if ((e = launch_tiles<false, 128>(a, 0, max128, s)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(s, f.joined, 0)) != hipSuccess) return e;
-    const int nchunk = ceil_div(H / 8, 256);
-    hipLaunchKernelGGL(combine_kernel, dim3(T * nchunk), dim3(256), 0, s, a, nchunk);
-    return hipGetLastError();
+    return mx ? run_prefill<true>(a, s) : run_prefill<false>(a, s);
 }
 
 }  // namespace moe

@@ -335,16 +335,19 @@ size_t moe_mxfp4_forward_workspace_bytes(int T, int H, int I, int E, int k);
 
 /* The routed-MoE layer of moe_nvfp4_forward over MXFP4 slots (the same
  * layer struct with slot_bytes = moe_mxfp4_slot_bytes(H, I); the same
- * routing inputs, combine, accumulate and error rules).  It runs the decode
- * path only: T <= 16, T*k <= 1024, H <= 2560 (larger T returns
- * MOE_ERR_UNSUPPORTED_SHAPE with nothing enqueued).  gate_up runs on
- * v_mfma_scale_f32_16x16x128_f8f6f4 with the fp4 codes and E8M0 scales used
- * as stored and the activations entered as two fp8 E4M3 terms with their own
- * E8M0 block scales (the bf16 value exactly, unless a block's values span
- * more than the fp8 range); down decodes its codes exactly to bf16 with the
- * scale applied by v_cvt_scalef32_pk_bf16_fp4 and multiplies them on
- * v_mfma_f32_16x16x32_bf16 against the hidden state as two bf16 terms.
- * Sums are fp32 in a fixed order (bit-reproducible). */
+ * routing inputs, combine, accumulate and error rules, the same 2 GiB
+ * buffer limits).  Decode path (T <= 16, T*k <= 1024, H <= 2560): gate_up
+ * runs on v_mfma_scale_f32_16x16x128_f8f6f4 with the fp4 codes and E8M0
+ * scales used as stored and the activations entered as two fp8 E4M3 terms
+ * with their own E8M0 block scales (the bf16 value exactly, unless a block's
+ * values span more than the fp8 range); down decodes its codes exactly to
+ * bf16 with the scale applied by v_cvt_scalef32_pk_bf16_fp4 and multiplies
+ * them on v_mfma_f32_16x16x32_bf16 against the hidden state as two bf16
+ * terms.  Larger T (H <= 8192) runs the grouped-GEMM prefill path of
+ * moe_nvfp4_forward with both matrices decoded exactly to bf16 by that
+ * converter, on v_mfma_f32_16x16x32_bf16 against the bf16 activations
+ * (gate_up) and the hidden state as two bf16 terms (down).  Sums are fp32 in
+ * a fixed order (bit-reproducible). */
 int moe_mxfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int T, const int32_t* topk_ids,
                       const float* topk_w, const int32_t* expert_offsets, const int32_t* sorted_assign,
                       const int32_t* assign_pos, float* y, int accumulate, void* ws, size_t ws_bytes,

@@ -179,7 +179,7 @@ def test_mx_route_forward_matches_route_then_forward(mx_layer, T):
     assert_close(y_acc.cpu().numpy(), ref_ns + y0.cpu().numpy(), f"mx route_forward accumulate T={T}")
 
 
-def test_mx_forward_refuses_prefill_and_wrong_slot_size(mx_layer):
+def test_mx_forward_refuses_wrong_slot_size_and_small_workspace(mx_layer):
     L = mx_layer
     dev = device_layer(L, "mxfp4")
     x = torch.zeros((17, L.H), dtype=torch.bfloat16, device="cuda")
@@ -187,10 +187,109 @@ def test_mx_forward_refuses_prefill_and_wrong_slot_size(mx_layer):
     y = torch.full((17, L.H), 3.0, device="cuda")
     ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
     st = dev.struct()
+    need = _lib.moe_mxfp4_forward_workspace_bytes(17, L.H, L.I, L.E, L.k)
+    assert need > ws.numel()
     rc = _lib.moe_mxfp4_forward(st, x, 17, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y, 0, ws, ws.numel())
-    assert rc == _lib.MOE_ERR_UNSUPPORTED_SHAPE and "decode path" in _lib.last_error()
+    assert rc == _lib.MOE_ERR_WORKSPACE_TOO_SMALL
     st.slot_bytes = _lib.moe_nvfp4_slot_bytes(L.H, L.I)  # an NVFP4 slot size
     rc = _lib.moe_mxfp4_forward(st, x, 4, r.ids, r.w, r.offsets, r.sorted_assign, r.assign_pos, y, 0, ws, ws.numel())
     assert rc == _lib.MOE_ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
     assert bool((y == 3.0).all())
+
+
+# ---------------------------------------------------------------- prefill (T > 16): the grouped GEMMs over MXFP4
+
+def _mx_with_tokens(base, T, seed, kind="uniform"):
+    xb, lg = synth.fresh_tokens(seed, T, base.H, base.E, kind)
+    return synth.LayerInputs(base.H, base.I, base.E, base.k, T, base.bank, base.slot_of_expert, base.shared_slot,
+                             base.wg, xb, lg)
+
+
+@pytest.mark.parametrize("T", [17, 40, 300])
+def test_mx_prefill_vs_oracle(mx_layer, T):
+    """MXFP4 prefill (128/64/32-row tiles of the grouped GEMMs) at H=2560, I=640, 256 experts top-8, every slot
+    distinct, experts at random slots; every token against the oracle; bit-reproducible."""
+    L = _mx_with_tokens(mx_layer, T, 1700 + T)
+    _announce(f"mxfp4 prefill T={T}")
+    dev = device_layer(L, "mxfp4")
+    x = device_x(L)
+    r = dl.route(device_logits(L), L.k)
+    y = dl.forward(dev, x, r)
+    y2 = dl.forward(dev, x, r)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "not bit-reproducible"
+    ids, w = oracle.route(L.logits, L.k)
+    ref = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w,
+                         nthreads=NTHREADS, fmt="mxfp4")
+    rel = assert_close(y.cpu().numpy(), ref, f"mx prefill T={T}")
+    print(f"mx prefill T={T} rel L2 {rel:.2e}")
+
+
+def test_mx_prefill_2048_sampled():
+    """The 2048-token prefill (Zipf routing) over an MXFP4 bank, 64 sampled tokens against the oracle."""
+    L = synth.make_layer("prefill_2048", n_distinct=16, fmt="mxfp4")
+    _announce("mxfp4 prefill 2048 sampled")
+    dev = device_layer(L, "mxfp4")
+    r = dl.route(device_logits(L), L.k)
+    y = dl.forward(dev, device_x(L), r)
+    torch.cuda.synchronize()
+    counts = np.diff(r.offsets.cpu().numpy())
+    print(f"per-expert counts: min {counts.min()} median {int(np.median(counts))} max {counts.max()}")
+    toks = np.random.default_rng(1).choice(L.T, 64, replace=False).astype(np.int32)
+    ids, w = oracle.route(L.logits, L.k)
+    ref = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w,
+                         tokens=toks, nthreads=NTHREADS, fmt="mxfp4")
+    assert_close(y.cpu().numpy()[toks], ref, "mx prefill 2048 sampled")
+
+
+def test_mx_prefill_odd_shapes():
+    """Small and odd sizes on the prefill path: one 128-column step (H=128), one 32-row slice (I=32), a partial
+    128-column tile of I (I=96) and a partial 256-column exponent chunk (H=384)."""
+    for (H, I, E, k, T) in [(128, 32, 5, 2, 17), (384, 96, 7, 3, 40), (384, 640, 64, 8, 40)]:
+        rng = np.random.default_rng(H + I + T)
+        bank = synth.make_bank(rng, H, I, E + 1, None, fmt="mxfp4")
+        L = synth.LayerInputs(H, I, E, k, T, bank, np.arange(E, dtype=np.int32), E,
+                              synth.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32) * 0.02),
+                              synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)),
+                              rng.standard_normal((T, E)).astype(np.float32))
+        _announce(f"mxfp4 prefill H={H} I={I} E={E} k={k} T={T}")
+        y = dl.forward(device_layer(L, "mxfp4"), device_x(L), dl.route(device_logits(L), k))
+        torch.cuda.synchronize()
+        ids, w = oracle.route(L.logits, k)
+        ref = oracle.forward(H, I, E, k, bank, L.slot_of_expert, E, L.wg, L.x, ids, w, fmt="mxfp4")
+        assert_close(y.cpu().numpy(), ref, f"mx prefill H={H} I={I} T={T}")
+
+
+def test_mx_prefill_route_forward_and_left_out_slots(mx_layer):
+    """route_forward at T=40 (routing launch + prefill) equals route + forward bit for bit; a slot map with experts
+    past the bank or -1 leaves them out, with and without the shared expert, accumulating into y."""
+    T = 40
+    L = _mx_with_tokens(mx_layer, T, 1900)
+    _announce("mxfp4 prefill route_forward and left-out slots T=40")
+    dev = device_layer(L, "mxfp4")
+    x, lgd = device_x(L), device_logits(L)
+    r_sep = dl.route(lgd, L.k)
+    y_sep = dl.forward(dev, x, r_sep)
+    y_one, r_one = dl.route_forward(dev, lgd, x)
+    ids, w = oracle.route(L.logits, L.k)
+    routed = np.unique(ids)
+    bad = L.slot_of_expert.copy()
+    n = L.bank.shape[0]
+    bad[routed[0::3]] = n
+    bad[routed[1::5]] = -1
+    want_map = np.where(bad >= n, -1, bad).astype(np.int32)
+    y0 = torch.from_numpy(np.random.default_rng(5).standard_normal((T, L.H)).astype(np.float32)).cuda()
+    y_acc = dl.forward(dev, x, r_sep, y=y0.clone(), accumulate=True, shared=False,
+                       slot_of_expert=torch.from_numpy(bad).cuda())
+    torch.cuda.synchronize()
+    for name in ("ids", "w", "offsets", "sorted_assign", "assign_pos"):
+        a, b = getattr(r_sep, name).cpu().numpy(), getattr(r_one, name).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"routing output {name} differs"
+    assert torch.equal(y_sep, y_one)
+    ref = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w,
+                         nthreads=NTHREADS, fmt="mxfp4")
+    assert_close(y_one.cpu().numpy(), ref, "mx prefill route_forward")
+    ref_left = oracle.forward(L.H, L.I, L.E, L.k, L.bank, want_map, -1, L.wg, L.x, ids, w, nthreads=NTHREADS,
+                              fmt="mxfp4")
+    assert_close(y_acc.cpu().numpy(), ref_left + y0.cpu().numpy(), "mx prefill left-out slots, accumulate")
