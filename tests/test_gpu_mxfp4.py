@@ -179,6 +179,33 @@ def test_mx_route_forward_matches_route_then_forward(mx_layer, T):
     assert_close(y_acc.cpu().numpy(), ref_ns + y0.cpu().numpy(), f"mx route_forward accumulate T={T}")
 
 
+@pytest.mark.parametrize("T", [14, 16])
+def test_mx_decode_leftover_items_run_together(mx_layer, T):
+    """Every token routed to 8 experts of its own: 8T active experts plus the shared one, in 32-row items (20 per
+    expert): 2,260 items at T=14 and 2,580 at T=16, against one item per wave (2,048), so 212 or 532 waves run a
+    second item after their first (the persistent wave kernel's multi-item path)."""
+    xb, lg = synth.fresh_tokens(1700 + T, T, mx_layer.H, mx_layer.E, "uniform")
+    lg = lg.copy()
+    for t in range(T):
+        lg[t, 8 * t:8 * t + 8] = 2.0 + np.arange(8, dtype=np.float32) * 0.125
+    L = synth.LayerInputs(mx_layer.H, mx_layer.I, mx_layer.E, mx_layer.k, T, mx_layer.bank, mx_layer.slot_of_expert,
+                          mx_layer.shared_slot, mx_layer.wg, xb, lg)
+    _announce(f"mxfp4 decode leftover items, T={T}, {8 * T} distinct experts + shared")
+    ids, w = oracle.route(L.logits, L.k)
+    assert len(np.unique(ids)) == 8 * T
+    dev = device_layer(L, "mxfp4")
+    r = dl.route(device_logits(L), L.k)
+    y = dl.forward(dev, device_x(L), r)
+    y2 = dl.forward(dev, device_x(L), r)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.ids.cpu().numpy(), ids)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32)), "not bit-reproducible"
+    ref = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w,
+                         nthreads=NTHREADS, fmt="mxfp4")
+    rel = assert_close(y.cpu().numpy(), ref, f"mx leftover items T={T}")
+    print(f"mx leftover T={T} rel L2 {rel:.2e}")
+
+
 def test_mx_forward_refuses_wrong_slot_size_and_small_workspace(mx_layer):
     L = mx_layer
     dev = device_layer(L, "mxfp4")
