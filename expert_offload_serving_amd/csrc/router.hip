@@ -11,7 +11,9 @@
 // takes columns [8g, 8g+8) of each 32-column chunk, the same for both
 // operands), in two groups of five 32-column chunks.  The 8 partial tiles
 // meet in LDS and are added in wave order, so the result does not depend on
-// timing.  Rows past T or E read zeros and are not written.
+// timing.  Rows past T or E read zeros and are not written.  The tiles are
+// dealt to the XCDs in contiguous ranges, so that the four expert tiles of a
+// token tile share one L2.
 // Decode batches (T <= 16) take the vector path below instead: the weights
 // are the traffic (E*H*2 bytes), so one workgroup per expert row spreads them
 // over E CUs (a 16-expert matrix tile would leave all but E/16 CUs idle).
@@ -30,7 +32,12 @@ __global__ void __launch_bounds__(kRW * kWave) router_logits_kernel(const uint16
     __shared__ f32x4_t part[kRW][MI * NJ][kWave];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int l16 = lane & 15, g = lane >> 4;
-    const int tb = (int)blockIdx.x / nbe, eb = (int)blockIdx.x % nbe;
+    // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs (block b to XCD b % 8), so the blocks of
+    // XCD x take one contiguous range of (token tile, expert tile) pairs: the expert tiles of a token tile then
+    // run on one XCD and its activation rows come from HBM once, into that XCD's L2, instead of once per tile
+    const int nblk = (int)gridDim.x, per = nblk / 8, extra = nblk % 8, xcd = (int)blockIdx.x % 8;
+    const int lb = xcd * per + min(xcd, extra) + (int)blockIdx.x / 8;
+    const int tb = lb / nbe, eb = lb % nbe;
     const int t0 = 16 * MI * tb, e0 = 16 * NJ * eb;
     const int kw = H / kRW;          // columns of this wave's range (a multiple of 32)
     const int kbeg = wave * kw;
