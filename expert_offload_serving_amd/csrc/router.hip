@@ -6,14 +6,17 @@
 // With more than 16 tokens the product is a dense contraction, so it runs on
 // v_mfma_f32_16x16x32_bf16 (bf16 x bf16 products are exact in fp32; fp32
 // accumulation).  A workgroup owns a tile of 32 tokens x 64 experts; its 8
-// waves split H into 8 equal ranges and each wave streams its range with
-// 16-byte buffer loads straight into MFMA operands (lane (row i, group g)
-// takes columns [8g, 8g+8) of each 32-column chunk, the same for both
-// operands), in two groups of five 32-column chunks.  The 8 partial tiles
-// meet in LDS and are added in wave order, so the result does not depend on
-// timing.  Rows past T or E read zeros and are not written.  The tiles are
-// dealt to the XCDs in contiguous ranges, so that the four expert tiles of a
-// token tile share one L2.
+// waves split H into 8 equal ranges.  A wave streams its range in groups of
+// 64 columns: each 16-byte buffer load covers 8 rows x 128 bytes (whole
+// cache lines), the group goes to the wave's own LDS area, and the MFMA
+// operands (lane (row i, group g): columns [8g, 8g+8) of a 32-column chunk)
+// are read from there while the next group's loads are in flight.  Loading
+// the operands straight from memory in MFMA order (16 rows x 64 bytes per
+// load) streams about 3x slower from L2.  The 8 partial tiles meet in LDS
+// and are added in wave order, so the result does not depend on timing.
+// Rows past T or E read zeros and are not written.  The tiles are dealt to
+// the XCDs in contiguous ranges, so that the four expert tiles of a token
+// tile share one L2.
 // Decode batches (T <= 16) take the vector path below instead: the weights
 // are the traffic (E*H*2 bytes), so one workgroup per expert row spreads them
 // over E CUs (a 16-expert matrix tile would leave all but E/16 CUs idle).
@@ -29,7 +32,12 @@ template <int MI, int NJ>
 __global__ void __launch_bounds__(kRW * kWave) router_logits_kernel(const uint16_t* __restrict__ x,
                                                                     const uint16_t* __restrict__ wr, int T, int H,
                                                                     int E, float* __restrict__ logits, int nbe) {
-    __shared__ f32x4_t part[kRW][MI * NJ][kWave];
+    constexpr int XR = 16 * MI, WR = 16 * NJ;  // token rows and expert rows of the tile
+    constexpr int PITCH = 144;                 // LDS bytes per staged row: 128 + 16, conflict-free fragment reads
+    constexpr int NXI = XR / 8, NWI = WR / 8;  // loads per 64-column group (8 rows x 128 bytes each)
+    constexpr int STAGE = (XR + WR) * PITCH;   // one wave's staging area
+    static_assert(kRW * MI * NJ * kWave * 16 <= kRW * STAGE, "the partial tiles reuse the staging areas");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRW * STAGE];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int l16 = lane & 15, g = lane >> 4;
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs (block b to XCD b % 8), so the blocks of
@@ -38,52 +46,68 @@ __global__ void __launch_bounds__(kRW * kWave) router_logits_kernel(const uint16
     const int nblk = (int)gridDim.x, per = nblk / 8, extra = nblk % 8, xcd = (int)blockIdx.x % 8;
     const int lb = xcd * per + min(xcd, extra) + (int)blockIdx.x / 8;
     const int tb = lb / nbe, eb = lb % nbe;
-    const int t0 = 16 * MI * tb, e0 = 16 * NJ * eb;
+    const int t0 = XR * tb, e0 = WR * eb;
     const int kw = H / kRW;          // columns of this wave's range (a multiple of 32)
     const int kbeg = wave * kw;
     const rsrc_t xres = make_rsrc(x, (uint32_t)((size_t)T * H * 2));
     const rsrc_t wres = make_rsrc(wr, (uint32_t)((size_t)E * H * 2));
-    int xoff[MI], woff[NJ];
+    // loads: lane (r = lane / 8, c = lane % 8) takes row 8 q + r, bytes [16 c, 16 c + 16) of the group's 128 bytes;
+    // a wave load is then 8 whole 128-byte lines (16 rows x 64 bytes per load, the MFMA operand order, streams
+    // about 3x slower from L2)
+    const int lr = lane >> 3, lc = lane & 7;
+    int xoff[NXI], woff[NWI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-        const int t = t0 + 16 * i + l16;
-        xoff[i] = t < T ? 2 * (t * H + kbeg + 8 * g) : kOob;
+    for (int q = 0; q < NXI; ++q) {
+        const int t = t0 + 8 * q + lr;
+        xoff[q] = t < T ? 2 * (t * H + kbeg + 8 * lc) : kOob;
     }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int e = e0 + 16 * j + l16;
-        woff[j] = e < E ? 2 * (e * H + kbeg + 8 * g) : kOob;
+    for (int q = 0; q < NWI; ++q) {
+        const int e = e0 + 8 * q + lr;
+        woff[q] = e < E ? 2 * (e * H + kbeg + 8 * lc) : kOob;
     }
+    uint8_t* st = lds + wave * STAGE;  // this wave's rows: tokens 0 .. XR-1, then experts
+    u32x4_t rx[NXI], rw[NWI];
+    auto load = [&](int n) {  // group n: columns [64 n, 64 n + 64) of the wave's range; past the range: zeros
+        const bool in = 64 * n + 8 * lc < kw;
+#pragma unroll
+        for (int q = 0; q < NXI; ++q) rx[q] = buf_load16(xres, in && xoff[q] != kOob ? xoff[q] + 128 * n : kOob);
+#pragma unroll
+        for (int q = 0; q < NWI; ++q) rw[q] = buf_load16(wres, in && woff[q] != kOob ? woff[q] + 128 * n : kOob);
+    };
     f32x4_t acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    // G chunks of 32 columns per group: every load of a group is issued before its first MFMA (decode: the
-    // whole range at once).  Chunks past the range, and lanes past T or E, load zeros (an offset past the
-    // resource), which add nothing.
-    constexpr int G = (MI + NJ <= 2) ? 10 : 5;
-    for (int c0 = 0; c0 < kw; c0 += 32 * G) {
-        u32x4_t a[G][MI], b[G][NJ];
+    const int ngroups = (kw + 63) / 64;
+    load(0);
+    for (int n = 0; n < ngroups; ++n) {
+        // the wave's own staging area: its LDS operations run in order, so no barrier is needed
 #pragma unroll
-        for (int q = 0; q < G; ++q) {
-            const int c = c0 + 32 * q;
-            const bool in = c < kw;
+        for (int q = 0; q < NXI; ++q) *reinterpret_cast<u32x4_t*>(st + (8 * q + lr) * PITCH + 16 * lc) = rx[q];
 #pragma unroll
-            for (int i = 0; i < MI; ++i) a[q][i] = buf_load16(xres, in && xoff[i] != kOob ? xoff[i] + 2 * c : kOob);
+        for (int q = 0; q < NWI; ++q) *reinterpret_cast<u32x4_t*>(st + (XR + 8 * q + lr) * PITCH + 16 * lc) = rw[q];
+        if (n + 1 < ngroups) load(n + 1);  // in flight while this group is multiplied
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) b[q][j] = buf_load16(wres, in && woff[j] != kOob ? woff[j] + 2 * c : kOob);
-        }
+        for (int m = 0; m < 2; ++m) {
+            if (64 * n + 32 * m >= kw) break;  // uniform: the half group past the range
+            bf16x8_t fa[MI], fb[NJ];
 #pragma unroll
-        for (int q = 0; q < G; ++q)
+            for (int i = 0; i < MI; ++i)
+                fa[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + (16 * i + l16) * PITCH + 64 * m + 16 * g));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                fb[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + (XR + 16 * j + l16) * PITCH + 64 * m + 16 * g));
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[q][i]),
-                                                                         __builtin_bit_cast(bf16x8_t, b[q][j]),
-                                                                         acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
     }
+    __syncthreads();  // every wave is done with its staging area: it now holds the partial tiles
+    f32x4_t(*part)[MI * NJ][kWave] = reinterpret_cast<f32x4_t(*)[MI * NJ][kWave]>(lds);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
