@@ -50,10 +50,10 @@ DTYPE_MX_PREFILL = "mxfp4w-bf16mfma-bf16x2h-fp32acc"  # MXFP4 prefill: weights d
 COUNTED_TRAFFIC = {
     "decode_bs1": (29_530_271, "a4931601b49db091"),
     "decode_bs16": (319_183_108, "a4931601b49db091"),
-    "prefill_2048": (1_181_021_846, "77beaae3e2c9a31c"),
+    "prefill_2048": (1_180_886_918, "6284de10fb5c8ffc"),
     "mxfp4_decode_bs1": (27_774_362, "1883acdbb16eff3b"),
     "mxfp4_decode_bs16": (330_863_930, "1883acdbb16eff3b"),
-    "mxfp4_prefill_2048": (1_177_641_693, "77beaae3e2c9a31c"),
+    "mxfp4_prefill_2048": (1_177_178_029, "6284de10fb5c8ffc"),
 }
 KERNEL_SOURCES = {"decode": ["decode.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],
                   "mxfp4": ["mxfp4.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],
