@@ -253,21 +253,27 @@ def test_mx_prefill_vs_oracle(mx_layer, T):
     print(f"mx prefill T={T} rel L2 {rel:.2e}")
 
 
-def test_mx_prefill_2048_sampled():
-    """The 2048-token prefill (Zipf routing) over an MXFP4 bank, 64 sampled tokens against the oracle."""
-    L = synth.make_layer("prefill_2048", n_distinct=16, fmt="mxfp4")
-    _announce("mxfp4 prefill 2048 sampled")
+def test_mx_prefill_2048_all_tokens_distinct_permuted():
+    """The 2048-token prefill (Zipf routing) over an MXFP4 bank in the benchmark's launch configuration, every
+    token against the oracle, with all 257 experts distinct and stored at random slots of a larger bank."""
+    L = synth.permute_slots(synth.make_layer("prefill_2048", n_distinct=16, fmt="mxfp4"), np.random.default_rng(2049),
+                            spare=40)
+    used = [int(s) for s in L.slot_of_expert] + [L.shared_slot]
+    assert len({hashlib.sha1(L.bank[j].tobytes()).digest() for j in used}) == len(used), "two experts share weights"
+    assert not np.array_equal(L.slot_of_expert, np.arange(L.E))
+    _announce(f"mxfp4 prefill 2048 all tokens, distinct permuted bank ({L.bank.shape[0]} slots)")
     dev = device_layer(L, "mxfp4")
     r = dl.route(device_logits(L), L.k)
     y = dl.forward(dev, device_x(L), r)
     torch.cuda.synchronize()
     counts = np.diff(r.offsets.cpu().numpy())
-    print(f"per-expert counts: min {counts.min()} median {int(np.median(counts))} max {counts.max()}")
-    toks = np.random.default_rng(1).choice(L.T, 64, replace=False).astype(np.int32)
+    print(f"per-expert counts: min {counts.min()} median {int(np.median(counts))} max {counts.max()}", flush=True)
     ids, w = oracle.route(L.logits, L.k)
+    assert np.array_equal(r.ids.cpu().numpy(), ids), "top-k ids differ from the oracle"
     ref = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w,
-                         tokens=toks, nthreads=NTHREADS, fmt="mxfp4")
-    assert_close(y.cpu().numpy()[toks], ref, "mx prefill 2048 sampled")
+                         nthreads=NTHREADS, fmt="mxfp4")
+    rel = assert_close(y.cpu().numpy(), ref, "mx prefill 2048 all tokens")
+    print(f"mx prefill 2048 rel L2 {rel:.2e}")
 
 
 def test_mx_prefill_odd_shapes():
