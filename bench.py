@@ -213,6 +213,24 @@ def run_gpu(inp, steps: int, warmup: int):
     torch.cuda.synchronize()
     route_ms = ev0.elapsed_time(ev1) / steps
 
+    # intermediate-axis slice check (decode): the last step's routing through the two I/2 slices of the bank,
+    # run one after the other on this GPU, the second accumulating into the first; the sum against the full-I
+    # output of the same step (bank copy 0 holds the same bytes as every other copy)
+    slice_check = None
+    if T <= 16 and I % 64 == 0:
+        slicer = dl.mx_slice_bank if fmt == "mxfp4" else dl.slice_bank
+        r_last = routes[total - 1]
+        acc = torch.empty((T, H), dtype=torch.float32, device=dev)
+        for rr in range(2):
+            part = dl.DeviceLayer(H, I // 2, E, k, slicer(bank[:nslot], H, I, rr, 2), maps[0].contiguous(), E, wg, fmt)
+            dl.forward(part, xs[total - 1], r_last, y=acc, accumulate=rr > 0)
+        torch.cuda.synchronize()
+        full = y[total - 1].double()
+        diff = acc.double() - full
+        slice_check = {"I_local": I // 2, "slices": 2,
+                       "rel_l2_vs_full": float(diff.norm() / full.norm()),
+                       "max_abs_err_over_max_abs": float(diff.abs().max() / full.abs().max())}
+
     distinct = []
     for i in range(warmup, total):
         off = routes[i].offsets.cpu().numpy()
@@ -220,7 +238,7 @@ def run_gpu(inp, steps: int, warmup: int):
     counts = np.diff(routes[total - 1].offsets.cpu().numpy())
     return dict(wall=wall, fwd_ms=fwd_ms, call_ms=call_ms, route_ms=route_ms, distinct=distinct, replay_ok=replay_ok,
                 y_last=y[total - 1].cpu().numpy(), ids_last=routes[total - 1].ids.cpu().numpy(),
-                counts_max=int(counts.max()), counts_min=int(counts.min()))
+                counts_max=int(counts.max()), counts_min=int(counts.min()), slice_check=slice_check)
 
 
 # ---------------------------------------------------------------- CPU baseline (the oracle)
@@ -324,7 +342,6 @@ def parity_sample(inp, res, tokens):
     """Relative L2 error of the last timed step's output against the oracle (a few tokens)."""
     import oracle
     H, I, E, k, T = inp["H"], inp["I"], inp["E"], inp["k"], inp["T"]
-    s = len(inp["xs"]) - 1 if False else None
     last = res["last_index"]
     x = inp["xs"][last]
     lg = inp["logits"][last]
@@ -568,15 +585,17 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic(name, "mxfp4"),
                 "kernel": "moe_mxfp4_route_forward decode call (mx_fused_kernel or mx_wave_kernel, routing in "
-                          "the prologue up to 8 tokens: gate_up on v_mfma_scale_f32_16x16x128_f8f6f4, down on "
-                          "v_mfma_f32_16x16x32_bf16; then dcombine_kernel), timed together with HIP events",
+                          "the prologue up to 8 tokens and in route_small_kernel above: gate_up on "
+                          "v_mfma_scale_f32_16x16x128_f8f6f4, down on v_mfma_f32_16x16x32_bf16; then "
+                          "dcombine_kernel), timed together with HIP events",
                 "per_launch": f"{bytes_fwd / 1e6:.2f} MB expert weights per forward ((D+1) x {sb} B, "
                               f"mean D = {mean_d:.2f})"}
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic(name, "decode"),
-                "kernel": "moe_nvfp4_route_forward decode call (fused_kernel or wave_kernel with the routing in "
-                          "its prologue, then dcombine_kernel), timed together with HIP events",
+                "kernel": "moe_nvfp4_route_forward decode call (up to 8 tokens fused_kernel routes in its "
+                          "prologue; above, route_small_kernel then wave_kernel; then dcombine_kernel), "
+                          "timed together with HIP events",
                 "per_launch": f"{bytes_fwd / 1e6:.2f} MB expert weights per forward ((D+1) x {sb} B, "
                               f"mean D = {mean_d:.2f})"}
     out = {
@@ -594,6 +613,8 @@ def bench_config(name: str, steps: int, warmup: int, replicas: int, distinct: in
                   "expert_weight_GBps_step": round(bytes_fwd / (ms_step * 1e-3) / 1e9, 1),
                   "graph_replay_matches_eager": bool(res["replay_ok"])},
     }
+    if res["slice_check"] is not None:
+        out["slice_check"] = res["slice_check"]
     if prefill:
         out["layer"]["forward_TFLOPs"] = round(flops / fwd_s / 1e12, 2)
         out["layer"]["expert_count_range"] = [res["counts_min"], res["counts_max"]]
