@@ -10,7 +10,8 @@
 // itself, so gate_up needs no decode on the vector ALUs at all.
 //
 // Work item = (expert, 32-row slice of I), one wave per item (as the NVFP4
-// wave kernel):
+// wave kernel; 64-row slices when 32-row items would outnumber the waves,
+// which halves the items and their partial sums):
 //   gate_up  16-row x 128-column records (lane 16a + i: row i, the 32
 //            columns [32a, 32a + 32), i.e. one scale block) are the A operand
 //            of the scaled MFMA as loaded; the activations are its B operand
@@ -19,7 +20,7 @@
 //            bits split 4 + 4, so the product is exact up to fp32 summation);
 //   SwiGLU   h = silu(gate) * up in fp32, then two bf16 terms (h_hi + h_lo
 //            carries 16 significant bits);
-//   down     the slice's 32 columns of every row: 64-row x 32-column records
+//   down     the slice's 32 (or 64) columns of every row: 64-row x 32-column records
 //            decoded exactly to bf16 by v_cvt_scalef32_pk_bf16_fp4, which
 //            applies the block's E8M0 scale in the conversion (e2m1 * 2^e is
 //            exact in bf16 for every E8M0 value), into
@@ -167,29 +168,44 @@ struct MxRing {
     uint32_t sc[8];
 };
 
-// gate_up group ga: chunks q = 2 ga, 2 ga + 1, each the slice's two gate and two up tiles (entry 4 (q & 1) + r).
+// Item geometry for SL intermediate rows (32 or 64): the slice has NTT gate tiles (rows SL s + 16 r) and the NTT
+// matching up tiles; a gate_up group is 8 records, CPG chunks of 128 columns of the 2 NTT tiles; the slice's SL
+// down columns are CH chunks of 32, and a down group is RGG row groups of 64 times those CH chunks.
+template <int SL>
+struct MxGeom {
+    static constexpr int NTT = SL / 16;
+    static constexpr int CPG = 4 / NTT;
+    static constexpr int CH = SL / 32;
+    static constexpr int RGG = 8 / CH;
+};
+
+// gate_up group ga: chunks q = CPG ga + qq, each the slice's NTT gate and NTT up tiles (entry 2 NTT qq + r).
+template <int SL>
 __device__ __forceinline__ void mx_issue_a(const DecArgs& a, const Item& it, int ga, int lane, MxRing& R) {
+    using G = MxGeom<SL>;
     const int KQ = a.H / 128, NT = 2 * a.I / 16, up = a.I / 16;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        const int q = 2 * ga + qq;
+    for (int qq = 0; qq < G::CPG; ++qq) {
+        const int q = G::CPG * ga + qq;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int rec = q * NT + (r < 2 ? 0 : up) + 2 * it.s + (r & 1);
-            R.cd[4 * qq + r] = buf_load16(it.sres, q < KQ ? a.gu_codes + rec * kRecBytes + 16 * lane : kOob);
-            R.sc[4 * qq + r] = __builtin_amdgcn_raw_buffer_load_b8(it.sres, q < KQ ? a.gu_scales + rec * 64 + lane
-                                                                                    : kOob, 0, 0);
+        for (int r = 0; r < 2 * G::NTT; ++r) {
+            const int rec = q * NT + (r < G::NTT ? 0 : up) + G::NTT * it.s + r % G::NTT;
+            R.cd[2 * G::NTT * qq + r] = buf_load16(it.sres, q < KQ ? a.gu_codes + rec * kRecBytes + 16 * lane : kOob);
+            R.sc[2 * G::NTT * qq + r] = __builtin_amdgcn_raw_buffer_load_b8(
+                it.sres, q < KQ ? a.gu_scales + rec * 64 + lane : kOob, 0, 0);
         }
     }
 }
 
-// down group gb: records (chunk s, row group 8 gb + r), entry r.
+// down group gb: records (chunk CH s + r % CH, row group RGG gb + r / CH), entry r.
+template <int SL>
 __device__ __forceinline__ void mx_issue_b(const DecArgs& a, const Item& it, int gb, int lane, MxRing& R) {
+    using G = MxGeom<SL>;
     const int NG = a.H / 64;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-        const int p = 8 * gb + r;
-        const int rec = it.s * NG + p;
+        const int p = G::RGG * gb + r / G::CH;
+        const int rec = (G::CH * it.s + r % G::CH) * NG + p;
         R.cd[r] = buf_load16(it.sres, p < NG ? a.dn_codes + rec * kRecBytes + 16 * lane : kOob);
         R.sc[r] = buf_load4(it.sres, p < NG ? a.dn_scales + rec * 64 + 4 * (lane & 15) : kOob);
     }
@@ -208,21 +224,23 @@ __device__ __forceinline__ void mx_x_operand(const uint8_t* xs, int T, int NB, i
     sl = srow[(T + 1) * NB + row * NB + 4 * q + g];
 }
 
+template <int SL>
 __device__ __forceinline__ void mx_compute_a(const DecArgs& a, const MxRing& R, int ga, const uint8_t* xs, int row,
-                                             int g, f32x4_t (&acc)[4]) {
+                                             int g, f32x4_t (&acc)[2 * MxGeom<SL>::NTT]) {
+    using G = MxGeom<SL>;
     const int KQ = a.H / 128, NB = a.H / 32;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        const int q = 2 * ga + qq;
+    for (int qq = 0; qq < G::CPG; ++qq) {
+        const int q = G::CPG * ga + qq;
         if (q >= KQ) continue;  // uniform: a padded chunk
         v8i_t bh, bl;
         int sh, sl;
         mx_x_operand(xs, a.T, NB, row, q, g, bh, bl, sh, sl);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const u32x4_t c = R.cd[4 * qq + r];
+        for (int r = 0; r < 2 * G::NTT; ++r) {
+            const u32x4_t c = R.cd[2 * G::NTT * qq + r];
             const v8i_t A = v8i_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-            const int sa = (int)R.sc[4 * qq + r];
+            const int sa = (int)R.sc[2 * G::NTT * qq + r];
             acc[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, bh, acc[r], 4, 0, 0, sa, 0, sh);
             acc[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, bl, acc[r], 4, 0, 0, sa, 0, sl);
         }
@@ -242,17 +260,26 @@ __device__ __forceinline__ bf16x8_t mx_down_frag(uint32_t code_word, uint32_t sc
     return __builtin_bit_cast(bf16x8_t, u);
 }
 
-__device__ __forceinline__ void mx_compute_b(const DecArgs& a, const MxRing& R, int gb, const bf16x8_t& Bh,
-                                             const bf16x8_t& Bl, float wc, const rsrc_t& pres, int pbase) {
+// The group's row groups: each 16-row tile j summed over the slice's CH column chunks, then stored.
+template <int SL>
+__device__ __forceinline__ void mx_compute_b(const DecArgs& a, const MxRing& R, int gb,
+                                             const bf16x8_t (&Bh)[MxGeom<SL>::CH], const bf16x8_t (&Bl)[MxGeom<SL>::CH],
+                                             float wc, const rsrc_t& pres, int pbase) {
+    using G = MxGeom<SL>;
     const int NG = a.H / 64;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int p = 8 * gb + r;
+    for (int rg = 0; rg < G::RGG; ++rg) {
+        const int p = G::RGG * gb + rg;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bf16x8_t A = mx_down_frag(word_of(R.cd[r], j), R.sc[r], j);
-            f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bh, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl, D, 0, 0, 0);
+            f32x4_t D = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int cc = 0; cc < G::CH; ++cc) {
+                const int r = G::CH * rg + cc;
+                const bf16x8_t A = mx_down_frag(word_of(R.cd[r], j), R.sc[r], j);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bh[cc], D, 0, 0, 0);
+                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl[cc], D, 0, 0, 0);
+            }
             buf_store16(pres, p < NG ? pbase + 4 * (64 * p + 16 * j) : kOob, D * wc);
         }
     }
@@ -260,8 +287,10 @@ __device__ __forceinline__ void mx_compute_b(const DecArgs& a, const MxRing& R, 
 
 // Persistent over items v = wave * grid + block + j * 8 * grid.  MULTI: some wave has more than one item.
 // ROUTE: the kernel routes the tokens itself in its prologue (from a.logits) and writes the routing outputs.
-template <bool MULTI, bool ROUTE>
+// SL: rows per item, 32, or 64 when 32-row items would outnumber the waves (half the items and partial sums).
+template <int SL, bool MULTI, bool ROUTE>
 __global__ void __launch_bounds__(kMT) mx_wave_kernel(DecArgs a, int nsl) {
+    using G = MxGeom<SL>;
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
     __shared__ Tables tb;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -274,14 +303,14 @@ __global__ void __launch_bounds__(kMT) mx_wave_kernel(DecArgs a, int nsl) {
     int v = __builtin_amdgcn_readfirstlane(wave * (int)gridDim.x + (int)blockIdx.x);
     const int c = lane & 15, g = lane >> 4;
     const int KQ = H / 128, NG = H / 64;
-    const int NGA = (KQ + 1) / 2;   // gate_up groups of two chunks
-    const int NGB = (NG + 7) / 8;   // down groups of eight row groups
+    const int NGA = (KQ + G::CPG - 1) / G::CPG;  // gate_up groups of CPG chunks
+    const int NGB = (NG + G::RGG - 1) / G::RGG;  // down groups of RGG row groups
     const rsrc_t pres = make_rsrc(a.part, (uint32_t)((size_t)(T * k + T) * nsl * H * 4));
 
     Item cur = decode_item(a, tb, n_act, nsl, v, v < n_items, c);
     MxRing R0, R1;
-    mx_issue_a(a, cur, 0, lane, R0);
-    mx_issue_a(a, cur, 1, lane, R1);
+    mx_issue_a<SL>(a, cur, 0, lane, R0);
+    mx_issue_a<SL>(a, cur, 1, lane, R1);
     __builtin_amdgcn_sched_barrier(0);
     mx_stage_x(a, xv, xs, tid, lane, wave);
     __syncthreads();
@@ -291,40 +320,43 @@ __global__ void __launch_bounds__(kMT) mx_wave_kernel(DecArgs a, int nsl) {
         const int row = cur.tok >= 0 ? cur.tok : T;
 
         // ---- gate_up on the scaled matrix cores: the slice's two gate and two up tiles over all of K
-        f32x4_t acc[4];
+        f32x4_t acc[2 * G::NTT];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int r = 0; r < 2 * G::NTT; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         int ga = 0;
         for (; ga + 2 < NGA; ga += 2) {
-            mx_compute_a(a, R0, ga, xs, row, g, acc);
+            mx_compute_a<SL>(a, R0, ga, xs, row, g, acc);
             __builtin_amdgcn_sched_barrier(0);
-            mx_issue_a(a, cur, ga + 2, lane, R0);
+            mx_issue_a<SL>(a, cur, ga + 2, lane, R0);
             __builtin_amdgcn_sched_barrier(0);
-            mx_compute_a(a, R1, ga + 1, xs, row, g, acc);
+            mx_compute_a<SL>(a, R1, ga + 1, xs, row, g, acc);
             __builtin_amdgcn_sched_barrier(0);
-            mx_issue_a(a, cur, ga + 3, lane, R1);
+            mx_issue_a<SL>(a, cur, ga + 3, lane, R1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        mx_compute_a(a, R0, ga, xs, row, g, acc);
+        mx_compute_a<SL>(a, R0, ga, xs, row, g, acc);
         __builtin_amdgcn_sched_barrier(0);
-        mx_issue_b(a, cur, 0, lane, R0);
+        mx_issue_b<SL>(a, cur, 0, lane, R0);
         __builtin_amdgcn_sched_barrier(0);
-        mx_compute_a(a, R1, ga + 1, xs, row, g, acc);
+        mx_compute_a<SL>(a, R1, ga + 1, xs, row, g, acc);
         __builtin_amdgcn_sched_barrier(0);
-        mx_issue_b(a, cur, 1, lane, R1);
+        mx_issue_b<SL>(a, cur, 1, lane, R1);
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- SwiGLU on this lane's rows 4g + [0, 4) of tiles 0 and 1 (token c), then the down operand:
-        // lane (c, g') needs slice rows 8g' + [0, 8): tile g' / 2, from lanes (c, 2 (g' & 1)) and (c, 2 (g' & 1) + 1)
-        bf16x8_t Bh, Bl;
-        {
+        // ---- SwiGLU on this lane's rows 4g + [0, 4) of each tile (token c), then the down operand of each
+        // 32-column chunk cc (tiles 2 cc and 2 cc + 1): lane (c, g') needs chunk rows 8g' + [0, 8): tile g' / 2 of
+        // the pair, from lanes (c, 2 (g' & 1)) and (c, 2 (g' & 1) + 1)
+        bf16x8_t Bh[G::CH], Bl[G::CH];
+#pragma unroll
+        for (int cc = 0; cc < G::CH; ++cc) {
             uint32_t PH[2][2], PL[2][2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int d = 0; d < 2; ++d) {
-                    const float h0 = silu_fast(acc[tt][2 * d]) * acc[2 + tt][2 * d];
-                    const float h1 = silu_fast(acc[tt][2 * d + 1]) * acc[2 + tt][2 * d + 1];
+                    const int gt = 2 * cc + tt;
+                    const float h0 = silu_fast(acc[gt][2 * d]) * acc[G::NTT + gt][2 * d];
+                    const float h1 = silu_fast(acc[gt][2 * d + 1]) * acc[G::NTT + gt][2 * d + 1];
                     split_bf16x2(h0, h1, PH[tt][d], PL[tt][d]);
                 }
             const int src0 = c + 32 * (g & 1), src1 = src0 + 16;
@@ -345,34 +377,34 @@ __global__ void __launch_bounds__(kMT) mx_wave_kernel(DecArgs a, int nsl) {
                 bl[d] = hi ? l10 : l00;
                 bl[2 + d] = hi ? l11 : l01;
             }
-            Bh = __builtin_bit_cast(bf16x8_t, u32x4_t{bh[0], bh[1], bh[2], bh[3]});
-            Bl = __builtin_bit_cast(bf16x8_t, u32x4_t{bl[0], bl[1], bl[2], bl[3]});
+            Bh[cc] = __builtin_bit_cast(bf16x8_t, u32x4_t{bh[0], bh[1], bh[2], bh[3]});
+            Bl[cc] = __builtin_bit_cast(bf16x8_t, u32x4_t{bl[0], bl[1], bl[2], bl[3]});
         }
 
-        // ---- down: the slice's 32 columns of all H rows, partial sums times the routing weight
+        // ---- down: the slice's SL columns of all H rows, partial sums times the routing weight
         const int pbase = c < cur.ne ? 4 * ((cur.prow * nsl + cur.s) * H + 4 * g) : kOob;
         int gb = 0;
         for (; gb + 2 < NGB; gb += 2) {
-            mx_compute_b(a, R0, gb, Bh, Bl, cur.wc, pres, pbase);
+            mx_compute_b<SL>(a, R0, gb, Bh, Bl, cur.wc, pres, pbase);
             __builtin_amdgcn_sched_barrier(0);
-            mx_issue_b(a, cur, gb + 2, lane, R0);
+            mx_issue_b<SL>(a, cur, gb + 2, lane, R0);
             __builtin_amdgcn_sched_barrier(0);
-            mx_compute_b(a, R1, gb + 1, Bh, Bl, cur.wc, pres, pbase);
+            mx_compute_b<SL>(a, R1, gb + 1, Bh, Bl, cur.wc, pres, pbase);
             __builtin_amdgcn_sched_barrier(0);
-            mx_issue_b(a, cur, gb + 3, lane, R1);
+            mx_issue_b<SL>(a, cur, gb + 3, lane, R1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        mx_compute_b(a, R0, gb, Bh, Bl, cur.wc, pres, pbase);
+        mx_compute_b<SL>(a, R0, gb, Bh, Bl, cur.wc, pres, pbase);
         if (!MULTI) {
-            mx_compute_b(a, R1, gb + 1, Bh, Bl, cur.wc, pres, pbase);
+            mx_compute_b<SL>(a, R1, gb + 1, Bh, Bl, cur.wc, pres, pbase);
             break;
         }
         __builtin_amdgcn_sched_barrier(0);
-        mx_issue_a(a, nxt, 0, lane, R0);
+        mx_issue_a<SL>(a, nxt, 0, lane, R0);
         __builtin_amdgcn_sched_barrier(0);
-        mx_compute_b(a, R1, gb + 1, Bh, Bl, cur.wc, pres, pbase);
+        mx_compute_b<SL>(a, R1, gb + 1, Bh, Bl, cur.wc, pres, pbase);
         __builtin_amdgcn_sched_barrier(0);
-        mx_issue_a(a, nxt, 1, lane, R1);
+        mx_issue_a<SL>(a, nxt, 1, lane, R1);
         __builtin_amdgcn_sched_barrier(0);
         cur = nxt;
         v += stride;
@@ -602,20 +634,34 @@ hipError_t mx_device_cus(int& ncu) {
 bool mx_decode_shape_supported(int H, int I) { return H % 128 == 0 && I % 32 == 0 && H <= 2560; }
 
 namespace {
-template <bool ROUTE>
-hipError_t launch_mx_kernels(const DecArgs& a, int items_max, int nsl, int ncu, size_t lds, hipStream_t s) {
+template <int SL, bool ROUTE>
+hipError_t launch_mx_wave(const DecArgs& a, int items_max, int nsl, int grid, size_t lds, hipStream_t s) {
     hipError_t e;
-    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<true, ROUTE>))) != hipSuccess) return e;
-    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<false, ROUTE>))) != hipSuccess) return e;
-    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_fused_kernel<ROUTE>))) != hipSuccess) return e;
-    const int grid = items_max < ncu ? items_max : ncu;
-    if (items_max <= ncu)  // one item per workgroup, shared by its waves
-        hipLaunchKernelGGL(mx_fused_kernel<ROUTE>, dim3(items_max), dim3(kMT), lds, s, a, nsl);
-    else if (items_max > grid * kMW)
-        hipLaunchKernelGGL((mx_wave_kernel<true, ROUTE>), dim3(grid), dim3(kMT), lds, s, a, nsl);
+    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<SL, true, ROUTE>))) != hipSuccess) return e;
+    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<SL, false, ROUTE>))) != hipSuccess) return e;
+    if (items_max > grid * kMW)
+        hipLaunchKernelGGL((mx_wave_kernel<SL, true, ROUTE>), dim3(grid), dim3(kMT), lds, s, a, nsl);
     else
-        hipLaunchKernelGGL((mx_wave_kernel<false, ROUTE>), dim3(grid), dim3(kMT), lds, s, a, nsl);
+        hipLaunchKernelGGL((mx_wave_kernel<SL, false, ROUTE>), dim3(grid), dim3(kMT), lds, s, a, nsl);
     return hipGetLastError();
+}
+
+// rows_max: most routed rows plus the shared expert's.  nsl (out): slices per expert of the items launched.
+template <bool ROUTE>
+hipError_t launch_mx_kernels(const DecArgs& a, int rows_max, int I, int& nsl, int ncu, size_t lds, hipStream_t s) {
+    hipError_t e;
+    nsl = I / 32;
+    const int items_max = rows_max * nsl;
+    if (items_max <= ncu) {  // one item per workgroup, shared by its waves
+        if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_fused_kernel<ROUTE>))) != hipSuccess) return e;
+        hipLaunchKernelGGL(mx_fused_kernel<ROUTE>, dim3(items_max), dim3(kMT), lds, s, a, nsl);
+        return hipGetLastError();
+    }
+    if (items_max > ncu * kMW && I % 64 == 0) {  // 32-row items would outnumber the waves: 64-row items
+        nsl = I / 64;
+        return launch_mx_wave<64, ROUTE>(a, rows_max * nsl, nsl, ncu, lds, s);
+    }
+    return launch_mx_wave<32, ROUTE>(a, items_max, nsl, ncu, lds, s);
 }
 }  // namespace
 
@@ -648,12 +694,11 @@ hipError_t launch_mx_decode(const Layer& L, const uint16_t* x, int T, const floa
     int ncu = 0;
     hipError_t e = mx_device_cus(ncu);
     if (e != hipSuccess) return e;
-    const int nsl = I / 32;
+    int nsl = 0;
     const int rows_max = (T * k < E ? T * k : E) + 1;
-    const int items_max = rows_max * nsl;
     const size_t lds = mx_lds_bytes(T, H);
-    e = route ? launch_mx_kernels<true>(a, items_max, nsl, ncu, lds, s)
-              : launch_mx_kernels<false>(a, items_max, nsl, ncu, lds, s);
+    e = route ? launch_mx_kernels<true>(a, rows_max, I, nsl, ncu, lds, s)
+              : launch_mx_kernels<false>(a, rows_max, I, nsl, ncu, lds, s);
     if (e != hipSuccess) return e;
     const int nch = H / 64;
     if (nsl <= 10) hipLaunchKernelGGL(dcombine_kernel<10>, dim3(T * nch), dim3(256), 0, s, a, nsl, nch);

@@ -180,17 +180,17 @@ def test_mx_route_forward_matches_route_then_forward(mx_layer, T):
 
 
 @pytest.mark.parametrize("T", [14, 16])
-def test_mx_decode_leftover_items_run_together(mx_layer, T):
-    """Every token routed to 8 experts of its own: 8T active experts plus the shared one, in 32-row items (20 per
-    expert): 2,260 items at T=14 and 2,580 at T=16, against one item per wave (2,048), so 212 or 532 waves run a
-    second item after their first (the persistent wave kernel's multi-item path)."""
+def test_mx_decode_distinct_experts_per_token(mx_layer, T):
+    """Every token routed to 8 experts of its own: 8T active experts plus the shared one.  As 32-row items (20 per
+    expert) they would be 2,260 at T=14 and 2,580 at T=16, more than one per wave (2,048), so the kernel runs
+    64-row items: 1,130 and 1,290, one per wave."""
     xb, lg = synth.fresh_tokens(1700 + T, T, mx_layer.H, mx_layer.E, "uniform")
     lg = lg.copy()
     for t in range(T):
         lg[t, 8 * t:8 * t + 8] = 2.0 + np.arange(8, dtype=np.float32) * 0.125
     L = synth.LayerInputs(mx_layer.H, mx_layer.I, mx_layer.E, mx_layer.k, T, mx_layer.bank, mx_layer.slot_of_expert,
                           mx_layer.shared_slot, mx_layer.wg, xb, lg)
-    _announce(f"mxfp4 decode leftover items, T={T}, {8 * T} distinct experts + shared")
+    _announce(f"mxfp4 decode, T={T}, {8 * T} distinct experts + shared")
     ids, w = oracle.route(L.logits, L.k)
     assert len(np.unique(ids)) == 8 * T
     dev = device_layer(L, "mxfp4")
@@ -202,8 +202,38 @@ def test_mx_decode_leftover_items_run_together(mx_layer, T):
     assert np.array_equal(y.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32)), "not bit-reproducible"
     ref = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w,
                          nthreads=NTHREADS, fmt="mxfp4")
-    rel = assert_close(y.cpu().numpy(), ref, f"mx leftover items T={T}")
-    print(f"mx leftover T={T} rel L2 {rel:.2e}")
+    rel = assert_close(y.cpu().numpy(), ref, f"mx distinct experts T={T}")
+    print(f"mx distinct experts T={T} rel L2 {rel:.2e}")
+
+
+@pytest.mark.parametrize("I", [1280, 672])
+def test_mx_decode_second_items_per_wave(I):
+    """16 tokens on 8 experts each of their own (128 + the shared expert) at H=1024: I=1280 gives 2,580 items of 64
+    rows and I=672 (not a multiple of 64) 2,709 items of 32 rows, both more than the 2,048 waves, so waves run a
+    second item after their first (the persistent wave kernel's multi-item path, for both item heights)."""
+    H, E, k, T = 1024, 128, 8, 16
+    r_w, r_x, r_l, r_g = np.random.default_rng(4000 + I).spawn(4)
+    bank = synth.make_bank(r_w, H, I, E + 1, n_distinct=8, fmt="mxfp4")
+    x = synth.f32_to_bf16_bits(r_x.standard_normal((T, H), dtype=np.float32))
+    lg = r_l.random((T, E), dtype=np.float32)
+    for t in range(T):
+        lg[t, 8 * t:8 * t + 8] = 2.0 + np.arange(8, dtype=np.float32) * 0.125
+    wg = synth.f32_to_bf16_bits(r_g.standard_normal(H, dtype=np.float32) * np.float32(0.02))
+    L = synth.LayerInputs(H, I, E, k, T, bank, np.arange(E, dtype=np.int32), E, wg, x, lg)
+    _announce(f"mxfp4 decode second items, H={H} I={I} T={T}")
+    ids, w = oracle.route(L.logits, L.k)
+    assert len(np.unique(ids)) == 8 * T
+    dev = device_layer(L, "mxfp4")
+    r = dl.route(device_logits(L), L.k)
+    y = dl.forward(dev, device_x(L), r)
+    y2 = dl.forward(dev, device_x(L), r)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.ids.cpu().numpy(), ids)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32)), "not bit-reproducible"
+    ref = oracle.forward(L.H, L.I, L.E, L.k, L.bank, L.slot_of_expert, L.shared_slot, L.wg, L.x, ids, w,
+                         nthreads=NTHREADS, fmt="mxfp4")
+    rel = assert_close(y.cpu().numpy(), ref, f"mx second items I={I}")
+    print(f"mx second items I={I} rel L2 {rel:.2e}")
 
 
 def test_mx_forward_refuses_wrong_slot_size_and_small_workspace(mx_layer):
