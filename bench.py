@@ -48,8 +48,8 @@ DTYPE_MX_PREFILL = "mxfp4w-bf16mfma-bf16x2h-fp32acc"  # MXFP4 prefill: weights d
 # kernels and scaled by what the same counters read for a plain copy of known size), with a digest of the kernel
 # sources they were taken on.  Reported as roofline.traffic only while those sources are unchanged.
 COUNTED_TRAFFIC = {
-    "decode_bs1": (29_530_271, "a4931601b49db091"),
-    "decode_bs16": (319_183_108, "a4931601b49db091"),
+    "decode_bs1": (29_530_115, "a4931601b49db091"),
+    "decode_bs16": (319_185_524, "a4931601b49db091"),
     "prefill_2048": (1_180_886_918, "6284de10fb5c8ffc"),
     "mxfp4_decode_bs1": (27_780_741, "835aeae1b974f739"),
     "mxfp4_decode_bs16": (301_277_280, "835aeae1b974f739"),
