@@ -51,8 +51,8 @@ COUNTED_TRAFFIC = {
     "decode_bs1": (29_530_115, "a4931601b49db091"),
     "decode_bs16": (319_185_524, "a4931601b49db091"),
     "prefill_2048": (1_180_886_918, "6284de10fb5c8ffc"),
-    "mxfp4_decode_bs1": (27_780_741, "835aeae1b974f739"),
-    "mxfp4_decode_bs16": (301_277_280, "835aeae1b974f739"),
+    "mxfp4_decode_bs1": (27_784_280, "ba5cf7dc0aa7c44f"),
+    "mxfp4_decode_bs16": (301_502_598, "ba5cf7dc0aa7c44f"),
     "mxfp4_prefill_2048": (1_177_178_029, "6284de10fb5c8ffc"),
 }
 KERNEL_SOURCES = {"decode": ["decode.hip", "decode_common.hpp", "route_device.hpp", "nvfp4_device.hpp"],

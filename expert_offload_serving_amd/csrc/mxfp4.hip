@@ -285,14 +285,70 @@ __device__ __forceinline__ void mx_compute_b(const DecArgs& a, const MxRing& R, 
     }
 }
 
+// SwiGLU on this lane's rows 4g + [0, 4) of each tile (token c), then the down operand of each 32-column chunk
+// cc (tiles 2 cc and 2 cc + 1): lane (c, g') needs chunk rows 8g' + [0, 8): tile g' / 2 of the pair, from lanes
+// (c, 2 (g' & 1)) and (c, 2 (g' & 1) + 1)
+template <int SL>
+__device__ __forceinline__ void mx_swiglu(const f32x4_t (&acc)[2 * MxGeom<SL>::NTT], int c, int g,
+                                          bf16x8_t (&Bh)[MxGeom<SL>::CH], bf16x8_t (&Bl)[MxGeom<SL>::CH]) {
+    using G = MxGeom<SL>;
+#pragma unroll
+    for (int cc = 0; cc < G::CH; ++cc) {
+        uint32_t PH[2][2], PL[2][2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const int gt = 2 * cc + tt;
+                const float h0 = silu_fast(acc[gt][2 * d]) * acc[G::NTT + gt][2 * d];
+                const float h1 = silu_fast(acc[gt][2 * d + 1]) * acc[G::NTT + gt][2 * d + 1];
+                split_bf16x2(h0, h1, PH[tt][d], PL[tt][d]);
+            }
+        const int src0 = c + 32 * (g & 1), src1 = src0 + 16;
+        const bool hi = g >= 2;
+        uint32_t bh[4], bl[4];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const uint32_t h00 = (uint32_t)__shfl((int)PH[0][d], src0, kWave);
+            const uint32_t h10 = (uint32_t)__shfl((int)PH[1][d], src0, kWave);
+            const uint32_t h01 = (uint32_t)__shfl((int)PH[0][d], src1, kWave);
+            const uint32_t h11 = (uint32_t)__shfl((int)PH[1][d], src1, kWave);
+            const uint32_t l00 = (uint32_t)__shfl((int)PL[0][d], src0, kWave);
+            const uint32_t l10 = (uint32_t)__shfl((int)PL[1][d], src0, kWave);
+            const uint32_t l01 = (uint32_t)__shfl((int)PL[0][d], src1, kWave);
+            const uint32_t l11 = (uint32_t)__shfl((int)PL[1][d], src1, kWave);
+            bh[d] = hi ? h10 : h00;
+            bh[2 + d] = hi ? h11 : h01;
+            bl[d] = hi ? l10 : l00;
+            bl[2 + d] = hi ? l11 : l01;
+        }
+        Bh[cc] = __builtin_bit_cast(bf16x8_t, u32x4_t{bh[0], bh[1], bh[2], bh[3]});
+        Bl[cc] = __builtin_bit_cast(bf16x8_t, u32x4_t{bl[0], bl[1], bl[2], bl[3]});
+    }
+}
+
+constexpr int kMU = 4;  // waves per workgroup that take items of their own under COOP: one per SIMD
+
+// Spin on an LDS counter until it reaches target (every wave it waits for is in this workgroup and arrives).
+__device__ __forceinline__ void mx_lds_wait_count(int* p, int target) {
+    while (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) __builtin_amdgcn_s_sleep(1);
+}
+
 // Persistent over items v = wave * grid + block + j * 8 * grid.  MULTI: some wave has more than one item.
 // ROUTE: the kernel routes the tokens itself in its prologue (from a.logits) and writes the routing outputs.
 // SL: rows per item, 32, or 64 when 32-row items would outnumber the waves (half the items and partial sums).
-template <int SL, bool MULTI, bool ROUTE>
+// COOP (with !MULTI): only the first kMU waves of a workgroup take items of their own; each item past kMU per
+// workgroup (a leftover) is run by the other kMU waves of one workgroup together, beside the first waves' items
+// from the start: wave kMU + w streams the gate_up groups w, w + kMU, ... and the down groups w, w + kMU, ...,
+// and the gate_up partial sums meet in LDS, added in wave order, before SwiGLU.  (A leftover run by one wave
+// would share one SIMD with another item for the whole call.)
+template <int SL, bool MULTI, bool ROUTE, bool COOP = false>
 __global__ void __launch_bounds__(kMT) mx_wave_kernel(DecArgs a, int nsl) {
     using G = MxGeom<SL>;
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
     __shared__ Tables tb;
+    __shared__ f32x4_t coop_red[COOP ? kMU : 1][COOP ? 2 * G::NTT : 1][kWave];
+    __shared__ int coop_cnt[2];  // partial sums written, partial sums read (counted per wave, never reset)
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int H = a.H, T = a.T, k = a.k;
     XRegs<kMW> xv;
@@ -300,7 +356,8 @@ __global__ void __launch_bounds__(kMT) mx_wave_kernel(DecArgs a, int nsl) {
                             : stage_tables<kMW>(a, tb, xv, tid, lane, wave);
     const int n_items = (n_act + (a.shared != nullptr ? 1 : 0)) * nsl;
     const int stride = (int)gridDim.x * kMW;
-    int v = __builtin_amdgcn_readfirstlane(wave * (int)gridDim.x + (int)blockIdx.x);
+    int v = __builtin_amdgcn_readfirstlane(COOP && wave >= kMU ? n_items : wave * (int)gridDim.x + (int)blockIdx.x);
+    if (COOP && tid < 2) coop_cnt[tid] = 0;
     const int c = lane & 15, g = lane >> 4;
     const int KQ = H / 128, NG = H / 64;
     const int NGA = (KQ + G::CPG - 1) / G::CPG;  // gate_up groups of CPG chunks
@@ -314,8 +371,9 @@ __global__ void __launch_bounds__(kMT) mx_wave_kernel(DecArgs a, int nsl) {
     __builtin_amdgcn_sched_barrier(0);
     mx_stage_x(a, xv, xs, tid, lane, wave);
     __syncthreads();
-    if (v >= n_items) return;  // uniform per wave; no barrier follows
-    do {
+    const bool coop_wave = COOP && wave >= kMU;  // runs leftover items, none of its own
+    if (v >= n_items && !coop_wave) return;      // uniform per wave; no barrier follows
+    if (v < n_items) do {
         const Item nxt = decode_item(a, tb, n_act, nsl, v + stride, MULTI && v + stride < n_items, c);
         const int row = cur.tok >= 0 ? cur.tok : T;
 
@@ -343,43 +401,8 @@ __global__ void __launch_bounds__(kMT) mx_wave_kernel(DecArgs a, int nsl) {
         mx_issue_b<SL>(a, cur, 1, lane, R1);
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- SwiGLU on this lane's rows 4g + [0, 4) of each tile (token c), then the down operand of each
-        // 32-column chunk cc (tiles 2 cc and 2 cc + 1): lane (c, g') needs chunk rows 8g' + [0, 8): tile g' / 2 of
-        // the pair, from lanes (c, 2 (g' & 1)) and (c, 2 (g' & 1) + 1)
         bf16x8_t Bh[G::CH], Bl[G::CH];
-#pragma unroll
-        for (int cc = 0; cc < G::CH; ++cc) {
-            uint32_t PH[2][2], PL[2][2];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int d = 0; d < 2; ++d) {
-                    const int gt = 2 * cc + tt;
-                    const float h0 = silu_fast(acc[gt][2 * d]) * acc[G::NTT + gt][2 * d];
-                    const float h1 = silu_fast(acc[gt][2 * d + 1]) * acc[G::NTT + gt][2 * d + 1];
-                    split_bf16x2(h0, h1, PH[tt][d], PL[tt][d]);
-                }
-            const int src0 = c + 32 * (g & 1), src1 = src0 + 16;
-            const bool hi = g >= 2;
-            uint32_t bh[4], bl[4];
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {
-                const uint32_t h00 = (uint32_t)__shfl((int)PH[0][d], src0, kWave);
-                const uint32_t h10 = (uint32_t)__shfl((int)PH[1][d], src0, kWave);
-                const uint32_t h01 = (uint32_t)__shfl((int)PH[0][d], src1, kWave);
-                const uint32_t h11 = (uint32_t)__shfl((int)PH[1][d], src1, kWave);
-                const uint32_t l00 = (uint32_t)__shfl((int)PL[0][d], src0, kWave);
-                const uint32_t l10 = (uint32_t)__shfl((int)PL[1][d], src0, kWave);
-                const uint32_t l01 = (uint32_t)__shfl((int)PL[0][d], src1, kWave);
-                const uint32_t l11 = (uint32_t)__shfl((int)PL[1][d], src1, kWave);
-                bh[d] = hi ? h10 : h00;
-                bh[2 + d] = hi ? h11 : h01;
-                bl[d] = hi ? l10 : l00;
-                bl[2 + d] = hi ? l11 : l01;
-            }
-            Bh[cc] = __builtin_bit_cast(bf16x8_t, u32x4_t{bh[0], bh[1], bh[2], bh[3]});
-            Bl[cc] = __builtin_bit_cast(bf16x8_t, u32x4_t{bl[0], bl[1], bl[2], bl[3]});
-        }
+        mx_swiglu<SL>(acc, c, g, Bh, Bl);
 
         // ---- down: the slice's SL columns of all H rows, partial sums times the routing weight
         const int pbase = c < cur.ne ? 4 * ((cur.prow * nsl + cur.s) * H + 4 * g) : kOob;
@@ -409,6 +432,79 @@ __global__ void __launch_bounds__(kMT) mx_wave_kernel(DecArgs a, int nsl) {
         cur = nxt;
         v += stride;
     } while (v < n_items);
+
+    if (coop_wave) {
+        // leftover items kMU * grid + b + grid * r of workgroup b, run by its waves kMU .. 2 kMU - 1 together
+        // (each takes part in every round, so all kMU of them arrive at every count below)
+        const int cw = wave - kMU;
+        const int grid = (int)gridDim.x;
+        for (int r = 0;; ++r) {
+            const int lv = kMU * grid + (int)blockIdx.x + grid * r;
+            if (lv >= n_items) break;  // uniform over the workgroup's leftover waves
+            const Item it = decode_item(a, tb, n_act, nsl, lv, true, c);
+            const int row = it.tok >= 0 ? it.tok : T;
+            f32x4_t acc[2 * G::NTT];
+#pragma unroll
+            for (int q = 0; q < 2 * G::NTT; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            // gate_up groups cw, cw + kMU, ...: groups past NGA load zeros and their chunks are skipped
+            int ga = cw;
+            mx_issue_a<SL>(a, it, ga, lane, R0);
+            mx_issue_a<SL>(a, it, ga + kMU, lane, R1);
+            __builtin_amdgcn_sched_barrier(0);
+            for (; ga + 2 * kMU < NGA; ga += 2 * kMU) {
+                mx_compute_a<SL>(a, R0, ga, xs, row, g, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                mx_issue_a<SL>(a, it, ga + 2 * kMU, lane, R0);
+                __builtin_amdgcn_sched_barrier(0);
+                mx_compute_a<SL>(a, R1, ga + kMU, xs, row, g, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                mx_issue_a<SL>(a, it, ga + 3 * kMU, lane, R1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            mx_compute_a<SL>(a, R0, ga, xs, row, g, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            mx_compute_a<SL>(a, R1, ga + kMU, xs, row, g, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            // the kMU partial sums meet in LDS (the previous round's have all been read)
+            mx_lds_wait_count(&coop_cnt[1], kMU * r);
+#pragma unroll
+            for (int q = 0; q < 2 * G::NTT; ++q) coop_red[cw][q][lane] = acc[q];
+            if (lane == 0) __hip_atomic_fetch_add(&coop_cnt[0], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            mx_lds_wait_count(&coop_cnt[0], kMU * (r + 1));
+#pragma unroll
+            for (int q = 0; q < 2 * G::NTT; ++q) {
+                f32x4_t t = coop_red[0][q][lane];
+#pragma unroll
+                for (int w = 1; w < kMU; ++w) t += coop_red[w][q][lane];
+                acc[q] = t;
+                __builtin_amdgcn_sched_barrier(0);  // a tile at a time
+            }
+            if (lane == 0) __hip_atomic_fetch_add(&coop_cnt[1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            bf16x8_t Bh[G::CH], Bl[G::CH];
+            mx_swiglu<SL>(acc, c, g, Bh, Bl);
+            // down groups cw, cw + kMU, ...: groups past NGB load zeros and store nothing
+            __builtin_amdgcn_sched_barrier(0);
+            mx_issue_b<SL>(a, it, cw, lane, R0);
+            mx_issue_b<SL>(a, it, cw + kMU, lane, R1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int pbase = c < it.ne ? 4 * ((it.prow * nsl + it.s) * H + 4 * g) : kOob;
+            int gb = cw;
+            for (; gb + 2 * kMU < NGB; gb += 2 * kMU) {
+                mx_compute_b<SL>(a, R0, gb, Bh, Bl, it.wc, pres, pbase);
+                __builtin_amdgcn_sched_barrier(0);
+                mx_issue_b<SL>(a, it, gb + 2 * kMU, lane, R0);
+                __builtin_amdgcn_sched_barrier(0);
+                mx_compute_b<SL>(a, R1, gb + kMU, Bh, Bl, it.wc, pres, pbase);
+                __builtin_amdgcn_sched_barrier(0);
+                mx_issue_b<SL>(a, it, gb + 3 * kMU, lane, R1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            mx_compute_b<SL>(a, R0, gb, Bh, Bl, it.wc, pres, pbase);
+            __builtin_amdgcn_sched_barrier(0);
+            mx_compute_b<SL>(a, R1, gb + kMU, Bh, Bl, it.wc, pres, pbase);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 }
 
 // ------------------------------------------------------------------ dequant hooks
@@ -639,8 +735,12 @@ hipError_t launch_mx_wave(const DecArgs& a, int items_max, int nsl, int grid, si
     hipError_t e;
     if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<SL, true, ROUTE>))) != hipSuccess) return e;
     if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<SL, false, ROUTE>))) != hipSuccess) return e;
+    if ((e = allow_mx_lds(reinterpret_cast<const void*>(&mx_wave_kernel<SL, false, ROUTE, true>))) != hipSuccess)
+        return e;
     if (items_max > grid * kMW)
         hipLaunchKernelGGL((mx_wave_kernel<SL, true, ROUTE>), dim3(grid), dim3(kMT), lds, s, a, nsl);
+    else if (items_max > grid * kMU && items_max <= grid * (kMU + 2))  // a few leftovers: up to two rounds
+        hipLaunchKernelGGL((mx_wave_kernel<SL, false, ROUTE, true>), dim3(grid), dim3(kMT), lds, s, a, nsl);
     else
         hipLaunchKernelGGL((mx_wave_kernel<SL, false, ROUTE>), dim3(grid), dim3(kMT), lds, s, a, nsl);
     return hipGetLastError();
